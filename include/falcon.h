@@ -1,0 +1,156 @@
+/*
+ * falcon.h - C interface of libfalcon: the Falcon fast-weight state update and
+ * read-after-write readout on AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2608.27763, "Fast Weight Attention for Continual
+ * Learning", as described by the papers.ananclaw.com explainer, section
+ * 核心方法 §1-§3, and the 163.com article, sections 01 and 02):
+ *
+ *   per (batch b, head h), t = 1..L, value rows i = 1..dv
+ *     x_t = k_{t-1}  (x_1 = k_prev, or the zero vector when k_prev == NULL)
+ *     y_t = v_t
+ *     W_t = { max(1, t-B+1), ..., t }     (B = window; 1 except Falcon-3/3A)
+ *     n_t = sum_{j in W_t} ||x_j||^2
+ *     eta_t = beta_t / (eps + n_t)        (one per value row for Falcon-2/2A)
+ *     regression   (Falcon-1/2/3):  S_t = (1 - eta_t lambda) S_{t-1}
+ *                                   + eta_t sum_{j in W_t} (y_j - S_{t-1} x_j) x_j^T
+ *     inner product (Falcon-1A/2A/3A): S_t = (1 - eta_t lambda) S_{t-1}
+ *                                   + eta_t sum_{j in W_t} y_j x_j^T
+ *     o_t = S_t q_t
+ *
+ * S is dv x dk (it maps key space to value space).  A fresh sequence starts
+ * from S_0 = 0 with x_1 = 0, which leaves S_1 = 0 (the step with x_1 = 0 is
+ * taken with unit decay and zero write; that equals the literal step because
+ * S_0 = 0).
+ *
+ * Layouts (all row-major and contiguous, element = dtype unless stated):
+ *   q, k     [batch, heads, L, dk]          v        [batch, heads, L, dv]
+ *   k_prev   [batch, heads, dk]             o        [batch, heads, L, dv]  float32
+ *   S0, S_out [batch, heads, dv, dk]  float32
+ *   beta_t   NULL (scalar beta), [batch, heads, L] (FALCON_BETA_TOKEN) or
+ *            [batch, heads, L, dv] (FALCON_BETA_CHANNEL, Falcon-2/2A only)
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, keeps no mutable global state and is reentrant.  Work is
+ * enqueued on `stream` (a hipStream_t passed as void*, NULL = the default
+ * stream) and is asynchronous; buffers must stay alive until it completes.
+ *
+ * Errors: the return value is the only channel (no printing, no abort).  All
+ * validation happens before any HIP call; a call that returns an error
+ * enqueues nothing.  FALCON_ERR_HIP reports a failed launch.
+ *
+ * Determinism: fixed reduction order and no atomics, so repeated calls give
+ * bitwise identical results.
+ */
+#ifndef FALCON_H
+#define FALCON_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FALCON_ABI_VERSION 1
+
+/* The six update rules (explainer, section 核心方法 §2, variant table;
+ * 163.com section 02: objective axis x granularity axis). */
+typedef enum {
+  FALCON_1 = 0,  /* squared error, one eta shared by all value channels */
+  FALCON_2 = 1,  /* squared error, one eta per value channel (row of S) */
+  FALCON_3 = 2,  /* squared error, sliding window of the B latest samples */
+  FALCON_1A = 3, /* negative inner product, shared eta */
+  FALCON_2A = 4, /* negative inner product, per-channel eta */
+  FALCON_3A = 5  /* negative inner product, sliding window */
+} falcon_variant;
+
+/* Element type of q, k, v, k_prev and beta_t.  S, o are always float32. */
+typedef enum { FALCON_BF16 = 0, FALCON_F32 = 1 } falcon_dtype;
+
+/* Shape of beta_t. */
+typedef enum {
+  FALCON_BETA_SCALAR = 0,  /* beta_t must be NULL; the float `beta` is used */
+  FALCON_BETA_TOKEN = 1,   /* one gain per (batch, head, token) */
+  FALCON_BETA_CHANNEL = 2  /* one gain per (batch, head, token, value channel) */
+} falcon_beta_kind;
+
+typedef enum {
+  FALCON_OK = 0,
+  FALCON_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum, misalignment,
+                                 non-finite or negative hyper-parameter, ... */
+  FALCON_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels cover */
+  FALCON_ERR_HIP = 3          /* the HIP runtime reported a launch failure */
+} falcon_status;
+
+/* Returns FALCON_ABI_VERSION. */
+int falcon_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* falcon_status_string(int status);
+
+/*
+ * falcon_fwd_recurrent - the recurrent form, one token at a time (explainer
+ * §3 "recurrent", O(d^2) per step).  Every variant, window >= 1, bf16 or fp32
+ * inputs.
+ *
+ *   variant   falcon_variant
+ *   window    B >= 1; must be 1 unless variant is FALCON_3 / FALCON_3A
+ *   beta, beta_t, beta_kind   plasticity gain (scalar, per token, per channel)
+ *   lambda    forgetting strength, finite, >= 0
+ *   eps       normalizer floor, finite, >= 0 (eps = 0 with a zero key after
+ *             the first step gives non-finite outputs)
+ *   batch, heads, seqlen (L >= 1), dk, dv     sizes; dk, dv in {16,32,64,128}
+ *   dtype     falcon_dtype of q, k, v, k_prev, beta_t
+ *   q, k, v   inputs (device)
+ *   k_prev    key carried from the previous call, or NULL (fresh sequence)
+ *   S0        initial state, or NULL (zero).  S0 != NULL requires k_prev.
+ *             window > 1 with S0 != NULL is unsupported (the window history
+ *             is not carried).
+ *   o         output [batch, heads, L, dv] float32 (must not alias inputs)
+ *   S_out     final state, or NULL; may equal S0 (in-place carry)
+ *   stream    hipStream_t or NULL
+ * All pointers 16-byte aligned.
+ */
+int falcon_fwd_recurrent(int variant, int window, float beta, const void* beta_t,
+                         int beta_kind, float lambda, float eps, int batch, int heads,
+                         int seqlen, int dk, int dv, int dtype, const void* q,
+                         const void* k, const void* v, const void* k_prev,
+                         const float* S0, float* o, float* S_out, void* stream);
+
+/*
+ * falcon_fwd_chunk - the chunk-parallel form (explainer §3 "chunk-parallel";
+ * 163.com section 02 (2): parallel inside a chunk, only the fixed-size state
+ * crosses chunks).  Same arguments and results as falcon_fwd_recurrent plus
+ *   chunk     tokens per chunk, in {16, 32, 64}; L % chunk == 0
+ * Restrictions (FALCON_ERR_UNSUPPORTED): dtype must be FALCON_BF16;
+ * window <= 4; window <= chunk.
+ * The result equals the recurrence up to floating-point rounding (state
+ * carried in float32, products on bf16 matrix cores with split-bf16 operands
+ * where an operand is not an exact bf16 input).
+ */
+int falcon_fwd_chunk(int variant, int window, float beta, const void* beta_t,
+                     int beta_kind, float lambda, float eps, int batch, int heads,
+                     int seqlen, int dk, int dv, int dtype, const void* q, const void* k,
+                     const void* v, const void* k_prev, const float* S0, float* o,
+                     float* S_out, int chunk, void* stream);
+
+/*
+ * falcon_decode_step - one token of the recurrent form for serving (explainer
+ * §3, recurrent form for inference; 163.com section 01 read-after-write):
+ *   x = k_prev, y = v, S <- update(S), o = S_new q, then k_prev <- k.
+ * S [nseq, heads, dv, dk] float32 and k_prev [nseq, heads, dk] are updated in
+ * place; q, k [nseq, heads, dk], v [nseq, heads, dv]; o [nseq, heads, dv]
+ * float32; beta_t NULL, [nseq, heads] (FALCON_BETA_TOKEN) or
+ * [nseq, heads, dv] (FALCON_BETA_CHANNEL, Falcon-2/2A).
+ * Variants FALCON_1, FALCON_2, FALCON_1A, FALCON_2A (the sliding-window
+ * variants need a carried history: FALCON_ERR_UNSUPPORTED).
+ * k_prev must not alias k.
+ */
+int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kind,
+                       float lambda, float eps, int nseq, int heads, int dk, int dv,
+                       int dtype, float* S, void* k_prev, const void* q, const void* k,
+                       const void* v, float* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALCON_H */

@@ -1,0 +1,185 @@
+"""ctypes binding of libfalcon's C entry points (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI; this
+module checks torch tensors (device, dtype, contiguity, shape), allocates the
+outputs with torch, and passes raw pointers plus the current HIP stream.  When
+the library is missing it raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+FALCON_1, FALCON_2, FALCON_3, FALCON_1A, FALCON_2A, FALCON_3A = range(6)
+VARIANT_NAMES = {"falcon1": FALCON_1, "falcon2": FALCON_2, "falcon3": FALCON_3,
+                 "falcon1a": FALCON_1A, "falcon2a": FALCON_2A, "falcon3a": FALCON_3A}
+_BF16, _F32 = 0, 1
+_BETA_SCALAR, _BETA_TOKEN, _BETA_CHANNEL = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FalconError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfalcon.so")
+
+
+def load_library():
+    """Load libfalcon.so from the package directory (built in-tree)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError("libfalcon.so not built at %s; run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.falcon_abi_version.restype = i
+    lib.falcon_abi_version.argtypes = []
+    lib.falcon_status_string.restype = ctypes.c_char_p
+    lib.falcon_status_string.argtypes = [i]
+    seq_args = [i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.falcon_fwd_recurrent.restype = i
+    lib.falcon_fwd_recurrent.argtypes = seq_args + [vp]
+    lib.falcon_fwd_chunk.restype = i
+    lib.falcon_fwd_chunk.argtypes = seq_args + [i, vp]
+    lib.falcon_decode_step.restype = i
+    lib.falcon_decode_step.argtypes = [i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                       vp, vp]
+    _LIB = lib
+    return lib
+
+
+def _variant(v):
+    if isinstance(v, str):
+        return VARIANT_NAMES[v.lower().replace("-", "")]
+    return int(v)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(torch, t):
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError("inputs must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check(torch, name, t, shape, dtype, device):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must live on %s" % (name, device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s shape %s != %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(torch, device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise(lib, fn, status):
+    if status != 0:
+        raise FalconError(fn, status, lib.falcon_status_string(status).decode())
+
+
+def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev, S0,
+              out, S_out, return_state, chunk, stream):
+    import torch
+    lib = load_library()
+    variant = _variant(variant)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, heads, L, d]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    dcode = _dtype_code(torch, q)
+    _check(torch, "q", q, (B, H, L, dk), dt, dev)
+    _check(torch, "k", k, (B, H, L, dk), dt, dev)
+    _check(torch, "v", v, (B, H, L, dv), dt, dev)
+    _check(torch, "k_prev", k_prev, (B, H, dk), dt, dev)
+    _check(torch, "S0", S0, (B, H, dv, dk), torch.float32, dev)
+    kind = _BETA_SCALAR
+    if beta_t is not None:
+        if beta_t.dim() == 3:
+            kind = _BETA_TOKEN
+            _check(torch, "beta_t", beta_t, (B, H, L), dt, dev)
+        else:
+            kind = _BETA_CHANNEL
+            _check(torch, "beta_t", beta_t, (B, H, L, dv), dt, dev)
+    if out is None:
+        out = torch.empty((B, H, L, dv), device=dev, dtype=torch.float32)
+    _check(torch, "out", out, (B, H, L, dv), torch.float32, dev)
+    if S_out is None and return_state:
+        S_out = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
+    _check(torch, "S_out", S_out, (B, H, dv, dk), torch.float32, dev)
+    args = [variant, int(window), float(beta if beta is not None else 0.0), _ptr(beta_t), kind,
+            float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k), _ptr(v),
+            _ptr(k_prev), _ptr(S0), _ptr(out), _ptr(S_out)]
+    if fn_name == "falcon_fwd_chunk":
+        args.append(int(chunk))
+    args.append(_stream(torch, dev, stream))
+    status = getattr(lib, fn_name)(*args)
+    _raise(lib, fn_name, status)
+    return (out, S_out) if return_state else out
+
+
+def fwd_recurrent(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
+                  k_prev=None, S0=None, out=None, S_out=None, return_state=False, stream=None):
+    """Recurrent form.  Returns o [B,H,L,dv] float32 (and S_L with return_state)."""
+    return _seq_call("falcon_fwd_recurrent", q, k, v, variant, beta, lam, eps, window, beta_t,
+                     k_prev, S0, out, S_out, return_state, None, stream)
+
+
+def fwd_chunk(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, chunk=64, window=1,
+              beta_t=None, k_prev=None, S0=None, out=None, S_out=None, return_state=False,
+              stream=None):
+    """Chunk-parallel form.  Returns o [B,H,L,dv] float32 (and S_L with return_state)."""
+    return _seq_call("falcon_fwd_chunk", q, k, v, variant, beta, lam, eps, window, beta_t,
+                     k_prev, S0, out, S_out, return_state, chunk, stream)
+
+
+def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, beta_t=None,
+                out=None, stream=None):
+    """One decode step; updates S and k_prev in place, returns o [N,H,dv] float32."""
+    import torch
+    lib = load_library()
+    variant = _variant(variant)
+    N, H, dv, dk = S.shape
+    dev = S.device
+    dt = q.dtype
+    dcode = _dtype_code(torch, q)
+    _check(torch, "S", S, (N, H, dv, dk), torch.float32, dev)
+    _check(torch, "k_prev", k_prev, (N, H, dk), dt, dev)
+    _check(torch, "q", q, (N, H, dk), dt, dev)
+    _check(torch, "k", k, (N, H, dk), dt, dev)
+    _check(torch, "v", v, (N, H, dv), dt, dev)
+    kind = _BETA_SCALAR
+    if beta_t is not None:
+        kind = _BETA_TOKEN if beta_t.dim() == 2 else _BETA_CHANNEL
+        _check(torch, "beta_t", beta_t, (N, H) if kind == _BETA_TOKEN else (N, H, dv), dt, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), device=dev, dtype=torch.float32)
+    _check(torch, "out", out, (N, H, dv), torch.float32, dev)
+    status = lib.falcon_decode_step(variant, float(beta if beta is not None else 0.0),
+                                    _ptr(beta_t), kind, float(lam), float(eps), N, H, dk, dv,
+                                    dcode, _ptr(S), _ptr(k_prev), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(out), _stream(torch, dev, stream))
+    _raise(lib, "falcon_decode_step", status)
+    return out
