@@ -1,0 +1,120 @@
+"""fp64 model of the chunk-parallel algorithm the HIP chunk kernel implements.
+
+Test-side only: it validates, against the oracle's recurrence, the algebra the
+kernel is built on (sub-chunks, window unknowns, decay products, blocked
+unit-lower-triangular solve, per-key folding, readout and carry).  It shares
+no code with the kernel; it is the same sequence of steps written in numpy.
+
+Within a sub-chunk of c steps starting from state S0 (per value row i):
+  g_t = prod_{r<=t} a_r (g_{-1} = 1), zeta_t = eta_t / g_t
+  unknowns u = (t, w), w = 0..B-1, key j(u) = t - w:
+    e_u + g_{t-1} sum_{s<t, w'} G[j(u), j(s,w')] z_{(s,w')} = y_{j(u)} - g_{t-1} S0 x_{j(u)}
+    z_u = zeta_t e_u   (inner-product family: e_u = y_{j(u)}, no solve)
+  o_t   = g_t (S0 q_t + sum_{s<=t, w'} (q_t . x_{j(s,w')}) z_{(s,w')})
+  S_c   = g_{c-1} (S0 + sum_j F_j x_j^T),  F_j = sum_{u: j(u)=j} z_u
+(163.com section 02 (2): inside a chunk everything is parallel, only the fixed
+size state crosses chunks; explainer §3 chunk-parallel form.)
+"""
+import numpy as np
+
+
+def sub_chunk_size(chunk, window):
+    c = chunk
+    while c * window > 64:
+        c //= 2
+    return c
+
+
+def chunk_forward(regression, per_row, q, k, v, *, beta, lam, eps, window, chunk,
+                  beta_t=None, k_prev=None, S0=None, blk=16):
+    """q, k [L, dk]; v [L, dv]; beta_t None, [L] or [L, dv].  One (batch, head)."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    B = window
+    c = sub_chunk_size(chunk, B)
+    U = c * B
+    S = np.zeros((dv, dk)) if S0 is None else S0.astype(np.float64).copy()
+    o = np.zeros((L, dv))
+
+    def key(g):                      # x_g (0-based global step g)
+        if g < 0:
+            return np.zeros(dk)
+        if g == 0:
+            return np.zeros(dk) if k_prev is None else k_prev.astype(np.float64)
+        return k[g - 1].astype(np.float64)
+
+    def val(g):
+        return np.zeros(dv) if g < 0 else v[g].astype(np.float64)
+
+    c_full = c
+    for t0 in range(0, L, c_full):
+        c = min(c_full, L - t0)          # ragged tail
+        U = c * B
+        nx = c + B - 1
+        X = np.stack([key(t0 - B + 1 + jj) for jj in range(nx)])      # [nx, dk]
+        Y = np.stack([val(t0 - B + 1 + jj) for jj in range(nx)])      # [nx, dv]
+        Q = q[t0:t0 + c].astype(np.float64)
+        jof = lambda u: u // B - u % B + B - 1                         # local key of unknown
+        # scalars
+        nrm = np.sum(X * X, axis=1)
+        eta = np.zeros((c, dv))
+        a = np.zeros((c, dv))
+        for t in range(c):
+            n = sum(nrm[jof(t * B + w)] for w in range(B))
+            if beta_t is None:
+                b = np.full(dv, beta)
+            elif beta_t.ndim == 2:
+                b = beta_t[t0 + t].astype(np.float64)
+            else:
+                b = np.full(dv, float(beta_t[t0 + t]))
+            if t0 + t == 0 and k_prev is None:
+                eta[t], a[t] = 0.0, 1.0                                # fresh start
+            else:
+                eta[t] = b / (eps + n)
+                a[t] = 1.0 - eta[t] * lam
+        if not per_row:
+            assert np.all(eta == eta[:, :1])
+        g = np.cumprod(a, axis=0)                                      # [c, dv]
+        gm1 = np.vstack([np.ones((1, dv)), g[:-1]])
+        zeta = eta / g
+        G = X @ X.T
+        P = Q @ X.T
+        # gathered, masked Gram over unknowns and readout weights
+        Gt = np.zeros((U, U))
+        Pt = np.zeros((c, U))
+        for u in range(U):
+            for u2 in range(U):
+                if u2 // B < u // B:
+                    Gt[u, u2] = G[jof(u), jof(u2)]
+        for t in range(c):
+            for u2 in range(U):
+                if u2 // B <= t:
+                    Pt[t, u2] = P[t, jof(u2)]
+        step = np.arange(U) // B
+        XS0 = X @ S.T                                                  # [nx, dv]
+        if regression:
+            R = np.stack([Y[jof(u)] - gm1[u // B] * XS0[jof(u)] for u in range(U)])  # [U, dv]
+            Z = np.zeros((U, dv))
+            for b0 in range(0, U, blk):
+                b1 = min(U, b0 + blk)
+                Rb = R[b0:b1] - gm1[step[b0:b1]] * (Gt[b0:b1, :b0] @ Z[:b0])
+                if not per_row:
+                    # shared diagonal block inverse T_bb = (I + A_bb)^-1
+                    A = gm1[step[b0:b1], 0][:, None] * Gt[b0:b1, b0:b1] \
+                        * zeta[step[b0:b1], 0][None, :]
+                    T = np.linalg.inv(np.eye(b1 - b0) + A)
+                    Eb = T @ Rb
+                    Z[b0:b1] = zeta[step[b0:b1]] * Eb
+                else:
+                    # per-row forward substitution inside the block
+                    for uu in range(b0, b1):
+                        e = Rb[uu - b0] - gm1[step[uu]] * (Gt[uu, b0:uu] @ Z[b0:uu])
+                        Z[uu] = zeta[step[uu]] * e
+        else:
+            Z = np.stack([zeta[u // B] * Y[jof(u)] for u in range(U)])
+        F = np.zeros((nx, dv))
+        for u in range(U):
+            F[jof(u)] += Z[u]
+        o[t0:t0 + c] = g * (Q @ S.T + Pt @ Z)
+        S = g[-1][:, None] * (S + F.T @ X)
+    return o, S

@@ -1,0 +1,148 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+declared in include/falcon.h, and rejects bad arguments before any HIP call
+(fake, never-dereferenced pointers are enough for that)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_recurrent_memory_amd as fw
+from weight_recurrent_memory_amd import binding
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "falcon.h")
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from weight_recurrent_memory_amd import build_lib
+        build_lib.build()
+    return fw.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(falcon_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("falcon_fwd_recurrent", "falcon_fwd_chunk", "falcon_decode_step",
+              "falcon_abi_version", "falcon_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing but the C interface leaks out of the library
+    falcon_syms = {s for s in exported if "falcon" in s}
+    assert falcon_syms == set(_declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.falcon_abi_version() == 1
+    assert lib.falcon_status_string(0) == b"ok"
+    assert lib.falcon_status_string(1) == b"invalid argument"
+    assert lib.falcon_status_string(2) == b"unsupported configuration"
+    assert lib.falcon_status_string(3) == b"HIP launch failure"
+    assert lib.falcon_status_string(99) == b"unknown status"
+
+
+# Fake device addresses: validation must reject every call below before touching them.
+P = [0x100000000 + 0x10000000 * i for i in range(12)]
+
+
+def _seq(lib, fn="falcon_fwd_chunk", **over):
+    a = dict(variant=0, window=1, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6,
+             batch=1, heads=1, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2],
+             k_prev=None, S0=None, o=P[3], S_out=None, chunk=64)
+    a.update(over)
+    args = [a["variant"], a["window"], a["beta"], a["beta_t"], a["beta_kind"], a["lam"], a["eps"],
+            a["batch"], a["heads"], a["seqlen"], a["dk"], a["dv"], a["dtype"], a["q"], a["k"],
+            a["v"], a["k_prev"], a["S0"], a["o"], a["S_out"]]
+    if fn == "falcon_fwd_chunk":
+        args.append(a["chunk"])
+    args.append(None)
+    return getattr(lib, fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["falcon_fwd_chunk", "falcon_fwd_recurrent"])
+@pytest.mark.parametrize("over,status", [
+    (dict(variant=6), INVALID),
+    (dict(variant=-1), INVALID),
+    (dict(window=0), INVALID),
+    (dict(window=2), INVALID),                       # window > 1 outside Falcon-3/3A
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(q=P[0] + 2), INVALID),                     # misaligned
+    (dict(seqlen=0), INVALID),
+    (dict(batch=-3), INVALID),
+    (dict(lam=-0.1), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(beta=float("inf")), INVALID),
+    (dict(beta_kind=1), INVALID),                    # per-token beta without a pointer
+    (dict(beta_kind=0, beta_t=P[5]), INVALID),       # pointer with scalar kind
+    (dict(beta_kind=2, beta_t=P[5]), INVALID),       # per-channel beta on Falcon-1
+    (dict(beta_kind=3, beta_t=P[5]), INVALID),
+    (dict(S0=P[6]), INVALID),                        # state without the carried key
+    (dict(o=P[0]), INVALID),                         # output aliases q
+    (dict(dtype=7), INVALID),
+    (dict(dk=48), UNSUPPORTED),
+    (dict(dv=256), UNSUPPORTED),
+    (dict(variant=2, window=2, k_prev=P[7], S0=P[6]), UNSUPPORTED),  # no window history
+])
+def test_seq_validation(lib, fn, over, status):
+    assert _seq(lib, fn, **over) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(chunk=0), INVALID),
+    (dict(chunk=48), UNSUPPORTED),
+    (dict(chunk=128), UNSUPPORTED),
+    (dict(dtype=1), UNSUPPORTED),
+    (dict(variant=2, window=8), UNSUPPORTED),
+    (dict(variant=2, window=32, chunk=16), INVALID),  # window > chunk
+])
+def test_chunk_only_validation(lib, over, status):
+    assert _seq(lib, "falcon_fwd_chunk", **over) == status
+
+
+def test_recurrent_window_limit(lib):
+    assert _seq(lib, "falcon_fwd_recurrent", variant=2, window=9) == UNSUPPORTED
+
+
+def _dec(lib, **over):
+    a = dict(variant=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, nseq=2, heads=2,
+             dk=64, dv=64, dtype=0, S=P[0], k_prev=P[1], q=P[2], k=P[3], v=P[4], o=P[5])
+    a.update(over)
+    return lib.falcon_decode_step(a["variant"], a["beta"], a["beta_t"], a["beta_kind"], a["lam"],
+                                  a["eps"], a["nseq"], a["heads"], a["dk"], a["dv"], a["dtype"],
+                                  a["S"], a["k_prev"], a["q"], a["k"], a["v"], a["o"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(variant=9), INVALID),
+    (dict(S=None), INVALID),
+    (dict(k_prev=P[3]), INVALID),                    # k_prev aliases k
+    (dict(o=P[0]), INVALID),
+    (dict(nseq=0), INVALID),
+    (dict(beta_kind=2, beta_t=P[6]), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(variant=2), UNSUPPORTED),                  # Falcon-3 needs window history
+    (dict(variant=5), UNSUPPORTED),
+    (dict(dk=80), UNSUPPORTED),
+])
+def test_decode_validation(lib, over, status):
+    assert _dec(lib, **over) == status

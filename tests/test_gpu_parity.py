@@ -1,0 +1,287 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Small cases span several tiles and a ragged tail and are compared element by
+element on every output; the full workloads are compared on sampled
+(batch, head) chains that the oracle recomputes one by one.
+"""
+import numpy as np
+import pytest
+
+from oracle import falcon_oracle as fo
+from weight_recurrent_memory_amd.inputs import WORKLOADS, decode_inputs, seq_inputs
+from parity_util import (TOL_BF16, TOL_F32, TOL_FP32_MATH, state_err, to_dev,
+                         token_normwise_err)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import weight_recurrent_memory_amd as fw  # noqa: E402
+
+ALL = [fw.FALCON_1, fw.FALCON_2, fw.FALCON_3, fw.FALCON_1A, fw.FALCON_2A, fw.FALCON_3A]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fw.load_library()
+
+
+def _win(variant, w=3):
+    return w if variant in (fw.FALCON_3, fw.FALCON_3A) else 1
+
+
+def _run_seq(form, variant, inp, dt, *, beta, lam, eps, window, chunk=64, carried=False):
+    q = to_dev(torch, inp["q"], dt)
+    k = to_dev(torch, inp["k"], dt)
+    v = to_dev(torch, inp["v"], dt)
+    bt = to_dev(torch, inp["beta_t"], dt) if "beta_t" in inp else None
+    kp = to_dev(torch, inp["k_prev"], dt) if carried else None
+    S0 = to_dev(torch, inp["S0"], torch.float32) if carried and "S0" in inp else None
+    kw = dict(variant=variant, beta=beta, lam=lam, eps=eps, window=window, beta_t=bt,
+              k_prev=kp, S0=S0, return_state=True)
+    if form == "chunk":
+        o, S = fw.fwd_chunk(q, k, v, chunk=chunk, **kw)
+    else:
+        o, S = fw.fwd_recurrent(q, k, v, **kw)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), S.cpu().numpy()
+
+
+def _oracle(variant, inp, *, beta, lam, eps, window, carried=False, chains=None):
+    sel = (lambda a: a) if chains is None else (lambda a: a.reshape((-1,) + a.shape[2:])[chains][:, None])
+    return fo.falcon_recurrence(
+        variant, sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), beta=beta, lam=lam, eps=eps,
+        window=window, beta_t=sel(inp["beta_t"]) if "beta_t" in inp else None,
+        k_prev=sel(inp["k_prev"]) if carried else None,
+        S0=sel(inp["S0"]) if carried and "S0" in inp else None)
+
+
+# ---------------------------------------------------------------------------
+# recurrent form
+
+def test_recurrent_fp32_1x1x64x16():
+    cfg = WORKLOADS["recurrent_f32_1x1x64x16"]
+    B, H, L, dk, dv = cfg["shape"]
+    inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="f32")
+    o, S = _run_seq("rec", fw.FALCON_1, inp, torch.float32, beta=cfg["beta"], lam=cfg["lam"],
+                    eps=cfg["eps"], window=1)
+    o_ref, S_ref, _ = _oracle(fw.FALCON_1, inp, beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"],
+                              window=1)
+    err, zok = token_normwise_err(o, o_ref)
+    print("recurrent fp32 1x1x64x16: o err %.3e  S err %.3e" % (err, state_err(S, S_ref)))
+    assert zok and err <= TOL_F32
+    assert state_err(S, S_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("carried", [False, True])
+def test_recurrent_small(variant, dtype, carried):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    win = _win(variant)
+    if carried and win > 1:
+        carried_S0 = False
+    else:
+        carried_S0 = carried
+    inp = seq_inputs(2, 3, 45, 32, 16, seed=200 + variant, dtype=dtype, with_k_prev=carried,
+                     with_S0=carried_S0, beta_per_channel=per_ch, beta_per_token=not per_ch,
+                     s_std=0.3)
+    if carried and not carried_S0:
+        inp.pop("S0", None)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o, S = _run_seq("rec", variant, inp, dt, beta=None, lam=0.02, eps=1e-6, window=win,
+                    carried=carried)
+    o_ref, S_ref, _ = _oracle(variant, inp, beta=None, lam=0.02, eps=1e-6, window=win,
+                              carried=carried)
+    err, zok = token_normwise_err(o, o_ref)
+    assert zok and err <= TOL_FP32_MATH, err
+    assert state_err(S, S_ref) <= TOL_FP32_MATH
+
+
+# ---------------------------------------------------------------------------
+# chunk form, small shapes: several tiles, ragged tails, every variant
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 16), (128, 32), (16, 128)])
+def test_chunk_small(variant, chunk, dk, dv):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    windows = [2, 4] if variant in (fw.FALCON_3, fw.FALCON_3A) else [1]
+    for win in windows:
+        if win > chunk:
+            continue
+        L = 3 * chunk + 11                                  # ragged tail
+        inp = seq_inputs(2, 2, L, dk, dv, seed=300 + variant * 7 + win, dtype="bf16",
+                         beta_per_channel=per_ch, beta_per_token=not per_ch)
+        o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=None, lam=0.02, eps=1e-6,
+                        window=win, chunk=chunk)
+        o_ref, S_ref, _ = _oracle(variant, inp, beta=None, lam=0.02, eps=1e-6, window=win)
+        err, zok = token_normwise_err(o, o_ref)
+        serr = state_err(S, S_ref)
+        print("chunk v%d C%d dk%d dv%d B%d: o err %.3e S err %.3e" % (variant, chunk, dk, dv, win,
+                                                                    err, serr))
+        assert zok, "tokens with o_ref == 0 must be exactly 0"
+        assert err <= TOL_BF16 and serr <= TOL_BF16
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_2, fw.FALCON_1A, fw.FALCON_2A])
+def test_chunk_carried_state(variant):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    inp = seq_inputs(2, 3, 150, 64, 64, seed=400 + variant, dtype="bf16", with_k_prev=True,
+                     with_S0=True, beta_per_channel=per_ch, beta_per_token=not per_ch, s_std=0.2)
+    o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=None, lam=0.01, eps=1e-6,
+                    window=1, chunk=64, carried=True)
+    o_ref, S_ref, _ = _oracle(variant, inp, beta=None, lam=0.01, eps=1e-6, window=1, carried=True)
+    err, zok = token_normwise_err(o, o_ref)
+    assert zok and err <= TOL_BF16, err
+    assert state_err(S, S_ref) <= TOL_BF16
+
+
+def test_chunk_resume_matches_single_call():
+    inp = seq_inputs(1, 4, 256, 64, 64, seed=410, dtype="bf16")
+    dt = torch.bfloat16
+    q, k, v = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
+    o_full, S_full = fw.fwd_chunk(q, k, v, variant=fw.FALCON_1, beta=0.5, lam=0.01, eps=1e-6,
+                                  return_state=True)
+    m = 128
+    o1, S1 = fw.fwd_chunk(q[:, :, :m].contiguous(), k[:, :, :m].contiguous(),
+                          v[:, :, :m].contiguous(), variant=fw.FALCON_1, beta=0.5, lam=0.01,
+                          eps=1e-6, return_state=True)
+    kp = k[:, :, m - 1].contiguous()
+    o2, S2 = fw.fwd_chunk(q[:, :, m:].contiguous(), k[:, :, m:].contiguous(),
+                          v[:, :, m:].contiguous(), variant=fw.FALCON_1, beta=0.5, lam=0.01,
+                          eps=1e-6, k_prev=kp, S0=S1, return_state=True)
+    torch.cuda.synchronize()
+    o_split = torch.cat([o1, o2], dim=2).cpu().numpy()
+    err, _ = token_normwise_err(o_split, o_full.cpu().numpy())
+    assert err <= 1e-4
+    assert state_err(S2.cpu().numpy(), S_full.cpu().numpy()) <= 1e-4
+
+
+def test_chunk_deterministic():
+    inp = seq_inputs(2, 4, 512, 64, 64, seed=420, dtype="bf16")
+    outs = []
+    for _ in range(2):
+        o, S = _run_seq("chunk", fw.FALCON_1, inp, torch.bfloat16, beta=0.5, lam=0.01, eps=1e-6,
+                        window=1, chunk=64)
+        outs.append((o, S))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("L", [1, 5, 64, 65])
+def test_chunk_short_sequences(L):
+    inp = seq_inputs(1, 2, L, 64, 32, seed=430 + L, dtype="bf16")
+    for variant in (fw.FALCON_1, fw.FALCON_3A):
+        win = _win(variant, 4)
+        o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=0.5, lam=0.01, eps=1e-6,
+                        window=win, chunk=64)
+        o_ref, S_ref, _ = _oracle(variant, inp, beta=0.5, lam=0.01, eps=1e-6, window=win)
+        err, zok = token_normwise_err(o, o_ref)
+        assert zok and err <= TOL_BF16
+        assert state_err(S, S_ref) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# chunk form at the full workload sizes, sampled chains
+
+def _full_chunk_case(name, variant, chains, window=1):
+    cfg = WORKLOADS[name]
+    B, H, L, dk, dv = cfg["shape"]
+    per_ch = bool(cfg.get("beta_per_channel"))
+    inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16", beta_per_channel=per_ch)
+    beta = cfg["beta"] if cfg["beta"] is not None else None
+    print("case %s variant %d: launching" % (name, variant), flush=True)
+    o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=beta, lam=cfg["lam"],
+                    eps=cfg["eps"], window=window, chunk=cfg["chunk"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    o_ref, S_ref, _ = _oracle(variant, inp, beta=beta, lam=cfg["lam"], eps=cfg["eps"],
+                              window=window, chains=chains)
+    o_s = o.reshape((-1,) + o.shape[2:])[chains]
+    S_s = S.reshape((-1,) + S.shape[2:])[chains]
+    err, zok = token_normwise_err(o_s, o_ref[:, 0])
+    serr = state_err(S_s, S_ref[:, 0])
+    print("%s variant %d: o err %.3e  S err %.3e" % (name, variant, err, serr))
+    assert zok and err <= TOL_BF16
+    assert serr <= TOL_BF16
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_1A])
+def test_chunk_8x12x2048x64(variant):
+    _full_chunk_case("chunk_8x12x2048x64", variant, chains=[0, 41, 95])
+
+
+def test_chunk_percol_8x12x4096x64():
+    _full_chunk_case("chunk_percol_8x12x4096x64", fw.FALCON_2, chains=[0, 50, 95])
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
+def test_chunk_window4_4x16x8192x128(variant):
+    _full_chunk_case("chunk_window4_4x16x8192x128", variant, chains=[0, 63], window=4)
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+def _decode_run(variant, nseq, heads, dk, dv, steps, pool, seed, sample, check_steps,
+                beta=0.5, lam=0.01, eps=1e-6, per_ch=False):
+    inp = decode_inputs(nseq, heads, dk, dv, seed=seed, steps=pool, beta_per_channel=per_ch)
+    dt = torch.bfloat16
+    S = to_dev(torch, inp["S"], torch.float32)
+    kp = to_dev(torch, inp["k_prev"], dt)
+    qs = to_dev(torch, inp["q"], dt)
+    ks = to_dev(torch, inp["k"], dt)
+    vs = to_dev(torch, inp["v"], dt)
+    bs = to_dev(torch, inp["beta_t"], dt) if per_ch else None
+    flat = lambda a: a.reshape((-1,) + a.shape[2:])
+    S_ref = flat(inp["S"].astype(np.float64))[sample][:, None]
+    kp_ref = flat(inp["k_prev"].astype(np.float64))[sample][:, None]
+    worst = 0.0
+    for s in range(1, steps + 1):
+        p = (s - 1) % pool
+        o = fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=variant, beta=beta, lam=lam,
+                           eps=eps, beta_t=bs[p] if per_ch else None)
+        pick = lambda a: flat(a[p].astype(np.float64))[sample][:, None]
+        o_ref, S_ref, kp_ref = fo.falcon_decode_step(
+            variant, S_ref, kp_ref, pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), beta=beta,
+            lam=lam, eps=eps, beta_t=pick(inp["beta_t"]) if per_ch else None)
+        if s in check_steps:
+            torch.cuda.synchronize()
+            o_s = flat(o.cpu().numpy())[sample]
+            err, _ = token_normwise_err(o_s, o_ref[:, 0])
+            worst = max(worst, err)
+            print("decode v%d step %d: o err %.3e" % (variant, s, err))
+            assert err <= TOL_BF16
+    torch.cuda.synchronize()
+    serr = state_err(flat(S.cpu().numpy())[sample], S_ref[:, 0])
+    print("decode v%d after %d steps: S err %.3e" % (variant, steps, serr))
+    assert serr <= TOL_BF16
+    np.testing.assert_array_equal(flat(kp.cpu().float().numpy())[sample], kp_ref[:, 0])
+    return worst
+
+
+def test_decode_512x12x64_1000_steps():
+    cfg = WORKLOADS["decode_512x12x64"]
+    N, H, dk, dv = cfg["shape"]
+    sample = np.array([0, 1, 777, 3000, N * H - 1])
+    _decode_run(fw.FALCON_1, N, H, dk, dv, 1000, 8, cfg["seed"], sample, {1, 10, 100, 1000},
+                beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"])
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_2, fw.FALCON_1A, fw.FALCON_2A])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (16, 128), (128, 32)])
+def test_decode_small(variant, dk, dv):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    sample = np.arange(6)
+    _decode_run(variant, 3, 2, dk, dv, 20, 4, 500 + variant, sample, {1, 20}, per_ch=per_ch)
+
+
+# ---------------------------------------------------------------------------
+# error paths through the binding
+
+def test_binding_rejects_unsupported():
+    q = torch.zeros((1, 1, 16, 48), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(fw.FalconError) as ei:
+        fw.fwd_chunk(q, q, q, variant=fw.FALCON_1)
+    assert ei.value.status == 2

@@ -1,0 +1,134 @@
+// falcon_decode.hip - one decode step of the Falcon recurrence for serving
+// (explainer of arXiv 2608.27763, section 核心方法 §3: the recurrent form serves
+// inference; 163.com section 01: write first, then read with the updated state).
+//
+// Per (sequence, head), with x = k_prev and y = v:
+//   r1 = S x, r2 = S q                     (one read pass over S)
+//   e  = y - r1 (regression) or y (inner product)
+//   S' = a S + eta e x^T                   (one write pass, in place)
+//   o  = a r2 + eta e (x . q)              (= S' q, read-after-write)
+//   k_prev <- k
+// The step is bound by HBM: S is read once and written once, ~1 flop per byte.
+// One workgroup owns one (sequence, head), so the in-place k_prev update cannot
+// race with another workgroup.  Each row of S is read by DK/4 lanes with 16-byte
+// loads; every lane issues all of its row loads before the first reduction so
+// the memory system sees PASSES independent 16-byte requests per lane.
+#include "falcon_device.h"
+#include "falcon_launch.h"
+
+namespace falcon {
+namespace {
+
+constexpr int kDecThreads = 256;
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
+  constexpr int TPR = DK / 4;                    // lanes per row
+  constexpr int RPP = kDecThreads / TPR;         // rows per pass
+  constexpr int PASSES = (DV + RPP - 1) / RPP;
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* __restrict__ bt = static_cast<const T*>(a.beta_t);
+  T* __restrict__ kp = static_cast<T*>(a.k_prev);
+
+  const long head = blockIdx.x;                  // sequence * heads + head
+  const int rloc = threadIdx.x / TPR;
+  const int cg = threadIdx.x % TPR;
+  const int c0 = cg * 4;
+  float* __restrict__ Sh = a.S + head * (long)DV * DK;
+
+  // Issue the state loads first.
+  floatx4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    if (row < DV) s[p] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sh + (long)row * DK + c0));
+    else s[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  float x[4], qq[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = ld_in(kp, head * DK + c0 + e);
+    qq[e] = ld_in(q, head * DK + c0 + e);
+  }
+  float yv[PASSES], bv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    const int rc = row < DV ? row : 0;
+    yv[p] = ld_in(v, head * DV + rc);
+    bv[p] = a.beta_kind == 0 ? a.beta
+            : (a.beta_kind == 1 ? ld_in(bt, head) : ld_in(bt, head * DV + rc));
+  }
+  // Every lane has read its slice of k_prev; only now may it be overwritten.
+  __syncthreads();
+  if (rloc == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kp[head * DK + c0 + e] = k[head * DK + c0 + e];
+  }
+  float n = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  float xq = x[0] * qq[0] + x[1] * qq[1] + x[2] * qq[2] + x[3] * qq[3];
+  n = group_sum<TPR>(n);
+  xq = group_sum<TPR>(xq);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    float r1 = s[p].x * x[0] + s[p].y * x[1] + s[p].z * x[2] + s[p].w * x[3];
+    float r2 = s[p].x * qq[0] + s[p].y * qq[1] + s[p].z * qq[2] + s[p].w * qq[3];
+    r1 = group_sum<TPR>(r1);
+    r2 = group_sum<TPR>(r2);
+    const float eta = bv[p] / (a.eps + n);
+    const float dec = 1.0f - eta * a.lambda;
+    const float e = a.regression ? yv[p] - r1 : yv[p];
+    const float w = eta * e;
+    floatx4 sn;
+    sn.x = dec * s[p].x + w * x[0];
+    sn.y = dec * s[p].y + w * x[1];
+    sn.z = dec * s[p].z + w * x[2];
+    sn.w = dec * s[p].w + w * x[3];
+    if (row < DV) {
+      __builtin_nontemporal_store(sn, reinterpret_cast<floatx4*>(Sh + (long)row * DK + c0));
+      if (cg == 0) a.o[head * DV + row] = dec * r2 + w * xq;
+    }
+  }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch3(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)((long)a.nseq * a.heads)),
+                     dim3(kDecThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+hipError_t launch_dv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dv) {
+    case 16: return launch3<T, DK, 16>(a, stream);
+    case 32: return launch3<T, DK, 32>(a, stream);
+    case 64: return launch3<T, DK, 64>(a, stream);
+    case 128: return launch3<T, DK, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_dk(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dk) {
+    case 16: return launch_dv<T, 16>(a, stream);
+    case 32: return launch_dv<T, 32>(a, stream);
+    case 64: return launch_dv<T, 64>(a, stream);
+    case 128: return launch_dv<T, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (a.dtype == 0) return launch_dk<uint16_t>(a, stream);
+  return launch_dk<float>(a, stream);
+}
+
+}  // namespace falcon

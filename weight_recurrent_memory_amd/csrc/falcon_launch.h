@@ -1,0 +1,49 @@
+// falcon_launch.h - internal interface between the C-ABI layer (falcon_api.cpp)
+// and the kernel launchers.  Arguments are already validated when these run.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace falcon {
+
+// Arguments of one sequence call (recurrent or chunk form).
+struct SeqArgs {
+  int variant;       // falcon_variant
+  int window;        // B
+  int regression;    // 1: Falcon-1/2/3, 0: Falcon-1A/2A/3A
+  float beta;        // scalar gain (beta_kind == 0)
+  const void* beta_t;
+  int beta_kind;     // 0 scalar, 1 per token, 2 per token and value channel
+  float lambda, eps;
+  int batch, heads, seqlen, dk, dv;
+  int dtype;         // 0 bf16, 1 fp32
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_prev;  // may be null
+  const float* S0;     // may be null
+  float* o;
+  float* S_out;        // may be null
+  int chunk;           // chunk form only
+};
+
+struct DecodeArgs {
+  int regression;
+  float beta;
+  const void* beta_t;
+  int beta_kind;
+  float lambda, eps;
+  int nseq, heads, dk, dv;
+  int dtype;
+  float* S;
+  void* k_prev;
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+};
+
+hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
+hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace falcon

@@ -1,0 +1,142 @@
+// falcon_recurrent.hip - recurrent form of the Falcon update, one token at a time
+// (explainer of arXiv 2608.27763, section 核心方法 §3 "recurrent": O(d^2) per
+// step, the inference form).
+//
+// Work decomposition: one workgroup per (batch*head, block of value rows).  Rows
+// of S evolve independently given x_t (the update acts row-wise; Falcon-2's
+// per-channel eta touches only its own row), so rows split freely across
+// workgroups.  Inside a workgroup a row is owned by DK/4 consecutive lanes, each
+// holding 4 state columns in registers; dot products reduce over that lane
+// group with cross-lane shuffles.  Per step, for every window sample j:
+//   r_j = s_i . x_j (pre-update state), e_j = y_{j,i} - r_j (or y_{j,i} for the
+//   inner-product family); s_i <- a_i s_i + eta_i sum_j e_j x_j; o_{t,i} = s_i . q_t.
+#include "falcon_device.h"
+#include "falcon_launch.h"
+
+namespace falcon {
+namespace {
+
+constexpr int kRecThreads = 256;
+constexpr int kMaxWindow = 8;
+
+template <typename T, int DK>
+__global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int rows_per_block) {
+  constexpr int CPT = 4;          // state columns per lane
+  constexpr int TPR = DK / CPT;   // lanes per row (4..32, divides the wave)
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* __restrict__ kp = static_cast<const T*>(a.k_prev);
+  const T* __restrict__ bt = static_cast<const T*>(a.beta_t);
+
+  const int chain = blockIdx.x;               // batch * heads + head
+  const int rloc = threadIdx.x / TPR;
+  const int cg = threadIdx.x % TPR;
+  const int row = blockIdx.y * rows_per_block + rloc;
+  const bool active = rloc < rows_per_block && row < a.dv;
+  const int rowc = active ? row : 0;           // clamped index for loads
+  const long L = a.seqlen;
+  const long qk_base = (long)chain * L * DK;
+  const long v_base = (long)chain * L * a.dv;
+  const int c0 = cg * CPT;
+
+  float s[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e)
+    s[e] = (a.S0 && active) ? a.S0[((long)chain * a.dv + rowc) * DK + c0 + e] : 0.0f;
+
+  const int B = a.window;
+  for (long t = 0; t < L; ++t) {
+    // window samples j = t - w, w = 0..B-1: x_g = k[g-1] (g >= 1), k_prev or 0 (g == 0)
+    float xw[kMaxWindow][CPT];
+    float yw[kMaxWindow];
+    float n = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMaxWindow; ++w) {
+      const long g = t - w;
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        float xv = 0.0f;
+        if (w < B && g >= 1) xv = ld_in(k, qk_base + (g - 1) * DK + c0 + e);
+        else if (w < B && g == 0 && kp) xv = ld_in(kp, (long)chain * DK + c0 + e);
+        xw[w][e] = xv;
+        part += xv * xv;
+      }
+      n += part;
+      yw[w] = (w < B && g >= 0) ? ld_in(v, v_base + g * a.dv + rowc) : 0.0f;
+    }
+    n = group_sum<TPR>(n);
+    float beta = a.beta;
+    if (a.beta_kind == 1) beta = ld_in(bt, (long)chain * L + t);
+    else if (a.beta_kind == 2) beta = ld_in(bt, ((long)chain * L + t) * a.dv + rowc);
+    float eta = beta / (a.eps + n);
+    float decay = 1.0f - eta * a.lambda;
+    if (t == 0 && !kp) {  // fresh sequence: S_0 = 0 and x_1 = 0 leave S_1 = 0
+      eta = 0.0f;
+      decay = 1.0f;
+    }
+    float ew[kMaxWindow];
+#pragma unroll
+    for (int w = 0; w < kMaxWindow; ++w) {
+      if (w < B) {
+        float r = 0.0f;
+        if (a.regression) {
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) r += s[e] * xw[w][e];
+          r = group_sum<TPR>(r);
+        }
+        ew[w] = yw[w] - r;
+      } else {
+        ew[w] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kMaxWindow; ++w) acc += ew[w] * xw[w][e];
+      s[e] = decay * s[e] + eta * acc;
+    }
+    float ov = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) ov += s[e] * ld_in(q, qk_base + t * DK + c0 + e);
+    ov = group_sum<TPR>(ov);
+    if (active && cg == 0) a.o[v_base + t * a.dv + row] = ov;
+  }
+  if (a.S_out && active) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) a.S_out[((long)chain * a.dv + row) * DK + c0 + e] = s[e];
+  }
+}
+
+template <typename T, int DK>
+hipError_t launch_typed(const SeqArgs& a, hipStream_t stream) {
+  constexpr int TPR = DK / 4;
+  int rows = kRecThreads / TPR;
+  if (rows > a.dv) rows = a.dv;
+  dim3 grid(a.batch * a.heads, (a.dv + rows - 1) / rows);
+  hipLaunchKernelGGL((recurrent_kernel<T, DK>), grid, dim3(kRecThreads), 0, stream, a, rows);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dk(const SeqArgs& a, hipStream_t stream) {
+  switch (a.dk) {
+    case 16: return launch_typed<T, 16>(a, stream);
+    case 32: return launch_typed<T, 32>(a, stream);
+    case 64: return launch_typed<T, 64>(a, stream);
+    case 128: return launch_typed<T, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream) {
+  (void)hipGetLastError();
+  if (a.dtype == 0) return launch_dk<uint16_t>(a, stream);
+  return launch_dk<float>(a, stream);
+}
+
+}  // namespace falcon
