@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the Falcon chunk-parallel forward (and the decode step) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+
+A step is one falcon_fwd_chunk call (Falcon-1, the regression update with its
+triangular solve: staging, Gram/q.x products, solve, readout and state carry)
+over one batch of the headline workload: 8 sequences x 12 heads x 2048 tokens,
+dk = dv = 64, chunk 64, bf16 q/k/v (q, k L2-normalized), beta = 0.5,
+lambda = 0.01, eps = 1e-6.  Inputs are resident in HBM before the timed region;
+launch time is measured with HIP events on the stream the kernel runs on.
+
+Prints one JSON line.  Besides the contract fields it carries
+  roofline      the chunk kernel against HBM bandwidth (algorithmic bytes)
+  cpu_baseline  the fp64 oracle on the host cores, same workload
+  secondary     the other workloads: Falcon-1A, per-channel Falcon-2, windowed
+                Falcon-3/3A at d = 128, the decode step (state GB/s), a copy
+                kernel for attainable bandwidth, and model-FLOP utilization.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Falcon chunk fwd tokens/s + MFMA util; decode-step state HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic.json")
+CHUNK_SOURCE = os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", "falcon_chunk.hip")
+
+
+def algorithmic_bytes(batch, heads, L, dk, dv, beta_channel=False, elem=2):
+    """Each input read once, o (fp32) written once."""
+    per_tok = (2 * dk + dv) * elem + dv * 4 + (dv * elem if beta_channel else 0)
+    return batch * heads * L * per_tok
+
+
+def model_flops_per_head_token(regression, d, C, B=1):
+    """Canonical single-level chunk-form model flops per head-token (2 flops per
+    multiply-add; triangular products counted on their non-zero part; no
+    split-bf16 compensation passes).  Per chunk of C steps with nx = C + B - 1
+    keys and C*B window unknowns:
+      q.x          C(C+1)/2 + C(B-1) dot products of length d
+      S0 q         d^2 per token
+      readout P Z  same count as q.x, times d
+      carry Z^T X  nx d^2
+      regression only: Gram nx(nx-1)/2 dot products, S0 x  nx d^2,
+                       triangular solve (CB)(CB-1)/2 times d
+    Gives 40,960 (Falcon-1, d = C = 64), 24,704 (Falcon-1A) and 258,956 / 85,248
+    (Falcon-3 / 3A, d = 128, C = 64, B = 4)."""
+    nx = C + B - 1
+    tri_p = C * (C + 1) / 2 + C * (B - 1)
+    f = 2 * tri_p * d / C + 2 * d * d + 2 * tri_p * d / C + 2 * nx * d * d / C
+    if regression:
+        tri_g = nx * (nx - 1) / 2
+        tri_s = (C * B) * (C * B - 1) / 2
+        f += 2 * tri_g * d / C + 2 * nx * d * d / C + 2 * tri_s * d / C
+    return f
+
+
+def _source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per launch from rocprofv3 counters, if they were taken on the
+    current chunk kernel source (else None)."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != _source_hash(CHUNK_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="profiling aid: run only this leg "
+                    "(headline|falcon1a|percol|window|decode|copy)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Falcon state update has no cross-GPU "
+              "communication in this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import weight_recurrent_memory_amd as fw
+    from weight_recurrent_memory_amd.inputs import WORKLOADS, decode_inputs, seq_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fw.load_library()
+
+    def up(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dt)
+
+    def time_calls(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(steps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps    # seconds per call
+
+    def seq_leg(name, variant, steps, warmup, window=1):
+        cfg = WORKLOADS[name]
+        B, H, L, dk, dv = cfg["shape"]
+        per_ch = bool(cfg.get("beta_per_channel"))
+        inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16",
+                         beta_per_channel=per_ch)
+        q, k, v = (up(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+        bt = up(inp["beta_t"], torch.bfloat16) if per_ch else None
+        out = torch.empty((B, H, L, dv), device=dev, dtype=torch.float32)
+        beta = cfg["beta"] if cfg["beta"] is not None else 0.0
+        fn = lambda: fw.fwd_chunk(q, k, v, variant=variant, beta=beta, lam=cfg["lam"],
+                                  eps=cfg["eps"], chunk=cfg["chunk"], window=window,
+                                  beta_t=bt, out=out)
+        sec = time_calls(fn, steps, warmup)
+        nbytes = algorithmic_bytes(B, H, L, dk, dv, beta_channel=per_ch)
+        return dict(sec=sec, tokens=B * L, head_tokens=B * H * L, bytes=nbytes, d=dk,
+                    chunk=cfg["chunk"], inp=inp, cfg=cfg)
+
+    out = {}
+    # ---------------- headline: Falcon-1 chunk forward, 8 x 12 x 2048 x 64 ----------------
+    head_name = "chunk_8x12x2048x64"
+    if args.only in (None, "headline"):
+        h = seq_leg(head_name, fw.FALCON_1, args.steps, args.warmup)
+        sec = h["sec"]
+        value = h["tokens"] / sec
+        achieved = h["bytes"] / sec / 1e9
+        mflops = model_flops_per_head_token(True, 64, 64) * h["head_tokens"]
+        traffic = _traffic()
+        out.update({
+            "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": sec * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": head_name, "variant": "falcon1", "batch": 8, "heads": 12,
+                       "seq_len": 2048, "dk": 64, "dv": 64, "chunk": 64, "beta": 0.5,
+                       "lambda": 0.01, "eps": 1e-6, "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": traffic,
+                         "kernel": "chunk_kernel<64,64,true,false>",
+                         "algorithmic_bytes_per_launch": h["bytes"],
+                         "avg_launch_us": sec * 1e6},
+            "mfma_model_util": {"model_tflops": mflops / sec / 1e12,
+                                "frac_of_bf16_peak": mflops / sec / 1e12 / BF16_PEAK_TFLOPS},
+        })
+        head_inp = h["inp"]
+    else:
+        head_inp = None
+
+    # ---------------- secondary workloads ----------------
+    sec_out = {}
+    if not args.no_secondary:
+        legs = [("falcon1a", head_name, fw.FALCON_1A, 1),
+                ("percol", "chunk_percol_8x12x4096x64", fw.FALCON_2, 1),
+                ("window_falcon3", "chunk_window4_4x16x8192x128", fw.FALCON_3, 4),
+                ("window_falcon3a", "chunk_window4_4x16x8192x128", fw.FALCON_3A, 4)]
+        names = {fw.FALCON_1A: "falcon1a", fw.FALCON_2: "falcon2", fw.FALCON_3: "falcon3",
+                 fw.FALCON_3A: "falcon3a"}
+        for key, name, variant, win in legs:
+            if args.only not in (None, key.split("_")[0]):
+                continue
+            r = seq_leg(name, variant, 20, 3, window=win)
+            fl = model_flops_per_head_token(variant in (fw.FALCON_2, fw.FALCON_3), r["d"], r["chunk"], win) * r["head_tokens"]
+            sec_out[key] = {"workload": name, "variant": names[variant],
+                            "tokens_per_s": r["tokens"] / r["sec"], "ms_per_call": r["sec"] * 1e3,
+                            "hbm_gbs": r["bytes"] / r["sec"] / 1e9,
+                            "hbm_frac": r["bytes"] / r["sec"] / 1e9 / HBM_PEAK_GBS,
+                            "model_tflops": fl / r["sec"] / 1e12,
+                            "mfma_model_frac": fl / r["sec"] / 1e12 / BF16_PEAK_TFLOPS}
+            del r
+            torch.cuda.empty_cache()
+        if args.only in (None, "decode"):
+            cfg = WORKLOADS["decode_512x12x64"]
+            N, H, dk, dv = cfg["shape"]
+            pool = 8
+            d = decode_inputs(N, H, dk, dv, seed=cfg["seed"], steps=pool)
+            S = up(d["S"], torch.float32)
+            kp = up(d["k_prev"], torch.bfloat16)
+            qs, ks, vs = (up(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+            o = torch.empty((N, H, dv), device=dev, dtype=torch.float32)
+            it = [0]
+
+            def step():
+                p = it[0] % pool
+                it[0] += 1
+                fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=fw.FALCON_1, beta=cfg["beta"],
+                               lam=cfg["lam"], eps=cfg["eps"], out=o)
+            sec = time_calls(step, args.decode_steps, 20)
+            state_bytes = 2 * N * H * dv * dk * 4
+            io_bytes = N * H * (3 * dk * 2 + dv * 2 + dv * 4 + dk * 2)  # k_prev r/w, q, k, v, o
+            sec_out["decode"] = {"workload": "decode_512x12x64", "variant": "falcon1",
+                                 "steps": args.decode_steps, "us_per_step": sec * 1e6,
+                                 "state_gbs": state_bytes / sec / 1e9,
+                                 "total_gbs": (state_bytes + io_bytes) / sec / 1e9,
+                                 "hbm_frac": (state_bytes + io_bytes) / sec / 1e9 / HBM_PEAK_GBS,
+                                 "bytes_per_step": state_bytes + io_bytes}
+            del S, qs, ks, vs
+            torch.cuda.empty_cache()
+        if args.only in (None, "copy"):
+            # attainable bandwidth: device-to-device copy of 1 GiB (also the known-size
+            # kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)
+            a = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+            b = torch.empty_like(a)
+            sec = time_calls(lambda: b.copy_(a), 20, 3)
+            sec_out["copy_1GiB"] = {"gbs": 2 * a.numel() * 4 / sec / 1e9}
+            del a, b
+    if sec_out:
+        out["secondary"] = sec_out
+
+    # ---------------- fp64 oracle on the host cores ----------------
+    if not args.no_cpu_baseline and args.only is None and head_inp is not None:
+        from threadpoolctl import threadpool_info
+        from oracle import falcon_oracle as fo
+        cfg = WORKLOADS[head_name]
+        t = time.perf_counter()
+        fo.falcon_recurrence(fw.FALCON_1, head_inp["q"], head_inp["k"], head_inp["v"],
+                             beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"])
+        cpu_sec = time.perf_counter() - t
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": 8 * 2048 / cpu_sec, "unit": "tokens/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": "the whole headline batch (8 x 12 x 2048 tokens, "
+                                         "Falcon-1, fp64 numpy recurrence), %.1f s" % cpu_sec,
+                               "host_cpus": len(os.sched_getaffinity(0))}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
