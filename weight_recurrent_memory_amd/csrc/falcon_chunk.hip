@@ -6,7 +6,7 @@
 // 163.com article, section 02 (2) (only the fixed-size state passes between
 // chunks; the per-column variant is made GPU-computable with a Gram / WY
 // representation and a batched triangular solve).  The algebra below is
-// derived from the recurrence itself:
+// derived from the recurrence itself.
 //
 // Within a sub-chunk of c steps that starts from state S0 (per value row i;
 // t, s are local steps, w = 0..B-1 a window slot, u = t*B + w an unknown whose
@@ -20,106 +20,198 @@
 //   o_t = g_t (S0 q_t + sum_{s(u)<=t} (q_t . x_{j(u)}) z_u)
 //   S_c = g_{c-1} (S0 + sum_j F_j x_j^T),   F_j = sum_{u: j(u)=j} z_u
 //
-// Kernel structure: one workgroup (4 wave64) per (batch*head, block of 16 value
-// rows); rows of S evolve independently, so the d_v split needs no
-// communication, and the state block stays on chip (LDS, fp32) for the whole
-// sequence.  Per sub-chunk:
-//   stage    keys (shifted by one, with a halo of B-1 keys for the window), q,
-//            v (this block's columns), beta into LDS; keys also transposed
-//   MFMA     Gram G = X X^T and P = Q X^T (exact: bf16 inputs, fp32 accumulate)
-//   scalars  norms from diag(G), eta, a, prefix products g (wave scan)
-//   T        16x16 diagonal-block inverses (I + A_bb)^-1, forward substitution
-//   MFMA     S0 X^T, S0 Q^T (S0 split into bf16 hi + lo)
-//   solve    blocked forward substitution over 16-unknown blocks: off-diagonal
-//            coupling G Z on MFMA (both operands split), diagonal block by
-//            T_bb (scalar eta) or per-row substitution (per-channel eta)
-//   MFMA     readout O += Z^T P^T, scaled by g_t, stored as fp32
-//   MFMA     carry S = g_{c-1} (S0 + F^T X)
-// The sub-chunk size is the caller's chunk (window 1) or the largest power of
-// two with c*B <= 64, so every triangular system has at most 64 unknowns.
+// Work decomposition.  One workgroup of 8 wave64 owns one (batch*head) chain
+// and 32 value rows (two blocks of 16); rows of S evolve independently, so the
+// d_v split needs no communication, and the fp32 state stays in LDS for the
+// whole sequence.  The per-chain quantities (Gram, q.x, decay products,
+// triangular factors) are computed once per workgroup and shared by both row
+// blocks.  Per sub-chunk (phase = the work between two workgroup barriers):
+//   P0  commit the prefetched q/k/v/beta registers to LDS (keys also
+//       transposed, key norms by lane-group reductions), then issue the global
+//       loads of the next sub-chunk so HBM latency hides behind this one
+//   P1  MFMA: Gram X X^T and P = Q X^T (exact: bf16 inputs, fp32 accumulate),
+//       S0 Q^T; wave 0: eta, a, g (prefix-product wave scan), zeta
+//   P2  wave 0: 16x16 diagonal-block inverses T_bb = (I + A_bb)^-1 by forward
+//       substitution; other waves: S0 X^T and the right-hand sides
+//   P2' MFMA: M_bj = T_bb diag(g_{t-1}) G_bj for the off-diagonal blocks
+//   P3  blocked solve, one wave per row block: each 16-unknown stage is one
+//       MFMA group  E_b = [T_bb | -M_b0 | ... ] [R_b ; Z_0 ; ...]
+//       (per-channel eta: off-diagonal coupling on MFMA, diagonal block by
+//       per-row forward substitution)
+//   P4  MFMA: readout O^T = S0 Q^T + Z^T P^T scaled by g_t, stored fp32;
+//       carry S = g_{c-1} (S0 + F^T X)
+// Operands that are not exact bf16 inputs are stored in LDS pre-split into
+// bf16 hi + lo (split-bf16, Henry, Tang & Heinecke, ARITH 2019) so the MFMA
+// loops issue no conversion work: hi*hi + hi*lo + lo*hi with fp32 accumulation.
+// The sub-chunk length is the caller's chunk, halved until chunk * window <= 64
+// (at most 64 unknowns per triangular system) and to at most 32 for dk = 128
+// (LDS budget); the result does not depend on it beyond rounding.
 #include "falcon_device.h"
 #include "falcon_launch.h"
 
 namespace falcon {
 namespace {
 
-constexpr int kChunkThreads = 256;
-constexpr int RB = 16;      // value rows per workgroup
-constexpr int UP = 64;      // max unknowns per sub-chunk
+constexpr int RB = 16;    // value rows per row block (one MFMA tile)
+constexpr int NRB = 2;    // row blocks per workgroup
+constexpr int RW = RB * NRB;
+constexpr int NW = 8;     // waves per workgroup
+constexpr int NT = 64 * NW;
 
-__device__ __forceinline__ int round_up(int x, int m) { return (x + m - 1) / m * m; }
+struct HL {
+  bf16x8 hi, lo;
+};
 
-// One 16x16 output tile: acc[m][n] += sum_k A[m][k] * Bt[n][k], operands stored
-// K-contiguous (row stride lda / ldb elements).  K is a multiple of 8; lanes
-// whose 8-wide k slot lies beyond K supply zeros.
-//   ABF / BBF: operand is exact bf16 (uint16_t*), otherwise fp32 split hi/lo.
-template <bool ABF, bool BBF>
-__device__ __forceinline__ floatx4 tile_nt(floatx4 acc, const void* A, int lda, const void* Bt,
-                                           int ldb, int K) {
+__device__ __forceinline__ HL hl_zero() {
+  HL z;
+  z.hi = zero_frag();
+  z.lo = zero_frag();
+  return z;
+}
+__device__ __forceinline__ HL hl_pair(const uint16_t* hi, const uint16_t* lo) {
+  HL f;
+  f.hi = frag_bf16(hi);
+  f.lo = frag_bf16(lo);
+  return f;
+}
+__device__ __forceinline__ HL hl_bf16(const uint16_t* p) {
+  HL f;
+  f.hi = frag_bf16(p);
+  f.lo = zero_frag();
+  return f;
+}
+__device__ __forceinline__ HL hl_f32(const float* p) {
+  HL f;
+  frag_split(p, f.hi, f.lo);
+  return f;
+}
+// 8 fp32 values (in registers) -> split fragment
+__device__ __forceinline__ HL hl_vals(const float* v) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
+  }
+  uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  uint4 Lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  HL f;
+  f.hi = __builtin_bit_cast(bf16x8, H);
+  f.lo = __builtin_bit_cast(bf16x8, Lo);
+  return f;
+}
+
+__device__ __forceinline__ void split1(float x, uint16_t& h, uint16_t& l) {
+  const uint32_t hb = f32_to_bf16_bits(x);
+  h = (uint16_t)hb;
+  l = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hb << 16));
+}
+
+// 4 consecutive fp32 -> 4 hi and 4 lo bf16 stored with one 8-byte write each.
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float* v) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
+  }
+  *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// acc[m][n] += sum_{k<K} A[m][k] B[n][k] for one 16x16 tile; fa(r, k) / fb(r, k)
+// return the fragment of operand row r (0..15) at k (multiple of 8).  AX / BX:
+// the operand is an exact bf16 value (its lo part is zero; pass skipped).
+template <bool AX, bool BX, class FA, class FB>
+__device__ __forceinline__ floatx4 mma_nt(floatx4 acc, int K, FA&& fa, FB&& fb) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int kq = (lane >> 4) * 8;
   for (int k0 = 0; k0 < K; k0 += 32) {
-    const bool in = (k0 + kq) < K;
-    bf16x8 ah, al, bh, bl;
-    if (ABF) {
-      ah = in ? frag_bf16(static_cast<const uint16_t*>(A) + r * lda + k0 + kq) : zero_frag();
-      al = zero_frag();
-    } else if (in) {
-      frag_split(static_cast<const float*>(A) + r * lda + k0 + kq, ah, al);
-    } else {
-      ah = al = zero_frag();
-    }
-    if (BBF) {
-      bh = in ? frag_bf16(static_cast<const uint16_t*>(Bt) + r * ldb + k0 + kq) : zero_frag();
-      bl = zero_frag();
-    } else if (in) {
-      frag_split(static_cast<const float*>(Bt) + r * ldb + k0 + kq, bh, bl);
-    } else {
-      bh = bl = zero_frag();
-    }
-    acc = mfma16(ah, bh, acc);
-    if (!BBF) acc = mfma16(ah, bl, acc);
-    if (!ABF) acc = mfma16(al, bh, acc);
+    const int k = k0 + kq;
+    const HL A = k < K ? fa(r, k) : hl_zero();
+    const HL Bv = k < K ? fb(r, k) : hl_zero();
+    acc = mfma16(A.hi, Bv.hi, acc);
+    if (!BX) acc = mfma16(A.hi, Bv.lo, acc);
+    if (!AX) acc = mfma16(A.lo, Bv.hi, acc);
   }
   return acc;
 }
 
-struct Geom {
-  int nchain;     // batch * heads
-  int nrb;        // dv / RB
-  int remap;      // 1: XCD-aware block mapping
+template <int DK, int CS, int B>
+struct Cfg {
+  static constexpr int U = CS * B;                 // unknowns per sub-chunk
+  static constexpr int NB = U / 16;                // 16-unknown blocks
+  static constexpr int NX = CS + B - 1;            // keys per sub-chunk (window halo)
+  static constexpr int NXP = (NX + 15) / 16 * 16;
+  static constexpr int VPR = DK / 8;               // 16-byte vectors per key row
+  static constexpr int KV = (NXP * VPR + NT - 1) / NT;
+  static constexpr int QV = (CS * VPR + NT - 1) / NT;
+  static constexpr int YV = (NXP * (RW / 8) + NT - 1) / NT;
+  static_assert(U % 16 == 0 && U <= 64, "at most 64 unknowns, whole blocks");
 };
 
-template <int DK, int CS>
-struct Smem {
-  static constexpr int NXP = (CS == 64) ? 64 : CS + 16;   // padded key rows (max over windows)
-  static constexpr int GN = (CS == 64) ? 16 : NXP;        // gather-source Gram size
-  uint16_t X[NXP][DK + 8];          // keys x_j, row-major
-  uint16_t XT[DK][NXP + 8];         // keys transposed
-  uint16_t Q[CS][DK + 8];
-  float YT[RB][NXP + 4];            // values, this block's columns, transposed
-  float S[RB][DK + 4];              // state rows (fp32, carried)
-  float Gt[UP][UP + 4];             // masked Gram over unknowns (s(u') < t(u))
-  float Pt[CS][UP + 4];             // masked readout weights (s(u') <= t)
-  float G[GN][GN + 4];              // key Gram (window > 1)
-  float P[CS][GN + 4];              // q . x (window > 1)
-  float T[4][16][20];               // diagonal-block inverses
-  float XS[RB][NXP + 4];            // S0 x_j
-  float RT[RB][UP + 4];             // right-hand sides (transposed)
-  float ZT[RB][UP + 4];             // z (transposed)
-  float FT[RB][NXP + 4];            // per-key folded z (window > 1)
+template <int DK, int CS, int B, bool REG, bool PERROW>
+struct Lds {
+  using C = Cfg<DK, CS, B>;
+  static constexpr int U = C::U, NXP = C::NXP, NB = C::NB;
+  static constexpr int SR = PERROW ? RW : 1;       // rows of per-step scalars
+  struct Split {
+    uint16_t hi[RW][U + 8];
+    uint16_t lo[RW][U + 8];
+  };
+  union {                    // keys (P0..P2), then z pre-split (P3..P4)
+    uint16_t X[NXP][DK + 8];
+    Split ZT;
+  } ra;
+  union {                    // queries (P0..P1), then right-hand sides (P2..P3)
+    uint16_t Q[CS][DK + 8];
+    Split RT;
+  } rb;
+  uint16_t XT[DK][NXP + 8];          // keys transposed (carry operand)
+  float YT[RW][NXP + 4];             // values of this workgroup's rows, transposed
+  float S[RW][DK + 4];               // state rows, fp32
+  uint16_t Shi[RW][DK + 8];          // state rows, split
+  uint16_t Slo[RW][DK + 8];
+  float OT[RW][CS + 4];              // S0 q_t
+  uint16_t Phi[CS][U + 8];           // masked q.x over unknowns, split
+  uint16_t Plo[CS][U + 8];
+  float GT[REG ? U : 1][U + 4];      // masked Gram over unknowns (see use)
+  float G[B > 1 ? NXP : 1][NXP + 4]; // key Gram (window gather source)
+  float P[B > 1 ? CS : 1][NXP + 4];  // key q.x (window gather source)
+  float XS[(REG && B > 1) ? RW : 1][NXP + 4];
+  uint16_t SAhi[(REG && !PERROW) ? NB : 1][16][U + 8];  // [T_bb | -M_b0 | ...]
+  uint16_t SAlo[(REG && !PERROW) ? NB : 1][16][U + 8];
+  uint16_t FThi[B > 1 ? RW : 1][NXP + 8];               // folded z (window)
+  uint16_t FTlo[B > 1 ? RW : 1][NXP + 8];
+  float RP[PERROW && REG ? RW : 1][U + 4];              // per-row right-hand sides
   float nrm[NXP];
-  float beta[RB][CS];
-  float gam[RB][CS];
-  float gm1[RB][CS];
-  float zeta[RB][CS];
+  float beta[SR][CS];
+  float gam[SR][CS];
+  float gm1[SR][CS];
+  float zeta[SR][CS];
 };
 
-template <int DK, int CS, bool REG, bool PERROW>
-__global__ __launch_bounds__(kChunkThreads) void chunk_kernel(SeqArgs a, Geom geo) {
-  using SM = Smem<DK, CS>;
-  constexpr int NXP = SM::NXP;
+struct Geom {
+  int nchain;
+  int nrbg;    // row-block groups per chain (ceil(dv / RW))
+  int remap;   // XCD-aware block mapping
+};
+
+template <int DK, int CS, int B, bool REG, bool PERROW>
+__global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
+  using C = Cfg<DK, CS, B>;
+  using SM = Lds<DK, CS, B, REG, PERROW>;
+  constexpr int U = C::U, NB = C::NB, NX = C::NX, NXP = C::NXP, VPR = C::VPR;
+  constexpr int KV = C::KV, QV = C::QV, YV = C::YV;
+  constexpr int NTT = CS / 16;     // step tiles
+  static_assert(!(PERROW && B > 1), "per-channel variants have window 1");
   __shared__ __align__(16) SM sm;
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
@@ -128,177 +220,167 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(SeqArgs a, Geom ge
   const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
   const uint16_t* __restrict__ bg = static_cast<const uint16_t*>(a.beta_t);
 
-  // Block -> (chain, row block).  Workgroups are dealt to the 8 XCDs round
-  // robin; with remap, the row blocks of one chain land on one XCD (same L2)
-  // and are dispatched back to back, so they share the q/k tiles they all read.
-  int chain, rb;
+  // Block -> (chain, row-block group).  Workgroups are dealt to the 8 XCDs round
+  // robin; with remap, the groups of one chain land on one XCD (same L2) and are
+  // dispatched back to back, so they share the q/k tiles they all read.
+  int chain, rbg;
   {
     const int b = blockIdx.x;
     if (geo.remap) {
       const int xcd = b & 7, slot = b >> 3;
-      chain = xcd + 8 * (slot / geo.nrb);
-      rb = slot % geo.nrb;
+      chain = xcd + 8 * (slot / geo.nrbg);
+      rbg = slot % geo.nrbg;
     } else {
-      chain = b / geo.nrb;
-      rb = b % geo.nrb;
+      chain = b / geo.nrbg;
+      rbg = b % geo.nrbg;
     }
   }
-  const int i0 = rb * RB;
+  const int dv = a.dv;
+  const int i0 = rbg * RW;
+  const int nrb = (dv - i0) >= RW ? NRB : 1;       // active row blocks (dv = 16: one)
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int B = a.window;
+  const int lr = lane & 15;          // tile column / fragment row
+  const int lg = lane >> 4;          // lane group
   const long L = a.seqlen;
-  const int dv = a.dv;
-  const int cs = CS;                   // sub-chunk length (window fits: cs * B <= 64)
-  const int U = cs * B;                // unknowns per sub-chunk
-  const int NX = cs + B - 1;           // keys per sub-chunk (with halo)
-  const int nxp = round_up(NX, 16);
-  const int nb = U / 16;               // diagonal blocks
   const long qk_base = (long)chain * L * DK;
   const long v_base = (long)chain * L * dv;
 
-  // state rows
-  for (int idx = tid; idx < RB * DK; idx += kChunkThreads) {
-    const int i = idx / DK, kk = idx % DK;
-    sm.S[i][kk] = a.S0 ? a.S0[((long)chain * dv + i0 + i) * DK + kk] : 0.0f;
-  }
-
-  for (long t0 = 0; t0 < L; t0 += CS) {
-    const int c = (int)((L - t0) < CS ? (L - t0) : CS);   // valid steps (ragged tail)
-    __syncthreads();
-    // ---------------- stage ----------------
-    constexpr int VPR = DK / 8;   // 16-byte vectors per key row
-    for (int idx = tid; idx < NXP * VPR; idx += kChunkThreads) {
+  // ---------------- prefetch registers ----------------
+  uint4 pk[KV], pq[QV], py[YV];
+  float pb[(PERROW ? RW : 1) * CS / NT + 1];
+  auto prefetch = [&](long t0) {
+    const int c = (int)((L - t0) < CS ? (L - t0) : CS);
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int idx = tid + v * NT;
       const int jj = idx / VPR, kv = idx % VPR;
       const long g = t0 - (B - 1) + jj;            // global step of key x_g
       uint4 val = {0u, 0u, 0u, 0u};
-      if (jj < NX && g < t0 + c) {
+      if (idx < NXP * VPR && jj < NX && g < t0 + c) {
         if (g >= 1) val = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
         else if (g == 0 && kpg) val = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
       }
-      *reinterpret_cast<uint4*>(&sm.X[jj][kv * 8]) = val;
-      const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.XT[kv * 8 + 2 * e][jj] = (uint16_t)(w4[e] & 0xFFFFu);
-        sm.XT[kv * 8 + 2 * e + 1][jj] = (uint16_t)(w4[e] >> 16);
-      }
+      pk[v] = val;
     }
-    for (int idx = tid; idx < CS * VPR; idx += kChunkThreads) {
+#pragma unroll
+    for (int v = 0; v < QV; ++v) {
+      const int idx = tid + v * NT;
       const int t = idx / VPR, kv = idx % VPR;
       uint4 val = {0u, 0u, 0u, 0u};
-      if (t < c) val = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
-      *reinterpret_cast<uint4*>(&sm.Q[t][kv * 8]) = val;
+      if (idx < CS * VPR && t < c) val = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
+      pq[v] = val;
     }
-    for (int idx = tid; idx < NXP * (RB / 8); idx += kChunkThreads) {
-      const int jj = idx / (RB / 8), h = idx % (RB / 8);
+#pragma unroll
+    for (int v = 0; v < YV; ++v) {
+      const int idx = tid + v * NT;
+      const int jj = idx / (RW / 8), h = idx % (RW / 8);
       const long g = t0 - (B - 1) + jj;
       uint4 val = {0u, 0u, 0u, 0u};
-      if (jj < NX && g >= 0 && g < t0 + c)
+      if (idx < NXP * (RW / 8) && jj < NX && g >= 0 && g < t0 + c && i0 + h * 8 < dv)
         val = *reinterpret_cast<const uint4*>(vg + v_base + g * dv + i0 + h * 8);
+      py[v] = val;
+    }
+    constexpr int NBT = (PERROW ? RW : 1) * CS;
+#pragma unroll
+    for (int v = 0; v < NBT / NT + 1; ++v) {
+      const int idx = tid + v * NT;
+      float bv = a.beta;
+      if (idx < NBT) {
+        const int i = idx / CS, t = idx % CS;
+        if (t < c) {
+          if (a.beta_kind == 1) bv = bf16_to_f32(bg[(long)chain * L + t0 + t]);
+          else if (a.beta_kind == 2 && i0 + i < dv)
+            bv = bf16_to_f32(bg[((long)chain * L + t0 + t) * dv + i0 + i]);
+        }
+      }
+      pb[v] = bv;
+    }
+  };
+
+  // ---------------- state ----------------
+  for (int idx = tid; idx < RW * DK; idx += NT) {
+    const int i = idx / DK, kk = idx % DK;
+    float s = 0.0f;
+    if (a.S0 && i0 + i < dv) s = a.S0[((long)chain * dv + i0 + i) * DK + kk];
+    sm.S[i][kk] = s;
+    split1(s, sm.Shi[i][kk], sm.Slo[i][kk]);
+  }
+  prefetch(0);
+
+  for (long t0 = 0; t0 < L; t0 += CS) {
+    const int c = (int)((L - t0) < CS ? (L - t0) : CS);     // valid steps (ragged tail)
+    __syncthreads();
+    // ================= P0: commit prefetched tiles =================
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int idx = tid + v * NT;
+      const int jj = idx / VPR, kv = idx % VPR;
+      const uint4 val = pk[v];
       const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+      float part = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.YT[h * 8 + 2 * e][jj] = bf16_to_f32((uint16_t)(w4[e] & 0xFFFFu));
-        sm.YT[h * 8 + 2 * e + 1][jj] = bf16_to_f32((uint16_t)(w4[e] >> 16));
+        const float lo = bf16_to_f32((uint16_t)(w4[e] & 0xFFFFu));
+        const float hi = bf16_to_f32((uint16_t)(w4[e] >> 16));
+        part += lo * lo + hi * hi;
       }
-    }
-    for (int idx = tid; idx < (PERROW ? RB : 1) * CS; idx += kChunkThreads) {
-      const int i = idx / CS, t = idx % CS;
-      float bv = a.beta;
-      if (t < c) {
-        if (a.beta_kind == 1) bv = bf16_to_f32(bg[(long)chain * L + t0 + t]);
-        else if (a.beta_kind == 2) bv = bf16_to_f32(bg[((long)chain * L + t0 + t) * dv + i0 + i]);
-      }
-      sm.beta[i][t] = bv;
-    }
-    __syncthreads();
-
-    // ---------------- Gram and q.x products (exact, MFMA) ----------------
-    if (B == 1) {
-      // keys and unknowns coincide: write the masked forms directly
-      constexpr int NT = CS / 16;
-      for (int task = wave; task < 2 * NT * NT; task += 4) {
-        const bool isG = task < NT * NT;
-        const int tt = isG ? task : task - NT * NT;
-        const int ti = tt / NT, tj = tt % NT;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (tj <= ti) {
-          const uint16_t* Ap = isG ? &sm.X[16 * ti][0] : &sm.Q[16 * ti][0];
-          acc = tile_nt<true, true>(acc, Ap, DK + 8, &sm.X[16 * tj][0], DK + 8, DK);
-        }
-        const int col = 16 * tj + (lane & 15);
+      part = group_sum<VPR>(part);
+      if (idx < NXP * VPR) {
+        *reinterpret_cast<uint4*>(&sm.ra.X[jj][kv * 8]) = val;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * ti + 4 * (lane >> 4) + r;
-          if (isG) {
-            sm.Gt[row][col] = (col < row) ? acc[r] : 0.0f;
-            if (col == row) sm.nrm[row] = acc[r];
-          } else {
-            sm.Pt[row][col] = (col <= row) ? acc[r] : 0.0f;
-          }
+        for (int e = 0; e < 4; ++e) {
+          sm.XT[kv * 8 + 2 * e][jj] = (uint16_t)(w4[e] & 0xFFFFu);
+          sm.XT[kv * 8 + 2 * e + 1][jj] = (uint16_t)(w4[e] >> 16);
         }
+        if (kv == 0) sm.nrm[jj] = part;
       }
-      // unknowns beyond CS (CS < 64): zero rows/cols so K-padding reads zeros
-      for (int idx = tid; idx < UP * UP; idx += kChunkThreads) {
-        const int r = idx / UP, cc = idx % UP;
-        if (r >= CS || cc >= CS) {
-          if (REG) sm.Gt[r][cc] = 0.0f;
-          if (r < CS) sm.Pt[r][cc] = 0.0f;
-        }
-      }
-    } else {
-      const int nt = nxp / 16;
-      constexpr int NQ = CS / 16;
-      for (int task = wave; task < nt * nt + NQ * nt; task += 4) {
-        const bool isG = task < nt * nt;
-        const int tt = isG ? task : task - nt * nt;
-        const int ti = tt / nt, tj = tt % nt;
-        const uint16_t* Ap = isG ? &sm.X[16 * ti][0] : &sm.Q[16 * ti][0];
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_nt<true, true>(acc, Ap, DK + 8, &sm.X[16 * tj][0], DK + 8, DK);
-        const int col = 16 * tj + (lane & 15);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * ti + 4 * (lane >> 4) + r;
-          if (isG) sm.G[row][col] = acc[r];
-          else sm.P[row][col] = acc[r];
-        }
-      }
-      __syncthreads();
-      for (int jj = tid; jj < nxp; jj += kChunkThreads) sm.nrm[jj] = sm.G[jj][jj];
-      // gather over unknowns u = t*B + w with key j(u) = t - w + B - 1
-      for (int idx = tid; idx < UP * UP; idx += kChunkThreads) {
-        const int u = idx / UP, u2 = idx % UP;
-        const int t = u / B, s = u2 / B;
-        if (REG) {
-          float gv = 0.0f;
-          if (u < U && u2 < U && s < t) gv = sm.G[t - u % B + B - 1][s - u2 % B + B - 1];
-          sm.Gt[u][u2] = gv;
-        }
-        if (u < CS) {
-          float pv = 0.0f;
-          if (u2 < U && s <= u) pv = sm.P[u][s - u2 % B + B - 1];
-          sm.Pt[u][u2] = pv;
+    for (int v = 0; v < QV; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < CS * VPR) *reinterpret_cast<uint4*>(&sm.rb.Q[idx / VPR][(idx % VPR) * 8]) = pq[v];
+    }
+#pragma unroll
+    for (int v = 0; v < YV; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < NXP * (RW / 8)) {
+        const int jj = idx / (RW / 8), h = idx % (RW / 8);
+        const uint4 val = py[v];
+        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.YT[h * 8 + 2 * e][jj] = bf16_to_f32((uint16_t)(w4[e] & 0xFFFFu));
+          sm.YT[h * 8 + 2 * e + 1][jj] = bf16_to_f32((uint16_t)(w4[e] >> 16));
         }
       }
     }
-    __syncthreads();
-
-    // ---------------- per-step scalars ----------------
-    // eta_t = beta_t / (eps + n_t), a_t = 1 - eta_t lambda; padded steps and
-    // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
     {
+      constexpr int NBT = (PERROW ? RW : 1) * CS;
+#pragma unroll
+      for (int v = 0; v < NBT / NT + 1; ++v) {
+        const int idx = tid + v * NT;
+        if (idx < NBT) sm.beta[idx / CS][idx % CS] = pb[v];
+      }
+    }
+    if (t0 + CS < L) prefetch(t0 + CS);
+    __syncthreads();
+
+    // ================= P1: Gram, q.x, S0 q; scalars =================
+    if (wave == 0 || (PERROW && wave < 4)) {
+      // eta_t = beta_t / (eps + n_t), a_t = 1 - eta_t lambda; padded steps and the
+      // fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
       const int t = lane;
       float n = 0.0f;
-      for (int w = 0; w < B; ++w) {
-        const int jj = t - w + B - 1;
-        if (t < CS) n += sm.nrm[jj];
+      if (t < CS) {
+#pragma unroll
+        for (int w = 0; w < B; ++w) n += sm.nrm[t - w + B - 1];
       }
       const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
-      constexpr int NR = PERROW ? RB : 1;
-      for (int i = wave; i < NR; i += 4) {
+      constexpr int NR = PERROW ? RW : 1;
+      constexpr int WST = PERROW ? 4 : 1;
+      for (int i = wave; i < NR; i += WST) {
         float eta = 0.0f, dec = 1.0f;
         if (live) {
           eta = sm.beta[i][t] / (a.eps + n);
@@ -319,223 +401,372 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_kernel(SeqArgs a, Geom ge
         }
       }
     }
-    __syncthreads();
-
-    // ---------------- diagonal-block inverses (scalar eta, regression) ----------------
-    if (REG && !PERROW) {
-      for (int bb = wave; bb < nb; bb += 4) {
-        if (lane < 16) {
-          const int cc = lane;
-          float tc[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ur = 16 * bb + r;
-            const float gr = sm.gm1[0][ur / B];
-            float acc = (r == cc) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int m = 0; m < r; ++m) {
-              const int um = 16 * bb + m;
-              acc -= gr * sm.Gt[ur][um] * sm.zeta[0][um / B] * tc[m];
-            }
-            tc[r] = acc;
+    {
+      // task list: [Gram tiles][q.x tiles][S0 q tiles]
+      constexpr int GN = B == 1 ? NTT : NXP / 16;      // Gram tile grid
+      constexpr int NG = REG ? (B == 1 ? NTT * (NTT + 1) / 2 : GN * GN) : 0;
+      constexpr int NP = B == 1 ? NTT * (NTT + 1) / 2 : NTT * (NXP / 16);
+      constexpr int NQ = NRB * NTT;
+      const int first = PERROW ? 4 : 1;      // waves busy with scalars start later
+      for (int task = (wave + NW - first) % NW; task < NG + NP + NQ; task += NW) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (task < NG + NP) {
+          const bool isG = task < NG;
+          int ti, tj, tt = isG ? task : task - NG;
+          if (B == 1) {     // lower-triangular tile enumeration
+            ti = 0;
+            while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
+            tj = tt - ti * (ti + 1) / 2;
+          } else {
+            const int gn = isG ? GN : NXP / 16;
+            ti = tt / gn;
+            tj = tt % gn;
           }
+          const uint16_t* Arow = isG ? &sm.ra.X[16 * ti][0] : &sm.rb.Q[16 * ti][0];
+          acc = mma_nt<true, true>(acc, DK,
+              [&](int r, int k) { return hl_bf16(Arow + r * (DK + 8) + k); },
+              [&](int r, int k) { return hl_bf16(&sm.ra.X[16 * tj + r][k]); });
+          const int col = 16 * tj + lr;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sm.T[bb][r][cc] = tc[r];
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * ti + 4 * lg + e;
+            if (B == 1) {
+              if (isG) {
+                const float gv = (col < row) ? acc[e] : 0.0f;
+                if (PERROW) sm.GT[row][col] = gv;       // Gt[u][u']
+                else sm.GT[col][row] = gv;              // Gt^T[u'][u]
+              } else {
+                split1((col <= row) ? acc[e] : 0.0f, sm.Phi[row][col], sm.Plo[row][col]);
+              }
+            } else {
+              if (isG) sm.G[row][col] = acc[e];
+              else sm.P[row][col] = acc[e];
+            }
+          }
+        } else {
+          const int qt = task - NG - NP;
+          const int rbk = qt / NTT, tt = qt % NTT;
+          if (rbk < nrb) {
+            acc = mma_nt<false, true>(acc, DK,
+                [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); },
+                [&](int r, int k) { return hl_bf16(&sm.rb.Q[16 * tt + r][k]); });
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.OT[16 * rbk + 4 * lg + e][16 * tt + lr] = acc[e];
+          }
         }
       }
     }
+    __syncthreads();
 
-    // ---------------- S0 products ----------------
-    floatx4 oacc = {0.f, 0.f, 0.f, 0.f};
-    const int ntq = CS / 16;
-    if (wave < ntq)
-      oacc = tile_nt<false, true>(oacc, &sm.S[0][0], DK + 4, &sm.Q[16 * wave][0], DK + 8, DK);
+    if (B > 1) {
+      // gather over unknowns u = t*B + w (key j(u) = t - w + B - 1)
+      for (int idx = tid; idx < (REG ? U * U : 0) + CS * U; idx += NT) {
+        if (REG && idx < U * U) {
+          const int u = idx / U, u2 = idx % U;
+          const int t = u / B, s = u2 / B;
+          const float gv = (s < t) ? sm.G[t - u % B + B - 1][s - u2 % B + B - 1] : 0.0f;
+          sm.GT[u2][u] = gv;                           // Gt^T (scalar eta only)
+        } else {
+          const int j = idx - (REG ? U * U : 0);
+          const int t = j / U, u2 = j % U, s = u2 / B;
+          const float pv = (s <= t) ? sm.P[t][s - u2 % B + B - 1] : 0.0f;
+          split1(pv, sm.Phi[t][u2], sm.Plo[t][u2]);
+        }
+      }
+      __syncthreads();
+    }
+
+    // ================= P2: diagonal inverses || S0 x and right-hand sides =================
     if (REG) {
-      for (int tj = wave; tj < nxp / 16; tj += 4) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_nt<false, true>(acc, &sm.S[0][0], DK + 4, &sm.X[16 * tj][0], DK + 8, DK);
-        const int col = 16 * tj + (lane & 15);
+      if (!PERROW && wave == NW - 1) {
+        // T_bb = (I + Gamma_- Gs Z)^-1 = Gamma_- (I + Gs D)^-1 Gamma_-^{-1},
+        // D = diag(zeta_m g_{t(m)-1}); lane = 16 b + column.
+        const int bb = lane >> 4, cc = lane & 15;
+        if (bb < NB) {
+          const int u0 = 16 * bb;
+          float acc[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.XS[4 * (lane >> 4) + r][col] = acc[r];
+          for (int r = 0; r < 16; ++r) acc[r] = (r == cc) ? 1.0f : 0.0f;
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int tm = (u0 + m) / B;
+            const float sv = sm.zeta[0][tm] * sm.gm1[0][tm] * acc[m];
+            const float* grow = &sm.GT[u0 + m][u0];     // Gt^T[u_m][u_r] = Gs[r][m]
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) acc[r] -= grow[r] * sv;
+          }
+          const float inv_c = 1.0f / sm.gm1[0][(u0 + cc) / B];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float tv = sm.gm1[0][(u0 + r) / B] * acc[r] * inv_c;
+            split1(tv, sm.SAhi[bb][r][cc], sm.SAlo[bb][r][cc]);
+          }
+        }
       }
-    }
-    __syncthreads();
-
-    // ---------------- right-hand sides / inner-product z ----------------
-    for (int idx = tid; idx < RB * UP; idx += kChunkThreads) {
-      const int i = idx / UP, u = idx % UP;
-      const int ir = PERROW ? i : 0;
-      float val = 0.0f;
-      if (u < U) {
+      // S0 x_j tiles (row block, key tile) -> right-hand sides; with scalar eta
+      // the last wave is busy with the diagonal inverses
+      constexpr int NXT = NXP / 16;
+      constexpr int NWS = PERROW ? NW : NW - 1;
+      for (int task = wave; wave < NWS && task < NRB * NXT; task += NWS) {
+        const int rbk = task / NXT, tj = task % NXT;
+        if (rbk >= nrb) continue;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_nt<false, true>(acc, DK,
+            [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); },
+            [&](int r, int k) { return hl_bf16(&sm.ra.X[16 * tj + r][k]); });
+        const int jj = 16 * tj + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * rbk + 4 * lg + e;
+          if (B == 1) {
+            const float rv = (jj < CS) ? sm.YT[i][jj] - sm.gm1[PERROW ? i : 0][jj] * acc[e] : 0.0f;
+            if (PERROW) sm.RP[i][jj] = rv;
+            else split1(rv, sm.rb.RT.hi[i][jj], sm.rb.RT.lo[i][jj]);
+          } else {
+            sm.XS[i][jj] = acc[e];
+          }
+        }
+      }
+    } else {
+      // inner-product family: z_u = zeta_t y_{j(u)}
+      for (int idx = tid; idx < RW * U; idx += NT) {
+        const int i = idx / U, u = idx % U;
         const int t = u / B, jj = t - u % B + B - 1;
-        if (REG) val = sm.YT[i][jj] - sm.gm1[ir][t] * sm.XS[i][jj];
-        else val = sm.zeta[ir][t] * sm.YT[i][jj];
+        const float zv = sm.zeta[PERROW ? i : 0][t] * sm.YT[i][jj];
+        split1(zv, sm.ra.ZT.hi[i][u], sm.ra.ZT.lo[i][u]);
       }
-      if (REG) sm.RT[i][u] = val;
-      else sm.ZT[i][u] = val;
     }
     __syncthreads();
 
-    // ---------------- blocked forward substitution (regression) ----------------
-    if (REG) {
-      for (int bb = 0; bb < nb; ++bb) {
-        if (wave == 0) {
+    // ================= P2': off-diagonal solve blocks, window right-hand sides =================
+    if (REG && !PERROW) {
+      // M_bj = T_bb diag(g_{t-1})_b Gs_bj, stored negated next to T_bb
+      constexpr int NM = NB * (NB - 1) / 2;
+      for (int task = wave; task < NM; task += NW) {
+        int bb = 1;
+        while (bb * (bb + 1) / 2 <= task) ++bb;
+        const int jb = task - bb * (bb - 1) / 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_nt<false, false>(acc, 16,
+            [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
+            [&](int r, int k) {
+              float v[8];
+              const float* gp = &sm.GT[16 * jb + r][16 * bb + k];   // Gs[u_m][u'] = Gt^T[u'][u_m]
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = gp[e] * sm.gm1[0][(16 * bb + k + e) / B];
+              return hl_vals(v);
+            });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * lg + e;
+          split1(-acc[e], sm.SAhi[bb][r][16 * (jb + 1) + lr], sm.SAlo[bb][r][16 * (jb + 1) + lr]);
+        }
+      }
+    }
+    if (REG && B > 1) {
+      for (int idx = tid; idx < RW * U; idx += NT) {
+        const int i = idx / U, u = idx % U;
+        const int t = u / B, jj = t - u % B + B - 1;
+        const float rv = sm.YT[i][jj] - sm.gm1[0][t] * sm.XS[i][jj];
+        split1(rv, sm.rb.RT.hi[i][u], sm.rb.RT.lo[i][u]);
+      }
+    }
+    if (REG) __syncthreads();
+
+    // ================= P3: blocked solve, one wave per row block =================
+    if (REG && wave < nrb) {
+      const int rbk = wave;
+      const int ib = 16 * rbk;
+      if (!PERROW) {
+        for (int bb = 0; bb < NB; ++bb) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma_nt<false, false>(acc, 16 * (bb + 1),
+              [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
+              [&](int r, int k) {
+                if (k < 16) return hl_pair(&sm.rb.RT.hi[ib + r][16 * bb + k], &sm.rb.RT.lo[ib + r][16 * bb + k]);
+                return hl_pair(&sm.ra.ZT.hi[ib + r][k - 16], &sm.ra.ZT.lo[ib + r][k - 16]);
+              });
+          // E_b[u][i]: lane holds u = 16 bb + 4 lg + e, i = lr
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = sm.zeta[0][(16 * bb + 4 * lg + e) / B] * acc[e];
+          store_split4(&sm.ra.ZT.hi[ib + lr][16 * bb + 4 * lg], &sm.ra.ZT.lo[ib + lr][16 * bb + 4 * lg], z);
+          wave_sync();
+        }
+      } else {
+        for (int bb = 0; bb < NB; ++bb) {
           const int u0 = 16 * bb;
           if (bb > 0) {
             floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-            cacc = tile_nt<false, false>(cacc, &sm.Gt[u0][0], UP + 4, &sm.ZT[0][0], UP + 4, u0);
-            const int i = lane & 15;
-            const int ir = PERROW ? i : 0;
-            float4 rv = *reinterpret_cast<float4*>(&sm.RT[i][u0 + 4 * (lane >> 4)]);
-            float rr[4] = {rv.x, rv.y, rv.z, rv.w};
+            cacc = mma_nt<false, false>(cacc, u0,
+                [&](int r, int k) { return hl_f32(&sm.GT[u0 + r][k]); },
+                [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int u = u0 + 4 * (lane >> 4) + r;
-              rr[r] -= sm.gm1[ir][u / B] * cacc[r];
+            for (int e = 0; e < 4; ++e) {
+              const int u = u0 + 4 * lg + e;
+              sm.RP[ib + lr][u] -= sm.gm1[ib + lr][u] * cacc[e];
             }
-            *reinterpret_cast<float4*>(&sm.RT[i][u0 + 4 * (lane >> 4)]) =
-                make_float4(rr[0], rr[1], rr[2], rr[3]);
+            wave_sync();
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          if (!PERROW) {
-            floatx4 eacc = {0.f, 0.f, 0.f, 0.f};
-            eacc = tile_nt<false, false>(eacc, &sm.T[bb][0][0], 20, &sm.RT[0][u0], UP + 4, 16);
-            const int i = lane & 15;
-            float zz[4];
+          if (lane < 16) {
+            const int i = ib + lane;
+            float acc[16], z[16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int u = u0 + 4 * (lane >> 4) + r;
-              zz[r] = sm.zeta[0][u / B] * eacc[r];
-            }
-            *reinterpret_cast<float4*>(&sm.ZT[i][u0 + 4 * (lane >> 4)]) =
-                make_float4(zz[0], zz[1], zz[2], zz[3]);
-          } else if (lane < RB) {
-            const int i = lane;
-            float z[16];
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int u = u0 + r;
-              float acc = 0.0f;
+            for (int m = 0; m < 16; ++m) {
+              const int u = u0 + m;
+              const float e = sm.RP[i][u] - sm.gm1[i][u] * acc[m];
+              z[m] = sm.zeta[i][u] * e;
 #pragma unroll
-              for (int m = 0; m < r; ++m) acc += sm.Gt[u][u0 + m] * z[m];
-              const float e = sm.RT[i][u] - sm.gm1[i][u / B] * acc;
-              z[r] = sm.zeta[i][u / B] * e;
+              for (int r = m + 1; r < 16; ++r) acc[r] += sm.GT[u0 + r][u] * z[m];
             }
 #pragma unroll
             for (int r = 0; r < 16; r += 4)
-              *reinterpret_cast<float4*>(&sm.ZT[i][u0 + r]) = make_float4(z[r], z[r + 1], z[r + 2], z[r + 3]);
+              store_split4(&sm.ra.ZT.hi[i][u0 + r], &sm.ra.ZT.lo[i][u0 + r], &z[r]);
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          wave_sync();
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
 
-    // ---------------- readout ----------------
-    if (wave < ntq) {
-      oacc = tile_nt<false, false>(oacc, &sm.ZT[0][0], UP + 4, &sm.Pt[16 * wave][0], UP + 4,
-                                   round_up(U, 16));
-      const int t = 16 * wave + (lane & 15);
-      const int ib = 4 * (lane >> 4);
-      if (t < c) {
-        float ov[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[r] = sm.gam[PERROW ? ib + r : 0][t] * oacc[r];
-        *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + ib) =
-            make_float4(ov[0], ov[1], ov[2], ov[3]);
-      }
-    }
-    // fold z onto keys for the window (j(u) = t - w + B - 1)
+    // ================= P4: fold (window), readout, carry =================
     if (B > 1) {
-      for (int idx = tid; idx < RB * NXP; idx += kChunkThreads) {
+      for (int idx = tid; idx < RW * NXP; idx += NT) {
         const int i = idx / NXP, jj = idx % NXP;
         float f = 0.0f;
+#pragma unroll
         for (int w = 0; w < B; ++w) {
           const int t = jj + w - (B - 1);
-          if (t >= 0 && t < CS) f += sm.ZT[i][t * B + w];
+          if (t >= 0 && t < CS) {
+            const int u = t * B + w;
+            f += bf16_to_f32(sm.ra.ZT.hi[i][u]) + bf16_to_f32(sm.ra.ZT.lo[i][u]);
+          }
         }
-        sm.FT[i][jj] = f;
+        split1(f, sm.FThi[i][jj], sm.FTlo[i][jj]);
       }
       __syncthreads();
     }
-
-    // ---------------- carry: S = g_{c-1} (S0 + F^T X) ----------------
     {
-      const float* Fp = (B > 1) ? &sm.FT[0][0] : &sm.ZT[0][0];
-      const int ldf = (B > 1) ? NXP + 4 : UP + 4;
-      for (int tk = wave; tk < DK / 16; tk += 4) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_nt<false, true>(acc, Fp, ldf, &sm.XT[16 * tk][0], NXP + 8, nxp);
-        const int kk = 16 * tk + (lane & 15);
+      constexpr int NR_T = NRB * NTT;          // readout tiles
+      constexpr int NC_T = NRB * (DK / 16);    // carry tiles
+      for (int task = wave; task < NR_T + NC_T; task += NW) {
+        if (task < NR_T) {
+          const int rbk = task / NTT, tt = task % NTT;
+          if (rbk >= nrb) continue;
+          const int ib = 16 * rbk;
+          floatx4 acc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * (lane >> 4) + r;
-          sm.S[i][kk] = sm.gam[PERROW ? i : 0][CS - 1] * (sm.S[i][kk] + acc[r]);
+          for (int e = 0; e < 4; ++e) acc[e] = sm.OT[ib + 4 * lg + e][16 * tt + lr];
+          const int K = (B == 1) ? 16 * (tt + 1) : (16 * (tt + 1) * B < U ? 16 * (tt + 1) * B : U);
+          acc = mma_nt<false, false>(acc, K,
+              [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); },
+              [&](int r, int k) { return hl_pair(&sm.Phi[16 * tt + r][k], &sm.Plo[16 * tt + r][k]); });
+          const int t = 16 * tt + lr;
+          if (t < c) {
+            float ov[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = sm.gam[PERROW ? ib + 4 * lg + e : 0][t] * acc[e];
+            *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + ib + 4 * lg) =
+                make_float4(ov[0], ov[1], ov[2], ov[3]);
+          }
+        } else {
+          const int ct = task - NR_T;
+          const int rbk = ct / (DK / 16), tk = ct % (DK / 16);
+          if (rbk >= nrb) continue;
+          const int ib = 16 * rbk;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (B == 1) {
+            acc = mma_nt<false, true>(acc, CS,
+                [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); },
+                [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); });
+          } else {
+            acc = mma_nt<false, true>(acc, NXP,
+                [&](int r, int k) { return hl_pair(&sm.FThi[ib + r][k], &sm.FTlo[ib + r][k]); },
+                [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); });
+          }
+          const int kk = 16 * tk + lr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = ib + 4 * lg + e;
+            const float s = sm.gam[PERROW ? i : 0][CS - 1] * (sm.S[i][kk] + acc[e]);
+            sm.S[i][kk] = s;
+            split1(s, sm.Shi[i][kk], sm.Slo[i][kk]);
+          }
         }
       }
     }
   }
   __syncthreads();
   if (a.S_out) {
-    for (int idx = tid; idx < RB * DK; idx += kChunkThreads) {
+    for (int idx = tid; idx < RW * DK; idx += NT) {
       const int i = idx / DK, kk = idx % DK;
-      a.S_out[((long)chain * dv + i0 + i) * DK + kk] = sm.S[i][kk];
+      if (i0 + i < dv) a.S_out[((long)chain * dv + i0 + i) * DK + kk] = sm.S[i][kk];
     }
   }
 }
 
-template <int DK, int CS, bool REG, bool PERROW>
-hipError_t launch4(const SeqArgs& a, hipStream_t stream) {
+template <int DK, int CS, int B, bool REG, bool PERROW>
+hipError_t launch5(const SeqArgs& a, hipStream_t stream) {
   Geom geo;
   geo.nchain = a.batch * a.heads;
-  geo.nrb = a.dv / RB;
+  geo.nrbg = (a.dv + RW - 1) / RW;
   geo.remap = (geo.nchain % 8 == 0) ? 1 : 0;
-  const unsigned nblocks = (unsigned)(geo.nchain * geo.nrb);
-  hipLaunchKernelGGL((chunk_kernel<DK, CS, REG, PERROW>), dim3(nblocks), dim3(kChunkThreads), 0,
-                     stream, a, geo);
+  const unsigned nblocks = (unsigned)(geo.nchain * geo.nrbg);
+  hipLaunchKernelGGL((chunk_kernel<DK, CS, B, REG, PERROW>), dim3(nblocks), dim3(NT), 0, stream,
+                     a, geo);
   return hipGetLastError();
 }
 
-template <int DK, int CS>
+template <int DK, int CS, int B>
 hipError_t launch_mode(const SeqArgs& a, hipStream_t stream) {
   const bool perrow = a.beta_kind == 2;
-  if (a.regression) {
-    return perrow ? launch4<DK, CS, true, true>(a, stream) : launch4<DK, CS, true, false>(a, stream);
+  if (B == 1 && perrow) {
+    return a.regression ? launch5<DK, CS, 1, true, true>(a, stream)
+                        : launch5<DK, CS, 1, false, true>(a, stream);
   }
-  return perrow ? launch4<DK, CS, false, true>(a, stream) : launch4<DK, CS, false, false>(a, stream);
+  return a.regression ? launch5<DK, CS, B, true, false>(a, stream)
+                      : launch5<DK, CS, B, false, false>(a, stream);
 }
 
 template <int DK>
-hipError_t launch_cs(const SeqArgs& a, hipStream_t stream, int cs) {
-  switch (cs) {
-    case 16: return launch_mode<DK, 16>(a, stream);
-    case 32: return launch_mode<DK, 32>(a, stream);
-    case 64: return launch_mode<DK, 64>(a, stream);
+hipError_t launch_shape(const SeqArgs& a, hipStream_t stream, int cs) {
+  switch (a.window) {
+    case 1:
+      if (cs == 16) return launch_mode<DK, 16, 1>(a, stream);
+      if (cs == 32) return launch_mode<DK, 32, 1>(a, stream);
+      if (DK < 128 && cs == 64) return launch_mode<DK, (DK < 128 ? 64 : 32), 1>(a, stream);
+      break;
+    case 2:
+      if (cs == 16) return launch_mode<DK, 16, 2>(a, stream);
+      if (cs == 32) return launch_mode<DK, 32, 2>(a, stream);
+      break;
+    case 3: return launch_mode<DK, 16, 3>(a, stream);
+    case 4: return launch_mode<DK, 16, 4>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Sub-chunk length: the caller's chunk, halved until chunk * window <= 64.
-int chunk_sub_length(int chunk, int window) {
+// Sub-chunk length: the caller's chunk, halved until chunk * window <= 64, and
+// at most 32 steps when dk = 128.
+int chunk_sub_length(int chunk, int window, int dk) {
   int c = chunk;
-  while (c * window > UP) c >>= 1;
+  while (c * window > 64) c >>= 1;
+  if (dk == 128 && c > 32) c = 32;
   return c;
 }
 
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
-  const int cs = chunk_sub_length(a.chunk, a.window);
+  const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
   switch (a.dk) {
-    case 16: return launch_cs<16>(a, stream, cs);
-    case 32: return launch_cs<32>(a, stream, cs);
-    case 64: return launch_cs<64>(a, stream, cs);
-    case 128: return launch_cs<128>(a, stream, cs);
+    case 16: return launch_shape<16>(a, stream, cs);
+    case 32: return launch_shape<32>(a, stream, cs);
+    case 64: return launch_shape<64>(a, stream, cs);
+    case 128: return launch_shape<128>(a, stream, cs);
   }
   return hipErrorInvalidValue;
 }
