@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libfalcon.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["falcon_api.cpp", "falcon_recurrent.hip", "falcon_decode.hip", "falcon_chunk.hip"]
+SOURCES = ["falcon_api.cpp", "falcon_recurrent.hip", "falcon_decode.hip", "falcon_chunk.hip",
+           "falcon_chunk_w1.hip"]
 ARCH = os.environ.get("FALCON_OFFLOAD_ARCH", "gfx950")
 
 

@@ -48,6 +48,7 @@
 // (LDS budget); the result does not depend on it beyond rounding.
 #include "falcon_device.h"
 #include "falcon_launch.h"
+#include "falcon_mma.h"
 
 namespace falcon {
 namespace {
@@ -57,92 +58,6 @@ constexpr int NRB = 2;    // row blocks per workgroup
 constexpr int RW = RB * NRB;
 constexpr int NW = 8;     // waves per workgroup
 constexpr int NT = 64 * NW;
-
-struct HL {
-  bf16x8 hi, lo;
-};
-
-__device__ __forceinline__ HL hl_zero() {
-  HL z;
-  z.hi = zero_frag();
-  z.lo = zero_frag();
-  return z;
-}
-__device__ __forceinline__ HL hl_pair(const uint16_t* hi, const uint16_t* lo) {
-  HL f;
-  f.hi = frag_bf16(hi);
-  f.lo = frag_bf16(lo);
-  return f;
-}
-__device__ __forceinline__ HL hl_bf16(const uint16_t* p) {
-  HL f;
-  f.hi = frag_bf16(p);
-  f.lo = zero_frag();
-  return f;
-}
-__device__ __forceinline__ HL hl_f32(const float* p) {
-  HL f;
-  frag_split(p, f.hi, f.lo);
-  return f;
-}
-// 8 fp32 values (in registers) -> split fragment
-__device__ __forceinline__ HL hl_vals(const float* v) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
-  }
-  uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  uint4 Lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
-  HL f;
-  f.hi = __builtin_bit_cast(bf16x8, H);
-  f.lo = __builtin_bit_cast(bf16x8, Lo);
-  return f;
-}
-
-__device__ __forceinline__ void split1(float x, uint16_t& h, uint16_t& l) {
-  const uint32_t hb = f32_to_bf16_bits(x);
-  h = (uint16_t)hb;
-  l = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hb << 16));
-}
-
-// 4 consecutive fp32 -> 4 hi and 4 lo bf16 stored with one 8-byte write each.
-__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float* v) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
-  }
-  *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// acc[m][n] += sum_{k<K} A[m][k] B[n][k] for one 16x16 tile; fa(r, k) / fb(r, k)
-// return the fragment of operand row r (0..15) at k (multiple of 8).  AX / BX:
-// the operand is an exact bf16 value (its lo part is zero; pass skipped).
-template <bool AX, bool BX, class FA, class FB>
-__device__ __forceinline__ floatx4 mma_nt(floatx4 acc, int K, FA&& fa, FB&& fb) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
-  const int kq = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const int k = k0 + kq;
-    const HL A = k < K ? fa(r, k) : hl_zero();
-    const HL Bv = k < K ? fb(r, k) : hl_zero();
-    acc = mfma16(A.hi, Bv.hi, acc);
-    if (!BX) acc = mfma16(A.hi, Bv.lo, acc);
-    if (!AX) acc = mfma16(A.lo, Bv.hi, acc);
-  }
-  return acc;
-}
 
 template <int DK, int CS, int B>
 struct Cfg {
@@ -239,13 +154,17 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
   const int i0 = rbg * RW;
   const int nrb = (dv - i0) >= RW ? NRB : 1;       // active row blocks (dv = 16: one)
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int lane = tid & 63;
   const int lr = lane & 15;          // tile column / fragment row
   const int lg = lane >> 4;          // lane group
   const long L = a.seqlen;
   const long qk_base = (long)chain * L * DK;
   const long v_base = (long)chain * L * dv;
+  // z lives over the keys (dead after P2') for the regression family and over
+  // the queries (dead after P1) for the inner-product family, whose z is written
+  // in P2 while the keys are still needed for the transposed copy.
+  typename SM::Split* const zt = REG ? &sm.ra.ZT : &sm.rb.RT;
 
   // ---------------- prefetch registers ----------------
   uint4 pk[KV], pq[QV], py[YV];
@@ -329,11 +248,6 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
       part = group_sum<VPR>(part);
       if (idx < NXP * VPR) {
         *reinterpret_cast<uint4*>(&sm.ra.X[jj][kv * 8]) = val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.XT[kv * 8 + 2 * e][jj] = (uint16_t)(w4[e] & 0xFFFFu);
-          sm.XT[kv * 8 + 2 * e + 1][jj] = (uint16_t)(w4[e] >> 16);
-        }
         if (kv == 0) sm.nrm[jj] = part;
       }
     }
@@ -481,26 +395,48 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
       if (!PERROW && wave == NW - 1) {
         // T_bb = (I + Gamma_- Gs Z)^-1 = Gamma_- (I + Gs D)^-1 Gamma_-^{-1},
         // D = diag(zeta_m g_{t(m)-1}); lane = 16 b + column.
-        const int bb = lane >> 4, cc = lane & 15;
-        if (bb < NB) {
-          const int u0 = 16 * bb;
-          float acc[16];
+        const int bb = (lane >> 4) < NB ? (lane >> 4) : 0;   // lanes beyond NB blocks redo block 0
+        const int cc = lane & 15;
+        const int u0 = 16 * bb;
+        float gmv[16], dm[16], acc[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = (r == cc) ? 1.0f : 0.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int tr = (u0 + r) / B;
+          gmv[r] = sm.gm1[0][tr];
+          dm[r] = sm.zeta[0][tr] * gmv[r];
+          acc[r] = (r == cc) ? 1.0f : 0.0f;
+        }
+        // rows of the block, two ahead of use (Gt^T[u_m][u_r] = Gs[r][m])
+        float4 g0[4], g1[4], g2[4];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int tm = (u0 + m) / B;
-            const float sv = sm.zeta[0][tm] * sm.gm1[0][tm] * acc[m];
-            const float* grow = &sm.GT[u0 + m][u0];     // Gt^T[u_m][u_r] = Gs[r][m]
+        for (int q4 = 0; q4 < 4; ++q4) {
+          g0[q4] = *reinterpret_cast<const float4*>(&sm.GT[u0][u0 + 4 * q4]);
+          g1[q4] = *reinterpret_cast<const float4*>(&sm.GT[u0 + 1][u0 + 4 * q4]);
+        }
 #pragma unroll
-            for (int r = m + 1; r < 16; ++r) acc[r] -= grow[r] * sv;
+        for (int m = 0; m < 16; ++m) {
+          if (m + 2 < 16) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              g2[q4] = *reinterpret_cast<const float4*>(&sm.GT[u0 + m + 2][u0 + 4 * q4]);
           }
+          const float sv = dm[m] * acc[m];
+          const float grow[16] = {g0[0].x, g0[0].y, g0[0].z, g0[0].w, g0[1].x, g0[1].y,
+                                  g0[1].z, g0[1].w, g0[2].x, g0[2].y, g0[2].z, g0[2].w,
+                                  g0[3].x, g0[3].y, g0[3].z, g0[3].w};
+#pragma unroll
+          for (int r = m + 1; r < 16; ++r) acc[r] -= grow[r] * sv;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            g0[q4] = g1[q4];
+            g1[q4] = g2[q4];
+          }
+        }
+        if ((lane >> 4) < NB) {
           const float inv_c = 1.0f / sm.gm1[0][(u0 + cc) / B];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float tv = sm.gm1[0][(u0 + r) / B] * acc[r] * inv_c;
-            split1(tv, sm.SAhi[bb][r][cc], sm.SAlo[bb][r][cc]);
-          }
+          for (int r = 0; r < 16; ++r)
+            split1(gmv[r] * acc[r] * inv_c, sm.SAhi[bb][r][cc], sm.SAlo[bb][r][cc]);
         }
       }
       // S0 x_j tiles (row block, key tile) -> right-hand sides; with scalar eta
@@ -533,7 +469,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
         const int i = idx / U, u = idx % U;
         const int t = u / B, jj = t - u % B + B - 1;
         const float zv = sm.zeta[PERROW ? i : 0][t] * sm.YT[i][jj];
-        split1(zv, sm.ra.ZT.hi[i][u], sm.ra.ZT.lo[i][u]);
+        split1(zv, zt->hi[i][u], zt->lo[i][u]);
       }
     }
     __syncthreads();
@@ -563,6 +499,15 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
         }
       }
     }
+    // keys transposed for the carry: XT[k][j], one 16-byte write per (k, 8 keys)
+    for (int idx = tid; idx < DK * (NXP / 8); idx += NT) {
+      const int kk = idx % DK, j8 = idx / DK;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)sm.ra.X[8 * j8 + 2 * e][kk] | ((uint32_t)sm.ra.X[8 * j8 + 2 * e + 1][kk] << 16);
+      *reinterpret_cast<uint4*>(&sm.XT[kk][8 * j8]) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
     if (REG && B > 1) {
       for (int idx = tid; idx < RW * U; idx += NT) {
         const int i = idx / U, u = idx % U;
@@ -571,7 +516,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
         split1(rv, sm.rb.RT.hi[i][u], sm.rb.RT.lo[i][u]);
       }
     }
-    if (REG) __syncthreads();
+    __syncthreads();
 
     // ================= P3: blocked solve, one wave per row block =================
     if (REG && wave < nrb) {
@@ -584,13 +529,13 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
               [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
               [&](int r, int k) {
                 if (k < 16) return hl_pair(&sm.rb.RT.hi[ib + r][16 * bb + k], &sm.rb.RT.lo[ib + r][16 * bb + k]);
-                return hl_pair(&sm.ra.ZT.hi[ib + r][k - 16], &sm.ra.ZT.lo[ib + r][k - 16]);
+                return hl_pair(&zt->hi[ib + r][k - 16], &zt->lo[ib + r][k - 16]);
               });
           // E_b[u][i]: lane holds u = 16 bb + 4 lg + e, i = lr
           float z[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) z[e] = sm.zeta[0][(16 * bb + 4 * lg + e) / B] * acc[e];
-          store_split4(&sm.ra.ZT.hi[ib + lr][16 * bb + 4 * lg], &sm.ra.ZT.lo[ib + lr][16 * bb + 4 * lg], z);
+          store_split4(&zt->hi[ib + lr][16 * bb + 4 * lg], &zt->lo[ib + lr][16 * bb + 4 * lg], z);
           wave_sync();
         }
       } else {
@@ -600,7 +545,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
             floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
             cacc = mma_nt<false, false>(cacc, u0,
                 [&](int r, int k) { return hl_f32(&sm.GT[u0 + r][k]); },
-                [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); });
+                [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); });
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int u = u0 + 4 * lg + e;
@@ -623,7 +568,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
             }
 #pragma unroll
             for (int r = 0; r < 16; r += 4)
-              store_split4(&sm.ra.ZT.hi[i][u0 + r], &sm.ra.ZT.lo[i][u0 + r], &z[r]);
+              store_split4(&zt->hi[i][u0 + r], &zt->lo[i][u0 + r], &z[r]);
           }
           wave_sync();
         }
@@ -641,7 +586,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
           const int t = jj + w - (B - 1);
           if (t >= 0 && t < CS) {
             const int u = t * B + w;
-            f += bf16_to_f32(sm.ra.ZT.hi[i][u]) + bf16_to_f32(sm.ra.ZT.lo[i][u]);
+            f += bf16_to_f32(zt->hi[i][u]) + bf16_to_f32(zt->lo[i][u]);
           }
         }
         split1(f, sm.FThi[i][jj], sm.FTlo[i][jj]);
@@ -661,7 +606,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
           for (int e = 0; e < 4; ++e) acc[e] = sm.OT[ib + 4 * lg + e][16 * tt + lr];
           const int K = (B == 1) ? 16 * (tt + 1) : (16 * (tt + 1) * B < U ? 16 * (tt + 1) * B : U);
           acc = mma_nt<false, false>(acc, K,
-              [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); },
+              [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); },
               [&](int r, int k) { return hl_pair(&sm.Phi[16 * tt + r][k], &sm.Plo[16 * tt + r][k]); });
           const int t = 16 * tt + lr;
           if (t < c) {
@@ -679,7 +624,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
           if (B == 1) {
             acc = mma_nt<false, true>(acc, CS,
-                [&](int r, int k) { return hl_pair(&sm.ra.ZT.hi[ib + r][k], &sm.ra.ZT.lo[ib + r][k]); },
+                [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); },
                 [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); });
           } else {
             acc = mma_nt<false, true>(acc, NXP,
@@ -721,11 +666,6 @@ hipError_t launch5(const SeqArgs& a, hipStream_t stream) {
 
 template <int DK, int CS, int B>
 hipError_t launch_mode(const SeqArgs& a, hipStream_t stream) {
-  const bool perrow = a.beta_kind == 2;
-  if (B == 1 && perrow) {
-    return a.regression ? launch5<DK, CS, 1, true, true>(a, stream)
-                        : launch5<DK, CS, 1, false, true>(a, stream);
-  }
   return a.regression ? launch5<DK, CS, B, true, false>(a, stream)
                       : launch5<DK, CS, B, false, false>(a, stream);
 }
@@ -733,11 +673,6 @@ hipError_t launch_mode(const SeqArgs& a, hipStream_t stream) {
 template <int DK>
 hipError_t launch_shape(const SeqArgs& a, hipStream_t stream, int cs) {
   switch (a.window) {
-    case 1:
-      if (cs == 16) return launch_mode<DK, 16, 1>(a, stream);
-      if (cs == 32) return launch_mode<DK, 32, 1>(a, stream);
-      if (DK < 128 && cs == 64) return launch_mode<DK, (DK < 128 ? 64 : 32), 1>(a, stream);
-      break;
     case 2:
       if (cs == 16) return launch_mode<DK, 16, 2>(a, stream);
       if (cs == 32) return launch_mode<DK, 32, 2>(a, stream);
@@ -762,6 +697,7 @@ int chunk_sub_length(int chunk, int window, int dk) {
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
+  if (a.window == 1) return launch_chunk_w1(a, stream, cs);
   switch (a.dk) {
     case 16: return launch_shape<16>(a, stream, cs);
     case 32: return launch_shape<32>(a, stream, cs);

@@ -1,0 +1,608 @@
+// falcon_chunk_w1.hip - chunk-parallel Falcon forward for window 1 (Falcon-1,
+// -2, -1A, -2A), software-pipelined across chunks on gfx950.
+//
+// Method and algebra: explainer of arXiv 2608.27763, section 核心方法 §3
+// (chunk-parallel form) and the 163.com article, section 02 (2) (only the
+// fixed-size state passes between chunks; Gram / WY representation with a
+// batched triangular solve).  With window 1 the unknowns of a chunk are the
+// residuals e_t = y_t - S_{t-1} x_t, t = 0..C-1, and (per value row)
+//   g_t = prod_{r<=t} a_r, zeta_t = eta_t / g_t, z_t = zeta_t e_t,
+//   e_t + g_{t-1} sum_{s<t} (x_t . x_s) z_s = y_t - g_{t-1} S0 x_t   (regression)
+//   z_t = zeta_t y_t                                                  (inner product)
+//   o_t = g_t (S0 q_t + sum_{s<=t} (q_t . x_s) z_s)
+//   S_C = g_{C-1} (S0 + sum_s z_s x_s^T)
+//
+// Why a separate kernel: everything that does not depend on the incoming
+// state S0 (Gram, q.x, decay products, the triangular factors) can be computed
+// one chunk ahead.  Each iteration c therefore runs, between three workgroup
+// barriers, the state-dependent chain of chunk c next to the state-independent
+// preparation of chunk c+1, so the serial pieces (the solve on two waves, the
+// diagonal-block inverses on one wave) overlap with matrix-core work of the
+// other waves instead of idling them:
+//   phase 1  commit chunk c+1's prefetched q/k/v/beta to LDS (second buffer)
+//            and issue chunk c+2's global loads; keys of chunk c transposed;
+//            S0 x_t and S0 q_t (kept in registers for the readout);
+//            off-diagonal solve blocks M_bj of chunk c; per-row scalars (Falcon-2)
+//   phase 2  solve of chunk c (one wave per 16-row block)  ||  Gram and q.x of
+//            chunk c+1, scalars of chunk c+1 (shared eta)
+//   phase 3  readout and state carry of chunk c  ||  diagonal-block inverses
+//            of chunk c+1 (shared eta) or its Gram (per-channel eta)
+// One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
+#include "falcon_device.h"
+#include "falcon_launch.h"
+#include "falcon_mma.h"
+
+namespace falcon {
+namespace {
+
+constexpr int RB = 16;
+constexpr int NRB = 2;
+constexpr int RW = RB * NRB;
+constexpr int NW = 8;
+constexpr int NT = 64 * NW;
+
+template <int DK, int CS, bool REG, bool PERROW>
+struct W1Lds {
+  static constexpr int NB = CS / 16;
+  static constexpr int SCB = PERROW ? 1 : 2;   // scalar buffers (shared eta: double)
+  static constexpr int SR = PERROW ? RW : 1;   // scalar rows
+  struct Split {
+    uint16_t hi[RW][CS + 8];
+    uint16_t lo[RW][CS + 8];
+  };
+  union Slot {               // keys of a chunk; once consumed, that chunk's z
+    uint16_t X[CS][DK + 8];
+    Split ZT;
+  };
+  Slot slot[2];
+  uint16_t Q[2][CS][DK + 8];
+  uint16_t XT[DK][CS + 8];           // keys of the current chunk, transposed
+  uint16_t YT[2][RW][CS + 8];        // values (bf16 bits), transposed
+  uint16_t BT[PERROW ? 2 : 1][PERROW ? RW : 1][CS];   // per-channel beta (bf16 bits)
+  float beta[2][CS];                 // shared beta (fp32)
+  float nrm[2][CS];
+  float S[RW][DK + 4];
+  uint16_t Shi[RW][DK + 8];
+  uint16_t Slo[RW][DK + 8];
+  float XS[REG ? RW : 1][CS + 4];    // S0 x_t
+  float GT[REG ? CS : 1][CS + 4];    // shared eta: Gram transposed; per-channel: Gram
+  uint16_t Phi[2][CS][CS + 8];       // masked q.x, split
+  uint16_t Plo[2][CS][CS + 8];
+  uint16_t SAhi[(REG && !PERROW) ? NB : 1][16][CS + 8];   // [T_bb | -M_b0 | ...]
+  uint16_t SAlo[(REG && !PERROW) ? NB : 1][16][CS + 8];
+  float RP[(REG && PERROW) ? RW : 1][CS + 4];              // per-row right-hand sides
+  float gam[SCB][SR][CS];
+  float gm1[SCB][SR][CS];
+  float zeta[SCB][SR][CS];
+};
+
+struct W1Geom {
+  int nrbg;
+  int remap;
+  int nchunks;
+};
+
+template <int DK, int CS, bool REG, bool PERROW>
+__global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
+  using SM = W1Lds<DK, CS, REG, PERROW>;
+  constexpr int NB = CS / 16, NTT = CS / 16, NKT = DK / 16, VPR = DK / 8;
+  constexpr int KV = (CS * VPR + NT - 1) / NT;
+  constexpr int YV = (CS * (RW / 8) + NT - 1) / NT;
+  constexpr int NBT = (PERROW ? RW : 1) * CS;
+  constexpr int BV = (NBT + NT - 1) / NT;
+  __shared__ __align__(16) SM sm;
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
+  const uint16_t* __restrict__ bg = static_cast<const uint16_t*>(a.beta_t);
+
+  int chain, rbg;
+  {
+    const int b = blockIdx.x;
+    if (geo.remap) {   // the row-block groups of one chain share an XCD (and its L2)
+      const int xcd = b & 7, slot = b >> 3;
+      chain = xcd + 8 * (slot / geo.nrbg);
+      rbg = slot % geo.nrbg;
+    } else {
+      chain = b / geo.nrbg;
+      rbg = b % geo.nrbg;
+    }
+  }
+  const int dv = a.dv;
+  const int i0 = rbg * RW;
+  const int nrb = (dv - i0) >= RW ? NRB : 1;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const long L = a.seqlen;
+  const long qk_base = (long)chain * L * DK;
+  const long v_base = (long)chain * L * dv;
+  const int nchunks = geo.nchunks;
+
+  // ---------------- prefetch registers (one chunk ahead of the commit) ----------------
+  uint4 pk[KV], pq[KV], py[YV];
+  uint32_t pb[BV];
+  auto prefetch = [&](int cidx) {
+    const long t0 = (long)cidx * CS;
+    const int c = (int)((L - t0) < CS ? (L - t0) : CS);
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int idx = tid + v * NT;
+      const int t = idx / VPR, kv = idx % VPR;
+      uint4 kval = {0u, 0u, 0u, 0u}, qval = {0u, 0u, 0u, 0u};
+      if (idx < CS * VPR && t < c) {
+        const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
+        if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
+        else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
+        qval = *reinterpret_cast<const uint4*>(qg + qk_base + g * DK + kv * 8);
+      }
+      pk[v] = kval;
+      pq[v] = qval;
+    }
+#pragma unroll
+    for (int v = 0; v < YV; ++v) {
+      const int idx = tid + v * NT;
+      const int t = idx / (RW / 8), h = idx % (RW / 8);
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (idx < CS * (RW / 8) && t < c && i0 + h * 8 < dv)
+        val = *reinterpret_cast<const uint4*>(vg + v_base + (t0 + t) * dv + i0 + h * 8);
+      py[v] = val;
+    }
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int idx = tid + v * NT;
+      uint32_t bits = 0;
+      if (idx < NBT && a.beta_kind != 0) {
+        const int i = idx / CS, t = idx % CS;
+        if (t < c) {
+          if (a.beta_kind == 1) bits = bg[(long)chain * L + t0 + t];
+          else if (i0 + i < dv) bits = bg[((long)chain * L + t0 + t) * dv + i0 + i];
+        }
+      }
+      pb[v] = bits;
+    }
+  };
+  auto commit = [&](int s) {
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const int idx = tid + v * NT;
+      const uint4 val = pk[v];
+      const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_to_f32((uint16_t)(w4[e] & 0xFFFFu));
+        const float hi = bf16_to_f32((uint16_t)(w4[e] >> 16));
+        part += lo * lo + hi * hi;
+      }
+      part = group_sum<VPR>(part);
+      if (idx < CS * VPR) {
+        const int t = idx / VPR, kv = idx % VPR;
+        *reinterpret_cast<uint4*>(&sm.slot[s].X[t][kv * 8]) = val;
+        *reinterpret_cast<uint4*>(&sm.Q[s][t][kv * 8]) = pq[v];
+        if (kv == 0) sm.nrm[s][t] = part;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < YV; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < CS * (RW / 8)) {
+        const int t = idx / (RW / 8), h = idx % (RW / 8);
+        const uint4 val = py[v];
+        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.YT[s][h * 8 + 2 * e][t] = (uint16_t)(w4[e] & 0xFFFFu);
+          sm.YT[s][h * 8 + 2 * e + 1][t] = (uint16_t)(w4[e] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int idx = tid + v * NT;
+      if (idx < NBT) {
+        if (PERROW) sm.BT[s][idx / CS][idx % CS] = (uint16_t)pb[v];
+        else sm.beta[s][idx] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)pb[v]);
+      }
+    }
+  };
+
+  // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
+  // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
+  // One wave per row of scalars; lane = step; prefix product by a wave scan.
+  auto scalars = [&](int s, int cidx, int dst, int row, int wv) {
+    (void)wv;
+    const long t0 = (long)cidx * CS;
+    const int c = (int)((L - t0) < CS ? (L - t0) : CS);
+    const int t = lane;
+    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+    float eta = 0.0f, dec = 1.0f;
+    if (live) {
+      const float bv = PERROW ? bf16_to_f32(sm.BT[s][row][t]) : sm.beta[s][t];
+      eta = bv / (a.eps + sm.nrm[s][t]);
+      dec = 1.0f - eta * a.lambda;
+    }
+    float gsc = dec;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(gsc, d, 64);
+      if (lane >= d) gsc *= o;
+    }
+    float gprev = __shfl_up(gsc, 1, 64);
+    if (lane == 0) gprev = 1.0f;
+    if (t < CS) {
+      sm.gam[dst][row][t] = gsc;
+      sm.gm1[dst][row][t] = gprev;
+      sm.zeta[dst][row][t] = eta / gsc;
+    }
+  };
+
+  // Gram (regression) and q.x tiles of slot s: lower triangle of 16x16 tiles.
+  constexpr int NLT = NTT * (NTT + 1) / 2;
+  auto gram_tile = [&](int s, int tt) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
+    const int tj = tt - ti * (ti + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma_nt<true, true>(acc, DK,
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * ti + r][k]); },
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * tj + r][k]); });
+    const int col = 16 * tj + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * ti + 4 * lg + e;
+      const float gv = (col < row) ? acc[e] : 0.0f;
+      if (PERROW) sm.GT[row][col] = gv;    // Gs[u][u']
+      else sm.GT[col][row] = gv;           // Gs^T[u'][u]
+    }
+  };
+  auto qx_tile = [&](int s, int tt) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
+    const int tj = tt - ti * (ti + 1) / 2;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mma_nt<true, true>(acc, DK,
+        [&](int r, int k) { return hl_bf16(&sm.Q[s][16 * ti + r][k]); },
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * tj + r][k]); });
+    const int col = 16 * tj + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * ti + 4 * lg + e;
+      split1((col <= row) ? acc[e] : 0.0f, sm.Phi[s][row][col], sm.Plo[s][row][col]);
+    }
+  };
+  // 16x16 diagonal-block inverses T_bb = Gamma_- (I + Gs D)^-1 Gamma_-^{-1},
+  // D = diag(zeta_m g_{m-1}); one wave, lane = 16 b + column.
+  auto diag_inverse = [&](int sc) {
+    const int bb = (lane >> 4) < NB ? (lane >> 4) : 0;
+    const int cc = lane & 15;
+    const int u0 = 16 * bb;
+    float gmv[16], dm[16], acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      gmv[r] = sm.gm1[sc][0][u0 + r];
+      dm[r] = sm.zeta[sc][0][u0 + r] * gmv[r];
+      acc[r] = (r == cc) ? 1.0f : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float sv = dm[m] * acc[m];
+      const float* grow = &sm.GT[u0 + m][u0];   // Gs^T[u_m][u_r] = Gs[r][m]
+#pragma unroll
+      for (int r = m + 1; r < 16; ++r) acc[r] -= grow[r] * sv;
+    }
+    if ((lane >> 4) < NB) {
+      const float inv_c = 1.0f / sm.gm1[sc][0][u0 + cc];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        split1(gmv[r] * acc[r] * inv_c, sm.SAhi[bb][r][cc], sm.SAlo[bb][r][cc]);
+    }
+  };
+
+  // ---------------- prologue: state, chunk 0 ----------------
+  for (int idx = tid; idx < RW * DK; idx += NT) {
+    const int i = idx / DK, kk = idx % DK;
+    float sv = 0.0f;
+    if (a.S0 && i0 + i < dv) sv = a.S0[((long)chain * dv + i0 + i) * DK + kk];
+    sm.S[i][kk] = sv;
+    split1(sv, sm.Shi[i][kk], sm.Slo[i][kk]);
+  }
+  prefetch(0);
+  commit(0);
+  if (nchunks > 1) prefetch(1);
+  __syncthreads();
+  for (int task = wave; task < (REG ? 2 : 1) * NLT; task += NW) {
+    if (task < NLT) qx_tile(0, task);
+    else gram_tile(0, task - NLT);
+  }
+  if (!PERROW && wave == NW - 1) scalars(0, 0, 0, 0, wave);
+  __syncthreads();
+  if (REG && !PERROW && wave == NW - 1) diag_inverse(0);
+  __syncthreads();
+
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int cur = ci & 1, nxt = cur ^ 1;
+    const bool has_next = ci + 1 < nchunks;
+    const long t0 = (long)ci * CS;
+    const int cval = (int)((L - t0) < CS ? (L - t0) : CS);
+    const int sc = PERROW ? 0 : cur;          // scalar buffer of chunk ci
+
+    // ================= phase 1 =================
+    if (has_next) {
+      commit(nxt);
+      if (ci + 2 < nchunks) prefetch(ci + 2);
+    }
+    // keys of chunk ci transposed (carry operand)
+    for (int idx = tid; idx < DK * (CS / 8); idx += NT) {
+      const int kk = idx % DK, j8 = idx / DK;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)sm.slot[cur].X[8 * j8 + 2 * e][kk] |
+               ((uint32_t)sm.slot[cur].X[8 * j8 + 2 * e + 1][kk] << 16);
+      *reinterpret_cast<uint4*>(&sm.XT[kk][8 * j8]) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // S0 q_t tiles stay in the registers of the wave that reads them out in phase 3
+    constexpr int NQ = NRB * NTT;
+    floatx4 qacc = {0.f, 0.f, 0.f, 0.f};
+    if (wave < NQ) {
+      const int rbk = wave / NTT, tt = wave % NTT;
+      if (rbk < nrb)
+        qacc = mma_nt<false, true>(qacc, DK,
+            [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); },
+            [&](int r, int k) { return hl_bf16(&sm.Q[cur][16 * tt + r][k]); });
+    }
+    {
+      constexpr int NXS = REG ? NRB * NTT : 0;
+      constexpr int NM = (REG && !PERROW) ? NB * (NB - 1) / 2 : 0;
+      for (int task = (wave + NQ) % NW; task < NXS + NM; task += NW) {
+        if (task < NXS) {
+          const int rbk = task / NTT, tj = task % NTT;
+          if (rbk >= nrb) continue;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma_nt<false, true>(acc, DK,
+              [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); },
+              [&](int r, int k) { return hl_bf16(&sm.slot[cur].X[16 * tj + r][k]); });
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.XS[16 * rbk + 4 * lg + e][16 * tj + lr] = acc[e];
+        } else {
+          // M_bj = T_bb diag(g_{t-1})_b Gs_bj (negated next to T_bb)
+          const int mt = task - NXS;
+          int bb = 1;
+          while (bb * (bb + 1) / 2 <= mt) ++bb;
+          const int jb = mt - bb * (bb - 1) / 2;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma_nt<false, false>(acc, 16,
+              [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
+              [&](int r, int k) {
+                float v[8];
+                const float* gp = &sm.GT[16 * jb + r][16 * bb + k];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = gp[e] * sm.gm1[sc][0][16 * bb + k + e];
+                return hl_vals(v);
+              });
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lg + e;
+            split1(-acc[e], sm.SAhi[bb][r][16 * (jb + 1) + lr], sm.SAlo[bb][r][16 * (jb + 1) + lr]);
+          }
+        }
+      }
+    }
+    if (PERROW && wave >= NW - 4) {
+      for (int i = wave - (NW - 4); i < RW; i += 4) scalars(cur, ci, 0, i, wave);
+    }
+    __syncthreads();
+
+    // ================= phase 2 =================
+    typename SM::Split* const zt = &sm.slot[cur].ZT;   // keys of ci are consumed
+    if (REG) {
+      if (wave < nrb) {
+        const int ib = 16 * wave;
+        if (!PERROW) {
+          for (int bb = 0; bb < NB; ++bb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_nt<false, false>(acc, 16 * (bb + 1),
+                [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
+                [&](int r, int k) {
+                  if (k < 16) {
+                    // right-hand side r_u = y_u - g_{u-1} (S0 x_u), formed on the fly
+                    const int u = 16 * bb + k;
+                    const uint4 yb = *reinterpret_cast<const uint4*>(&sm.YT[cur][ib + r][u]);
+                    const uint32_t yw[4] = {yb.x, yb.y, yb.z, yb.w};
+                    const float4 x0 = *reinterpret_cast<const float4*>(&sm.XS[ib + r][u]);
+                    const float4 x1 = *reinterpret_cast<const float4*>(&sm.XS[ib + r][u + 4]);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                      const uint16_t yv = (e & 1) ? (uint16_t)(yw[e >> 1] >> 16) : (uint16_t)(yw[e >> 1] & 0xFFFFu);
+                      v[e] = bf16_to_f32(yv) - sm.gm1[sc][0][u + e] * xs[e];
+                    }
+                    return hl_vals(v);
+                  }
+                  return hl_pair(&zt->hi[ib + r][k - 16], &zt->lo[ib + r][k - 16]);
+                });
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = sm.zeta[sc][0][16 * bb + 4 * lg + e] * acc[e];
+            store_split4(&zt->hi[ib + lr][16 * bb + 4 * lg], &zt->lo[ib + lr][16 * bb + 4 * lg], z);
+            wave_sync();
+          }
+        } else {
+          // right-hand sides, then per stage: off-diagonal coupling on MFMA and the
+          // diagonal block by per-row forward substitution
+          for (int idx = lane; idx < RB * CS; idx += 64) {
+            const int i = ib + idx / CS, u = idx % CS;
+            sm.RP[i][u] = bf16_to_f32(sm.YT[cur][i][u]) - sm.gm1[0][i][u] * sm.XS[i][u];
+          }
+          wave_sync();
+          for (int bb = 0; bb < NB; ++bb) {
+            const int u0 = 16 * bb;
+            if (bb > 0) {
+              floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
+              cacc = mma_nt<false, false>(cacc, u0,
+                  [&](int r, int k) { return hl_f32(&sm.GT[u0 + r][k]); },
+                  [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); });
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int u = u0 + 4 * lg + e;
+                sm.RP[ib + lr][u] -= sm.gm1[0][ib + lr][u] * cacc[e];
+              }
+              wave_sync();
+            }
+            if (lane < 16) {
+              const int i = ib + lane;
+              float acc[16], z[16];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+              for (int m = 0; m < 16; ++m) {
+                const int u = u0 + m;
+                const float e = sm.RP[i][u] - sm.gm1[0][i][u] * acc[m];
+                z[m] = sm.zeta[0][i][u] * e;
+#pragma unroll
+                for (int r = m + 1; r < 16; ++r) acc[r] += sm.GT[u0 + r][u] * z[m];
+              }
+#pragma unroll
+              for (int r = 0; r < 16; r += 4)
+                store_split4(&zt->hi[i][u0 + r], &zt->lo[i][u0 + r], &z[r]);
+            }
+            wave_sync();
+          }
+        }
+      }
+    } else {
+      // inner-product family: z_t = zeta_t y_t
+      for (int idx = tid; idx < RW * CS; idx += NT) {
+        const int i = idx / CS, t = idx % CS;
+        const float zv = sm.zeta[sc][PERROW ? i : 0][t] * bf16_to_f32(sm.YT[cur][i][t]);
+        split1(zv, zt->hi[i][t], zt->lo[i][t]);
+      }
+    }
+    if (has_next) {
+      // state-independent preparation of chunk ci+1 on the waves not solving
+      const int w0 = REG ? NRB : 0;
+      const int nws = NW - w0;
+      constexpr int NG2 = (REG && !PERROW) ? NLT : 0;   // per-channel Gram waits for phase 3
+      if (wave >= w0) {
+        for (int task = wave - w0; task < NLT + NG2; task += nws) {
+          if (task < NLT) qx_tile(nxt, task);
+          else gram_tile(nxt, task - NLT);
+        }
+      }
+      if (!PERROW && wave == NW - 1) scalars(nxt, ci + 1, nxt, 0, wave);
+    }
+    __syncthreads();
+
+    // ================= phase 3 =================
+    if (wave < NQ) {
+      const int rbk = wave / NTT, tt = wave % NTT;
+      if (rbk < nrb) {
+        const int ib = 16 * rbk;
+        floatx4 acc = mma_nt<false, false>(qacc, 16 * (tt + 1),
+            [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); },
+            [&](int r, int k) { return hl_pair(&sm.Phi[cur][16 * tt + r][k], &sm.Plo[cur][16 * tt + r][k]); });
+        const int t = 16 * tt + lr;
+        if (t < cval) {
+          float ov[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = sm.gam[sc][PERROW ? ib + 4 * lg + e : 0][t] * acc[e];
+          *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + ib + 4 * lg) =
+              make_float4(ov[0], ov[1], ov[2], ov[3]);
+        }
+      }
+    }
+    {
+      // carry tiles, dealt so the diagonal-inverse wave gets the fewest
+      constexpr int NC = NRB * NKT;
+      for (int task = wave; task < NC; task += NW) {
+        const int rbk = task / NKT, tk = task % NKT;
+        if (rbk >= nrb) continue;
+        const int ib = 16 * rbk;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_nt<false, true>(acc, CS,
+            [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); },
+            [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); });
+        const int kk = 16 * tk + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ib + 4 * lg + e;
+          const float s = sm.gam[sc][PERROW ? i : 0][CS - 1] * (sm.S[i][kk] + acc[e]);
+          sm.S[i][kk] = s;
+          split1(s, sm.Shi[i][kk], sm.Slo[i][kk]);
+        }
+      }
+    }
+    if (has_next) {
+      if (REG && !PERROW && wave == NW - 1) diag_inverse(nxt);
+      if (REG && PERROW) {
+        for (int task = wave; task < NLT; task += NW) gram_tile(nxt, task);
+      }
+    }
+    __syncthreads();
+  }
+  if (a.S_out) {
+    for (int idx = tid; idx < RW * DK; idx += NT) {
+      const int i = idx / DK, kk = idx % DK;
+      if (i0 + i < dv) a.S_out[((long)chain * dv + i0 + i) * DK + kk] = sm.S[i][kk];
+    }
+  }
+}
+
+template <int DK, int CS, bool REG, bool PERROW>
+hipError_t launch_w1(const SeqArgs& a, hipStream_t stream) {
+  W1Geom geo;
+  const int nchain = a.batch * a.heads;
+  geo.nrbg = (a.dv + RW - 1) / RW;
+  geo.remap = (nchain % 8 == 0) ? 1 : 0;
+  geo.nchunks = (int)((a.seqlen + CS - 1) / CS);
+  const unsigned nblocks = (unsigned)(nchain * geo.nrbg);
+  hipLaunchKernelGGL((chunk_w1_kernel<DK, CS, REG, PERROW>), dim3(nblocks), dim3(NT), 0, stream,
+                     a, geo);
+  return hipGetLastError();
+}
+
+template <int DK, int CS>
+hipError_t launch_w1_mode(const SeqArgs& a, hipStream_t stream) {
+  const bool perrow = a.beta_kind == 2;
+  if (perrow) {
+    // per-channel scalars are per row: at most 32-step sub-chunks (LDS budget)
+    constexpr int CSP = CS > 32 ? 32 : CS;
+    return a.regression ? launch_w1<DK, CSP, true, true>(a, stream)
+                        : launch_w1<DK, CSP, false, true>(a, stream);
+  }
+  return a.regression ? launch_w1<DK, CS, true, false>(a, stream)
+                      : launch_w1<DK, CS, false, false>(a, stream);
+}
+
+}  // namespace
+
+// Window-1 chunk form; cs is the sub-chunk length (16, 32 or 64; 32 at most for
+// dk = 128).
+hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs) {
+  switch (a.dk) {
+    case 16:
+      if (cs == 16) return launch_w1_mode<16, 16>(a, stream);
+      if (cs == 32) return launch_w1_mode<16, 32>(a, stream);
+      return launch_w1_mode<16, 64>(a, stream);
+    case 32:
+      if (cs == 16) return launch_w1_mode<32, 16>(a, stream);
+      if (cs == 32) return launch_w1_mode<32, 32>(a, stream);
+      return launch_w1_mode<32, 64>(a, stream);
+    case 64:
+      if (cs == 16) return launch_w1_mode<64, 16>(a, stream);
+      if (cs == 32) return launch_w1_mode<64, 32>(a, stream);
+      return launch_w1_mode<64, 64>(a, stream);
+    case 128:
+      if (cs == 16) return launch_w1_mode<128, 16>(a, stream);
+      return launch_w1_mode<128, 32>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace falcon

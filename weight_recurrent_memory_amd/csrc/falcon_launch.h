@@ -44,6 +44,8 @@ struct DecodeArgs {
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
+// window-1 chunk form (falcon_chunk_w1.hip); cs = sub-chunk length
+hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace falcon

@@ -1,0 +1,100 @@
+// falcon_mma.h - MFMA tile helpers of the chunk kernels: split-bf16 operand
+// fragments and a 16x16 output tile product over a K range.
+//
+// Fragment convention (v_mfma_f32_16x16x32_bf16, wave64) and the split-bf16
+// scheme are described in falcon_device.h.  An operand "row" is K-contiguous in
+// LDS; fa(r, k) / fb(r, k) return the 8-wide fragment of row r at k.
+#pragma once
+#include "falcon_device.h"
+
+namespace falcon {
+
+struct HL {
+  bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ HL hl_zero() {
+  HL z;
+  z.hi = zero_frag();
+  z.lo = zero_frag();
+  return z;
+}
+__device__ __forceinline__ HL hl_pair(const uint16_t* hi, const uint16_t* lo) {
+  HL f;
+  f.hi = frag_bf16(hi);
+  f.lo = frag_bf16(lo);
+  return f;
+}
+__device__ __forceinline__ HL hl_bf16(const uint16_t* p) {
+  HL f;
+  f.hi = frag_bf16(p);
+  f.lo = zero_frag();
+  return f;
+}
+__device__ __forceinline__ HL hl_f32(const float* p) {
+  HL f;
+  frag_split(p, f.hi, f.lo);
+  return f;
+}
+// 8 fp32 values (in registers) -> split fragment
+__device__ __forceinline__ HL hl_vals(const float* v) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
+  }
+  uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  uint4 Lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  HL f;
+  f.hi = __builtin_bit_cast(bf16x8, H);
+  f.lo = __builtin_bit_cast(bf16x8, Lo);
+  return f;
+}
+
+__device__ __forceinline__ void split1(float x, uint16_t& h, uint16_t& l) {
+  const uint32_t hb = f32_to_bf16_bits(x);
+  h = (uint16_t)hb;
+  l = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hb << 16));
+}
+
+// 4 consecutive fp32 -> 4 hi and 4 lo bf16 stored with one 8-byte write each.
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float* v) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = f32_to_bf16_bits(v[e]);
+    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
+  }
+  *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// acc[m][n] += sum_{k<K} A[m][k] B[n][k] for one 16x16 tile; fa(r, k) / fb(r, k)
+// return the fragment of operand row r (0..15) at k (multiple of 8).  AX / BX:
+// the operand is an exact bf16 value (its lo part is zero; pass skipped).
+template <bool AX, bool BX, class FA, class FB>
+__device__ __forceinline__ floatx4 mma_nt(floatx4 acc, int K, FA&& fa, FB&& fb) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int kq = (lane >> 4) * 8;
+  const bool whole = (K & 31) == 0;      // every lane's k slot is in range
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const int k = k0 + kq;
+    const bool in = whole || k < K;
+    const HL A = in ? fa(r, k) : hl_zero();
+    const HL Bv = in ? fb(r, k) : hl_zero();
+    acc = mfma16(A.hi, Bv.hi, acc);
+    if (!BX) acc = mfma16(A.hi, Bv.lo, acc);
+    if (!AX) acc = mfma16(A.lo, Bv.hi, acc);
+  }
+  return acc;
+}
+
+}  // namespace falcon
