@@ -33,7 +33,8 @@ METRIC = "Falcon chunk fwd tokens/s + MFMA util; decode-step state HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic.json")
-CHUNK_SOURCE = os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", "falcon_chunk.hip")
+CHUNK_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
+                 for f in ("falcon_chunk_w1.hip", "falcon_mma.h", "falcon_device.h")]
 
 
 def algorithmic_bytes(batch, heads, L, dk, dv, beta_channel=False, elem=2):
@@ -65,9 +66,12 @@ def model_flops_per_head_token(regression, d, C, B=1):
     return f
 
 
-def _source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic():
@@ -78,7 +82,7 @@ def _traffic():
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != _source_hash(CHUNK_SOURCE):
+    if rec.get("source_sha256_16") != _source_hash(CHUNK_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 
@@ -165,7 +169,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": traffic,
-                         "kernel": "chunk_kernel<64,64,true,false>",
+                         "kernel": "chunk_w1_kernel<64,64,true,false>",
                          "algorithmic_bytes_per_launch": h["bytes"],
                          "avg_launch_us": sec * 1e6},
             "mfma_model_util": {"model_tflops": mflops / sec / 1e12,
