@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
   // ---------------- prefetch registers ----------------
   uint4 pk[KV], pq[QV], py[YV];
   float pb[(PERROW ? RW : 1) * CS / NT + 1];
-  auto prefetch = [&](long t0) {
+  auto prefetch = [&](long t0) __attribute__((always_inline)) {
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
 #pragma unroll
     for (int v = 0; v < KV; ++v) {

@@ -71,9 +71,9 @@ struct W1Lds {
   uint16_t SAhi[(REG && !PERROW) ? NB : 1][16][CS + 8];   // [T_bb | -M_b0 | ...]
   uint16_t SAlo[(REG && !PERROW) ? NB : 1][16][CS + 8];
   float RP[(REG && PERROW) ? RW : 1][CS + 4];              // per-row right-hand sides
-  float gam[SCB][SR][CS];
-  float gm1[SCB][SR][CS];
-  float zeta[SCB][SR][CS];
+  alignas(16) float gam[SCB][SR][CS];
+  alignas(16) float gm1[SCB][SR][CS];
+  alignas(16) float zeta[SCB][SR][CS];
 };
 
 struct W1Geom {
@@ -88,8 +88,6 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
   constexpr int NB = CS / 16, NTT = CS / 16, NKT = DK / 16, VPR = DK / 8;
   constexpr int KV = (CS * VPR + NT - 1) / NT;
   constexpr int YV = (CS * (RW / 8) + NT - 1) / NT;
-  constexpr int NBT = (PERROW ? RW : 1) * CS;
-  constexpr int BV = (NBT + NT - 1) / NT;
   __shared__ __align__(16) SM sm;
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
@@ -124,9 +122,12 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
   const int nchunks = geo.nchunks;
 
   // ---------------- prefetch registers (one chunk ahead of the commit) ----------------
+  // Loads land in registers that nothing reads before the next commit, so the
+  // compiler issues them without waiting (no widening or merging after a load).
   uint4 pk[KV], pq[KV], py[YV];
-  uint32_t pb[BV];
-  auto prefetch = [&](int cidx) {
+  uint4 pbc[PERROW ? YV : 1];     // per-channel beta, same tiling as v
+  uint32_t pbt = 0;               // per-token beta of step tid (tid < CS)
+  auto prefetch = [&](int cidx) __attribute__((always_inline)) {
     const long t0 = (long)cidx * CS;
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
 #pragma unroll
@@ -152,21 +153,22 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         val = *reinterpret_cast<const uint4*>(vg + v_base + (t0 + t) * dv + i0 + h * 8);
       py[v] = val;
     }
+    if (PERROW) {
 #pragma unroll
-    for (int v = 0; v < BV; ++v) {
-      const int idx = tid + v * NT;
-      uint32_t bits = 0;
-      if (idx < NBT && a.beta_kind != 0) {
-        const int i = idx / CS, t = idx % CS;
-        if (t < c) {
-          if (a.beta_kind == 1) bits = bg[(long)chain * L + t0 + t];
-          else if (i0 + i < dv) bits = bg[((long)chain * L + t0 + t) * dv + i0 + i];
-        }
+      for (int v = 0; v < YV; ++v) {
+        const int idx = tid + v * NT;
+        const int t = idx / (RW / 8), h = idx % (RW / 8);
+        uint4 val = {0u, 0u, 0u, 0u};
+        if (idx < CS * (RW / 8) && t < c && i0 + h * 8 < dv)
+          val = *reinterpret_cast<const uint4*>(bg + ((long)chain * L + t0 + t) * dv + i0 + h * 8);
+        pbc[v] = val;
       }
-      pb[v] = bits;
+    } else {
+      pbt = 0;
+      if (a.beta_kind == 1 && tid < c) pbt = (uint32_t)bg[(long)chain * L + t0 + tid];
     }
   };
-  auto commit = [&](int s) {
+  auto commit = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
       const int idx = tid + v * NT;
@@ -201,20 +203,30 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         }
       }
     }
+    if (PERROW) {
 #pragma unroll
-    for (int v = 0; v < BV; ++v) {
-      const int idx = tid + v * NT;
-      if (idx < NBT) {
-        if (PERROW) sm.BT[s][idx / CS][idx % CS] = (uint16_t)pb[v];
-        else sm.beta[s][idx] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)pb[v]);
+      for (int v = 0; v < YV; ++v) {
+        const int idx = tid + v * NT;
+        if (idx < CS * (RW / 8)) {
+          const int t = idx / (RW / 8), h = idx % (RW / 8);
+          const uint4 val = pbc[v];
+          const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sm.BT[s][h * 8 + 2 * e][t] = (uint16_t)(w4[e] & 0xFFFFu);
+            sm.BT[s][h * 8 + 2 * e + 1][t] = (uint16_t)(w4[e] >> 16);
+          }
+        }
       }
+    } else if (tid < CS) {
+      sm.beta[s][tid] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)pbt);
     }
   };
 
   // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
   // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
   // One wave per row of scalars; lane = step; prefix product by a wave scan.
-  auto scalars = [&](int s, int cidx, int dst, int row, int wv) {
+  auto scalars = [&](int s, int cidx, int dst, int row, int wv) __attribute__((always_inline)) {
     (void)wv;
     const long t0 = (long)cidx * CS;
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
@@ -243,41 +255,47 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
 
   // Gram (regression) and q.x tiles of slot s: lower triangle of 16x16 tiles.
   constexpr int NLT = NTT * (NTT + 1) / 2;
-  auto gram_tile = [&](int s, int tt) {
+  auto gram_tile = [&](int s, int tt) __attribute__((always_inline)) {
     int ti = 0;
     while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
     const int tj = tt - ti * (ti + 1) / 2;
+    // output rows = the index that is contiguous in GT, so a lane stores a float4:
+    // shared eta keeps Gs^T[u'][u] (rows u = tile ti), per-channel Gs[u][u'] (rows u' = tj)
+    const int ra = PERROW ? tj : ti, rb2 = PERROW ? ti : tj;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mma_nt<true, true>(acc, DK,
-        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * ti + r][k]); },
-        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * tj + r][k]); });
-    const int col = 16 * tj + lr;
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * ra + r][k]); },
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * rb2 + r][k]); });
+    const int col = 16 * rb2 + lr;           // the other index
+    float gv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * ti + 4 * lg + e;
-      const float gv = (col < row) ? acc[e] : 0.0f;
-      if (PERROW) sm.GT[row][col] = gv;    // Gs[u][u']
-      else sm.GT[col][row] = gv;           // Gs^T[u'][u]
+      const int row = 16 * ra + 4 * lg + e;
+      const int u = PERROW ? col : row, u2 = PERROW ? row : col;   // Gs[u][u'], u' < u
+      gv[e] = (u2 < u) ? acc[e] : 0.0f;
     }
+    *reinterpret_cast<float4*>(&sm.GT[col][16 * ra + 4 * lg]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
   };
-  auto qx_tile = [&](int s, int tt) {
+  auto qx_tile = [&](int s, int tt) __attribute__((always_inline)) {
     int ti = 0;
     while ((ti + 1) * (ti + 2) / 2 <= tt) ++ti;
-    const int tj = tt - ti * (ti + 1) / 2;
+    const int tj = tt - ti * (ti + 1) / 2;     // step tile ti, key tile tj <= ti
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mma_nt<true, true>(acc, DK,
-        [&](int r, int k) { return hl_bf16(&sm.Q[s][16 * ti + r][k]); },
-        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * tj + r][k]); });
-    const int col = 16 * tj + lr;
+        [&](int r, int k) { return hl_bf16(&sm.slot[s].X[16 * tj + r][k]); },
+        [&](int r, int k) { return hl_bf16(&sm.Q[s][16 * ti + r][k]); });
+    const int t = 16 * ti + lr;
+    float pv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * ti + 4 * lg + e;
-      split1((col <= row) ? acc[e] : 0.0f, sm.Phi[s][row][col], sm.Plo[s][row][col]);
+      const int u = 16 * tj + 4 * lg + e;
+      pv[e] = (u <= t) ? acc[e] : 0.0f;
     }
+    store_split4(&sm.Phi[s][t][16 * tj + 4 * lg], &sm.Plo[s][t][16 * tj + 4 * lg], pv);
   };
   // 16x16 diagonal-block inverses T_bb = Gamma_- (I + Gs D)^-1 Gamma_-^{-1},
   // D = diag(zeta_m g_{m-1}); one wave, lane = 16 b + column.
-  auto diag_inverse = [&](int sc) {
+  auto diag_inverse = [&](int sc) __attribute__((always_inline)) {
     const int bb = (lane >> 4) < NB ? (lane >> 4) : 0;
     const int cc = lane & 15;
     const int u0 = 16 * bb;
@@ -324,6 +342,12 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
   if (REG && !PERROW && wave == NW - 1) diag_inverse(0);
   __syncthreads();
 
+  // The readout of chunk c is stored during phase 1 of chunk c+1, after that
+  // phase's commit and prefetch: global stores share the in-order
+  // vector-memory counter with the loads, so a store issued shortly before a
+  // commit would make the commit wait for the store's completion.
+  float4 opend = make_float4(0.f, 0.f, 0.f, 0.f);
+  float* optr = nullptr;
   for (int ci = 0; ci < nchunks; ++ci) {
     const int cur = ci & 1, nxt = cur ^ 1;
     const bool has_next = ci + 1 < nchunks;
@@ -332,19 +356,28 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     const int sc = PERROW ? 0 : cur;          // scalar buffer of chunk ci
 
     // ================= phase 1 =================
-    if (has_next) {
-      commit(nxt);
-      if (ci + 2 < nchunks) prefetch(ci + 2);
-    }
+    if (has_next) commit(nxt);
+    if (has_next && ci + 2 < nchunks) prefetch(ci + 2);
+    if (optr) *reinterpret_cast<float4*>(optr) = opend;
+    optr = nullptr;
     // keys of chunk ci transposed (carry operand)
-    for (int idx = tid; idx < DK * (CS / 8); idx += NT) {
-      const int kk = idx % DK, j8 = idx / DK;
-      uint32_t w[4];
+    // (8 keys x 4 columns per thread: 8-byte reads, 16-byte writes)
+    for (int idx = tid; idx < (DK / 4) * (CS / 8); idx += NT) {
+      const int c4 = idx % (DK / 4), j8 = idx / (DK / 4);
+      uint2 rw[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)sm.slot[cur].X[8 * j8 + 2 * e][kk] |
-               ((uint32_t)sm.slot[cur].X[8 * j8 + 2 * e + 1][kk] << 16);
-      *reinterpret_cast<uint4*>(&sm.XT[kk][8 * j8]) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int e = 0; e < 8; ++e) rw[e] = *reinterpret_cast<const uint2*>(&sm.slot[cur].X[8 * j8 + e][4 * c4]);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t a0 = (cc < 2) ? rw[2 * e].x : rw[2 * e].y;
+          const uint32_t a1 = (cc < 2) ? rw[2 * e + 1].x : rw[2 * e + 1].y;
+          w[e] = (cc & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+        }
+        *reinterpret_cast<uint4*>(&sm.XT[4 * c4 + cc][8 * j8]) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
     // S0 q_t tiles stay in the registers of the wave that reads them out in phase 3
     constexpr int NQ = NRB * NTT;
@@ -364,32 +397,32 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
           const int rbk = task / NTT, tj = task % NTT;
           if (rbk >= nrb) continue;
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mma_nt<false, true>(acc, DK,
-              [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); },
-              [&](int r, int k) { return hl_bf16(&sm.slot[cur].X[16 * tj + r][k]); });
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.XS[16 * rbk + 4 * lg + e][16 * tj + lr] = acc[e];
+          acc = mma_nt<true, false>(acc, DK,
+              [&](int r, int k) { return hl_bf16(&sm.slot[cur].X[16 * tj + r][k]); },
+              [&](int r, int k) { return hl_pair(&sm.Shi[16 * rbk + r][k], &sm.Slo[16 * rbk + r][k]); });
+          *reinterpret_cast<float4*>(&sm.XS[16 * rbk + lr][16 * tj + 4 * lg]) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
         } else {
           // M_bj = T_bb diag(g_{t-1})_b Gs_bj (negated next to T_bb)
           const int mt = task - NXS;
           int bb = 1;
           while (bb * (bb + 1) / 2 <= mt) ++bb;
           const int jb = mt - bb * (bb - 1) / 2;
+          // computed transposed: M^T[u'][r] = sum_m g_{m-1} Gs[m][u'] T_bb[r][m]
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
           acc = mma_nt<false, false>(acc, 16,
-              [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); },
               [&](int r, int k) {
-                float v[8];
-                const float* gp = &sm.GT[16 * jb + r][16 * bb + k];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = gp[e] * sm.gm1[sc][0][16 * bb + k + e];
+                const float4 g0 = *reinterpret_cast<const float4*>(&sm.GT[16 * jb + r][16 * bb + k]);
+                const float4 g1 = *reinterpret_cast<const float4*>(&sm.GT[16 * jb + r][16 * bb + k + 4]);
+                const float4 m0 = *reinterpret_cast<const float4*>(&sm.gm1[sc][0][16 * bb + k]);
+                const float4 m1 = *reinterpret_cast<const float4*>(&sm.gm1[sc][0][16 * bb + k + 4]);
+                const float v[8] = {g0.x * m0.x, g0.y * m0.y, g0.z * m0.z, g0.w * m0.w,
+                                    g1.x * m1.x, g1.y * m1.y, g1.z * m1.z, g1.w * m1.w};
                 return hl_vals(v);
-              });
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * lg + e;
-            split1(-acc[e], sm.SAhi[bb][r][16 * (jb + 1) + lr], sm.SAlo[bb][r][16 * (jb + 1) + lr]);
-          }
+              },
+              [&](int r, int k) { return hl_pair(&sm.SAhi[bb][r][k], &sm.SAlo[bb][r][k]); });
+          const float mv[4] = {-acc[0], -acc[1], -acc[2], -acc[3]};
+          store_split4(&sm.SAhi[bb][lr][16 * (jb + 1) + 4 * lg], &sm.SAlo[bb][lr][16 * (jb + 1) + 4 * lg], mv);
         }
       }
     }
@@ -416,20 +449,22 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
                     const uint32_t yw[4] = {yb.x, yb.y, yb.z, yb.w};
                     const float4 x0 = *reinterpret_cast<const float4*>(&sm.XS[ib + r][u]);
                     const float4 x1 = *reinterpret_cast<const float4*>(&sm.XS[ib + r][u + 4]);
+                    const float4 m0 = *reinterpret_cast<const float4*>(&sm.gm1[sc][0][u]);
+                    const float4 m1 = *reinterpret_cast<const float4*>(&sm.gm1[sc][0][u + 4]);
                     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
                     float v[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                       const uint16_t yv = (e & 1) ? (uint16_t)(yw[e >> 1] >> 16) : (uint16_t)(yw[e >> 1] & 0xFFFFu);
-                      v[e] = bf16_to_f32(yv) - sm.gm1[sc][0][u + e] * xs[e];
+                      v[e] = bf16_to_f32(yv) - gm[e] * xs[e];
                     }
                     return hl_vals(v);
                   }
                   return hl_pair(&zt->hi[ib + r][k - 16], &zt->lo[ib + r][k - 16]);
                 });
-            float z[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = sm.zeta[sc][0][16 * bb + 4 * lg + e] * acc[e];
+            const float4 zf = *reinterpret_cast<const float4*>(&sm.zeta[sc][0][16 * bb + 4 * lg]);
+            const float z[4] = {zf.x * acc[0], zf.y * acc[1], zf.z * acc[2], zf.w * acc[3]};
             store_split4(&zt->hi[ib + lr][16 * bb + 4 * lg], &zt->lo[ib + lr][16 * bb + 4 * lg], z);
             wave_sync();
           }
@@ -512,8 +547,8 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
           float ov[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = sm.gam[sc][PERROW ? ib + 4 * lg + e : 0][t] * acc[e];
-          *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + ib + 4 * lg) =
-              make_float4(ov[0], ov[1], ov[2], ov[3]);
+          opend = make_float4(ov[0], ov[1], ov[2], ov[3]);
+          optr = a.o + v_base + (t0 + t) * dv + i0 + ib + 4 * lg;
         }
       }
     }
@@ -525,17 +560,17 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         if (rbk >= nrb) continue;
         const int ib = 16 * rbk;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma_nt<false, true>(acc, CS,
-            [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); },
-            [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); });
-        const int kk = 16 * tk + lr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = ib + 4 * lg + e;
-          const float s = sm.gam[sc][PERROW ? i : 0][CS - 1] * (sm.S[i][kk] + acc[e]);
-          sm.S[i][kk] = s;
-          split1(s, sm.Shi[i][kk], sm.Slo[i][kk]);
-        }
+        acc = mma_nt<true, false>(acc, CS,
+            [&](int r, int k) { return hl_bf16(&sm.XT[16 * tk + r][k]); },
+            [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); });
+        // lane holds S_new[i][k..k+3] for i = ib + lr, k = 16 tk + 4 lg
+        const int i = ib + lr, k0 = 16 * tk + 4 * lg;
+        const float gC = sm.gam[sc][PERROW ? i : 0][CS - 1];
+        const float4 so = *reinterpret_cast<const float4*>(&sm.S[i][k0]);
+        const float sn[4] = {gC * (so.x + acc[0]), gC * (so.y + acc[1]), gC * (so.z + acc[2]),
+                             gC * (so.w + acc[3])};
+        *reinterpret_cast<float4*>(&sm.S[i][k0]) = make_float4(sn[0], sn[1], sn[2], sn[3]);
+        store_split4(&sm.Shi[i][k0], &sm.Slo[i][k0], sn);
       }
     }
     if (has_next) {
@@ -546,6 +581,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     }
     __syncthreads();
   }
+  if (optr) *reinterpret_cast<float4*>(optr) = opend;
   if (a.S_out) {
     for (int idx = tid; idx < RW * DK; idx += NT) {
       const int i = idx / DK, kk = idx % DK;

@@ -79,22 +79,32 @@ __device__ __forceinline__ void wave_sync() {
 // acc[m][n] += sum_{k<K} A[m][k] B[n][k] for one 16x16 tile; fa(r, k) / fb(r, k)
 // return the fragment of operand row r (0..15) at k (multiple of 8).  AX / BX:
 // the operand is an exact bf16 value (its lo part is zero; pass skipped).
+// The split passes (and, for exact operands, alternate k steps) accumulate into
+// independent registers so consecutive MFMAs do not wait on each other; the
+// partial sums are added at the end (fixed order, deterministic).
 template <bool AX, bool BX, class FA, class FB>
 __device__ __forceinline__ floatx4 mma_nt(floatx4 acc, int K, FA&& fa, FB&& fb) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int kq = (lane >> 4) * 8;
   const bool whole = (K & 31) == 0;      // every lane's k slot is in range
-  for (int k0 = 0; k0 < K; k0 += 32) {
+  floatx4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
+  int step = 0;
+  for (int k0 = 0; k0 < K; k0 += 32, ++step) {
     const int k = k0 + kq;
     const bool in = whole || k < K;
     const HL A = in ? fa(r, k) : hl_zero();
     const HL Bv = in ? fb(r, k) : hl_zero();
-    acc = mfma16(A.hi, Bv.hi, acc);
-    if (!BX) acc = mfma16(A.hi, Bv.lo, acc);
-    if (!AX) acc = mfma16(A.lo, Bv.hi, acc);
+    if (AX && BX) {
+      if (step & 1) c1 = mfma16(A.hi, Bv.hi, c1);
+      else acc = mfma16(A.hi, Bv.hi, acc);
+    } else {
+      acc = mfma16(A.hi, Bv.hi, acc);
+      if (!BX) c1 = mfma16(A.hi, Bv.lo, c1);
+      if (!AX) c2 = mfma16(A.lo, Bv.hi, c2);
+    }
   }
-  return acc;
+  return acc + c1 + c2;
 }
 
 }  // namespace falcon
