@@ -30,11 +30,25 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Two fp32 -> one packed bf16 pair (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const floatx2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Split-bf16 of a pair: h = bf16(a) | bf16(b) << 16, l = the packed remainders.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& h, uint32_t& l) {
+  h = pack_bf16x2(a, b);
+  l = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ float bf16_round(float x) {
@@ -62,18 +76,13 @@ __device__ __forceinline__ bf16x8 frag_bf16(const uint16_t* p) {
 
 // 8 consecutive fp32 values (16-byte aligned) split into hi and lo bf16 parts.
 __device__ __forceinline__ void frag_split(const float* p, bf16x8& hi, bf16x8& lo) {
-  float4 a = *reinterpret_cast<const float4*>(p);
-  float4 b = *reinterpret_cast<const float4*>(p + 4);
-  float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    float r = v[e] - __uint_as_float(h[e] << 16);
-    l[e] = f32_to_bf16_bits(r);
-  }
-  uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  uint4 Lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  uint4 H, Lo;
+  split_pair(a.x, a.y, H.x, Lo.x);
+  split_pair(a.z, a.w, H.y, Lo.y);
+  split_pair(b.x, b.y, H.z, Lo.z);
+  split_pair(b.z, b.w, H.w, Lo.w);
   hi = __builtin_bit_cast(bf16x8, H);
   lo = __builtin_bit_cast(bf16x8, Lo);
 }

@@ -38,14 +38,11 @@ __device__ __forceinline__ HL hl_f32(const float* p) {
 }
 // 8 fp32 values (in registers) -> split fragment
 __device__ __forceinline__ HL hl_vals(const float* v) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
-  }
-  uint4 H = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  uint4 Lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+  uint4 H, Lo;
+  split_pair(v[0], v[1], H.x, Lo.x);
+  split_pair(v[2], v[3], H.y, Lo.y);
+  split_pair(v[4], v[5], H.z, Lo.z);
+  split_pair(v[6], v[7], H.w, Lo.w);
   HL f;
   f.hi = __builtin_bit_cast(bf16x8, H);
   f.lo = __builtin_bit_cast(bf16x8, Lo);
@@ -60,14 +57,11 @@ __device__ __forceinline__ void split1(float x, uint16_t& h, uint16_t& l) {
 
 // 4 consecutive fp32 -> 4 hi and 4 lo bf16 stored with one 8-byte write each.
 __device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, const float* v) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = f32_to_bf16_bits(v[e]);
-    l[e] = f32_to_bf16_bits(v[e] - __uint_as_float(h[e] << 16));
-  }
-  *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  uint2 H, Lo;
+  split_pair(v[0], v[1], H.x, Lo.x);
+  split_pair(v[2], v[3], H.y, Lo.y);
+  *reinterpret_cast<uint2*>(hi) = H;
+  *reinterpret_cast<uint2*>(lo) = Lo;
 }
 
 __device__ __forceinline__ void wave_sync() {
