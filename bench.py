@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic.json")
 CHUNK_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
-                 for f in ("falcon_chunk_w1.hip", "falcon_mma.h", "falcon_device.h")]
+                 for f in ("falcon_chunk_wy.hip", "falcon_mma.h", "falcon_device.h")]
 
 
 def algorithmic_bytes(batch, heads, L, dk, dv, beta_channel=False, elem=2):
@@ -156,7 +156,7 @@ def main():
         sec = h["sec"]
         value = h["tokens"] / sec
         achieved = h["bytes"] / sec / 1e9
-        mflops = model_flops_per_head_token(True, 64, 64) * h["head_tokens"]
+        mflops = model_flops_per_head_token(True, 64, 32) * h["head_tokens"]
         traffic = _traffic()
         out.update({
             "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -164,12 +164,13 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": head_name, "variant": "falcon1", "batch": 8, "heads": 12,
-                       "seq_len": 2048, "dk": 64, "dv": 64, "chunk": 64, "beta": 0.5,
+                       "seq_len": 2048, "dk": 64, "dv": 64, "chunk": 64, "kernel_chunk": 32,
+                       "beta": 0.5,
                        "lambda": 0.01, "eps": 1e-6, "parallelism": "single-gpu"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": traffic,
-                         "kernel": "chunk_w1_kernel<64,64,true,false>",
+                         "kernel": "chunk_wy_kernel<64,true>",
                          "algorithmic_bytes_per_launch": h["bytes"],
                          "avg_launch_us": sec * 1e6},
             "mfma_model_util": {"model_tflops": mflops / sec / 1e12,

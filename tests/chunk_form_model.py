@@ -118,3 +118,84 @@ def chunk_forward(regression, per_row, q, k, v, *, beta, lam, eps, window, chunk
         o[t0:t0 + c] = g * (Q @ S.T + Pt @ Z)
         S = g[-1][:, None] * (S + F.T @ X)
     return o, S
+
+
+def chunk_forward_wy(regression, q, k, v, *, beta, lam, eps, chunk, beta_t=None, k_prev=None,
+                     S0=None, blk=16):
+    """Window 1, gains shared by the value rows (scalar or per token): the form in
+    which every state-independent factor of a chunk is formed ahead of the state.
+
+    With omega_t = zeta_t g_{t-1} (= eta_t / a_t) the chunk's equations become
+      (I + diag(omega) L) z = diag(omega) (y / g_{t-1} - S0 x_t),  L = strictly lower Gram,
+    so with N = (I + diag(omega) L)^-1 (unit lower triangular, the same for every
+    value row) and Nw = N diag(omega):
+      z = Ut - S0 Wt,  Ut[:, t] = sum_s Nw[t, s] y_s / g_{s-1},  Wt[:, t] = sum_s Nw[t, s] x_s
+    N is built the way the kernel builds it: 16x16 diagonal blocks by forward
+    substitution, then each block column downwards,
+      N_bj = -T_bb sum_{m=j}^{b-1} (diag(omega) L)_bm N_mj.
+    Readout and carry are those of chunk_forward; the inner-product family has
+    z = zeta * y.
+    """
+    L_, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else S0.astype(np.float64).copy()
+    o = np.zeros((L_, dv))
+    for t0 in range(0, L_, chunk):
+        C = chunk                               # padded to the full chunk, like the kernel
+        c = min(chunk, L_ - t0)
+        X = np.zeros((C, dk))
+        Y = np.zeros((C, dv))
+        Q = np.zeros((C, dk))
+        for t in range(c):
+            g = t0 + t
+            if g >= 1:
+                X[t] = k[g - 1]
+            elif k_prev is not None:
+                X[t] = k_prev
+            Y[t] = v[g]
+            Q[t] = q[g]
+        eta = np.zeros(C)
+        a = np.ones(C)
+        for t in range(c):
+            if t0 + t == 0 and k_prev is None:
+                continue
+            b = beta if beta_t is None else float(beta_t[t0 + t])
+            eta[t] = b / (eps + X[t] @ X[t])
+            a[t] = 1.0 - eta[t] * lam
+        g = np.cumprod(a)
+        gm1 = np.concatenate([[1.0], g[:-1]])
+        zeta = eta / g
+        omega = zeta * gm1
+        if regression:
+            G = X @ X.T
+            M = omega[:, None] * np.tril(G, -1)
+            N = np.zeros((C, C))
+            nb = C // blk
+            T = []
+            for bb in range(nb):                 # diagonal blocks: forward substitution
+                u0 = bb * blk
+                Tb = np.zeros((blk, blk))
+                for cc in range(blk):
+                    col = np.zeros(blk)
+                    for r in range(blk):
+                        col[r] = (1.0 if r == cc else 0.0) - M[u0 + r, u0:u0 + r] @ col[:r]
+                    Tb[:, cc] = col
+                T.append(Tb)
+                N[u0:u0 + blk, u0:u0 + blk] = Tb
+            for j in range(nb - 1):              # block columns, downwards
+                for bb in range(j + 1, nb):
+                    r0, c0 = bb * blk, j * blk
+                    X1 = sum(M[r0:r0 + blk, m * blk:(m + 1) * blk] @ N[m * blk:(m + 1) * blk, c0:c0 + blk]
+                             for m in range(j, bb))
+                    N[r0:r0 + blk, c0:c0 + blk] = -T[bb] @ X1
+            Nw = N * omega[None, :]
+            Ut = (Y / gm1[:, None]).T @ Nw.T     # [dv, C]
+            Wt = X.T @ Nw.T                      # [dk, C]
+            Z = Ut - S @ Wt                      # [dv, C]
+        else:
+            Z = (zeta[:, None] * Y).T
+        P = np.tril(Q @ X.T)                     # [C, C], s <= t
+        O = (S @ Q.T + Z @ P.T) * g[None, :]     # [dv, C]
+        o[t0:t0 + c] = O.T[:c]
+        S = g[-1] * (S + Z @ X)
+    return o, S

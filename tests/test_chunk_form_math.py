@@ -8,7 +8,7 @@ import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import seq_inputs
-from chunk_form_model import chunk_forward
+from chunk_form_model import chunk_forward, chunk_forward_wy
 
 pytestmark = pytest.mark.cpu
 
@@ -37,3 +37,21 @@ def test_chunk_form_equals_recurrence(variant, chunk, carried):
                              S0=None if not carried else inp["S0"][0, 0])
         np.testing.assert_allclose(o, o_ref[0, 0], rtol=1e-9, atol=1e-10)
         np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-9, atol=1e-10)
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_1, fo.FALCON_1A])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("carried", [False, True])
+def test_precomputed_inverse_form_equals_recurrence(variant, chunk, carried):
+    inp = seq_inputs(1, 1, 150, 8, 5, seed=300 + variant + chunk, dtype="bf16",
+                     beta_per_token=True, with_k_prev=carried, with_S0=carried, s_std=0.3)
+    kw = dict(beta=None, lam=0.02, eps=1e-6, window=1, beta_t=inp["beta_t"],
+              k_prev=inp.get("k_prev"), S0=inp.get("S0"))
+    o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], **kw)
+    o, S = chunk_forward_wy(fo.is_regression(variant), inp["q"][0, 0], inp["k"][0, 0],
+                            inp["v"][0, 0], beta=None, lam=0.02, eps=1e-6, chunk=chunk,
+                            beta_t=inp["beta_t"][0, 0],
+                            k_prev=None if not carried else inp["k_prev"][0, 0],
+                            S0=None if not carried else inp["S0"][0, 0])
+    np.testing.assert_allclose(o, o_ref[0, 0], rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-9, atol=1e-10)

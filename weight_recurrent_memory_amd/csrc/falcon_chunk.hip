@@ -697,6 +697,7 @@ int chunk_sub_length(int chunk, int window, int dk) {
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
+  if (chunk_wy_supported(a)) return launch_chunk_wy(a, stream);
   if (a.window == 1) return launch_chunk_w1(a, stream, cs);
   switch (a.dk) {
     case 16: return launch_shape<16>(a, stream, cs);

@@ -44,8 +44,12 @@ struct DecodeArgs {
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
-// window-1 chunk form (falcon_chunk_w1.hip); cs = sub-chunk length
+// window-1 chunk form, per-channel gains (falcon_chunk_w1.hip); cs = sub-chunk length
 hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs);
+// window-1 chunk form, gains shared by the value rows, dk in {32, 64}
+// (falcon_chunk_wy.hip); 32-step chunks whatever the requested chunk
+bool chunk_wy_supported(const SeqArgs& a);
+hipError_t launch_chunk_wy(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace falcon
