@@ -47,7 +47,6 @@ constexpr int CS = 32;       // chunk length
 constexpr int RW = 32;       // value rows per workgroup
 constexpr int NW = 8;
 constexpr int NT = 64 * NW;
-constexpr int NPRE = NT - 128;   // threads of the preparation waves
 
 // position of index k in the fragment order (groups of 32)
 __device__ __forceinline__ int fpos(int k) {
@@ -67,8 +66,7 @@ struct WyLds {
   uint16_t Plo[2][CS][TR];
   uint16_t Whi[2][CS][XR];               // Wt^T[t][k], k in fragment order
   uint16_t Wlo[2][CS][XR];
-  uint16_t SAhi[2][2][16][TR];           // [T_00 | 0], [T_11 | -T_11 M_10], fragment order
-  uint16_t SAlo[2][2][16][TR];
+  float SA[2][2][16][CS + 8];            // [T_00 | 0], [T_11 | -T_11 M_10], fragment order
   float G[2][CS][CS + 8];                // Gram (whole 32 x 32)
   float Ut[2][RW][CS + 8];               // Ut[i][t]
   float beta[4][CS];                     // gains by chunk & 3
@@ -120,8 +118,6 @@ template <int DK, bool REG>
 __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   using SM = WyLds<DK>;
   constexpr int NKT = DK / 16, NKS = DK / 32, VPR = DK / 8;
-  constexpr int KV = (CS * VPR + NPRE - 1) / NPRE;    // uint4 of k (or q) per prep thread
-  constexpr int YV = (CS * (RW / 8) + NPRE - 1) / NPRE;
   static_assert(DK % 32 == 0 && DK <= 64, "dk in {32, 64}");
   __shared__ __align__(16) SM sm;
 
@@ -151,7 +147,6 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const int ptid = tid - 128;             // preparation-thread index (waves 2..7)
   const long L = a.seqlen;
   const long qk_base = (long)chain * L * DK;
   const long v_base = (long)chain * L * dv;
@@ -162,55 +157,77 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   };
 
   // ---------------- zero the fragment slots no stage writes ----------------
-  for (int idx = tid; idx < 2 * 2 * 16 * SM::TR; idx += NT) {
-    (&sm.SAhi[0][0][0][0])[idx] = 0;
-    (&sm.SAlo[0][0][0][0])[idx] = 0;
-  }
+  for (int idx = tid; idx < 2 * 2 * 16 * (CS + 8); idx += NT) (&sm.SA[0][0][0][0])[idx] = 0.0f;
   for (int idx = tid; idx < 2 * CS * SM::TR; idx += NT) {
     (&sm.Phi[0][0][0])[idx] = 0;
     (&sm.Plo[0][0][0])[idx] = 0;
   }
 
-  // ---------------- global loads, issued one iteration before their commit ----------------
-  uint4 pk[KV], pq[KV], py[YV];
-  uint32_t pbt = 0;
-  auto prefetch_k = [&](int j) __attribute__((always_inline)) {   // keys (and beta) of chunk j
-    const long t0 = (long)j * CS;
-    const int c = steps(j);
-#pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int idx = ptid + v * NPRE;
-      const int t = idx / VPR, kv = idx % VPR;
-      uint4 kval = {0u, 0u, 0u, 0u};
-      if (idx < CS * VPR && t < c) {
-        const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
-        if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
-        else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
-      }
-      pk[v] = kval;
-    }
-    pbt = 0;
-    if (a.beta_kind == 1 && ptid < c) pbt = (uint32_t)bg[(long)chain * L + t0 + ptid];
+  // ---------------- global loads and their commits to LDS ----------------
+  // Waves 2..5 move keys and queries (one 16-byte piece of a row per thread),
+  // waves 6..7 values and gains.  A load is issued one iteration before its
+  // commit.
+  constexpr int KQ = (CS * VPR + 255) / 256;
+  struct PSet {
+    uint4 k[KQ], q[KQ], v, v2;
+    uint32_t b;
   };
-  auto prefetch_qv = [&](int j) __attribute__((always_inline)) {  // queries and values of chunk j
-    const long t0 = (long)j * CS;
-    const int c = steps(j);
+  const int kt_id = tid - 128;             // 0..255 on waves 2..5
+  const int vt_id = tid - 384;             // 0..127 on waves 6..7 (gains: wave 6)
+  const int vv_id = tid - 448;             // 0..63 on wave 7 (values)
+  // keys and gains of chunk jk, queries and values of chunk jq (out of range: skipped)
+  auto prefetch = [&](PSet& p, int jk, int jq) __attribute__((always_inline)) {
+    if (wave < 6) {
+      if (jk >= 0 && jk < nchunks) {
+        const long t0 = (long)jk * CS;
+        const int c = steps(jk);
 #pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int idx = ptid + v * NPRE;
-      const int t = idx / VPR, kv = idx % VPR;
-      uint4 qval = {0u, 0u, 0u, 0u};
-      if (idx < CS * VPR && t < c) qval = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
-      pq[v] = qval;
-    }
+        for (int u = 0; u < KQ; ++u) {
+          const int idx = kt_id + 256 * u;
+          const int t = idx / VPR, kv = idx % VPR;
+          uint4 kval = {0u, 0u, 0u, 0u};
+          if (idx < CS * VPR && t < c) {
+            const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
+            if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
+            else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
+          }
+          p.k[u] = kval;
+        }
+      }
+      if (jq >= 0 && jq < nchunks) {
+        const long t0 = (long)jq * CS;
+        const int c = steps(jq);
 #pragma unroll
-    for (int v = 0; v < YV; ++v) {
-      const int idx = ptid + v * NPRE;
-      const int t = idx / (RW / 8), h = idx % (RW / 8);
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (idx < CS * (RW / 8) && t < c && i0 + h * 8 < dv)
-        val = *reinterpret_cast<const uint4*>(vg + v_base + (t0 + t) * dv + i0 + h * 8);
-      py[v] = val;
+        for (int u = 0; u < KQ; ++u) {
+          const int idx = kt_id + 256 * u;
+          const int t = idx / VPR, kv = idx % VPR;
+          uint4 qval = {0u, 0u, 0u, 0u};
+          if (idx < CS * VPR && t < c) qval = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
+          p.q[u] = qval;
+        }
+      }
+    } else {
+      if (jq >= 0 && jq < nchunks && vv_id >= 0 && vv_id < (CS / 4) * (RW / 4)) {
+        // a 4 (steps) x 4 (value rows) block: t = t4.., i = i4..
+        const long t0 = (long)jq * CS;
+        const int c = steps(jq);
+        const int i4 = 4 * (vv_id % (RW / 4)), t4 = 4 * (vv_id / (RW / 4));
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint2 val = {0u, 0u};
+          if (t4 + e < c && i0 + i4 < dv) val = *reinterpret_cast<const uint2*>(vg + v_base + (t0 + t4 + e) * dv + i0 + i4);
+          w[2 * e] = val.x;
+          w[2 * e + 1] = val.y;
+        }
+        p.v = make_uint4(w[0], w[1], w[2], w[3]);
+        p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      if (jk >= 0 && jk < nchunks) {
+        const long t0 = (long)jk * CS;
+        p.b = 0;
+        if (a.beta_kind == 1 && vt_id < steps(jk)) p.b = (uint32_t)bg[(long)chain * L + t0 + vt_id];
+      }
     }
   };
   // 8 consecutive k (k0 % 8 == 0) -> two 4-groups at their fragment positions
@@ -218,48 +235,41 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     *reinterpret_cast<uint2*>(row + fpos(k0)) = make_uint2(val.x, val.y);
     *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
   };
-  auto commit_k = [&](int j) __attribute__((always_inline)) {
-    const int xb = j & 3, nb = j & 3;
+  auto commit = [&](const PSet& p, int jk, int jq) __attribute__((always_inline)) {
+    if (wave < 6) {
 #pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int idx = ptid + v * NPRE;
-      if (idx < CS * VPR) {
+      for (int u = 0; u < KQ; ++u) {
+        const int idx = kt_id + 256 * u;
         const int t = idx / VPR, kv = idx % VPR;
-        put8(&sm.X[xb][t][0], kv * 8, pk[v]);
-      }
-    }
-    if (ptid < CS) sm.beta[nb][ptid] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)pbt);
-  };
-  auto commit_qv = [&](int j) __attribute__((always_inline)) {
-    const int qb = j & 3, yb = j & 1;
-#pragma unroll
-    for (int v = 0; v < KV; ++v) {
-      const int idx = ptid + v * NPRE;
-      if (idx < CS * VPR) {
-        const int t = idx / VPR, kv = idx % VPR;
-        put8(&sm.Q[qb][t][0], kv * 8, pq[v]);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < YV; ++v) {
-      const int idx = ptid + v * NPRE;
-      if (idx < CS * (RW / 8)) {
-        const int t = idx / (RW / 8), h = idx % (RW / 8);
-        const uint4 val = py[v];
-        const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.YT[yb][h * 8 + 2 * e][t] = (uint16_t)(w4[e] & 0xFFFFu);
-          sm.YT[yb][h * 8 + 2 * e + 1][t] = (uint16_t)(w4[e] >> 16);
+        if (idx < CS * VPR) {
+          if (jk >= 0 && jk < nchunks) put8(&sm.X[jk & 3][t][0], kv * 8, p.k[u]);
+          if (jq >= 0 && jq < nchunks) put8(&sm.Q[jq & 3][t][0], kv * 8, p.q[u]);
         }
       }
+    } else {
+      if (jq >= 0 && jq < nchunks && vv_id >= 0 && vv_id < (CS / 4) * (RW / 4)) {
+        const int i4 = 4 * (vv_id % (RW / 4)), t4 = 4 * (vv_id / (RW / 4));
+        // rows: step t4+e holds values i4..i4+3 in (w[2e], w[2e+1])
+        const uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = w[2 * e + (ii >> 1)];
+            h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
+          }
+          *reinterpret_cast<uint2*>(&sm.YT[jq & 1][i4 + ii][t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+      }
+      if (jk >= 0 && jk < nchunks && vt_id < CS)
+        sm.beta[jk & 3][vt_id] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)p.b);
     }
   };
 
   // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
   // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
-  // One wave; lane = step; prefix product by a wave scan.
-  // ||x_t||^2 is the Gram diagonal (regression) or summed from the key row.
+  // One wave; lane = step.
   auto scalars = [&](int j) __attribute__((always_inline)) {
     const int sb = j & 3;
     const long t0 = (long)j * CS;
@@ -267,29 +277,24 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     const int t = lane;
     const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
     const int tr = t < CS ? t : 0;
-    float nrm;
-    if constexpr (REG) {
-      nrm = sm.G[j & 1][tr][tr];
-    } else {
-      nrm = 0.0f;
-      uint4 xr[DK / 8];
+    uint4 xr[DK / 8];
 #pragma unroll
-      for (int k8 = 0; k8 < DK; k8 += 8) xr[k8 / 8] = *reinterpret_cast<const uint4*>(&sm.X[j & 3][tr][k8]);
+    for (int k8 = 0; k8 < DK; k8 += 8) xr[k8 / 8] = *reinterpret_cast<const uint4*>(&sm.X[j & 3][tr][k8]);
+    const float bv = sm.beta[sb][tr];
+    float nrm = 0.0f;
 #pragma unroll
-      for (int k8 = 0; k8 < DK; k8 += 8) {
-        const uint4 w = xr[k8 / 8];
-        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+    for (int k8 = 0; k8 < DK; k8 += 8) {
+      const uint32_t w4[4] = {xr[k8 / 8].x, xr[k8 / 8].y, xr[k8 / 8].z, xr[k8 / 8].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(w4[e] << 16);
-          const float hi = __uint_as_float(w4[e] & 0xFFFF0000u);
-          nrm += lo * lo + hi * hi;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(w4[e] << 16);
+        const float hi = __uint_as_float(w4[e] & 0xFFFF0000u);
+        nrm += lo * lo + hi * hi;
       }
     }
     float eta = 0.0f, dec = 1.0f;
     if (live) {
-      eta = sm.beta[sb][t] / (a.eps + nrm);
+      eta = bv / (a.eps + nrm);
       dec = 1.0f - eta * a.lambda;
     }
     // inclusive prefix product over the 32 steps: within rows of 16 lanes by
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     gsc *= dpp_shr<2>(gsc, 1.0f);
     gsc *= dpp_shr<4>(gsc, 1.0f);
     gsc *= dpp_shr<8>(gsc, 1.0f);
-    const float row0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsc), 15));
+    const float row0 = lane_value(gsc, 15);
     if (lane >= 16) gsc *= row0;
     const float gprev = dpp_shr<1>(gsc, lane == 16 ? row0 : 1.0f);
     if (t < CS) {
@@ -312,44 +317,59 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     }
   };
 
-  // Gram tile (ti, tj) of chunk j: G[t][s] = x_t . x_s (lane: 4 consecutive s of one t)
-  auto gram_tile = [&](int j, int ti, int tj) __attribute__((always_inline)) {
-    const int xb = j & 3;
+  // 16-row fragments of a key or query block: rows 16 b + lr, all k
+  struct RowFrags {
+    bf16x8 f[2][NKS];
+  };
+  auto row_frags = [&](const uint16_t (*rows)[SM::XR]) __attribute__((always_inline)) {
+    RowFrags r;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) r.f[b][ks] = frag_bf16(&rows[16 * b + lr][32 * ks + 8 * lg]);
+    return r;
+  };
+  // 16x16 product tile sum_k A[16 ba + .][k] B[16 bb + .][k] (exact bf16 operands)
+  auto tile_dot = [&](const RowFrags& A, int ba, const RowFrags& B, int bb) __attribute__((always_inline)) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 fa = frag_bf16(&sm.X[xb][16 * tj + lr][32 * ks + 8 * lg]);
-      const bf16x8 fb = frag_bf16(&sm.X[xb][16 * ti + lr][32 * ks + 8 * lg]);
-      if (ks & 1) acc2 = mfma16(fa, fb, acc2);
-      else acc = mfma16(fa, fb, acc);
+      if (ks & 1) acc2 = mfma16(A.f[ba][ks], B.f[bb][ks], acc2);
+      else acc = mfma16(A.f[ba][ks], B.f[bb][ks], acc);
     }
-    acc += acc2;
-    *reinterpret_cast<float4*>(&sm.G[j & 1][16 * ti + lr][16 * tj + 4 * lg]) =
-        make_float4(acc[0], acc[1], acc[2], acc[3]);
+    return acc + acc2;
   };
-  // q.x tile (ti >= tj) of chunk j: P[t][s] = q_t . x_s for s <= t, split, s in fragment order
-  auto qx_tile = [&](int j, int ti, int tj) __attribute__((always_inline)) {
-    const int xb = j & 3;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  // Gram of chunk j: G[t][s] = x_t . x_s, all four 16x16 tiles (lane: 4 consecutive s of one t)
+  auto gram_store = [&](int j, const RowFrags& X) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 fa = frag_bf16(&sm.X[xb][16 * tj + lr][32 * ks + 8 * lg]);
-      const bf16x8 fb = frag_bf16(&sm.Q[xb][16 * ti + lr][32 * ks + 8 * lg]);
-      if (ks & 1) acc2 = mfma16(fa, fb, acc2);
-      else acc = mfma16(fa, fb, acc);
-    }
-    acc += acc2;
-    const int t = 16 * ti + lr;
-    float pv[4];
+    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = (16 * tj + 4 * lg + e <= t) ? acc[e] : 0.0f;
-    const int p = 8 * lg + 4 * tj;
-    store_split4(&sm.Phi[j & 1][t][p], &sm.Plo[j & 1][t][p], pv);
+      for (int tj = 0; tj < 2; ++tj) {
+        const floatx4 acc = tile_dot(X, tj, X, ti);
+        *reinterpret_cast<float4*>(&sm.G[j & 1][16 * ti + lr][16 * tj + 4 * lg]) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
   };
-  // keys transposed: XT[k][t] from X[t][k]; a thread moves a 4 (t) x 4 (k) block
-  auto transpose_keys = [&](int j) __attribute__((always_inline)) {
+  // q.x of chunk j: P[t][s] = q_t . x_s for s <= t, split, s in fragment order
+  // (tiles (0,0), (1,0), (1,1); tile (0,1) stays zero)
+  auto qx_store = [&](int j, const RowFrags& X, const RowFrags& Qf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj <= ti; ++tj) {
+        const floatx4 acc = tile_dot(X, tj, Qf, ti);
+        const int t = 16 * ti + lr;
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = (16 * tj + 4 * lg + e <= t) ? acc[e] : 0.0f;
+        const int p = 8 * lg + 4 * tj;
+        store_split4(&sm.Phi[j & 1][t][p], &sm.Plo[j & 1][t][p], pv);
+      }
+  };
+  // keys transposed: XT[k][t] from X[t][k]; item idx moves a 4 (t) x 4 (k) block
+  auto transpose_keys = [&](int j, int idx) __attribute__((always_inline)) {
     const int xb = j & 3;
-    for (int idx = ptid; idx < (CS / 4) * (DK / 4); idx += NPRE) {
+    if (idx < (CS / 4) * (DK / 4)) {
       const int t4 = 4 * (idx % (CS / 4)), k4 = 4 * (idx / (CS / 4));
       const int pk4 = fpos(k4);
       uint2 rw[4];
@@ -371,34 +391,38 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   // [T_00 | 0] and [T_11 | -T_11 M_10] of chunk j by forward substitution, one
   // wave: lanes 0..15 the columns of T_00, lanes 16..47 the 32 columns of block 1.
   // Every Gram entry the sweep uses is read before it starts (one wait).
-  auto solve_factors = [&](int j) __attribute__((always_inline)) {
+  auto solve_factors = [&](int j, auto&& between) __attribute__((always_inline)) {
     const int gb = j & 1, sb = j & 3;
     const int blk = lane < 16 ? 0 : 1;
     const int col = lane < 16 ? lane : (lane < 48 ? lane - 16 : 0);   // 0..15 / 0..31
     const int u0 = 16 * blk;
     float rhs[16], acc[16];               // rhs becomes the solution in place
-    float4 gr[16][4];
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (4 * q + 3 > m) gr[m][q] = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + m][u0 + 4 * q]);
     float om[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 o4 = *reinterpret_cast<const float4*>(&sm.omega[sb][u0 + 4 * q]);
       om[4 * q] = o4.x; om[4 * q + 1] = o4.y; om[4 * q + 2] = o4.z; om[4 * q + 3] = o4.w;
     }
-    if (blk == 1 && col >= 16) {
-      // -M_10[:, c'] = -omega_{16+m} G[16+m][c'] = -omega_{16+m} G[c'][16+m]
-      const int cp = col - 16;
+    // -M_10[:, c'] = -omega_{16+m} G[16+m][c'] = -omega_{16+m} G[c'][16+m]
+    const int cp = (blk == 1 && col >= 16) ? col - 16 : 0;
+    float4 gv[4];
 #pragma unroll
-      for (int m = 0; m < 16; m += 4) {
-        const float4 gv = *reinterpret_cast<const float4*>(&sm.G[gb][cp][16 + m]);
-        rhs[m] = -om[m] * gv.x;
-        rhs[m + 1] = -om[m + 1] * gv.y;
-        rhs[m + 2] = -om[m + 2] * gv.z;
-        rhs[m + 3] = -om[m + 3] * gv.w;
+    for (int q = 0; q < 4; ++q) gv[q] = *reinterpret_cast<const float4*>(&sm.G[gb][cp][16 + 4 * q]);
+    // rows 0..7 of the diagonal block (every 4-group that holds some r > m)
+    float4 gr[16][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * q + 3 > m) gr[m][q] = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + m][u0 + 4 * q]);
+    between();
+    if (blk == 1 && col >= 16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rhs[4 * q] = -om[4 * q] * gv[q].x;
+        rhs[4 * q + 1] = -om[4 * q + 1] * gv[q].y;
+        rhs[4 * q + 2] = -om[4 * q + 2] * gv[q].z;
+        rhs[4 * q + 3] = -om[4 * q + 3] * gv[q].w;
       }
     } else {
 #pragma unroll
@@ -408,76 +432,99 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
+      if (m == 4) {   // rows 8..15, read while rows 4..7 are swept
+#pragma unroll
+        for (int m2 = 8; m2 < 16; ++m2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (4 * q + 3 > m2) gr[m2][q] = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + m2][u0 + 4 * q]);
+      }
       rhs[m] -= om[m] * acc[m];
 #pragma unroll
       for (int r = m + 1; r < 16; ++r) {   // column m below m: G[u0+r][u0+m] = G[u0+m][u0+r]
         const float4 g4 = gr[m][r >> 2];
-        const float gv = (r & 3) == 0 ? g4.x : (r & 3) == 1 ? g4.y : (r & 3) == 2 ? g4.z : g4.w;
-        acc[r] += gv * rhs[m];
+        const float g = (r & 3) == 0 ? g4.x : (r & 3) == 1 ? g4.y : (r & 3) == 2 ? g4.z : g4.w;
+        acc[r] += g * rhs[m];
       }
     }
     if (lane < 48) {
       const int cc = col & 15;
       const int p = 8 * (cc >> 2) + ((col >> 4) << 2) + (cc & 3);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) split1(rhs[m], sm.SAhi[gb][blk][m][p], sm.SAlo[gb][blk][m][p]);
+      for (int m = 0; m < 16; ++m) sm.SA[gb][blk][m][p] = rhs[m];
     }
   };
-  // Blocked solve of chunk j for one 16-column tile of R = [omega x | zeta y]:
+  // Blocked solve of chunk j for 16-column tiles of R = [omega x | zeta y]:
   // keys: columns 16 tile.. of the keys (-> Wt^T); else value rows 16 tile.. (-> Ut).
-  // Results: lane holds t = 4 lg + e (block 0) and 16 + 4 lg + e (block 1), column lr.
-  auto solve_tile = [&](int j, bool keys, int tile) __attribute__((always_inline)) {
-    const int gb = j & 1, sb = j & 3, xb = j & 3;
+  // The factors and the row scales are read once for the tiles of a wave.
+  struct SolveA {
+    HL a0, a1;
+    float4 s0, s1;
+  };
+  struct SolveIn {
     float r0[4], r1[4];
-    {
-      const float4 s0 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][4 * lg] : &sm.zeta[sb][4 * lg]);
-      const float4 s1 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][16 + 4 * lg] : &sm.zeta[sb][16 + 4 * lg]);
-      uint2 x0, x1;
-      if (keys) {   // XT positions 8 lg.. hold t = 4 lg.., 8 lg + 4.. hold t = 16 + 4 lg..
-        x0 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg]);
-        x1 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg + 4]);
-      } else {
-        x0 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][4 * lg]);
-        x1 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][16 + 4 * lg]);
-      }
-      r0[0] = s0.x * __uint_as_float(x0.x << 16);
-      r0[1] = s0.y * __uint_as_float(x0.x & 0xFFFF0000u);
-      r0[2] = s0.z * __uint_as_float(x0.y << 16);
-      r0[3] = s0.w * __uint_as_float(x0.y & 0xFFFF0000u);
-      r1[0] = s1.x * __uint_as_float(x1.x << 16);
-      r1[1] = s1.y * __uint_as_float(x1.x & 0xFFFF0000u);
-      r1[2] = s1.z * __uint_as_float(x1.y << 16);
-      r1[3] = s1.w * __uint_as_float(x1.y & 0xFFFF0000u);
+  };
+  auto solve_factors_load = [&](int j, bool keys) __attribute__((always_inline)) {
+    const int gb = j & 1, sb = j & 3;
+    SolveA f;
+    f.s0 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][4 * lg] : &sm.zeta[sb][4 * lg]);
+    f.s1 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][16 + 4 * lg] : &sm.zeta[sb][16 + 4 * lg]);
+    f.a0 = hl_f32(&sm.SA[gb][0][lr][8 * lg]);
+    f.a1 = hl_f32(&sm.SA[gb][1][lr][8 * lg]);
+    return f;
+  };
+  auto solve_load = [&](int j, bool keys, int tile, const SolveA& f) __attribute__((always_inline)) {
+    const int gb = j & 1, xb = j & 3;
+    SolveIn in;
+    uint2 x0, x1;
+    if (keys) {   // XT positions 8 lg.. hold t = 4 lg.., 8 lg + 4.. hold t = 16 + 4 lg..
+      x0 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg]);
+      x1 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg + 4]);
+    } else {
+      x0 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][4 * lg]);
+      x1 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][16 + 4 * lg]);
     }
+    in.r0[0] = f.s0.x * __uint_as_float(x0.x << 16);
+    in.r0[1] = f.s0.y * __uint_as_float(x0.x & 0xFFFF0000u);
+    in.r0[2] = f.s0.z * __uint_as_float(x0.y << 16);
+    in.r0[3] = f.s0.w * __uint_as_float(x0.y & 0xFFFF0000u);
+    in.r1[0] = f.s1.x * __uint_as_float(x1.x << 16);
+    in.r1[1] = f.s1.y * __uint_as_float(x1.x & 0xFFFF0000u);
+    in.r1[2] = f.s1.z * __uint_as_float(x1.y << 16);
+    in.r1[3] = f.s1.w * __uint_as_float(x1.y & 0xFFFF0000u);
+    return in;
+  };
+  // W_0 = T_00 R_0 (lane: t = 4 lg + e, column lr), W_1 = [T_11 | -T_11 M_10] [R_1 ; W_0].
+  // Key tiles are stored as Wt^T rows (8-byte stores): the same products with the
+  // operands swapped give the transposed tiles (lane: 4 consecutive k of one t).
+  auto solve_store = [&](int j, bool keys, int tile, const SolveA& f, const SolveIn& in) __attribute__((always_inline)) {
+    const int gb = j & 1;
     const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-    const HL a0 = hl_pair(&sm.SAhi[gb][0][lr][8 * lg], &sm.SAlo[gb][0][lr][8 * lg]);
-    const HL a1 = hl_pair(&sm.SAhi[gb][1][lr][8 * lg], &sm.SAlo[gb][1][lr][8 * lg]);
     const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
-    const HL b0 = hl_two(r0, zero4);
-    const floatx4 w0 = mma3(zacc, a0, b0);
+    const HL b0 = hl_two(in.r0, zero4);
+    const floatx4 w0 = mma3(zacc, f.a0, b0);
     const float w0v[4] = {w0[0], w0[1], w0[2], w0[3]};
-    const HL b1 = hl_two(r1, w0v);
+    const HL b1 = hl_two(in.r1, w0v);
     if (keys) {
-      // Wt^T rows are written with 8-byte stores: the same products with the
-      // operands swapped give the transposed tiles (lane: 4 consecutive k of one t)
-      const floatx4 v0 = mma3(zacc, b0, a0);
-      const floatx4 v1 = mma3(zacc, b1, a1);
+      const floatx4 v0 = mma3(zacc, b0, f.a0);
+      const floatx4 v1 = mma3(zacc, b1, f.a1);
       const int p = fpos(16 * tile + 4 * lg);
       const float f0[4] = {v0[0], v0[1], v0[2], v0[3]};
       const float f1[4] = {v1[0], v1[1], v1[2], v1[3]};
       store_split4(&sm.Whi[gb][lr][p], &sm.Wlo[gb][lr][p], f0);
       store_split4(&sm.Whi[gb][16 + lr][p], &sm.Wlo[gb][16 + lr][p], f1);
     } else {
-      const floatx4 w1 = mma3(zacc, a1, b1);
+      const floatx4 w1 = mma3(zacc, f.a1, b1);
       float* u = &sm.Ut[gb][16 * tile + lr][0];
       *reinterpret_cast<float4*>(u + 4 * lg) = make_float4(w0[0], w0[1], w0[2], w0[3]);
       *reinterpret_cast<float4*>(u + 16 + 4 * lg) = make_float4(w1[0], w1[1], w1[2], w1[3]);
     }
   };
-  // inner-product family: z_t = zeta_t y_t, kept where the regression keeps Ut
-  auto zeta_y = [&](int j) __attribute__((always_inline)) {
+  // inner-product family: z_t = zeta_t y_t, kept where the regression keeps Ut;
+  // item idx covers 4 steps of one value row
+  auto zeta_y = [&](int j, int idx) __attribute__((always_inline)) {
     const int gb = j & 1, sb = j & 3;
-    for (int idx = ptid; idx < RW * (CS / 4); idx += NPRE) {
+    if (idx < RW * (CS / 4)) {
       const int i = idx / (CS / 4), t4 = 4 * (idx % (CS / 4));
       const uint2 yb = *reinterpret_cast<const uint2*>(&sm.YT[gb][i][t4]);
       const float4 z = *reinterpret_cast<const float4*>(&sm.zeta[sb][t4]);
@@ -510,8 +557,10 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
     __syncthreads();
-    for (int c = -4; c < nchunks; ++c) {
-      if (state_wave && c >= 0) {
+    // same barrier count as the preparation loop: an even number of iterations
+    const int cend = nchunks + (nchunks & 1);
+    for (int c = -4; c < cend; ++c) {
+      if (state_wave && c >= 0 && c < nchunks) {
         // ---- state chain of chunk c (registers) ----
         const int cb = c & 1, xb = c & 3;
         const long t0 = (long)c * CS;
@@ -590,37 +639,71 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     }
   } else {
     // ---------------- preparation waves ----------------
-    prefetch_k(0);
+    // iteration c:  wave 2  Gram of c+3, q.x of c+1
+    //               wave 3  Wt tiles 0, 1 of c+1    wave 4  Wt tiles 2, 3 of c+1
+    //               wave 5  Ut tiles of c+1
+    //               wave 6  scalars of c+3, keys of c+2 transposed
+    //               wave 7  factors of c+2
+    //               all     commit keys/gains of c+4, queries/values of c+2;
+    //                       load keys/gains of c+5, queries/values of c+3
+    // A wave reads its LDS operands first, then commits and loads, then computes:
+    // the LDS round trip overlaps the commit.
+    PSet ps;
+    prefetch(ps, 0, -1);
     __syncthreads();
-    for (int c = -4; c < nchunks; ++c) {
-      // ---- preparation: every stage reads only what earlier iterations wrote ----
-      if (c + 4 < nchunks) commit_k(c + 4);
-      if (c + 2 >= 0 && c + 2 < nchunks) commit_qv(c + 2);
-      if (c + 5 < nchunks) prefetch_k(c + 5);
-      if (c + 3 >= 0 && c + 3 < nchunks) prefetch_qv(c + 3);
+    auto iteration = [&](int c, PSet& cur, PSet& nxt) __attribute__((always_inline)) {
       const bool v1 = c + 1 >= 0 && c + 1 < nchunks;
       const bool v2 = c + 2 >= 0 && c + 2 < nchunks;
       const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
-      if (v2) transpose_keys(c + 2);
-      if (v2 && wave == 7) {
-        scalars(c + 2);
-        wave_sync();
-      }
-      if constexpr (REG) {
-        if (v3 && wave < 6) gram_tile(c + 3, (wave - 2) >> 1, (wave - 2) & 1);
-        if (v2 && wave == 7) solve_factors(c + 2);
-        if (v1) {
-          if (wave - 2 < NKT) solve_tile(c + 1, true, wave - 2);
-          if (wave == 6) {
-            solve_tile(c + 1, false, 0);
-            if (nrb > 1) solve_tile(c + 1, false, 1);
+      auto move = [&]() __attribute__((always_inline)) {
+        commit(cur, c + 4, c + 2);
+        prefetch(nxt, c + 5, c + 3);
+      };
+      if (wave == 2) {
+        const RowFrags xg = row_frags(sm.X[(c + 3) & 3]);
+        const RowFrags xq = row_frags(sm.X[(c + 1) & 3]);
+        const RowFrags qq = row_frags(sm.Q[(c + 1) & 3]);
+        move();
+        if (REG && v3) gram_store(c + 3, xg);
+        if (v1) qx_store(c + 1, xq, qq);
+      } else if (wave < 6) {
+        if constexpr (REG) {
+          const bool keys = wave < 5;
+          const int t0 = keys ? 2 * (wave - 3) : 0;     // first tile of the pair
+          const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
+          const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 4 has no key tiles
+          const SolveA f = solve_factors_load(c + 1, keys);
+          const SolveIn in0 = solve_load(c + 1, keys, lt0, f);
+          const SolveIn in1 = solve_load(c + 1, keys, two ? lt0 + 1 : lt0, f);
+          move();
+          if (v1 && (!keys || t0 < NKT)) {
+            solve_store(c + 1, keys, t0, f, in0);
+            if (two) solve_store(c + 1, keys, t0 + 1, f, in1);
           }
+        } else {
+          move();
+          if (v1) zeta_y(c + 1, (wave - 3) * 64 + lane);
+        }
+      } else if (wave == 6) {
+        move();
+        if (v3) scalars(c + 3);
+        if (v2) {
+          transpose_keys(c + 2, lane);
+          transpose_keys(c + 2, 64 + lane);
         }
       } else {
-        if (v1) zeta_y(c + 1);
+        if constexpr (REG) {
+          if (v2) solve_factors(c + 2, [&]() __attribute__((always_inline)) { move(); });
+          else move();
+        } else {
+          move();
+          if (v1) zeta_y(c + 1, 192 + lane);
+        }
       }
-      // q.x tiles (0,0), (1,0), (1,1) of chunk c+1 on waves 2, 3, 4
-      if (v1 && wave < 5) qx_tile(c + 1, (wave - 1) >> 1, (wave - 2) >> 1);
+    };
+    const int cend = nchunks + (nchunks & 1);
+    for (int c = -4; c < cend; ++c) {
+      iteration(c, ps, ps);
       __syncthreads();
     }
   }
