@@ -119,6 +119,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   using SM = WyLds<DK>;
   constexpr int NKT = DK / 16, NKS = DK / 32, VPR = DK / 8;
   static_assert(DK % 32 == 0 && DK <= 64, "dk in {32, 64}");
+  static_assert((CS / 4) * (RW / 4) == 64 && CS <= 64, "values and gains: one wave");
   __shared__ __align__(16) SM sm;
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
@@ -168,65 +169,46 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   // waves 6..7 values and gains.  A load is issued one iteration before its
   // commit.
   constexpr int KQ = (CS * VPR + 255) / 256;
-  struct PSet {
-    uint4 k[KQ], q[KQ], v, v2;
+  struct KQSet {            // waves 2..5: one 16-byte piece of a key row and a query row
+    uint4 k[KQ], q[KQ];
+  };
+  struct VBSet {            // wave 6: a 4 (steps) x 4 (value rows) block and one gain
+    uint4 v, v2;
     uint32_t b;
   };
-  const int kt_id = tid - 128;             // 0..255 on waves 2..5
-  const int vt_id = tid - 384;             // 0..127 on waves 6..7 (gains: wave 6)
-  const int vv_id = tid - 448;             // 0..63 on wave 7 (values)
-  // keys and gains of chunk jk, queries and values of chunk jq (out of range: skipped)
-  auto prefetch = [&](PSet& p, int jk, int jq) __attribute__((always_inline)) {
-    if (wave < 6) {
-      if (jk >= 0 && jk < nchunks) {
-        const long t0 = (long)jk * CS;
-        const int c = steps(jk);
+  // waves w and w + 4 share a SIMD (and its matrix core): the state waves 0, 1 are
+  // paired with the VALU/LDS roles on waves 4, 5; the matrix-core roles take 2, 3, 6, 7
+  const int kq_slot = wave == 2 ? 0 : wave == 3 ? 1 : wave == 6 ? 2 : 3;
+  const int kt_id = 64 * kq_slot + lane;   // 0..255 on waves 2, 3, 6, 7
+  const int vt_id = lane;                  // 0..63 on wave 4
+  // keys of chunk jk, queries of chunk jq (out of range: skipped)
+  auto prefetch_kq = [&](KQSet& p, int jk, int jq) __attribute__((always_inline)) {
+    if (jk >= 0 && jk < nchunks) {
+      const long t0 = (long)jk * CS;
+      const int c = steps(jk);
 #pragma unroll
-        for (int u = 0; u < KQ; ++u) {
-          const int idx = kt_id + 256 * u;
-          const int t = idx / VPR, kv = idx % VPR;
-          uint4 kval = {0u, 0u, 0u, 0u};
-          if (idx < CS * VPR && t < c) {
-            const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
-            if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
-            else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
-          }
-          p.k[u] = kval;
+      for (int u = 0; u < KQ; ++u) {
+        const int idx = kt_id + 256 * u;
+        const int t = idx / VPR, kv = idx % VPR;
+        uint4 kval = {0u, 0u, 0u, 0u};
+        if (idx < CS * VPR && t < c) {
+          const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
+          if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
+          else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
         }
+        p.k[u] = kval;
       }
-      if (jq >= 0 && jq < nchunks) {
-        const long t0 = (long)jq * CS;
-        const int c = steps(jq);
+    }
+    if (jq >= 0 && jq < nchunks) {
+      const long t0 = (long)jq * CS;
+      const int c = steps(jq);
 #pragma unroll
-        for (int u = 0; u < KQ; ++u) {
-          const int idx = kt_id + 256 * u;
-          const int t = idx / VPR, kv = idx % VPR;
-          uint4 qval = {0u, 0u, 0u, 0u};
-          if (idx < CS * VPR && t < c) qval = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
-          p.q[u] = qval;
-        }
-      }
-    } else {
-      if (jq >= 0 && jq < nchunks && vv_id >= 0 && vv_id < (CS / 4) * (RW / 4)) {
-        // a 4 (steps) x 4 (value rows) block: t = t4.., i = i4..
-        const long t0 = (long)jq * CS;
-        const int c = steps(jq);
-        const int i4 = 4 * (vv_id % (RW / 4)), t4 = 4 * (vv_id / (RW / 4));
-        uint32_t w[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint2 val = {0u, 0u};
-          if (t4 + e < c && i0 + i4 < dv) val = *reinterpret_cast<const uint2*>(vg + v_base + (t0 + t4 + e) * dv + i0 + i4);
-          w[2 * e] = val.x;
-          w[2 * e + 1] = val.y;
-        }
-        p.v = make_uint4(w[0], w[1], w[2], w[3]);
-        p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
-      }
-      if (jk >= 0 && jk < nchunks) {
-        const long t0 = (long)jk * CS;
-        p.b = 0;
-        if (a.beta_kind == 1 && vt_id < steps(jk)) p.b = (uint32_t)bg[(long)chain * L + t0 + vt_id];
+      for (int u = 0; u < KQ; ++u) {
+        const int idx = kt_id + 256 * u;
+        const int t = idx / VPR, kv = idx % VPR;
+        uint4 qval = {0u, 0u, 0u, 0u};
+        if (idx < CS * VPR && t < c) qval = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
+        p.q[u] = qval;
       }
     }
   };
@@ -235,36 +217,59 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     *reinterpret_cast<uint2*>(row + fpos(k0)) = make_uint2(val.x, val.y);
     *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
   };
-  auto commit = [&](const PSet& p, int jk, int jq) __attribute__((always_inline)) {
-    if (wave < 6) {
+  auto commit_kq = [&](const KQSet& p, int jk, int jq) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < KQ; ++u) {
-        const int idx = kt_id + 256 * u;
-        const int t = idx / VPR, kv = idx % VPR;
-        if (idx < CS * VPR) {
-          if (jk >= 0 && jk < nchunks) put8(&sm.X[jk & 3][t][0], kv * 8, p.k[u]);
-          if (jq >= 0 && jq < nchunks) put8(&sm.Q[jq & 3][t][0], kv * 8, p.q[u]);
-        }
+    for (int u = 0; u < KQ; ++u) {
+      const int idx = kt_id + 256 * u;
+      const int t = idx / VPR, kv = idx % VPR;
+      if (idx < CS * VPR) {
+        if (jk >= 0 && jk < nchunks) put8(&sm.X[jk & 3][t][0], kv * 8, p.k[u]);
+        if (jq >= 0 && jq < nchunks) put8(&sm.Q[jq & 3][t][0], kv * 8, p.q[u]);
       }
-    } else {
-      if (jq >= 0 && jq < nchunks && vv_id >= 0 && vv_id < (CS / 4) * (RW / 4)) {
-        const int i4 = 4 * (vv_id % (RW / 4)), t4 = 4 * (vv_id / (RW / 4));
-        // rows: step t4+e holds values i4..i4+3 in (w[2e], w[2e+1])
-        const uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          uint32_t h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t x = w[2 * e + (ii >> 1)];
-            h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
-          }
-          *reinterpret_cast<uint2*>(&sm.YT[jq & 1][i4 + ii][t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        }
-      }
-      if (jk >= 0 && jk < nchunks && vt_id < CS)
-        sm.beta[jk & 3][vt_id] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)p.b);
     }
+  };
+  // gains of chunk jb, values of chunk jv
+  auto prefetch_vb = [&](VBSet& p, int jb, int jv) __attribute__((always_inline)) {
+    if (jv >= 0 && jv < nchunks) {
+      // a 4 (steps) x 4 (value rows) block: t = t4.., i = i4..
+      const long t0 = (long)jv * CS;
+      const int c = steps(jv);
+      const int i4 = 4 * (vt_id % (RW / 4)), t4 = 4 * (vt_id / (RW / 4));
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint2 val = {0u, 0u};
+        if (t4 + e < c && i0 + i4 < dv) val = *reinterpret_cast<const uint2*>(vg + v_base + (t0 + t4 + e) * dv + i0 + i4);
+        w[2 * e] = val.x;
+        w[2 * e + 1] = val.y;
+      }
+      p.v = make_uint4(w[0], w[1], w[2], w[3]);
+      p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    if (jb >= 0 && jb < nchunks) {
+      const long t0 = (long)jb * CS;
+      p.b = 0;
+      if (a.beta_kind == 1 && vt_id < steps(jb)) p.b = (uint32_t)bg[(long)chain * L + t0 + vt_id];
+    }
+  };
+  auto commit_vb = [&](const VBSet& p, int jb, int jv) __attribute__((always_inline)) {
+    if (jv >= 0 && jv < nchunks) {
+      const int i4 = 4 * (vt_id % (RW / 4)), t4 = 4 * (vt_id / (RW / 4));
+      // rows: step t4+e holds values i4..i4+3 in (w[2e], w[2e+1])
+      const uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = w[2 * e + (ii >> 1)];
+          h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
+        }
+        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][i4 + ii][t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+    }
+    if (jb >= 0 && jb < nchunks && vt_id < CS)
+      sm.beta[jb & 3][vt_id] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)p.b);
   };
 
   // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
@@ -640,71 +645,99 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   } else {
     // ---------------- preparation waves ----------------
     // iteration c:  wave 2  Gram of c+3, q.x of c+1
-    //               wave 3  Wt tiles 0, 1 of c+1    wave 4  Wt tiles 2, 3 of c+1
-    //               wave 5  Ut tiles of c+1
-    //               wave 6  scalars of c+3, keys of c+2 transposed
-    //               wave 7  factors of c+2
-    //               all     commit keys/gains of c+4, queries/values of c+2;
-    //                       load keys/gains of c+5, queries/values of c+3
-    // A wave reads its LDS operands first, then commits and loads, then computes:
-    // the LDS round trip overlaps the commit.
-    PSet ps;
-    prefetch(ps, 0, -1);
-    __syncthreads();
-    auto iteration = [&](int c, PSet& cur, PSet& nxt) __attribute__((always_inline)) {
-      const bool v1 = c + 1 >= 0 && c + 1 < nchunks;
-      const bool v2 = c + 2 >= 0 && c + 2 < nchunks;
-      const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
-      auto move = [&]() __attribute__((always_inline)) {
-        commit(cur, c + 4, c + 2);
-        prefetch(nxt, c + 5, c + 3);
-      };
-      if (wave == 2) {
-        const RowFrags xg = row_frags(sm.X[(c + 3) & 3]);
-        const RowFrags xq = row_frags(sm.X[(c + 1) & 3]);
-        const RowFrags qq = row_frags(sm.Q[(c + 1) & 3]);
-        move();
-        if (REG && v3) gram_store(c + 3, xg);
-        if (v1) qx_store(c + 1, xq, qq);
-      } else if (wave < 6) {
-        if constexpr (REG) {
-          const bool keys = wave < 5;
-          const int t0 = keys ? 2 * (wave - 3) : 0;     // first tile of the pair
-          const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
-          const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 4 has no key tiles
-          const SolveA f = solve_factors_load(c + 1, keys);
-          const SolveIn in0 = solve_load(c + 1, keys, lt0, f);
-          const SolveIn in1 = solve_load(c + 1, keys, two ? lt0 + 1 : lt0, f);
+    //               wave 3  Wt tiles 0, 1 of c+1    wave 6  Wt tiles 2, 3 of c+1
+    //               wave 7  Ut tiles of c+1
+    //               waves 2, 3, 6, 7  commit keys of c+4, queries of c+2
+    //               wave 4  scalars of c+3, keys of c+2 transposed, commit gains of
+    //                       c+4 and values of c+2
+    //               wave 5  factors of c+2 (inner-product family: z of c+1 in part
+    //                       and the keys of c+2 transposed, instead of wave 4)
+    // A wave reads its LDS operands first, then commits, then computes (the LDS
+    // round trip overlaps the commit).  Global loads are issued two iterations
+    // before their commit, into two register sets used alternately.  Each role
+    // runs its own loop (same barrier count), so it carries only its registers.
+    const int cend = nchunks + (nchunks & 1);
+    if (wave != 4 && wave != 5) {
+      KQSet ps0, ps1;
+      prefetch_kq(ps0, 0, -2);
+      prefetch_kq(ps1, 1, -1);
+      __syncthreads();
+      auto iteration = [&](int c, KQSet& cur) __attribute__((always_inline)) {
+        const bool v1 = c + 1 >= 0 && c + 1 < nchunks;
+        const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
+        auto move = [&]() __attribute__((always_inline)) {
+          commit_kq(cur, c + 4, c + 2);
+          prefetch_kq(cur, c + 6, c + 4);
+        };
+        if (wave == 2) {
+          const RowFrags xg = row_frags(sm.X[(c + 3) & 3]);
+          const RowFrags xq = row_frags(sm.X[(c + 1) & 3]);
+          const RowFrags qq = row_frags(sm.Q[(c + 1) & 3]);
           move();
-          if (v1 && (!keys || t0 < NKT)) {
-            solve_store(c + 1, keys, t0, f, in0);
-            if (two) solve_store(c + 1, keys, t0 + 1, f, in1);
-          }
+          if (REG && v3) gram_store(c + 3, xg);
+          if (v1) qx_store(c + 1, xq, qq);
         } else {
-          move();
-          if (v1) zeta_y(c + 1, (wave - 3) * 64 + lane);
+          if constexpr (REG) {
+            const bool keys = wave != 7;
+            const int t0 = keys ? (wave == 3 ? 0 : 2) : 0;   // first tile of the pair
+            const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
+            const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 6 has no key tiles
+            const SolveA f = solve_factors_load(c + 1, keys);
+            const SolveIn in0 = solve_load(c + 1, keys, lt0, f);
+            const SolveIn in1 = solve_load(c + 1, keys, two ? lt0 + 1 : lt0, f);
+            move();
+            if (v1 && (!keys || t0 < NKT)) {
+              solve_store(c + 1, keys, t0, f, in0);
+              if (two) solve_store(c + 1, keys, t0 + 1, f, in1);
+            }
+          } else {
+            move();
+            if (v1) zeta_y(c + 1, 64 * (kq_slot - 1) + lane);      // waves 3, 6, 7: items 0..191
+          }
         }
-      } else if (wave == 6) {
-        move();
+      };
+      for (int c = -4; c < cend; c += 2) {
+        iteration(c, ps0);
+        __syncthreads();
+        iteration(c + 1, ps1);
+        __syncthreads();
+      }
+    } else if (wave == 4) {
+      VBSet ps0, ps1;
+      prefetch_vb(ps0, 0, -2);
+      prefetch_vb(ps1, 1, -1);
+      __syncthreads();
+      auto iteration = [&](int c, VBSet& cur) __attribute__((always_inline)) {
+        const bool v2 = c + 2 >= 0 && c + 2 < nchunks;
+        const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
+        commit_vb(cur, c + 4, c + 2);
+        prefetch_vb(cur, c + 6, c + 4);
         if (v3) scalars(c + 3);
-        if (v2) {
+        if (REG && v2) {        // inner-product family: wave 5 transposes the keys
           transpose_keys(c + 2, lane);
           transpose_keys(c + 2, 64 + lane);
         }
-      } else {
-        if constexpr (REG) {
-          if (v2) solve_factors(c + 2, [&]() __attribute__((always_inline)) { move(); });
-          else move();
-        } else {
-          move();
-          if (v1) zeta_y(c + 1, 192 + lane);
-        }
+      };
+      for (int c = -4; c < cend; c += 2) {
+        iteration(c, ps0);
+        __syncthreads();
+        iteration(c + 1, ps1);
+        __syncthreads();
       }
-    };
-    const int cend = nchunks + (nchunks & 1);
-    for (int c = -4; c < cend; ++c) {
-      iteration(c, ps, ps);
+    } else {
       __syncthreads();
+      for (int c = -4; c < cend; ++c) {
+        if constexpr (REG) {
+          if (c + 2 >= 0 && c + 2 < nchunks) solve_factors(c + 2, [&]() __attribute__((always_inline)) {});
+        } else {
+          if (c + 1 >= 0 && c + 1 < nchunks) zeta_y(c + 1, 192 + lane);
+          if (c + 2 >= 0 && c + 2 < nchunks) {
+            transpose_keys(c + 2, lane);
+            transpose_keys(c + 2, 64 + lane);
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 }
