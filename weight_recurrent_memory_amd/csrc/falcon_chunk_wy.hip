@@ -70,10 +70,10 @@ struct WyLds {
   float G[2][CS][CS + 8];                // Gram (whole 32 x 32)
   float Ut[2][RW][CS + 8];               // Ut[i][t]
   float beta[4][CS];                     // gains by chunk & 3
-  alignas(16) float gam[4][CS];
-  alignas(16) float gm1[4][CS];
-  alignas(16) float zeta[4][CS];
-  alignas(16) float omega[4][CS];
+  alignas(16) float gam[8][CS];          // per-step scalars by chunk & 7
+  alignas(16) float gm1[8][CS];
+  alignas(16) float zeta[8][CS];
+  alignas(16) float omega[8][CS];
 };
 
 struct WyGeom {
@@ -165,14 +165,17 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   }
 
   // ---------------- global loads and their commits to LDS ----------------
-  // Waves 2..5 move keys and queries (one 16-byte piece of a row per thread),
-  // waves 6..7 values and gains.  A load is issued one iteration before its
-  // commit.
+  // Waves 2, 3, 6, 7 move keys and queries (one 16-byte piece of a row per
+  // thread), wave 4 values and gains.  A load is issued two iterations before its
+  // commit, into one of two register sets used alternately.  Every prefetch
+  // issues the same loads in the same order whatever the chunk and the lane (a
+  // piece out of range reads the chain's first row instead and is zeroed at
+  // commit), so the wait before a commit counts only the loads of its own set.
   constexpr int KQ = (CS * VPR + 255) / 256;
-  struct KQSet {            // waves 2..5: one 16-byte piece of a key row and a query row
+  struct KQSet {            // one 16-byte piece of a key row and of a query row
     uint4 k[KQ], q[KQ];
   };
-  struct VBSet {            // wave 6: a 4 (steps) x 4 (value rows) block and one gain
+  struct VBSet {            // a 4 (steps) x 4 (value rows) block and one gain
     uint4 v, v2;
     uint32_t b;
   };
@@ -181,35 +184,26 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   const int kq_slot = wave == 2 ? 0 : wave == 3 ? 1 : wave == 6 ? 2 : 3;
   const int kt_id = 64 * kq_slot + lane;   // 0..255 on waves 2, 3, 6, 7
   const int vt_id = lane;                  // 0..63 on wave 4
-  // keys of chunk jk, queries of chunk jq (out of range: skipped)
+  auto live_chunk = [&](int j) __attribute__((always_inline)) { return j >= 0 && j < nchunks; };
+  // key x_g = k_{g-1}; x_0 = k_prev, or 0 on a fresh sequence
+  auto key_ok = [&](int j, int t) __attribute__((always_inline)) {
+    return live_chunk(j) && t < steps(j) && ((long)j * CS + t >= 1 || kpg != nullptr);
+  };
+  // keys of chunk jk, queries of chunk jq
   auto prefetch_kq = [&](KQSet& p, int jk, int jq) __attribute__((always_inline)) {
-    if (jk >= 0 && jk < nchunks) {
-      const long t0 = (long)jk * CS;
-      const int c = steps(jk);
+    const uint16_t* first = kg + qk_base;
 #pragma unroll
-      for (int u = 0; u < KQ; ++u) {
-        const int idx = kt_id + 256 * u;
-        const int t = idx / VPR, kv = idx % VPR;
-        uint4 kval = {0u, 0u, 0u, 0u};
-        if (idx < CS * VPR && t < c) {
-          const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
-          if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
-          else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
-        }
-        p.k[u] = kval;
-      }
-    }
-    if (jq >= 0 && jq < nchunks) {
-      const long t0 = (long)jq * CS;
-      const int c = steps(jq);
-#pragma unroll
-      for (int u = 0; u < KQ; ++u) {
-        const int idx = kt_id + 256 * u;
-        const int t = idx / VPR, kv = idx % VPR;
-        uint4 qval = {0u, 0u, 0u, 0u};
-        if (idx < CS * VPR && t < c) qval = *reinterpret_cast<const uint4*>(qg + qk_base + (t0 + t) * DK + kv * 8);
-        p.q[u] = qval;
-      }
+    for (int u = 0; u < KQ; ++u) {
+      const int idx = kt_id + 256 * u;
+      const int t = idx / VPR, kv = idx % VPR;
+      const bool in = idx < CS * VPR;
+      const long g = (long)jk * CS + t;
+      const uint16_t* ks = first;
+      if (in && key_ok(jk, t)) ks = g >= 1 ? kg + qk_base + (g - 1) * DK + kv * 8 : kpg + (long)chain * DK + kv * 8;
+      const uint16_t* qs = qg + qk_base;
+      if (in && live_chunk(jq) && t < steps(jq)) qs = qg + qk_base + ((long)jq * CS + t) * DK + kv * 8;
+      p.k[u] = *reinterpret_cast<const uint4*>(ks);
+      p.q[u] = *reinterpret_cast<const uint4*>(qs);
     }
   };
   // 8 consecutive k (k0 % 8 == 0) -> two 4-groups at their fragment positions
@@ -218,45 +212,50 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
   };
   auto commit_kq = [&](const KQSet& p, int jk, int jq) __attribute__((always_inline)) {
+    const uint4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < KQ; ++u) {
       const int idx = kt_id + 256 * u;
       const int t = idx / VPR, kv = idx % VPR;
       if (idx < CS * VPR) {
-        if (jk >= 0 && jk < nchunks) put8(&sm.X[jk & 3][t][0], kv * 8, p.k[u]);
-        if (jq >= 0 && jq < nchunks) put8(&sm.Q[jq & 3][t][0], kv * 8, p.q[u]);
+        if (live_chunk(jk)) put8(&sm.X[jk & 3][t][0], kv * 8, key_ok(jk, t) ? p.k[u] : zero);
+        if (live_chunk(jq)) put8(&sm.Q[jq & 3][t][0], kv * 8, t < steps(jq) ? p.q[u] : zero);
       }
     }
+  };
+  // a 4 (steps) x 4 (value rows) block of wave 4's lane: steps t4.., value rows i4..
+  const int vb_i4 = 4 * (vt_id % (RW / 4)), vb_t4 = 4 * (vt_id / (RW / 4));
+  auto value_ok = [&](int j, int e) __attribute__((always_inline)) {
+    return live_chunk(j) && vb_t4 + e < steps(j) && i0 + vb_i4 < dv;
+  };
+  auto gain_ok = [&](int j) __attribute__((always_inline)) {
+    return a.beta_kind == 1 && live_chunk(j) && vt_id < steps(j);
   };
   // gains of chunk jb, values of chunk jv
   auto prefetch_vb = [&](VBSet& p, int jb, int jv) __attribute__((always_inline)) {
-    if (jv >= 0 && jv < nchunks) {
-      // a 4 (steps) x 4 (value rows) block: t = t4.., i = i4..
-      const long t0 = (long)jv * CS;
-      const int c = steps(jv);
-      const int i4 = 4 * (vt_id % (RW / 4)), t4 = 4 * (vt_id / (RW / 4));
-      uint32_t w[8];
+    const long t0 = (long)jv * CS;
+    uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint2 val = {0u, 0u};
-        if (t4 + e < c && i0 + i4 < dv) val = *reinterpret_cast<const uint2*>(vg + v_base + (t0 + t4 + e) * dv + i0 + i4);
-        w[2 * e] = val.x;
-        w[2 * e + 1] = val.y;
-      }
-      p.v = make_uint4(w[0], w[1], w[2], w[3]);
-      p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t* src = vg + v_base;
+      if (value_ok(jv, e)) src = vg + v_base + (t0 + vb_t4 + e) * dv + i0 + vb_i4;
+      const uint2 val = *reinterpret_cast<const uint2*>(src);
+      w[2 * e] = val.x;
+      w[2 * e + 1] = val.y;
     }
-    if (jb >= 0 && jb < nchunks) {
-      const long t0 = (long)jb * CS;
-      p.b = 0;
-      if (a.beta_kind == 1 && vt_id < steps(jb)) p.b = (uint32_t)bg[(long)chain * L + t0 + vt_id];
-    }
+    p.v = make_uint4(w[0], w[1], w[2], w[3]);
+    p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
+    const uint16_t* bsrc = vg + v_base;
+    if (gain_ok(jb)) bsrc = bg + (long)chain * L + (long)jb * CS + vt_id;
+    p.b = *bsrc;
   };
   auto commit_vb = [&](const VBSet& p, int jb, int jv) __attribute__((always_inline)) {
-    if (jv >= 0 && jv < nchunks) {
-      const int i4 = 4 * (vt_id % (RW / 4)), t4 = 4 * (vt_id / (RW / 4));
+    if (live_chunk(jv)) {
       // rows: step t4+e holds values i4..i4+3 in (w[2e], w[2e+1])
-      const uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
+      uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!value_ok(jv, e)) w[2 * e] = w[2 * e + 1] = 0u;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         uint32_t h[4];
@@ -265,38 +264,40 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
           const uint32_t x = w[2 * e + (ii >> 1)];
           h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
         }
-        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][i4 + ii][t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][vb_i4 + ii][vb_t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
     }
-    if (jb >= 0 && jb < nchunks && vt_id < CS)
-      sm.beta[jb & 3][vt_id] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)p.b);
+    if (live_chunk(jb) && vt_id < CS)
+      sm.beta[jb & 3][vt_id] = a.beta_kind == 0 ? a.beta : (gain_ok(jb) ? bf16_to_f32((uint16_t)p.b) : 0.0f);
   };
 
   // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
   // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
-  // One wave; lane = step.
+  // One wave: lane = step t (mod 32); lanes t and t + 32 take half of row t
+  // each, in packed bf16 dot products, and swap their partial sums.
   auto scalars = [&](int j) __attribute__((always_inline)) {
-    const int sb = j & 3;
+    const int sb = j & 7;
     const long t0 = (long)j * CS;
     const int c = steps(j);
-    const int t = lane;
+    const int t = lane & 31;
     const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
-    const int tr = t < CS ? t : 0;
-    uint4 xr[DK / 8];
+    const int half = (lane >> 5) * (DK / 2);
+    uint4 xr[DK / 16];
 #pragma unroll
-    for (int k8 = 0; k8 < DK; k8 += 8) xr[k8 / 8] = *reinterpret_cast<const uint4*>(&sm.X[j & 3][tr][k8]);
-    const float bv = sm.beta[sb][tr];
-    float nrm = 0.0f;
+    for (int k8 = 0; k8 < DK / 2; k8 += 8) xr[k8 / 8] = *reinterpret_cast<const uint4*>(&sm.X[j & 3][t][half + k8]);
+    const float bv = sm.beta[j & 3][t];
+    float part = 0.0f;
 #pragma unroll
-    for (int k8 = 0; k8 < DK; k8 += 8) {
+    for (int k8 = 0; k8 < DK / 2; k8 += 8) {
       const uint32_t w4[4] = {xr[k8 / 8].x, xr[k8 / 8].y, xr[k8 / 8].z, xr[k8 / 8].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(w4[e] << 16);
-        const float hi = __uint_as_float(w4[e] & 0xFFFF0000u);
-        nrm += lo * lo + hi * hi;
+        const bf16x2 v = __builtin_bit_cast(bf16x2, w4[e]);
+        part = __builtin_amdgcn_fdot2_f32_bf16(v, v, part, false);
       }
     }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    const float nrm = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     float eta = 0.0f, dec = 1.0f;
     if (live) {
       eta = bv / (a.eps + nrm);
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     const float row0 = lane_value(gsc, 15);
     if (lane >= 16) gsc *= row0;
     const float gprev = dpp_shr<1>(gsc, lane == 16 ? row0 : 1.0f);
-    if (t < CS) {
+    if (lane < CS) {
       const float z = eta / gsc;
       sm.gam[sb][t] = gsc;
       sm.gm1[sb][t] = gprev;
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   // wave: lanes 0..15 the columns of T_00, lanes 16..47 the 32 columns of block 1.
   // Every Gram entry the sweep uses is read before it starts (one wait).
   auto solve_factors = [&](int j, auto&& between) __attribute__((always_inline)) {
-    const int gb = j & 1, sb = j & 3;
+    const int gb = j & 1, sb = j & 7;
     const int blk = lane < 16 ? 0 : 1;
     const int col = lane < 16 ? lane : (lane < 48 ? lane - 16 : 0);   // 0..15 / 0..31
     const int u0 = 16 * blk;
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     float r0[4], r1[4];
   };
   auto solve_factors_load = [&](int j, bool keys) __attribute__((always_inline)) {
-    const int gb = j & 1, sb = j & 3;
+    const int gb = j & 1, sb = j & 7;
     SolveA f;
     f.s0 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][4 * lg] : &sm.zeta[sb][4 * lg]);
     f.s1 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][16 + 4 * lg] : &sm.zeta[sb][16 + 4 * lg]);
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   // inner-product family: z_t = zeta_t y_t, kept where the regression keeps Ut;
   // item idx covers 4 steps of one value row
   auto zeta_y = [&](int j, int idx) __attribute__((always_inline)) {
-    const int gb = j & 1, sb = j & 3;
+    const int gb = j & 1, sb = j & 7;
     if (idx < RW * (CS / 4)) {
       const int i = idx / (CS / 4), t4 = 4 * (idx % (CS / 4));
       const uint2 yb = *reinterpret_cast<const uint2*>(&sm.YT[gb][i][t4]);
@@ -541,6 +542,8 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
 
   // The state waves and the preparation waves run separate loops with the same
   // barrier count (one per iteration), so neither carries the other's registers.
+  // iterations c = -5 .. cend-1 (an even count, for the twice-unrolled loops)
+  const int cend = nchunks + ((nchunks + 5) & 1);
   if (wave < 2) {
     // ---------------- state waves ----------------
     const int rt = wave;                       // row tile
@@ -562,37 +565,42 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
     __syncthreads();
-    // same barrier count as the preparation loop: an even number of iterations
-    const int cend = nchunks + (nchunks & 1);
-    for (int c = -4; c < cend; ++c) {
+    // The operands of chunk c+1 (written two or more iterations earlier) are read
+    // at the end of iteration c, while the barrier is pending.
+    struct StateOps {
+      bf16x8 qf[2][NKS], xf[NKT];
+      HL wf[2][NKS], pf[2];
+      float4 ut4[2];
+      float gt[2], gC;
+    };
+    auto load_ops = [&](int j) __attribute__((always_inline)) {
+      StateOps o;
+      const int cb = j & 1, xb = j & 3, sb = j & 7;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (REG)
+            o.wf[tt][ks] = hl_pair(&sm.Whi[cb][16 * tt + lr][32 * ks + 8 * lg], &sm.Wlo[cb][16 * tt + lr][32 * ks + 8 * lg]);
+          o.qf[tt][ks] = frag_bf16(&sm.Q[xb][16 * tt + lr][32 * ks + 8 * lg]);
+        }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) o.ut4[tt] = *reinterpret_cast<const float4*>(&sm.Ut[cb][16 * rt + lr][16 * tt + 4 * lg]);
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) o.xf[kt] = frag_bf16(&sm.XT[xb][16 * kt + lr][8 * lg]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        o.pf[tt] = hl_pair(&sm.Phi[cb][16 * tt + lr][8 * lg], &sm.Plo[cb][16 * tt + lr][8 * lg]);
+        o.gt[tt] = sm.gam[sb][16 * tt + lr];
+      }
+      o.gC = sm.gam[sb][CS - 1];
+      return o;
+    };
+    StateOps ops;
+    for (int c = -5; c < cend; ++c) {
       if (state_wave && c >= 0 && c < nchunks) {
         // ---- state chain of chunk c (registers) ----
-        const int cb = c & 1, xb = c & 3;
         const long t0 = (long)c * CS;
-        // every LDS operand of the chunk is read before the first product
-        bf16x8 qf[2][NKS], xf[NKT];
-        HL wf[2][NKS], pf[2];
-        float4 ut4[2];
-        float gt[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            if constexpr (REG)
-              wf[tt][ks] = hl_pair(&sm.Whi[cb][16 * tt + lr][32 * ks + 8 * lg], &sm.Wlo[cb][16 * tt + lr][32 * ks + 8 * lg]);
-            qf[tt][ks] = frag_bf16(&sm.Q[xb][16 * tt + lr][32 * ks + 8 * lg]);
-          }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) ut4[tt] = *reinterpret_cast<const float4*>(&sm.Ut[cb][16 * rt + lr][16 * tt + 4 * lg]);
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) xf[kt] = frag_bf16(&sm.XT[xb][16 * kt + lr][8 * lg]);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          pf[tt] = hl_pair(&sm.Phi[cb][16 * tt + lr][8 * lg], &sm.Plo[cb][16 * tt + lr][8 * lg]);
-          gt[tt] = sm.gam[xb][16 * tt + lr];
-        }
-        const float gC = sm.gam[xb][CS - 1];
-
         floatx4 oacc[2], zacc[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -600,40 +608,42 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
           zacc[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            if constexpr (REG) zacc[tt] = mma3(zacc[tt], wf[tt][ks], sf[ks]);   // (Wt^T S)[t][i]
-            oacc[tt] = mma2(oacc[tt], sf[ks], qf[tt][ks]);                      // (S q)[i][t]
+            if constexpr (REG) zacc[tt] = mma3(zacc[tt], ops.wf[tt][ks], sf[ks]);   // (Wt^T S)[t][i]
+            oacc[tt] = mma2(oacc[tt], sf[ks], ops.qf[tt][ks]);                      // (S q)[i][t]
           }
         }
         // z[t][i] = Ut[i][t] - (Wt^T S)[t][i]; lane: t = 16 tt + 4 lg + e, i = lr
         float z[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          z[tt][0] = ut4[tt].x - zacc[tt][0];
-          z[tt][1] = ut4[tt].y - zacc[tt][1];
-          z[tt][2] = ut4[tt].z - zacc[tt][2];
-          z[tt][3] = ut4[tt].w - zacc[tt][3];
+          z[tt][0] = ops.ut4[tt].x - zacc[tt][0];
+          z[tt][1] = ops.ut4[tt].y - zacc[tt][1];
+          z[tt][2] = ops.ut4[tt].z - zacc[tt][2];
+          z[tt][3] = ops.ut4[tt].w - zacc[tt][3];
         }
         const HL zf = hl_two(z[0], z[1]);                               // rows i, t in fragment order
         // carry: S[i][k] <- g_{C-1} (S[i][k] + sum_t z[i][t] x_t[k])
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
           floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-          cacc = mma2(cacc, xf[kt], zf);
+          cacc = mma2(cacc, ops.xf[kt], zf);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[kt][e] = gC * (sv[kt][e] + cacc[e]);
+          for (int e = 0; e < 4; ++e) sv[kt][e] = ops.gC * (sv[kt][e] + cacc[e]);
         }
         // readout: o[t][i] = g_t ((S q)[i][t] + sum_{s<=t} z[i][s] (q_t . x_s))
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          oacc[tt] = mma3(oacc[tt], zf, pf[tt]);
+          oacc[tt] = mma3(oacc[tt], zf, ops.pf[tt]);
           const int t = 16 * tt + lr;
+          const float gt = ops.gt[tt];
           if (t0 + t < L)
             *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + 16 * rt + 4 * lg) =
-                make_float4(gt[tt] * oacc[tt][0], gt[tt] * oacc[tt][1], gt[tt] * oacc[tt][2], gt[tt] * oacc[tt][3]);
+                make_float4(gt * oacc[tt][0], gt * oacc[tt][1], gt * oacc[tt][2], gt * oacc[tt][3]);
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
       }
+      if (state_wave && c + 1 >= 0 && c + 1 < nchunks) ops = load_ops(c + 1);
       __syncthreads();
     }
     if (state_wave && a.S_out) {
@@ -644,81 +654,79 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     }
   } else {
     // ---------------- preparation waves ----------------
-    // iteration c:  wave 2  Gram of c+3, q.x of c+1
-    //               wave 3  Wt tiles 0, 1 of c+1    wave 6  Wt tiles 2, 3 of c+1
-    //               wave 7  Ut tiles of c+1
-    //               waves 2, 3, 6, 7  commit keys of c+4, queries of c+2
-    //               wave 4  scalars of c+3, keys of c+2 transposed, commit gains of
-    //                       c+4 and values of c+2
-    //               wave 5  factors of c+2 (inner-product family: z of c+1 in part
-    //                       and the keys of c+2 transposed, instead of wave 4)
+    // iteration c:  wave 2  Gram of c+4, q.x of c+2, keys of c+3 transposed
+    //               wave 3  Wt tiles 0, 1 of c+2    wave 6  Wt tiles 2, 3 of c+2
+    //               wave 7  Ut tiles of c+2
+    //               waves 2, 3, 6, 7  commit keys of c+5, queries of c+3
+    //               wave 4  scalars of c+4, commit gains of c+5 and values of c+3
+    //               wave 5  factors of c+3 (inner-product family: part of z of c+2)
     // A wave reads its LDS operands first, then commits, then computes (the LDS
     // round trip overlaps the commit).  Global loads are issued two iterations
     // before their commit, into two register sets used alternately.  Each role
     // runs its own loop (same barrier count), so it carries only its registers.
-    const int cend = nchunks + (nchunks & 1);
-    if (wave != 4 && wave != 5) {
+    // keys and queries move on waves 2, 3, 6, 7 inside their role's own loop
+    auto kq_loop = [&](auto&& body) __attribute__((always_inline)) {
       KQSet ps0, ps1;
       prefetch_kq(ps0, 0, -2);
       prefetch_kq(ps1, 1, -1);
       __syncthreads();
-      auto iteration = [&](int c, KQSet& cur) __attribute__((always_inline)) {
-        const bool v1 = c + 1 >= 0 && c + 1 < nchunks;
-        const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
-        auto move = [&]() __attribute__((always_inline)) {
-          commit_kq(cur, c + 4, c + 2);
-          prefetch_kq(cur, c + 6, c + 4);
-        };
-        if (wave == 2) {
-          const RowFrags xg = row_frags(sm.X[(c + 3) & 3]);
-          const RowFrags xq = row_frags(sm.X[(c + 1) & 3]);
-          const RowFrags qq = row_frags(sm.Q[(c + 1) & 3]);
-          move();
-          if (REG && v3) gram_store(c + 3, xg);
-          if (v1) qx_store(c + 1, xq, qq);
-        } else {
-          if constexpr (REG) {
-            const bool keys = wave != 7;
-            const int t0 = keys ? (wave == 3 ? 0 : 2) : 0;   // first tile of the pair
-            const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
-            const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 6 has no key tiles
-            const SolveA f = solve_factors_load(c + 1, keys);
-            const SolveIn in0 = solve_load(c + 1, keys, lt0, f);
-            const SolveIn in1 = solve_load(c + 1, keys, two ? lt0 + 1 : lt0, f);
-            move();
-            if (v1 && (!keys || t0 < NKT)) {
-              solve_store(c + 1, keys, t0, f, in0);
-              if (two) solve_store(c + 1, keys, t0 + 1, f, in1);
-            }
-          } else {
-            move();
-            if (v1) zeta_y(c + 1, 64 * (kq_slot - 1) + lane);      // waves 3, 6, 7: items 0..191
-          }
-        }
-      };
-      for (int c = -4; c < cend; c += 2) {
-        iteration(c, ps0);
+      for (int c = -5; c < cend; c += 2) {
+        body(c, [&]() __attribute__((always_inline)) {
+          commit_kq(ps0, c + 5, c + 3);
+          prefetch_kq(ps0, c + 7, c + 5);
+        });
         __syncthreads();
-        iteration(c + 1, ps1);
+        body(c + 1, [&]() __attribute__((always_inline)) {
+          commit_kq(ps1, c + 6, c + 4);
+          prefetch_kq(ps1, c + 8, c + 6);
+        });
         __syncthreads();
       }
+    };
+    if (wave == 2) {
+      kq_loop([&](int c, auto&& move) __attribute__((always_inline)) {
+        const RowFrags xg = row_frags(sm.X[(c + 4) & 3]);
+        const RowFrags xq = row_frags(sm.X[(c + 2) & 3]);
+        const RowFrags qq = row_frags(sm.Q[(c + 2) & 3]);
+        move();
+        if (REG && live_chunk(c + 4)) gram_store(c + 4, xg);
+        if (live_chunk(c + 2)) qx_store(c + 2, xq, qq);
+        if (live_chunk(c + 3)) {
+          transpose_keys(c + 3, lane);
+          transpose_keys(c + 3, 64 + lane);
+        }
+      });
+    } else if (wave != 4 && wave != 5) {
+      kq_loop([&](int c, auto&& move) __attribute__((always_inline)) {
+        if constexpr (REG) {
+          const bool keys = wave != 7;
+          const int t0 = keys ? (wave == 3 ? 0 : 2) : 0;   // first tile of the pair
+          const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
+          const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 6 has no key tiles
+          const SolveA f = solve_factors_load(c + 2, keys);
+          const SolveIn in0 = solve_load(c + 2, keys, lt0, f);
+          const SolveIn in1 = solve_load(c + 2, keys, two ? lt0 + 1 : lt0, f);
+          move();
+          if (live_chunk(c + 2) && (!keys || t0 < NKT)) {
+            solve_store(c + 2, keys, t0, f, in0);
+            if (two) solve_store(c + 2, keys, t0 + 1, f, in1);
+          }
+        } else {
+          move();
+          if (live_chunk(c + 2)) zeta_y(c + 2, 64 * (kq_slot - 1) + lane);      // waves 3, 6, 7: items 0..191
+        }
+      });
     } else if (wave == 4) {
       VBSet ps0, ps1;
       prefetch_vb(ps0, 0, -2);
       prefetch_vb(ps1, 1, -1);
       __syncthreads();
       auto iteration = [&](int c, VBSet& cur) __attribute__((always_inline)) {
-        const bool v2 = c + 2 >= 0 && c + 2 < nchunks;
-        const bool v3 = c + 3 >= 0 && c + 3 < nchunks;
-        commit_vb(cur, c + 4, c + 2);
-        prefetch_vb(cur, c + 6, c + 4);
-        if (v3) scalars(c + 3);
-        if (REG && v2) {        // inner-product family: wave 5 transposes the keys
-          transpose_keys(c + 2, lane);
-          transpose_keys(c + 2, 64 + lane);
-        }
+        commit_vb(cur, c + 5, c + 3);
+        prefetch_vb(cur, c + 7, c + 5);
+        if (c + 4 >= 0 && c + 4 < nchunks) scalars(c + 4);
       };
-      for (int c = -4; c < cend; c += 2) {
+      for (int c = -5; c < cend; c += 2) {
         iteration(c, ps0);
         __syncthreads();
         iteration(c + 1, ps1);
@@ -726,15 +734,11 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
       }
     } else {
       __syncthreads();
-      for (int c = -4; c < cend; ++c) {
+      for (int c = -5; c < cend; ++c) {
         if constexpr (REG) {
-          if (c + 2 >= 0 && c + 2 < nchunks) solve_factors(c + 2, [&]() __attribute__((always_inline)) {});
+          if (c + 3 >= 0 && c + 3 < nchunks) solve_factors(c + 3, [&]() __attribute__((always_inline)) {});
         } else {
-          if (c + 1 >= 0 && c + 1 < nchunks) zeta_y(c + 1, 192 + lane);
-          if (c + 2 >= 0 && c + 2 < nchunks) {
-            transpose_keys(c + 2, lane);
-            transpose_keys(c + 2, 64 + lane);
-          }
+          if (c + 2 >= 0 && c + 2 < nchunks) zeta_y(c + 2, 192 + lane);
         }
         __syncthreads();
       }
