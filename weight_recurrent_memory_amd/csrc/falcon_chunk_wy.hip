@@ -82,13 +82,12 @@ struct WyGeom {
   int nchunks;
 };
 
-// the three passes accumulate independently (no MFMA waits on the previous one)
+// split-bf16 product: the three passes chain through the accumulator (the matrix
+// core forwards it between back-to-back products), small terms first
 __device__ __forceinline__ floatx4 mma3(floatx4 acc, const HL& a, const HL& b) {
-  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  const floatx4 c1 = mfma16(a.hi, b.lo, z);
-  const floatx4 c2 = mfma16(a.lo, b.hi, z);
-  acc = mfma16(a.hi, b.hi, acc);
-  return acc + (c1 + c2);
+  acc = mfma16(a.hi, b.lo, acc);
+  acc = mfma16(a.lo, b.hi, acc);
+  return mfma16(a.hi, b.hi, acc);
 }
 __device__ __forceinline__ floatx4 mma2(floatx4 acc, const bf16x8& a, const HL& b) {
   acc = mfma16(a, b.hi, acc);
