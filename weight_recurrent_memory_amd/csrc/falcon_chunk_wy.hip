@@ -61,12 +61,13 @@ struct WyLds {
   uint16_t X[4][CS][XR];                 // keys by chunk & 3, k in fragment order
   uint16_t Q[4][CS][XR];                 // queries by chunk & 3
   uint16_t XT[4][DK][TR];                // keys transposed, t in fragment order
-  uint16_t YT[2][RW][TR];                // values transposed, t natural
+  uint16_t YT[2][RW][TR];                // values transposed, t in fragment order
   uint16_t Phi[2][CS][TR];               // q.x (s <= t), s in fragment order
   uint16_t Plo[2][CS][TR];
   uint16_t Whi[2][CS][XR];               // Wt^T[t][k], k in fragment order
   uint16_t Wlo[2][CS][XR];
   float SA[2][2][16][CS + 8];            // [T_00 | 0], [T_11 | -T_11 M_10], fragment order
+  float TT[2][16][16 + 4];               // T_00^T (row = column of T_00)
   float G[2][CS][CS + 8];                // Gram (whole 32 x 32)
   float Ut[2][RW][CS + 8];               // Ut[i][t]
   float beta[4][CS];                     // gains by chunk & 3
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
           const uint32_t x = w[2 * e + (ii >> 1)];
           h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
         }
-        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][vb_i4 + ii][vb_t4]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][vb_i4 + ii][fpos(vb_t4)]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
     }
     if (live_chunk(jb) && vt_id < CS)
@@ -458,71 +459,75 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
 #pragma unroll
       for (int m = 0; m < 16; ++m) sm.SA[gb][blk][m][p] = rhs[m];
     }
-  };
-  // Blocked solve of chunk j for 16-column tiles of R = [omega x | zeta y]:
-  // keys: columns 16 tile.. of the keys (-> Wt^T); else value rows 16 tile.. (-> Ut).
-  // The factors and the row scales are read once for the tiles of a wave.
-  struct SolveA {
-    HL a0, a1;
-    float4 s0, s1;
-  };
-  struct SolveIn {
-    float r0[4], r1[4];
-  };
-  auto solve_factors_load = [&](int j, bool keys) __attribute__((always_inline)) {
-    const int gb = j & 1, sb = j & 7;
-    SolveA f;
-    f.s0 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][4 * lg] : &sm.zeta[sb][4 * lg]);
-    f.s1 = *reinterpret_cast<const float4*>(keys ? &sm.omega[sb][16 + 4 * lg] : &sm.zeta[sb][16 + 4 * lg]);
-    f.a0 = hl_f32(&sm.SA[gb][0][lr][8 * lg]);
-    f.a1 = hl_f32(&sm.SA[gb][1][lr][8 * lg]);
-    return f;
-  };
-  auto solve_load = [&](int j, bool keys, int tile, const SolveA& f) __attribute__((always_inline)) {
-    const int gb = j & 1, xb = j & 3;
-    SolveIn in;
-    uint2 x0, x1;
-    if (keys) {   // XT positions 8 lg.. hold t = 4 lg.., 8 lg + 4.. hold t = 16 + 4 lg..
-      x0 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg]);
-      x1 = *reinterpret_cast<const uint2*>(&sm.XT[xb][16 * tile + lr][8 * lg + 4]);
-    } else {
-      x0 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][4 * lg]);
-      x1 = *reinterpret_cast<const uint2*>(&sm.YT[gb][16 * tile + lr][16 + 4 * lg]);
+    if (lane < 16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(&sm.TT[gb][lane][4 * q]) = make_float4(rhs[4 * q], rhs[4 * q + 1], rhs[4 * q + 2], rhs[4 * q + 3]);
     }
-    in.r0[0] = f.s0.x * __uint_as_float(x0.x << 16);
-    in.r0[1] = f.s0.y * __uint_as_float(x0.x & 0xFFFF0000u);
-    in.r0[2] = f.s0.z * __uint_as_float(x0.y << 16);
-    in.r0[3] = f.s0.w * __uint_as_float(x0.y & 0xFFFF0000u);
-    in.r1[0] = f.s1.x * __uint_as_float(x1.x << 16);
-    in.r1[1] = f.s1.y * __uint_as_float(x1.x & 0xFFFF0000u);
-    in.r1[2] = f.s1.z * __uint_as_float(x1.y << 16);
-    in.r1[3] = f.s1.w * __uint_as_float(x1.y & 0xFFFF0000u);
-    return in;
   };
-  // W_0 = T_00 R_0 (lane: t = 4 lg + e, column lr), W_1 = [T_11 | -T_11 M_10] [R_1 ; W_0].
-  // Key tiles are stored as Wt^T rows (8-byte stores): the same products with the
-  // operands swapped give the transposed tiles (lane: 4 consecutive k of one t).
-  auto solve_store = [&](int j, bool keys, int tile, const SolveA& f, const SolveIn& in) __attribute__((always_inline)) {
+  // Blocked solve of chunk j as one product.  With the row scales s (omega for
+  // the keys, zeta for the values) folded into the factor,
+  //   W = F [x | y],   F = T diag(s) = [[T_00 S_0, 0], [N T_00 S_0, T_11 S_1]],
+  // N = -T_11 M_10.  Lane (lr, lg) builds rows lr (block 0) and 16 + lr (block 1)
+  // of F at fragment slots 8 lg.. (steps 4 lg..) and 8 lg + 4.. (steps 16 + 4 lg..);
+  // N T_00 is one small split-bf16 product.  Key tiles give Wt^T rows (lane: 4
+  // consecutive k of one t), value tiles Ut rows (lane: 4 consecutive t of one i).
+  struct SolveOps {
+    float4 s0, s1, t00, t11, n, tt;
+    bf16x8 op[2];            // the x or y fragments of the wave's two tiles
+  };
+  struct FRows {
+    HL f[2];
+  };
+  auto solve_load = [&](int j, bool keys, int tile0, int tile1) __attribute__((always_inline)) {
+    const int gb = j & 1, sb = j & 7, xb = j & 3;
+    SolveOps o;
+    const float* sc = keys ? sm.omega[sb] : sm.zeta[sb];
+    o.s0 = *reinterpret_cast<const float4*>(sc + 4 * lg);
+    o.s1 = *reinterpret_cast<const float4*>(sc + 16 + 4 * lg);
+    o.t00 = *reinterpret_cast<const float4*>(&sm.SA[gb][0][lr][8 * lg]);
+    o.t11 = *reinterpret_cast<const float4*>(&sm.SA[gb][1][lr][8 * lg]);
+    o.n = *reinterpret_cast<const float4*>(&sm.SA[gb][1][lr][8 * lg + 4]);
+    o.tt = *reinterpret_cast<const float4*>(&sm.TT[gb][lr][4 * lg]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int tile = e ? tile1 : tile0;
+      o.op[e] = keys ? frag_bf16(&sm.XT[xb][16 * tile + lr][8 * lg]) : frag_bf16(&sm.YT[gb][16 * tile + lr][8 * lg]);
+    }
+    return o;
+  };
+  auto factor_rows = [&](const SolveOps& o) __attribute__((always_inline)) {
+    const float z4[4] = {0.f, 0.f, 0.f, 0.f};
+    const float av[4] = {o.tt.x, o.tt.y, o.tt.z, o.tt.w};
+    const float bv[4] = {o.n.x, o.n.y, o.n.z, o.n.w};
+    // (T_00^T N^T)[c][m] with c = 4 lg + e, m = lr: the lane gets (N T_00)[lr][4 lg + e]
+    const floatx4 p = mma3(floatx4{0.f, 0.f, 0.f, 0.f}, hl_two(av, z4), hl_two(bv, z4));
+    const float f0[4] = {o.t00.x * o.s0.x, o.t00.y * o.s0.y, o.t00.z * o.s0.z, o.t00.w * o.s0.w};
+    const float f1a[4] = {p[0] * o.s0.x, p[1] * o.s0.y, p[2] * o.s0.z, p[3] * o.s0.w};
+    const float f1b[4] = {o.t11.x * o.s1.x, o.t11.y * o.s1.y, o.t11.z * o.s1.z, o.t11.w * o.s1.w};
+    FRows r;
+    r.f[0] = hl_two(f0, z4);
+    r.f[1] = hl_two(f1a, f1b);
+    return r;
+  };
+  auto solve_tile = [&](int j, bool keys, int tile, const FRows& r, const bf16x8& op) __attribute__((always_inline)) {
     const int gb = j & 1;
-    const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
     const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
-    const HL b0 = hl_two(in.r0, zero4);
-    const floatx4 w0 = mma3(zacc, f.a0, b0);
-    const float w0v[4] = {w0[0], w0[1], w0[2], w0[3]};
-    const HL b1 = hl_two(in.r1, w0v);
     if (keys) {
-      const floatx4 v0 = mma3(zacc, b0, f.a0);
-      const floatx4 v1 = mma3(zacc, b1, f.a1);
       const int p = fpos(16 * tile + 4 * lg);
-      const float f0[4] = {v0[0], v0[1], v0[2], v0[3]};
-      const float f1[4] = {v1[0], v1[1], v1[2], v1[3]};
-      store_split4(&sm.Whi[gb][lr][p], &sm.Wlo[gb][lr][p], f0);
-      store_split4(&sm.Whi[gb][16 + lr][p], &sm.Wlo[gb][16 + lr][p], f1);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const floatx4 w = mma2(zacc, op, r.f[tt]);        // Wt^T[16 tile + 4 lg + e][16 tt + lr]
+        const float f[4] = {w[0], w[1], w[2], w[3]};
+        store_split4(&sm.Whi[gb][16 * tt + lr][p], &sm.Wlo[gb][16 * tt + lr][p], f);
+      }
     } else {
-      const floatx4 w1 = mma3(zacc, f.a1, b1);
       float* u = &sm.Ut[gb][16 * tile + lr][0];
-      *reinterpret_cast<float4*>(u + 4 * lg) = make_float4(w0[0], w0[1], w0[2], w0[3]);
-      *reinterpret_cast<float4*>(u + 16 + 4 * lg) = make_float4(w1[0], w1[1], w1[2], w1[3]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const floatx4 w = mma2(zacc, r.f[tt], op);        // Ut[16 tile + lr][16 tt + 4 lg + e]
+        *reinterpret_cast<float4*>(u + 16 * tt + 4 * lg) = make_float4(w[0], w[1], w[2], w[3]);
+      }
     }
   };
   // inner-product family: z_t = zeta_t y_t, kept where the regression keeps Ut;
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     const int gb = j & 1, sb = j & 7;
     if (idx < RW * (CS / 4)) {
       const int i = idx / (CS / 4), t4 = 4 * (idx % (CS / 4));
-      const uint2 yb = *reinterpret_cast<const uint2*>(&sm.YT[gb][i][t4]);
+      const uint2 yb = *reinterpret_cast<const uint2*>(&sm.YT[gb][i][fpos(t4)]);
       const float4 z = *reinterpret_cast<const float4*>(&sm.zeta[sb][t4]);
       *reinterpret_cast<float4*>(&sm.Ut[gb][i][t4]) =
           make_float4(z.x * __uint_as_float(yb.x << 16), z.y * __uint_as_float(yb.x & 0xFFFF0000u),
@@ -702,13 +707,12 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
           const int t0 = keys ? (wave == 3 ? 0 : 2) : 0;   // first tile of the pair
           const bool two = keys ? (t0 + 1 < NKT) : (nrb > 1);
           const int lt0 = (!keys || t0 < NKT) ? t0 : 0;   // dk = 32: wave 6 has no key tiles
-          const SolveA f = solve_factors_load(c + 2, keys);
-          const SolveIn in0 = solve_load(c + 2, keys, lt0, f);
-          const SolveIn in1 = solve_load(c + 2, keys, two ? lt0 + 1 : lt0, f);
+          const SolveOps o = solve_load(c + 2, keys, lt0, two ? lt0 + 1 : lt0);
           move();
           if (live_chunk(c + 2) && (!keys || t0 < NKT)) {
-            solve_store(c + 2, keys, t0, f, in0);
-            if (two) solve_store(c + 2, keys, t0 + 1, f, in1);
+            const FRows r = factor_rows(o);
+            solve_tile(c + 2, keys, t0, r, o.op[0]);
+            if (two) solve_tile(c + 2, keys, t0 + 1, r, o.op[1]);
           }
         } else {
           move();
