@@ -71,6 +71,7 @@ struct WyLds {
   float G[2][CS][CS + 8];                // Gram (whole 32 x 32)
   float Ut[2][RW][CS + 8];               // Ut[i][t]
   float beta[4][CS];                     // gains by chunk & 3
+  float knorm[4][CS];                    // squared key norms by chunk & 3
   alignas(16) float gam[8][CS];          // per-step scalars by chunk & 7
   alignas(16) float gm1[8][CS];
   alignas(16) float zeta[8][CS];
@@ -167,17 +168,24 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   // ---------------- global loads and their commits to LDS ----------------
   // Waves 2, 3, 6, 7 move keys and queries (one 16-byte piece of a row per
   // thread), wave 4 values and gains.  A load is issued two iterations before its
-  // commit, into one of two register sets used alternately.  Every prefetch
-  // issues the same loads in the same order whatever the chunk and the lane (a
-  // piece out of range reads the chain's first row instead and is zeroed at
-  // commit), so the wait before a commit counts only the loads of its own set.
-  constexpr int KQ = (CS * VPR + 255) / 256;
+  // commit, into one of two register sets used alternately.  The loads go through
+  // per-chain buffer resources: a piece past the end of the sequence (or before
+  // its start, or a padding lane's, whose offset is parked above 2^31) reads 0,
+  // so every prefetch issues the same loads in the same order and the wait before
+  // a commit counts only the loads of its own set.  The per-lane offsets are fixed;
+  // a chunk adds a uniform stride.
+  static_assert(CS * VPR <= 256, "one key piece and one query piece per thread");
   struct KQSet {            // one 16-byte piece of a key row and of a query row
-    uint4 k[KQ], q[KQ];
+    uint4 k, q;
   };
   struct VBSet {            // a 4 (steps) x 4 (value rows) block and one gain
     uint4 v, v2;
     uint32_t b;
+  };
+  constexpr int BUF_WORD3 = 0x00020000;     // raw 32-bit buffer, range checked
+  constexpr uint32_t PARKED = 0xC0000000u;  // offset that is always out of range
+  auto rsrc = [](const void* base, long bytes) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, BUF_WORD3);
   };
   // waves w and w + 4 share a SIMD (and its matrix core): the state waves 0, 1 are
   // paired with the VALU/LDS roles on waves 4, 5; the matrix-core roles take 2, 3, 6, 7
@@ -185,122 +193,106 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   const int kt_id = 64 * kq_slot + lane;   // 0..255 on waves 2, 3, 6, 7
   const int vt_id = lane;                  // 0..63 on wave 4
   auto live_chunk = [&](int j) __attribute__((always_inline)) { return j >= 0 && j < nchunks; };
-  // key x_g = k_{g-1}; x_0 = k_prev, or 0 on a fresh sequence
-  auto key_ok = [&](int j, int t) __attribute__((always_inline)) {
-    return live_chunk(j) && t < steps(j) && ((long)j * CS + t >= 1 || kpg != nullptr);
+  // key and query piece of this thread: step kq_t of the chunk, k = 8 kq_kv ..
+  const bool kq_in = kt_id < CS * VPR;     // uniform per wave
+  const int kq_t = kt_id / VPR, kq_kv = kt_id % VPR;
+  const auto rk = rsrc(kg + qk_base, L * DK * 2);
+  const auto rq = rsrc(qg + qk_base, L * DK * 2);
+  // key x_g = k_{g-1}: row g - 1 (the first step of the sequence reads 0 there and
+  // takes k_prev at commit)
+  const uint32_t koff = kq_in ? (uint32_t)(((kq_t - 1) * DK + kq_kv * 8) * 2) : PARKED;
+  const uint32_t qoff = kq_in ? (uint32_t)((kq_t * DK + kq_kv * 8) * 2) : PARKED;
+  constexpr uint32_t KQ_CHUNK = CS * DK * 2;
+  auto ld128 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
   };
   // keys of chunk jk, queries of chunk jq
   auto prefetch_kq = [&](KQSet& p, int jk, int jq) __attribute__((always_inline)) {
-    const uint16_t* first = kg + qk_base;
-#pragma unroll
-    for (int u = 0; u < KQ; ++u) {
-      const int idx = kt_id + 256 * u;
-      const int t = idx / VPR, kv = idx % VPR;
-      const bool in = idx < CS * VPR;
-      const long g = (long)jk * CS + t;
-      const uint16_t* ks = first;
-      if (in && key_ok(jk, t)) ks = g >= 1 ? kg + qk_base + (g - 1) * DK + kv * 8 : kpg + (long)chain * DK + kv * 8;
-      const uint16_t* qs = qg + qk_base;
-      if (in && live_chunk(jq) && t < steps(jq)) qs = qg + qk_base + ((long)jq * CS + t) * DK + kv * 8;
-      p.k[u] = *reinterpret_cast<const uint4*>(ks);
-      p.q[u] = *reinterpret_cast<const uint4*>(qs);
-    }
+    p.k = ld128(rk, koff + (uint32_t)jk * KQ_CHUNK);
+    p.q = ld128(rq, qoff + (uint32_t)jq * KQ_CHUNK);
   };
+  uint4 kprev = {0u, 0u, 0u, 0u};          // x_0 of the chain (0 on a fresh sequence)
+  if (kpg != nullptr && kq_in && kq_t == 0 && wave >= 2 && wave != 4 && wave != 5)
+    kprev = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kq_kv * 8);
   // 8 consecutive k (k0 % 8 == 0) -> two 4-groups at their fragment positions
   auto put8 = [&](uint16_t* row, int k0, uint4 val) __attribute__((always_inline)) {
     *reinterpret_cast<uint2*>(row + fpos(k0)) = make_uint2(val.x, val.y);
     *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
   };
+  // The keys' squared norms are formed here, from the registers: packed bf16 dot
+  // products, then a sum over the VPR threads of a row by DPP row shifts (the
+  // row's last thread ends with the total).
   auto commit_kq = [&](const KQSet& p, int jk, int jq) __attribute__((always_inline)) {
-    const uint4 zero = {0u, 0u, 0u, 0u};
+    if (kq_in) {
+      if (live_chunk(jk)) {
+        const uint4 kv = (jk == 0 && kq_t == 0) ? kprev : p.k;
+        put8(&sm.X[jk & 3][kq_t][0], kq_kv * 8, kv);
+        float part = 0.0f;
+        const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-    for (int u = 0; u < KQ; ++u) {
-      const int idx = kt_id + 256 * u;
-      const int t = idx / VPR, kv = idx % VPR;
-      if (idx < CS * VPR) {
-        if (live_chunk(jk)) put8(&sm.X[jk & 3][t][0], kv * 8, key_ok(jk, t) ? p.k[u] : zero);
-        if (live_chunk(jq)) put8(&sm.Q[jq & 3][t][0], kv * 8, t < steps(jq) ? p.q[u] : zero);
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 v = __builtin_bit_cast(bf16x2, w4[e]);
+          part = __builtin_amdgcn_fdot2_f32_bf16(v, v, part, false);
+        }
+        part += dpp_shr<1>(part, 0.0f);
+        part += dpp_shr<2>(part, 0.0f);
+        if constexpr (VPR == 8) part += dpp_shr<4>(part, 0.0f);
+        if (kq_kv == VPR - 1) sm.knorm[jk & 3][kq_t] = part;
       }
+      if (live_chunk(jq)) put8(&sm.Q[jq & 3][kq_t][0], kq_kv * 8, p.q);
     }
   };
   // a 4 (steps) x 4 (value rows) block of wave 4's lane: steps t4.., value rows i4..
   const int vb_i4 = 4 * (vt_id % (RW / 4)), vb_t4 = 4 * (vt_id / (RW / 4));
-  auto value_ok = [&](int j, int e) __attribute__((always_inline)) {
-    return live_chunk(j) && vb_t4 + e < steps(j) && i0 + vb_i4 < dv;
-  };
-  auto gain_ok = [&](int j) __attribute__((always_inline)) {
-    return a.beta_kind == 1 && live_chunk(j) && vt_id < steps(j);
-  };
+  const auto rv = rsrc(vg + v_base, L * dv * 2);
+  const auto rb = a.beta_kind == 1 ? rsrc(bg + (long)chain * L, L * 2) : rsrc(vg, 0);
+  const uint32_t voff = i0 + vb_i4 < dv ? (uint32_t)((vb_t4 * dv + i0 + vb_i4) * 2) : PARKED;
+  const uint32_t V_CHUNK = (uint32_t)(CS * dv * 2);
   // gains of chunk jb, values of chunk jv
   auto prefetch_vb = [&](VBSet& p, int jb, int jv) __attribute__((always_inline)) {
-    const long t0 = (long)jv * CS;
     uint32_t w[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint16_t* src = vg + v_base;
-      if (value_ok(jv, e)) src = vg + v_base + (t0 + vb_t4 + e) * dv + i0 + vb_i4;
-      const uint2 val = *reinterpret_cast<const uint2*>(src);
-      w[2 * e] = val.x;
-      w[2 * e + 1] = val.y;
+      const auto val = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + (uint32_t)jv * V_CHUNK + (uint32_t)(e * dv * 2)), 0, 0);
+      w[2 * e] = val[0];
+      w[2 * e + 1] = val[1];
     }
     p.v = make_uint4(w[0], w[1], w[2], w[3]);
     p.v2 = make_uint4(w[4], w[5], w[6], w[7]);
-    const uint16_t* bsrc = vg + v_base;
-    if (gain_ok(jb)) bsrc = bg + (long)chain * L + (long)jb * CS + vt_id;
-    p.b = *bsrc;
+    p.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)((uint32_t)vt_id * 2 + (uint32_t)jb * (CS * 2)), 0, 0);
   };
   auto commit_vb = [&](const VBSet& p, int jb, int jv) __attribute__((always_inline)) {
     if (live_chunk(jv)) {
-      // rows: step t4+e holds values i4..i4+3 in (w[2e], w[2e+1])
-      uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!value_ok(jv, e)) w[2 * e] = w[2 * e + 1] = 0u;
+      // step t4+e holds values i4..i4+3 in (w[2e], w[2e+1]); value row i4+ii takes
+      // the low (ii even) or high (ii odd) halves of w[2e + ii/2], e = 0..3
+      const uint32_t w[8] = {p.v.x, p.v.y, p.v.z, p.v.w, p.v2.x, p.v2.y, p.v2.z, p.v2.w};
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        uint32_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = w[2 * e + (ii >> 1)];
-          h[e] = (ii & 1) ? (x >> 16) : (x & 0xFFFFu);
-        }
-        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][vb_i4 + ii][fpos(vb_t4)]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        const uint32_t sel = (ii & 1) ? 0x07060302u : 0x05040100u;
+        const int h = ii >> 1;
+        *reinterpret_cast<uint2*>(&sm.YT[jv & 1][vb_i4 + ii][fpos(vb_t4)]) =
+            make_uint2(__builtin_amdgcn_perm(w[2 + h], w[h], sel), __builtin_amdgcn_perm(w[6 + h], w[4 + h], sel));
       }
     }
     if (live_chunk(jb) && vt_id < CS)
-      sm.beta[jb & 3][vt_id] = a.beta_kind == 0 ? a.beta : (gain_ok(jb) ? bf16_to_f32((uint16_t)p.b) : 0.0f);
+      sm.beta[jb & 3][vt_id] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)p.b);
   };
 
   // eta_t = beta_t / (eps + ||x_t||^2), a_t = 1 - eta_t lambda; padded steps and
   // the fresh-sequence first step (x_1 = 0 on S_0 = 0) take eta = 0, a = 1.
-  // One wave: lane = step t (mod 32); lanes t and t + 32 take half of row t
-  // each, in packed bf16 dot products, and swap their partial sums.
+  // One wave: lane = step t (mod 32); the squared key norms were formed at commit.
   auto scalars = [&](int j) __attribute__((always_inline)) {
     const int sb = j & 7;
     const long t0 = (long)j * CS;
     const int c = steps(j);
     const int t = lane & 31;
     const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
-    const int half = (lane >> 5) * (DK / 2);
-    uint4 xr[DK / 16];
-#pragma unroll
-    for (int k8 = 0; k8 < DK / 2; k8 += 8) xr[k8 / 8] = *reinterpret_cast<const uint4*>(&sm.X[j & 3][t][half + k8]);
+    const float nrm = sm.knorm[j & 3][t];
     const float bv = sm.beta[j & 3][t];
-    float part = 0.0f;
-#pragma unroll
-    for (int k8 = 0; k8 < DK / 2; k8 += 8) {
-      const uint32_t w4[4] = {xr[k8 / 8].x, xr[k8 / 8].y, xr[k8 / 8].z, xr[k8 / 8].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 v = __builtin_bit_cast(bf16x2, w4[e]);
-        part = __builtin_amdgcn_fdot2_f32_bf16(v, v, part, false);
-      }
-    }
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    const float nrm = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     float eta = 0.0f, dec = 1.0f;
     if (live) {
-      eta = bv / (a.eps + nrm);
+      eta = bv * __builtin_amdgcn_rcpf(a.eps + nrm);
       dec = 1.0f - eta * a.lambda;
     }
     // inclusive prefix product over the 32 steps: within rows of 16 lanes by
@@ -315,7 +307,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     if (lane >= 16) gsc *= row0;
     const float gprev = dpp_shr<1>(gsc, lane == 16 ? row0 : 1.0f);
     if (lane < CS) {
-      const float z = eta / gsc;
+      const float z = eta * __builtin_amdgcn_rcpf(gsc);
       sm.gam[sb][t] = gsc;
       sm.gm1[sb][t] = gprev;
       sm.zeta[sb][t] = z;
@@ -765,7 +757,9 @@ hipError_t launch_wy(const SeqArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool chunk_wy_supported(const SeqArgs& a) {
-  return a.window == 1 && a.beta_kind != 2 && (a.dk == 32 || a.dk == 64);
+  // per-chain key, query and value blocks addressed by 32-bit buffer offsets
+  const long bytes = (long)a.seqlen * (a.dk > a.dv ? a.dk : a.dv) * 2;
+  return a.window == 1 && a.beta_kind != 2 && (a.dk == 32 || a.dk == 64) && bytes < (1L << 30);
 }
 
 // Window-1 chunk form with gains shared by the value rows, 32-step chunks.
