@@ -109,6 +109,24 @@ __device__ __forceinline__ float dpp_shr(float v, float fill) {
 __device__ __forceinline__ float lane_value(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
 }
+// acc + g(lane N of this 16-lane row) * r, the row broadcast folded into the
+// multiply-add as a DPP operand.  g is only ever loaded from LDS (never written by
+// the vector ALU), so the DPP read needs no wait states.
+template <int N>
+__device__ __forceinline__ float fmac_row_bcast(float acc, float g, float r) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(g), "v"(r), "i"(N));
+  return acc;
+}
+// forward substitution of (I + M) x = rhs over one 16-step block from step M on,
+// M = diag(om) L(G): lane m of each 16-lane row holds row m of the block's Gram
+// matrix in g[], so entry G[m][r] (= G[r][m]) is a row broadcast from lane m
+template <int M>
+__device__ __forceinline__ void sweep_from(float (&rhs)[16], float (&acc)[16], const float (&g)[16], const float (&om)[16]) {
+  rhs[M] = __builtin_fmaf(-om[M], acc[M], rhs[M]);
+#pragma unroll
+  for (int r = M + 1; r < 16; ++r) acc[r] = fmac_row_bcast<M>(acc[r], g[r], rhs[M]);
+  if constexpr (M < 15) sweep_from<M + 1>(rhs, acc, g, om);
+}
 // a split fragment from two groups of 4 fp32 (slots 0-3, 4-7)
 __device__ __forceinline__ HL hl_two(const float* a, const float* b) {
   const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -387,64 +405,41 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     }
   };
   // [T_00 | 0] and [T_11 | -T_11 M_10] of chunk j by forward substitution, one
-  // wave: lanes 0..15 the columns of T_00, lanes 16..47 the 32 columns of block 1.
-  // Every Gram entry the sweep uses is read before it starts (one wait).
-  auto solve_factors = [&](int j, auto&& between) __attribute__((always_inline)) {
+  // wave: lanes 0..15 the columns of T_00, lanes 16..47 the 32 columns of block 1
+  // (each 16-lane row holds one block; lanes 48..63 repeat block 1).
+  auto solve_factors = [&](int j) __attribute__((always_inline)) {
     const int gb = j & 1, sb = j & 7;
     const int blk = lane < 16 ? 0 : 1;
     const int col = lane < 16 ? lane : (lane < 48 ? lane - 16 : 0);   // 0..15 / 0..31
     const int u0 = 16 * blk;
     float rhs[16], acc[16];               // rhs becomes the solution in place
-    float om[16];
+    float om[16], g[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 o4 = *reinterpret_cast<const float4*>(&sm.omega[sb][u0 + 4 * q]);
       om[4 * q] = o4.x; om[4 * q + 1] = o4.y; om[4 * q + 2] = o4.z; om[4 * q + 3] = o4.w;
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + lr][u0 + 4 * q]);
+      g[4 * q] = g4.x; g[4 * q + 1] = g4.y; g[4 * q + 2] = g4.z; g[4 * q + 3] = g4.w;
     }
     // -M_10[:, c'] = -omega_{16+m} G[16+m][c'] = -omega_{16+m} G[c'][16+m]
     const int cp = (blk == 1 && col >= 16) ? col - 16 : 0;
     float4 gv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) gv[q] = *reinterpret_cast<const float4*>(&sm.G[gb][cp][16 + 4 * q]);
-    // rows 0..7 of the diagonal block (every 4-group that holds some r > m)
-    float4 gr[16][4];
+    const bool ncol = blk == 1 && col >= 16;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int q = 0; q < 4; ++q) {
+      const float gq[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (4 * q + 3 > m) gr[m][q] = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + m][u0 + 4 * q]);
-    between();
-    if (blk == 1 && col >= 16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rhs[4 * q] = -om[4 * q] * gv[q].x;
-        rhs[4 * q + 1] = -om[4 * q + 1] * gv[q].y;
-        rhs[4 * q + 2] = -om[4 * q + 2] * gv[q].z;
-        rhs[4 * q + 3] = -om[4 * q + 3] * gv[q].w;
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * q + e;
+        rhs[m] = ncol ? -om[m] * gq[e] : (m == col ? 1.0f : 0.0f);
       }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 16; ++m) rhs[m] = (m == col) ? 1.0f : 0.0f;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      if (m == 4) {   // rows 8..15, read while rows 4..7 are swept
-#pragma unroll
-        for (int m2 = 8; m2 < 16; ++m2)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (4 * q + 3 > m2) gr[m2][q] = *reinterpret_cast<const float4*>(&sm.G[gb][u0 + m2][u0 + 4 * q]);
-      }
-      rhs[m] -= om[m] * acc[m];
-#pragma unroll
-      for (int r = m + 1; r < 16; ++r) {   // column m below m: G[u0+r][u0+m] = G[u0+m][u0+r]
-        const float4 g4 = gr[m][r >> 2];
-        const float g = (r & 3) == 0 ? g4.x : (r & 3) == 1 ? g4.y : (r & 3) == 2 ? g4.z : g4.w;
-        acc[r] += g * rhs[m];
-      }
-    }
+    asm volatile("s_nop 4");              // any EXEC write settles before the DPP sweep
+    sweep_from<0>(rhs, acc, g, om);
     if (lane < 48) {
       const int cc = col & 15;
       const int p = 8 * (cc >> 2) + ((col >> 4) << 2) + (cc & 3);
@@ -731,7 +726,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
       __syncthreads();
       for (int c = -5; c < cend; ++c) {
         if constexpr (REG) {
-          if (c + 3 >= 0 && c + 3 < nchunks) solve_factors(c + 3, [&]() __attribute__((always_inline)) {});
+          if (c + 3 >= 0 && c + 3 < nchunks) solve_factors(c + 3);
         } else {
           if (c + 2 >= 0 && c + 2 < nchunks) zeta_y(c + 2, 192 + lane);
         }
