@@ -13,20 +13,22 @@
 // same for every value row, so with W = (I + M)^-1 R, R_t = [omega_t x_t | zeta_t y_t],
 //   z = Ut - S0 Wt,   Wt^T = W[:, keys],  Ut^T = W[:, values]
 //   o_t = g_t (S0 q_t + sum_{s<=t} (q_t . x_s) z_s),   S_C = g_{C-1} (S0 + sum_s z_s x_s^T)
-// W is formed by a blocked forward solve over 16-step blocks:
-//   W_0 = T_00 R_0,   W_1 = [T_11 | -T_11 M_10] [R_1 ; W_0],   T_bb = (I + M_bb)^-1
+// W is formed from 16-step blocks: T_bb = (I + M_bb)^-1 by forward substitution,
+// N = -T_11 M_10, and with the row scales s folded in (omega for x, zeta for y)
+//   W = F [x | y],   F = T diag(s) = [[T_00 S_0, 0], [N T_00 S_0, T_11 S_1]].
 // The inner-product family has z_t = zeta_t y_t (no solve).
 //
 // Structure.  One workgroup = 8 wave64 = one (batch*head) chain x 32 value
 // rows; chunks of C = 32 steps.  Waves 0 and 1 ("state waves") each own 16 rows
 // of the state: S (fp32) and z never leave their registers; per chunk they run
 // S q, z = Ut - Wt S, the carry S <- g (S + Z X^T) and the readout, four small
-// matrix-core products.  Waves 2..7 prepare later chunks, each stage reading
-// only what an earlier iteration wrote, so one barrier per chunk suffices:
-//   iteration c:  state chunk c | solve and q.x of c+1 | keys transposed,
-//                 scalars and [T_00], [T_11 | -T_11 M_10] of c+2 | Gram of c+3 |
-//                 keys of c+4, queries and values of c+2 to LDS (loaded one
-//                 iteration earlier)
+// matrix-core products, then read the next chunk's operands.  Waves 2..7 prepare
+// later chunks, each stage reading only what an earlier iteration wrote, so one
+// barrier per chunk suffices:
+//   iteration c:  state chunk c | Wt, Ut and q.x of c+2 | keys transposed and
+//                 factors T_00, [T_11 | N] of c+3 | Gram and scalars of c+4 |
+//                 keys of c+5, queries and values of c+3 to LDS (loaded two
+//                 iterations earlier)
 // LDS operands that meet a register operand of the state waves are stored in
 // the order of that register fragment: within every 32-wide group, positions
 // 8g..8g+3 hold indices 4g..4g+3 and 8g+4..8g+7 hold 16+4g..16+4g+3, so every
