@@ -590,6 +590,8 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
       return o;
     };
     StateOps ops;
+    // output row t of the current chunk, value columns i0 + 16 rt + 4 lg .. (t = lr here)
+    float* orow = a.o + v_base + (long)lr * dv + i0 + 16 * rt + 4 * lg;
     for (int c = -5; c < cend; ++c) {
       if (state_wave && c >= 0 && c < nchunks) {
         // ---- state chain of chunk c (registers) ----
@@ -618,23 +620,22 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
         // carry: S[i][k] <- g_{C-1} (S[i][k] + sum_t z[i][t] x_t[k])
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-          floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-          cacc = mma2(cacc, ops.xf[kt], zf);
+          const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, ops.xf[kt], zf);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[kt][e] = ops.gC * (sv[kt][e] + cacc[e]);
+          for (int e = 0; e < 4; ++e) sv[kt][e] = ops.gC * cacc[e];
         }
         // readout: o[t][i] = g_t ((S q)[i][t] + sum_{s<=t} z[i][s] (q_t . x_s))
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           oacc[tt] = mma3(oacc[tt], zf, ops.pf[tt]);
-          const int t = 16 * tt + lr;
           const float gt = ops.gt[tt];
-          if (t0 + t < L)
-            *reinterpret_cast<float4*>(a.o + v_base + (t0 + t) * dv + i0 + 16 * rt + 4 * lg) =
+          if (t0 + 16 * tt + lr < L)
+            *reinterpret_cast<float4*>(orow + 16 * tt * dv) =
                 make_float4(gt * oacc[tt][0], gt * oacc[tt][1], gt * oacc[tt][2], gt * oacc[tt][3]);
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+        orow += CS * dv;
       }
       if (state_wave && c + 1 >= 0 && c + 1 < nchunks) ops = load_ops(c + 1);
       __syncthreads();
