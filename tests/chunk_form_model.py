@@ -199,3 +199,89 @@ def chunk_forward_wy(regression, q, k, v, *, beta, lam, eps, chunk, beta_t=None,
         o[t0:t0 + c] = O.T[:c]
         S = g[-1] * (S + Z @ X)
     return o, S
+
+
+def chunk_forward_folded(regression, q, k, v, *, beta, lam, eps, window, beta_t=None,
+                         k_prev=None, S0=None, cs=16, blk=16):
+    """Key-folded form for a window B >= 1 with gains shared by the value rows.
+
+    Sub-chunks of cs steps; the key tile of sub-chunk c is the 2 cs keys of
+    sub-chunks c-1 and c (tile index m; key of unknown u = (t, w) is
+    m(u) = cs + t - w).  With V = (I + M)^-1 (M over the unknowns, coupling only
+    earlier steps) the state-independent matrices are
+      F_x = V diag(omega_u) Gath,  F_y = V diag(zeta_u) Gath   (Gath[u, m] = [m(u) = m])
+      H_x = Gath^T F_x,  H_y = Gath^T F_y,  Q_x = P' F_x,  Q_y = P' F_y
+    (P'[t, u] = (q_t . x_m(u)) [t(u) <= t]); the inner-product family has
+    F_x = 0 and F_y = diag(zeta_u) Gath.  Per value row the state enters only
+    through XS = X S0^T:
+      Fk = H_y Y - H_x XS,  o = g (Q S0^T + Q_y Y - Q_x XS),  S_c = g_last (S0 + Fk^T X).
+    """
+    L, dk = q.shape
+    dv = v.shape[1]
+    B = window
+    S = np.zeros((dv, dk)) if S0 is None else S0.astype(np.float64).copy()
+    o = np.zeros((L, dv))
+    NXT = 2 * cs
+
+    def key(g):
+        if g < 0:
+            return np.zeros(dk)
+        if g == 0:
+            return np.zeros(dk) if k_prev is None else k_prev.astype(np.float64)
+        return k[g - 1].astype(np.float64)
+
+    def val(g):
+        return np.zeros(dv) if g < 0 or g >= L else v[g].astype(np.float64)
+
+    for t0 in range(0, L, cs):
+        c = min(cs, L - t0)
+        U = cs * B
+        X = np.stack([key(t0 - cs + m) if t0 - cs + m < t0 + c else np.zeros(dk)
+                      for m in range(NXT)])                           # [2cs, dk]
+        Y = np.stack([val(t0 - cs + m) if t0 - cs + m < t0 + c else np.zeros(dv)
+                      for m in range(NXT)])
+        Q = np.zeros((cs, dk))
+        Q[:c] = q[t0:t0 + c]
+        mof = lambda u: cs + u // B - u % B
+        nrm = np.sum(X * X, axis=1)
+        eta = np.zeros(cs)
+        a = np.ones(cs)
+        for t in range(c):
+            n = sum(nrm[mof(t * B + w)] for w in range(B))
+            b = beta if beta_t is None else float(beta_t[t0 + t])
+            if not (t0 + t == 0 and k_prev is None):
+                eta[t] = b / (eps + n)
+                a[t] = 1.0 - eta[t] * lam
+        g = np.cumprod(a)
+        gm1 = np.concatenate([[1.0], g[:-1]])
+        zeta = eta / g
+        omega = zeta * gm1
+        G = X @ X.T
+        P = Q @ X.T
+        tu = np.arange(U) // B
+        Gath = np.zeros((U, NXT))
+        Gath[np.arange(U), [mof(u) for u in range(U)]] = 1.0
+        Pp = np.array([[P[t, mof(u)] if tu[u] <= t else 0.0 for u in range(U)] for t in range(cs)])
+        if regression:
+            Gp = Gath @ G @ Gath.T
+            M = omega[tu][:, None] * Gp * (tu[None, :] < tu[:, None])
+            # blocked forward solve of (I + M) V = I, blocks of blk unknowns
+            V = np.zeros((U, U))
+            for b0 in range(0, U, blk):
+                b1 = b0 + blk
+                T = np.linalg.inv(np.eye(blk) + M[b0:b1, b0:b1])
+                rhs = np.zeros((blk, U))
+                rhs[:, b0:b1] = np.eye(blk)
+                V[b0:b1] = T @ (rhs - M[b0:b1, :b0] @ V[:b0])
+            Fx = V @ (omega[tu][:, None] * Gath)
+            Fy = V @ (zeta[tu][:, None] * Gath)
+        else:
+            Fx = np.zeros((U, NXT))
+            Fy = zeta[tu][:, None] * Gath
+        Hx, Hy = Gath.T @ Fx, Gath.T @ Fy
+        Qx, Qy = Pp @ Fx, Pp @ Fy
+        XS = X @ S.T                                                  # [2cs, dv]
+        Fk = Hy @ Y - Hx @ XS
+        o[t0:t0 + c] = (g[:, None] * (Q @ S.T + Qy @ Y - Qx @ XS))[:c]
+        S = g[c - 1] * (S + Fk.T @ X)
+    return o, S

@@ -8,7 +8,7 @@ import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import seq_inputs
-from chunk_form_model import chunk_forward, chunk_forward_wy
+from chunk_form_model import chunk_forward, chunk_forward_folded, chunk_forward_wy
 
 pytestmark = pytest.mark.cpu
 
@@ -55,3 +55,21 @@ def test_precomputed_inverse_form_equals_recurrence(variant, chunk, carried):
                             S0=None if not carried else inp["S0"][0, 0])
     np.testing.assert_allclose(o, o_ref[0, 0], rtol=1e-9, atol=1e-10)
     np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-9, atol=1e-10)
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_1, fo.FALCON_3, fo.FALCON_1A, fo.FALCON_3A])
+@pytest.mark.parametrize("carried_key", [False, True])
+def test_key_folded_form_equals_recurrence(variant, carried_key):
+    windowed = variant in (fo.FALCON_3, fo.FALCON_3A)
+    for window in ([2, 3, 4] if windowed else [1]):
+        inp = seq_inputs(1, 1, 75, 8, 5, seed=500 + variant + window, dtype="bf16",
+                         beta_per_token=True, with_k_prev=carried_key, s_std=0.3)
+        kw = dict(beta=None, lam=0.02, eps=1e-6, window=window, beta_t=inp["beta_t"],
+                  k_prev=inp.get("k_prev"))
+        o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], **kw)
+        o, S = chunk_forward_folded(fo.is_regression(variant), inp["q"][0, 0], inp["k"][0, 0],
+                                    inp["v"][0, 0], beta=None, lam=0.02, eps=1e-6,
+                                    window=window, beta_t=inp["beta_t"][0, 0],
+                                    k_prev=inp["k_prev"][0, 0] if carried_key else None)
+        np.testing.assert_allclose(o, o_ref[0, 0], rtol=1e-9, atol=1e-10)
+        np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-9, atol=1e-10)
