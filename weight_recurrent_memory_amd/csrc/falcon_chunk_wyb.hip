@@ -1,0 +1,754 @@
+// falcon_chunk_wyb.hip - chunk-parallel Falcon forward for a sliding window of
+// B = 2 or 4 samples with gains shared by the value rows (Falcon-3, Falcon-3A;
+// scalar or per-token beta), dk in {64, 128}.
+//
+// Method: explainer of arXiv 2608.27763, section 核心方法 §3 (chunk-parallel
+// form) and the 163.com article, section 02 (2) (only the fixed-size state
+// crosses chunks; Gram / WY representation with a triangular solve).  Key-folded
+// form, derived from the recurrence:
+//   sub-chunks of 16 steps; the key tile of sub-chunk c holds the 32 keys of
+//   sub-chunks c-1 and c (tile index m).  The unknown u = (t, w) (step t, window
+//   slot w) has key m(u) = 16 + t - w.  With g_t = prod_{r<=t} a_r,
+//   zeta_t = eta_t / g_t, omega_t = zeta_t g_{t-1} and
+//     M[u][u'] = omega_t(u) (x_m(u) . x_m(u'))  for t(u') < t(u),   V = (I + M)^-1
+//     F_x = V diag(omega_t(u)) Gath,  F_y = V diag(zeta_t(u)) Gath   (Gath[u][m] = [m(u) = m])
+//     H = Gath^T F,  Q = P' F,  P'[t][u] = (q_t . x_m(u)) [t(u) <= t]
+//   the state enters only through XS = X S0^T (keys x value rows):
+//     Fk = H_y Y - H_x XS,   o_t = g_t (S0 q_t + (Q_y Y)_t - (Q_x XS)_t),
+//     S_c = g_15 (S0 + Fk^T X).
+//   The inner-product family has F_x = 0 and F_y = diag(zeta) Gath, so
+//   H_y = diag(c_m) with c_m the sum of zeta over the unknowns of key m.
+//   V is formed over 16-unknown blocks: T_bb = (I + M_bb)^-1 by forward
+//   substitution, then V_b = T_bb (R_b - sum_{b'<b} M_bb' V_b') for the folded
+//   right-hand sides R = diag(s) Gath.
+//
+// Structure.  One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
+// Iteration c: waves 0, 1 run the state of sub-chunk c (16 rows each, S in
+// registers); waves 2..7 prepare sub-chunk c+1 in four phases separated by
+// workgroup barriers:
+//   1  Gram and q.x of the key tile, keys transposed, per-step scalars
+//   2  T_bb by a DPP forward substitution (regression) | Fk and readout terms
+//      of the inner-product family
+//   3  blocked substitution for F_x, F_y and the folds H, Q (regression)
+//   4  H_y Y and Q_y Y (regression); commit the loads of sub-chunk c+2 to LDS
+//      and issue those of c+3
+// The state waves spread their work over the same four phases.
+// Operands are stored in the fragment order of the register operand they meet
+// (within a 32-wide group, slots 8g..8g+3 hold indices 4g..4g+3 and
+// 8g+4..8g+7 hold 16+4g..16+4g+3); non-exact operands are split-bf16 (Henry,
+// Tang & Heinecke, ARITH 2019).
+#include <type_traits>
+
+#include "falcon_device.h"
+#include "falcon_launch.h"
+#include "falcon_mma.h"
+
+namespace falcon {
+namespace {
+
+constexpr int CS = 16;       // steps per sub-chunk
+constexpr int NXT = 32;      // keys per tile
+constexpr int RW = 32;       // value rows per workgroup
+constexpr int NW = 8;
+constexpr int NT = 64 * NW;
+
+__device__ __forceinline__ int fpos(int k) {
+  const int kk = k & 31;
+  return (k & ~31) + 8 * ((kk & 15) >> 2) + ((kk >> 4) << 2) + (kk & 3);
+}
+
+template <int DK>
+struct WybLds {
+  static constexpr int XR = DK + 16;     // bf16 row: DK (fragment order) + pad
+  uint16_t X[4][CS][XR];                 // key blocks by sub-chunk & 3
+  uint16_t Q[4][CS][XR];                 // query blocks
+  uint16_t XT[4][DK][CS + 8];            // key blocks transposed, steps natural
+  uint16_t YT[4][RW][CS + 8];            // value blocks transposed, steps natural
+  float knorm[4][CS];
+  float beta[4][CS];
+  float G[NXT][NXT + 4];                 // Gram of the key tile
+  float P[CS][NXT + 4];                  // q . x over the tile
+  alignas(16) float gam[2][CS];
+  alignas(16) float zeta[2][CS];
+  alignas(16) float omega[2][CS];
+  alignas(16) float zcum[2][CS];         // prefix sums of zeta
+  float TS[4][16][16 + 4];               // diagonal blocks of T, row-major
+  uint16_t Hxhi[2][NXT][NXT + 8];        // -H_x rows, keys in fragment order
+  uint16_t Hxlo[2][NXT][NXT + 8];
+  uint16_t Qxhi[2][CS][NXT + 8];         // -Q_x rows
+  uint16_t Qxlo[2][CS][NXT + 8];
+  uint16_t Hyhi[NXT][NXT + 8];           // H_y rows
+  uint16_t Hylo[NXT][NXT + 8];
+  uint16_t Qyhi[CS][NXT + 8];            // Q_y rows
+  uint16_t Qylo[CS][NXT + 8];
+  float Ufk[2][RW][NXT + 4];             // (H_y Y)[m][i] stored [i][m]
+  float Oy[2][CS][RW + 4];               // (Q_y Y)[t][i]
+};
+
+struct WybGeom {
+  int nrbg;
+  int remap;
+  int nchunks;
+};
+
+// acc + g(lane N of this 16-lane row) * r as one DPP multiply-add (g is only
+// loaded from LDS, never written by the vector ALU, so no wait states apply)
+template <int N>
+__device__ __forceinline__ float fmac_bcast(float acc, float g, float r) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(g), "v"(r), "i"(N));
+  return acc;
+}
+// forward substitution of (I + M) x = rhs over a 16-unknown block from pivot
+// P on, M = diag(om) L(g): lane m of each 16-lane row holds row m in g[]
+template <int P>
+__device__ __forceinline__ void sweep(float (&rhs)[16], float (&acc)[16], const float (&g)[16], const float (&om)[16]) {
+  rhs[P] = __builtin_fmaf(-om[P], acc[P], rhs[P]);
+#pragma unroll
+  for (int r = P + 1; r < 16; ++r) acc[r] = fmac_bcast<P>(acc[r], g[r], rhs[P]);
+  if constexpr (P < 15) sweep<P + 1>(rhs, acc, g, om);
+}
+template <int N>
+__device__ __forceinline__ float dpp_shr(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             0x110 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ floatx4 mma3(floatx4 acc, const HL& a, const HL& b) {
+  acc = mfma16(a.hi, b.lo, acc);
+  acc = mfma16(a.lo, b.hi, acc);
+  return mfma16(a.hi, b.hi, acc);
+}
+__device__ __forceinline__ floatx4 mma2(floatx4 acc, const bf16x8& a, const HL& b) {
+  acc = mfma16(a, b.hi, acc);
+  return mfma16(a, b.lo, acc);
+}
+__device__ __forceinline__ floatx4 mma2(floatx4 acc, const HL& a, const bf16x8& b) {
+  acc = mfma16(a.hi, b, acc);
+  return mfma16(a.lo, b, acc);
+}
+__device__ __forceinline__ HL hl_two(const float* a, const float* b) {
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return hl_vals(v);
+}
+__device__ __forceinline__ HL hl_x4(const floatx4& a, const floatx4& b) {
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return hl_vals(v);
+}
+__device__ __forceinline__ floatx4 f4x(const float4& v) { return floatx4{v.x, v.y, v.z, v.w}; }
+// two groups of 4 bf16 (8-byte reads) as one fragment
+__device__ __forceinline__ bf16x8 frag_two(const uint16_t* a, const uint16_t* b) {
+  const uint2 x = *reinterpret_cast<const uint2*>(a);
+  const uint2 y = *reinterpret_cast<const uint2*>(b);
+  return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
+}
+
+template <int DK, bool REG, int B>
+__global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
+  using SM = WybLds<DK>;
+  constexpr int NKT = DK / 16, NKS = DK / 32, VPR = DK / 8;
+  constexpr int U = 16 * B, NB = B, NKU = (NB + 1) / 2;
+  static_assert(B == 2 || B == 4, "window 2 or 4");
+  static_assert(DK == 64 || DK == 128, "dk in {64, 128}");
+  __shared__ __align__(16) SM sm;
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
+  const uint16_t* __restrict__ bg = static_cast<const uint16_t*>(a.beta_t);
+
+  int chain, rbg;
+  {
+    const int b = blockIdx.x;
+    if (geo.remap) {   // the row groups of one chain share an XCD (and its L2)
+      const int xcd = b & 7, slot = b >> 3;
+      chain = xcd + 8 * (slot / geo.nrbg);
+      rbg = slot % geo.nrbg;
+    } else {
+      chain = b / geo.nrbg;
+      rbg = b % geo.nrbg;
+    }
+  }
+  const int dv = a.dv;
+  const int i0 = rbg * RW;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const long L = a.seqlen;
+  const long qk_base = (long)chain * L * DK;
+  const long v_base = (long)chain * L * dv;
+  const int nchunks = geo.nchunks;
+  auto live_chunk = [&](int j) __attribute__((always_inline)) { return j >= 0 && j < nchunks; };
+  auto steps = [&](int j) __attribute__((always_inline)) {
+    const long t0 = (long)j * CS;
+    return (int)((L - t0) < CS ? (L - t0) : CS);
+  };
+  // key tile index of unknown u and its step
+  auto mof = [](int u) __attribute__((always_inline)) { return 16 + u / B - u % B; };
+
+  // ---------------- block -1 (before the sequence) is zero ----------------
+  for (int idx = tid; idx < CS * SM::XR; idx += NT) (&sm.X[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < DK * (CS + 8); idx += NT) (&sm.XT[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < RW * (CS + 8); idx += NT) (&sm.YT[3][0][0])[idx] = 0;
+  if (tid < CS) sm.knorm[3][tid] = 0.0f;
+
+  // ---------------- global loads (buffer resources, range checked) ----------------
+  // wave 6 moves the keys of a sub-chunk, wave 7 its queries, values and gains;
+  // loads are issued one iteration before their commit.  Pieces past the end of
+  // the sequence (or before its start) read 0.
+  constexpr int BUF_WORD3 = 0x00020000;
+  constexpr uint32_t PARKED = 0xC0000000u;
+  auto rsrc = [](const void* base, long bytes) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, BUF_WORD3);
+  };
+  auto ld128 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  constexpr int KP = CS * VPR / 64;        // 16-byte pieces per lane of a key or query block
+  struct KSet { uint4 p[KP]; };
+  struct QSet { uint4 p[KP]; uint4 v, v2; uint32_t b; };
+  const auto rk = rsrc(kg + qk_base, L * DK * 2);
+  const auto rq = rsrc(qg + qk_base, L * DK * 2);
+  const auto rv = rsrc(vg + v_base, L * dv * 2);
+  const auto rb = a.beta_kind == 1 ? rsrc(bg + (long)chain * L, L * 2) : rsrc(vg, 0);
+  constexpr uint32_t KQ_CHUNK = CS * DK * 2;
+  // key x_g = k_{g-1}: piece p of the block is row p / VPR, k = 8 (p % VPR)
+  auto koff = [&](int u) __attribute__((always_inline)) {
+    const int p = lane + 64 * u;
+    return (uint32_t)(((p / VPR - 1) * DK + (p % VPR) * 8) * 2);
+  };
+  auto qoff = [&](int u) __attribute__((always_inline)) {
+    const int p = lane + 64 * u;
+    return (uint32_t)(((p / VPR) * DK + (p % VPR) * 8) * 2);
+  };
+  // values: lanes 0..31 move a 4 (steps) x 4 (rows) block, t4 = 4 (lane / 8), i4 = 4 (lane % 8)
+  const int vb_t4 = 4 * ((lane & 31) >> 3), vb_i4 = 4 * (lane & 7);
+  const uint32_t voff = (lane < 32 && i0 + vb_i4 < dv) ? (uint32_t)((vb_t4 * dv + i0 + vb_i4) * 2) : PARKED;
+  const uint32_t V_CHUNK = (uint32_t)(CS * dv * 2);
+  uint4 kprev[KP];
+#pragma unroll
+  for (int u = 0; u < KP; ++u) {
+    kprev[u] = make_uint4(0u, 0u, 0u, 0u);
+    const int p = lane + 64 * u;
+    if (wave == 6 && kpg != nullptr && p / VPR == 0)
+      kprev[u] = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + (p % VPR) * 8);
+  }
+  auto prefetch_k = [&](KSet& s, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) s.p[u] = ld128(rk, koff(u) + (uint32_t)j * KQ_CHUNK);
+  };
+  auto prefetch_q = [&](QSet& s, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) s.p[u] = ld128(rq, qoff(u) + (uint32_t)j * KQ_CHUNK);
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto val = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + (uint32_t)j * V_CHUNK + (uint32_t)(e * dv * 2)), 0, 0);
+      w[2 * e] = val[0];
+      w[2 * e + 1] = val[1];
+    }
+    s.v = make_uint4(w[0], w[1], w[2], w[3]);
+    s.v2 = make_uint4(w[4], w[5], w[6], w[7]);
+    s.b = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)((uint32_t)(lane & 15) * 2 + (uint32_t)j * (CS * 2)), 0, 0);
+  };
+  auto put8 = [&](uint16_t* row, int k0, uint4 val) __attribute__((always_inline)) {
+    *reinterpret_cast<uint2*>(row + fpos(k0)) = make_uint2(val.x, val.y);
+    *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
+  };
+  // keys of sub-chunk j to LDS, with their squared norms (packed bf16 dot
+  // products, then a DPP sum over the VPR threads of a row)
+  auto commit_k = [&](const KSet& s, int j) __attribute__((always_inline)) {
+    const int jb = j & 3;
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int p = lane + 64 * u;
+      const int t = p / VPR, kv = p % VPR;
+      const uint4 val = (j == 0 && t == 0) ? kprev[u] : s.p[u];
+      put8(&sm.X[jb][t][0], kv * 8, val);
+      float part = 0.0f;
+      const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 v = __builtin_bit_cast(bf16x2, w4[e]);
+        part = __builtin_amdgcn_fdot2_f32_bf16(v, v, part, false);
+      }
+      part += dpp_shr<1>(part, 0.0f);
+      part += dpp_shr<2>(part, 0.0f);
+      part += dpp_shr<4>(part, 0.0f);
+      if constexpr (VPR == 16) part += dpp_shr<8>(part, 0.0f);
+      if (kv == VPR - 1) sm.knorm[jb][t] = part;
+    }
+  };
+  auto commit_q = [&](const QSet& s, int j) __attribute__((always_inline)) {
+    const int jb = j & 3;
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int p = lane + 64 * u;
+      put8(&sm.Q[jb][p / VPR][0], (p % VPR) * 8, s.p[u]);
+    }
+    if (lane < 32) {
+      const uint32_t w[8] = {s.v.x, s.v.y, s.v.z, s.v.w, s.v2.x, s.v2.y, s.v2.z, s.v2.w};
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t sel = (ii & 1) ? 0x07060302u : 0x05040100u;
+        const int h = ii >> 1;
+        *reinterpret_cast<uint2*>(&sm.YT[jb][vb_i4 + ii][vb_t4]) =
+            make_uint2(__builtin_amdgcn_perm(w[2 + h], w[h], sel), __builtin_amdgcn_perm(w[6 + h], w[4 + h], sel));
+      }
+    } else if (lane < 48) {
+      sm.beta[jb][lane & 15] = a.beta_kind == 0 ? a.beta : bf16_to_f32((uint16_t)s.b);
+    }
+  };
+
+  // ---------------- phase-1 stages of sub-chunk j ----------------
+  // Gram tile (mi, mj) of the key tile (blocks j-1, j): stored transposed, G symmetric
+  auto gram_tile = [&](int j, int mi, int mj) __attribute__((always_inline)) {
+    const int bi = (j - 1 + mi) & 3, bj = (j - 1 + mj) & 3;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      acc = mfma16(frag_bf16(&sm.X[bi][lr][32 * ks + 8 * lg]), frag_bf16(&sm.X[bj][lr][32 * ks + 8 * lg]), acc);
+    *reinterpret_cast<float4*>(&sm.G[16 * mj + lr][16 * mi + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  // q.x: P^T tile mj -> P[t][16 mj + 4 lg ..]
+  auto qx_tile = [&](int j, int mj) __attribute__((always_inline)) {
+    const int bj = (j - 1 + mj) & 3;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      acc = mfma16(frag_bf16(&sm.X[bj][lr][32 * ks + 8 * lg]), frag_bf16(&sm.Q[j & 3][lr][32 * ks + 8 * lg]), acc);
+    *reinterpret_cast<float4*>(&sm.P[lr][16 * mj + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  // keys transposed: XT[k][t] from X[t][k]; item idx moves a 4 (t) x 4 (k) block
+  auto transpose_keys = [&](int j, int idx) __attribute__((always_inline)) {
+    const int jb = j & 3;
+    if (idx < (CS / 4) * (DK / 4)) {
+      const int t4 = 4 * (idx % (CS / 4)), k4 = 4 * (idx / (CS / 4));
+      const int pk4 = fpos(k4);
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 r = *reinterpret_cast<const uint2*>(&sm.X[jb][t4 + e][pk4]);
+        w[2 * e] = r.x;
+        w[2 * e + 1] = r.y;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t sel = (kk & 1) ? 0x07060302u : 0x05040100u;
+        const int h = kk >> 1;
+        *reinterpret_cast<uint2*>(&sm.XT[jb][k4 + kk][t4]) =
+            make_uint2(__builtin_amdgcn_perm(w[2 + h], w[h], sel), __builtin_amdgcn_perm(w[6 + h], w[4 + h], sel));
+      }
+    }
+  };
+  // eta_t = beta_t / (eps + n_t), n_t = sum of the window's squared key norms;
+  // a_t = 1 - eta_t lambda; padded steps and the fresh-sequence first step take
+  // eta = 0, a = 1.  Lanes 0..15 = steps (one DPP row).
+  auto scalars = [&](int j) __attribute__((always_inline)) {
+    const int t = lr;
+    const int sb = j & 1;
+    float n = 0.0f;
+#pragma unroll
+    for (int w = 0; w < B; ++w) {
+      const int m = 16 + t - w;
+      n += m >= 16 ? sm.knorm[j & 3][m - 16] : sm.knorm[(j - 1) & 3][m];
+    }
+    const bool live = t < steps(j) && !((long)j * CS + t == 0 && kpg == nullptr);
+    float eta = 0.0f, dec = 1.0f;
+    if (live) {
+      eta = sm.beta[j & 3][t] * __builtin_amdgcn_rcpf(a.eps + n);
+      dec = 1.0f - eta * a.lambda;
+    }
+    float gsc = dec;
+    gsc *= dpp_shr<1>(gsc, 1.0f);
+    gsc *= dpp_shr<2>(gsc, 1.0f);
+    gsc *= dpp_shr<4>(gsc, 1.0f);
+    gsc *= dpp_shr<8>(gsc, 1.0f);
+    const float gprev = dpp_shr<1>(gsc, 1.0f);
+    const float z = eta * __builtin_amdgcn_rcpf(gsc);
+    float zc = z;
+    zc += dpp_shr<1>(zc, 0.0f);
+    zc += dpp_shr<2>(zc, 0.0f);
+    zc += dpp_shr<4>(zc, 0.0f);
+    zc += dpp_shr<8>(zc, 0.0f);
+    if (lane < 16) {
+      sm.gam[sb][t] = gsc;
+      sm.zeta[sb][t] = z;
+      sm.omega[sb][t] = z * gprev;
+      sm.zcum[sb][t] = zc;
+    }
+  };
+
+  // ---------------- phase 2 (regression): diagonal blocks of T ----------------
+  // One wave; 16-lane row b = block b (rows beyond B repeat the last block).
+  // Lane n solves column n of (I + M_bb).  Row n of the block's coupling,
+  // G[m(u_n)][m(u_r)] for the unknowns u_r of other steps, is read around the
+  // block's key range; the same-step entries are zero.
+  auto diag_blocks = [&](int j) __attribute__((always_inline)) {
+    const int sb = j & 1;
+    const int b = lg < B ? lg : B - 1;
+    const int n = lr;
+    const int un = 16 * b + n;
+    const int mn = mof(un);
+    const int base = 16 + 16 * b / B;          // key of (first step of the block, w = 0)
+    constexpr int NG = (B == 4) ? 2 : 3;       // float4 groups from base - 4
+    float gr[4 * NG];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.G[mn][base - 4 + 4 * q]);
+      gr[4 * q] = g4.x; gr[4 * q + 1] = g4.y; gr[4 * q + 2] = g4.z; gr[4 * q + 3] = g4.w;
+    }
+    float g[16], om[16];
+    float os[16 / B];
+#pragma unroll
+    for (int q = 0; q < 16 / B; q += 4) {
+      const float4 o4 = *reinterpret_cast<const float4*>(&sm.omega[sb][16 * b / B + q]);
+      os[q] = o4.x; os[q + 1] = o4.y; os[q + 2] = o4.z; os[q + 3] = o4.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = r / B - r % B;           // key of u_r relative to base
+      g[r] = (r / B == n / B) ? 0.0f : gr[off + 4];
+      om[r] = os[r / B];
+    }
+    float rhs[16], acc[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      rhs[m] = (m == n) ? 1.0f : 0.0f;
+      acc[m] = 0.0f;
+    }
+    asm volatile("s_nop 4");
+    sweep<0>(rhs, acc, g, om);
+    if (lg < B) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.TS[b][r][n] = rhs[r];
+    }
+  };
+
+  // ---------------- phase 3 (regression): blocked substitution and folds ----------------
+  // One wave per (F_x | F_y) x key-column tile mc.  V[b] (C layout) holds
+  // V[16 b + 4 lg + e][16 mc + lr]; Vop[k] the split fragment over blocks 2k, 2k+1.
+  auto combine = [&](int j, bool fx, int mc) __attribute__((always_inline)) {
+    const int sb = j & 1;
+    const float* sc = fx ? sm.omega[sb] : sm.zeta[sb];
+    const float z4[4] = {0.f, 0.f, 0.f, 0.f};
+    const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 V[NB];
+    HL Vop[NKU];
+    // -M[u][u'] for u = 16 b + lr and the unknowns u' of blocks b1 (slots 0-3) and
+    // b2 (slots 4-7; b2 < 0: none)
+    auto mfrag = [&](int b, int b1, int b2) __attribute__((always_inline)) {
+      const int u = 16 * b + lr;
+      const float nom = -sm.omega[sb][u / B];
+      const float* grow = &sm.G[mof(u)][0];
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = nom * grow[mof(16 * b1 + 4 * lg + q)];
+        v[4 + q] = b2 >= 0 ? nom * grow[mof(16 * (b2 < 0 ? 0 : b2) + 4 * lg + q)] : 0.0f;
+      }
+      return hl_vals(v);
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      floatx4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {     // R_b = diag(s) Gath, column 16 mc + lr
+        const int u = 16 * b + 4 * lg + e;
+        acc[e] = mof(u) == 16 * mc + lr ? sc[u / B] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; 2 * k < b; ++k) {  // - sum over earlier blocks 2k, 2k+1
+        const bool two = 2 * k + 1 < b;
+        const HL mf = mfrag(b, 2 * k, two ? 2 * k + 1 : -1);
+        acc = mma3(acc, mf, Vop[k]);
+      }
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.TS[b][lr][4 * lg]);
+      const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+      const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+      V[b] = mma3(zacc, hl_two(tv, z4), hl_two(av, z4));
+      if ((b & 1) == 0) Vop[b / 2] = hl_x4(V[b], zacc);
+      else Vop[b / 2] = hl_x4(V[b - 1], V[b]);
+    }
+    // folds: (Gath^T V)^T tiles and (P' V)^T
+    const float sign = fx ? -1.0f : 1.0f;          // -H_x, -Q_x; +H_y, +Q_y
+    uint16_t* Hhi = fx ? &sm.Hxhi[sb][0][0] : &sm.Hyhi[0][0];
+    uint16_t* Hlo = fx ? &sm.Hxlo[sb][0][0] : &sm.Hylo[0][0];
+    uint16_t* Qhi = fx ? &sm.Qxhi[sb][0][0] : &sm.Qyhi[0][0];
+    uint16_t* Qlo = fx ? &sm.Qxlo[sb][0][0] : &sm.Qylo[0][0];
+    constexpr int HS = NXT + 8;
+#pragma unroll
+    for (int mj = 0; mj < 2; ++mj) {
+      floatx4 h = zacc;
+#pragma unroll
+      for (int k = 0; k < NKU; ++k) {
+        uint32_t gw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ua = 32 * k + 4 * lg + 2 * (e & 1) + 16 * (e >> 1);   // slots 2e, 2e+1
+          const int m = 16 * mj + lr;
+          const uint32_t lo = (ua < U && mof(ua) == m) ? 0x3F80u : 0u;
+          const uint32_t hi = (ua + 1 < U && mof(ua + 1) == m) ? 0x3F80u : 0u;
+          gw[e] = lo | (hi << 16);
+        }
+        const bf16x8 gf = __builtin_bit_cast(bf16x8, make_uint4(gw[0], gw[1], gw[2], gw[3]));
+        h = mma2(h, Vop[k], gf);
+      }
+      const float hv[4] = {sign * h[0], sign * h[1], sign * h[2], sign * h[3]};
+      store_split4(Hhi + (16 * mj + lr) * HS + 8 * lg + 4 * mc, Hlo + (16 * mj + lr) * HS + 8 * lg + 4 * mc, hv);
+    }
+    {
+      floatx4 qa = zacc;
+#pragma unroll
+      for (int k = 0; k < NKU; ++k) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int u = 32 * k + 4 * lg + (e & 3) + 16 * (e >> 2);
+          pv[e] = (u < U && u / B <= lr) ? sm.P[lr][mof(u)] : 0.0f;
+        }
+        qa = mma3(qa, Vop[k], hl_vals(pv));
+      }
+      const float qv[4] = {sign * qa[0], sign * qa[1], sign * qa[2], sign * qa[3]};
+      store_split4(Qhi + lr * HS + 8 * lg + 4 * mc, Qlo + lr * HS + 8 * lg + 4 * mc, qv);
+    }
+  };
+
+  // values of the key tile as a fragment over keys (slots 0-3: block j-1, 4-7: block j)
+  auto yfrag = [&](int j, int i) __attribute__((always_inline)) {
+    return frag_two(&sm.YT[(j - 1) & 3][i][4 * lg], &sm.YT[j & 3][i][4 * lg]);
+  };
+  // ---------------- phase 4 (regression): H_y Y and Q_y Y ----------------
+  auto ufk_tile = [&](int j, int mt, int it) __attribute__((always_inline)) {
+    const HL hy = hl_pair(&sm.Hyhi[16 * mt + lr][8 * lg], &sm.Hylo[16 * mt + lr][8 * lg]);
+    const floatx4 acc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, hy, yfrag(j, 16 * it + lr));
+    *reinterpret_cast<float4*>(&sm.Ufk[j & 1][16 * it + lr][16 * mt + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  auto oy_tile = [&](int j, int it, const HL& qy) __attribute__((always_inline)) {
+    const floatx4 acc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, yfrag(j, 16 * it + lr), qy);
+    *reinterpret_cast<float4*>(&sm.Oy[j & 1][lr][16 * it + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  };
+  // ---------------- phase 2 (inner-product family) ----------------
+  // c_{m,t} = sum of zeta_s over the unknowns (s, w) of key m with s <= t
+  auto ckey = [&](int sb, int m, int t) __attribute__((always_inline)) {
+    const int lo = m - 16 < 0 ? 0 : m - 16;
+    const int hi0 = m - 16 + B - 1;
+    const int hi = hi0 < t ? hi0 : t;
+    if (hi < lo) return 0.0f;
+    return sm.zcum[sb][hi] - (lo > 0 ? sm.zcum[sb][lo - 1] : 0.0f);
+  };
+  auto ip_ufk = [&](int j) __attribute__((always_inline)) {   // Ufk[i][m] = c_m y_m[i]
+    const int i = lane & 31, half = lane >> 5;
+    const int jb = (j - 1 + half) & 3;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint2 y = *reinterpret_cast<const uint2*>(&sm.YT[jb][i][4 * q4]);
+      const float yv[4] = {bf16_to_f32((uint16_t)(y.x & 0xFFFFu)), bf16_to_f32((uint16_t)(y.x >> 16)),
+                           bf16_to_f32((uint16_t)(y.y & 0xFFFFu)), bf16_to_f32((uint16_t)(y.y >> 16))};
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = ckey(j & 1, 16 * half + 4 * q4 + e, 15) * yv[e];
+      *reinterpret_cast<float4*>(&sm.Ufk[j & 1][i][16 * half + 4 * q4]) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  };
+  auto ip_oy = [&](int j) __attribute__((always_inline)) {     // Q_y[t][m] = P[t][m] c_{m,t}
+    const int t = lr;
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = 4 * lg + (e & 3) + 16 * (e >> 2);
+      pv[e] = sm.P[t][m] * ckey(j & 1, m, t);
+    }
+    const HL qy = hl_vals(pv);
+    oy_tile(j, 0, qy);
+    oy_tile(j, 1, qy);
+  };
+
+  // iterations c = -2 .. nchunks-1: state of sub-chunk c, preparation of c+1,
+  // commit of c+2, loads of c+3
+  const int c_begin = -2;
+  if (wave < 2) {
+    // ---------------- state waves ----------------
+    const int rt = wave;
+    float sv[NKT][4];                          // S[16 rt + lr][16 kt + 4 lg + e]
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 16 * rt + lr, kk = 16 * kt + 4 * lg + e;
+        sv[kt][e] = (a.S0 && i < dv) ? a.S0[((long)chain * dv + i) * DK + kk] : 0.0f;
+      }
+    HL sf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+    float* orow = a.o + v_base + (long)lr * dv + i0 + 16 * rt + 4 * lg;
+    const bool rows_in = i0 + 16 * rt < dv;
+    for (int c = c_begin; c < nchunks; ++c) {
+      const bool run = c >= 0 && rows_in;
+      const int cb = c & 1;
+      HL xsf;
+      floatx4 fk[2];
+      __syncthreads();
+      // phase 1: XS = X S0^T, Fk = Ufk - H_x XS
+      if (run) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cb][16 * rt + lr][16 * mi + 4 * lg]));
+        if constexpr (REG) {
+          floatx4 xs[2];
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) {
+            xs[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+              xs[mi] = mma2(xs[mi], frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * ks + 8 * lg]), sf[ks]);
+          }
+          xsf = hl_x4(xs[0], xs[1]);
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+            fk[mi] = mma3(fk[mi], hl_pair(&sm.Hxhi[cb][16 * mi + lr][8 * lg], &sm.Hxlo[cb][16 * mi + lr][8 * lg]), xsf);
+        }
+      }
+      __syncthreads();
+      // phase 2: readout  o_t = g_t (S0 q_t + O_y - Q_x XS)
+      if (run) {
+        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cb][lr][16 * rt + 4 * lg]));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) oacc = mma2(oacc, sf[ks], frag_bf16(&sm.Q[c & 3][lr][32 * ks + 8 * lg]));
+        if constexpr (REG) oacc = mma3(oacc, xsf, hl_pair(&sm.Qxhi[cb][lr][8 * lg], &sm.Qxlo[cb][lr][8 * lg]));
+        const float gt = sm.gam[cb][lr];
+        if ((long)c * CS + lr < L)
+          *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
+        orow += CS * dv;
+      }
+      __syncthreads();
+      // phase 3: carry S <- g_15 (S + Fk^T X)
+      if (run) {
+        const HL fkf = hl_x4(fk[0], fk[1]);
+        const float gC = sm.gam[cb][CS - 1];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][16 * kt + lr][4 * lg], &sm.XT[c & 3][16 * kt + lr][4 * lg]);
+          const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xt, fkf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
+        }
+      }
+      __syncthreads();
+      // phase 4: split the new state
+      if (run) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+      }
+    }
+    __syncthreads();
+    if (rows_in && a.S_out && i0 + 16 * rt + lr < dv) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+        *reinterpret_cast<float4*>(a.S_out + ((long)chain * dv + i0 + 16 * rt + lr) * DK + 16 * kt + 4 * lg) =
+            make_float4(sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]);
+    }
+  } else {
+    // ---------------- preparation waves ----------------
+    KSet ks0;
+    QSet qs0;
+    if (wave == 6) prefetch_k(ks0, 0);
+    if (wave == 7) prefetch_q(qs0, 0);
+    for (int c = c_begin; c < nchunks; ++c) {
+      const int j = c + 1;
+      const bool pj = live_chunk(j);
+      __syncthreads();
+      // phase 1
+      if (pj) {
+        if (wave == 2) {
+          if constexpr (REG) { gram_tile(j, 0, 0); gram_tile(j, 1, 0); }
+        } else if (wave == 3) {
+          if constexpr (REG) { gram_tile(j, 0, 1); gram_tile(j, 1, 1); }
+        } else if (wave == 4) {
+          qx_tile(j, 0);
+          qx_tile(j, 1);
+        } else if (wave == 5) {
+          scalars(j);
+        } else {
+          transpose_keys(j, 64 * (wave - 6) + lane);
+        }
+      }
+      __syncthreads();
+      // phase 2
+      if (pj) {
+        if constexpr (REG) {
+          if (wave == 4) diag_blocks(j);
+        } else {
+          if (wave == 2) ip_ufk(j);
+          if (wave == 3) ip_oy(j);
+        }
+      }
+      __syncthreads();
+      // phase 3
+      if (pj) {
+        if constexpr (REG) {
+          if (wave == 2) combine(j, true, 0);
+          if (wave == 3) combine(j, true, 1);
+          if (wave == 5) combine(j, false, 0);
+          if (wave == 6) combine(j, false, 1);
+        }
+      }
+      __syncthreads();
+      // phase 4
+      if (pj) {
+        if constexpr (REG) {
+          if (wave == 2) { ufk_tile(j, 0, 0); ufk_tile(j, 0, 1); }
+          if (wave == 3) { ufk_tile(j, 1, 0); ufk_tile(j, 1, 1); }
+          if (wave == 4) {
+            const HL qy = hl_pair(&sm.Qyhi[lr][8 * lg], &sm.Qylo[lr][8 * lg]);
+            oy_tile(j, 0, qy);
+            oy_tile(j, 1, qy);
+          }
+        }
+      }
+      if (wave == 6 && live_chunk(c + 2)) commit_k(ks0, c + 2);
+      if (wave == 7 && live_chunk(c + 2)) commit_q(qs0, c + 2);
+      if (wave == 6) prefetch_k(ks0, c + 3);
+      if (wave == 7) prefetch_q(qs0, c + 3);
+    }
+    __syncthreads();
+  }
+}
+
+template <int DK, bool REG, int B>
+hipError_t launch_wyb(const SeqArgs& a, hipStream_t stream) {
+  static_assert(sizeof(WybLds<DK>) <= 160 * 1024, "LDS budget");
+  WybGeom geo;
+  const int nchain = a.batch * a.heads;
+  geo.nrbg = (a.dv + RW - 1) / RW;
+  geo.remap = (nchain % 8 == 0) ? 1 : 0;
+  geo.nchunks = (int)((a.seqlen + CS - 1) / CS);
+  const unsigned nblocks = (unsigned)(nchain * geo.nrbg);
+  hipLaunchKernelGGL((chunk_wyb_kernel<DK, REG, B>), dim3(nblocks), dim3(NT), 0, stream, a, geo);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_wyb_dk(const SeqArgs& a, hipStream_t stream) {
+  if (a.window == 2) return a.regression ? launch_wyb<DK, true, 2>(a, stream) : launch_wyb<DK, false, 2>(a, stream);
+  return a.regression ? launch_wyb<DK, true, 4>(a, stream) : launch_wyb<DK, false, 4>(a, stream);
+}
+
+}  // namespace
+
+bool chunk_wyb_supported(const SeqArgs& a) {
+  const long bytes = (long)a.seqlen * (a.dk > a.dv ? a.dk : a.dv) * 2;
+  return (a.window == 2 || a.window == 4) && a.beta_kind != 2 && (a.dk == 64 || a.dk == 128) &&
+         a.dv % 4 == 0 && bytes < (1L << 30);
+}
+
+// Sliding-window chunk form (window 2 or 4), gains shared by the value rows,
+// 16-step sub-chunks whatever the requested chunk.
+hipError_t launch_chunk_wyb(const SeqArgs& a, hipStream_t stream) {
+  if (a.dk == 64) return launch_wyb_dk<64>(a, stream);
+  if (a.dk == 128) return launch_wyb_dk<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace falcon

@@ -50,6 +50,10 @@ hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs);
 // (falcon_chunk_wy.hip); 32-step chunks whatever the requested chunk
 bool chunk_wy_supported(const SeqArgs& a);
 hipError_t launch_chunk_wy(const SeqArgs& a, hipStream_t stream);
+// sliding-window chunk form (window 2 or 4), gains shared by the value rows, dk in
+// {64, 128} (falcon_chunk_wyb.hip); 16-step sub-chunks whatever the requested chunk
+bool chunk_wyb_supported(const SeqArgs& a);
+hipError_t launch_chunk_wyb(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace falcon
