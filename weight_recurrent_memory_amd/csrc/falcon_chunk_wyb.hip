@@ -83,6 +83,11 @@ struct WybLds {
   uint16_t Qylo[CS][NXT + 8];
   float Ufk[2][RW][NXT + 4];             // (H_y Y)[m][i] stored [i][m]
   float Oy[2][CS][RW + 4];               // (Q_y Y)[t][i]
+  uint16_t Mhi[4][16][NXT + 8];          // -M fragments of the blocked solve, by (block, pair)
+  uint16_t Mlo[4][16][NXT + 8];
+  uint16_t Pfhi[2][CS][NXT + 8];         // P' fragments over the unknowns, by pair of blocks
+  uint16_t Pflo[2][CS][NXT + 8];
+  alignas(16) float cm[2][NXT];          // inner-product family: sum of zeta per key
 };
 
 struct WybGeom {
@@ -343,6 +348,17 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       }
     }
   };
+  // c_{m,t} = sum of zeta_s over the unknowns (s, w) of key m with s <= t
+  auto ckey = [&](int sb, int m, int t) __attribute__((always_inline)) {
+    const int lo = m - 16 < 0 ? 0 : m - 16;
+    const int hi0 = m - 16 + B - 1;
+    const int hi = hi0 < t ? hi0 : t;
+    const int hic = hi < 0 ? 0 : hi;
+    const float top = sm.zcum[sb][hic];
+    const float bot = sm.zcum[sb][lo > 0 ? lo - 1 : 0];
+    const float v = top - (lo > 0 ? bot : 0.0f);
+    return hi < lo ? 0.0f : v;
+  };
   // eta_t = beta_t / (eps + n_t), n_t = sum of the window's squared key norms;
   // a_t = 1 - eta_t lambda; padded steps and the fresh-sequence first step take
   // eta = 0, a = 1.  Lanes 0..15 = steps (one DPP row).
@@ -378,6 +394,9 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       sm.zeta[sb][t] = z;
       sm.omega[sb][t] = z * gprev;
       sm.zcum[sb][t] = zc;
+    }
+    if constexpr (!REG) {   // c_m: zeta summed over the unknowns of key m (this wave wrote zcum)
+      if (lane < NXT) sm.cm[sb][lane] = ckey(sb, lane, CS - 1);
     }
   };
 
@@ -427,6 +446,43 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
   };
 
+  // ---------------- phase 2 (regression): operand fragments of the blocked solve ----------------
+  // fragment f = (block b, pair k): -M[u][u'] for u = 16 b + lr and the unknowns
+  // u' of blocks 2k (slots 0-3) and 2k+1 (slots 4-7, zero unless 2k+1 < b)
+  constexpr int NMF = NB == 4 ? 4 : 1;
+  auto mf_bk = [](int f, int& b, int& k) __attribute__((always_inline)) {
+    b = f == 0 ? 1 : f == 1 ? 2 : 3;
+    k = f == 3 ? 1 : 0;
+  };
+  auto mfrag_store = [&](int j, int f) __attribute__((always_inline)) {
+    int b, k;
+    mf_bk(f, b, k);
+    const int b2 = 2 * k + 1 < b ? 2 * k + 1 : -1;
+    const int sb = j & 1;
+    const int u = 16 * b + lr;
+    const float nom = -sm.omega[sb][u / B];
+    const float* grow = &sm.G[mof(u)][0];
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = nom * grow[mof(32 * k + 4 * lg + q)];
+      v[4 + q] = b2 >= 0 ? nom * grow[mof(16 * (b2 < 0 ? 0 : b2) + 4 * lg + q)] : 0.0f;
+    }
+    store_split4(&sm.Mhi[f][lr][8 * lg], &sm.Mlo[f][lr][8 * lg], v);
+    store_split4(&sm.Mhi[f][lr][8 * lg + 4], &sm.Mlo[f][lr][8 * lg + 4], v + 4);
+  };
+  // P'[t][u] = P[t][m(u)] [t(u) <= t] over the unknowns of blocks 2k, 2k+1
+  auto pfrag_store = [&](int k) __attribute__((always_inline)) {
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = 32 * k + 4 * lg + (e & 3) + 16 * (e >> 2);
+      pv[e] = (u < U && u / B <= lr) ? sm.P[lr][mof(u < U ? u : 0)] : 0.0f;
+    }
+    store_split4(&sm.Pfhi[k][lr][8 * lg], &sm.Pflo[k][lr][8 * lg], pv);
+    store_split4(&sm.Pfhi[k][lr][8 * lg + 4], &sm.Pflo[k][lr][8 * lg + 4], pv + 4);
+  };
+
   // ---------------- phase 3 (regression): blocked substitution and folds ----------------
   // One wave per (F_x | F_y) x key-column tile mc.  V[b] (C layout) holds
   // V[16 b + 4 lg + e][16 mc + lr]; Vop[k] the split fragment over blocks 2k, 2k+1.
@@ -437,20 +493,18 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
     floatx4 V[NB];
     HL Vop[NKU];
-    // -M[u][u'] for u = 16 b + lr and the unknowns u' of blocks b1 (slots 0-3) and
-    // b2 (slots 4-7; b2 < 0: none)
-    auto mfrag = [&](int b, int b1, int b2) __attribute__((always_inline)) {
-      const int u = 16 * b + lr;
-      const float nom = -sm.omega[sb][u / B];
-      const float* grow = &sm.G[mof(u)][0];
-      float v[8];
+    // every operand fragment is read before the substitution starts
+    HL mf[NMF], tf[NB], pf[NKU];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = nom * grow[mof(16 * b1 + 4 * lg + q)];
-        v[4 + q] = b2 >= 0 ? nom * grow[mof(16 * (b2 < 0 ? 0 : b2) + 4 * lg + q)] : 0.0f;
-      }
-      return hl_vals(v);
-    };
+    for (int f = 0; f < NMF; ++f) mf[f] = hl_pair(&sm.Mhi[f][lr][8 * lg], &sm.Mlo[f][lr][8 * lg]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.TS[b][lr][4 * lg]);
+      const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+      tf[b] = hl_two(tv, z4);
+    }
+#pragma unroll
+    for (int k = 0; k < NKU; ++k) pf[k] = hl_pair(&sm.Pfhi[k][lr][8 * lg], &sm.Pflo[k][lr][8 * lg]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       floatx4 acc;
@@ -460,15 +514,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         acc[e] = mof(u) == 16 * mc + lr ? sc[u / B] : 0.0f;
       }
 #pragma unroll
-      for (int k = 0; 2 * k < b; ++k) {  // - sum over earlier blocks 2k, 2k+1
-        const bool two = 2 * k + 1 < b;
-        const HL mf = mfrag(b, 2 * k, two ? 2 * k + 1 : -1);
-        acc = mma3(acc, mf, Vop[k]);
-      }
-      const float4 t4 = *reinterpret_cast<const float4*>(&sm.TS[b][lr][4 * lg]);
-      const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+      for (int k = 0; 2 * k < b; ++k)    // - sum over earlier blocks 2k, 2k+1
+        acc = mma3(acc, mf[b == 1 ? 0 : b == 2 ? 1 : (k == 0 ? 2 : 3)], Vop[k]);
       const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
-      V[b] = mma3(zacc, hl_two(tv, z4), hl_two(av, z4));
+      V[b] = mma3(zacc, tf[b], hl_two(av, z4));
       if ((b & 1) == 0) Vop[b / 2] = hl_x4(V[b], zacc);
       else Vop[b / 2] = hl_x4(V[b - 1], V[b]);
     }
@@ -502,15 +551,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     {
       floatx4 qa = zacc;
 #pragma unroll
-      for (int k = 0; k < NKU; ++k) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int u = 32 * k + 4 * lg + (e & 3) + 16 * (e >> 2);
-          pv[e] = (u < U && u / B <= lr) ? sm.P[lr][mof(u)] : 0.0f;
-        }
-        qa = mma3(qa, Vop[k], hl_vals(pv));
-      }
+      for (int k = 0; k < NKU; ++k) qa = mma3(qa, Vop[k], pf[k]);
       const float qv[4] = {sign * qa[0], sign * qa[1], sign * qa[2], sign * qa[3]};
       store_split4(Qhi + lr * HS + 8 * lg + 4 * mc, Qlo + lr * HS + 8 * lg + 4 * mc, qv);
     }
@@ -531,14 +572,6 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     *reinterpret_cast<float4*>(&sm.Oy[j & 1][lr][16 * it + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   };
   // ---------------- phase 2 (inner-product family) ----------------
-  // c_{m,t} = sum of zeta_s over the unknowns (s, w) of key m with s <= t
-  auto ckey = [&](int sb, int m, int t) __attribute__((always_inline)) {
-    const int lo = m - 16 < 0 ? 0 : m - 16;
-    const int hi0 = m - 16 + B - 1;
-    const int hi = hi0 < t ? hi0 : t;
-    if (hi < lo) return 0.0f;
-    return sm.zcum[sb][hi] - (lo > 0 ? sm.zcum[sb][lo - 1] : 0.0f);
-  };
   auto ip_ufk = [&](int j) __attribute__((always_inline)) {   // Ufk[i][m] = c_m y_m[i]
     const int i = lane & 31, half = lane >> 5;
     const int jb = (j - 1 + half) & 3;
@@ -548,8 +581,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       const float yv[4] = {bf16_to_f32((uint16_t)(y.x & 0xFFFFu)), bf16_to_f32((uint16_t)(y.x >> 16)),
                            bf16_to_f32((uint16_t)(y.y & 0xFFFFu)), bf16_to_f32((uint16_t)(y.y >> 16))};
       float o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = ckey(j & 1, 16 * half + 4 * q4 + e, 15) * yv[e];
+      const float4 c4 = *reinterpret_cast<const float4*>(&sm.cm[j & 1][16 * half + 4 * q4]);
+      o[0] = c4.x * yv[0]; o[1] = c4.y * yv[1]; o[2] = c4.z * yv[2]; o[3] = c4.w * yv[3];
       *reinterpret_cast<float4*>(&sm.Ufk[j & 1][i][16 * half + 4 * q4]) = make_float4(o[0], o[1], o[2], o[3]);
     }
   };
@@ -567,7 +600,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   };
 
   // iterations c = -2 .. nchunks-1: state of sub-chunk c, preparation of c+1,
-  // commit of c+2, loads of c+3
+  // commit of c+2, loads of c+3.  Regression: four phases per iteration; inner
+  // product: two.
   const int c_begin = -2;
   if (wave < 2) {
     // ---------------- state waves ----------------
@@ -590,12 +624,39 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       const int cb = c & 1;
       HL xsf;
       floatx4 fk[2];
+      auto readout = [&]() __attribute__((always_inline)) {   // o_t = g_t (S0 q_t + O_y - Q_x XS)
+        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cb][lr][16 * rt + 4 * lg]));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) oacc = mma2(oacc, sf[ks], frag_bf16(&sm.Q[c & 3][lr][32 * ks + 8 * lg]));
+        if constexpr (REG) oacc = mma3(oacc, xsf, hl_pair(&sm.Qxhi[cb][lr][8 * lg], &sm.Qxlo[cb][lr][8 * lg]));
+        const float gt = sm.gam[cb][lr];
+        if ((long)c * CS + lr < L)
+          *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
+        orow += CS * dv;
+      };
+      auto carry = [&]() __attribute__((always_inline)) {     // S <- g_15 (S + Fk^T X)
+        const HL fkf = hl_x4(fk[0], fk[1]);
+        const float gC = sm.gam[cb][CS - 1];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][16 * kt + lr][4 * lg], &sm.XT[c & 3][16 * kt + lr][4 * lg]);
+          const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xt, fkf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
+        }
+      };
+      auto resplit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+      };
       __syncthreads();
-      // phase 1: XS = X S0^T, Fk = Ufk - H_x XS
       if (run) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cb][16 * rt + lr][16 * mi + 4 * lg]));
-        if constexpr (REG) {
+      }
+      if constexpr (REG) {
+        // phase 1: XS = X S0^T, Fk = Ufk - H_x XS
+        if (run) {
           floatx4 xs[2];
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {
@@ -609,37 +670,19 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
           for (int mi = 0; mi < 2; ++mi)
             fk[mi] = mma3(fk[mi], hl_pair(&sm.Hxhi[cb][16 * mi + lr][8 * lg], &sm.Hxlo[cb][16 * mi + lr][8 * lg]), xsf);
         }
-      }
-      __syncthreads();
-      // phase 2: readout  o_t = g_t (S0 q_t + O_y - Q_x XS)
-      if (run) {
-        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cb][lr][16 * rt + 4 * lg]));
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) oacc = mma2(oacc, sf[ks], frag_bf16(&sm.Q[c & 3][lr][32 * ks + 8 * lg]));
-        if constexpr (REG) oacc = mma3(oacc, xsf, hl_pair(&sm.Qxhi[cb][lr][8 * lg], &sm.Qxlo[cb][lr][8 * lg]));
-        const float gt = sm.gam[cb][lr];
-        if ((long)c * CS + lr < L)
-          *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
-        orow += CS * dv;
-      }
-      __syncthreads();
-      // phase 3: carry S <- g_15 (S + Fk^T X)
-      if (run) {
-        const HL fkf = hl_x4(fk[0], fk[1]);
-        const float gC = sm.gam[cb][CS - 1];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-          const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][16 * kt + lr][4 * lg], &sm.XT[c & 3][16 * kt + lr][4 * lg]);
-          const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xt, fkf);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
+        __syncthreads();
+        if (run) readout();           // phase 2
+        __syncthreads();
+        if (run) carry();             // phase 3
+        __syncthreads();
+        if (run) resplit();           // phase 4
+      } else {
+        if (run) {                    // phase 1
+          readout();
+          carry();
         }
-      }
-      __syncthreads();
-      // phase 4: split the new state
-      if (run) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+        __syncthreads();
+        if (run) resplit();           // phase 2
       }
     }
     __syncthreads();
@@ -655,11 +698,23 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     QSet qs0;
     if (wave == 6) prefetch_k(ks0, 0);
     if (wave == 7) prefetch_q(qs0, 0);
+    // commit of sub-chunk c+2 (its ring slot is free during the whole iteration)
+    // and the loads of c+3
+    auto move = [&](int c) __attribute__((always_inline)) {
+      if (wave == 6) {
+        if (live_chunk(c + 2)) commit_k(ks0, c + 2);
+        prefetch_k(ks0, c + 3);
+      }
+      if (wave == 7) {
+        if (live_chunk(c + 2)) commit_q(qs0, c + 2);
+        prefetch_q(qs0, c + 3);
+      }
+    };
     for (int c = c_begin; c < nchunks; ++c) {
       const int j = c + 1;
       const bool pj = live_chunk(j);
       __syncthreads();
-      // phase 1
+      // phase 1: Gram, q.x, scalars, keys transposed
       if (pj) {
         if (wave == 2) {
           if constexpr (REG) { gram_tile(j, 0, 0); gram_tile(j, 1, 0); }
@@ -675,29 +730,29 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         }
       }
       __syncthreads();
-      // phase 2
-      if (pj) {
-        if constexpr (REG) {
+      if constexpr (REG) {
+        // phase 2: diagonal blocks of T; -M and P' fragments; commits
+        if (pj) {
           if (wave == 4) diag_blocks(j);
-        } else {
-          if (wave == 2) ip_ufk(j);
-          if (wave == 3) ip_oy(j);
+          if (wave == 2) { mfrag_store(j, 0); if (NMF > 3) mfrag_store(j, 3); }
+          if (wave == 3 && NMF > 1) { mfrag_store(j, 1); mfrag_store(j, 2); }
+          if (wave == 5) {
+#pragma unroll
+            for (int k = 0; k < NKU; ++k) pfrag_store(k);
+          }
         }
-      }
-      __syncthreads();
-      // phase 3
-      if (pj) {
-        if constexpr (REG) {
+        move(c);
+        __syncthreads();
+        // phase 3: blocked substitution and folds
+        if (pj) {
           if (wave == 2) combine(j, true, 0);
           if (wave == 3) combine(j, true, 1);
           if (wave == 5) combine(j, false, 0);
           if (wave == 6) combine(j, false, 1);
         }
-      }
-      __syncthreads();
-      // phase 4
-      if (pj) {
-        if constexpr (REG) {
+        __syncthreads();
+        // phase 4: H_y Y, Q_y Y
+        if (pj) {
           if (wave == 2) { ufk_tile(j, 0, 0); ufk_tile(j, 0, 1); }
           if (wave == 3) { ufk_tile(j, 1, 0); ufk_tile(j, 1, 1); }
           if (wave == 4) {
@@ -706,11 +761,14 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
             oy_tile(j, 1, qy);
           }
         }
+      } else {
+        // phase 2: Fk and readout terms; commits
+        if (pj) {
+          if (wave == 2) ip_ufk(j);
+          if (wave == 3) ip_oy(j);
+        }
+        move(c);
       }
-      if (wave == 6 && live_chunk(c + 2)) commit_k(ks0, c + 2);
-      if (wave == 7 && live_chunk(c + 2)) commit_q(qs0, c + 2);
-      if (wave == 6) prefetch_k(ks0, c + 3);
-      if (wave == 7) prefetch_q(qs0, c + 3);
     }
     __syncthreads();
   }
