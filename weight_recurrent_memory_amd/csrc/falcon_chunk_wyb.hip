@@ -77,10 +77,10 @@ struct WybLds {
   uint16_t Hxlo[2][NXT][NXT + 8];
   uint16_t Qxhi[2][CS][NXT + 8];         // -Q_x rows
   uint16_t Qxlo[2][CS][NXT + 8];
-  uint16_t Hyhi[NXT][NXT + 8];           // H_y rows
-  uint16_t Hylo[NXT][NXT + 8];
-  uint16_t Qyhi[CS][NXT + 8];            // Q_y rows
-  uint16_t Qylo[CS][NXT + 8];
+  uint16_t Hyhi[2][NXT][NXT + 8];        // H_y rows
+  uint16_t Hylo[2][NXT][NXT + 8];
+  uint16_t Qyhi[2][CS][NXT + 8];         // Q_y rows
+  uint16_t Qylo[2][CS][NXT + 8];
   float Ufk[2][RW][NXT + 4];             // (H_y Y)[m][i] stored [i][m]
   float Oy[2][CS][RW + 4];               // (Q_y Y)[t][i]
   uint16_t Mhi[4][16][NXT + 8];          // -M fragments of the blocked solve, by (block, pair)
@@ -486,6 +486,23 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   // ---------------- phase 3 (regression): blocked substitution and folds ----------------
   // One wave per (F_x | F_y) x key-column tile mc.  V[b] (C layout) holds
   // V[16 b + 4 lg + e][16 mc + lr]; Vop[k] the split fragment over blocks 2k, 2k+1.
+  // Gath fragments (B operand over the unknowns of blocks 2k, 2k+1; column m = 16 mj + lr)
+  bf16x8 gath[2][NKU];
+#pragma unroll
+  for (int mj = 0; mj < 2; ++mj)
+#pragma unroll
+    for (int k = 0; k < NKU; ++k) {
+      uint32_t gw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ua = 32 * k + 4 * lg + 2 * (e & 1) + 16 * (e >> 1);   // slots 2e, 2e+1
+        const int m = 16 * mj + lr;
+        const uint32_t lo = (ua < U && mof(ua) == m) ? 0x3F80u : 0u;
+        const uint32_t hi = (ua + 1 < U && mof(ua + 1) == m) ? 0x3F80u : 0u;
+        gw[e] = lo | (hi << 16);
+      }
+      gath[mj][k] = __builtin_bit_cast(bf16x8, make_uint4(gw[0], gw[1], gw[2], gw[3]));
+    }
   auto combine = [&](int j, bool fx, int mc) __attribute__((always_inline)) {
     const int sb = j & 1;
     const float* sc = fx ? sm.omega[sb] : sm.zeta[sb];
@@ -523,28 +540,16 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
     // folds: (Gath^T V)^T tiles and (P' V)^T
     const float sign = fx ? -1.0f : 1.0f;          // -H_x, -Q_x; +H_y, +Q_y
-    uint16_t* Hhi = fx ? &sm.Hxhi[sb][0][0] : &sm.Hyhi[0][0];
-    uint16_t* Hlo = fx ? &sm.Hxlo[sb][0][0] : &sm.Hylo[0][0];
-    uint16_t* Qhi = fx ? &sm.Qxhi[sb][0][0] : &sm.Qyhi[0][0];
-    uint16_t* Qlo = fx ? &sm.Qxlo[sb][0][0] : &sm.Qylo[0][0];
+    uint16_t* Hhi = fx ? &sm.Hxhi[sb][0][0] : &sm.Hyhi[sb][0][0];
+    uint16_t* Hlo = fx ? &sm.Hxlo[sb][0][0] : &sm.Hylo[sb][0][0];
+    uint16_t* Qhi = fx ? &sm.Qxhi[sb][0][0] : &sm.Qyhi[sb][0][0];
+    uint16_t* Qlo = fx ? &sm.Qxlo[sb][0][0] : &sm.Qylo[sb][0][0];
     constexpr int HS = NXT + 8;
 #pragma unroll
     for (int mj = 0; mj < 2; ++mj) {
       floatx4 h = zacc;
 #pragma unroll
-      for (int k = 0; k < NKU; ++k) {
-        uint32_t gw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ua = 32 * k + 4 * lg + 2 * (e & 1) + 16 * (e >> 1);   // slots 2e, 2e+1
-          const int m = 16 * mj + lr;
-          const uint32_t lo = (ua < U && mof(ua) == m) ? 0x3F80u : 0u;
-          const uint32_t hi = (ua + 1 < U && mof(ua + 1) == m) ? 0x3F80u : 0u;
-          gw[e] = lo | (hi << 16);
-        }
-        const bf16x8 gf = __builtin_bit_cast(bf16x8, make_uint4(gw[0], gw[1], gw[2], gw[3]));
-        h = mma2(h, Vop[k], gf);
-      }
+      for (int k = 0; k < NKU; ++k) h = mma2(h, Vop[k], gath[mj][k]);
       const float hv[4] = {sign * h[0], sign * h[1], sign * h[2], sign * h[3]};
       store_split4(Hhi + (16 * mj + lr) * HS + 8 * lg + 4 * mc, Hlo + (16 * mj + lr) * HS + 8 * lg + 4 * mc, hv);
     }
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   };
   // ---------------- phase 4 (regression): H_y Y and Q_y Y ----------------
   auto ufk_tile = [&](int j, int mt, int it) __attribute__((always_inline)) {
-    const HL hy = hl_pair(&sm.Hyhi[16 * mt + lr][8 * lg], &sm.Hylo[16 * mt + lr][8 * lg]);
+    const HL hy = hl_pair(&sm.Hyhi[j & 1][16 * mt + lr][8 * lg], &sm.Hylo[j & 1][16 * mt + lr][8 * lg]);
     const floatx4 acc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, hy, yfrag(j, 16 * it + lr));
     *reinterpret_cast<float4*>(&sm.Ufk[j & 1][16 * it + lr][16 * mt + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   };
@@ -649,13 +654,13 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
       };
-      __syncthreads();
-      if (run) {
+      auto load_fk = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cb][16 * rt + lr][16 * mi + 4 * lg]));
-      }
+      };
+      __syncthreads();
       if constexpr (REG) {
-        // phase 1: XS = X S0^T, Fk = Ufk - H_x XS
+        // phase 1: XS = X S0^T
         if (run) {
           floatx4 xs[2];
 #pragma unroll
@@ -666,17 +671,24 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
               xs[mi] = mma2(xs[mi], frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * ks + 8 * lg]), sf[ks]);
           }
           xsf = hl_x4(xs[0], xs[1]);
+        }
+        __syncthreads();
+        // phase 2: Fk = Ufk - H_x XS; readout
+        if (run) {
+          load_fk();
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi)
             fk[mi] = mma3(fk[mi], hl_pair(&sm.Hxhi[cb][16 * mi + lr][8 * lg], &sm.Hxlo[cb][16 * mi + lr][8 * lg]), xsf);
+          readout();
         }
         __syncthreads();
-        if (run) readout();           // phase 2
-        __syncthreads();
-        if (run) carry();             // phase 3
-        __syncthreads();
-        if (run) resplit();           // phase 4
+        // phase 3: carry, new split
+        if (run) {
+          carry();
+          resplit();
+        }
       } else {
+        if (run) load_fk();
         if (run) {                    // phase 1
           readout();
           carry();
@@ -714,54 +726,54 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       const int j = c + 1;
       const bool pj = live_chunk(j);
       __syncthreads();
-      // phase 1: Gram, q.x, scalars, keys transposed
-      if (pj) {
-        if (wave == 2) {
-          if constexpr (REG) { gram_tile(j, 0, 0); gram_tile(j, 1, 0); }
-        } else if (wave == 3) {
-          if constexpr (REG) { gram_tile(j, 0, 1); gram_tile(j, 1, 1); }
-        } else if (wave == 4) {
-          qx_tile(j, 0);
-          qx_tile(j, 1);
-        } else if (wave == 5) {
-          scalars(j);
-        } else {
-          transpose_keys(j, 64 * (wave - 6) + lane);
-        }
-      }
-      __syncthreads();
       if constexpr (REG) {
+        // phase 1: H_y Y, Q_y Y of sub-chunk c; Gram, q.x, scalars, keys transposed of c+1
+        const bool pc = live_chunk(c);
+        if (wave == 2) {
+          if (pc) ufk_tile(c, 0, 0);
+          if (pj) { gram_tile(j, 0, 0); gram_tile(j, 1, 0); }
+        } else if (wave == 3) {
+          if (pc) ufk_tile(c, 0, 1);
+          if (pj) { gram_tile(j, 0, 1); gram_tile(j, 1, 1); }
+        } else if (wave == 4) {
+          if (pc) ufk_tile(c, 1, 0);
+          if (pj) { qx_tile(j, 0); qx_tile(j, 1); }
+        } else if (wave == 5) {
+          if (pc) ufk_tile(c, 1, 1);
+          if (pj) transpose_keys(j, lane);
+        } else if (wave == 6) {
+          if (pc) oy_tile(c, 0, hl_pair(&sm.Qyhi[c & 1][lr][8 * lg], &sm.Qylo[c & 1][lr][8 * lg]));
+          if (pj) scalars(j);
+        } else {
+          if (pc) oy_tile(c, 1, hl_pair(&sm.Qyhi[c & 1][lr][8 * lg], &sm.Qylo[c & 1][lr][8 * lg]));
+          if (pj) transpose_keys(j, 64 + lane);
+        }
+        __syncthreads();
         // phase 2: diagonal blocks of T; -M and P' fragments; commits
         if (pj) {
           if (wave == 4) diag_blocks(j);
-          if (wave == 2) { mfrag_store(j, 0); if (NMF > 3) mfrag_store(j, 3); }
-          if (wave == 3 && NMF > 1) { mfrag_store(j, 1); mfrag_store(j, 2); }
-          if (wave == 5) {
-#pragma unroll
-            for (int k = 0; k < NKU; ++k) pfrag_store(k);
-          }
+          if (wave == 2) { mfrag_store(j, 0); if (NMF > 1) mfrag_store(j, 1); }
+          if (wave == 3 && NMF > 2) { mfrag_store(j, 2); mfrag_store(j, 3); }
+          if (wave == 5) pfrag_store(0);
+          if (wave == 7 && NKU > 1) pfrag_store(NKU - 1);
         }
         move(c);
         __syncthreads();
-        // phase 3: blocked substitution and folds
+        // phase 3: blocked substitution and folds (one wave per SIMD)
         if (pj) {
           if (wave == 2) combine(j, true, 0);
           if (wave == 3) combine(j, true, 1);
-          if (wave == 5) combine(j, false, 0);
-          if (wave == 6) combine(j, false, 1);
-        }
-        __syncthreads();
-        // phase 4: H_y Y, Q_y Y
-        if (pj) {
-          if (wave == 2) { ufk_tile(j, 0, 0); ufk_tile(j, 0, 1); }
-          if (wave == 3) { ufk_tile(j, 1, 0); ufk_tile(j, 1, 1); }
-          if (wave == 4) {
-            const HL qy = hl_pair(&sm.Qyhi[lr][8 * lg], &sm.Qylo[lr][8 * lg]);
-            oy_tile(j, 0, qy);
-            oy_tile(j, 1, qy);
-          }
+          if (wave == 4) combine(j, false, 0);
+          if (wave == 5) combine(j, false, 1);
         }
       } else {
+        // phase 1: Gram-free stages of c+1
+        if (pj) {
+          if (wave == 4) { qx_tile(j, 0); qx_tile(j, 1); }
+          else if (wave == 5) scalars(j);
+          else if (wave >= 6) transpose_keys(j, 64 * (wave - 6) + lane);
+        }
+        __syncthreads();
         // phase 2: Fk and readout terms; commits
         if (pj) {
           if (wave == 2) ip_ufk(j);
