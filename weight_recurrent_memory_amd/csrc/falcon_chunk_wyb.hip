@@ -510,6 +510,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
     floatx4 V[NB];
     HL Vop[NKU];
+    uint4 vh[NKU], vl[NKU];
     // every operand fragment is read before the substitution starts
     HL mf[NMF], tf[NB], pf[NKU];
 #pragma unroll
@@ -535,8 +536,19 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         acc = mma3(acc, mf[b == 1 ? 0 : b == 2 ? 1 : (k == 0 ? 2 : 3)], Vop[k]);
       const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
       V[b] = mma3(zacc, tf[b], hl_two(av, z4));
-      if ((b & 1) == 0) Vop[b / 2] = hl_x4(V[b], zacc);
-      else Vop[b / 2] = hl_x4(V[b - 1], V[b]);
+      // split V[b] once; its halves fill slots 0-3 (b even) or 4-7 (b odd) of Vop
+      uint32_t hh[2], ll[2];
+      split_pair(V[b][0], V[b][1], hh[0], ll[0]);
+      split_pair(V[b][2], V[b][3], hh[1], ll[1]);
+      if ((b & 1) == 0) {
+        vh[b / 2] = make_uint4(hh[0], hh[1], 0u, 0u);
+        vl[b / 2] = make_uint4(ll[0], ll[1], 0u, 0u);
+      } else {
+        vh[b / 2].z = hh[0]; vh[b / 2].w = hh[1];
+        vl[b / 2].z = ll[0]; vl[b / 2].w = ll[1];
+      }
+      Vop[b / 2].hi = __builtin_bit_cast(bf16x8, vh[b / 2]);
+      Vop[b / 2].lo = __builtin_bit_cast(bf16x8, vl[b / 2]);
     }
     // folds: (Gath^T V)^T tiles and (P' V)^T
     const float sign = fx ? -1.0f : 1.0f;          // -H_x, -Q_x; +H_y, +Q_y
@@ -660,8 +672,9 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       };
       __syncthreads();
       if constexpr (REG) {
-        // phase 1: XS = X S0^T
+        // phase 1: split the state, XS = X S0^T
         if (run) {
+          resplit();
           floatx4 xs[2];
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {
@@ -682,11 +695,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
           readout();
         }
         __syncthreads();
-        // phase 3: carry, new split
-        if (run) {
-          carry();
-          resplit();
-        }
+        // phase 3: carry
+        if (run) carry();
       } else {
         if (run) load_fk();
         if (run) {                    // phase 1
