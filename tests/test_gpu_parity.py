@@ -173,12 +173,29 @@ def test_chunk_deterministic():
 @pytest.mark.parametrize("L", [1, 5, 64, 65])
 def test_chunk_short_sequences(L):
     inp = seq_inputs(1, 2, L, 64, 32, seed=430 + L, dtype="bf16")
-    for variant in (fw.FALCON_1, fw.FALCON_3A):
+    for variant in (fw.FALCON_1, fw.FALCON_3, fw.FALCON_3A):
         win = _win(variant, 4)
         o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=0.5, lam=0.01, eps=1e-6,
                         window=win, chunk=64)
         o_ref, S_ref, _ = _oracle(variant, inp, beta=0.5, lam=0.01, eps=1e-6, window=win)
         err, zok = token_normwise_err(o, o_ref)
+        assert zok and err <= TOL_BF16
+        assert state_err(S, S_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 32)])
+def test_chunk_window_carried_key(variant, dk, dv):
+    """Sliding window with the previous key carried in (x_1 = k_prev), per-token gains."""
+    for win in (2, 4):
+        inp = seq_inputs(2, 2, 83, dk, dv, seed=470 + variant + win + dk, dtype="bf16",
+                         with_k_prev=True, beta_per_token=True)
+        o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=None, lam=0.02, eps=1e-6,
+                        window=win, chunk=64, carried=True)
+        o_ref, S_ref, _ = _oracle(variant, inp, beta=None, lam=0.02, eps=1e-6, window=win,
+                                  carried=True)
+        err, zok = token_normwise_err(o, o_ref)
+        print("window %d dk %d: o err %.3e S err %.3e" % (win, dk, err, state_err(S, S_ref)))
         assert zok and err <= TOL_BF16
         assert state_err(S, S_ref) <= TOL_BF16
 
