@@ -24,15 +24,16 @@
 //
 // Structure.  One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
 // Iteration c: waves 0, 1 run the state of sub-chunk c (16 rows each, S in
-// registers); waves 2..7 prepare sub-chunk c+1 in four phases separated by
-// workgroup barriers:
-//   1  Gram and q.x of the key tile, keys transposed, per-step scalars
-//   2  T_bb by a DPP forward substitution (regression) | Fk and readout terms
-//      of the inner-product family
-//   3  blocked substitution for F_x, F_y and the folds H, Q (regression)
-//   4  H_y Y and Q_y Y (regression); commit the loads of sub-chunk c+2 to LDS
-//      and issue those of c+3
-// The state waves spread their work over the same four phases.
+// registers); waves 2..7 finish sub-chunk c and prepare c+1 in three phases
+// separated by workgroup barriers (regression family):
+//   1  H_y Y, Q_y Y of c | Gram and q.x of the key tile, keys transposed and
+//      per-step scalars of c+1               (state: split S, XS = X S0^T)
+//   2  T_bb by a DPP forward substitution, -M and P' fragments of c+1; commit
+//      the loads of c+2 to LDS and issue those of c+3   (state: Fk, readout)
+//   3  blocked substitution for F_x, F_y and the folds H, Q of c+1, one wave
+//      per SIMD                              (state: carry)
+// The inner-product family needs two phases: scalars, q.x and transposes of
+// c+1 (state: readout, carry), then Fk and Q_y Y of c+1 and the commits.
 // Operands are stored in the fragment order of the register operand they meet
 // (within a 32-wide group, slots 8g..8g+3 hold indices 4g..4g+3 and
 // 8g+4..8g+7 hold 16+4g..16+4g+3); non-exact operands are split-bf16 (Henry,
