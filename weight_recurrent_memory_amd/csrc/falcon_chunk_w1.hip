@@ -35,6 +35,14 @@
 namespace falcon {
 namespace {
 
+// v of lane - N within the same 16-lane row (DPP row_shr); lanes whose source
+// lies outside the row return `fill`
+template <int N>
+__device__ __forceinline__ float row_shr(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             0x110 + N, 0xF, 0xF, false));
+}
+
 constexpr int RB = 16;
 constexpr int NRB = 2;
 constexpr int RW = RB * NRB;
@@ -253,6 +261,39 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     }
   };
 
+  // Per-channel scalars of rows r0 .. r0 + 64/CS - 1 in one call (lane = row slot
+  // x CS + step): prefix products by DPP row shifts (16-lane rows), the upper half
+  // of a 32-step row times the lower half's total.
+  auto scalars_rows = [&](int s, int cidx, int dst, int r0) __attribute__((always_inline)) {
+    static_assert(!PERROW || CS == 16 || CS == 32, "per-channel sub-chunks of 16 or 32 steps");
+    const long t0 = (long)cidx * CS;
+    const int c = (int)((L - t0) < CS ? (L - t0) : CS);
+    const int t = lane % CS, row = r0 + lane / CS;
+    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+    float eta = 0.0f, dec = 1.0f;
+    if (live) {
+      eta = bf16_to_f32(sm.BT[s][row][t]) * __builtin_amdgcn_rcpf(a.eps + sm.nrm[s][t]);
+      dec = 1.0f - eta * a.lambda;
+    }
+    float g = dec;
+    g *= row_shr<1>(g, 1.0f);
+    g *= row_shr<2>(g, 1.0f);
+    g *= row_shr<4>(g, 1.0f);
+    g *= row_shr<8>(g, 1.0f);
+    float fill = 1.0f;
+    if constexpr (CS == 32) {
+      const float tA = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 15));
+      const float tB = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 47));
+      const float tot = lane < 32 ? tA : tB;
+      if ((lane & 31) >= 16) g *= tot;
+      fill = (lane & 31) == 16 ? tot : 1.0f;
+    }
+    const float gprev = row_shr<1>(g, fill);
+    sm.gam[dst][row][t] = g;
+    sm.gm1[dst][row][t] = gprev;
+    sm.zeta[dst][row][t] = eta * __builtin_amdgcn_rcpf(g);
+  };
+
   // Gram (regression) and q.x tiles of slot s: lower triangle of 16x16 tiles.
   constexpr int NLT = NTT * (NTT + 1) / 2;
   auto gram_tile = [&](int s, int tt) __attribute__((always_inline)) {
@@ -426,8 +467,11 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         }
       }
     }
-    if (PERROW && wave >= NW - 4) {
-      for (int i = wave - (NW - 4); i < RW; i += 4) scalars(cur, ci, 0, i, wave);
+    if constexpr (PERROW) {
+      if (wave >= NW - 4) {
+        constexpr int RPC = 64 / CS;     // rows per call
+        for (int r0 = RPC * (wave - (NW - 4)); r0 < RW; r0 += 4 * RPC) scalars_rows(cur, ci, 0, r0);
+      }
     }
     __syncthreads();
 
