@@ -23,10 +23,11 @@
 //            and issue chunk c+2's global loads; keys of chunk c transposed;
 //            S0 x_t and S0 q_t (kept in registers for the readout);
 //            off-diagonal solve blocks M_bj of chunk c; per-row scalars (Falcon-2)
-//   phase 2  solve of chunk c (one wave per 16-row block)  ||  Gram and q.x of
-//            chunk c+1, scalars of chunk c+1 (shared eta)
+//   phase 2  solve of chunk c (shared eta: one wave per 16-row block, next to
+//            Gram, q.x and scalars of chunk c+1; per-channel eta: one value row
+//            per 16-lane row on every wave)
 //   phase 3  readout and state carry of chunk c  ||  diagonal-block inverses
-//            of chunk c+1 (shared eta) or its Gram (per-channel eta)
+//            of chunk c+1 (shared eta) or its Gram and q.x (per-channel eta)
 // One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
 #include "falcon_device.h"
 #include "falcon_launch.h"
@@ -41,6 +42,38 @@ template <int N>
 __device__ __forceinline__ float row_shr(float v, float fill) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
                                                              0x110 + N, 0xF, 0xF, false));
+}
+
+// g times the g of lane - N within the same 16-lane row; lanes whose source lies
+// outside the row are disabled by the DPP bounds rule and keep g (the nop gives
+// the two wait states a DPP read needs after a VALU write)
+template <int N>
+__device__ __forceinline__ float row_shr_mul(float g) {
+  asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:%1 row_mask:0xf bank_mask:0xf" : "+v"(g) : "i"(N));
+  return g;
+}
+
+// acc + g * (v of lane N of the same 16-lane row); the nop gives the two wait
+// states a DPP read needs after a VALU write of v
+template <int N>
+__device__ __forceinline__ float fmac_bcast(float acc, float v, float g) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc) : "v"(v), "v"(g), "i"(N));
+  return acc;
+}
+
+// Per-channel forward substitution, step M onwards, for the row held by one
+// 16-lane row: lane l owns the unknowns u = l + 16 j, with partial sums
+// acc[j] = sum_{m<M} Gs[u][m] z_m and g[j][m] = Gs[u][m] (zero for m >= u).
+// z_M is formed on every lane and taken from lane M mod 16, its owner.
+template <int NS, int M>
+__device__ __forceinline__ void row_sweep(float (&acc)[NS], const float (&g)[NS][16 * NS], const float (&rp)[NS],
+                                          const float (&gm)[NS], const float (&ze)[NS]) {
+  constexpr int J = M / 16;
+  const float z = ze[J] * __builtin_fmaf(-gm[J], acc[J], rp[J]);
+#pragma unroll
+  for (int j = J; j < NS; ++j) acc[j] = fmac_bcast<M % 16>(acc[j], z, g[j][M]);
+  if constexpr (M + 1 < 16 * NS) row_sweep<NS, M + 1>(acc, g, rp, gm, ze);
 }
 
 constexpr int RB = 16;
@@ -78,7 +111,6 @@ struct W1Lds {
   uint16_t Plo[2][CS][CS + 8];
   uint16_t SAhi[(REG && !PERROW) ? NB : 1][16][CS + 8];   // [T_bb | -M_b0 | ...]
   uint16_t SAlo[(REG && !PERROW) ? NB : 1][16][CS + 8];
-  float RP[(REG && PERROW) ? RW : 1][CS + 4];              // per-row right-hand sides
   alignas(16) float gam[SCB][SR][CS];
   alignas(16) float gm1[SCB][SR][CS];
   alignas(16) float zeta[SCB][SR][CS];
@@ -261,37 +293,80 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     }
   };
 
-  // Per-channel scalars of rows r0 .. r0 + 64/CS - 1 in one call (lane = row slot
-  // x CS + step): prefix products by DPP row shifts (16-lane rows), the upper half
-  // of a 32-step row times the lower half's total.
-  auto scalars_rows = [&](int s, int cidx, int dst, int r0) __attribute__((always_inline)) {
+  // Per-channel scalars of NC groups of 64/CS rows, group k = rows r0 + k rstep
+  // + lane / CS (lane = row slot x CS + step): prefix products by DPP row shifts
+  // (16-lane rows), the upper half of a 32-step row times the lower half's total.
+  // All loads first, then the scans, then the stores: LDS stores in between
+  // would keep the compiler from issuing the later loads early.
+  auto scalars_rows = [&](auto nc_tag, int s, int cidx, int dst, int r0, int rstep) __attribute__((always_inline)) {
     static_assert(!PERROW || CS == 16 || CS == 32, "per-channel sub-chunks of 16 or 32 steps");
+    constexpr int NC = decltype(nc_tag)::value;
     const long t0 = (long)cidx * CS;
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
-    const int t = lane % CS, row = r0 + lane / CS;
+    const int t = lane % CS, rl = lane / CS;
     const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
-    float eta = 0.0f, dec = 1.0f;
-    if (live) {
-      eta = bf16_to_f32(sm.BT[s][row][t]) * __builtin_amdgcn_rcpf(a.eps + sm.nrm[s][t]);
-      dec = 1.0f - eta * a.lambda;
+    const float rn = __builtin_amdgcn_rcpf(a.eps + sm.nrm[s][t]);
+    float eta[NC], g[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const float bv = bf16_to_f32(sm.BT[s][r0 + k * rstep + rl][t]);
+      eta[k] = live ? bv * rn : 0.0f;
+      g[k] = __builtin_fmaf(-eta[k], a.lambda, 1.0f);
     }
-    float g = dec;
-    g *= row_shr<1>(g, 1.0f);
-    g *= row_shr<2>(g, 1.0f);
-    g *= row_shr<4>(g, 1.0f);
-    g *= row_shr<8>(g, 1.0f);
-    float fill = 1.0f;
-    if constexpr (CS == 32) {
-      const float tA = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 15));
-      const float tB = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), 47));
-      const float tot = lane < 32 ? tA : tB;
-      if ((lane & 31) >= 16) g *= tot;
-      fill = (lane & 31) == 16 ? tot : 1.0f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<1>(g[k]);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<2>(g[k]);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<4>(g[k]);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<8>(g[k]);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      float fill = 1.0f;
+      if constexpr (CS == 32) {
+        const float tA = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g[k]), 15));
+        const float tB = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g[k]), 47));
+        const float tot = lane < 32 ? tA : tB;
+        if ((lane & 31) >= 16) g[k] *= tot;
+        fill = (lane & 31) == 16 ? tot : 1.0f;
+      }
+      const float gprev = row_shr<1>(g[k], fill);
+      const int row = r0 + k * rstep + rl;
+      sm.gam[dst][row][t] = g[k];
+      sm.gm1[dst][row][t] = gprev;
+      sm.zeta[dst][row][t] = eta[k] * __builtin_amdgcn_rcpf(g[k]);
     }
-    const float gprev = row_shr<1>(g, fill);
-    sm.gam[dst][row][t] = g;
-    sm.gm1[dst][row][t] = gprev;
-    sm.zeta[dst][row][t] = eta * __builtin_amdgcn_rcpf(g);
+  };
+
+  // Per-channel residual solve of the chunk in slot s: value row 4 wave + lg on
+  // the 16-lane row lg, right-hand sides r_u = y_u - g_{u-1} (S0 x_u), and the
+  // per-channel Gram (strictly lower, zero at and above the diagonal) held per
+  // lane; once the sweep has passed step u the partial sum of u no longer
+  // changes, so each lane forms its own z_u from it at the end.
+  auto row_solve = [&](int s, typename SM::Split* zt) __attribute__((always_inline)) {
+    constexpr int NS = CS / 16;
+    const int i = 4 * wave + lg;
+    float g[NS][CS], rp[NS], gm[NS], ze[NS], acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+#pragma unroll
+      for (int m = 0; m < 16 * (j + 1); m += 4) {
+        const float4 gv = *reinterpret_cast<const float4*>(&sm.GT[lr + 16 * j][m]);
+        g[j][m] = gv.x; g[j][m + 1] = gv.y; g[j][m + 2] = gv.z; g[j][m + 3] = gv.w;
+      }
+      const int u = lr + 16 * j;
+      gm[j] = sm.gm1[0][i][u];
+      ze[j] = sm.zeta[0][i][u];
+      rp[j] = bf16_to_f32(sm.YT[s][i][u]) - gm[j] * sm.XS[i][u];
+      acc[j] = 0.0f;
+    }
+    row_sweep<NS, 0>(acc, g, rp, gm, ze);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float z = ze[j] * __builtin_fmaf(-gm[j], acc[j], rp[j]);
+      split1(z, zt->hi[i][lr + 16 * j], zt->lo[i][lr + 16 * j]);
+    }
   };
 
   // Gram (regression) and q.x tiles of slot s: lower triangle of 16x16 tiles.
@@ -469,8 +544,8 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     }
     if constexpr (PERROW) {
       if (wave >= NW - 4) {
-        constexpr int RPC = 64 / CS;     // rows per call
-        for (int r0 = RPC * (wave - (NW - 4)); r0 < RW; r0 += 4 * RPC) scalars_rows(cur, ci, 0, r0);
+        constexpr int RPC = 64 / CS;     // rows per 64 lanes
+        scalars_rows(std::integral_constant<int, RW / (4 * RPC)>{}, cur, ci, 0, RPC * (wave - (NW - 4)), 4 * RPC);
       }
     }
     __syncthreads();
@@ -478,9 +553,9 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     // ================= phase 2 =================
     typename SM::Split* const zt = &sm.slot[cur].ZT;   // keys of ci are consumed
     if (REG) {
-      if (wave < nrb) {
+      if (!PERROW && wave < nrb) {
         const int ib = 16 * wave;
-        if (!PERROW) {
+        {
           for (int bb = 0; bb < NB; ++bb) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_nt<false, false>(acc, 16 * (bb + 1),
@@ -512,48 +587,10 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
             store_split4(&zt->hi[ib + lr][16 * bb + 4 * lg], &zt->lo[ib + lr][16 * bb + 4 * lg], z);
             wave_sync();
           }
-        } else {
-          // right-hand sides, then per stage: off-diagonal coupling on MFMA and the
-          // diagonal block by per-row forward substitution
-          for (int idx = lane; idx < RB * CS; idx += 64) {
-            const int i = ib + idx / CS, u = idx % CS;
-            sm.RP[i][u] = bf16_to_f32(sm.YT[cur][i][u]) - sm.gm1[0][i][u] * sm.XS[i][u];
-          }
-          wave_sync();
-          for (int bb = 0; bb < NB; ++bb) {
-            const int u0 = 16 * bb;
-            if (bb > 0) {
-              floatx4 cacc = {0.f, 0.f, 0.f, 0.f};
-              cacc = mma_nt<false, false>(cacc, u0,
-                  [&](int r, int k) { return hl_f32(&sm.GT[u0 + r][k]); },
-                  [&](int r, int k) { return hl_pair(&zt->hi[ib + r][k], &zt->lo[ib + r][k]); });
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int u = u0 + 4 * lg + e;
-                sm.RP[ib + lr][u] -= sm.gm1[0][ib + lr][u] * cacc[e];
-              }
-              wave_sync();
-            }
-            if (lane < 16) {
-              const int i = ib + lane;
-              float acc[16], z[16];
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-              for (int m = 0; m < 16; ++m) {
-                const int u = u0 + m;
-                const float e = sm.RP[i][u] - sm.gm1[0][i][u] * acc[m];
-                z[m] = sm.zeta[0][i][u] * e;
-#pragma unroll
-                for (int r = m + 1; r < 16; ++r) acc[r] += sm.GT[u0 + r][u] * z[m];
-              }
-#pragma unroll
-              for (int r = 0; r < 16; r += 4)
-                store_split4(&zt->hi[i][u0 + r], &zt->lo[i][u0 + r], &z[r]);
-            }
-            wave_sync();
-          }
         }
+      }
+      if constexpr (PERROW) {
+        if (wave < 4 * nrb) row_solve(cur, zt);
       }
     } else {
       // inner-product family: z_t = zeta_t y_t
@@ -563,7 +600,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         split1(zv, zt->hi[i][t], zt->lo[i][t]);
       }
     }
-    if (has_next) {
+    if (has_next && !(REG && PERROW)) {
       // state-independent preparation of chunk ci+1 on the waves not solving
       const int w0 = REG ? NRB : 0;
       const int nws = NW - w0;
@@ -620,7 +657,12 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     if (has_next) {
       if (REG && !PERROW && wave == NW - 1) diag_inverse(nxt);
       if (REG && PERROW) {
-        for (int task = wave; task < NLT; task += NW) gram_tile(nxt, task);
+        // Gram of chunk ci+1 on waves 0-2 and its q.x on waves 4-6 (the solve
+        // of phase 2 occupies every wave)
+        for (int task = wave & 3; task < NLT; task += 4) {
+          if (wave >= 4) qx_tile(nxt, task);
+          else gram_tile(nxt, task);
+        }
       }
     }
     __syncthreads();
