@@ -119,7 +119,8 @@ int falcon_fwd_recurrent(int variant, int window, float beta, const void* beta_t
  * falcon_fwd_chunk - the chunk-parallel form (explainer §3 "chunk-parallel";
  * 163.com section 02 (2): parallel inside a chunk, only the fixed-size state
  * crosses chunks).  Same arguments and results as falcon_fwd_recurrent plus
- *   chunk     tokens per chunk, in {16, 32, 64}; L % chunk == 0
+ *   chunk     tokens per chunk, in {16, 32, 64}; any L (a short last chunk is
+ *             handled in place)
  * Restrictions (FALCON_ERR_UNSUPPORTED): dtype must be FALCON_BF16;
  * window <= 4; window <= chunk.
  * The result equals the recurrence up to floating-point rounding (state
