@@ -42,6 +42,12 @@ notes of the repository):
 * A fresh sequence starts at S_0 = 0 with x_1 = 0; then S_1 = 0 exactly.  With
   eps = 0 the literal step is 0/0 there; the oracle defines S_1 = 0 and raises
   for a zero denominator on a non-zero state.
+* Resuming a Falcon-3/3A sequence: besides S and the carried key, the window
+  of the first B-1 steps reaches back into the previous call, so the caller
+  carries the B-1 latest samples (x_j, y_j) as a history (oldest first).  The
+  window is then "the B latest causal samples" over the joined sample list.
+  A zero sample adds nothing to n_t or to the write, so a history of zeros is
+  the same as none (a fresh sequence).
 
 Functions
 ---------
@@ -51,6 +57,9 @@ Functions
                         products (the masked-parallel form of explainer §3),
                         tiny inputs only.
 ``falcon_decode_step``  exactly one step of the recurrence with x = k_prev.
+``falcon_history``      the B-1 latest samples after a call (the history the
+                        next call of a Falcon-3/3A sequence needs).
+``falcon_decode_step_window``  one step with a carried window history.
 """
 from __future__ import annotations
 
@@ -105,31 +114,49 @@ def _check_args(variant, window, q, k, v, beta_t):
         raise ValueError("per-channel beta is Falcon-2/2A only")
 
 
+def _join_history(window, x, y, x_hist, y_hist):
+    """Samples of the history (oldest first) followed by those of this call."""
+    if x_hist is None and y_hist is None:
+        return x, y, 0
+    if x_hist is None or y_hist is None:
+        raise ValueError("x_hist and y_hist go together")
+    if window < 2:
+        raise ValueError("a window history needs window > 1")
+    if x_hist.shape != x.shape[:2] + (window - 1, x.shape[-1]) or \
+            y_hist.shape != y.shape[:2] + (window - 1, y.shape[-1]):
+        raise ValueError("history shapes must be [B, H, window-1, d]")
+    return np.concatenate([x_hist, x], axis=2), np.concatenate([y_hist, y], axis=2), window - 1
+
+
 def falcon_recurrence(variant, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6, window=1,
                       beta_t=None, k_prev=None, S0=None, same_step=False,
-                      return_states=False):
+                      x_hist=None, y_hist=None, return_states=False):
     """Run the Falcon recurrence in fp64, one token at a time.
 
     Shapes: q, k [B, H, L, dk]; v [B, H, L, dv]; beta_t None, [B, H, L] or
-    [B, H, L, dv] (Falcon-2/2A); k_prev [B, H, dk]; S0 [B, H, dv, dk].
+    [B, H, L, dv] (Falcon-2/2A); k_prev [B, H, dk]; S0 [B, H, dv, dk];
+    x_hist [B, H, window-1, dk], y_hist [B, H, window-1, dv]: the samples
+    before step 1 that the first windows reach (oldest first), or None.
     Returns (o [B, H, L, dv], S_L [B, H, dv, dk], k_last [B, H, dk]) and, with
     ``return_states``, also every S_t as [B, H, L, dv, dk].
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     beta_t, k_prev, S0 = _as64(beta_t), _as64(k_prev), _as64(S0)
+    x_hist, y_hist = _as64(x_hist), _as64(y_hist)
     _check_args(variant, window, q, k, v, beta_t)
     Bz, H, L, dk = q.shape
     dv = v.shape[-1]
     regression = _REGRESSION[variant]
     x = _shift_keys(k, k_prev, same_step)
     y = v
+    x, y, P = _join_history(window, x, y, x_hist, y_hist)   # sample P + t is step t's own
     S = np.zeros((Bz, H, dv, dk)) if S0 is None else S0.copy()
     o = np.zeros((Bz, H, L, dv))
     states = np.zeros((Bz, H, L, dv, dk)) if return_states else None
     for t in range(L):
-        lo = max(0, t - window + 1)
-        Xw = x[:, :, lo:t + 1]                      # [B, H, w, dk]
-        Yw = y[:, :, lo:t + 1]                      # [B, H, w, dv]
+        lo = max(0, P + t - window + 1)
+        Xw = x[:, :, lo:P + t + 1]                  # [B, H, w, dk]
+        Yw = y[:, :, lo:P + t + 1]                  # [B, H, w, dv]
         n = np.sum(Xw * Xw, axis=(-1, -2))          # [B, H]
         b = _beta_rows(beta, beta_t, t, (Bz, H), dv)  # [B, H, dv]
         denom = eps + n
@@ -157,6 +184,47 @@ def falcon_recurrence(variant, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6, window=1
     return o, S, k_last
 
 
+def falcon_history(k, v, window, *, k_prev=None, x_hist=None, y_hist=None, same_step=False):
+    """The window-1 latest samples (x_j, y_j) after a call, oldest first.
+
+    The joined sample list is the incoming history (if any) followed by this
+    call's samples x_t (the shifted keys) and y_t = v_t; the result is its
+    tail, padded in front with zero samples when the list is shorter.
+    Returns (x_hist [B, H, window-1, dk], y_hist [B, H, window-1, dv]).
+    """
+    k, v = _as64(k), _as64(v)
+    x = _shift_keys(k, _as64(k_prev), same_step)
+    x, y, _ = _join_history(window, x, v, _as64(x_hist), _as64(y_hist))
+    n = window - 1
+    Bz, H, Lx, dk = x.shape
+    dv = y.shape[-1]
+    xo = np.zeros((Bz, H, n, dk))
+    yo = np.zeros((Bz, H, n, dv))
+    take = min(n, Lx)
+    if take > 0:
+        xo[:, :, n - take:] = x[:, :, Lx - take:]
+        yo[:, :, n - take:] = y[:, :, Lx - take:]
+    return xo, yo
+
+
+def falcon_decode_step_window(variant, window, S, k_prev, x_hist, y_hist, q, k, v, *,
+                              beta=0.5, lam=0.0, eps=1e-6):
+    """One decode step of Falcon-3/3A with a carried window history.
+
+    x = k_prev, y = v; the window is the history (window-1 samples, oldest
+    first) plus this sample.  Shapes: S [N, H, dv, dk]; k_prev, q, k [N, H, dk];
+    v [N, H, dv]; x_hist [N, H, window-1, dk]; y_hist [N, H, window-1, dv].
+    Returns (o, S_new, k_prev_new, x_hist_new, y_hist_new).
+    """
+    q3, k3, v3 = _as64(q)[:, :, None], _as64(k)[:, :, None], _as64(v)[:, :, None]
+    o, S_new, _ = falcon_recurrence(variant, q3, k3, v3, beta=beta, lam=lam, eps=eps,
+                                    window=window, k_prev=_as64(k_prev), S0=_as64(S),
+                                    x_hist=x_hist, y_hist=y_hist)
+    xh, yh = falcon_history(k3, v3, window, k_prev=_as64(k_prev), x_hist=x_hist,
+                            y_hist=y_hist)
+    return o[:, :, 0], S_new, _as64(k).copy(), xh, yh
+
+
 def falcon_decode_step(variant, S, k_prev, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6,
                        beta_t=None):
     """One decode step: x = k_prev, y = v, update S, o = S_new q; k_prev <- k.
@@ -165,7 +233,8 @@ def falcon_decode_step(variant, S, k_prev, q, k, v, *, beta=0.5, lam=0.0, eps=1e
     beta_t None, [N, H] or [N, H, dv].  Returns (o, S_new, k_prev_new).
     """
     if variant in _WINDOWED:
-        raise ValueError("decode keeps no window history; Falcon-3/3A unsupported")
+        raise ValueError("Falcon-3/3A decode needs its window history: "
+                         "use falcon_decode_step_window")
     bt = None
     if beta_t is not None:
         beta_t = _as64(beta_t)

@@ -291,3 +291,91 @@ def test_bf16_rounding_matches_torch():
     ours = to_bf16_values(a)
     ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(ours, ref)
+
+
+def _seg(inp, lo, hi):
+    return {n: (None if inp.get(n) is None else inp[n][:, :, lo:hi])
+            for n in ("q", "k", "v", "beta_t")}
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_3, fo.FALCON_3A])
+@pytest.mark.parametrize("window", [2, 3, 4])
+@pytest.mark.parametrize("cuts", [(5,), (1, 2), (2, 3, 9)])
+def test_window_resume_split(variant, window, cuts):
+    # a resumed Falcon-3/3A call carries S, the key and the window-1 latest
+    # samples; pieces of any length (also shorter than the window) chained this
+    # way give the one-call result over the whole sequence
+    L = 13
+    inp = _tiny(83 + window, B=2, H=2, L=L, dk=4, dv=3, beta_per_token=True)
+    kw = dict(beta=None, lam=0.05, eps=1e-6, window=window)
+    o, S, kl = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], beta_t=inp["beta_t"], **kw)
+    bounds = [0] + list(cuts) + [L]
+    outs, state, kp, xh, yh = [], None, None, None, None
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        sg = _seg(inp, lo, hi)
+        oo, state, k_last = fo.falcon_recurrence(variant, sg["q"], sg["k"], sg["v"], beta_t=sg["beta_t"],
+                                                 k_prev=kp, S0=state, x_hist=xh, y_hist=yh, **kw)
+        xh, yh = fo.falcon_history(sg["k"], sg["v"], window, k_prev=kp, x_hist=xh, y_hist=yh)
+        kp = k_last
+        outs.append(oo)
+    np.testing.assert_allclose(np.concatenate(outs, axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(state, S, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(kp, kl)
+
+
+def test_window_history_is_the_latest_samples():
+    # the carried samples are (x_j, y_j) = (k_{j-1}, v_j) for the last window-1
+    # steps, read off a plain list of the samples of every call so far
+    rng = np.random.default_rng(12)
+    B, H, dk, dv, window = 1, 2, 3, 2, 4
+    kp0 = rng.standard_normal((B, H, dk))
+    ks = [rng.standard_normal((B, H, n, dk)) for n in (2, 1, 5)]
+    vs = [rng.standard_normal((B, H, n, dv)) for n in (2, 1, 5)]
+    xs, ys = [], []          # every sample of the sequence, in order
+    kp, xh, yh = kp0, None, None
+    for k, v in zip(ks, vs):
+        for t in range(k.shape[2]):
+            xs.append(kp if t == 0 else k[:, :, t - 1])
+            ys.append(v[:, :, t])
+        xh, yh = fo.falcon_history(k, v, window, k_prev=kp, x_hist=xh, y_hist=yh)
+        kp = k[:, :, -1]
+        n = window - 1
+        pad = max(0, n - len(xs))
+        want_x = [np.zeros((B, H, dk))] * pad + xs[len(xs) - (n - pad):]
+        want_y = [np.zeros((B, H, dv))] * pad + ys[len(ys) - (n - pad):]
+        np.testing.assert_array_equal(xh, np.stack(want_x, axis=2))
+        np.testing.assert_array_equal(yh, np.stack(want_y, axis=2))
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_3, fo.FALCON_3A])
+def test_zero_history_is_no_history(variant):
+    # zero samples add nothing to the normalizer or to the write
+    inp = _tiny(86, B=1, H=2, L=7, dk=4, dv=3, with_k_prev=True, with_S0=True)
+    kw = dict(beta=0.7, lam=0.05, eps=1e-6, window=3, k_prev=inp["k_prev"], S0=inp["S0"])
+    a = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], **kw)
+    b = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"],
+                             x_hist=np.zeros((1, 2, 2, 4)), y_hist=np.zeros((1, 2, 2, 3)), **kw)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_3, fo.FALCON_3A])
+@pytest.mark.parametrize("window", [2, 4])
+def test_window_decode_equals_recurrence(variant, window):
+    # prefill, then one decode step per token with the carried history, equals
+    # the recurrence over the whole sequence
+    L, L1 = 9, 3
+    inp = _tiny(87, B=2, H=2, L=L, dk=4, dv=3)
+    kw = dict(beta=0.6, lam=0.05, eps=1e-6)
+    o, S, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], window=window, **kw)
+    sg = _seg(inp, 0, L1)
+    o1, St, kp = fo.falcon_recurrence(variant, sg["q"], sg["k"], sg["v"], window=window, **kw)
+    xh, yh = fo.falcon_history(sg["k"], sg["v"], window)
+    got = [o1]
+    for t in range(L1, L):
+        ot, St, kp, xh, yh = fo.falcon_decode_step_window(
+            variant, window, St, kp, xh, yh, inp["q"][:, :, t], inp["k"][:, :, t],
+            inp["v"][:, :, t], **kw)
+        got.append(ot[:, :, None])
+    np.testing.assert_allclose(np.concatenate(got, axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(St, S, rtol=1e-13, atol=1e-14)
