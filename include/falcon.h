@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 1
+#define FALCON_ABI_VERSION 2
 
 /* The six update rules (explainer, section 核心方法 §2, variant table;
  * 163.com section 02: objective axis x granularity axis). */
@@ -102,8 +102,8 @@ const char* falcon_status_string(int status);
  *   q, k, v   inputs (device)
  *   k_prev    key carried from the previous call, or NULL (fresh sequence)
  *   S0        initial state, or NULL (zero).  S0 != NULL requires k_prev.
- *             window > 1 with S0 != NULL is unsupported (the window history
- *             is not carried).
+ *             window > 1 with S0 != NULL is unsupported here (the window
+ *             history is carried by falcon_fwd_recurrent_hist).
  *   o         output [batch, heads, L, dv] float32 (must not alias inputs)
  *   S_out     final state, or NULL; may equal S0 (in-place carry)
  *   stream    hipStream_t or NULL
@@ -149,6 +149,60 @@ int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kin
                        float lambda, float eps, int nseq, int heads, int dk, int dv,
                        int dtype, float* S, void* k_prev, const void* q, const void* k,
                        const void* v, float* o, void* stream);
+
+/*
+ * Carried window history (Falcon-3/3A).  The window of step t holds the B
+ * latest causal samples (explainer §2 variant table; 163.com section 02 (2)),
+ * so when a sequence is split into calls the first B-1 steps of a call reach
+ * samples of the previous one.  Besides S and k_prev the caller then carries
+ * those samples:
+ *   x_hist [batch, heads, B-1, dk], y_hist [batch, heads, B-1, dv], element
+ *   type `dtype`: the samples (x_j, y_j) = (k_{j-1}, v_j) before step 1, oldest
+ *   first.  A zero row stands for a missing sample (it adds nothing to the
+ *   normalizer or to the write), so a fresh sequence may start from zeros.
+ *
+ * falcon_fwd_recurrent_hist / falcon_fwd_chunk_hist - falcon_fwd_recurrent /
+ * falcon_fwd_chunk with
+ *   x_hist, y_hist     the incoming history, or both NULL (none).  Non-NULL
+ *                      requires window > 1 and k_prev.
+ *   x_hist_out, y_hist_out   the B-1 latest samples after the call (same
+ *                      shapes), or both NULL.  Requires window > 1.  Written
+ *                      by a kernel enqueued after the main one, so they may
+ *                      equal x_hist / y_hist exactly (in-place carry); any
+ *                      other overlap with an argument is an error.
+ * With window > 1, S0 != NULL requires the incoming history (the state of a
+ * resumed sequence is meaningless without its window samples).
+ */
+int falcon_fwd_recurrent_hist(int variant, int window, float beta, const void* beta_t,
+                              int beta_kind, float lambda, float eps, int batch, int heads,
+                              int seqlen, int dk, int dv, int dtype, const void* q,
+                              const void* k, const void* v, const void* k_prev,
+                              const float* S0, const void* x_hist, const void* y_hist,
+                              float* o, float* S_out, void* x_hist_out, void* y_hist_out,
+                              void* stream);
+int falcon_fwd_chunk_hist(int variant, int window, float beta, const void* beta_t,
+                          int beta_kind, float lambda, float eps, int batch, int heads,
+                          int seqlen, int dk, int dv, int dtype, const void* q, const void* k,
+                          const void* v, const void* k_prev, const float* S0,
+                          const void* x_hist, const void* y_hist, float* o, float* S_out,
+                          void* x_hist_out, void* y_hist_out, int chunk, void* stream);
+
+/*
+ * falcon_decode_step_hist - falcon_decode_step for every variant, with the
+ * window history of Falcon-3/3A:
+ *   window    B in 1..8; > 1 only for FALCON_3 / FALCON_3A
+ *   x_hist, y_hist   [nseq, heads, B-1, dk] / [nseq, heads, B-1, dv] (dtype),
+ *             oldest first; required when window > 1, NULL when window == 1.
+ * The window of the step is the history plus (x, y) = (k_prev, v).  S, k_prev
+ * and the history are updated in place: the oldest sample is dropped and
+ * (k_prev, v) appended, then k_prev <- k.  beta_t as in falcon_decode_step
+ * (per-channel gains only for Falcon-2/2A).  No argument may overlap another.
+ */
+int falcon_decode_step_hist(int variant, int window, float beta, const void* beta_t,
+                            int beta_kind, float lambda, float eps, int nseq, int heads, int dk,
+                            int dv, int dtype, float* S, void* k_prev, void* x_hist,
+                            void* y_hist, const void* q, const void* k, const void* v, float* o,
+                            void* stream);
 
 #ifdef __cplusplus
 }

@@ -295,6 +295,116 @@ def test_decode_small(variant, dk, dv):
 
 
 # ---------------------------------------------------------------------------
+# carried window history (resumed Falcon-3/3A sequences and their decode)
+
+@pytest.mark.parametrize("form", ["rec", "chunk"])
+@pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
+@pytest.mark.parametrize("dk,dv,window", [(64, 64, 2), (64, 64, 4), (128, 32, 4), (32, 32, 3),
+                                          (64, 16, 3)])
+def test_window_history_resume(form, variant, dk, dv, window):
+    """Resumed call: S0, k_prev and the window history in; o, S and the history out."""
+    if form == "rec" and dk == 128:
+        pytest.skip("covered by the chunk form")
+    inp = seq_inputs(2, 2, 77, dk, dv, seed=600 + 7 * variant + 3 * window + dk, dtype="bf16",
+                     with_k_prev=True, with_S0=True, beta_per_token=True, s_std=0.2,
+                     history=window - 1)
+    dt = torch.bfloat16
+    q, k, v, bt, kp, xh, yh = (to_dev(torch, inp[n], dt)
+                               for n in ("q", "k", "v", "beta_t", "k_prev", "x_hist", "y_hist"))
+    S0 = to_dev(torch, inp["S0"], torch.float32)
+    kw = dict(variant=variant, beta=None, lam=0.02, eps=1e-6, window=window, beta_t=bt,
+              k_prev=kp, S0=S0, x_hist=xh, y_hist=yh, return_state=True, return_history=True)
+    if form == "chunk":
+        o, S, xo, yo = fw.fwd_chunk(q, k, v, chunk=64, **kw)
+    else:
+        o, S, xo, yo = fw.fwd_recurrent(q, k, v, **kw)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = fo.falcon_recurrence(
+        variant, inp["q"], inp["k"], inp["v"], beta=None, lam=0.02, eps=1e-6, window=window,
+        beta_t=inp["beta_t"], k_prev=inp["k_prev"], S0=inp["S0"], x_hist=inp["x_hist"],
+        y_hist=inp["y_hist"])
+    xr, yr = fo.falcon_history(inp["k"], inp["v"], window, k_prev=inp["k_prev"],
+                               x_hist=inp["x_hist"], y_hist=inp["y_hist"])
+    err, zok = token_normwise_err(o.cpu().numpy(), o_ref)
+    serr = state_err(S.cpu().numpy(), S_ref)
+    tol = TOL_BF16 if form == "chunk" else TOL_FP32_MATH
+    print("%s v%d dk %d window %d: o err %.3e S err %.3e" % (form, variant, dk, window, err, serr))
+    assert zok and err <= tol and serr <= tol
+    np.testing.assert_array_equal(xo.float().cpu().numpy(), xr)
+    np.testing.assert_array_equal(yo.float().cpu().numpy(), yr)
+
+
+@pytest.mark.parametrize("form", ["rec", "chunk"])
+@pytest.mark.parametrize("window", [2, 4])
+def test_window_history_split_in_place(form, window):
+    """Pieces of 1, 2 and the rest tokens chained with an in-place history carry
+    equal one call over the whole sequence (the oracle's)."""
+    L, dk, dv = 70, 64, 32
+    inp = seq_inputs(1, 3, L, dk, dv, seed=640 + window, dtype="bf16", beta_per_token=True)
+    dt = torch.bfloat16
+    q, k, v, bt = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "beta_t"))
+    xh = torch.zeros((1, 3, window - 1, dk), device="cuda", dtype=dt)
+    yh = torch.zeros((1, 3, window - 1, dv), device="cuda", dtype=dt)
+    S = torch.zeros((1, 3, dv, dk), device="cuda", dtype=torch.float32)
+    kp = None
+    outs = []
+    for lo, hi in ((0, 1), (1, 3), (3, L)):
+        sl = lambda t: t[:, :, lo:hi].contiguous()
+        kw = dict(variant=fw.FALCON_3, beta=None, lam=0.02, eps=1e-6, window=window,
+                  beta_t=sl(bt), k_prev=kp, S0=S if kp is not None else None,
+                  x_hist=xh if kp is not None else None, y_hist=yh if kp is not None else None,
+                  S_out=S, return_state=True, x_hist_out=xh, y_hist_out=yh, return_history=True)
+        fn = fw.fwd_chunk if form == "chunk" else fw.fwd_recurrent
+        o, _, _, _ = fn(sl(q), sl(k), sl(v), **kw)
+        kp = k[:, :, hi - 1].contiguous()
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = fo.falcon_recurrence(fw.FALCON_3, inp["q"], inp["k"], inp["v"], beta=None,
+                                           lam=0.02, eps=1e-6, window=window,
+                                           beta_t=inp["beta_t"])
+    err, zok = token_normwise_err(torch.cat(outs, dim=2).cpu().numpy(), o_ref)
+    serr = state_err(S.cpu().numpy(), S_ref)
+    tol = TOL_BF16 if form == "chunk" else TOL_FP32_MATH
+    print("%s window %d split: o err %.3e S err %.3e" % (form, window, err, serr))
+    assert zok and err <= tol and serr <= tol
+    xr, yr = fo.falcon_history(inp["k"], inp["v"], window)
+    np.testing.assert_array_equal(xh.float().cpu().numpy(), xr)
+    np.testing.assert_array_equal(yh.float().cpu().numpy(), yr)
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
+@pytest.mark.parametrize("dk,dv,window", [(64, 64, 4), (16, 128, 2), (128, 32, 3), (32, 16, 8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_window(variant, dk, dv, window, dtype):
+    """Decode steps with the window history updated in place, against the oracle's
+    windowed decode step by step."""
+    steps, pool = 12, 4
+    inp = decode_inputs(3, 2, dk, dv, seed=660 + variant + window + dk, steps=pool, s_std=0.2,
+                        dtype=dtype, history=window - 1)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    S = to_dev(torch, inp["S"], torch.float32)
+    kp, xh, yh = (to_dev(torch, inp[n], dt) for n in ("k_prev", "x_hist", "y_hist"))
+    qs, ks, vs = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
+    S_r, kp_r, xh_r, yh_r = (inp[n].astype(np.float64) for n in ("S", "k_prev", "x_hist", "y_hist"))
+    for s in range(steps):
+        p = s % pool
+        o = fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=variant, beta=0.6, lam=0.02,
+                           eps=1e-6, window=window, x_hist=xh, y_hist=yh)
+        o_r, S_r, kp_r, xh_r, yh_r = fo.falcon_decode_step_window(
+            variant, window, S_r, kp_r, xh_r, yh_r, inp["q"][p], inp["k"][p], inp["v"][p],
+            beta=0.6, lam=0.02, eps=1e-6)
+        torch.cuda.synchronize()
+        err, zok = token_normwise_err(o.cpu().numpy(), o_r)
+        assert zok and err <= TOL_FP32_MATH, (s, err)
+    serr = state_err(S.cpu().numpy(), S_r)
+    print("decode window %d v%d dk %d dv %d %s: S err %.3e" % (window, variant, dk, dv, dtype, serr))
+    assert serr <= TOL_FP32_MATH
+    np.testing.assert_array_equal(kp.float().cpu().numpy(), kp_r)
+    np.testing.assert_array_equal(xh.float().cpu().numpy(), xh_r)
+    np.testing.assert_array_equal(yh.float().cpu().numpy(), yh_r)
+
+
+# ---------------------------------------------------------------------------
 # error paths through the binding
 
 def test_binding_rejects_unsupported():

@@ -38,8 +38,9 @@ bool per_channel_variant(int variant) { return variant == FALCON_2 || variant ==
 
 bool window_variant(int variant) { return variant == FALCON_3 || variant == FALCON_3A; }
 
-// Validation shared by the recurrent and the chunk form.
-int check_seq(const falcon::SeqArgs& a) {
+// Validation shared by the recurrent and the chunk form.  hist_api: called from
+// an entry point that can carry the window history.
+int check_seq(const falcon::SeqArgs& a, bool hist_api) {
   if (a.variant < FALCON_1 || a.variant > FALCON_3A) return FALCON_ERR_INVALID_ARG;
   if (a.window < 1) return FALCON_ERR_INVALID_ARG;
   if (a.window != 1 && !window_variant(a.variant)) return FALCON_ERR_INVALID_ARG;
@@ -85,11 +86,78 @@ int check_seq(const falcon::SeqArgs& a) {
     if (overlap(so, ins[i])) return FALCON_ERR_INVALID_ARG;
   if (overlap(so, ins[6])) return FALCON_ERR_INVALID_ARG;
   if (!supported_dim(a.dk) || !supported_dim(a.dv)) return FALCON_ERR_UNSUPPORTED;
-  if (a.window > 1 && a.S0) return FALCON_ERR_UNSUPPORTED;
+  if (!hist_api && a.window > 1 && a.S0) return FALCON_ERR_UNSUPPORTED;
+  return FALCON_OK;
+}
+
+// Validation of the window history arguments (after check_seq).
+int check_history(const falcon::SeqArgs& a, const void* xo, const void* yo) {
+  const bool hin = a.x_hist != nullptr, hout = xo != nullptr;
+  if ((a.x_hist == nullptr) != (a.y_hist == nullptr)) return FALCON_ERR_INVALID_ARG;
+  if ((xo == nullptr) != (yo == nullptr)) return FALCON_ERR_INVALID_ARG;
+  if ((hin || hout) && a.window < 2) return FALCON_ERR_INVALID_ARG;
+  if (hin && !a.k_prev) return FALCON_ERR_INVALID_ARG;
+  if (a.window > 1 && a.S0 && !hin) return FALCON_ERR_INVALID_ARG;
+  if (!hin && !hout) return FALCON_OK;
+  const void* ptrs[] = {a.x_hist, a.y_hist, xo, yo};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
+  const size_t es = a.dtype == FALCON_BF16 ? 2 : 4;
+  const size_t BH = (size_t)a.batch * a.heads, L = (size_t)a.seqlen, NH = (size_t)a.window - 1;
+  const size_t xb = BH * NH * a.dk * es, yb = BH * NH * a.dv * es;
+  Range rxh{a.x_hist, xb}, ryh{a.y_hist, yb}, rxo{xo, xb}, ryo{yo, yb};
+  Range others[] = {{a.q, BH * L * a.dk * es},
+                    {a.k, BH * L * a.dk * es},
+                    {a.v, BH * L * a.dv * es},
+                    {a.k_prev, BH * a.dk * es},
+                    {a.S0, BH * a.dv * a.dk * 4},
+                    {a.o, BH * L * a.dv * 4},
+                    {a.S_out, BH * a.dv * a.dk * 4},
+                    {a.beta_t, BH * L * (a.beta_kind == FALCON_BETA_CHANNEL ? a.dv : 1) * es}};
+  // the incoming history is read by the main kernel: no output may overlap it
+  // (the history outputs are written afterwards)
+  for (int i = 5; i < 7; ++i)
+    if (overlap(rxh, others[i]) || overlap(ryh, others[i])) return FALCON_ERR_INVALID_ARG;
+  if (overlap(rxh, ryh)) return FALCON_ERR_INVALID_ARG;
+  // outputs: equal to their own incoming history or disjoint from it, disjoint
+  // from everything else
+  for (const Range& r : others)
+    if (overlap(rxo, r) || overlap(ryo, r)) return FALCON_ERR_INVALID_ARG;
+  if (overlap(rxo, ryo) || overlap(rxo, ryh) || overlap(ryo, rxh)) return FALCON_ERR_INVALID_ARG;
+  if (xo != a.x_hist && overlap(rxo, rxh)) return FALCON_ERR_INVALID_ARG;
+  if (yo != a.y_hist && overlap(ryo, ryh)) return FALCON_ERR_INVALID_ARG;
   return FALCON_OK;
 }
 
 int finish_launch(hipError_t e) { return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP; }
+
+// The history outputs are written after the main kernel, on the same stream.
+int launch_with_history(bool chunk_form, const falcon::SeqArgs& a, void* xo, void* yo,
+                        hipStream_t stream) {
+  hipError_t e = chunk_form ? falcon::launch_chunk(a, stream) : falcon::launch_recurrent(a, stream);
+  if (e == hipSuccess && xo) e = falcon::launch_history_out(a, xo, yo, stream);
+  return finish_launch(e);
+}
+
+int fwd_recurrent(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipStream_t stream) {
+  int st = check_seq(a, hist_api);
+  if (st == FALCON_OK && hist_api) st = check_history(a, xo, yo);
+  if (st != FALCON_OK) return st;
+  if (a.window > 8) return FALCON_ERR_UNSUPPORTED;
+  return launch_with_history(false, a, xo, yo, stream);
+}
+
+int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipStream_t stream) {
+  int st = check_seq(a, hist_api);
+  if (st == FALCON_OK && hist_api) st = check_history(a, xo, yo);
+  if (st != FALCON_OK) return st;
+  if (a.chunk < 1) return FALCON_ERR_INVALID_ARG;
+  if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return FALCON_ERR_UNSUPPORTED;
+  if (a.window > a.chunk) return FALCON_ERR_INVALID_ARG;
+  if (a.window > 4) return FALCON_ERR_UNSUPPORTED;
+  if (a.dtype != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
+  return launch_with_history(true, a, xo, yo, stream);
+}
 
 }  // namespace
 
@@ -114,10 +182,21 @@ FALCON_EXPORT int falcon_fwd_recurrent(int variant, int window, float beta, cons
   falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
                     0};
-  int st = check_seq(a);
-  if (st != FALCON_OK) return st;
-  if (window > 8) return FALCON_ERR_UNSUPPORTED;
-  return finish_launch(falcon::launch_recurrent(a, (hipStream_t)stream));
+  return fwd_recurrent(a, false, nullptr, nullptr, (hipStream_t)stream);
+}
+
+FALCON_EXPORT int falcon_fwd_recurrent_hist(int variant, int window, float beta,
+                                            const void* beta_t, int beta_kind, float lambda,
+                                            float eps, int batch, int heads, int seqlen, int dk,
+                                            int dv, int dtype, const void* q, const void* k,
+                                            const void* v, const void* k_prev, const float* S0,
+                                            const void* x_hist, const void* y_hist, float* o,
+                                            float* S_out, void* x_hist_out, void* y_hist_out,
+                                            void* stream) {
+  falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
+                    eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
+                    0, x_hist, y_hist};
+  return fwd_recurrent(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
 }
 
 FALCON_EXPORT int falcon_fwd_chunk(int variant, int window, float beta, const void* beta_t,
@@ -129,21 +208,33 @@ FALCON_EXPORT int falcon_fwd_chunk(int variant, int window, float beta, const vo
   falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
                     chunk};
-  int st = check_seq(a);
-  if (st != FALCON_OK) return st;
-  if (chunk < 1) return FALCON_ERR_INVALID_ARG;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return FALCON_ERR_UNSUPPORTED;
-  if (window > chunk) return FALCON_ERR_INVALID_ARG;
-  if (window > 4) return FALCON_ERR_UNSUPPORTED;
-  if (dtype != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
-  return finish_launch(falcon::launch_chunk(a, (hipStream_t)stream));
+  return fwd_chunk(a, false, nullptr, nullptr, (hipStream_t)stream);
 }
 
-FALCON_EXPORT int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kind,
-                                     float lambda, float eps, int nseq, int heads, int dk,
-                                     int dv, int dtype, float* S, void* k_prev, const void* q,
-                                     const void* k, const void* v, float* o, void* stream) {
+FALCON_EXPORT int falcon_fwd_chunk_hist(int variant, int window, float beta, const void* beta_t,
+                                        int beta_kind, float lambda, float eps, int batch,
+                                        int heads, int seqlen, int dk, int dv, int dtype,
+                                        const void* q, const void* k, const void* v,
+                                        const void* k_prev, const float* S0, const void* x_hist,
+                                        const void* y_hist, float* o, float* S_out,
+                                        void* x_hist_out, void* y_hist_out, int chunk,
+                                        void* stream) {
+  falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
+                    eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
+                    chunk, x_hist, y_hist};
+  return fwd_chunk(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
+}
+
+namespace {
+
+int decode_step(int variant, int window, float beta, const void* beta_t, int beta_kind,
+                float lambda, float eps, int nseq, int heads, int dk, int dv, int dtype, float* S,
+                void* k_prev, void* x_hist, void* y_hist, const void* q, const void* k,
+                const void* v, float* o, bool hist_api, void* stream) {
   if (variant < FALCON_1 || variant > FALCON_3A) return FALCON_ERR_INVALID_ARG;
+  if (window < 1 || (window != 1 && !window_variant(variant))) return FALCON_ERR_INVALID_ARG;
+  if ((x_hist == nullptr) != (y_hist == nullptr)) return FALCON_ERR_INVALID_ARG;
+  if ((x_hist != nullptr) != (window > 1)) return FALCON_ERR_INVALID_ARG;
   if (beta_kind < FALCON_BETA_SCALAR || beta_kind > FALCON_BETA_CHANNEL)
     return FALCON_ERR_INVALID_ARG;
   if (beta_kind == FALCON_BETA_SCALAR) {
@@ -157,22 +248,44 @@ FALCON_EXPORT int falcon_decode_step(int variant, float beta, const void* beta_t
   if (nseq < 1 || heads < 1 || dk < 1 || dv < 1) return FALCON_ERR_INVALID_ARG;
   if (dtype != FALCON_BF16 && dtype != FALCON_F32) return FALCON_ERR_INVALID_ARG;
   if (!S || !k_prev || !q || !k || !v || !o) return FALCON_ERR_INVALID_ARG;
-  const void* ptrs[] = {S, k_prev, q, k, v, o, beta_t};
+  const void* ptrs[] = {S, k_prev, q, k, v, o, beta_t, x_hist, y_hist};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
   const size_t es = dtype == FALCON_BF16 ? 2 : 4;
-  const size_t NH = (size_t)nseq * heads;
+  const size_t NH = (size_t)nseq * heads, W1 = (size_t)window - 1;
   if ((double)NH * dk * dv > 1099511627776.0) return FALCON_ERR_INVALID_ARG;
   Range rS{S, NH * dv * dk * 4}, rkp{k_prev, NH * dk * es}, rq{q, NH * dk * es},
       rk{k, NH * dk * es}, rv{v, NH * dv * es}, ro{o, NH * dv * 4},
-      rb{beta_t, NH * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * es};
-  Range all[] = {rS, rkp, rq, rk, rv, ro, rb};
-  for (int i = 0; i < 7; ++i)
-    for (int j = i + 1; j < 7; ++j)
+      rb{beta_t, NH * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * es},
+      rxh{x_hist, NH * W1 * dk * es}, ryh{y_hist, NH * W1 * dv * es};
+  Range all[] = {rS, rkp, rq, rk, rv, ro, rb, rxh, ryh};
+  for (int i = 0; i < 9; ++i)
+    for (int j = i + 1; j < 9; ++j)
       if (overlap(all[i], all[j])) return FALCON_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return FALCON_ERR_UNSUPPORTED;
-  if (window_variant(variant)) return FALCON_ERR_UNSUPPORTED;
-  falcon::DecodeArgs a{is_regression(variant), beta, beta_t, beta_kind, lambda, eps, nseq,
-                       heads, dk, dv, dtype, S, k_prev, q, k, v, o};
+  if (!hist_api && window_variant(variant)) return FALCON_ERR_UNSUPPORTED;
+  if (window > 8) return FALCON_ERR_UNSUPPORTED;
+  falcon::DecodeArgs a{is_regression(variant), window, x_hist, y_hist, beta, beta_t, beta_kind,
+                       lambda, eps, nseq, heads, dk, dv, dtype, S, k_prev, q, k, v, o};
   return finish_launch(falcon::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+FALCON_EXPORT int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kind,
+                                     float lambda, float eps, int nseq, int heads, int dk,
+                                     int dv, int dtype, float* S, void* k_prev, const void* q,
+                                     const void* k, const void* v, float* o, void* stream) {
+  return decode_step(variant, 1, beta, beta_t, beta_kind, lambda, eps, nseq, heads, dk, dv,
+                     dtype, S, k_prev, nullptr, nullptr, q, k, v, o, false, stream);
+}
+
+FALCON_EXPORT int falcon_decode_step_hist(int variant, int window, float beta,
+                                          const void* beta_t, int beta_kind, float lambda,
+                                          float eps, int nseq, int heads, int dk, int dv,
+                                          int dtype, float* S, void* k_prev, void* x_hist,
+                                          void* y_hist, const void* q, const void* k,
+                                          const void* v, float* o, void* stream) {
+  return decode_step(variant, window, beta, beta_t, beta_kind, lambda, eps, nseq, heads, dk, dv,
+                     dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }

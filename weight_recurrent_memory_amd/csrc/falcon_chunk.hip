@@ -133,6 +133,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
   const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
   const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
+  const uint16_t* __restrict__ xhg = static_cast<const uint16_t*>(a.x_hist);
+  const uint16_t* __restrict__ yhg = static_cast<const uint16_t*>(a.y_hist);
   const uint16_t* __restrict__ bg = static_cast<const uint16_t*>(a.beta_t);
 
   // Block -> (chain, row-block group).  Workgroups are dealt to the 8 XCDs round
@@ -180,6 +182,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
       if (idx < NXP * VPR && jj < NX && g < t0 + c) {
         if (g >= 1) val = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
         else if (g == 0 && kpg) val = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
+        else if (g < 0 && xhg)   // carried window history, slot B-1+g
+          val = *reinterpret_cast<const uint4*>(xhg + ((long)chain * (B - 1) + (B - 1) + g) * DK + kv * 8);
       }
       pk[v] = val;
     }
@@ -197,8 +201,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
       const int jj = idx / (RW / 8), h = idx % (RW / 8);
       const long g = t0 - (B - 1) + jj;
       uint4 val = {0u, 0u, 0u, 0u};
-      if (idx < NXP * (RW / 8) && jj < NX && g >= 0 && g < t0 + c && i0 + h * 8 < dv)
-        val = *reinterpret_cast<const uint4*>(vg + v_base + g * dv + i0 + h * 8);
+      if (idx < NXP * (RW / 8) && jj < NX && g < t0 + c && i0 + h * 8 < dv) {
+        if (g >= 0) val = *reinterpret_cast<const uint4*>(vg + v_base + g * dv + i0 + h * 8);
+        else if (yhg) val = *reinterpret_cast<const uint4*>(yhg + ((long)chain * (B - 1) + (B - 1) + g) * dv + i0 + h * 8);
+      }
       py[v] = val;
     }
     constexpr int NBT = (PERROW ? RW : 1) * CS;

@@ -198,6 +198,32 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   for (int idx = tid; idx < DK * (CS + 8); idx += NT) (&sm.XT[3][0][0])[idx] = 0;
   for (int idx = tid; idx < RW * (CS + 8); idx += NT) (&sm.YT[3][0][0])[idx] = 0;
   if (tid < CS) sm.knorm[3][tid] = 0.0f;
+  if (a.x_hist) {
+    // a resumed sequence: its last B-1 rows are the carried window samples
+    // (oldest first), which the first steps' windows reach
+    const uint16_t* __restrict__ xhg = static_cast<const uint16_t*>(a.x_hist);
+    const uint16_t* __restrict__ yhg = static_cast<const uint16_t*>(a.y_hist);
+    constexpr int NH = B - 1;
+    __syncthreads();
+    for (int idx = tid; idx < NH * DK; idx += NT) {
+      const int h = idx / DK, kk = idx % DK, t = CS - NH + h;
+      const uint16_t xv = xhg[((long)chain * NH + h) * DK + kk];
+      sm.X[3][t][fpos(kk)] = xv;
+      sm.XT[3][kk][t] = xv;
+    }
+    for (int idx = tid; idx < NH * RW; idx += NT) {
+      const int h = idx / RW, i = idx % RW, t = CS - NH + h;
+      sm.YT[3][i][t] = (i0 + i < dv) ? yhg[((long)chain * NH + h) * dv + i0 + i] : (uint16_t)0;
+    }
+    if (tid < NH) {
+      float n = 0.0f;
+      for (int kk = 0; kk < DK; ++kk) {
+        const float xv = bf16_to_f32(xhg[((long)chain * NH + tid) * DK + kk]);
+        n += xv * xv;
+      }
+      sm.knorm[3][CS - NH + tid] = n;
+    }
+  }
 
   // ---------------- global loads (buffer resources, range checked) ----------------
   // wave 6 moves the keys of a sub-chunk, wave 7 its queries, values and gains;

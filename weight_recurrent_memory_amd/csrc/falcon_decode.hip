@@ -94,10 +94,130 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// Sliding-window step (Falcon-3/3A): the window is the carried history of
+// B-1 samples (oldest first) plus (x, y) = (k_prev, v):
+//   n = sum_w ||x_w||^2, r_w = S x_w, e_w = y_w - r_w (or y_w), r2 = S q
+//   S' = a S + eta sum_w e_w x_w^T,  o = a r2 + eta sum_w e_w (x_w . q)
+// then the history drops its oldest sample and appends (x, y), and k_prev <- k.
+constexpr int kMaxDecWindow = 8;
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kDecThreads) void decode_window_kernel(DecodeArgs a) {
+  constexpr int TPR = DK / 4;
+  constexpr int RPP = kDecThreads / TPR;
+  constexpr int PASSES = (DV + RPP - 1) / RPP;
+  constexpr int MW = kMaxDecWindow;
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* __restrict__ bt = static_cast<const T*>(a.beta_t);
+  T* kp = static_cast<T*>(a.k_prev);
+  T* xh = static_cast<T*>(a.x_hist);
+  T* yh = static_cast<T*>(a.y_hist);
+
+  const long head = blockIdx.x;
+  const int rloc = threadIdx.x / TPR;
+  const int cg = threadIdx.x % TPR;
+  const int c0 = cg * 4;
+  const int B = a.window, NH = B - 1;
+  float* __restrict__ Sh = a.S + head * (long)DV * DK;
+
+  floatx4 s[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    if (row < DV) s[p] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sh + (long)row * DK + c0));
+    else s[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  float x[MW][4], qq[4];
+#pragma unroll
+  for (int w = 0; w < MW; ++w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float xv = 0.0f;
+      if (w < NH) xv = ld_in(xh, (head * NH + w) * DK + c0 + e);
+      else if (w == NH) xv = ld_in(kp, head * DK + c0 + e);
+      x[w][e] = xv;
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qq[e] = ld_in(q, head * DK + c0 + e);
+  float yv[PASSES][MW], bv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    const int rc = row < DV ? row : 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) {
+      float y = 0.0f;
+      if (w < NH) y = ld_in(yh, (head * NH + w) * DV + rc);
+      else if (w == NH) y = ld_in(v, head * DV + rc);
+      yv[p][w] = y;
+    }
+    bv[p] = a.beta_kind == 0 ? a.beta : ld_in(bt, head);
+  }
+  // every lane has read k_prev and the history; only now may they change
+  __syncthreads();
+  if (rloc == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long c = c0 + e;
+      for (int w = 0; w + 1 < NH; ++w) xh[(head * NH + w) * DK + c] = xh[(head * NH + w + 1) * DK + c];
+      xh[(head * NH + NH - 1) * DK + c] = kp[head * DK + c];
+      kp[head * DK + c] = k[head * DK + c];
+    }
+  }
+  float n = 0.0f, xq[MW];
+#pragma unroll
+  for (int w = 0; w < MW; ++w) {
+    n += x[w][0] * x[w][0] + x[w][1] * x[w][1] + x[w][2] * x[w][2] + x[w][3] * x[w][3];
+    xq[w] = 0.0f;
+    if (w < B) xq[w] = group_sum<TPR>(x[w][0] * qq[0] + x[w][1] * qq[1] + x[w][2] * qq[2] + x[w][3] * qq[3]);
+  }
+  n = group_sum<TPR>(n);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = p * RPP + rloc;
+    float r2 = s[p].x * qq[0] + s[p].y * qq[1] + s[p].z * qq[2] + s[p].w * qq[3];
+    r2 = group_sum<TPR>(r2);
+    const float eta = bv[p] / (a.eps + n);
+    const float dec = 1.0f - eta * a.lambda;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f}, ow = 0.0f;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) {
+      if (w < B) {
+        float e = yv[p][w];
+        if (a.regression) {
+          float r1 = s[p].x * x[w][0] + s[p].y * x[w][1] + s[p].z * x[w][2] + s[p].w * x[w][3];
+          e -= group_sum<TPR>(r1);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += e * x[w][c];
+        ow += e * xq[w];
+      }
+    }
+    floatx4 sn;
+    sn.x = dec * s[p].x + eta * acc[0];
+    sn.y = dec * s[p].y + eta * acc[1];
+    sn.z = dec * s[p].z + eta * acc[2];
+    sn.w = dec * s[p].w + eta * acc[3];
+    if (row < DV) {
+      __builtin_nontemporal_store(sn, reinterpret_cast<floatx4*>(Sh + (long)row * DK + c0));
+      if (cg == 0) {
+        a.o[head * DV + row] = dec * r2 + eta * ow;
+        for (int w = 0; w + 1 < NH; ++w) yh[(head * NH + w) * DV + row] = yh[(head * NH + w + 1) * DV + row];
+        yh[(head * NH + NH - 1) * DV + row] = v[head * DV + row];
+      }
+    }
+  }
+}
+
 template <typename T, int DK, int DV>
 hipError_t launch3(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3((unsigned)((long)a.nseq * a.heads)),
-                     dim3(kDecThreads), 0, stream, a);
+  const dim3 grid((unsigned)((long)a.nseq * a.heads));
+  if (a.window > 1)
+    hipLaunchKernelGGL((decode_window_kernel<T, DK, DV>), grid, dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), grid, dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,10 +24,18 @@ struct SeqArgs {
   float* o;
   float* S_out;        // may be null
   int chunk;           // chunk form only
+  // window history of a resumed Falcon-3/3A sequence: the window-1 samples
+  // (x_j, y_j) before step 1, oldest first, [chain][window-1][dk or dv]; null:
+  // none (zero samples)
+  const void* x_hist = nullptr;
+  const void* y_hist = nullptr;
 };
 
 struct DecodeArgs {
   int regression;
+  int window;        // 1, or B > 1 with x_hist / y_hist
+  void* x_hist;      // [nseq*heads][window-1][dk], oldest first, updated in place
+  void* y_hist;      // [nseq*heads][window-1][dv]
   float beta;
   const void* beta_t;
   int beta_kind;
@@ -55,5 +63,8 @@ hipError_t launch_chunk_wy(const SeqArgs& a, hipStream_t stream);
 bool chunk_wyb_supported(const SeqArgs& a);
 hipError_t launch_chunk_wyb(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// the window-1 latest samples after a sequence call, written to x_out / y_out
+// (which may equal a.x_hist / a.y_hist); enqueue after the call's kernel
+hipError_t launch_history_out(const SeqArgs& a, void* x_out, void* y_out, hipStream_t stream);
 
 }  // namespace falcon

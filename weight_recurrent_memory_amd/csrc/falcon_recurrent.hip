@@ -28,6 +28,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
   const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ kp = static_cast<const T*>(a.k_prev);
   const T* __restrict__ bt = static_cast<const T*>(a.beta_t);
+  const T* __restrict__ xh = static_cast<const T*>(a.x_hist);
+  const T* __restrict__ yh = static_cast<const T*>(a.y_hist);
 
   const int chain = blockIdx.x;               // batch * heads + head
   const int rloc = threadIdx.x / TPR;
@@ -47,7 +49,8 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
 
   const int B = a.window;
   for (long t = 0; t < L; ++t) {
-    // window samples j = t - w, w = 0..B-1: x_g = k[g-1] (g >= 1), k_prev or 0 (g == 0)
+    // window samples g = t - w, w = 0..B-1: x_g = k[g-1] (g >= 1), k_prev or 0
+    // (g == 0); g < 0 is history slot B-1+g when one is carried, else zero
     float xw[kMaxWindow][CPT];
     float yw[kMaxWindow];
     float n = 0.0f;
@@ -60,11 +63,15 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
         float xv = 0.0f;
         if (w < B && g >= 1) xv = ld_in(k, qk_base + (g - 1) * DK + c0 + e);
         else if (w < B && g == 0 && kp) xv = ld_in(kp, (long)chain * DK + c0 + e);
+        else if (w < B && g < 0 && xh) xv = ld_in(xh, ((long)chain * (B - 1) + (B - 1) + g) * DK + c0 + e);
         xw[w][e] = xv;
         part += xv * xv;
       }
       n += part;
-      yw[w] = (w < B && g >= 0) ? ld_in(v, v_base + g * a.dv + rowc) : 0.0f;
+      float yv = 0.0f;
+      if (w < B && g >= 0) yv = ld_in(v, v_base + g * a.dv + rowc);
+      else if (w < B && yh) yv = ld_in(yh, ((long)chain * (B - 1) + (B - 1) + g) * a.dv + rowc);
+      yw[w] = yv;
     }
     n = group_sum<TPR>(n);
     float beta = a.beta;
@@ -131,7 +138,55 @@ hipError_t launch_dk(const SeqArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// The window-1 latest samples after a call, oldest first: slot h holds sample
+// s = L - (B-1) + h (0-based steps; sample s pairs x_s with y_s = v_s, x_s =
+// k_{s-1}, x_0 = k_prev or 0); s < 0 comes from the incoming history slot
+// B-1+s (zero without one).  One thread per column walks the slots in
+// ascending order: in-place use (out == incoming history) reads slot L+h > h
+// before anything at or above slot h has been written.
+template <typename T>
+__global__ __launch_bounds__(256) void history_out_kernel(SeqArgs a, T* xo, T* yo) {
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* __restrict__ kp = static_cast<const T*>(a.k_prev);
+  const T* xh = static_cast<const T*>(a.x_hist);
+  const T* yh = static_cast<const T*>(a.y_hist);
+  const long chain = blockIdx.x;
+  const int NH = a.window - 1;
+  const long L = a.seqlen;
+  for (int c = threadIdx.x; c < a.dk + a.dv; c += blockDim.x) {
+    const bool isx = c < a.dk;
+    const int col = isx ? c : c - a.dk;
+    const int d = isx ? a.dk : a.dv;
+    T* out = isx ? xo : yo;
+    const T* hin = isx ? xh : yh;
+    for (int h = 0; h < NH; ++h) {
+      const long s = L - NH + h;
+      T val = T(0);
+      if (s >= 0) {
+        if (!isx) val = v[(chain * L + s) * a.dv + col];
+        else if (s >= 1) val = k[(chain * L + s - 1) * a.dk + col];
+        else if (kp) val = kp[chain * a.dk + col];
+      } else if (hin) {
+        val = hin[(chain * NH + NH + s) * d + col];
+      }
+      out[(chain * NH + h) * d + col] = val;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_history_out(const SeqArgs& a, void* x_out, void* y_out, hipStream_t stream) {
+  const dim3 grid((unsigned)((long)a.batch * a.heads));
+  if (a.dtype == 0)
+    hipLaunchKernelGGL(history_out_kernel<uint16_t>, grid, dim3(256), 0, stream, a,
+                       static_cast<uint16_t*>(x_out), static_cast<uint16_t*>(y_out));
+  else
+    hipLaunchKernelGGL(history_out_kernel<float>, grid, dim3(256), 0, stream, a,
+                       static_cast<float*>(x_out), static_cast<float*>(y_out));
+  return hipGetLastError();
+}
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();

@@ -51,13 +51,16 @@ def _l2n(a: np.ndarray) -> np.ndarray:
 
 
 def seq_inputs(batch, heads, L, dk, dv, *, seed, dtype="bf16", beta_per_token=False,
-               beta_per_channel=False, with_k_prev=False, with_S0=False, s_std=0.02):
+               beta_per_channel=False, with_k_prev=False, with_S0=False, s_std=0.02,
+               history=0):
     """q, k [B,H,L,dk], v [B,H,L,dv] ~ N(0,1) with q, k L2-normalized per token.
 
     Returns a dict of float32 arrays holding exactly the values of the chosen
     dtype (bf16-rounded when dtype == "bf16"); optional beta_t
     (sigmoid(N(0,1)) per token, or per token and value channel), k_prev
-    (one normalized key per (batch, head)) and S0 (N(0, s_std^2)).
+    (one normalized key per (batch, head)), S0 (N(0, s_std^2)) and, with
+    history = n > 0, a carried window history x_hist [B,H,n,dk] (normalized
+    keys) and y_hist [B,H,n,dv] (N(0,1)), drawn after everything else.
     """
     rng = np.random.default_rng(seed)
     q = _l2n(rng.standard_normal((batch, heads, L, dk), dtype=np.float32))
@@ -75,17 +78,21 @@ def seq_inputs(batch, heads, L, dk, dv, *, seed, dtype="bf16", beta_per_token=Fa
     if with_S0:
         out["S0"] = (s_std * rng.standard_normal((batch, heads, dv, dk),
                                                  dtype=np.float32)).astype(np.float32)
+    if history > 0:
+        out["x_hist"] = _l2n(rng.standard_normal((batch, heads, history, dk), dtype=np.float32))
+        out["y_hist"] = rng.standard_normal((batch, heads, history, dv), dtype=np.float32)
     if dtype == "bf16":
-        for name in ("q", "k", "v", "beta_t", "k_prev"):
+        for name in ("q", "k", "v", "beta_t", "k_prev", "x_hist", "y_hist"):
             if name in out:
                 out[name] = to_bf16_values(out[name])
     return out
 
 
 def decode_inputs(nseq, heads, dk, dv, *, seed, steps=1, s_std=0.02, dtype="bf16",
-                  beta_per_channel=False):
+                  beta_per_channel=False, history=0):
     """Decode workload: S [N,H,dv,dk] ~ N(0, s_std^2) fp32, k_prev [N,H,dk], and a
-    pool of ``steps`` per-step (q, k, v) with q, k normalized; bf16-rounded."""
+    pool of ``steps`` per-step (q, k, v) with q, k normalized; bf16-rounded.  With
+    history = n > 0 also a window history x_hist [N,H,n,dk], y_hist [N,H,n,dv]."""
     rng = np.random.default_rng(seed)
     S = (s_std * rng.standard_normal((nseq, heads, dv, dk), dtype=np.float32)).astype(np.float32)
     k_prev = _l2n(rng.standard_normal((nseq, heads, dk), dtype=np.float32))
@@ -96,8 +103,11 @@ def decode_inputs(nseq, heads, dk, dv, *, seed, steps=1, s_std=0.02, dtype="bf16
     if beta_per_channel:
         z = rng.standard_normal((steps, nseq, heads, dv), dtype=np.float32)
         out["beta_t"] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    if history > 0:
+        out["x_hist"] = _l2n(rng.standard_normal((nseq, heads, history, dk), dtype=np.float32))
+        out["y_hist"] = rng.standard_normal((nseq, heads, history, dv), dtype=np.float32)
     if dtype == "bf16":
-        for name in ("q", "k", "v", "k_prev", "beta_t"):
+        for name in ("q", "k", "v", "k_prev", "beta_t", "x_hist", "y_hist"):
             if name in out:
                 out[name] = to_bf16_values(out[name])
     return out
