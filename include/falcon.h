@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 2
+#define FALCON_ABI_VERSION 3
 
 /* The six update rules (explainer, section 核心方法 §2, variant table;
  * 163.com section 02: objective axis x granularity axis). */
@@ -151,20 +151,31 @@ int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kin
                        const void* v, float* o, void* stream);
 
 /*
+ * Extended entry points: the same computations with a carried window history
+ * and a choice of sample pairing.
+ *
+ * flags: 0, or FALCON_SAME_STEP - pair each value with the same step's key,
+ *   x_t = k_t (explainer §1, the alternative alignment it warns against; the
+ *   163.com article, section 01, explains why the default pairs v_t with
+ *   k_{t-1}).  The carried key is then meaningless: k_prev must be NULL, and
+ *   S0 needs no k_prev.  Other bits are invalid.
+ *
  * Carried window history (Falcon-3/3A).  The window of step t holds the B
  * latest causal samples (explainer §2 variant table; 163.com section 02 (2)),
  * so when a sequence is split into calls the first B-1 steps of a call reach
  * samples of the previous one.  Besides S and k_prev the caller then carries
  * those samples:
  *   x_hist [batch, heads, B-1, dk], y_hist [batch, heads, B-1, dv], element
- *   type `dtype`: the samples (x_j, y_j) = (k_{j-1}, v_j) before step 1, oldest
- *   first.  A zero row stands for a missing sample (it adds nothing to the
- *   normalizer or to the write), so a fresh sequence may start from zeros.
+ *   type `dtype`: the samples (x_j, y_j) before step 1, oldest first, with
+ *   x_j = k_{j-1} (x_j = k_j under FALCON_SAME_STEP) and y_j = v_j.  A zero row
+ *   stands for a missing sample (it adds nothing to the normalizer or to the
+ *   write), so a fresh sequence may start from zeros.
  *
- * falcon_fwd_recurrent_hist / falcon_fwd_chunk_hist - falcon_fwd_recurrent /
+ * falcon_fwd_recurrent_ex / falcon_fwd_chunk_ex - falcon_fwd_recurrent /
  * falcon_fwd_chunk with
+ *   flags              as above
  *   x_hist, y_hist     the incoming history, or both NULL (none).  Non-NULL
- *                      requires window > 1 and k_prev.
+ *                      requires window > 1, and k_prev unless FALCON_SAME_STEP.
  *   x_hist_out, y_hist_out   the B-1 latest samples after the call (same
  *                      shapes), or both NULL.  Requires window > 1.  Written
  *                      by a kernel enqueued after the main one, so they may
@@ -173,36 +184,40 @@ int falcon_decode_step(int variant, float beta, const void* beta_t, int beta_kin
  * With window > 1, S0 != NULL requires the incoming history (the state of a
  * resumed sequence is meaningless without its window samples).
  */
-int falcon_fwd_recurrent_hist(int variant, int window, float beta, const void* beta_t,
-                              int beta_kind, float lambda, float eps, int batch, int heads,
-                              int seqlen, int dk, int dv, int dtype, const void* q,
-                              const void* k, const void* v, const void* k_prev,
-                              const float* S0, const void* x_hist, const void* y_hist,
-                              float* o, float* S_out, void* x_hist_out, void* y_hist_out,
-                              void* stream);
-int falcon_fwd_chunk_hist(int variant, int window, float beta, const void* beta_t,
-                          int beta_kind, float lambda, float eps, int batch, int heads,
-                          int seqlen, int dk, int dv, int dtype, const void* q, const void* k,
-                          const void* v, const void* k_prev, const float* S0,
-                          const void* x_hist, const void* y_hist, float* o, float* S_out,
-                          void* x_hist_out, void* y_hist_out, int chunk, void* stream);
+#define FALCON_SAME_STEP 1
+int falcon_fwd_recurrent_ex(int variant, int window, int flags, float beta, const void* beta_t,
+                            int beta_kind, float lambda, float eps, int batch, int heads,
+                            int seqlen, int dk, int dv, int dtype, const void* q,
+                            const void* k, const void* v, const void* k_prev,
+                            const float* S0, const void* x_hist, const void* y_hist,
+                            float* o, float* S_out, void* x_hist_out, void* y_hist_out,
+                            void* stream);
+int falcon_fwd_chunk_ex(int variant, int window, int flags, float beta, const void* beta_t,
+                        int beta_kind, float lambda, float eps, int batch, int heads,
+                        int seqlen, int dk, int dv, int dtype, const void* q, const void* k,
+                        const void* v, const void* k_prev, const float* S0,
+                        const void* x_hist, const void* y_hist, float* o, float* S_out,
+                        void* x_hist_out, void* y_hist_out, int chunk, void* stream);
 
 /*
- * falcon_decode_step_hist - falcon_decode_step for every variant, with the
- * window history of Falcon-3/3A:
+ * falcon_decode_step_ex - falcon_decode_step for every variant, with the
+ * window history of Falcon-3/3A and the pairing flag:
  *   window    B in 1..8; > 1 only for FALCON_3 / FALCON_3A
+ *   flags     0 or FALCON_SAME_STEP (then x = k, and k_prev must be NULL and
+ *             is not updated)
  *   x_hist, y_hist   [nseq, heads, B-1, dk] / [nseq, heads, B-1, dv] (dtype),
  *             oldest first; required when window > 1, NULL when window == 1.
- * The window of the step is the history plus (x, y) = (k_prev, v).  S, k_prev
- * and the history are updated in place: the oldest sample is dropped and
- * (k_prev, v) appended, then k_prev <- k.  beta_t as in falcon_decode_step
+ * The window of the step is the history plus (x, y), x = k_prev (x = k under
+ * FALCON_SAME_STEP), y = v.  S, k_prev and the history are updated in place:
+ * the oldest sample is dropped and (x, y) appended, then k_prev <- k (prefix
+ * pairing only).  beta_t as in falcon_decode_step
  * (per-channel gains only for Falcon-2/2A).  No argument may overlap another.
  */
-int falcon_decode_step_hist(int variant, int window, float beta, const void* beta_t,
-                            int beta_kind, float lambda, float eps, int nseq, int heads, int dk,
-                            int dv, int dtype, float* S, void* k_prev, void* x_hist,
-                            void* y_hist, const void* q, const void* k, const void* v, float* o,
-                            void* stream);
+int falcon_decode_step_ex(int variant, int window, int flags, float beta, const void* beta_t,
+                          int beta_kind, float lambda, float eps, int nseq, int heads, int dk,
+                          int dv, int dtype, float* S, void* k_prev, void* x_hist,
+                          void* y_hist, const void* q, const void* k, const void* v, float* o,
+                          void* stream);
 
 #ifdef __cplusplus
 }

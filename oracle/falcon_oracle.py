@@ -208,26 +208,30 @@ def falcon_history(k, v, window, *, k_prev=None, x_hist=None, y_hist=None, same_
 
 
 def falcon_decode_step_window(variant, window, S, k_prev, x_hist, y_hist, q, k, v, *,
-                              beta=0.5, lam=0.0, eps=1e-6):
+                              beta=0.5, lam=0.0, eps=1e-6, same_step=False):
     """One decode step of Falcon-3/3A with a carried window history.
 
-    x = k_prev, y = v; the window is the history (window-1 samples, oldest
-    first) plus this sample.  Shapes: S [N, H, dv, dk]; k_prev, q, k [N, H, dk];
-    v [N, H, dv]; x_hist [N, H, window-1, dk]; y_hist [N, H, window-1, dv].
-    Returns (o, S_new, k_prev_new, x_hist_new, y_hist_new).
+    x = k_prev (x = k with same_step), y = v; the window is the history
+    (window-1 samples, oldest first) plus this sample.  Shapes: S [N, H, dv, dk];
+    k_prev, q, k [N, H, dk]; v [N, H, dv]; x_hist [N, H, window-1, dk]; y_hist
+    [N, H, window-1, dv].  Returns (o, S_new, k_prev_new, x_hist_new, y_hist_new);
+    with same_step k_prev plays no part and comes back unchanged.
     """
     q3, k3, v3 = _as64(q)[:, :, None], _as64(k)[:, :, None], _as64(v)[:, :, None]
+    kp = None if same_step else _as64(k_prev)
     o, S_new, _ = falcon_recurrence(variant, q3, k3, v3, beta=beta, lam=lam, eps=eps,
-                                    window=window, k_prev=_as64(k_prev), S0=_as64(S),
-                                    x_hist=x_hist, y_hist=y_hist)
-    xh, yh = falcon_history(k3, v3, window, k_prev=_as64(k_prev), x_hist=x_hist,
-                            y_hist=y_hist)
-    return o[:, :, 0], S_new, _as64(k).copy(), xh, yh
+                                    window=window, k_prev=kp, S0=_as64(S),
+                                    x_hist=x_hist, y_hist=y_hist, same_step=same_step)
+    xh, yh = falcon_history(k3, v3, window, k_prev=kp, x_hist=x_hist, y_hist=y_hist,
+                            same_step=same_step)
+    k_next = k_prev if same_step else _as64(k).copy()
+    return o[:, :, 0], S_new, k_next, xh, yh
 
 
 def falcon_decode_step(variant, S, k_prev, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6,
-                       beta_t=None):
+                       beta_t=None, same_step=False):
     """One decode step: x = k_prev, y = v, update S, o = S_new q; k_prev <- k.
+    With same_step: x = k, and k_prev plays no part (returned unchanged).
 
     Shapes: S [N, H, dv, dk]; k_prev, q, k [N, H, dk]; v [N, H, dv];
     beta_t None, [N, H] or [N, H, dv].  Returns (o, S_new, k_prev_new).
@@ -241,8 +245,9 @@ def falcon_decode_step(variant, S, k_prev, q, k, v, *, beta=0.5, lam=0.0, eps=1e
         bt = beta_t[:, :, None] if beta_t.ndim == 2 else beta_t[:, :, None, :]
     o, S_new, _ = falcon_recurrence(
         variant, _as64(q)[:, :, None], _as64(k)[:, :, None], _as64(v)[:, :, None],
-        beta=beta, lam=lam, eps=eps, beta_t=bt, k_prev=_as64(k_prev), S0=_as64(S))
-    return o[:, :, 0], S_new, _as64(k).copy()
+        beta=beta, lam=lam, eps=eps, beta_t=bt, k_prev=None if same_step else _as64(k_prev),
+        S0=_as64(S), same_step=same_step)
+    return o[:, :, 0], S_new, (k_prev if same_step else _as64(k).copy())
 
 
 def falcon_masked_parallel(variant, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6, window=1,

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.falcon_abi_version() == 2
+    assert lib.falcon_abi_version() == 3
     assert lib.falcon_status_string(0) == b"ok"
     assert lib.falcon_status_string(1) == b"invalid argument"
     assert lib.falcon_status_string(2) == b"unsupported configuration"
@@ -148,23 +148,23 @@ def test_decode_validation(lib, over, status):
     assert _dec(lib, **over) == status
 
 
-def _seqh(lib, fn="falcon_fwd_chunk_hist", **over):
-    a = dict(variant=2, window=3, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6,
+def _seqh(lib, fn="falcon_fwd_chunk_ex", **over):
+    a = dict(variant=2, window=3, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6,
              batch=1, heads=1, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2],
              k_prev=P[7], S0=P[6], x_hist=P[8], y_hist=P[9], o=P[3], S_out=None, xo=None,
              yo=None, chunk=64)
     a.update(over)
-    args = [a["variant"], a["window"], a["beta"], a["beta_t"], a["beta_kind"], a["lam"], a["eps"],
-            a["batch"], a["heads"], a["seqlen"], a["dk"], a["dv"], a["dtype"], a["q"], a["k"],
-            a["v"], a["k_prev"], a["S0"], a["x_hist"], a["y_hist"], a["o"], a["S_out"], a["xo"],
-            a["yo"]]
-    if fn == "falcon_fwd_chunk_hist":
+    args = [a["variant"], a["window"], a["flags"], a["beta"], a["beta_t"], a["beta_kind"],
+            a["lam"], a["eps"], a["batch"], a["heads"], a["seqlen"], a["dk"], a["dv"], a["dtype"],
+            a["q"], a["k"], a["v"], a["k_prev"], a["S0"], a["x_hist"], a["y_hist"], a["o"],
+            a["S_out"], a["xo"], a["yo"]]
+    if fn == "falcon_fwd_chunk_ex":
         args.append(a["chunk"])
     args.append(None)
     return getattr(lib, fn)(*args)
 
 
-@pytest.mark.parametrize("fn", ["falcon_fwd_chunk_hist", "falcon_fwd_recurrent_hist"])
+@pytest.mark.parametrize("fn", ["falcon_fwd_chunk_ex", "falcon_fwd_recurrent_ex"])
 @pytest.mark.parametrize("over,status", [
     (dict(y_hist=None), INVALID),                    # history comes in pairs
     (dict(xo=P[10]), INVALID),                       # so do its outputs
@@ -176,21 +176,24 @@ def _seqh(lib, fn="falcon_fwd_chunk_hist", **over):
     (dict(xo=P[0], yo=P[10]), INVALID),              # history output aliases q
     (dict(xo=P[8] + 64, yo=P[10]), INVALID),         # partial overlap with the input history
     (dict(variant=0, window=2), INVALID),            # window outside Falcon-3/3A
+    (dict(flags=2), INVALID),                        # unknown flag
+    (dict(flags=1), INVALID),                        # same-step pairing takes no k_prev
+    (dict(flags=1, k_prev=None, x_hist=None, y_hist=None), INVALID),  # windowed S0, no history
 ])
 def test_history_validation(lib, fn, over, status):
     assert _seqh(lib, fn, **over) == status
 
 
 def _dech(lib, **over):
-    a = dict(variant=2, window=3, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, nseq=2,
+    a = dict(variant=2, window=3, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, nseq=2,
              heads=2, dk=64, dv=64, dtype=0, S=P[0], k_prev=P[1], x_hist=P[6], y_hist=P[7],
              q=P[2], k=P[3], v=P[4], o=P[5])
     a.update(over)
-    return lib.falcon_decode_step_hist(a["variant"], a["window"], a["beta"], a["beta_t"],
-                                       a["beta_kind"], a["lam"], a["eps"], a["nseq"], a["heads"],
-                                       a["dk"], a["dv"], a["dtype"], a["S"], a["k_prev"],
-                                       a["x_hist"], a["y_hist"], a["q"], a["k"], a["v"], a["o"],
-                                       None)
+    return lib.falcon_decode_step_ex(a["variant"], a["window"], a["flags"], a["beta"],
+                                     a["beta_t"], a["beta_kind"], a["lam"], a["eps"], a["nseq"],
+                                     a["heads"], a["dk"], a["dv"], a["dtype"], a["S"],
+                                     a["k_prev"], a["x_hist"], a["y_hist"], a["q"], a["k"], a["v"],
+                                     a["o"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -202,6 +205,9 @@ def _dech(lib, **over):
     (dict(x_hist=P[5]), INVALID),                    # history aliases o
     (dict(window=9), UNSUPPORTED),
     (dict(beta_kind=2, beta_t=P[8]), INVALID),       # per-channel gain on Falcon-3
+    (dict(flags=1), INVALID),                        # same-step pairing takes no k_prev
+    (dict(k_prev=None), INVALID),                    # prefix pairing needs it
+    (dict(flags=4, k_prev=None), INVALID),
 ])
 def test_decode_history_validation(lib, over, status):
     assert _dech(lib, **over) == status

@@ -301,19 +301,24 @@ def test_decode_small(variant, dk, dv):
 @pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
 @pytest.mark.parametrize("dk,dv,window", [(64, 64, 2), (64, 64, 4), (128, 32, 4), (32, 32, 3),
                                           (64, 16, 3)])
-def test_window_history_resume(form, variant, dk, dv, window):
+@pytest.mark.parametrize("same_step", [False, True])
+def test_window_history_resume(form, variant, dk, dv, window, same_step):
     """Resumed call: S0, k_prev and the window history in; o, S and the history out."""
     if form == "rec" and dk == 128:
         pytest.skip("covered by the chunk form")
     inp = seq_inputs(2, 2, 77, dk, dv, seed=600 + 7 * variant + 3 * window + dk, dtype="bf16",
                      with_k_prev=True, with_S0=True, beta_per_token=True, s_std=0.2,
                      history=window - 1)
+    if same_step:
+        inp.pop("k_prev")
     dt = torch.bfloat16
-    q, k, v, bt, kp, xh, yh = (to_dev(torch, inp[n], dt)
-                               for n in ("q", "k", "v", "beta_t", "k_prev", "x_hist", "y_hist"))
+    q, k, v, bt, xh, yh = (to_dev(torch, inp[n], dt)
+                           for n in ("q", "k", "v", "beta_t", "x_hist", "y_hist"))
+    kp = None if same_step else to_dev(torch, inp["k_prev"], dt)
     S0 = to_dev(torch, inp["S0"], torch.float32)
     kw = dict(variant=variant, beta=None, lam=0.02, eps=1e-6, window=window, beta_t=bt,
-              k_prev=kp, S0=S0, x_hist=xh, y_hist=yh, return_state=True, return_history=True)
+              k_prev=kp, S0=S0, x_hist=xh, y_hist=yh, return_state=True, return_history=True,
+              same_step=same_step)
     if form == "chunk":
         o, S, xo, yo = fw.fwd_chunk(q, k, v, chunk=64, **kw)
     else:
@@ -321,10 +326,10 @@ def test_window_history_resume(form, variant, dk, dv, window):
     torch.cuda.synchronize()
     o_ref, S_ref, _ = fo.falcon_recurrence(
         variant, inp["q"], inp["k"], inp["v"], beta=None, lam=0.02, eps=1e-6, window=window,
-        beta_t=inp["beta_t"], k_prev=inp["k_prev"], S0=inp["S0"], x_hist=inp["x_hist"],
-        y_hist=inp["y_hist"])
-    xr, yr = fo.falcon_history(inp["k"], inp["v"], window, k_prev=inp["k_prev"],
-                               x_hist=inp["x_hist"], y_hist=inp["y_hist"])
+        beta_t=inp["beta_t"], k_prev=inp.get("k_prev"), S0=inp["S0"], x_hist=inp["x_hist"],
+        y_hist=inp["y_hist"], same_step=same_step)
+    xr, yr = fo.falcon_history(inp["k"], inp["v"], window, k_prev=inp.get("k_prev"),
+                               x_hist=inp["x_hist"], y_hist=inp["y_hist"], same_step=same_step)
     err, zok = token_normwise_err(o.cpu().numpy(), o_ref)
     serr = state_err(S.cpu().numpy(), S_ref)
     tol = TOL_BF16 if form == "chunk" else TOL_FP32_MATH
@@ -375,7 +380,8 @@ def test_window_history_split_in_place(form, window):
 @pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
 @pytest.mark.parametrize("dk,dv,window", [(64, 64, 4), (16, 128, 2), (128, 32, 3), (32, 16, 8)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_window(variant, dk, dv, window, dtype):
+@pytest.mark.parametrize("same_step", [False, True])
+def test_decode_window(variant, dk, dv, window, dtype, same_step):
     """Decode steps with the window history updated in place, against the oracle's
     windowed decode step by step."""
     steps, pool = 12, 4
@@ -386,13 +392,14 @@ def test_decode_window(variant, dk, dv, window, dtype):
     kp, xh, yh = (to_dev(torch, inp[n], dt) for n in ("k_prev", "x_hist", "y_hist"))
     qs, ks, vs = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
     S_r, kp_r, xh_r, yh_r = (inp[n].astype(np.float64) for n in ("S", "k_prev", "x_hist", "y_hist"))
+    kp_dev = None if same_step else kp
     for s in range(steps):
         p = s % pool
-        o = fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=variant, beta=0.6, lam=0.02,
-                           eps=1e-6, window=window, x_hist=xh, y_hist=yh)
+        o = fw.decode_step(S, kp_dev, qs[p], ks[p], vs[p], variant=variant, beta=0.6, lam=0.02,
+                           eps=1e-6, window=window, x_hist=xh, y_hist=yh, same_step=same_step)
         o_r, S_r, kp_r, xh_r, yh_r = fo.falcon_decode_step_window(
             variant, window, S_r, kp_r, xh_r, yh_r, inp["q"][p], inp["k"][p], inp["v"][p],
-            beta=0.6, lam=0.02, eps=1e-6)
+            beta=0.6, lam=0.02, eps=1e-6, same_step=same_step)
         torch.cuda.synchronize()
         err, zok = token_normwise_err(o.cpu().numpy(), o_r)
         assert zok and err <= TOL_FP32_MATH, (s, err)
@@ -402,6 +409,70 @@ def test_decode_window(variant, dk, dv, window, dtype):
     np.testing.assert_array_equal(kp.float().cpu().numpy(), kp_r)
     np.testing.assert_array_equal(xh.float().cpu().numpy(), xh_r)
     np.testing.assert_array_equal(yh.float().cpu().numpy(), yh_r)
+
+
+# ---------------------------------------------------------------------------
+# same-step pairing (x_t = k_t): every kernel family
+
+@pytest.mark.parametrize("form", ["rec", "chunk"])
+@pytest.mark.parametrize("variant,dk,dv,window", [
+    (fw.FALCON_1, 64, 64, 1), (fw.FALCON_1A, 32, 32, 1), (fw.FALCON_2, 64, 64, 1),
+    (fw.FALCON_2A, 32, 16, 1), (fw.FALCON_1, 128, 32, 1), (fw.FALCON_3, 64, 64, 4),
+    (fw.FALCON_3A, 128, 32, 2), (fw.FALCON_3, 32, 32, 3), (fw.FALCON_3A, 64, 16, 3)])
+@pytest.mark.parametrize("with_S0", [False, True])
+def test_same_step_pairing(form, variant, dk, dv, window, with_S0):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    inp = seq_inputs(2, 2, 83, dk, dv, seed=700 + 11 * variant + dk + window, dtype="bf16",
+                     with_S0=with_S0, beta_per_channel=per_ch, beta_per_token=not per_ch,
+                     s_std=0.2)
+    dt = torch.bfloat16
+    q, k, v, bt = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "beta_t"))
+    S0 = to_dev(torch, inp["S0"], torch.float32) if with_S0 else None
+    hist = {}
+    if with_S0 and window > 1:   # a windowed state travels with its history (zero: none)
+        hist = dict(x_hist=torch.zeros((2, 2, window - 1, dk), device="cuda", dtype=dt),
+                    y_hist=torch.zeros((2, 2, window - 1, dv), device="cuda", dtype=dt))
+    kw = dict(variant=variant, beta=None, lam=0.02, eps=1e-6, window=window, beta_t=bt, S0=S0,
+              same_step=True, return_state=True, **hist)
+    if form == "chunk":
+        o, S = fw.fwd_chunk(q, k, v, chunk=64, **kw)
+    else:
+        o, S = fw.fwd_recurrent(q, k, v, **kw)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], beta=None,
+                                           lam=0.02, eps=1e-6, window=window,
+                                           beta_t=inp["beta_t"], S0=inp.get("S0"),
+                                           same_step=True)
+    err, zok = token_normwise_err(o.cpu().numpy(), o_ref)
+    serr = state_err(S.cpu().numpy(), S_ref)
+    tol = TOL_BF16 if form == "chunk" else TOL_FP32_MATH
+    print("same-step %s v%d dk %d dv %d window %d: o err %.3e S err %.3e"
+          % (form, variant, dk, dv, window, err, serr))
+    assert zok and err <= tol and serr <= tol
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_2, fw.FALCON_1A])
+def test_decode_same_step(variant):
+    per_ch = variant == fw.FALCON_2
+    inp = decode_inputs(3, 2, 64, 32, seed=720 + variant, steps=4, s_std=0.2,
+                        beta_per_channel=per_ch)
+    dt = torch.bfloat16
+    S = to_dev(torch, inp["S"], torch.float32)
+    qs, ks, vs = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
+    bs = to_dev(torch, inp["beta_t"], dt) if per_ch else None
+    S_r = inp["S"].astype(np.float64)
+    for s in range(8):
+        p = s % 4
+        o = fw.decode_step(S, None, qs[p], ks[p], vs[p], variant=variant, beta=0.6, lam=0.02,
+                           eps=1e-6, beta_t=bs[p] if per_ch else None, same_step=True)
+        o_r, S_r, _ = fo.falcon_decode_step(variant, S_r, None, inp["q"][p], inp["k"][p],
+                                            inp["v"][p], beta=0.6, lam=0.02, eps=1e-6,
+                                            beta_t=inp["beta_t"][p] if per_ch else None,
+                                            same_step=True)
+        torch.cuda.synchronize()
+        err, zok = token_normwise_err(o.cpu().numpy(), o_r)
+        assert zok and err <= TOL_FP32_MATH, (s, err)
+    assert state_err(S.cpu().numpy(), S_r) <= TOL_FP32_MATH
 
 
 # ---------------------------------------------------------------------------

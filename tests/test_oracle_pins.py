@@ -361,16 +361,19 @@ def test_zero_history_is_no_history(variant):
 
 @pytest.mark.parametrize("variant", [fo.FALCON_3, fo.FALCON_3A])
 @pytest.mark.parametrize("window", [2, 4])
-def test_window_decode_equals_recurrence(variant, window):
+@pytest.mark.parametrize("same_step", [False, True])
+def test_window_decode_equals_recurrence(variant, window, same_step):
     # prefill, then one decode step per token with the carried history, equals
-    # the recurrence over the whole sequence
+    # the recurrence over the whole sequence (either pairing)
     L, L1 = 9, 3
     inp = _tiny(87, B=2, H=2, L=L, dk=4, dv=3)
-    kw = dict(beta=0.6, lam=0.05, eps=1e-6)
+    kw = dict(beta=0.6, lam=0.05, eps=1e-6, same_step=same_step)
     o, S, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], window=window, **kw)
     sg = _seg(inp, 0, L1)
     o1, St, kp = fo.falcon_recurrence(variant, sg["q"], sg["k"], sg["v"], window=window, **kw)
-    xh, yh = fo.falcon_history(sg["k"], sg["v"], window)
+    xh, yh = fo.falcon_history(sg["k"], sg["v"], window, same_step=same_step)
+    if same_step:
+        kp = None
     got = [o1]
     for t in range(L1, L):
         ot, St, kp, xh, yh = fo.falcon_decode_step_window(
@@ -378,4 +381,23 @@ def test_window_decode_equals_recurrence(variant, window):
             inp["v"][:, :, t], **kw)
         got.append(ot[:, :, None])
     np.testing.assert_allclose(np.concatenate(got, axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(St, S, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_1, fo.FALCON_2A])
+def test_same_step_decode_equals_recurrence(variant):
+    # with same-step pairing a decode step writes (k_t, v_t) and reads with q_t
+    inp = _tiny(88, B=2, H=2, L=6, dk=4, dv=3, with_S0=True,
+                beta_per_channel=variant == fo.FALCON_2A)
+    kw = dict(beta=0.6, lam=0.05, eps=1e-6)
+    bt = inp.get("beta_t")
+    o, S, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], S0=inp["S0"],
+                                   beta_t=bt, same_step=True, **kw)
+    St = inp["S0"]
+    for t in range(6):
+        ot, St, kp = fo.falcon_decode_step(variant, St, None, inp["q"][:, :, t], inp["k"][:, :, t],
+                                           inp["v"][:, :, t], same_step=True,
+                                           beta_t=None if bt is None else bt[:, :, t], **kw)
+        assert kp is None
+        np.testing.assert_allclose(ot, o[:, :, t], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(St, S, rtol=1e-13, atol=1e-14)

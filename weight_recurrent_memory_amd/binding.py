@@ -15,6 +15,7 @@ VARIANT_NAMES = {"falcon1": FALCON_1, "falcon2": FALCON_2, "falcon3": FALCON_3,
                  "falcon1a": FALCON_1A, "falcon2a": FALCON_2A, "falcon3a": FALCON_3A}
 _BF16, _F32 = 0, 1
 _BETA_SCALAR, _BETA_TOKEN, _BETA_CHANNEL = 0, 1, 2
+SAME_STEP = 1        # flag: pair v_t with k_t instead of k_{t-1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -52,15 +53,15 @@ def load_library():
     lib.falcon_decode_step.restype = i
     lib.falcon_decode_step.argtypes = [i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp, vp,
                                        vp, vp]
-    hist_args = [i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                 vp]
-    lib.falcon_fwd_recurrent_hist.restype = i
-    lib.falcon_fwd_recurrent_hist.argtypes = hist_args + [vp]
-    lib.falcon_fwd_chunk_hist.restype = i
-    lib.falcon_fwd_chunk_hist.argtypes = hist_args + [i, vp]
-    lib.falcon_decode_step_hist.restype = i
-    lib.falcon_decode_step_hist.argtypes = [i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, vp]
+    ex_args = [i, i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+               vp]
+    lib.falcon_fwd_recurrent_ex.restype = i
+    lib.falcon_fwd_recurrent_ex.argtypes = ex_args + [vp]
+    lib.falcon_fwd_chunk_ex.restype = i
+    lib.falcon_fwd_chunk_ex.argtypes = ex_args + [i, vp]
+    lib.falcon_decode_step_ex.restype = i
+    lib.falcon_decode_step_ex.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp]
     _LIB = lib
     return lib
 
@@ -109,7 +110,7 @@ def _raise(lib, fn, status):
 
 def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev, S0,
               out, S_out, return_state, chunk, stream, x_hist=None, y_hist=None,
-              return_history=False, x_hist_out=None, y_hist_out=None):
+              return_history=False, x_hist_out=None, y_hist_out=None, same_step=False):
     import torch
     lib = load_library()
     variant = _variant(variant)
@@ -139,8 +140,8 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
     if S_out is None and return_state:
         S_out = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
     _check(torch, "S_out", S_out, (B, H, dv, dk), torch.float32, dev)
-    hist = (x_hist is not None or y_hist is not None or return_history
-            or x_hist_out is not None or y_hist_out is not None)
+    ext = (x_hist is not None or y_hist is not None or return_history
+           or x_hist_out is not None or y_hist_out is not None or same_step)
     nh = int(window) - 1
     _check(torch, "x_hist", x_hist, (B, H, nh, dk), dt, dev)
     _check(torch, "y_hist", y_hist, (B, H, nh, dv), dt, dev)
@@ -151,15 +152,16 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
             y_hist_out = torch.empty((B, H, nh, dv), device=dev, dtype=dt)
     _check(torch, "x_hist_out", x_hist_out, (B, H, nh, dk), dt, dev)
     _check(torch, "y_hist_out", y_hist_out, (B, H, nh, dv), dt, dev)
-    args = [variant, int(window), float(beta if beta is not None else 0.0), _ptr(beta_t), kind,
+    args = [float(beta if beta is not None else 0.0), _ptr(beta_t), kind,
             float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k), _ptr(v),
             _ptr(k_prev), _ptr(S0)]
-    if hist:
-        fn_name += "_hist"
+    if ext:
+        fn_name += "_ex"
+        args = [variant, int(window), SAME_STEP if same_step else 0] + args
         args += [_ptr(x_hist), _ptr(y_hist), _ptr(out), _ptr(S_out), _ptr(x_hist_out),
                  _ptr(y_hist_out)]
     else:
-        args += [_ptr(out), _ptr(S_out)]
+        args = [variant, int(window)] + args + [_ptr(out), _ptr(S_out)]
     if fn_name.startswith("falcon_fwd_chunk"):
         args.append(int(chunk))
     args.append(_stream(torch, dev, stream))
@@ -174,31 +176,31 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
 def fwd_recurrent(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
                   k_prev=None, S0=None, out=None, S_out=None, return_state=False, stream=None,
                   x_hist=None, y_hist=None, return_history=False, x_hist_out=None,
-                  y_hist_out=None):
+                  y_hist_out=None, same_step=False):
     """Recurrent form.  Returns o [B,H,L,dv] float32, then S_L with return_state,
     then the window history after the call (x_hist, y_hist) with return_history.
     x_hist [B,H,window-1,dk] / y_hist [B,H,window-1,dv]: carried window samples of a
-    resumed Falcon-3/3A sequence, oldest first."""
+    resumed Falcon-3/3A sequence, oldest first.  same_step: x_t = k_t (no k_prev)."""
     return _seq_call("falcon_fwd_recurrent", q, k, v, variant, beta, lam, eps, window, beta_t,
                      k_prev, S0, out, S_out, return_state, None, stream, x_hist, y_hist,
-                     return_history, x_hist_out, y_hist_out)
+                     return_history, x_hist_out, y_hist_out, same_step)
 
 
 def fwd_chunk(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, chunk=64, window=1,
               beta_t=None, k_prev=None, S0=None, out=None, S_out=None, return_state=False,
               stream=None, x_hist=None, y_hist=None, return_history=False, x_hist_out=None,
-              y_hist_out=None):
-    """Chunk-parallel form; results and history arguments as fwd_recurrent."""
+              y_hist_out=None, same_step=False):
+    """Chunk-parallel form; results, history and pairing arguments as fwd_recurrent."""
     return _seq_call("falcon_fwd_chunk", q, k, v, variant, beta, lam, eps, window, beta_t,
                      k_prev, S0, out, S_out, return_state, chunk, stream, x_hist, y_hist,
-                     return_history, x_hist_out, y_hist_out)
+                     return_history, x_hist_out, y_hist_out, same_step)
 
 
 def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, beta_t=None,
-                out=None, stream=None, window=1, x_hist=None, y_hist=None):
+                out=None, stream=None, window=1, x_hist=None, y_hist=None, same_step=False):
     """One decode step; updates S and k_prev (and, for window > 1, the window
     history x_hist [N,H,window-1,dk] / y_hist [N,H,window-1,dv]) in place,
-    returns o [N,H,dv] float32."""
+    returns o [N,H,dv] float32.  same_step: x = k; k_prev must be None."""
     import torch
     lib = load_library()
     variant = _variant(variant)
@@ -218,14 +220,15 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
     if out is None:
         out = torch.empty((N, H, dv), device=dev, dtype=torch.float32)
     _check(torch, "out", out, (N, H, dv), torch.float32, dev)
-    if window > 1 or x_hist is not None or y_hist is not None:
+    if window > 1 or x_hist is not None or y_hist is not None or same_step:
         _check(torch, "x_hist", x_hist, (N, H, int(window) - 1, dk), dt, dev)
         _check(torch, "y_hist", y_hist, (N, H, int(window) - 1, dv), dt, dev)
-        status = lib.falcon_decode_step_hist(
-            variant, int(window), float(beta if beta is not None else 0.0), _ptr(beta_t), kind,
-            float(lam), float(eps), N, H, dk, dv, dcode, _ptr(S), _ptr(k_prev), _ptr(x_hist),
-            _ptr(y_hist), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(torch, dev, stream))
-        _raise(lib, "falcon_decode_step_hist", status)
+        status = lib.falcon_decode_step_ex(
+            variant, int(window), SAME_STEP if same_step else 0,
+            float(beta if beta is not None else 0.0), _ptr(beta_t), kind, float(lam), float(eps),
+            N, H, dk, dv, dcode, _ptr(S), _ptr(k_prev), _ptr(x_hist), _ptr(y_hist), _ptr(q),
+            _ptr(k), _ptr(v), _ptr(out), _stream(torch, dev, stream))
+        _raise(lib, "falcon_decode_step_ex", status)
         return out
     status = lib.falcon_decode_step(variant, float(beta if beta is not None else 0.0),
                                     _ptr(beta_t), kind, float(lam), float(eps), N, H, dk, dv,

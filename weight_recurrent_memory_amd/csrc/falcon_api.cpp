@@ -58,7 +58,10 @@ int check_seq(const falcon::SeqArgs& a, bool hist_api) {
     return FALCON_ERR_INVALID_ARG;
   if (a.dtype != FALCON_BF16 && a.dtype != FALCON_F32) return FALCON_ERR_INVALID_ARG;
   if (!a.q || !a.k || !a.v || !a.o) return FALCON_ERR_INVALID_ARG;
-  if (a.S0 && !a.k_prev) return FALCON_ERR_INVALID_ARG;
+  // prefix pairing: a live state needs the key it pairs with the first value;
+  // same-step pairing has no carried key
+  if (a.key_shift && a.S0 && !a.k_prev) return FALCON_ERR_INVALID_ARG;
+  if (!a.key_shift && a.k_prev) return FALCON_ERR_INVALID_ARG;
   const void* ptrs[] = {a.q, a.k, a.v, a.k_prev, a.S0, a.o, a.S_out, a.beta_t};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
@@ -96,7 +99,7 @@ int check_history(const falcon::SeqArgs& a, const void* xo, const void* yo) {
   if ((a.x_hist == nullptr) != (a.y_hist == nullptr)) return FALCON_ERR_INVALID_ARG;
   if ((xo == nullptr) != (yo == nullptr)) return FALCON_ERR_INVALID_ARG;
   if ((hin || hout) && a.window < 2) return FALCON_ERR_INVALID_ARG;
-  if (hin && !a.k_prev) return FALCON_ERR_INVALID_ARG;
+  if (hin && a.key_shift && !a.k_prev) return FALCON_ERR_INVALID_ARG;
   if (a.window > 1 && a.S0 && !hin) return FALCON_ERR_INVALID_ARG;
   if (!hin && !hout) return FALCON_OK;
   const void* ptrs[] = {a.x_hist, a.y_hist, xo, yo};
@@ -185,17 +188,18 @@ FALCON_EXPORT int falcon_fwd_recurrent(int variant, int window, float beta, cons
   return fwd_recurrent(a, false, nullptr, nullptr, (hipStream_t)stream);
 }
 
-FALCON_EXPORT int falcon_fwd_recurrent_hist(int variant, int window, float beta,
-                                            const void* beta_t, int beta_kind, float lambda,
-                                            float eps, int batch, int heads, int seqlen, int dk,
-                                            int dv, int dtype, const void* q, const void* k,
-                                            const void* v, const void* k_prev, const float* S0,
-                                            const void* x_hist, const void* y_hist, float* o,
-                                            float* S_out, void* x_hist_out, void* y_hist_out,
-                                            void* stream) {
+FALCON_EXPORT int falcon_fwd_recurrent_ex(int variant, int window, int flags, float beta,
+                                          const void* beta_t, int beta_kind, float lambda,
+                                          float eps, int batch, int heads, int seqlen, int dk,
+                                          int dv, int dtype, const void* q, const void* k,
+                                          const void* v, const void* k_prev, const float* S0,
+                                          const void* x_hist, const void* y_hist, float* o,
+                                          float* S_out, void* x_hist_out, void* y_hist_out,
+                                          void* stream) {
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
   falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
-                    0, x_hist, y_hist};
+                    0, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
   return fwd_recurrent(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
 }
 
@@ -211,27 +215,31 @@ FALCON_EXPORT int falcon_fwd_chunk(int variant, int window, float beta, const vo
   return fwd_chunk(a, false, nullptr, nullptr, (hipStream_t)stream);
 }
 
-FALCON_EXPORT int falcon_fwd_chunk_hist(int variant, int window, float beta, const void* beta_t,
-                                        int beta_kind, float lambda, float eps, int batch,
-                                        int heads, int seqlen, int dk, int dv, int dtype,
-                                        const void* q, const void* k, const void* v,
-                                        const void* k_prev, const float* S0, const void* x_hist,
-                                        const void* y_hist, float* o, float* S_out,
-                                        void* x_hist_out, void* y_hist_out, int chunk,
-                                        void* stream) {
+FALCON_EXPORT int falcon_fwd_chunk_ex(int variant, int window, int flags, float beta,
+                                      const void* beta_t, int beta_kind, float lambda, float eps,
+                                      int batch, int heads, int seqlen, int dk, int dv, int dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const void* k_prev, const float* S0, const void* x_hist,
+                                      const void* y_hist, float* o, float* S_out,
+                                      void* x_hist_out, void* y_hist_out, int chunk,
+                                      void* stream) {
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
   falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
-                    chunk, x_hist, y_hist};
+                    chunk, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
   return fwd_chunk(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
 }
 
 namespace {
 
-int decode_step(int variant, int window, float beta, const void* beta_t, int beta_kind,
-                float lambda, float eps, int nseq, int heads, int dk, int dv, int dtype, float* S,
-                void* k_prev, void* x_hist, void* y_hist, const void* q, const void* k,
-                const void* v, float* o, bool hist_api, void* stream) {
+int decode_step(int variant, int window, int flags, float beta, const void* beta_t,
+                int beta_kind, float lambda, float eps, int nseq, int heads, int dk, int dv,
+                int dtype, float* S, void* k_prev, void* x_hist, void* y_hist, const void* q,
+                const void* k, const void* v, float* o, bool hist_api, void* stream) {
   if (variant < FALCON_1 || variant > FALCON_3A) return FALCON_ERR_INVALID_ARG;
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
+  const int key_shift = (flags & FALCON_SAME_STEP) ? 0 : 1;
+  if ((k_prev != nullptr) != (key_shift == 1)) return FALCON_ERR_INVALID_ARG;
   if (window < 1 || (window != 1 && !window_variant(variant))) return FALCON_ERR_INVALID_ARG;
   if ((x_hist == nullptr) != (y_hist == nullptr)) return FALCON_ERR_INVALID_ARG;
   if ((x_hist != nullptr) != (window > 1)) return FALCON_ERR_INVALID_ARG;
@@ -247,7 +255,7 @@ int decode_step(int variant, int window, float beta, const void* beta_t, int bet
   if (!finite_nonneg(lambda) || !finite_nonneg(eps)) return FALCON_ERR_INVALID_ARG;
   if (nseq < 1 || heads < 1 || dk < 1 || dv < 1) return FALCON_ERR_INVALID_ARG;
   if (dtype != FALCON_BF16 && dtype != FALCON_F32) return FALCON_ERR_INVALID_ARG;
-  if (!S || !k_prev || !q || !k || !v || !o) return FALCON_ERR_INVALID_ARG;
+  if (!S || !q || !k || !v || !o) return FALCON_ERR_INVALID_ARG;
   const void* ptrs[] = {S, k_prev, q, k, v, o, beta_t, x_hist, y_hist};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
@@ -266,7 +274,8 @@ int decode_step(int variant, int window, float beta, const void* beta_t, int bet
   if (!hist_api && window_variant(variant)) return FALCON_ERR_UNSUPPORTED;
   if (window > 8) return FALCON_ERR_UNSUPPORTED;
   falcon::DecodeArgs a{is_regression(variant), window, x_hist, y_hist, beta, beta_t, beta_kind,
-                       lambda, eps, nseq, heads, dk, dv, dtype, S, k_prev, q, k, v, o};
+                       lambda, eps, nseq, heads, dk, dv, dtype, S, k_prev, q, k, v, o,
+                       key_shift};
   return finish_launch(falcon::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -276,16 +285,16 @@ FALCON_EXPORT int falcon_decode_step(int variant, float beta, const void* beta_t
                                      float lambda, float eps, int nseq, int heads, int dk,
                                      int dv, int dtype, float* S, void* k_prev, const void* q,
                                      const void* k, const void* v, float* o, void* stream) {
-  return decode_step(variant, 1, beta, beta_t, beta_kind, lambda, eps, nseq, heads, dk, dv,
+  return decode_step(variant, 1, 0, beta, beta_t, beta_kind, lambda, eps, nseq, heads, dk, dv,
                      dtype, S, k_prev, nullptr, nullptr, q, k, v, o, false, stream);
 }
 
-FALCON_EXPORT int falcon_decode_step_hist(int variant, int window, float beta,
-                                          const void* beta_t, int beta_kind, float lambda,
-                                          float eps, int nseq, int heads, int dk, int dv,
-                                          int dtype, float* S, void* k_prev, void* x_hist,
-                                          void* y_hist, const void* q, const void* k,
-                                          const void* v, float* o, void* stream) {
-  return decode_step(variant, window, beta, beta_t, beta_kind, lambda, eps, nseq, heads, dk, dv,
-                     dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
+FALCON_EXPORT int falcon_decode_step_ex(int variant, int window, int flags, float beta,
+                                        const void* beta_t, int beta_kind, float lambda,
+                                        float eps, int nseq, int heads, int dk, int dv,
+                                        int dtype, float* S, void* k_prev, void* x_hist,
+                                        void* y_hist, const void* q, const void* k,
+                                        const void* v, float* o, void* stream) {
+  return decode_step(variant, window, flags, beta, beta_t, beta_kind, lambda, eps, nseq, heads,
+                     dk, dv, dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }

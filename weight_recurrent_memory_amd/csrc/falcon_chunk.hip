@@ -180,7 +180,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
       const long g = t0 - (B - 1) + jj;            // global step of key x_g
       uint4 val = {0u, 0u, 0u, 0u};
       if (idx < NXP * VPR && jj < NX && g < t0 + c) {
-        if (g >= 1) val = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
+        if (g >= a.key_shift) val = *reinterpret_cast<const uint4*>(kg + qk_base + (g - a.key_shift) * DK + kv * 8);
         else if (g == 0 && kpg) val = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
         else if (g < 0 && xhg)   // carried window history, slot B-1+g
           val = *reinterpret_cast<const uint4*>(xhg + ((long)chain * (B - 1) + (B - 1) + g) * DK + kv * 8);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
 #pragma unroll
         for (int w = 0; w < B; ++w) n += sm.nrm[t - w + B - 1];
       }
-      const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+      const bool live = t < c && !(t0 + t == 0 && kpg == nullptr && a.key_shift);
       constexpr int NR = PERROW ? RW : 1;
       constexpr int WST = PERROW ? 4 : 1;
       for (int i = wave; i < NR; i += WST) {

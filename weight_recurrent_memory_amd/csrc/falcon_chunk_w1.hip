@@ -176,8 +176,8 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
       const int t = idx / VPR, kv = idx % VPR;
       uint4 kval = {0u, 0u, 0u, 0u}, qval = {0u, 0u, 0u, 0u};
       if (idx < CS * VPR && t < c) {
-        const long g = t0 + t;   // key x_g = k_{g-1}; x_0 = k_prev or 0
-        if (g >= 1) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - 1) * DK + kv * 8);
+        const long g = t0 + t;   // key x_g = k_{g-s}; with s = 1, x_0 = k_prev or 0
+        if (g >= a.key_shift) kval = *reinterpret_cast<const uint4*>(kg + qk_base + (g - a.key_shift) * DK + kv * 8);
         else if (kpg) kval = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + kv * 8);
         qval = *reinterpret_cast<const uint4*>(qg + qk_base + g * DK + kv * 8);
       }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     const long t0 = (long)cidx * CS;
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
     const int t = lane;
-    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr && a.key_shift);
     float eta = 0.0f, dec = 1.0f;
     if (live) {
       const float bv = PERROW ? bf16_to_f32(sm.BT[s][row][t]) : sm.beta[s][t];
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     const long t0 = (long)cidx * CS;
     const int c = (int)((L - t0) < CS ? (L - t0) : CS);
     const int t = lane % CS, rl = lane / CS;
-    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr && a.key_shift);
     const float rn = __builtin_amdgcn_rcpf(a.eps + sm.nrm[s][t]);
     float eta[NC], g[NC];
 #pragma unroll

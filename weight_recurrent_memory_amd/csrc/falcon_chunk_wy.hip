@@ -218,9 +218,9 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   const int kq_t = kt_id / VPR, kq_kv = kt_id % VPR;
   const auto rk = rsrc(kg + qk_base, L * DK * 2);
   const auto rq = rsrc(qg + qk_base, L * DK * 2);
-  // key x_g = k_{g-1}: row g - 1 (the first step of the sequence reads 0 there and
-  // takes k_prev at commit)
-  const uint32_t koff = kq_in ? (uint32_t)(((kq_t - 1) * DK + kq_kv * 8) * 2) : PARKED;
+  // key x_g = k_{g-s}: row g - s (with s = 1 the first step of the sequence reads 0
+  // there and takes k_prev at commit)
+  const uint32_t koff = kq_in ? (uint32_t)(((kq_t - a.key_shift) * DK + kq_kv * 8) * 2) : PARKED;
   const uint32_t qoff = kq_in ? (uint32_t)((kq_t * DK + kq_kv * 8) * 2) : PARKED;
   constexpr uint32_t KQ_CHUNK = CS * DK * 2;
   auto ld128 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   auto commit_kq = [&](const KQSet& p, int jk, int jq) __attribute__((always_inline)) {
     if (kq_in) {
       if (live_chunk(jk)) {
-        const uint4 kv = (jk == 0 && kq_t == 0) ? kprev : p.k;
+        const uint4 kv = (jk == 0 && kq_t == 0 && a.key_shift) ? kprev : p.k;
         put8(&sm.X[jk & 3][kq_t][0], kq_kv * 8, kv);
         float part = 0.0f;
         const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     const long t0 = (long)j * CS;
     const int c = steps(j);
     const int t = lane & 31;
-    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr);
+    const bool live = t < c && !(t0 + t == 0 && kpg == nullptr && a.key_shift);
     const float nrm = sm.knorm[j & 3][t];
     const float bv = sm.beta[j & 3][t];
     float eta = 0.0f, dec = 1.0f;

@@ -246,10 +246,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   const auto rv = rsrc(vg + v_base, L * dv * 2);
   const auto rb = a.beta_kind == 1 ? rsrc(bg + (long)chain * L, L * 2) : rsrc(vg, 0);
   constexpr uint32_t KQ_CHUNK = CS * DK * 2;
-  // key x_g = k_{g-1}: piece p of the block is row p / VPR, k = 8 (p % VPR)
+  // key x_g = k_{g-s}: piece p of the block is row p / VPR - s, k = 8 (p % VPR)
   auto koff = [&](int u) __attribute__((always_inline)) {
     const int p = lane + 64 * u;
-    return (uint32_t)(((p / VPR - 1) * DK + (p % VPR) * 8) * 2);
+    return (uint32_t)(((p / VPR - a.key_shift) * DK + (p % VPR) * 8) * 2);
   };
   auto qoff = [&](int u) __attribute__((always_inline)) {
     const int p = lane + 64 * u;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     for (int u = 0; u < KP; ++u) {
       const int p = lane + 64 * u;
       const int t = p / VPR, kv = p % VPR;
-      const uint4 val = (j == 0 && t == 0) ? kprev[u] : s.p[u];
+      const uint4 val = (j == 0 && t == 0 && a.key_shift) ? kprev[u] : s.p[u];
       put8(&sm.X[jb][t][0], kv * 8, val);
       float part = 0.0f;
       const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       const int m = 16 + t - w;
       n += m >= 16 ? sm.knorm[j & 3][m - 16] : sm.knorm[(j - 1) & 3][m];
     }
-    const bool live = t < steps(j) && !((long)j * CS + t == 0 && kpg == nullptr);
+    const bool live = t < steps(j) && !((long)j * CS + t == 0 && kpg == nullptr && a.key_shift);
     float eta = 0.0f, dec = 1.0f;
     if (live) {
       eta = sm.beta[j & 3][t] * __builtin_amdgcn_rcpf(a.eps + n);

@@ -2,7 +2,8 @@
 // (explainer of arXiv 2608.27763, section 核心方法 §3: the recurrent form serves
 // inference; 163.com section 01: write first, then read with the updated state).
 //
-// Per (sequence, head), with x = k_prev and y = v:
+// Per (sequence, head), with x = k_prev (prefix pairing; x = k with same-step
+// pairing, which leaves k_prev alone) and y = v:
 //   r1 = S x, r2 = S q                     (one read pass over S)
 //   e  = y - r1 (regression) or y (inner product)
 //   S' = a S + eta e x^T                   (one write pass, in place)
@@ -47,9 +48,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
     else s[p] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   float x[4], qq[4];
+  const T* xsrc = a.key_shift ? kp : k;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    x[e] = ld_in(kp, head * DK + c0 + e);
+    x[e] = ld_in(xsrc, head * DK + c0 + e);
     qq[e] = ld_in(q, head * DK + c0 + e);
   }
   float yv[PASSES], bv[PASSES];
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
   }
   // Every lane has read its slice of k_prev; only now may it be overwritten.
   __syncthreads();
-  if (rloc == 0) {
+  if (rloc == 0 && a.key_shift) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) kp[head * DK + c0 + e] = k[head * DK + c0 + e];
   }
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecodeArgs a) {
 // B-1 samples (oldest first) plus (x, y) = (k_prev, v):
 //   n = sum_w ||x_w||^2, r_w = S x_w, e_w = y_w - r_w (or y_w), r2 = S q
 //   S' = a S + eta sum_w e_w x_w^T,  o = a r2 + eta sum_w e_w (x_w . q)
-// then the history drops its oldest sample and appends (x, y), and k_prev <- k.
+// then the history drops its oldest sample and appends (x, y), and k_prev <- k
+// (prefix pairing; with same-step pairing x = k and k_prev is not used).
 constexpr int kMaxDecWindow = 8;
 
 template <typename T, int DK, int DV>
@@ -129,6 +132,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_window_kernel(DecodeArgs a
     if (row < DV) s[p] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sh + (long)row * DK + c0));
     else s[p] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  const T* xcur = a.key_shift ? static_cast<const T*>(kp) : k;   // this step's x
   float x[MW][4], qq[4];
 #pragma unroll
   for (int w = 0; w < MW; ++w)
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_window_kernel(DecodeArgs a
     for (int e = 0; e < 4; ++e) {
       float xv = 0.0f;
       if (w < NH) xv = ld_in(xh, (head * NH + w) * DK + c0 + e);
-      else if (w == NH) xv = ld_in(kp, head * DK + c0 + e);
+      else if (w == NH) xv = ld_in(xcur, head * DK + c0 + e);
       x[w][e] = xv;
     }
 #pragma unroll
@@ -162,8 +166,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_window_kernel(DecodeArgs a
     for (int e = 0; e < 4; ++e) {
       const long c = c0 + e;
       for (int w = 0; w + 1 < NH; ++w) xh[(head * NH + w) * DK + c] = xh[(head * NH + w + 1) * DK + c];
-      xh[(head * NH + NH - 1) * DK + c] = kp[head * DK + c];
-      kp[head * DK + c] = k[head * DK + c];
+      xh[(head * NH + NH - 1) * DK + c] = xcur[head * DK + c];
+      if (a.key_shift) kp[head * DK + c] = k[head * DK + c];
     }
   }
   float n = 0.0f, xq[MW];

@@ -29,6 +29,9 @@ struct SeqArgs {
   // none (zero samples)
   const void* x_hist = nullptr;
   const void* y_hist = nullptr;
+  // sample pairing: x_t = k_{t - key_shift}; 1 = the previous key (x_1 = k_prev
+  // or 0), 0 = the same step's key
+  int key_shift = 1;
 };
 
 struct DecodeArgs {
@@ -48,6 +51,7 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   float* o;
+  int key_shift;     // 1: x = k_prev (then k_prev <- k); 0: x = k, k_prev unused
 };
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);

@@ -48,9 +48,10 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
     s[e] = (a.S0 && active) ? a.S0[((long)chain * a.dv + rowc) * DK + c0 + e] : 0.0f;
 
   const int B = a.window;
+  const int ks = a.key_shift;
   for (long t = 0; t < L; ++t) {
-    // window samples g = t - w, w = 0..B-1: x_g = k[g-1] (g >= 1), k_prev or 0
-    // (g == 0); g < 0 is history slot B-1+g when one is carried, else zero
+    // window samples g = t - w, w = 0..B-1: x_g = k[g-ks] (g >= ks), k_prev or 0
+    // (g == 0 < ks); g < 0 is history slot B-1+g when one is carried, else zero
     float xw[kMaxWindow][CPT];
     float yw[kMaxWindow];
     float n = 0.0f;
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
         float xv = 0.0f;
-        if (w < B && g >= 1) xv = ld_in(k, qk_base + (g - 1) * DK + c0 + e);
+        if (w < B && g >= ks) xv = ld_in(k, qk_base + (g - ks) * DK + c0 + e);
         else if (w < B && g == 0 && kp) xv = ld_in(kp, (long)chain * DK + c0 + e);
         else if (w < B && g < 0 && xh) xv = ld_in(xh, ((long)chain * (B - 1) + (B - 1) + g) * DK + c0 + e);
         xw[w][e] = xv;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(SeqArgs a, int r
     else if (a.beta_kind == 2) beta = ld_in(bt, ((long)chain * L + t) * a.dv + rowc);
     float eta = beta / (a.eps + n);
     float decay = 1.0f - eta * a.lambda;
-    if (t == 0 && !kp) {  // fresh sequence: S_0 = 0 and x_1 = 0 leave S_1 = 0
+    if (t == 0 && !kp && ks) {  // fresh sequence: S_0 = 0 and x_1 = 0 leave S_1 = 0
       eta = 0.0f;
       decay = 1.0f;
     }
@@ -140,7 +141,7 @@ hipError_t launch_dk(const SeqArgs& a, hipStream_t stream) {
 
 // The window-1 latest samples after a call, oldest first: slot h holds sample
 // s = L - (B-1) + h (0-based steps; sample s pairs x_s with y_s = v_s, x_s =
-// k_{s-1}, x_0 = k_prev or 0); s < 0 comes from the incoming history slot
+// k_{s-shift}, x_0 = k_prev or 0 when shift = 1); s < 0 comes from the incoming history slot
 // B-1+s (zero without one).  One thread per column walks the slots in
 // ascending order: in-place use (out == incoming history) reads slot L+h > h
 // before anything at or above slot h has been written.
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void history_out_kernel(SeqArgs a, T* xo, T* y
       T val = T(0);
       if (s >= 0) {
         if (!isx) val = v[(chain * L + s) * a.dv + col];
-        else if (s >= 1) val = k[(chain * L + s - 1) * a.dk + col];
+        else if (s >= a.key_shift) val = k[(chain * L + s - a.key_shift) * a.dk + col];
         else if (kp) val = kp[chain * a.dk + col];
       } else if (hin) {
         val = hin[(chain * NH + NH + s) * d + col];
