@@ -60,6 +60,11 @@ Functions
 ``falcon_history``      the B-1 latest samples after a call (the history the
                         next call of a Falcon-3/3A sequence needs).
 ``falcon_decode_step_window``  one step with a carried window history.
+``falcon_backward``     gradients of <dO, o> + <dS_L, S_L> + <dk_last, k_last>
+                        with respect to every input, by reverse-mode
+                        differentiation of the recurrence step by step (the
+                        pages give no gradients; this is the chain rule applied
+                        to the definition above).
 """
 from __future__ import annotations
 
@@ -307,3 +312,97 @@ def falcon_masked_parallel(variant, q, k, v, *, beta=0.5, lam=0.0, eps=1e-6, win
                         acc += float(S0[bi, hi, i] @ w)
                     o[bi, hi, t, i] = acc
     return o
+
+
+def falcon_backward(variant, q, k, v, dO, *, beta=0.5, lam=0.0, eps=1e-6, window=1,
+                    beta_t=None, k_prev=None, S0=None, same_step=False, dS_L=None,
+                    dk_last=None):
+    """Reverse-mode gradients of the recurrence.
+
+    The scalar being differentiated is  sum_t <dO_t, o_t> + <dS_L, S_L> +
+    <dk_last, k_last>  (dS_L and dk_last optional: the gradients arriving from a
+    later call of the same sequence).  Shapes as ``falcon_recurrence``; dO
+    [B, H, L, dv].  Returns a dict with dq, dk, dv and, when the input was given,
+    dbeta_t (same shape as beta_t), dk_prev and dS0.  A scalar beta gets no
+    gradient (it is a hyper-parameter here).
+
+    Each step S_t = a S_{t-1} + eta sum_j e_j x_j^T, o_t = S_t q_t is undone in
+    reverse order with the stored S_{t-1}: the adjoint dS of S_t gains dO_t q_t^T,
+    then flows to eta, to the window samples (x_j, y_j), to n_t and to S_{t-1}.
+    """
+    q, k, v, dO = _as64(q), _as64(k), _as64(v), _as64(dO)
+    beta_t, k_prev, S0 = _as64(beta_t), _as64(k_prev), _as64(S0)
+    _check_args(variant, window, q, k, v, beta_t)
+    Bz, H, L, dk = q.shape
+    dv = v.shape[-1]
+    regression = _REGRESSION[variant]
+    o, S_L, _, states = falcon_recurrence(variant, q, k, v, beta=beta, lam=lam, eps=eps,
+                                          window=window, beta_t=beta_t, k_prev=k_prev, S0=S0,
+                                          same_step=same_step, return_states=True)
+    x = _shift_keys(k, k_prev, same_step)
+    y = v
+    dx = np.zeros_like(x)
+    dy = np.zeros_like(y)
+    dq = np.zeros_like(q)
+    dbeta = None if beta_t is None else np.zeros_like(beta_t)
+    dS = np.zeros((Bz, H, dv, dk)) if dS_L is None else _as64(dS_L).copy()
+    S_init = np.zeros((Bz, H, dv, dk)) if S0 is None else S0
+    for t in range(L - 1, -1, -1):
+        S_t = states[:, :, t]
+        S_prev = states[:, :, t - 1] if t > 0 else S_init
+        # o_t = S_t q_t
+        dq[:, :, t] = np.matmul(np.swapaxes(S_t, -1, -2), dO[:, :, t][..., None])[..., 0]
+        dS = dS + dO[:, :, t][..., None] * q[:, :, t][:, :, None, :]
+        # the step's own quantities, recomputed from S_{t-1} as in the forward
+        lo = max(0, t - window + 1)
+        Xw = x[:, :, lo:t + 1]
+        Yw = y[:, :, lo:t + 1]
+        n = np.sum(Xw * Xw, axis=(-1, -2))
+        b = _beta_rows(beta, beta_t, t, (Bz, H), dv)
+        denom = eps + n
+        zero = denom == 0.0
+        denom_s = np.where(zero, 1.0, denom)
+        eta = np.where(zero[..., None], 0.0, b / denom_s[..., None])        # [B, H, dv]
+        a = 1.0 - eta * lam
+        E = Yw - np.matmul(Xw, np.swapaxes(S_prev, -1, -2)) if regression else Yw
+        write = np.matmul(np.swapaxes(E, -1, -2), Xw)                       # sum_j e_j x_j^T
+        # S_t = a S_prev + eta write   (a, eta per value row)
+        d_eta = np.sum(dS * (-lam * S_prev + write), axis=-1)               # [B, H, dv]
+        d_eta = np.where(zero[..., None], 0.0, d_eta)
+        dE = np.swapaxes(np.matmul(dS, np.swapaxes(Xw, -1, -2)), -1, -2) * eta[:, :, None, :]
+        dXw = np.matmul(E, eta[..., None] * dS)                              # from the write
+        dS_prev = a[..., None] * dS
+        if regression:   # E = Y - X S_prev^T
+            dS_prev = dS_prev - np.matmul(np.swapaxes(dE, -1, -2), Xw)
+            dXw = dXw - np.matmul(dE, S_prev)
+        dy[:, :, lo:t + 1] += dE
+        # eta = beta / (eps + n), n = sum of the window's squared norms
+        dn = -np.sum(d_eta * eta, axis=-1) / denom_s                         # [B, H]
+        dXw = dXw + 2.0 * dn[..., None, None] * Xw
+        dx[:, :, lo:t + 1] += dXw
+        if dbeta is not None:
+            g = d_eta / denom_s[..., None]
+            if dbeta.ndim == 4:
+                dbeta[:, :, t] = g
+            else:
+                dbeta[:, :, t] = np.sum(g, axis=-1)
+        dS = dS_prev
+    # x_t = k_{t-1} (x_1 = k_prev) or, same-step, x_t = k_t
+    dk_ = np.zeros_like(k)
+    dk_prev = None
+    if same_step:
+        dk_ += dx
+    else:
+        dk_[:, :, :-1] += dx[:, :, 1:]
+        if k_prev is not None:
+            dk_prev = dx[:, :, 0].copy()
+    if dk_last is not None and L > 0:
+        dk_[:, :, -1] += _as64(dk_last)
+    out = dict(dq=dq, dk=dk_, dv=dy)
+    if dbeta is not None:
+        out["dbeta_t"] = dbeta
+    if k_prev is not None and not same_step:
+        out["dk_prev"] = dk_prev
+    if S0 is not None:
+        out["dS0"] = dS
+    return out

@@ -401,3 +401,72 @@ def test_same_step_decode_equals_recurrence(variant):
         assert kp is None
         np.testing.assert_allclose(ot, o[:, :, t], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(St, S, rtol=1e-13, atol=1e-14)
+
+
+def _fd_loss(variant, inp, dO, dS_L, dk_last, kw):
+    o, S, kl = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], beta_t=inp.get("beta_t"),
+                                    k_prev=inp.get("k_prev"), S0=inp.get("S0"), **kw)
+    return float(np.sum(dO * o) + np.sum(dS_L * S) + np.sum(dk_last * kl))
+
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("same_step", [False, True])
+@pytest.mark.parametrize("carried", [False, True])
+def test_backward_matches_finite_differences(variant, same_step, carried):
+    # the backward is the chain rule through the recurrence; central differences
+    # of the (pinned) forward along random directions check every input's gradient
+    per_ch = variant in (fo.FALCON_2, fo.FALCON_2A)
+    window = _window(variant)
+    inp = _tiny(95 + variant, B=1, H=2, L=7, dk=4, dv=3, beta_per_channel=per_ch,
+                beta_per_token=not per_ch, with_k_prev=carried and not same_step,
+                with_S0=carried)
+    inp = {n: a.astype(np.float64) for n, a in inp.items()}
+    rng = np.random.default_rng(7 + variant)
+    dO = rng.standard_normal(inp["v"].shape)
+    dS_L = rng.standard_normal((1, 2, 3, 4))
+    dk_last = rng.standard_normal((1, 2, 4))
+    kw = dict(beta=None, lam=0.05, eps=1e-3, window=window, same_step=same_step)
+    g = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta_t=inp["beta_t"],
+                           k_prev=inp.get("k_prev"), S0=inp.get("S0"), dS_L=dS_L,
+                           dk_last=dk_last, **kw)
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta_t": "dbeta_t", "k_prev": "dk_prev",
+             "S0": "dS0"}
+    h = 1e-6
+    for name, gname in names.items():
+        if name not in inp:
+            assert gname not in g
+            continue
+        for _ in range(2):
+            u = rng.standard_normal(inp[name].shape)
+            plus = dict(inp); plus[name] = inp[name] + h * u
+            minus = dict(inp); minus[name] = inp[name] - h * u
+            fd = (_fd_loss(variant, plus, dO, dS_L, dk_last, kw)
+                  - _fd_loss(variant, minus, dO, dS_L, dk_last, kw)) / (2 * h)
+            an = float(np.sum(g[gname] * u))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (name, fd, an)
+
+
+def test_backward_of_one_step_by_hand():
+    # one Falcon-1 step from S0 with x = k_prev, scalar beta, loss = <dO, o> only:
+    # o = S1 q, S1 = a S0 + eta (y - S0 x) x^T; d/dq = S1^T dO and d/dv = eta (x.(S1-adjoint))
+    rng = np.random.default_rng(11)
+    dk, dv = 3, 2
+    S0 = rng.standard_normal((1, 1, dv, dk))
+    kp = rng.standard_normal((1, 1, dk))
+    q = rng.standard_normal((1, 1, 1, dk))
+    k = rng.standard_normal((1, 1, 1, dk))
+    v = rng.standard_normal((1, 1, 1, dv))
+    dO = rng.standard_normal((1, 1, 1, dv))
+    beta, lam, eps = 0.7, 0.1, 0.01
+    g = fo.falcon_backward(fo.FALCON_1, q, k, v, dO, beta=beta, lam=lam, eps=eps, k_prev=kp, S0=S0)
+    x, s0, qq, y, do = kp[0, 0], S0[0, 0], q[0, 0, 0], v[0, 0, 0], dO[0, 0, 0]
+    eta = beta / (eps + x @ x)
+    a = 1 - eta * lam
+    S1 = a * s0 + eta * np.outer(y - s0 @ x, x)
+    G = np.outer(do, qq)                       # adjoint of S1
+    np.testing.assert_allclose(g["dq"][0, 0, 0], S1.T @ do, rtol=1e-12)
+    np.testing.assert_allclose(g["dv"][0, 0, 0], eta * (G @ x), rtol=1e-12)
+    # S0 enters through a S0 and -eta (S0 x) x^T
+    np.testing.assert_allclose(g["dS0"][0, 0], a * G - eta * np.outer(G @ x, x), rtol=1e-12)
+    # k is not used by this step (it only becomes k_last)
+    np.testing.assert_array_equal(g["dk"], np.zeros_like(k))
