@@ -285,3 +285,167 @@ def chunk_forward_folded(regression, q, k, v, *, beta, lam, eps, window, beta_t=
         o[t0:t0 + c] = (g[:, None] * (Q @ S.T + Qy @ Y - Qx @ XS))[:c]
         S = g[c - 1] * (S + Fk.T @ X)
     return o, S
+
+
+def chunk_backward(regression, q, k, v, dO, *, beta, lam, eps, chunk, beta_t=None, k_prev=None,
+                   S0=None, same_step=False, dS_L=None, dk_last=None):
+    """Backward of the window-1 chunk form, per value row, one chain.
+
+    q, k [L, dk]; v, dO [L, dv]; beta_t None, [L] or [L, dv] (per channel).  The
+    derivation (chain rule through the chunk equations of the module docstring,
+    0-based steps t of a chunk, row i implicit, gC = g_{c-1}):
+      forward   r_t = y_t - g_{t-1} (s0.x_t); e = A^-1 r, A_ts = [t==s] + g_{t-1} G_ts zeta_s
+                (s < t); z = zeta e; o_t = g_t (q_t.s0 + sum_{s<=t} P_ts z_s);
+                s_end = gC (s0 + sum_s z_s x_s)
+      backward  dz_s = sum_{t>=s} P_ts g_t do_t + gC (x_s.ds_end);  de = zeta dz
+                dr = A^-T de:  dr_s = de_s - zeta_s sum_{t>s} G_ts w_t,  w_t = g_{t-1} dr_t
+                ds0 = gC ds_end + sum_t g_t do_t q_t - sum_t w_t x_t
+                dG_ts = -sum_i w_t z_s (t > s),  dP_ts = sum_i g_t do_t z_s (s <= t)
+                dq_t = sum_i g_t do_t s0 + sum_s dP_ts x_s
+                dx_t = sum_i (-w_t s0 + gC z_t ds_end) + sum_s (dG_ts + dG_st) x_s
+                       + sum_t' dP_t't q_t' + 2 dn_t x_t
+      scalars   dg_t += do_t o_t / g_t;  dg_{t-1} -= dr_t (h_t + s0.x_t), h_t = sum_{s<t} G_ts z_s;
+                dzeta_t = dz_t e_t - e_t sum_{t'>t} G_t't w_t';  dgC += ds_end.s_end / gC;
+                zeta = eta / g;  g_t = prod_{r<=t} a_r;  a = 1 - lambda eta;
+                eta = beta / (eps + n):  dbeta = deta / (eps + n),  dn = -sum_i deta eta / (eps + n)
+    Inner-product family: e = r = y (no solve, no terms through A or s0.x).
+    """
+    f64 = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    q, k, v, dO = f64(q), f64(k), f64(v), f64(dO)
+    beta_t, k_prev, S0, dS_L, dk_last = f64(beta_t), f64(k_prev), f64(S0), f64(dS_L), f64(dk_last)
+    L, dk = q.shape
+    dv = v.shape[-1]
+    x = np.zeros_like(k)
+    if same_step:
+        x[:] = k
+    else:
+        x[1:] = k[:-1]
+        if k_prev is not None:
+            x[0] = k_prev
+    fresh = (k_prev is None) and not same_step
+    nrm = np.sum(x * x, axis=-1)
+
+    def scalars(t0, c):
+        bt = np.empty((c, dv))
+        for t in range(c):
+            if beta_t is None:
+                bt[t] = beta
+            elif beta_t.ndim == 2:
+                bt[t] = beta_t[t0 + t]
+            else:
+                bt[t] = beta_t[t0 + t]
+        eta = bt / (eps + nrm[t0:t0 + c])[:, None]
+        if fresh and t0 == 0:
+            eta[0] = 0.0
+        a = 1.0 - lam * eta
+        g = np.cumprod(a, axis=0)                    # g_t, inclusive
+        gm = np.vstack([np.ones((1, dv)), g[:-1]])    # g_{t-1}
+        return eta, a, g, gm, eta / g
+
+    def forward_chunk(t0, c, S):
+        X, Q, Y = x[t0:t0 + c], q[t0:t0 + c], v[t0:t0 + c]
+        G = X @ X.T
+        P = np.tril(Q @ X.T)
+        eta, a, g, gm, zeta = scalars(t0, c)
+        XS = X @ S.T                                  # [c, dv] = s0 . x_t per row
+        E = np.zeros((c, dv))
+        Z = np.zeros((c, dv))
+        for t in range(c):
+            if regression:
+                h = G[t, :t] @ Z[:t]
+                E[t] = Y[t] - gm[t] * (XS[t] + h)
+            else:
+                E[t] = Y[t]
+            Z[t] = zeta[t] * E[t]
+        S_end = g[-1][:, None] * (S + Z.T @ X)
+        return dict(X=X, Q=Q, G=G, P=P, eta=eta, a=a, g=g, gm=gm, zeta=zeta, XS=XS, E=E, Z=Z,
+                    S=S, S_end=S_end)
+
+    # forward sweep: chunk-start states
+    starts = list(range(0, L, chunk))
+    S = np.zeros((dv, dk)) if S0 is None else S0.copy()
+    S_starts = []
+    for t0 in starts:
+        c = min(chunk, L - t0)
+        S_starts.append(S)
+        S = forward_chunk(t0, c, S)["S_end"]
+    # backward sweep
+    dq = np.zeros_like(q)
+    dx = np.zeros_like(x)
+    dy = np.zeros_like(v)
+    dbeta = None if beta_t is None else np.zeros_like(beta_t)
+    dS = np.zeros((dv, dk)) if dS_L is None else dS_L.copy()
+    for ci in range(len(starts) - 1, -1, -1):
+        t0 = starts[ci]
+        c = min(chunk, L - t0)
+        f = forward_chunk(t0, c, S_starts[ci])
+        X, Q, G, P, S0c = f["X"], f["Q"], f["G"], f["P"], f["S"]
+        eta, a, g, gm, zeta, E, Z = f["eta"], f["a"], f["g"], f["gm"], f["zeta"], f["E"], f["Z"]
+        dOc = dO[t0:t0 + c]
+        gC = g[-1]                                    # [dv]
+        QS = Q @ S0c.T                                # q_t . s0
+        ohat = QS + P @ Z                             # o_t / g_t
+        gdo = g * dOc                                 # g_t do_t
+        dg = dOc * ohat                               # from o_t = g_t ohat_t
+        dgC = np.sum(dS * f["S_end"], axis=1) / gC
+        XdS = X @ dS.T                                # x_s . ds_end  [c, dv]
+        dZ = P.T @ gdo + gC * XdS
+        dzeta = dZ * E
+        dE = zeta * dZ
+        if regression:
+            W = np.zeros((c, dv))
+            dR = np.zeros((c, dv))
+            for s in range(c - 1, -1, -1):
+                gs = G[s + 1:, s] @ W[s + 1:] if s + 1 < c else np.zeros(dv)
+                dR[s] = dE[s] - zeta[s] * gs
+                W[s] = gm[s] * dR[s]
+                dzeta[s] -= E[s] * gs
+            Hh = np.tril(G, -1) @ Z                   # h_t
+            dgm = -dR * (Hh + f["XS"])
+        else:
+            dR = dE
+            W = np.zeros((c, dv))
+            dgm = np.zeros((c, dv))
+        dy[t0:t0 + c] = dR
+        dS_prev = gC[:, None] * dS + gdo.T @ Q - W.T @ X
+        dG = -np.tril(W @ Z.T, -1)
+        dP = np.tril(gdo @ Z.T)
+        dq[t0:t0 + c] = gdo @ S0c + dP @ X
+        dxc = -W @ S0c + (gC * Z) @ dS + (dG + dG.T) @ X + dP.T @ Q
+        # scalars
+        deta = dzeta / g
+        dg = dg - dzeta * zeta / g
+        dg[-1] += dgC
+        dg[:-1] += dgm[1:]                            # g_{t-1} of step t is g_{t-1}
+        # g_t = prod_{r<=t} a_r  ->  da_r = sum_{t>=r} dg_t g_t / a_r
+        suffix = np.cumsum((dg * g)[::-1], axis=0)[::-1]
+        da = suffix / a
+        deta = deta - lam * da
+        if fresh and t0 == 0:
+            deta[0] = 0.0
+        den = eps + nrm[t0:t0 + c]
+        dn = -np.sum(deta * eta, axis=1) / den
+        dxc += 2.0 * dn[:, None] * X
+        dx[t0:t0 + c] += dxc
+        if dbeta is not None:
+            if dbeta.ndim == 2:
+                dbeta[t0:t0 + c] = deta / den[:, None]
+            else:
+                dbeta[t0:t0 + c] = np.sum(deta, axis=1) / den
+        dS = dS_prev
+    dk_ = np.zeros_like(k)
+    out = {}
+    if same_step:
+        dk_ += dx
+    else:
+        dk_[:-1] += dx[1:]
+        if k_prev is not None:
+            out["dk_prev"] = dx[0].copy()
+    if dk_last is not None:
+        dk_[-1] += dk_last
+    out.update(dq=dq, dk=dk_, dv=dy)
+    if dbeta is not None:
+        out["dbeta_t"] = dbeta
+    if S0 is not None:
+        out["dS0"] = dS
+    return out

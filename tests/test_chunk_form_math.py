@@ -8,7 +8,7 @@ import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import seq_inputs
-from chunk_form_model import chunk_forward, chunk_forward_folded, chunk_forward_wy
+from chunk_form_model import chunk_backward, chunk_forward, chunk_forward_folded, chunk_forward_wy
 
 pytestmark = pytest.mark.cpu
 
@@ -73,3 +73,31 @@ def test_key_folded_form_equals_recurrence(variant, carried_key):
                                     k_prev=inp["k_prev"][0, 0] if carried_key else None)
         np.testing.assert_allclose(o, o_ref[0, 0], rtol=1e-9, atol=1e-10)
         np.testing.assert_allclose(S, S_ref[0, 0], rtol=1e-9, atol=1e-10)
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_1, fo.FALCON_2, fo.FALCON_1A, fo.FALCON_2A])
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("carried,same_step", [(False, False), (True, False), (False, True),
+                                               (True, True)])
+def test_chunk_backward_equals_oracle_backward(variant, chunk, carried, same_step):
+    per_row = variant in (fo.FALCON_2, fo.FALCON_2A)
+    inp = seq_inputs(1, 1, 75, 8, 5, seed=900 + variant + chunk, dtype="bf16",
+                     beta_per_channel=per_row, beta_per_token=not per_row,
+                     with_k_prev=carried and not same_step, with_S0=carried, s_std=0.3)
+    rng = np.random.default_rng(3 + variant)
+    dO = rng.standard_normal((1, 1, 75, 5))
+    dS_L = rng.standard_normal((1, 1, 5, 8))
+    dk_last = rng.standard_normal((1, 1, 8))
+    kw = dict(beta=None, lam=0.02, eps=1e-6)
+    ref = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta_t=inp["beta_t"],
+                             k_prev=inp.get("k_prev"), S0=inp.get("S0"), same_step=same_step,
+                             dS_L=dS_L, dk_last=dk_last, **kw)
+    sq = lambda a: None if a is None else a[0, 0]
+    got = chunk_backward(fo.is_regression(variant), sq(inp["q"]), sq(inp["k"]), sq(inp["v"]),
+                         dO[0, 0], chunk=chunk, beta_t=sq(inp["beta_t"]),
+                         k_prev=sq(inp.get("k_prev")), S0=sq(inp.get("S0")),
+                         same_step=same_step, dS_L=dS_L[0, 0], dk_last=dk_last[0, 0], **kw)
+    assert set(got) == set(ref)
+    for name in ref:
+        np.testing.assert_allclose(got[name], ref[name][0, 0], rtol=1e-8, atol=1e-9,
+                                   err_msg=name)
