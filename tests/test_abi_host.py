@@ -29,13 +29,16 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(falcon_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:unsigned\s+long\s+long|\w+)\**\s+\**(falcon_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("falcon_fwd_recurrent", "falcon_fwd_chunk", "falcon_decode_step",
-              "falcon_abi_version", "falcon_status_string"):
+              "falcon_fwd_recurrent_ex", "falcon_fwd_chunk_ex", "falcon_decode_step_ex",
+              "falcon_bwd_chunk", "falcon_bwd_workspace_bytes", "falcon_abi_version",
+              "falcon_status_string"):
         assert n in names
 
 
@@ -211,3 +214,43 @@ def _dech(lib, **over):
 ])
 def test_decode_history_validation(lib, over, status):
     assert _dech(lib, **over) == status
+
+
+
+def _bwd(lib, **over):
+    a = dict(variant=0, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, batch=1,
+             heads=2, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2], k_prev=None,
+             S0=None, dO=P[3], dS_L=None, dk_last=None, dq=P[4], dk_=P[5], dv_=P[6],
+             dbeta_t=None, dk_prev=None, dS0=None, ws=P[7], wsb=1 << 26)
+    a.update(over)
+    return lib.falcon_bwd_chunk(a["variant"], a["flags"], a["beta"], a["beta_t"], a["beta_kind"],
+                                a["lam"], a["eps"], a["batch"], a["heads"], a["seqlen"], a["dk"],
+                                a["dv"], a["dtype"], a["q"], a["k"], a["v"], a["k_prev"], a["S0"],
+                                a["dO"], a["dS_L"], a["dk_last"], a["dq"], a["dk_"], a["dv_"],
+                                a["dbeta_t"], a["dk_prev"], a["dS0"], a["ws"], a["wsb"], None)
+
+
+def test_backward_workspace_size(lib):
+    # one fp32 state per 16-token chunk and (batch, head)
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32) == 2 * 3 * 7 * 32 * 64 * 4
+    assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32) == 0
+    assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(variant=2), UNSUPPORTED),                  # Falcon-3: no backward yet
+    (dict(dk=128), UNSUPPORTED),
+    (dict(flags=2), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(wsb=1024), INVALID),                       # workspace too small
+    (dict(dbeta_t=P[8]), INVALID),                   # scalar beta has no gradient
+    (dict(dk_prev=P[8]), INVALID),                   # no k_prev
+    (dict(dS0=P[8]), INVALID),                       # no S0
+    (dict(dq=P[0]), INVALID),                        # output aliases q
+    (dict(ws=P[4]), INVALID),                        # workspace aliases dq
+    (dict(dk_=P[4]), INVALID),                       # two outputs alias
+    (dict(S0=P[9]), INVALID),                        # state without the carried key
+])
+def test_backward_validation(lib, over, status):
+    assert _bwd(lib, **over) == status

@@ -476,6 +476,47 @@ def test_decode_same_step(variant):
 
 
 # ---------------------------------------------------------------------------
+# backward of the window-1 chunk form
+
+def _grad_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_2, fw.FALCON_1A, fw.FALCON_2A])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 16), (16, 64)])
+@pytest.mark.parametrize("carried,same_step", [(False, False), (True, False), (True, True)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_small(variant, dk, dv, carried, same_step, dtype):
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    L = 75
+    inp = seq_inputs(2, 2, L, dk, dv, seed=800 + 5 * variant + dk + dv, dtype=dtype,
+                     beta_per_channel=per_ch, beta_per_token=not per_ch,
+                     with_k_prev=carried and not same_step, with_S0=carried, s_std=0.2)
+    rng = np.random.default_rng(801 + variant)
+    dO = rng.standard_normal((2, 2, L, dv)).astype(np.float32)
+    dS_L = rng.standard_normal((2, 2, dv, dk)).astype(np.float32)
+    dk_last = rng.standard_normal((2, 2, dk)).astype(np.float32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda n: to_dev(torch, inp[n], dt) if n in inp else None
+    f32 = lambda a: to_dev(torch, a, torch.float32)
+    got = fw.bwd_chunk(dev("q"), dev("k"), dev("v"), f32(dO), variant=variant, beta=None,
+                       lam=0.02, eps=1e-6, beta_t=dev("beta_t"), k_prev=dev("k_prev"),
+                       S0=to_dev(torch, inp["S0"], torch.float32) if "S0" in inp else None,
+                       dS_L=f32(dS_L), dk_last=f32(dk_last), same_step=same_step)
+    torch.cuda.synchronize()
+    ref = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta=None, lam=0.02,
+                             eps=1e-6, beta_t=inp["beta_t"], k_prev=inp.get("k_prev"),
+                             S0=inp.get("S0"), same_step=same_step, dS_L=dS_L, dk_last=dk_last)
+    assert set(got) == set(ref)
+    errs = {n: _grad_err(got[n].cpu().numpy(), ref[n]) for n in ref}
+    print("backward v%d dk %d dv %d %s: %s" % (variant, dk, dv, dtype,
+                                               {n: "%.2e" % e for n, e in errs.items()}))
+    assert max(errs.values()) <= TOL_FP32_MATH, errs
+
+
+# ---------------------------------------------------------------------------
 # error paths through the binding
 
 def test_binding_rejects_unsupported():

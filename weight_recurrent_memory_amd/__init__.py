@@ -6,6 +6,6 @@ load the library; the first call does, and fails loudly if it is missing.
 """
 from .binding import (  # noqa: F401
     FALCON_1, FALCON_2, FALCON_3, FALCON_1A, FALCON_2A, FALCON_3A,
-    VARIANT_NAMES, FalconError, decode_step, fwd_chunk, fwd_recurrent, library_path,
+    VARIANT_NAMES, FalconError, bwd_chunk, decode_step, fwd_chunk, fwd_recurrent, library_path,
     load_library,
 )

@@ -62,6 +62,12 @@ def load_library():
     lib.falcon_decode_step_ex.restype = i
     lib.falcon_decode_step_ex.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp]
+    lib.falcon_bwd_workspace_bytes.restype = ctypes.c_ulonglong
+    lib.falcon_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.falcon_bwd_chunk.restype = i
+    lib.falcon_bwd_chunk.argtypes = [i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_ulonglong,
+                                     vp]
     _LIB = lib
     return lib
 
@@ -235,4 +241,50 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
                                     dcode, _ptr(S), _ptr(k_prev), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(out), _stream(torch, dev, stream))
     _raise(lib, "falcon_decode_step", status)
+    return out
+
+
+def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, beta_t=None, k_prev=None,
+              S0=None, dS_L=None, dk_last=None, same_step=False, stream=None):
+    """Gradients of sum <dO, o> + <dS_L, S_L> + <dk_last, k_last> for the window-1
+    chunk form.  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
+    dk_prev / dS0 when beta_t / k_prev / S0 are given."""
+    import torch
+    lib = load_library()
+    variant = _variant(variant)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    dcode = _dtype_code(torch, q)
+    f32 = torch.float32
+    for name, t, shape, tdt in (("q", q, (B, H, L, dk), dt), ("k", k, (B, H, L, dk), dt),
+                                ("v", v, (B, H, L, dv), dt), ("dO", dO, (B, H, L, dv), f32),
+                                ("k_prev", k_prev, (B, H, dk), dt), ("S0", S0, (B, H, dv, dk), f32),
+                                ("dS_L", dS_L, (B, H, dv, dk), f32),
+                                ("dk_last", dk_last, (B, H, dk), f32)):
+        _check(torch, name, t, shape, tdt, dev)
+    kind = _BETA_SCALAR
+    if beta_t is not None:
+        kind = _BETA_TOKEN if beta_t.dim() == 3 else _BETA_CHANNEL
+        _check(torch, "beta_t", beta_t, (B, H, L) if kind == _BETA_TOKEN else (B, H, L, dv), dt,
+               dev)
+    out = dict(dq=torch.empty((B, H, L, dk), device=dev, dtype=f32),
+               dk=torch.empty((B, H, L, dk), device=dev, dtype=f32),
+               dv=torch.empty((B, H, L, dv), device=dev, dtype=f32))
+    if beta_t is not None:
+        out["dbeta_t"] = torch.empty(beta_t.shape, device=dev, dtype=f32)
+    if k_prev is not None and not same_step:
+        out["dk_prev"] = torch.empty((B, H, dk), device=dev, dtype=f32)
+    if S0 is not None:
+        out["dS0"] = torch.empty((B, H, dv, dk), device=dev, dtype=f32)
+    wsb = int(lib.falcon_bwd_workspace_bytes(B, H, L, dk, dv))
+    ws = torch.empty((max(wsb, 16) // 4 + 4,), device=dev, dtype=f32)
+    status = lib.falcon_bwd_chunk(
+        variant, SAME_STEP if same_step else 0, float(beta if beta is not None else 0.0),
+        _ptr(beta_t), kind, float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k),
+        _ptr(v), _ptr(k_prev), _ptr(S0), _ptr(dO), _ptr(dS_L), _ptr(dk_last), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dbeta_t")), _ptr(out.get("dk_prev")),
+        _ptr(out.get("dS0")), _ptr(ws), wsb, _stream(torch, dev, stream))
+    _raise(lib, "falcon_bwd_chunk", status)
     return out

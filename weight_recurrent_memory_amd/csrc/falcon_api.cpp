@@ -298,3 +298,68 @@ FALCON_EXPORT int falcon_decode_step_ex(int variant, int window, int flags, floa
   return decode_step(variant, window, flags, beta, beta_t, beta_kind, lambda, eps, nseq, heads,
                      dk, dv, dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }
+
+FALCON_EXPORT unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk,
+                                                            int dv) {
+  if (batch < 1 || heads < 1 || seqlen < 1 || !supported_dim(dk) || !supported_dim(dv)) return 0;
+  return (unsigned long long)falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv);
+}
+
+FALCON_EXPORT int falcon_bwd_chunk(int variant, int flags, float beta, const void* beta_t,
+                                   int beta_kind, float lambda, float eps, int batch, int heads,
+                                   int seqlen, int dk, int dv, int dtype, const void* q,
+                                   const void* k, const void* v, const void* k_prev,
+                                   const float* S0, const float* dO, const float* dS_L,
+                                   const float* dk_last, float* dq, float* dk_out, float* dv_out,
+                                   float* dbeta_t, float* dk_prev, float* dS0, void* workspace,
+                                   unsigned long long workspace_bytes, void* stream) {
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
+  const int key_shift = (flags & FALCON_SAME_STEP) ? 0 : 1;
+  // the forward arguments are checked as the forward checks them (dO takes the
+  // place of o: same shape, and it must not overlap an input either)
+  falcon::SeqArgs a{variant, 1, is_regression(variant), beta, beta_t, beta_kind, lambda, eps,
+                    batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0,
+                    const_cast<float*>(dO), nullptr, 0, nullptr, nullptr, key_shift};
+  int st = check_seq(a, true);
+  if (st != FALCON_OK) return st;
+  if (!dq || !dk_out || !dv_out || !workspace) return FALCON_ERR_INVALID_ARG;
+  if (dbeta_t && beta_kind == FALCON_BETA_SCALAR) return FALCON_ERR_INVALID_ARG;
+  if (dk_prev && (!k_prev || !key_shift)) return FALCON_ERR_INVALID_ARG;
+  if (dS0 && !S0) return FALCON_ERR_INVALID_ARG;
+  const void* ptrs[] = {dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
+  if (window_variant(variant)) return FALCON_ERR_UNSUPPORTED;
+  if (dk > 64 || dv > 64) return FALCON_ERR_UNSUPPORTED;
+  const size_t es = dtype == FALCON_BF16 ? 2 : 4;
+  const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
+  const size_t need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv);
+  if (workspace_bytes < need) return FALCON_ERR_INVALID_ARG;
+  Range outs[] = {{dq, BH * L * dk * 4},
+                  {dk_out, BH * L * dk * 4},
+                  {dv_out, BH * L * dv * 4},
+                  {dbeta_t, BH * L * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * 4},
+                  {dk_prev, BH * dk * 4},
+                  {dS0, BH * dv * dk * 4},
+                  {workspace, need}};
+  Range ins[] = {{q, BH * L * dk * es},
+                 {k, BH * L * dk * es},
+                 {v, BH * L * dv * es},
+                 {k_prev, BH * dk * es},
+                 {S0, BH * dv * dk * 4},
+                 {beta_t, BH * L * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * es},
+                 {dO, BH * L * dv * 4},
+                 {dS_L, BH * dv * dk * 4},
+                 {dk_last, BH * dk * 4}};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = i + 1; j < 7; ++j)
+      if (overlap(outs[i], outs[j])) return FALCON_ERR_INVALID_ARG;
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return FALCON_ERR_INVALID_ARG;
+  }
+  falcon::BwdArgs b{is_regression(variant), key_shift, beta, beta_t, beta_kind, lambda, eps,
+                    batch, heads, (long)seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO, dS_L,
+                    dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0,
+                    static_cast<float*>(workspace)};
+  return finish_launch(falcon::launch_backward(b, (hipStream_t)stream));
+}

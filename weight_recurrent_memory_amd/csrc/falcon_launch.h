@@ -54,6 +54,37 @@ struct DecodeArgs {
   int key_shift;     // 1: x = k_prev (then k_prev <- k); 0: x = k, k_prev unused
 };
 
+// Backward of the window-1 chunk form (falcon_backward.hip).
+struct BwdArgs {
+  int regression;
+  int key_shift;
+  float beta;
+  const void* beta_t;
+  int beta_kind;
+  float lambda, eps;
+  int batch, heads;
+  long seqlen;
+  int ndk, ndv;      // sizes
+  int dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_prev;
+  const float* S0;
+  const float* dO;
+  const float* dS_L;     // may be null
+  const float* dk_last;  // may be null
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dbeta_t;        // may be null
+  float* dk_prev;        // may be null
+  float* dS0;            // may be null
+  float* workspace;      // backward_workspace_bytes(...)
+};
+size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
 // window-1 chunk form, per-channel gains (falcon_chunk_w1.hip); cs = sub-chunk length
