@@ -14,8 +14,9 @@ Prints one JSON line.  Besides the contract fields it carries
   roofline      the chunk kernel against HBM bandwidth (algorithmic bytes)
   cpu_baseline  the fp64 oracle on the host cores, same workload
   secondary     the other workloads: Falcon-1A, per-channel Falcon-2, windowed
-                Falcon-3/3A at d = 128, the decode step (state GB/s), a copy
-                kernel for attainable bandwidth, and model-FLOP utilization.
+                Falcon-3/3A at d = 128, the backward of the headline workload,
+                the decode step (state GB/s), a copy kernel for attainable
+                bandwidth, and model-FLOP utilization.
 """
 from __future__ import annotations
 
@@ -96,7 +97,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="profiling aid: run only this leg "
-                    "(headline|falcon1a|percol|window|decode|copy)")
+                    "(headline|falcon1a|percol|window|backward|decode|copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Falcon state update has no cross-GPU "
@@ -201,6 +202,28 @@ def main():
                             "model_tflops": fl / r["sec"] / 1e12,
                             "mfma_model_frac": fl / r["sec"] / 1e12 / BF16_PEAK_TFLOPS}
             del r
+            torch.cuda.empty_cache()
+        if args.only in (None, "backward"):
+            # gradients of the headline workload: q, k, v bf16 and dO fp32 read, dq, dk,
+            # dv fp32 written (the per-chunk state checkpoints in the workspace are
+            # extra traffic, not counted)
+            cfg = WORKLOADS[head_name]
+            B, H, L, dk, dv = cfg["shape"]
+            inp = head_inp if head_inp is not None else seq_inputs(B, H, L, dk, dv, seed=cfg["seed"],
+                                                                  dtype="bf16")
+            q, k, v = (up(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+            dO = torch.randn((B, H, L, dv), device=dev, dtype=torch.float32,
+                             generator=torch.Generator(device=dev).manual_seed(7))
+            fn = lambda: fw.bwd_chunk(q, k, v, dO, variant=fw.FALCON_1, beta=cfg["beta"],
+                                      lam=cfg["lam"], eps=cfg["eps"])
+            sec = time_calls(fn, 10, 2)
+            nbytes = B * H * L * ((2 * dk + dv) * 2 + dv * 4 + (2 * dk + dv) * 4)
+            sec_out["backward"] = {"workload": head_name, "variant": "falcon1",
+                                   "ms_per_call": sec * 1e3, "tokens_per_s": B * L / sec,
+                                   "hbm_gbs": nbytes / sec / 1e9,
+                                   "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": nbytes}
+            del q, k, v, dO
             torch.cuda.empty_cache()
         if args.only in (None, "decode"):
             cfg = WORKLOADS["decode_512x12x64"]

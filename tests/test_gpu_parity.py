@@ -516,6 +516,27 @@ def test_backward_small(variant, dk, dv, carried, same_step, dtype):
     assert max(errs.values()) <= TOL_FP32_MATH, errs
 
 
+def test_backward_8x12x2048x64_sampled():
+    """Headline workload: all chains on the GPU, two chains recomputed by the oracle."""
+    cfg = WORKLOADS["chunk_8x12x2048x64"]
+    B, H, L, dk, dv = cfg["shape"]
+    inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16")
+    rng = np.random.default_rng(809)
+    dO = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    dt = torch.bfloat16
+    got = fw.bwd_chunk(*(to_dev(torch, inp[n], dt) for n in ("q", "k", "v")),
+                       to_dev(torch, dO, torch.float32), variant=fw.FALCON_1, beta=cfg["beta"],
+                       lam=cfg["lam"], eps=cfg["eps"])
+    torch.cuda.synchronize()
+    chains = np.array([5, B * H - 1])
+    sel = lambda a: a.reshape((-1,) + a.shape[2:])[chains][:, None]
+    ref = fo.falcon_backward(fw.FALCON_1, sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(dO),
+                             beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"])
+    errs = {n: _grad_err(sel(got[n].cpu().numpy()), ref[n]) for n in ref}
+    print("backward 8x12x2048x64 chains %s: %s" % (list(chains), {n: "%.2e" % e for n, e in errs.items()}))
+    assert max(errs.values()) <= 1e-3, errs
+
+
 # ---------------------------------------------------------------------------
 # error paths through the binding
 
