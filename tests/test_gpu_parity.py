@@ -538,6 +538,43 @@ def test_backward_8x12x2048x64_sampled():
 
 
 # ---------------------------------------------------------------------------
+# short sequences against the masked-parallel evaluation (explainer §3)
+
+@pytest.mark.parametrize("variant", ALL)
+@pytest.mark.parametrize("same_step", [False, True])
+def test_short_sequence_matches_masked_parallel(variant, same_step):
+    """For L <= 64 the chunk form is the masked-parallel system itself (causally
+    masked Gram and q.x over the whole sequence, one triangular solve); checked
+    against the oracle's transition-product expansion, which never forms a
+    residual."""
+    per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
+    win = _win(variant, 2)
+    L, dk, dv = 24, 16, 16
+    inp = seq_inputs(1, 2, L, dk, dv, seed=740 + variant, dtype="bf16", with_S0=True,
+                     beta_per_channel=per_ch, beta_per_token=not per_ch, s_std=0.2)
+    dt = torch.bfloat16
+    q, k, v, bt = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "beta_t"))
+    S0 = to_dev(torch, inp["S0"], torch.float32)
+    extra = {}
+    if win > 1:   # a windowed state travels with its history (zero: none)
+        extra = dict(x_hist=torch.zeros((1, 2, win - 1, dk), device="cuda", dtype=dt),
+                     y_hist=torch.zeros((1, 2, win - 1, dv), device="cuda", dtype=dt))
+    kp = None
+    if not same_step:   # a live state needs the key it pairs with the first value
+        kp = to_dev(torch, inp["k"][:, :, -1], dt)
+    o = fw.fwd_chunk(q, k, v, variant=variant, beta=None, lam=0.02, eps=1e-6, chunk=64,
+                     window=win, beta_t=bt, S0=S0, k_prev=kp, same_step=same_step, **extra)
+    torch.cuda.synchronize()
+    kp_ref = None if same_step else inp["k"][:, :, -1]
+    o_ref = fo.falcon_masked_parallel(variant, inp["q"], inp["k"], inp["v"], beta=None, lam=0.02,
+                                      eps=1e-6, window=win, beta_t=inp["beta_t"], k_prev=kp_ref,
+                                      S0=inp["S0"], same_step=same_step)
+    err, zok = token_normwise_err(o.cpu().numpy(), o_ref)
+    print("masked-parallel v%d same_step %d: o err %.3e" % (variant, same_step, err))
+    assert zok and err <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
 # error paths through the binding
 
 def test_binding_rejects_unsupported():
