@@ -229,9 +229,8 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  * fp32 with the chunk-start states recomputed by a forward sweep.
  *
  * falcon_bwd_workspace_bytes - bytes of device workspace falcon_bwd_chunk needs
- *   (per 16-token chunk and (batch, head): the fp32 start state, S0 x, the
- *   Gram, the inverted triangular factor and five per-step scalars); 0 for
- *   invalid sizes.
+ *   (per 16-token chunk and (batch, head), fp32: the chunk-start state
+ *   (dv x dk), S0 x (16 x dv) and the key Gram (16 x 16)); 0 for invalid sizes.
  *
  * falcon_bwd_chunk
  *   variant ... k_prev, S0, flags   as falcon_fwd_chunk_ex (window 1; flags 0 or

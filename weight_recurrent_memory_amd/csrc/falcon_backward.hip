@@ -27,16 +27,18 @@
 // forward sweep over 16-step chunks stores each chunk's starting state in the
 // caller's workspace; the backward sweep walks the chunks in reverse, reloads
 // that state, recomputes the chunk's forward quantities and carries dS.  Per
-// chunk: dk-long dot products (Gram, q.x, S0 x, S0 q, dS x) by all threads;
-// then, with gains shared by the value rows, one wave forms the scalars and
-// T = A^-1 and the waves share E = T R, its transpose dR = T^T dE and the
-// per-step sums over rows that feed the scalar chain; with per-channel gains A
-// differs per row and the sweeps run on one lane per value row.  Last the sums
-// over rows (dG, dP, dn) and the dk-wide products (dq, dx, dS).  Every product
-// is a 16x16 output tile on the fp32 matrix cores (v_mfma_f32_16x16x4_f32,
-// exact fp32 products): with the K index of step j of a 16-wide block taken as
+// chunk: dk-long dot products (Gram, q.x, S0 x, S0 q, dS x) on the matrix
+// cores; then each value row runs its own triangular sweeps (forward for z,
+// transposed for dr) and its scalar chain on one 16-lane row, lane t = step t,
+// with DPP broadcasts and shifts in place of LDS round trips, so shared,
+// per-token and per-channel gains take the same path.  Last the sums over rows
+// (dG, dP, dn) and the dk-wide products (dq, dx, dS).  Every product is a 16x16
+// output tile on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32
+// products): with the K index of step j of a 16-wide block taken as
 // 4 (lane / 16) + j, a lane feeds four steps from one 16-byte LDS read where
-// the operand is contiguous in K.  Arithmetic is fp32 throughout.
+// the operand is contiguous in K.  The chunk-start records (state, S0 x, Gram)
+// written by the forward sweep come back through the workspace.  Arithmetic is
+// fp32 throughout.
 #include "falcon_device.h"
 #include "falcon_launch.h"
 
@@ -55,28 +57,25 @@ struct BwdLds {
   float Q[BC][DK + 4];
   float Y[BC][DV + 4];        // values
   float dO[BC][DV + 4];
-  float bt[BC][DV];           // per-channel gain per step and row
-  float bts[BC];              // shared gain per step
+  float bt[BC][DV];           // gain per step and row
   float nrm[BC];
   float G[BC][BC + 4];        // strictly lower
   float P[BC][BC + 4];        // lower incl. diagonal
-  float Tm[BC][BC + 4];       // A^-1 (shared gains)
   float XS[BC][DV + 4];       // s0_i . x_t
   float QS[BC][DV + 4];       // s0_i . q_t
   float XdS[BC][DV + 4];      // ds_i . x_t
   float sds[DV];              // s0_i . ds_i
-  float E[BC][DV + 4];        // residuals (shared gains)
+  float E[BC][DV + 4];        // residuals
   float dZ[BC][DV + 4];
   float H[BC][DV + 4];        // sum_{s<t} G_ts z_s
   float Z[BC][DV + 4];
   float W[BC][DV + 4];        // gm_t dr_t (regression), 0 (inner product)
   float GD[BC][DV + 4];       // g_t do_t
-  float DE[BC][DV + 4];       // d eta (per channel)
+  float DE[BC][DV + 4];       // d eta
+  float DGO[BC][DV + 4];      // do_t (o_t / g_t)
   float ETA[BC][DV + 4];
   float dxp[BC][DK + 4];      // partial dx
   float gC[DV];
-  float sv[5][BC];            // shared scalars: eta, a, g, gm, zeta
-  float part[4][DV / 16][BC];  // per row tile: sums over its 16 rows (dO o/g, z XdS, dgm, dzeta)
   float dG[BC][BC + 4];
   float dP[BC][BC + 4];
   float dn[BC];
@@ -89,24 +88,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// acc + (g of lane N of the same 16-lane row) * r: one DPP multiply-add; g comes
-// straight from LDS (never written by the vector ALU, so no DPP wait states)
-template <int N>
-__device__ __forceinline__ float fmac_bcast(float acc, float g, float r) {
-  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(g), "v"(r), "i"(N));
-  return acc;
-}
-// forward substitution x_M = rhs_M - om_M acc_M, acc_r += g_M[r] zs_M x_M
-// (r > M), steps M.. of a 16-unknown system; lane m of a 16-lane row holds g_m[]
-template <int M>
-__device__ __forceinline__ void sweep16(float (&rhs)[16], float (&acc)[16], const float (&g)[16], const float (&om)[16],
-                                        const float (&zs)[16]) {
-  rhs[M] = __builtin_fmaf(-om[M], acc[M], rhs[M]);
-  const float xm = zs[M] * rhs[M];
-#pragma unroll
-  for (int r = M + 1; r < 16; ++r) acc[r] = fmac_bcast<M>(acc[r], g[r], xm);
-  if constexpr (M < 15) sweep16<M + 1>(rhs, acc, g, om, zs);
-}
 // v times the v of lane - N in the same 16-lane row (lanes whose source is
 // outside the row keep v: the DPP bounds rule disables them)
 template <int N>
@@ -118,6 +99,44 @@ template <int N>
 __device__ __forceinline__ float row_shr_fill(float v, float fill) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
                                                              0x110 + N, 0xF, 0xF, false));
+}
+
+// acc + g * (v of lane N of the same 16-lane row) with v just written by the
+// vector ALU (the nop gives the two wait states a DPP read of it needs)
+template <int N>
+__device__ __forceinline__ float fmac_bcast_nop(float acc, float v, float g) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc) : "v"(v), "v"(g), "i"(N));
+  return acc;
+}
+// v of lane 15 of the same 16-lane row on every lane of the row
+__device__ __forceinline__ float row_last(float v) {
+  float r;
+  asm("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:15 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ float row_shl_fill(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             0x100 + N, 0xF, 0xF, false));
+}
+// Per-row sweeps, one value row per 16-lane row, lane t = step t of the chunk.
+// Forward: e_t = y_t - gm_t (xs_t + acc_t), z_t = zeta_t e_t with acc_t =
+// sum_{s<t} G_ts z_s; every lane forms its candidate z and step M takes lane M's
+// (grow = the lane's Gram row, zero at and above the diagonal).
+template <int M>
+__device__ __forceinline__ void fsweep(float& acc, const float (&grow)[16], float y, float xs, float gm, float zeta) {
+  const float zc = zeta * (y - gm * (xs + acc));
+  acc = fmac_bcast_nop<M>(acc, zc, grow[M]);
+  if constexpr (M < 15) fsweep<M + 1>(acc, grow, y, xs, gm, zeta);
+}
+// Transposed: dr_s = zeta_s (dz_s - acc2_s), w_s = gm_s dr_s with acc2_s =
+// sum_{t>s} G_ts w_t, steps M = 15 .. 0 (gcol = the lane's Gram column)
+template <int M>
+__device__ __forceinline__ void bsweep(float& acc2, const float (&gcol)[16], float dz, float gm, float zeta) {
+  const float wc = gm * zeta * (dz - acc2);
+  acc2 = fmac_bcast_nop<M>(acc2, wc, gcol[M]);
+  if constexpr (M > 0) bsweep<M - 1>(acc2, gcol, dz, gm, zeta);
 }
 
 // raw 16-byte register images of four elements (converted only when stored
@@ -172,7 +191,7 @@ __device__ __forceinline__ floatx4 mtile(floatx4 acc, int lane, FA fa, FB fb) {
   return acc;
 }
 
-template <typename T, int DK, int DV, bool PERROW>
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   using SM = BwdLds<DK, DV>;
   constexpr int GX = BC * DK / 4, GY = BC * DV / 4, GS = DV * DK / 4;
@@ -194,17 +213,16 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   const bool fresh = ks == 1 && kpg == nullptr;
   const long qk_base = chain * L * DK;
   const long v_base = chain * L * DV;
-  // workspace per chunk: start state, S0 x, Gram, (shared gains) T and scalars
-  constexpr int WS_XS = DV * DK, WS_G = WS_XS + BC * DV, WS_T = WS_G + BC * BC;
-  constexpr int WS_SV = WS_T + BC * BC, WS_CHUNK = WS_SV + 5 * BC;
+  // workspace per chunk: start state, S0 x, Gram
+  constexpr int WS_XS = DV * DK, WS_G = WS_XS + BC * DV, WS_CHUNK = WS_G + BC * BC;
   float* __restrict__ ws = a.workspace + chain * (long)nch * WS_CHUNK;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   // ---- chunk inputs: issue_chunk starts every global load of a chunk into
   // registers (bwd: also q, dO and the chunk's workspace record: start state,
-  // S0 x, Gram, T, scalars); commit_chunk stores them to LDS.  A chunk's loads
+  // S0 x, Gram); commit_chunk stores them to LDS.  A chunk's loads
   // are issued one chunk ahead, so they fly while the previous chunk computes.
-  constexpr int NG = 2 * GX + 2 * GY + (PERROW ? GY : 0) + WS_CHUNK / 4;
+  constexpr int NG = 2 * GX + 2 * GY + GY + WS_CHUNK / 4;
   constexpr int NPER = (NG + BNT - 1) / BNT;
   // buffer resources (per chain; a range-checked load past the end, or at the
   // parked offset, returns 0), so every load is issued unconditionally
@@ -218,8 +236,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   const auto rsq = rsrc(qg + qk_base, L * DK * ES);
   const auto rsv = rsrc(vg + v_base, L * DV * ES);
   const auto rsdo = rsrc(a.dO + v_base, L * DV * 4);
-  const auto rsb = PERROW ? rsrc(bg + v_base, L * DV * ES)
-                         : (a.beta_kind == 1 ? rsrc(bg + chain * L, L * ES) : rsrc(vg, 0));
+  const auto rsb = a.beta_kind == 2 ? rsrc(bg + v_base, L * DV * ES)
+                                    : (a.beta_kind == 1 ? rsrc(bg + chain * L, L * ES) : rsrc(vg, 0));
   const auto rsws = rsrc(ws, (long)nch * WS_CHUNK * 4);
   auto ldr_t = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
     if constexpr (sizeof(T) == 2) {
@@ -234,7 +252,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  auto issue_chunk = [&](uint4 (&val)[NPER], uint32_t& bval, int ci, bool bwd) {
+  auto issue_chunk = [&](uint4 (&val)[NPER], int ci, bool bwd) {
     const long t0 = (long)ci * BC;
     const int c = (int)((L - t0) < BC ? (L - t0) : BC);
 #pragma unroll
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         } else {
           v = ldr_t(rsq, (bwd && t < c) ? (uint32_t)((st * DK + k4) * ES) : PARKED);
         }
-      } else if (g < 2 * GX + 2 * GY + (PERROW ? GY : 0)) {
+      } else if (g < 2 * GX + 2 * GY + GY) {
         const int r0 = g - 2 * GX;
         const int which = r0 / GY, r = r0 % GY;
         const int t = r / (DV / 4), i4 = 4 * (r % (DV / 4));
@@ -259,18 +277,23 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         const bool in = t < c;
         if (which == 0) v = ldr_t(rsv, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
         else if (which == 1) v = ldr_f(rsdo, (in && bwd) ? (uint32_t)((st * DV + i4) * 4) : PARKED);
-        else v = ldr_t(rsb, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
+        else if (a.beta_kind == 2) v = ldr_t(rsb, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
+        else if (a.beta_kind == 1) {   // per-token gain of step t, for every row
+          uint32_t b;
+          if constexpr (sizeof(T) == 2) b = __builtin_amdgcn_raw_buffer_load_b16(rsb, in ? (uint32_t)(st * ES) : PARKED, 0, 0);
+          else b = __builtin_amdgcn_raw_buffer_load_b32(rsb, in ? (uint32_t)(st * ES) : PARKED, 0, 0);
+          v = make_uint4(b, 0u, 0u, 0u);
+        } else {
+          v = make_uint4(0u, 0u, 0u, 0u);
+        }
       } else {
         const int e = 4 * (g - (NG - WS_CHUNK / 4));
         v = ldr_f(rsws, (bwd && g < NG) ? (uint32_t)(((long)ci * WS_CHUNK + e) * 4) : PARKED);
       }
       val[u] = v;
     }
-    bval = 0u;
-    if (!PERROW && a.beta_kind == 1)
-      bval = __builtin_amdgcn_raw_buffer_load_b16(rsb, (tid < c && tid < BC) ? (uint32_t)((t0 + tid) * ES) : PARKED, 0, 0);
   };
-  auto commit_chunk = [&](const uint4 (&val)[NPER], uint32_t bval, int ci, bool bwd) {
+  auto commit_chunk = [&](const uint4 (&val)[NPER], int ci, bool bwd) {
 #pragma unroll
     for (int u = 0; u < NPER; ++u) {
       const int g = tid + u * BNT;
@@ -278,13 +301,26 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         const int r = g < GX ? g : g - GX;
         const int t = r / (DK / 4), k4 = 4 * (r % (DK / 4));
         *reinterpret_cast<float4*>(g < GX ? &sm.X[t][k4] : &sm.Q[t][k4]) = cvt4(val[u], kg);
-      } else if (g < 2 * GX + 2 * GY + (PERROW ? GY : 0)) {
+      } else if (g < 2 * GX + 2 * GY + GY) {
         const int r0 = g - 2 * GX;
         const int which = r0 / GY, r = r0 % GY;
         const int t = r / (DV / 4), i4 = 4 * (r % (DV / 4));
         if (which == 0) *reinterpret_cast<float4*>(&sm.Y[t][i4]) = cvt4(val[u], vg);
         else if (which == 1) *reinterpret_cast<float4*>(&sm.dO[t][i4]) = cvt4(val[u], a.dO);
-        else *reinterpret_cast<float4*>(&sm.bt[t][i4]) = cvt4(val[u], bg);
+        else {
+          float4 b4;
+          if (a.beta_kind == 2) {
+            b4 = cvt4(val[u], bg);
+          } else {
+            float b = a.beta;
+            if (a.beta_kind == 1) {
+              if constexpr (sizeof(T) == 2) b = bf16_to_f32((uint16_t)val[u].x);
+              else b = __uint_as_float(val[u].x);
+            }
+            b4 = make_float4(b, b, b, b);
+          }
+          *reinterpret_cast<float4*>(&sm.bt[t][i4]) = b4;
+        }
       } else if (g < NG) {
         const float4 v = cvt4(val[u], a.dO);
         if (bwd) {
@@ -292,25 +328,9 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           float* dst;
           if (e < WS_XS) dst = &sm.S[e / DK][e % DK];
           else if (e < WS_G) dst = &sm.XS[(e - WS_XS) / DV][(e - WS_XS) % DV];
-          else if (e < WS_T) dst = &sm.G[(e - WS_G) / BC][(e - WS_G) % BC];
-          else if (e < WS_SV) dst = &sm.Tm[(e - WS_T) / BC][(e - WS_T) % BC];
-          else dst = &sm.sv[(e - WS_SV) / BC][(e - WS_SV) % BC];
+          else dst = &sm.G[(e - WS_G) / BC][(e - WS_G) % BC];
           *reinterpret_cast<float4*>(dst) = v;
         }
-      }
-    }
-    if (!PERROW && tid < BC) {
-      float b = a.beta;
-      if (a.beta_kind == 1) {
-        if constexpr (sizeof(T) == 2) b = bf16_to_f32((uint16_t)bval);
-        else b = 0.0f;   // fp32 gains take the 4-byte path below
-      }
-      sm.bts[tid] = b;
-    }
-    if constexpr (sizeof(T) == 4) {
-      if (!PERROW && a.beta_kind == 1 && tid < BC) {
-        const long t0 = (long)ci * BC;
-        sm.bts[tid] = t0 + tid < L ? ld_in(bg, chain * L + t0 + tid) : 0.0f;
       }
     }
     if (ci == 0 && ks == 1 && kpg && tid < DK / 4)   // the carried key is x_0
@@ -346,89 +366,17 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       wsc[WS_XS + t * DV + i] = acc[r];
     }
   };
-  // shared gains, one wave (lane t of each 16-lane row): eta, a, g, gm, zeta,
-  // and T = A^-1, A_ts = [t==s] + gm_t G_ts zeta_s (s < t), column j on lane j
-  auto shared_scalars_and_inverse = [&](long t0, int c, float* wsc) {
-    const int t = lane & 15;
-    float eta = 0.0f;
-    if (t < c && !(fresh && t0 + t == 0)) eta = sm.bts[t] / (a.eps + sm.nrm[t]);
-    const float av = 1.0f - eta * a.lambda;
-    float g = av;
-    g = row_shr_mul<1>(g);
-    g = row_shr_mul<2>(g);
-    g = row_shr_mul<4>(g);
-    g = row_shr_mul<8>(g);
-    const float gm = row_shr_fill<1>(g, 1.0f);
-    const float zeta = eta / g;
-    if (lane < 16) {
-      sm.sv[0][t] = eta;
-      sm.sv[1][t] = av;
-      sm.sv[2][t] = g;
-      sm.sv[3][t] = gm;
-      sm.sv[4][t] = zeta;
-    }
-    // lane m holds column m of the strictly lower Gram; column j of T on lane j:
-    // x_r = [r == j] - gm_r sum_{s<r} G_rs zeta_s x_s
-    float gcol[BC], om[BC], zs[BC], rhs[BC], acc[BC];
-#pragma unroll
-    for (int r = 0; r < BC; ++r) {
-      gcol[r] = sm.G[r][t];
-      om[r] = sm.sv[3][r];
-      zs[r] = sm.sv[4][r];
-      rhs[r] = r == t ? 1.0f : 0.0f;
-      acc[r] = 0.0f;
-    }
-    sweep16<0>(rhs, acc, gcol, om, zs);
-    if (lane < 16) {
-#pragma unroll
-      for (int r = 0; r < BC; ++r) {
-        sm.Tm[r][t] = rhs[r];
-        wsc[WS_T + r * BC + t] = rhs[r];
-      }
-      wsc[WS_SV + t] = eta;
-      wsc[WS_SV + BC + t] = av;
-      wsc[WS_SV + 2 * BC + t] = g;
-      wsc[WS_SV + 3 * BC + t] = gm;
-      wsc[WS_SV + 4 * BC + t] = zeta;
-    }
-  };
-  // E = T R with R = Y - gm XS (regression; T = I and R = Y for the inner
-  // product), Z = zeta E: row tiles ib on waves 0..NIB-1
-  auto shared_residual_tile = [&](int ib) {
-    {
-      floatx4 acc = zero4;
-      if (a.regression) {
-        acc = mtile<BC>(zero4, lane, [&](int m, int k) { return f4(&sm.Tm[m][k]); },
-                        [&](int k, int n) {
-                          const int i = 16 * ib + n;
-                          return make_float4(sm.Y[k][i] - sm.sv[3][k] * sm.XS[k][i],
-                                             sm.Y[k + 1][i] - sm.sv[3][k + 1] * sm.XS[k + 1][i],
-                                             sm.Y[k + 2][i] - sm.sv[3][k + 2] * sm.XS[k + 2][i],
-                                             sm.Y[k + 3][i] - sm.sv[3][k + 3] * sm.XS[k + 3][i]);
-                        });
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = sm.Y[rq + r][16 * ib + mn];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rq + r, i = 16 * ib + mn;
-        sm.E[t][i] = acc[r];
-        sm.Z[t][i] = sm.sv[4][t] * acc[r];
-      }
-    }
-  };
-  // backward sweep: q.x (lower incl. diagonal), S0 q, dS x tiles, (shared gains)
-  // E = T R tiles; s0.ds, the key norms and g_t do_t on the vector ALU
+  // backward sweep: q.x (lower incl. diagonal), S0 q, dS x tiles; s0.ds and the
+  // key norms on the vector ALU
   auto bwd_products = [&]() {
-    const int ntile = 1 + 2 * NIB + (PERROW ? 0 : NIB);
+    const int ntile = 1 + 2 * NIB;
     for (int tt = wave; tt < ntile; tt += BNW) {
       if (tt == 0) {
         const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&sm.Q[m][k]); },
                                       [&](int k, int n) { return f4(&sm.X[n][k]); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm.P[rq + r][mn] = mn <= rq + r ? acc[r] : 0.0f;
-      } else if (tt < 1 + 2 * NIB) {
+      } else {
         const int kind = (tt - 1) / NIB, ib = (tt - 1) % NIB;
         const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(kind == 0 ? &sm.Q[m][k] : &sm.X[m][k]); },
                                       [&](int k, int n) { return f4(kind == 1 ? &sm.dS[16 * ib + n][k] : &sm.S[16 * ib + n][k]); });
@@ -437,8 +385,6 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           if (kind == 0) sm.QS[rq + r][16 * ib + mn] = acc[r];
           else sm.XdS[rq + r][16 * ib + mn] = acc[r];
         }
-      } else {
-        shared_residual_tile(tt - 1 - 2 * NIB);
       }
     }
     nrm_and();
@@ -449,70 +395,64 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       for (int k = 0; k < DK; k += 4) acc = dot4(f4(&sm.S[i][k]), f4(&sm.dS[i][k]), acc);
       sm.sds[i] = acc;
     }
-    if (!PERROW) {
-      for (int idx = tid; idx < BC * DV; idx += BNT)
-        sm.GD[idx / DV][idx % DV] = sm.sv[2][idx / DV] * sm.dO[idx / DV][idx % DV];
-    }
   };
-  // sum over the 16 columns of a tile row (lanes of one 16-lane row), written
-  // by the row's first lane
-  auto tile_row_sums = [&](float (&dst)[BC], const float (&v)[4]) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s2 = group_sum<16>(v[r]);
-      if (mn == 0) dst[rq + r] = s2;
-    }
+  // lane t of the 16-lane row of value row i: eta, a, g (prefix product by DPP
+  // row shifts), gm = g_{t-1}, zeta
+  struct RowScal { float eta, av, g, gm, zeta; };
+  auto row_scal_dpp = [&](int i, long t0, int c) __attribute__((always_inline)) {
+    const int t = lane & 15;
+    RowScal r;
+    r.eta = 0.0f;
+    if (t < c && !(fresh && t0 + t == 0)) r.eta = sm.bt[t][i] / (a.eps + sm.nrm[t]);
+    r.av = 1.0f - r.eta * a.lambda;
+    float g = r.av;
+    g = row_shr_mul<1>(g);
+    g = row_shr_mul<2>(g);
+    g = row_shr_mul<4>(g);
+    g = row_shr_mul<8>(g);
+    r.g = g;
+    r.gm = row_shr_fill<1>(g, 1.0f);
+    r.zeta = r.eta / g;
+    return r;
   };
-  // per-channel: scalars of row i (eta, a, g, gm, zeta)
-  auto row_scalars = [&](int i, long t0, int c, float (&eta)[BC], float (&av)[BC], float (&g)[BC],
-                         float (&gm)[BC], float (&zeta)[BC]) {
-    float gp = 1.0f;
+  // forward sweep of value row i (lane t): z (and for the backward e, h, eta,
+  // g do) into LDS, gC
+  auto row_forward = [&](int i, const RowScal& r, bool bwd) __attribute__((always_inline)) {
+    const int t = lane & 15;
+    const float y = sm.Y[t][i], xs = sm.XS[t][i];
+    float acc = 0.0f;
+    if (a.regression) {
+      float grow[16];
 #pragma unroll
-    for (int t = 0; t < BC; ++t) {
-      float e = 0.0f;
-      if (t < c && !(fresh && t0 + t == 0)) e = sm.bt[t][i] / (a.eps + sm.nrm[t]);
-      eta[t] = e;
-      av[t] = 1.0f - e * a.lambda;
-      gm[t] = gp;
-      gp *= av[t];
-      g[t] = gp;
-      zeta[t] = e / gp;
+      for (int m = 0; m < 16; ++m) grow[m] = sm.G[t][m];
+      fsweep<0>(acc, grow, y, xs, r.gm, r.zeta);
     }
-  };
-  // per-channel: forward solve of row i
-  auto row_solve = [&](int i, const float (&gm)[BC], const float (&zeta)[BC], float (&e)[BC],
-                       float (&z)[BC], float (&h)[BC]) {
-#pragma unroll
-    for (int t = 0; t < BC; ++t) {
-      float hs = 0.0f;
-      if (a.regression) {
-#pragma unroll
-        for (int s2 = 0; s2 < t; ++s2) hs = __builtin_fmaf(sm.G[t][s2], z[s2], hs);
-        e[t] = sm.Y[t][i] - gm[t] * (sm.XS[t][i] + hs);
-      } else {
-        e[t] = sm.Y[t][i];
-      }
-      h[t] = hs;
-      z[t] = zeta[t] * e[t];
+    const float e = a.regression ? y - r.gm * (xs + acc) : y;
+    sm.Z[t][i] = r.zeta * e;
+    if (bwd) {
+      sm.E[t][i] = e;
+      sm.H[t][i] = acc;
+      sm.ETA[t][i] = r.eta;
+      sm.GD[t][i] = r.g * sm.dO[t][i];
     }
+    const float gc = row_last(r.g);
+    if (t == 0) sm.gC[i] = gc;
   };
-
   // ================= forward sweep: chunk-start states =================
   for (int idx = tid; idx < DV * DK; idx += BNT) {
     const int i = idx / DK, kk = idx % DK;
     sm.S[i][kk] = a.S0 ? a.S0[(chain * DV + i) * DK + kk] : 0.0f;
   }
   uint4 pre[NPER];
-  uint32_t pre_b;
-  issue_chunk(pre, pre_b, 0, false);
+  issue_chunk(pre, 0, false);
   for (int ci = 0; ci < nch; ++ci) {
     const long t0 = (long)ci * BC;
     const int c = (int)((L - t0) < BC ? (L - t0) : BC);
-    commit_chunk(pre, pre_b, ci, false);
+    commit_chunk(pre, ci, false);
     lds_barrier();
-    if (ci + 1 < nch) issue_chunk(pre, pre_b, ci + 1, false);
+    if (ci + 1 < nch) issue_chunk(pre, ci + 1, false);
     // record the chunk for the backward sweep: start state (all threads); wave 0:
-    // Gram, key norms and (shared gains) scalars and T; waves 1..NIB: S0 x tiles
+    // Gram and key norms; waves 1..NIB: S0 x tiles
     float* __restrict__ wsc = ws + (long)ci * WS_CHUNK;
     for (int idx = tid; idx < GS; idx += BNT) {
       const int e = 4 * idx;
@@ -528,25 +468,11 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         }
       }
       nrm_and();
-      if (!PERROW) shared_scalars_and_inverse(t0, c, wsc);
     } else if (wave <= NIB) {
       xs_tile(wave - 1, wsc);
     }
     lds_barrier();
-    if constexpr (!PERROW) {
-      if (wave < NIB) shared_residual_tile(wave);
-      if (tid < DV) sm.gC[tid] = sm.sv[2][BC - 1];
-    } else {
-      if (tid < DV) {
-        const int i = tid;
-        float eta[BC], av[BC], g[BC], gm[BC], zeta[BC], e[BC], z[BC], h[BC];
-        row_scalars(i, t0, c, eta, av, g, gm, zeta);
-        row_solve(i, gm, zeta, e, z, h);
-#pragma unroll
-        for (int t = 0; t < BC; ++t) sm.Z[t][i] = z[t];
-        sm.gC[i] = g[BC - 1];
-      }
-    }
+    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), false);
     lds_barrier();
     // S <- gC (S + Z^T X): tiles (ib, kb)
     for (int tt = wave; tt < NIB * NKB; tt += BNW) {
@@ -576,236 +502,109 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     for (int kk = tid; kk < DK; kk += BNT)
       a.dk[qk_base + (L - 1) * DK + kk] = a.dk_last ? a.dk_last[chain * DK + kk] : 0.0f;
   }
-  issue_chunk(pre, pre_b, nch - 1, true);
+  issue_chunk(pre, nch - 1, true);
   for (int ci = nch - 1; ci >= 0; --ci) {
     const long t0 = (long)ci * BC;
     const int c = (int)((L - t0) < BC ? (L - t0) : BC);
-    commit_chunk(pre, pre_b, ci, true);
+    commit_chunk(pre, ci, true);
     lds_barrier();
-    if (ci > 0) issue_chunk(pre, pre_b, ci - 1, true);
+    if (ci > 0) issue_chunk(pre, ci - 1, true);
     bwd_products();
     lds_barrier();
-    if constexpr (!PERROW) {
-      // ---- gains shared by the rows: matrix form ----
-      // H = L(G) Z;  o/g = QS + P Z (sum over rows of dO o/g);  dZ = P^T GD + gC XdS
-      // (and the sum over rows of Z XdS): tiles (kind, ib)
-      {
-        const float gc = sm.sv[2][BC - 1];
-        for (int tt = wave; tt < 3 * NIB; tt += BNW) {
-          const int kind = tt / NIB, ib = tt % NIB;
-          floatx4 acc;
-          float v[4];
-          if (kind == 0) {
-            acc = mtile<BC>(zero4, lane, [&](int m, int k) { return f4(&sm.G[m][k]); },
-                            [&](int k, int n) { return col4(sm.Z, k, 16 * ib + n); });
+    // ---- per-row sweeps on 16-lane DPP rows, shared products on the matrix cores ----
+    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), true);
+    lds_barrier();
+    // o/g = QS + P Z (kept as do o/g), dZ = P^T GD + gC XdS: tiles (kind, ib)
+    for (int tt = wave; tt < 2 * NIB; tt += BNW) {
+      const int kind = tt / NIB, ib = tt % NIB;
+      floatx4 acc;
+      if (kind == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.H[rq + r][16 * ib + mn] = acc[r];
-          } else if (kind == 1) {
+        for (int r = 0; r < 4; ++r) acc[r] = sm.QS[rq + r][16 * ib + mn];
+        acc = mtile<BC>(acc, lane, [&](int m, int k) { return f4(&sm.P[m][k]); },
+                        [&](int k, int n) { return col4(sm.Z, k, 16 * ib + n); });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = sm.QS[rq + r][16 * ib + mn];
-            acc = mtile<BC>(acc, lane, [&](int m, int k) { return f4(&sm.P[m][k]); },
-                            [&](int k, int n) { return col4(sm.Z, k, 16 * ib + n); });
+        for (int r = 0; r < 4; ++r) sm.DGO[rq + r][16 * ib + mn] = sm.dO[rq + r][16 * ib + mn] * acc[r];
+      } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = sm.dO[rq + r][16 * ib + mn] * acc[r];
-            tile_row_sums(sm.part[0][ib], v);
-          } else {
+        for (int r = 0; r < 4; ++r) acc[r] = sm.gC[16 * ib + mn] * sm.XdS[rq + r][16 * ib + mn];
+        acc = mtile<BC>(acc, lane, [&](int m, int k) { return col4(sm.P, k, m); },
+                        [&](int k, int n) { return col4(sm.GD, k, 16 * ib + n); });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gc * sm.XdS[rq + r][16 * ib + mn];
-            acc = mtile<BC>(acc, lane, [&](int m, int k) { return col4(sm.P, k, m); },
-                            [&](int k, int n) { return col4(sm.GD, k, 16 * ib + n); });
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = rq + r, i = 16 * ib + mn;
-              sm.dZ[t][i] = acc[r];
-              v[r] = sm.Z[t][i] * sm.XdS[t][i];
-            }
-            tile_row_sums(sm.part[1][ib], v);
-          }
-        }
+        for (int r = 0; r < 4; ++r) sm.dZ[rq + r][16 * ib + mn] = acc[r];
       }
-      lds_barrier();
-      // dR = T^T (zeta dZ); W = gm dR (regression); dv = dR; sum over rows of -dR (H + XS)
-      if (wave < NIB) {
-        const int ib = wave;
-        floatx4 acc = mtile<BC>(zero4, lane, [&](int m, int k) { return col4(sm.Tm, k, m); },
-                                [&](int k, int n) {
-                                  const int i = 16 * ib + n;
-                                  return make_float4(sm.sv[4][k] * sm.dZ[k][i], sm.sv[4][k + 1] * sm.dZ[k + 1][i],
-                                                     sm.sv[4][k + 2] * sm.dZ[k + 2][i], sm.sv[4][k + 3] * sm.dZ[k + 3][i]);
-                                });
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s2 = rq + r, i = 16 * ib + mn;
-          const float dr = acc[r];
-          sm.W[s2][i] = a.regression ? sm.sv[3][s2] * dr : 0.0f;
-          if (s2 < c) a.dv[v_base + (t0 + s2) * DV + i] = dr;
-          v[r] = a.regression ? -dr * (sm.H[s2][i] + sm.XS[s2][i]) : 0.0f;
-        }
-        tile_row_sums(sm.part[2][ib], v);
-      }
-      lds_barrier();
-      // sum over rows of E (dZ - L(G)^T W); dG = -L(W Z^T); dP = lower(GD Z^T)
-      for (int tt = wave; tt < NIB + 2; tt += BNW) {
-        if (tt < NIB) {
-          const int ib = tt;
-          const floatx4 acc = mtile<BC>(zero4, lane, [&](int m, int k) { return col4(sm.G, k, m); },
-                                        [&](int k, int n) { return col4(sm.W, k, 16 * ib + n); });
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int s2 = rq + r, i = 16 * ib + mn;
-            v[r] = sm.E[s2][i] * (sm.dZ[s2][i] - acc[r]);
-          }
-          tile_row_sums(sm.part[3][ib], v);
-        } else {
-          const bool dg = tt == NIB;
-          const floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(dg ? &sm.W[m][k] : &sm.GD[m][k]); },
-                                        [&](int k, int n) { return f4(&sm.Z[n][k]); });
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = rq + r, s2 = mn;
-            if (dg) sm.dG[t][s2] = (a.regression && s2 < t) ? -acc[r] : 0.0f;
-            else sm.dP[t][s2] = s2 <= t ? acc[r] : 0.0f;
-          }
-        }
-      }
-      lds_barrier();
-      // scalar chain (one wave, lane t of each 16-lane row)
-      if (wave == 0) {
-        const int t = lane & 15;
-        const float g = sm.sv[2][t], zeta = sm.sv[4][t], eta = sm.sv[0][t];
-        float sdgo = 0.0f, szx = 0.0f, sdzeta = 0.0f;
-#pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-          sdgo += sm.part[0][ib][t];
-          szx += sm.part[1][ib][t];
-          sdzeta += sm.part[3][ib][t];
-        }
-        float sdgm_next = 0.0f;
-        if (t + 1 < BC) {
-#pragma unroll
-          for (int ib = 0; ib < NIB; ++ib) sdgm_next += sm.part[2][ib][t + 1];
-        }
-        float dgc = szx;
-        for (int i = t; i < DV; i += 16) dgc += sm.sds[i];
-        dgc = group_sum<16>(dgc);
-        float dg = sdgo - sdzeta * zeta / g + sdgm_next;
-        if (t == BC - 1) dg += dgc;
-        float suf = dg * g;
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) {
-          const float o = __shfl_down(suf, d, 16);
-          if (t + d < 16) suf += o;
-        }
-        float deta = sdzeta / g - a.lambda * (suf / sm.sv[1][t]);
-        if (t >= c || (fresh && t0 + t == 0)) deta = 0.0f;
-        const float den = a.eps + sm.nrm[t];
-        if (lane < 16) {
-          sm.dn[t] = -deta * eta / den;
-          if (a.dbeta_t && t < c) a.dbeta_t[chain * L + t0 + t] = deta / den;
-        }
-        if (tid < DV) sm.gC[tid] = sm.sv[2][BC - 1];
-      }
-      lds_barrier();
-    } else {
-      // ---- per-channel gains: one lane per value row ----
-      if (tid < DV) {
-        const int i = tid;
-        float eta[BC], av[BC], g[BC], gm[BC], zeta[BC], e[BC], z[BC], h[BC];
-        row_scalars(i, t0, c, eta, av, g, gm, zeta);
-        row_solve(i, gm, zeta, e, z, h);
-        const float gc = g[BC - 1];
-        float gdo[BC], dg[BC], dz[BC], dzeta[BC], w[BC], dr[BC];
-        float dgc = sm.sds[i];
-#pragma unroll
-        for (int t = 0; t < BC; ++t) {
-          float oh = sm.QS[t][i];
-#pragma unroll
-          for (int s2 = 0; s2 <= t; ++s2) oh = __builtin_fmaf(sm.P[t][s2], z[s2], oh);
-          const float dov = sm.dO[t][i];
-          gdo[t] = g[t] * dov;
-          dg[t] = dov * oh;
-          dgc = __builtin_fmaf(z[t], sm.XdS[t][i], dgc);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < BC; ++s2) {
-          float acc = gc * sm.XdS[s2][i];
-#pragma unroll
-          for (int t = s2; t < BC; ++t) acc = __builtin_fmaf(sm.P[t][s2], gdo[t], acc);
-          dz[s2] = acc;
-          dzeta[s2] = acc * e[s2];
-        }
-        if (a.regression) {
-#pragma unroll
-          for (int s2 = BC - 1; s2 >= 0; --s2) {
-            float gs = 0.0f;
-#pragma unroll
-            for (int t = s2 + 1; t < BC; ++t) gs = __builtin_fmaf(sm.G[t][s2], w[t], gs);
-            dr[s2] = zeta[s2] * dz[s2] - zeta[s2] * gs;
-            w[s2] = gm[s2] * dr[s2];
-            dzeta[s2] -= e[s2] * gs;
-          }
-          // terms through gm_t = g_{t-1} (t >= 1)
-#pragma unroll
-          for (int t = 1; t < BC; ++t) dg[t - 1] -= dr[t] * (h[t] + sm.XS[t][i]);
-        } else {
-#pragma unroll
-          for (int s2 = 0; s2 < BC; ++s2) {
-            dr[s2] = zeta[s2] * dz[s2];
-            w[s2] = 0.0f;
-          }
-        }
-        float deta[BC];
-#pragma unroll
-        for (int t = 0; t < BC; ++t) {
-          deta[t] = dzeta[t] / g[t];
-          dg[t] -= dzeta[t] * zeta[t] / g[t];
-        }
-        dg[BC - 1] += dgc;
-        float suf = 0.0f;
-#pragma unroll
-        for (int r = BC - 1; r >= 0; --r) {
-          suf = __builtin_fmaf(dg[r], g[r], suf);
-          deta[r] -= a.lambda * (suf / av[r]);
-          if (r >= c || (fresh && t0 + r == 0)) deta[r] = 0.0f;
-        }
-#pragma unroll
-        for (int t = 0; t < BC; ++t) {
-          sm.Z[t][i] = z[t];
-          sm.W[t][i] = w[t];
-          sm.GD[t][i] = gdo[t];
-          sm.DE[t][i] = deta[t];
-          sm.ETA[t][i] = eta[t];
-          if (t < c) {
-            a.dv[v_base + (t0 + t) * DV + i] = dr[t];
-            if (a.dbeta_t) a.dbeta_t[v_base + (t0 + t) * DV + i] = deta[t] / (a.eps + sm.nrm[t]);
-          }
-        }
-        sm.gC[i] = gc;
-      }
-      lds_barrier();
-      // ---- sums over value rows: dG, dP (matrix cores), dn ----
-      for (int tt = wave; tt < 2; tt += BNW) {
-        const bool dg = tt == 0;
-        const floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(dg ? &sm.W[m][k] : &sm.GD[m][k]); },
-                                      [&](int k, int n) { return f4(&sm.Z[n][k]); });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = rq + r, s2 = mn;
-          if (dg) sm.dG[t][s2] = (a.regression && s2 < t) ? -acc[r] : 0.0f;
-          else sm.dP[t][s2] = s2 <= t ? acc[r] : 0.0f;
-        }
-      }
-      if (tid >= BNT - BC) {
-        const int t = tid - (BNT - BC);
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < DV; k += 4) acc = dot4(f4(&sm.DE[t][k]), f4(&sm.ETA[t][k]), acc);
-        sm.dn[t] = -acc / (a.eps + sm.nrm[t]);
-      }
-      lds_barrier();
     }
+    lds_barrier();
+    // transposed sweep and the scalar chain of each row (lane t of its 16-lane row)
+    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) {
+      const int t = lane & 15;
+      const RowScal r = row_scal_dpp(i, t0, c);
+      const float dz = sm.dZ[t][i], e = sm.E[t][i];
+      float acc2 = 0.0f;
+      if (a.regression) {
+        float gcol[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) gcol[m] = sm.G[m][t];
+        bsweep<15>(acc2, gcol, dz, r.gm, r.zeta);
+      }
+      const float dr = r.zeta * (dz - acc2);
+      const float w = a.regression ? r.gm * dr : 0.0f;
+      const float dzeta = e * (dz - acc2);
+      const float dgm = a.regression ? -dr * (sm.H[t][i] + sm.XS[t][i]) : 0.0f;
+      // d gC: s0.ds + sum_t z_t (x_t . ds), a row sum
+      float zx = sm.Z[t][i] * sm.XdS[t][i];
+      zx += row_shr_fill<1>(zx, 0.0f);
+      zx += row_shr_fill<2>(zx, 0.0f);
+      zx += row_shr_fill<4>(zx, 0.0f);
+      zx += row_shr_fill<8>(zx, 0.0f);
+      const float dgc = row_last(zx) + sm.sds[i];
+      float dg = sm.DGO[t][i] - dzeta * r.zeta / r.g + row_shl_fill<1>(dgm, 0.0f);
+      if (t == BC - 1) dg += dgc;
+      // suffix sums over t' >= t of dg g
+      float suf = dg * r.g;
+      suf += row_shl_fill<1>(suf, 0.0f);
+      suf += row_shl_fill<2>(suf, 0.0f);
+      suf += row_shl_fill<4>(suf, 0.0f);
+      suf += row_shl_fill<8>(suf, 0.0f);
+      float deta = dzeta / r.g - a.lambda * (suf / r.av);
+      if (t >= c || (fresh && t0 + t == 0)) deta = 0.0f;
+      sm.W[t][i] = w;
+      sm.DE[t][i] = deta;
+      if (t < c) {
+        a.dv[v_base + (t0 + t) * DV + i] = dr;
+        if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (t0 + t) * DV + i] = deta / (a.eps + sm.nrm[t]);
+      }
+    }
+    lds_barrier();
+    // ---- sums over value rows: dG, dP (matrix cores), dn ----
+    for (int tt = wave; tt < 2; tt += BNW) {
+      const bool dg = tt == 0;
+      const floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(dg ? &sm.W[m][k] : &sm.GD[m][k]); },
+                                    [&](int k, int n) { return f4(&sm.Z[n][k]); });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rq + r, s2 = mn;
+        if (dg) sm.dG[t][s2] = (a.regression && s2 < t) ? -acc[r] : 0.0f;
+        else sm.dP[t][s2] = s2 <= t ? acc[r] : 0.0f;
+      }
+    }
+    if (tid >= BNT - BC) {
+      const int t = tid - (BNT - BC);
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < DV; k += 4) acc = dot4(f4(&sm.DE[t][k]), f4(&sm.ETA[t][k]), acc);
+      sm.dn[t] = -acc / (a.eps + sm.nrm[t]);
+      if (a.dbeta_t && a.beta_kind == 1 && t < c) {   // a per-token gain feeds every row
+        float sde = 0.0f;
+#pragma unroll
+        for (int k = 0; k < DV; k += 4) {
+          const float4 d4 = f4(&sm.DE[t][k]);
+          sde += d4.x + d4.y + d4.z + d4.w;
+        }
+        a.dbeta_t[chain * L + t0 + t] = sde / (a.eps + sm.nrm[t]);
+      }
+    }
+    lds_barrier();
     // ---- dq and dx, column tiles kb: waves 0..NKB-1 take dq and the gC z ds part
     // of dx (to LDS); waves NKB..2NKB-1 the rest of dx, completed after the barrier
     floatx4 dxr = zero4;
@@ -896,10 +695,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
 template <typename T, int DK, int DV>
 hipError_t launch_bwd3(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((long)a.batch * a.heads));
-  if (a.beta_kind == 2)
-    hipLaunchKernelGGL((backward_kernel<T, DK, DV, true>), grid, dim3(BNT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((backward_kernel<T, DK, DV, false>), grid, dim3(BNT), 0, stream, a);
+  hipLaunchKernelGGL((backward_kernel<T, DK, DV>), grid, dim3(BNT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -926,9 +722,9 @@ hipError_t launch_bwd_dk(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv) {
-  // per chunk: start state, S0 x, Gram, T, five per-step scalars (fp32)
+  // per chunk: start state, S0 x, Gram (fp32)
   const long nch = (seqlen + BC - 1) / BC;
-  const long per_chunk = (long)dv * dk + (long)BC * dv + 2L * BC * BC + 5L * BC;
+  const long per_chunk = (long)dv * dk + (long)BC * dv + (long)BC * BC;
   return (size_t)batch * heads * nch * per_chunk * sizeof(float);
 }
 
