@@ -122,7 +122,9 @@ int falcon_fwd_recurrent(int variant, int window, float beta, const void* beta_t
  *   chunk     tokens per chunk, in {16, 32, 64}; any L (a short last chunk is
  *             handled in place)
  * Restrictions (FALCON_ERR_UNSUPPORTED): dtype must be FALCON_BF16;
- * window <= 4; window <= chunk.
+ * window <= 4, except FALCON_3A with gains shared by the value rows (scalar or
+ * per-token beta), dk in {64, 128} and dv a multiple of 32: window <= 16.
+ * window <= chunk (FALCON_ERR_INVALID_ARG otherwise).
  * The result equals the recurrence up to floating-point rounding (state
  * carried in float32, products on bf16 matrix cores with split-bf16 operands
  * where an operand is not an exact bf16 input).

@@ -116,6 +116,9 @@ def test_seq_validation(lib, fn, over, status):
     (dict(chunk=128), UNSUPPORTED),
     (dict(dtype=1), UNSUPPORTED),
     (dict(variant=2, window=8), UNSUPPORTED),
+    (dict(variant=5, window=17), UNSUPPORTED),       # inner-product windows up to 16
+    (dict(variant=5, window=8, dk=32, dv=32), UNSUPPORTED),
+    (dict(variant=5, window=8, dv=16), UNSUPPORTED),
     (dict(variant=2, window=32, chunk=16), INVALID),  # window > chunk
 ])
 def test_chunk_only_validation(lib, over, status):

@@ -200,6 +200,28 @@ def test_chunk_window_carried_key(variant, dk, dv):
         assert state_err(S, S_ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 32)])
+@pytest.mark.parametrize("window", [1, 3, 8, 16])
+@pytest.mark.parametrize("carried", [False, True])
+def test_chunk_inner_product_windows(dk, dv, window, carried):
+    """Inner-product family over windows 1..16, several 64-step chunks and a ragged
+    tail; carried: previous key and start state in, per-token gains."""
+    variant = fw.FALCON_1A if window == 1 else fw.FALCON_3A
+    L = 3 * 64 + 29
+    inp = seq_inputs(2, 2, L, dk, dv, seed=480 + window + dk + dv, dtype="bf16",
+                     with_k_prev=carried, with_S0=carried and window == 1, beta_per_token=carried,
+                     s_std=0.2)
+    o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=None if carried else 0.5,
+                    lam=0.03, eps=1e-6, window=window, chunk=64, carried=carried)
+    o_ref, S_ref, _ = _oracle(variant, inp, beta=None if carried else 0.5, lam=0.03, eps=1e-6,
+                              window=window, carried=carried)
+    err, zok = token_normwise_err(o, o_ref)
+    serr = state_err(S, S_ref)
+    print("inner product dk %d dv %d window %d: o err %.3e S err %.3e" % (dk, dv, window, err, serr))
+    assert zok and err <= TOL_BF16
+    assert serr <= TOL_BF16
+
+
 # ---------------------------------------------------------------------------
 # chunk form at the full workload sizes, sampled chains
 

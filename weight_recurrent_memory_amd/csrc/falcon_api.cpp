@@ -157,8 +157,9 @@ int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipSt
   if (a.chunk < 1) return FALCON_ERR_INVALID_ARG;
   if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return FALCON_ERR_UNSUPPORTED;
   if (a.window > a.chunk) return FALCON_ERR_INVALID_ARG;
-  if (a.window > 4) return FALCON_ERR_UNSUPPORTED;
   if (a.dtype != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
+  // wider windows: the inner-product kernel takes any window up to 16
+  if (a.window > 4 && !falcon::chunk_ip_supported(a)) return FALCON_ERR_UNSUPPORTED;
   return launch_with_history(true, a, xo, yo, stream);
 }
 

@@ -704,6 +704,7 @@ hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
   if (chunk_wy_supported(a)) return launch_chunk_wy(a, stream);
+  if (chunk_ip_supported(a)) return launch_chunk_ip(a, stream);
   if (chunk_wyb_supported(a)) return launch_chunk_wyb(a, stream);
   if (a.window == 1) return launch_chunk_w1(a, stream, cs);
   switch (a.dk) {

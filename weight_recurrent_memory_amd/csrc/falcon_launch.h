@@ -97,6 +97,10 @@ hipError_t launch_chunk_wy(const SeqArgs& a, hipStream_t stream);
 // {64, 128} (falcon_chunk_wyb.hip); 16-step sub-chunks whatever the requested chunk
 bool chunk_wyb_supported(const SeqArgs& a);
 hipError_t launch_chunk_wyb(const SeqArgs& a, hipStream_t stream);
+// inner-product family, any window up to 16, gains shared by the value rows, dk in
+// {64, 128}, dv a multiple of 32 (falcon_chunk_ip.hip); 64-step chunks
+bool chunk_ip_supported(const SeqArgs& a);
+hipError_t launch_chunk_ip(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // the window-1 latest samples after a sequence call, written to x_out / y_out
 // (which may equal a.x_hist / a.y_hist); enqueue after the call's kernel
