@@ -61,8 +61,8 @@ struct IpLds {
   uint16_t XT[DK][KR];                 // keys transposed, keys in natural order
   uint16_t Q[IC][XR];                  // queries, dk in fragment order
   uint16_t YT[IRB][KR];                // values transposed
-  float knp[IC][NP];                   // next chunk: squared-norm partials [key][dk quad]
-  float bnext[IC];                     // next chunk: gains
+  float knp[2][IC][NP];                // squared-norm partials [key][dk quad], by chunk parity
+  float bnext[2][IC];                  // gains, by chunk parity
   float kn[IK];                        // squared key norms (16 halo rows + the chunk)
   float gs[2][IC];                     // g_t, by chunk parity
   float zs[2][IC];                     // prefix sums Z of zeta, by chunk parity
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
   constexpr int HKS = HKT / 2 > 0 ? HKT / 2 : 1;
   constexpr int NKB = (IC / 4) * (DK / 4);      // 4 x 4 key blocks per chunk
   constexpr int KQP = IC * DK / 8 / INT;        // 16-byte query pieces per thread
-  constexpr int SCW = 0;                        // the wave that forms the scalars
+  constexpr int SCW = 4;                        // the wave that forms the scalars (lightest readout)
   static_assert(DK == 64 || DK == 128, "dk in {64, 128}");
   static_assert(KQP >= 1 && NKB <= INT, "loader shape");
   __shared__ __align__(16) SM sm;
@@ -262,10 +262,10 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
       for (int e = 0; e < 4; ++e) {
         float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, r[e].x), __builtin_bit_cast(bf16x2, r[e].x), 0.0f, false);
         p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, r[e].y), __builtin_bit_cast(bf16x2, r[e].y), p, false);
-        sm.knp[4 * tq + e][kq] = p;
+        sm.knp[c & 1][4 * tq + e][kq] = p;
       }
     }
-    if (wave == INW - 1) sm.bnext[lane] = a.beta_kind == 1 ? bf16_to_f32(st.b) : a.beta;
+    if (wave == INW - 1) sm.bnext[c & 1][lane] = a.beta_kind == 1 ? bf16_to_f32(st.b) : a.beta;
   };
   // after the barrier: chunk c to LDS; for c > 0 the previous chunk's last 16
   // samples move to the halo rows first (each thread moves exactly what it then
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     float nsum = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < DK / 16; ++q4) {
-      const float4 v = *reinterpret_cast<const float4*>(&sm.knp[t][4 * q4]);
+      const float4 v = *reinterpret_cast<const float4*>(&sm.knp[pb][t][4 * q4]);
       nsum += (v.x + v.y) + (v.z + v.w);
     }
     const float hv = (c > 0 && lane < 16) ? sm.kn[IC + lane] : 0.0f;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     for (int w = 0; w < B; ++w) n += sm.kn[16 + t - w];
     const int st = c * IC + t;
     const bool live = st < L && !(fresh && st == 0);
-    const float eta = live ? sm.bnext[t] * __builtin_amdgcn_rcpf(a.eps + n) : 0.0f;
+    const float eta = live ? sm.bnext[pb][t] * __builtin_amdgcn_rcpf(a.eps + n) : 0.0f;
     const float av = live ? 1.0f - eta * a.lambda : 1.0f;
     float g = av;
     g *= ip_shr<1>(g, 1.0f);
@@ -393,6 +393,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
   issue(s0, 0);
   issue(s1, 1);
   norms_and_gains(s0, 0);
+  norms_and_gains(s1, 1);
   commit(s0, 0);
   issue(s0, 2);
   __syncthreads();
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
                                                   floatx4{sv[2 * k + 1][0], sv[2 * k + 1][1], sv[2 * k + 1][2], sv[2 * k + 1][3]});
     };
     resplit();
-    auto body = [&](int c, Set& nxt) __attribute__((always_inline)) {
+    auto body = [&](int c, Set& nxt, const Set& far) __attribute__((always_inline)) {
       const int pb = c & 1;
       const float g63 = sm.gs[pb][IC - 1];
       // S0 q partial sums over this wave's dk half: (S Q^T) tiles [row][t]
@@ -491,18 +492,17 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
           for (int e = 0; e < 4; ++e) sv[kt][e] = g63 * acc[kt][e];
       }
       resplit();
-      if (c + 1 < nchunks) norms_and_gains(nxt, c + 1);
+      if (c + 2 < nchunks) norms_and_gains(far, c + 2);
       __syncthreads();
       if (c + 1 < nchunks) commit(nxt, c + 1);
-      if (wave == SCW) scalars(c + 1);
       issue(nxt, c + 3);
       __syncthreads();
     };
     // pairs of chunks, so that each register set keeps its registers (an odd
     // count runs one empty chunk: no live step, no output, the state unchanged)
     for (int c = 0; c < nchunks; c += 2) {
-      body(c, s1);
-      body(c + 1, s0);
+      body(c, s1, s0);
+      body(c + 1, s0, s1);
     }
     if (a.S_out) {
 #pragma unroll
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
       constexpr int nmb = tt + 2;              // key tiles up to the diagonal
       constexpr int nk = (nmb + 1) / 2;        // 32-key steps over them
       const int t = 16 * tt + lr;
-      auto body = [&](int c, Set& nxt) __attribute__((always_inline)) {
+      auto body = [&](int c, Set& nxt, const Set& far) __attribute__((always_inline)) {
         const int pb = c & 1;
         // the step and key indices are made opaque per chunk: otherwise the
         // compiler hoists the weight's lane conditions out of the loop as 40
@@ -543,13 +543,6 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
           for (int mb = 0; mb < nmb; ++mb) p[mb] = mfma16(xf[mb][ks], qf[ks], p[mb]);
         // weights c_{j,t} = Z_{min(j+B-1,t)} - Z_{j-1} where 0 <= max(j, 0) <= min(j+B-1, t)
         const float zt = sm.zs[pb][tv];
-        float4 zp4[nmb], zq4[nmb];
-#pragma unroll
-        for (int mb = 0; mb < nmb; ++mb) {
-          const int j0 = 16 * mb - 16 + 4 * lgv;
-          zp4[mb] = *reinterpret_cast<const float4*>(&sm.zp[pb][16 + j0]);
-          zq4[mb] = *reinterpret_cast<const float4*>(&sm.zq[pb][16 + j0]);
-        }
         bf16x8 yf[2][nk];
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
@@ -562,15 +555,27 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
 #pragma unroll
         for (int mb = 0; mb < nmb; ++mb) {
           const int j0 = 16 * mb - 16 + 4 * lgv;
-          const float zpv[4] = {zp4[mb].x, zp4[mb].y, zp4[mb].z, zp4[mb].w};
-          const float zqv[4] = {zq4[mb].x, zq4[mb].y, zq4[mb].z, zq4[mb].w};
+          if (16 * tt >= 16 * mb + B - 2) {
+            // the whole tile lies below the window band (t >= j + B - 1): the
+            // weight depends on the key only and equals c_{j, C-1}
+            const float4 w4 = *reinterpret_cast<const float4*>(&sm.c63[pb][16 + j0]);
+            p[mb][0] *= w4.x;
+            p[mb][1] *= w4.y;
+            p[mb][2] *= w4.z;
+            p[mb][3] *= w4.w;
+          } else {
+            const float4 zp4 = *reinterpret_cast<const float4*>(&sm.zp[pb][16 + j0]);
+            const float4 zq4 = *reinterpret_cast<const float4*>(&sm.zq[pb][16 + j0]);
+            const float zpv[4] = {zp4.x, zp4.y, zp4.z, zp4.w};
+            const float zqv[4] = {zq4.x, zq4.y, zq4.z, zq4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            const int hj = j + B - 1;
-            const float top = hj >= tv ? zt : zqv[r];
-            const bool ok = (hj < tv ? hj : tv) >= (j > 0 ? j : 0);
-            p[mb][r] *= ok ? top - zpv[r] : 0.0f;
+            for (int r = 0; r < 4; ++r) {
+              const int j = j0 + r;
+              const int hj = j + B - 1;
+              const float top = hj >= tv ? zt : zqv[r];
+              const bool ok = (hj < tv ? hj : tv) >= (j > 0 ? j : 0);
+              p[mb][r] *= ok ? top - zpv[r] : 0.0f;
+            }
           }
         }
         // Y^T (c o P)^T: tiles [row][t]; the operand over 32 keys pairs two tiles
@@ -583,7 +588,10 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
 #pragma unroll
           for (int r2 = 0; r2 < 2; ++r2) oi[r2] = mfma16(yf[r2][k], pf.lo, oi[r2]);
         }
-        if (c + 1 < nchunks) norms_and_gains(nxt, c + 1);
+        // the next chunk's scalars (its norms were complete at the last barrier)
+        // and the norm partials of the one after
+        if (wave == SCW) scalars(c + 1);
+        if (c + 2 < nchunks) norms_and_gains(far, c + 2);
         __syncthreads();
         // o_t = g_t (S0 q_t + intra-chunk part)
         const float gt = sm.gs[pb][t];
@@ -602,8 +610,8 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
         __syncthreads();
       };
       for (int c = 0; c < nchunks; c += 2) {
-        body(c, s1);
-        body(c + 1, s0);
+        body(c, s1, s0);
+        body(c + 1, s0, s1);
       }
     };
     if (wave == 4) readout(std::integral_constant<int, 0>{});
