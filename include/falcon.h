@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 3
+#define FALCON_ABI_VERSION 4
 
 /* The six update rules (explainer, section 核心方法 §2, variant table;
  * 163.com section 02: objective axis x granularity axis). */
@@ -222,21 +222,25 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
                           void* stream);
 
 /*
- * Backward pass of the window-1 chunk form (Falcon-1, -2, -1A, -2A): gradients
+ * Backward pass of the chunk form (every variant; window 1, 2 or 4): gradients
  * of  sum_t <dO_t, o_t> + <dS_L, S_L> + <dk_last, k_last>  with respect to q, k,
  * v, the gains, k_prev and S0.  The pages present the chunk-parallel form as
  * the training form (explainer §3; 163.com section 02 (2)) but print no
  * gradients; these are the chain rule through the chunk equations (per value
- * row: the triangular solve, its transpose, the decay products), computed in
- * fp32 with the chunk-start states recomputed by a forward sweep.
+ * row: the triangular solve over the (step, window slot) unknowns, its
+ * transpose, the decay products), computed in fp32 with the chunk-start states
+ * recomputed by a forward sweep.
  *
  * falcon_bwd_workspace_bytes - bytes of device workspace falcon_bwd_chunk needs
- *   (per 16-token chunk and (batch, head), fp32: the chunk-start state
- *   (dv x dk), S0 x (16 x dv) and the key Gram (16 x 16)); 0 for invalid sizes.
+ *   (per chunk of 16 / window steps and (batch, head), fp32: the chunk-start
+ *   state (dv x dk), S0 x (16 x dv) and the unknowns' Gram (16 x 16)); 0 for
+ *   invalid sizes or a window other than 1, 2, 4.
  *
  * falcon_bwd_chunk
- *   variant ... k_prev, S0, flags   as falcon_fwd_chunk_ex (window 1; flags 0 or
+ *   variant ... k_prev, S0, flags   as falcon_fwd_chunk_ex (flags 0 or
  *             FALCON_SAME_STEP); dk, dv in {16, 32, 64}; dtype bf16 or fp32
+ *   window    1, or 2 or 4 for FALCON_3 / FALCON_3A; a windowed call takes no
+ *             start state (S0 must be NULL: its window history is not an input)
  *   dO        [batch, heads, L, dv] float32, gradient of o
  *   dS_L      [batch, heads, dv, dk] float32 gradient of the final state, or NULL
  *   dk_last   [batch, heads, dk] float32 gradient of k_last = k_L (the key a
@@ -247,18 +251,20 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  *   dk_prev   [batch, heads, dk] float32, or NULL; needs k_prev
  *   dS0       [batch, heads, dv, dk] float32, or NULL; needs S0
  *   workspace, workspace_bytes   device scratch of at least
- *             falcon_bwd_workspace_bytes(...) bytes, 16-byte aligned
+ *             falcon_bwd_workspace_bytes(..., window) bytes, 16-byte aligned
  * Outputs must not overlap each other, the inputs or the workspace.
- * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for Falcon-3/3A or sizes above 64.
+ * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for window 3 or above 4, a
+ * windowed start state, or sizes above 64.
  */
-unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk, int dv);
-int falcon_bwd_chunk(int variant, int flags, float beta, const void* beta_t, int beta_kind,
-                     float lambda, float eps, int batch, int heads, int seqlen, int dk, int dv,
-                     int dtype, const void* q, const void* k, const void* v, const void* k_prev,
-                     const float* S0, const float* dO, const float* dS_L, const float* dk_last,
-                     float* dq, float* dk_out, float* dv_out, float* dbeta_t, float* dk_prev,
-                     float* dS0, void* workspace, unsigned long long workspace_bytes,
-                     void* stream);
+unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk, int dv,
+                                              int window);
+int falcon_bwd_chunk(int variant, int window, int flags, float beta, const void* beta_t,
+                     int beta_kind, float lambda, float eps, int batch, int heads, int seqlen,
+                     int dk, int dv, int dtype, const void* q, const void* k, const void* v,
+                     const void* k_prev, const float* S0, const float* dO, const float* dS_L,
+                     const float* dk_last, float* dq, float* dk_out, float* dv_out,
+                     float* dbeta_t, float* dk_prev, float* dS0, void* workspace,
+                     unsigned long long workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -55,7 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.falcon_abi_version() == 3
+    assert lib.falcon_abi_version() == 4
     assert lib.falcon_status_string(0) == b"ok"
     assert lib.falcon_status_string(1) == b"invalid argument"
     assert lib.falcon_status_string(2) == b"unsupported configuration"
@@ -221,12 +221,12 @@ def test_decode_history_validation(lib, over, status):
 
 
 def _bwd(lib, **over):
-    a = dict(variant=0, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, batch=1,
+    a = dict(variant=0, window=1, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, batch=1,
              heads=2, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2], k_prev=None,
              S0=None, dO=P[3], dS_L=None, dk_last=None, dq=P[4], dk_=P[5], dv_=P[6],
              dbeta_t=None, dk_prev=None, dS0=None, ws=P[7], wsb=1 << 26)
     a.update(over)
-    return lib.falcon_bwd_chunk(a["variant"], a["flags"], a["beta"], a["beta_t"], a["beta_kind"],
+    return lib.falcon_bwd_chunk(a["variant"], a["window"], a["flags"], a["beta"], a["beta_t"], a["beta_kind"],
                                 a["lam"], a["eps"], a["batch"], a["heads"], a["seqlen"], a["dk"],
                                 a["dv"], a["dtype"], a["q"], a["k"], a["v"], a["k_prev"], a["S0"],
                                 a["dO"], a["dS_L"], a["dk_last"], a["dq"], a["dk_"], a["dv_"],
@@ -234,14 +234,22 @@ def _bwd(lib, **over):
 
 
 def test_backward_workspace_size(lib):
-    # per 16-token chunk and (batch, head): start state, S0 x, Gram (fp32)
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32) == 2 * 3 * 7 * (32 * 64 + 16 * 32 + 256) * 4
-    assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32) == 0
-    assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32) == 0
+    # per chunk of 16 / window steps and (batch, head): start state, S0 x, Gram (fp32)
+    rec = (32 * 64 + 16 * 32 + 256) * 4
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 1) == 2 * 3 * 7 * rec
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 2) == 2 * 3 * 13 * rec
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 4) == 2 * 3 * 25 * rec
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 3) == 0
+    assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32, 1) == 0
+    assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32, 1) == 0
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(variant=2), UNSUPPORTED),                  # Falcon-3: no backward yet
+    (dict(variant=2, window=3), UNSUPPORTED),        # windows 1, 2, 4 only
+    (dict(variant=5, window=8), UNSUPPORTED),
+    (dict(variant=0, window=2), INVALID),            # window > 1 outside Falcon-3/3A
+    (dict(variant=2, window=0), INVALID),
+    (dict(variant=2, window=2, k_prev=P[8], S0=P[9]), UNSUPPORTED),   # windowed start state
     (dict(dk=128), UNSUPPORTED),
     (dict(flags=2), INVALID),
     (dict(dq=None), INVALID),

@@ -538,6 +538,42 @@ def test_backward_small(variant, dk, dv, carried, same_step, dtype):
     assert max(errs.values()) <= TOL_FP32_MATH, errs
 
 
+@pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
+@pytest.mark.parametrize("window", [2, 4])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 16)])
+@pytest.mark.parametrize("carried,same_step,per_token", [(False, False, False), (True, False, True),
+                                                         (False, True, True)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_window(variant, window, dk, dv, carried, same_step, per_token, dtype):
+    """Sliding window: the chunk's unknowns are (step, window slot) pairs; several
+    chunks, a ragged tail, halo samples crossing chunk boundaries."""
+    L = 37
+    inp = seq_inputs(2, 2, L, dk, dv, seed=820 + 5 * variant + window + dk + dv, dtype=dtype,
+                     beta_per_token=per_token, with_k_prev=carried and not same_step)
+    rng = np.random.default_rng(821 + variant + window)
+    dO = rng.standard_normal((2, 2, L, dv)).astype(np.float32)
+    dS_L = rng.standard_normal((2, 2, dv, dk)).astype(np.float32)
+    dk_last = rng.standard_normal((2, 2, dk)).astype(np.float32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda n: to_dev(torch, inp[n], dt) if n in inp else None
+    f32 = lambda a: to_dev(torch, a, torch.float32)
+    beta = None if per_token else 0.5
+    got = fw.bwd_chunk(dev("q"), dev("k"), dev("v"), f32(dO), variant=variant, beta=beta,
+                       lam=0.02, eps=1e-6, window=window, beta_t=dev("beta_t"),
+                       k_prev=dev("k_prev"), dS_L=f32(dS_L), dk_last=f32(dk_last),
+                       same_step=same_step)
+    torch.cuda.synchronize()
+    ref = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta=beta, lam=0.02,
+                             eps=1e-6, window=window, beta_t=inp.get("beta_t"),
+                             k_prev=inp.get("k_prev"), same_step=same_step, dS_L=dS_L,
+                             dk_last=dk_last)
+    assert set(got) == set(ref)
+    errs = {n: _grad_err(got[n].cpu().numpy(), ref[n]) for n in ref}
+    print("backward window %d v%d dk %d dv %d %s: %s" % (window, variant, dk, dv, dtype,
+                                                         {n: "%.2e" % e for n, e in errs.items()}))
+    assert max(errs.values()) <= TOL_FP32_MATH, errs
+
+
 def test_backward_8x12x2048x64_sampled():
     """Headline workload: all chains on the GPU, two chains recomputed by the oracle."""
     cfg = WORKLOADS["chunk_8x12x2048x64"]

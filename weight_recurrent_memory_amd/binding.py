@@ -63,9 +63,9 @@ def load_library():
     lib.falcon_decode_step_ex.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp]
     lib.falcon_bwd_workspace_bytes.restype = ctypes.c_ulonglong
-    lib.falcon_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.falcon_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.falcon_bwd_chunk.restype = i
-    lib.falcon_bwd_chunk.argtypes = [i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp,
+    lib.falcon_bwd_chunk.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_ulonglong,
                                      vp]
     _LIB = lib
@@ -244,10 +244,10 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
     return out
 
 
-def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, beta_t=None, k_prev=None,
-              S0=None, dS_L=None, dk_last=None, same_step=False, stream=None):
-    """Gradients of sum <dO, o> + <dS_L, S_L> + <dk_last, k_last> for the window-1
-    chunk form.  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
+def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
+              k_prev=None, S0=None, dS_L=None, dk_last=None, same_step=False, stream=None):
+    """Gradients of sum <dO, o> + <dS_L, S_L> + <dk_last, k_last> for the chunk form
+    (window 1, 2 or 4).  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
     dk_prev / dS0 when beta_t / k_prev / S0 are given."""
     import torch
     lib = load_library()
@@ -278,10 +278,10 @@ def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, beta_t=None,
         out["dk_prev"] = torch.empty((B, H, dk), device=dev, dtype=f32)
     if S0 is not None:
         out["dS0"] = torch.empty((B, H, dv, dk), device=dev, dtype=f32)
-    wsb = int(lib.falcon_bwd_workspace_bytes(B, H, L, dk, dv))
+    wsb = int(lib.falcon_bwd_workspace_bytes(B, H, L, dk, dv, int(window)))
     ws = torch.empty((max(wsb, 16) // 4 + 4,), device=dev, dtype=f32)
     status = lib.falcon_bwd_chunk(
-        variant, SAME_STEP if same_step else 0, float(beta if beta is not None else 0.0),
+        variant, int(window), SAME_STEP if same_step else 0, float(beta if beta is not None else 0.0),
         _ptr(beta_t), kind, float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k),
         _ptr(v), _ptr(k_prev), _ptr(S0), _ptr(dO), _ptr(dS_L), _ptr(dk_last), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dbeta_t")), _ptr(out.get("dk_prev")),

@@ -300,13 +300,17 @@ FALCON_EXPORT int falcon_decode_step_ex(int variant, int window, int flags, floa
                      dk, dv, dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }
 
+bool bwd_window(int window) { return window == 1 || window == 2 || window == 4; }
+
 FALCON_EXPORT unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk,
-                                                            int dv) {
-  if (batch < 1 || heads < 1 || seqlen < 1 || !supported_dim(dk) || !supported_dim(dv)) return 0;
-  return (unsigned long long)falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv);
+                                                            int dv, int window) {
+  if (batch < 1 || heads < 1 || seqlen < 1 || !supported_dim(dk) || !supported_dim(dv) ||
+      !bwd_window(window))
+    return 0;
+  return (unsigned long long)falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);
 }
 
-FALCON_EXPORT int falcon_bwd_chunk(int variant, int flags, float beta, const void* beta_t,
+FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float beta, const void* beta_t,
                                    int beta_kind, float lambda, float eps, int batch, int heads,
                                    int seqlen, int dk, int dv, int dtype, const void* q,
                                    const void* k, const void* v, const void* k_prev,
@@ -318,7 +322,7 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int flags, float beta, const voi
   const int key_shift = (flags & FALCON_SAME_STEP) ? 0 : 1;
   // the forward arguments are checked as the forward checks them (dO takes the
   // place of o: same shape, and it must not overlap an input either)
-  falcon::SeqArgs a{variant, 1, is_regression(variant), beta, beta_t, beta_kind, lambda, eps,
+  falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda, eps,
                     batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0,
                     const_cast<float*>(dO), nullptr, 0, nullptr, nullptr, key_shift};
   int st = check_seq(a, true);
@@ -330,11 +334,14 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int flags, float beta, const voi
   const void* ptrs[] = {dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
-  if (window_variant(variant)) return FALCON_ERR_UNSUPPORTED;
+  // windows: 1, 2 or 4; a windowed start state would need its window history,
+  // which this entry point does not take
+  if (!bwd_window(window)) return FALCON_ERR_UNSUPPORTED;
+  if (window > 1 && S0) return FALCON_ERR_UNSUPPORTED;
   if (dk > 64 || dv > 64) return FALCON_ERR_UNSUPPORTED;
   const size_t es = dtype == FALCON_BF16 ? 2 : 4;
   const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
-  const size_t need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv);
+  const size_t need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);
   if (workspace_bytes < need) return FALCON_ERR_INVALID_ARG;
   Range outs[] = {{dq, BH * L * dk * 4},
                   {dk_out, BH * L * dk * 4},
@@ -358,7 +365,7 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int flags, float beta, const voi
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return FALCON_ERR_INVALID_ARG;
   }
-  falcon::BwdArgs b{is_regression(variant), key_shift, beta, beta_t, beta_kind, lambda, eps,
+  falcon::BwdArgs b{is_regression(variant), window, key_shift, beta, beta_t, beta_kind, lambda, eps,
                     batch, heads, (long)seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO, dS_L,
                     dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0,
                     static_cast<float*>(workspace)};

@@ -41,6 +41,7 @@
 // fp32 throughout.
 #include "falcon_device.h"
 #include "falcon_launch.h"
+#include "falcon_mma.h"
 
 namespace falcon {
 namespace {
@@ -49,16 +50,23 @@ constexpr int BC = 16;        // chunk length of the backward
 constexpr int BNT = 512;
 constexpr int BNW = BNT / 64;
 
-template <int DK, int DV>
+template <int DK, int DV, int BW>
 struct BwdLds {
+  static constexpr int WR = BW > 1 ? BC : 1;     // rows of the window-only arrays
+  static constexpr int WH = BW > 1 ? BW - 1 : 1;
   float S[DV][DK + 4];        // chunk-start state
   float dS[DV][DK + 4];       // gradient of the chunk-end state
-  float X[BC][DK + 4];        // keys x_t (shifted)
+  float X[BC][DK + 4];        // key tile: samples t0 - (B-1) + k (shifted keys)
   float Q[BC][DK + 4];
   float Y[BC][DV + 4];        // values
   float dO[BC][DV + 4];
   float bt[BC][DV];           // gain per step and row
-  float nrm[BC];
+  float nrm[BC];              // squared norms of the key tile rows
+  float nsum[BC];             // per step: window sums of the squared norms
+  float XU[WR][DK + 4];       // window: the key of each unknown (step, slot)
+  float DR[WR][DV + 4];       // window: d y per unknown
+  float dxh[2][WH][DK];       // window: d x of the samples before the chunk (to the next one)
+  float dyh[2][WH][DV];
   float G[BC][BC + 4];        // strictly lower
   float P[BC][BC + 4];        // lower incl. diagonal
   float XS[BC][DV + 4];       // s0_i . x_t
@@ -191,9 +199,14 @@ __device__ __forceinline__ floatx4 mtile(floatx4 acc, int lane, FA fa, FB fb) {
   return acc;
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int BW>
 __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
-  using SM = BwdLds<DK, DV>;
+  using SM = BwdLds<DK, DV, BW>;
+  // unknowns u = BW s + w (step s of the chunk, window slot w) on the 16 lanes of a
+  // row; the chunk has NS steps and a key tile of NK rows (the BW-1 samples
+  // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w
+  constexpr int NS = BC / BW, NK = BW - 1 + NS;
+  static_assert(BC % BW == 0, "window 1, 2 or 4");
   constexpr int GX = BC * DK / 4, GY = BC * DV / 4, GS = DV * DK / 4;
   constexpr int NIB = DV / 16, NKB = DK / 16;     // row and column tiles
   __shared__ __align__(16) SM sm;
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   const int mn = lane & 15, rq = 4 * (lane >> 4);   // tile column, first tile row of the lane
   const long chain = blockIdx.x;
   const long L = a.seqlen;
-  const int nch = (int)((L + BC - 1) / BC);
+  const int nch = (int)((L + NS - 1) / NS);
   const int ks = a.key_shift;
   const bool fresh = ks == 1 && kpg == nullptr;
   const long qk_base = chain * L * DK;
@@ -217,6 +230,9 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   constexpr int WS_XS = DV * DK, WS_G = WS_XS + BC * DV, WS_CHUNK = WS_G + BC * BC;
   float* __restrict__ ws = a.workspace + chain * (long)nch * WS_CHUNK;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // the keys as the unknowns see them (window 1: the tile itself)
+  float (*XU)[DK + 4] = BW == 1 ? sm.X : sm.XU;
+  const float* nsum = BW == 1 ? sm.nrm : sm.nsum;
 
   // ---- chunk inputs: issue_chunk starts every global load of a chunk into
   // registers (bwd: also q, dO and the chunk's workspace record: start state,
@@ -253,8 +269,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
   auto issue_chunk = [&](uint4 (&val)[NPER], int ci, bool bwd) {
-    const long t0 = (long)ci * BC;
-    const int c = (int)((L - t0) < BC ? (L - t0) : BC);
+    const long t0 = (long)ci * NS;
+    const int c = (int)((L - t0) < NS ? (L - t0) : NS);
 #pragma unroll
     for (int u = 0; u < NPER; ++u) {
       const int g = tid + u * BNT;
@@ -263,9 +279,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         const int r = g < GX ? g : g - GX;
         const int t = r / (DK / 4), k4 = 4 * (r % (DK / 4));
         const long st = t0 + t;
-        if (g < GX) {   // x_t = k_{t - ks}; the carried key x_0 is put in at commit
-          const bool in = t < c && st >= ks;
-          v = ldr_t(rsk, in ? (uint32_t)(((st - ks) * DK + k4) * ES) : PARKED);
+        if (g < GX) {   // tile row t: sample j, x_j = k_{j - ks}; the carried key x_0 is put in at commit
+          const long j = t0 - (BW - 1) + t;
+          const bool in = t < NK && j >= ks && j < L;
+          v = ldr_t(rsk, in ? (uint32_t)(((j - ks) * DK + k4) * ES) : PARKED);
         } else {
           v = ldr_t(rsq, (bwd && t < c) ? (uint32_t)((st * DK + k4) * ES) : PARKED);
         }
@@ -275,7 +292,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         const int t = r / (DV / 4), i4 = 4 * (r % (DV / 4));
         const long st = t0 + t;
         const bool in = t < c;
-        if (which == 0) v = ldr_t(rsv, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
+        const long j = t0 - (BW - 1) + t;     // values: tile row t is sample j
+        if (which == 0) v = ldr_t(rsv, (t < NK && j >= 0 && j < L) ? (uint32_t)((j * DV + i4) * ES) : PARKED);
         else if (which == 1) v = ldr_f(rsdo, (in && bwd) ? (uint32_t)((st * DV + i4) * 4) : PARKED);
         else if (a.beta_kind == 2) v = ldr_t(rsb, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
         else if (a.beta_kind == 1) {   // per-token gain of step t, for every row
@@ -334,30 +352,46 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       }
     }
     if (ci == 0 && ks == 1 && kpg && tid < DK / 4)   // the carried key is x_0
-      *reinterpret_cast<float4*>(&sm.X[0][4 * tid]) = ld4(kpg, chain * DK + 4 * tid);
+      *reinterpret_cast<float4*>(&sm.X[BW - 1][4 * tid]) = ld4(kpg, chain * DK + 4 * tid);
   };
-  auto nrm_and = [&]() {
+  // after a commit: the unknowns' keys (window) and, on wave 0, the tile's
+  // squared norms and their window sums per step
+  auto gather = [&]() {
+    if constexpr (BW > 1) {
+      for (int idx = tid; idx < BC * DK / 4; idx += BNT) {
+        const int u = idx / (DK / 4), k4 = 4 * (idx % (DK / 4));
+        const int s = u / BW, w = u % BW;
+        *reinterpret_cast<float4*>(&sm.XU[u][k4]) = f4(&sm.X[BW - 1 + s - w][k4]);
+      }
+    }
     if (tid < BC) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < DK; k += 4) acc = dot4(f4(&sm.X[tid][k]), f4(&sm.X[tid][k]), acc);
       sm.nrm[tid] = acc;
+      if constexpr (BW > 1) {
+        wave_sync();
+        float n = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BW; ++w) n += tid < NS ? sm.nrm[BW - 1 + tid - w] : 0.0f;
+        sm.nsum[tid] = n;
+      }
     }
   };
   // forward sweep: Gram (strictly lower) and S0 x tiles, also into the workspace
   auto gram_tile = [&](float* wsc) {
-    const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&sm.X[m][k]); },
-                                  [&](int k, int n) { return f4(&sm.X[n][k]); });
+    const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&XU[m][k]); },
+                                  [&](int k, int n) { return f4(&XU[n][k]); });
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = rq + r, s2 = mn;
-      const float gv = (a.regression && s2 < t) ? acc[r] : 0.0f;
+      const int t = rq + r, s2 = mn;   // unknowns: only earlier steps couple
+      const float gv = (a.regression && s2 / BW < t / BW) ? acc[r] : 0.0f;
       sm.G[t][s2] = gv;
       wsc[WS_G + t * BC + s2] = gv;
     }
   };
   auto xs_tile = [&](int ib, float* wsc) {
-    const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&sm.X[m][k]); },
+    const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&XU[m][k]); },
                                   [&](int k, int n) { return f4(&sm.S[16 * ib + n][k]); });
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -373,12 +407,12 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     for (int tt = wave; tt < ntile; tt += BNW) {
       if (tt == 0) {
         const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(&sm.Q[m][k]); },
-                                      [&](int k, int n) { return f4(&sm.X[n][k]); });
+                                      [&](int k, int n) { return f4(&XU[n][k]); });
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.P[rq + r][mn] = mn <= rq + r ? acc[r] : 0.0f;
+        for (int r = 0; r < 4; ++r) sm.P[rq + r][mn] = mn / BW <= rq + r ? acc[r] : 0.0f;   // [step][unknown]
       } else {
         const int kind = (tt - 1) / NIB, ib = (tt - 1) % NIB;
-        const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(kind == 0 ? &sm.Q[m][k] : &sm.X[m][k]); },
+        const floatx4 acc = mtile<DK>(zero4, lane, [&](int m, int k) { return f4(kind == 0 ? &sm.Q[m][k] : &XU[m][k]); },
                                       [&](int k, int n) { return f4(kind == 1 ? &sm.dS[16 * ib + n][k] : &sm.S[16 * ib + n][k]); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -387,7 +421,6 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         }
       }
     }
-    nrm_and();
     if (tid >= BNT - DV) {
       const int i = tid - (BNT - DV);
       float acc = 0.0f;
@@ -396,30 +429,37 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       sm.sds[i] = acc;
     }
   };
-  // lane t of the 16-lane row of value row i: eta, a, g (prefix product by DPP
-  // row shifts), gm = g_{t-1}, zeta
+  // lane u of the 16-lane row of value row i (unknown u, step s = u / BW): eta,
+  // a, g (prefix product by DPP row shifts over the lanes, each step's factor
+  // entering once, on its slot-0 lane), gm = g_{s-1}, zeta
   struct RowScal { float eta, av, g, gm, zeta; };
   auto row_scal_dpp = [&](int i, long t0, int c) __attribute__((always_inline)) {
-    const int t = lane & 15;
+    const int u = lane & 15, s = u / BW;
     RowScal r;
     r.eta = 0.0f;
-    if (t < c && !(fresh && t0 + t == 0)) r.eta = sm.bt[t][i] / (a.eps + sm.nrm[t]);
+    if (s < c && !(fresh && t0 + s == 0)) r.eta = sm.bt[s][i] / (a.eps + nsum[s]);
     r.av = 1.0f - r.eta * a.lambda;
-    float g = r.av;
+    float g = (u % BW == 0) ? r.av : 1.0f;
     g = row_shr_mul<1>(g);
     g = row_shr_mul<2>(g);
     g = row_shr_mul<4>(g);
     g = row_shr_mul<8>(g);
     r.g = g;
-    r.gm = row_shr_fill<1>(g, 1.0f);
+    if constexpr (BW == 1) {
+      r.gm = row_shr_fill<1>(g, 1.0f);
+    } else {   // g at the last lane of the previous step
+      const float gp = __shfl(g, (lane & 48) | ((s * BW + 15) & 15));
+      r.gm = s == 0 ? 1.0f : gp;
+    }
     r.zeta = r.eta / g;
     return r;
   };
   // forward sweep of value row i (lane t): z (and for the backward e, h, eta,
   // g do) into LDS, gC
   auto row_forward = [&](int i, const RowScal& r, bool bwd) __attribute__((always_inline)) {
-    const int t = lane & 15;
-    const float y = sm.Y[t][i], xs = sm.XS[t][i];
+    const int t = lane & 15;   // unknown
+    const int s = t / BW;
+    const float y = sm.Y[BW - 1 + s - t % BW][i], xs = sm.XS[t][i];
     float acc = 0.0f;
     if (a.regression) {
       float grow[16];
@@ -432,8 +472,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     if (bwd) {
       sm.E[t][i] = e;
       sm.H[t][i] = acc;
-      sm.ETA[t][i] = r.eta;
-      sm.GD[t][i] = r.g * sm.dO[t][i];
+      if (t % BW == 0) {   // step quantities
+        sm.ETA[s][i] = r.eta;
+        sm.GD[s][i] = r.g * sm.dO[s][i];
+      }
     }
     const float gc = row_last(r.g);
     if (t == 0) sm.gC[i] = gc;
@@ -446,11 +488,15 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   uint4 pre[NPER];
   issue_chunk(pre, 0, false);
   for (int ci = 0; ci < nch; ++ci) {
-    const long t0 = (long)ci * BC;
-    const int c = (int)((L - t0) < BC ? (L - t0) : BC);
+    const long t0 = (long)ci * NS;
+    const int c = (int)((L - t0) < NS ? (L - t0) : NS);
     commit_chunk(pre, ci, false);
     lds_barrier();
     if (ci + 1 < nch) issue_chunk(pre, ci + 1, false);
+    if constexpr (BW > 1) {
+      gather();
+      lds_barrier();
+    }
     // record the chunk for the backward sweep: start state (all threads); wave 0:
     // Gram and key norms; waves 1..NIB: S0 x tiles
     float* __restrict__ wsc = ws + (long)ci * WS_CHUNK;
@@ -467,7 +513,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           wsc[WS_G + (rq + r) * BC + mn] = 0.0f;
         }
       }
-      nrm_and();
+      if constexpr (BW == 1) gather();
     } else if (wave <= NIB) {
       xs_tile(wave - 1, wsc);
     }
@@ -481,7 +527,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sm.S[16 * ib + rq + r][16 * kb + mn];
       acc = mtile<BC>(acc, lane, [&](int m, int k) { return col4(sm.Z, k, 16 * ib + m); },
-                      [&](int k, int n) { return col4(sm.X, k, 16 * kb + n); });
+                      [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + rq + r;
@@ -502,13 +548,23 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     for (int kk = tid; kk < DK; kk += BNT)
       a.dk[qk_base + (L - 1) * DK + kk] = a.dk_last ? a.dk_last[chain * DK + kk] : 0.0f;
   }
+  if constexpr (BW > 1) {   // no later chunk: nothing carried into the last one
+    for (int idx = tid; idx < 2 * (BW - 1) * DK; idx += BNT) (&sm.dxh[0][0][0])[idx] = 0.0f;
+    for (int idx = tid; idx < 2 * (BW - 1) * DV; idx += BNT) (&sm.dyh[0][0][0])[idx] = 0.0f;
+  }
   issue_chunk(pre, nch - 1, true);
   for (int ci = nch - 1; ci >= 0; --ci) {
-    const long t0 = (long)ci * BC;
-    const int c = (int)((L - t0) < BC ? (L - t0) : BC);
+    const long t0 = (long)ci * NS;
+    const int c = (int)((L - t0) < NS ? (L - t0) : NS);
     commit_chunk(pre, ci, true);
     lds_barrier();
     if (ci > 0) issue_chunk(pre, ci - 1, true);
+    if constexpr (BW > 1) {
+      gather();
+      lds_barrier();
+    } else {
+      gather();   // wave 0: the key norms
+    }
     bwd_products();
     lds_barrier();
     // ---- per-row sweeps on 16-lane DPP rows, shared products on the matrix cores ----
@@ -549,8 +605,17 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       }
       const float dr = r.zeta * (dz - acc2);
       const float w = a.regression ? r.gm * dr : 0.0f;
-      const float dzeta = e * (dz - acc2);
-      const float dgm = a.regression ? -dr * (sm.H[t][i] + sm.XS[t][i]) : 0.0f;
+      float dzeta = e * (dz - acc2);
+      float dgm = a.regression ? -dr * (sm.H[t][i] + sm.XS[t][i]) : 0.0f;
+      const int s = t / BW;
+      if constexpr (BW > 1) {   // step sums over the step's window slots (lanes of a group)
+        dzeta += __shfl_xor(dzeta, 1);
+        dgm += __shfl_xor(dgm, 1);
+        if constexpr (BW == 4) {
+          dzeta += __shfl_xor(dzeta, 2);
+          dgm += __shfl_xor(dgm, 2);
+        }
+      }
       // d gC: s0.ds + sum_t z_t (x_t . ds), a row sum
       float zx = sm.Z[t][i] * sm.XdS[t][i];
       zx += row_shr_fill<1>(zx, 0.0f);
@@ -558,21 +623,26 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       zx += row_shr_fill<4>(zx, 0.0f);
       zx += row_shr_fill<8>(zx, 0.0f);
       const float dgc = row_last(zx) + sm.sds[i];
-      float dg = sm.DGO[t][i] - dzeta * r.zeta / r.g + row_shl_fill<1>(dgm, 0.0f);
-      if (t == BC - 1) dg += dgc;
-      // suffix sums over t' >= t of dg g
-      float suf = dg * r.g;
+      // dgm of the next step (gm_{s+1} = g_s) is BW lanes up
+      float dg = sm.DGO[s][i] - dzeta * r.zeta / r.g + row_shl_fill<BW>(dgm, 0.0f);
+      if (s == NS - 1) dg += dgc;
+      // suffix sums over steps s' >= s of dg g (one lane per step, its last slot)
+      float suf = (t % BW == BW - 1) ? dg * r.g : 0.0f;
       suf += row_shl_fill<1>(suf, 0.0f);
       suf += row_shl_fill<2>(suf, 0.0f);
       suf += row_shl_fill<4>(suf, 0.0f);
       suf += row_shl_fill<8>(suf, 0.0f);
       float deta = dzeta / r.g - a.lambda * (suf / r.av);
-      if (t >= c || (fresh && t0 + t == 0)) deta = 0.0f;
+      if (s >= c || (fresh && t0 + s == 0)) deta = 0.0f;
       sm.W[t][i] = w;
-      sm.DE[t][i] = deta;
-      if (t < c) {
-        a.dv[v_base + (t0 + t) * DV + i] = dr;
-        if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (t0 + t) * DV + i] = deta / (a.eps + sm.nrm[t]);
+      if (t % BW == 0) sm.DE[s][i] = deta;
+      if constexpr (BW == 1) {
+        if (t < c) {
+          a.dv[v_base + (t0 + t) * DV + i] = dr;
+          if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (t0 + t) * DV + i] = deta / (a.eps + sm.nrm[t]);
+        }
+      } else {
+        sm.DR[t][i] = dr;   // d y of the unknown's sample, summed per sample below
       }
     }
     lds_barrier();
@@ -584,8 +654,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rq + r, s2 = mn;
-        if (dg) sm.dG[t][s2] = (a.regression && s2 < t) ? -acc[r] : 0.0f;
-        else sm.dP[t][s2] = s2 <= t ? acc[r] : 0.0f;
+        if (dg) sm.dG[t][s2] = (a.regression && s2 / BW < t / BW) ? -acc[r] : 0.0f;
+        else sm.dP[t][s2] = s2 / BW <= t ? acc[r] : 0.0f;   // [step][unknown]
       }
     }
     if (tid >= BNT - BC) {
@@ -593,7 +663,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < DV; k += 4) acc = dot4(f4(&sm.DE[t][k]), f4(&sm.ETA[t][k]), acc);
-      sm.dn[t] = -acc / (a.eps + sm.nrm[t]);
+      sm.dn[t] = -acc / (a.eps + nsum[t]);   // per step
       if (a.dbeta_t && a.beta_kind == 1 && t < c) {   // a per-token gain feeds every row
         float sde = 0.0f;
 #pragma unroll
@@ -601,7 +671,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           const float4 d4 = f4(&sm.DE[t][k]);
           sde += d4.x + d4.y + d4.z + d4.w;
         }
-        a.dbeta_t[chain * L + t0 + t] = sde / (a.eps + sm.nrm[t]);
+        a.dbeta_t[chain * L + t0 + t] = sde / (a.eps + nsum[t]);
       }
     }
     lds_barrier();
@@ -615,7 +685,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(&sm.GD[m][k]); },
                               [&](int k, int n) { return col4(sm.S, k, 16 * kb + n); });
       acc = mtile<BC>(acc, lane, [&](int m, int k) { return f4(&sm.dP[m][k]); },
-                      [&](int k, int n) { return col4(sm.X, k, 16 * kb + n); });
+                      [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rq + r;
@@ -642,7 +712,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
                         return make_float4(sm.dG[m][k] + sm.dG[k][m], sm.dG[m][k + 1] + sm.dG[k + 1][m],
                                            sm.dG[m][k + 2] + sm.dG[k + 2][m], sm.dG[m][k + 3] + sm.dG[k + 3][m]);
                       },
-                      [&](int k, int n) { return col4(sm.X, k, 16 * kb + n); });
+                      [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
       dxr = mtile<BC>(dxr, lane, [&](int m, int k) { return col4(sm.dP, k, m); },
                       [&](int k, int n) { return col4(sm.Q, k, 16 * kb + n); });
     }
@@ -652,15 +722,19 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rq + r, kk = 16 * kb + mn;
-        float v = dxr[r] + sm.dxp[t][kk] + 2.0f * sm.dn[t] * sm.X[t][kk];
-        const long j = t0 + t - ks;    // x_t = k_j
-        if (t < c) {
-          if (j >= 0) {
-            if (ks == 0 && j == L - 1 && a.dk_last) v += a.dk_last[chain * DK + kk];
-            a.dk[qk_base + j * DK + kk] = v;
-          } else if (a.dk_prev) {
-            a.dk_prev[chain * DK + kk] = v;
+        float v = dxr[r] + sm.dxp[t][kk] + 2.0f * sm.dn[t / BW] * XU[t][kk];
+        if constexpr (BW == 1) {
+          const long j = t0 + t - ks;    // x_t = k_j
+          if (t < c) {
+            if (j >= 0) {
+              if (ks == 0 && j == L - 1 && a.dk_last) v += a.dk_last[chain * DK + kk];
+              a.dk[qk_base + j * DK + kk] = v;
+            } else if (a.dk_prev) {
+              a.dk_prev[chain * DK + kk] = v;
+            }
           }
+        } else {
+          sm.dxp[t][kk] = v;   // d x of the unknown's key, summed per sample below
         }
       }
     }
@@ -680,11 +754,58 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
                         const float4 w4 = col4(sm.W, k, 16 * ib + m);
                         return make_float4(-w4.x, -w4.y, -w4.z, -w4.w);
                       },
-                      [&](int k, int n) { return col4(sm.X, k, 16 * kb + n); });
+                      [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.dS[16 * ib + rq + r][16 * kb + mn] = acc[r];
     }
     lds_barrier();
+    if constexpr (BW > 1) {
+      // d x and d y per sample: the sum over the unknowns that hold it (slot w of
+      // step k - (BW-1) + w for tile row k).  The tile's first BW-1 rows are the
+      // previous chunk's last samples: their sums go to that chunk, which adds
+      // them to its rows NS .. NS+BW-2 (double-buffered by chunk parity).  Nothing
+      // here is touched by the next chunk's commit.
+      const int cur = ci & 1, nxt = (ci + 1) & 1;
+      for (int idx = tid; idx < NK * DK; idx += BNT) {
+        const int k = idx / DK, kk = idx % DK;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BW; ++w) {
+          const int st = k - (BW - 1) + w;
+          if (st >= 0 && st < NS) v += sm.dxp[BW * st + w][kk];
+        }
+        if (k < BW - 1) {
+          sm.dxh[cur][k][kk] = v;
+        } else {
+          if (k >= NS) v += sm.dxh[nxt][k - NS][kk];
+          const long j = t0 - (BW - 1) + k;     // sample; x_j = k_{j - ks}
+          if (j < L) {
+            if (j - ks >= 0) {
+              if (ks == 0 && j == L - 1 && a.dk_last) v += a.dk_last[chain * DK + kk];
+              a.dk[qk_base + (j - ks) * DK + kk] = v;
+            } else if (a.dk_prev) {
+              a.dk_prev[chain * DK + kk] = v;
+            }
+          }
+        }
+      }
+      for (int idx = tid; idx < NK * DV; idx += BNT) {
+        const int k = idx / DV, i = idx % DV;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BW; ++w) {
+          const int st = k - (BW - 1) + w;
+          if (st >= 0 && st < NS) v += sm.DR[BW * st + w][i];
+        }
+        if (k < BW - 1) {
+          sm.dyh[cur][k][i] = v;
+        } else {
+          if (k >= NS) v += sm.dyh[nxt][k - NS][i];
+          const long j = t0 - (BW - 1) + k;
+          if (j < L) a.dv[v_base + j * DV + i] = v;
+        }
+      }
+    }
   }
   if (a.dS0) {
     for (int idx = tid; idx < DV * DK; idx += BNT)
@@ -695,7 +816,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
 template <typename T, int DK, int DV>
 hipError_t launch_bwd3(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((long)a.batch * a.heads));
-  hipLaunchKernelGGL((backward_kernel<T, DK, DV>), grid, dim3(BNT), 0, stream, a);
+  if (a.window == 1) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 1>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 2) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 2>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 4) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 4>), grid, dim3(BNT), 0, stream, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -721,9 +845,10 @@ hipError_t launch_bwd_dk(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv) {
-  // per chunk: start state, S0 x, Gram (fp32)
-  const long nch = (seqlen + BC - 1) / BC;
+size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv, int window) {
+  // per chunk of 16 / window steps: start state, S0 x, Gram (fp32)
+  const long ns = BC / window;
+  const long nch = (seqlen + ns - 1) / ns;
   const long per_chunk = (long)dv * dk + (long)BC * dv + (long)BC * BC;
   return (size_t)batch * heads * nch * per_chunk * sizeof(float);
 }

@@ -54,9 +54,10 @@ struct DecodeArgs {
   int key_shift;     // 1: x = k_prev (then k_prev <- k); 0: x = k, k_prev unused
 };
 
-// Backward of the window-1 chunk form (falcon_backward.hip).
+// Backward of the chunk form, windows 1, 2, 4 (falcon_backward.hip).
 struct BwdArgs {
   int regression;
+  int window;        // 1, 2 or 4
   int key_shift;
   float beta;
   const void* beta_t;
@@ -82,7 +83,7 @@ struct BwdArgs {
   float* dS0;            // may be null
   float* workspace;      // backward_workspace_bytes(...)
 };
-size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv);
+size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv, int window);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
