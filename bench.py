@@ -223,6 +223,14 @@ def main():
                                    "hbm_gbs": nbytes / sec / 1e9,
                                    "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
                                    "algorithmic_bytes": nbytes}
+            # the sliding-window backward (window 4) on the same tokens
+            fn = lambda: fw.bwd_chunk(q, k, v, dO, variant=fw.FALCON_3, beta=cfg["beta"],
+                                      lam=cfg["lam"], eps=cfg["eps"], window=4)
+            sec = time_calls(fn, 4, 1)
+            sec_out["backward_window4"] = {"workload": head_name, "variant": "falcon3",
+                                           "window": 4, "ms_per_call": sec * 1e3,
+                                           "tokens_per_s": B * L / sec,
+                                           "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS}
             del q, k, v, dO
             torch.cuda.empty_cache()
         if args.only in (None, "decode"):
