@@ -54,38 +54,39 @@ template <int DK, int DV, int BW>
 struct BwdLds {
   static constexpr int WR = BW > 1 ? BC : 1;     // rows of the window-only arrays
   static constexpr int WH = BW > 1 ? BW - 1 : 1;
-  float S[DV][DK + 4];        // chunk-start state
-  float dS[DV][DK + 4];       // gradient of the chunk-end state
-  float X[BC][DK + 4];        // key tile: samples t0 - (B-1) + k (shifted keys)
-  float Q[BC][DK + 4];
-  float Y[BC][DV + 4];        // values
-  float dO[BC][DV + 4];
+  static constexpr int KP = DK + 4, VP = DV + 4, BP = BC + 4;   // fp32 row pitches
+  float S[DV][KP];        // chunk-start state
+  float dS[DV][KP];       // gradient of the chunk-end state
+  float X[BC][KP];        // key tile: samples t0 - (B-1) + k (shifted keys)
+  float Q[BC][KP];
+  float Y[BC][VP];        // values
+  float dO[BC][VP];
   float bt[BC][DV];           // gain per step and row
   float nrm[BC];              // squared norms of the key tile rows
   float nsum[BC];             // per step: window sums of the squared norms
-  float XU[WR][DK + 4];       // window: the key of each unknown (step, slot)
-  float DR[WR][DV + 4];       // window: d y per unknown
+  float XU[WR][KP];       // window: the key of each unknown (step, slot)
+  float DR[WR][VP];       // window: d y per unknown
   float dxh[2][WH][DK];       // window: d x of the samples before the chunk (to the next one)
   float dyh[2][WH][DV];
-  float G[BC][BC + 4];        // strictly lower
-  float P[BC][BC + 4];        // lower incl. diagonal
-  float XS[BC][DV + 4];       // s0_i . x_t
-  float QS[BC][DV + 4];       // s0_i . q_t
-  float XdS[BC][DV + 4];      // ds_i . x_t
+  float G[BC][BP];        // strictly lower
+  float P[BC][BP];        // lower incl. diagonal
+  float XS[BC][VP];       // s0_i . x_t
+  float QS[BC][VP];       // s0_i . q_t
+  float XdS[BC][VP];      // ds_i . x_t
   float sds[DV];              // s0_i . ds_i
-  float E[BC][DV + 4];        // residuals
-  float dZ[BC][DV + 4];
-  float H[BC][DV + 4];        // sum_{s<t} G_ts z_s
-  float Z[BC][DV + 4];
-  float W[BC][DV + 4];        // gm_t dr_t (regression), 0 (inner product)
-  float GD[BC][DV + 4];       // g_t do_t
-  float DE[BC][DV + 4];       // d eta
-  float DGO[BC][DV + 4];      // do_t (o_t / g_t)
-  float ETA[BC][DV + 4];
-  float dxp[BC][DK + 4];      // partial dx
+  float E[BC][VP];        // residuals
+  float dZ[BC][VP];
+  float H[BC][VP];        // sum_{s<t} G_ts z_s
+  float Z[BC][VP];
+  float W[BC][VP];        // gm_t dr_t (regression), 0 (inner product)
+  float GD[BC][VP];       // g_t do_t
+  float DE[BC][VP];       // d eta
+  float DGO[BC][VP];      // do_t (o_t / g_t)
+  float ETA[BC][VP];
+  float dxp[BC][KP];      // partial dx
   float gC[DV];
-  float dG[BC][BC + 4];
-  float dP[BC][BC + 4];
+  float dG[BC][BP];
+  float dP[BC][BP];
   float dn[BC];
 };
 
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   float* __restrict__ ws = a.workspace + chain * (long)nch * WS_CHUNK;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   // the keys as the unknowns see them (window 1: the tile itself)
-  float (*XU)[DK + 4] = BW == 1 ? sm.X : sm.XU;
+  float (*XU)[SM::KP] = BW == 1 ? sm.X : sm.XU;
   const float* nsum = BW == 1 ? sm.nrm : sm.nsum;
 
   // ---- chunk inputs: issue_chunk starts every global load of a chunk into

@@ -57,6 +57,7 @@ struct IpLds {
   static constexpr int XR = DK + 16;   // bf16 row: DK (fragment order) + pad
   static constexpr int KR = IK + 4;    // transposed rows: 80 keys + pad
   static constexpr int NP = DK / 4 + 4;
+  static constexpr int OPP = 16 + 4;     // fp32 rows of the partial sums
   uint16_t X[IK][XR];                  // keys, dk in fragment order
   uint16_t XT[DK][KR];                 // keys transposed, keys in natural order
   uint16_t Q[IC][XR];                  // queries, dk in fragment order
@@ -69,7 +70,7 @@ struct IpLds {
   float zp[2][IK + 4];                 // [16 + j] = Z_{j-1} (0 for j <= 0), key j = -16..63
   float zq[2][IK + 4];                 // [16 + j] = Z_{min(j+B-1, C-1)}
   float c63[2][IK];                    // c_{m, C-1}, by chunk parity
-  float opart[4][IC][16 + 4];          // S0 q partial sums of the state waves, [t][row]
+  float opart[4][IC][OPP];             // S0 q partial sums of the state waves, [t][row]
 };
 
 struct IpGeom {

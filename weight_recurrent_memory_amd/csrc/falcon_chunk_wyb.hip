@@ -61,33 +61,39 @@ __device__ __forceinline__ int fpos(int k) {
 template <int DK>
 struct WybLds {
   static constexpr int XR = DK + 16;     // bf16 row: DK (fragment order) + pad
+  static constexpr int TP = CS + 12;     // bf16 rows over the steps of a block
+  static constexpr int HP = NXT + 16;    // bf16 rows over the key tile
+  static constexpr int FP = NXT + 4;     // fp32 rows over the key tile
+  static constexpr int OP = RW + 4;      // fp32 rows over the value rows
+  static constexpr int SP = 16 + 8;      // fp32 rows of a 16 x 16 block
+  // (pads chosen on the whole kernel by the LDS bank-conflict counter)
   uint16_t X[4][CS][XR];                 // key blocks by sub-chunk & 3
   uint16_t Q[4][CS][XR];                 // query blocks
-  uint16_t XT[4][DK][CS + 8];            // key blocks transposed, steps natural
-  uint16_t YT[4][RW][CS + 8];            // value blocks transposed, steps natural
+  uint16_t XT[4][DK][TP];                // key blocks transposed, steps natural
+  uint16_t YT[4][RW][TP];                // value blocks transposed, steps natural
   float knorm[4][CS];
   float beta[4][CS];
-  float G[NXT][NXT + 4];                 // Gram of the key tile
-  float P[CS][NXT + 4];                  // q . x over the tile
+  float G[NXT][FP];                      // Gram of the key tile
+  float P[CS][FP];                       // q . x over the tile
   alignas(16) float gam[2][CS];
   alignas(16) float zeta[2][CS];
   alignas(16) float omega[2][CS];
   alignas(16) float zcum[2][CS];         // prefix sums of zeta
-  float TS[4][16][16 + 4];               // diagonal blocks of T, row-major
-  uint16_t Hxhi[2][NXT][NXT + 8];        // -H_x rows, keys in fragment order
-  uint16_t Hxlo[2][NXT][NXT + 8];
-  uint16_t Qxhi[2][CS][NXT + 8];         // -Q_x rows
-  uint16_t Qxlo[2][CS][NXT + 8];
-  uint16_t Hyhi[2][NXT][NXT + 8];        // H_y rows
-  uint16_t Hylo[2][NXT][NXT + 8];
-  uint16_t Qyhi[2][CS][NXT + 8];         // Q_y rows
-  uint16_t Qylo[2][CS][NXT + 8];
-  float Ufk[2][RW][NXT + 4];             // (H_y Y)[m][i] stored [i][m]
-  float Oy[2][CS][RW + 4];               // (Q_y Y)[t][i]
-  uint16_t Mhi[4][16][NXT + 8];          // -M fragments of the blocked solve, by (block, pair)
-  uint16_t Mlo[4][16][NXT + 8];
-  uint16_t Pfhi[2][CS][NXT + 8];         // P' fragments over the unknowns, by pair of blocks
-  uint16_t Pflo[2][CS][NXT + 8];
+  float TS[4][16][SP];                   // diagonal blocks of T, row-major
+  uint16_t Hxhi[2][NXT][HP];             // -H_x rows, keys in fragment order
+  uint16_t Hxlo[2][NXT][HP];
+  uint16_t Qxhi[2][CS][HP];              // -Q_x rows
+  uint16_t Qxlo[2][CS][HP];
+  uint16_t Hyhi[2][NXT][HP];             // H_y rows
+  uint16_t Hylo[2][NXT][HP];
+  uint16_t Qyhi[2][CS][HP];              // Q_y rows
+  uint16_t Qylo[2][CS][HP];
+  float Ufk[2][RW][FP];                  // (H_y Y)[m][i] stored [i][m]
+  float Oy[2][CS][OP];                   // (Q_y Y)[t][i]
+  uint16_t Mhi[4][16][HP];               // -M fragments of the blocked solve, by (block, pair)
+  uint16_t Mlo[4][16][HP];
+  uint16_t Pfhi[2][CS][HP];              // P' fragments over the unknowns, by pair of blocks
+  uint16_t Pflo[2][CS][HP];
   alignas(16) float cm[2][NXT];          // inner-product family: sum of zeta per key
 };
 
@@ -195,8 +201,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 
   // ---------------- block -1 (before the sequence) is zero ----------------
   for (int idx = tid; idx < CS * SM::XR; idx += NT) (&sm.X[3][0][0])[idx] = 0;
-  for (int idx = tid; idx < DK * (CS + 8); idx += NT) (&sm.XT[3][0][0])[idx] = 0;
-  for (int idx = tid; idx < RW * (CS + 8); idx += NT) (&sm.YT[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < DK * SM::TP; idx += NT) (&sm.XT[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < RW * SM::TP; idx += NT) (&sm.YT[3][0][0])[idx] = 0;
   if (tid < CS) sm.knorm[3][tid] = 0.0f;
   if (a.x_hist) {
     // a resumed sequence: its last B-1 rows are the carried window samples
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     uint16_t* Hlo = fx ? &sm.Hxlo[sb][0][0] : &sm.Hylo[sb][0][0];
     uint16_t* Qhi = fx ? &sm.Qxhi[sb][0][0] : &sm.Qyhi[sb][0][0];
     uint16_t* Qlo = fx ? &sm.Qxlo[sb][0][0] : &sm.Qylo[sb][0][0];
-    constexpr int HS = NXT + 8;
+    constexpr int HS = SM::HP;
 #pragma unroll
     for (int mj = 0; mj < 2; ++mj) {
       floatx4 h = zacc;
