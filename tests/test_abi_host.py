@@ -239,13 +239,14 @@ def test_backward_workspace_size(lib):
     assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 1) == 2 * 3 * 7 * rec
     assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 2) == 2 * 3 * 13 * rec
     assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 4) == 2 * 3 * 25 * rec
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 3) == 0
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 3) == 2 * 3 * 20 * rec
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 5) == 0
     assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32, 1) == 0
     assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32, 1) == 0
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(variant=2, window=3), UNSUPPORTED),        # windows 1, 2, 4 only
+    (dict(variant=2, window=5), UNSUPPORTED),        # windows 1..4 only
     (dict(variant=5, window=8), UNSUPPORTED),
     (dict(variant=0, window=2), INVALID),            # window > 1 outside Falcon-3/3A
     (dict(variant=2, window=0), INVALID),

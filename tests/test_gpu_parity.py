@@ -539,7 +539,7 @@ def test_backward_small(variant, dk, dv, carried, same_step, dtype):
 
 
 @pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
-@pytest.mark.parametrize("window", [2, 4])
+@pytest.mark.parametrize("window", [2, 3, 4])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (32, 16)])
 @pytest.mark.parametrize("carried,same_step,per_token", [(False, False, False), (True, False, True),
                                                          (False, True, True)])

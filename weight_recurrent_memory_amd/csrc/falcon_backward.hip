@@ -205,9 +205,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   using SM = BwdLds<DK, DV, BW>;
   // unknowns u = BW s + w (step s of the chunk, window slot w) on the 16 lanes of a
   // row; the chunk has NS steps and a key tile of NK rows (the BW-1 samples
-  // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w
+  // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w.  With
+  // window 3 lane 15 is past the last step: its tile row NK is zero, so it stays 0.
   constexpr int NS = BC / BW, NK = BW - 1 + NS;
-  static_assert(BC % BW == 0, "window 1, 2 or 4");
+  static_assert(BW >= 1 && BW <= 4, "window 1..4");   // window 3: 15 unknowns, lane 15 idle
   constexpr int GX = BC * DK / 4, GY = BC * DV / 4, GS = DV * DK / 4;
   constexpr int NIB = DV / 16, NKB = DK / 16;     // row and column tiles
   __shared__ __align__(16) SM sm;
@@ -610,11 +611,21 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       float dgm = a.regression ? -dr * (sm.H[t][i] + sm.XS[t][i]) : 0.0f;
       const int s = t / BW;
       if constexpr (BW > 1) {   // step sums over the step's window slots (lanes of a group)
-        dzeta += __shfl_xor(dzeta, 1);
-        dgm += __shfl_xor(dgm, 1);
-        if constexpr (BW == 4) {
-          dzeta += __shfl_xor(dzeta, 2);
-          dgm += __shfl_xor(dgm, 2);
+        if constexpr (BW == 3) {   // groups of three lanes: gather from the group
+          const int g0 = (lane & 48) | (s < NS ? s * 3 : 0);
+          dzeta = __shfl(dzeta, g0) + __shfl(dzeta, g0 + 1) + __shfl(dzeta, g0 + 2);
+          dgm = __shfl(dgm, g0) + __shfl(dgm, g0 + 1) + __shfl(dgm, g0 + 2);
+          if (s >= NS) {   // the idle lane
+            dzeta = 0.0f;
+            dgm = 0.0f;
+          }
+        } else {
+          dzeta += __shfl_xor(dzeta, 1);
+          dgm += __shfl_xor(dgm, 1);
+          if constexpr (BW == 4) {
+            dzeta += __shfl_xor(dzeta, 2);
+            dgm += __shfl_xor(dgm, 2);
+          }
         }
       }
       // d gC: s0.ds + sum_t z_t (x_t . ds), a row sum
@@ -819,6 +830,7 @@ hipError_t launch_bwd3(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((long)a.batch * a.heads));
   if (a.window == 1) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 1>), grid, dim3(BNT), 0, stream, a);
   else if (a.window == 2) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 2>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 3) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 3>), grid, dim3(BNT), 0, stream, a);
   else if (a.window == 4) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 4>), grid, dim3(BNT), 0, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
