@@ -231,14 +231,18 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  * transpose, the decay products), computed in fp32 with the chunk-start states
  * recomputed by a forward sweep.
  *
- * falcon_bwd_workspace_bytes - bytes of device workspace falcon_bwd_chunk needs
- *   (per chunk of floor(16 / window) steps and (batch, head), fp32: the chunk-start
- *   state (dv x dk), S0 x (16 x dv) and the unknowns' Gram (16 x 16)); 0 for
- *   invalid sizes or a window outside 1..4.
+ * falcon_bwd_workspace_bytes - bytes of device workspace falcon_bwd_chunk needs:
+ *   per (batch, head), per slice of R value rows (R = min(dv, 64) with dk <= 64,
+ *   16 with dk = 128; a head's rows are split over dv / R workgroups) and per
+ *   chunk of floor(16 / window) steps, fp32: the chunk-start state (R x dk), S0 x
+ *   (16 x R) and the unknowns' Gram (16 x 16); with two or more slices also each
+ *   slice's partial dq, dk (L x dk each), dk_prev (dk) and per-token dbeta (L),
+ *   which a second kernel adds in slice order.  0 for invalid sizes or a window
+ *   outside 1..4.
  *
  * falcon_bwd_chunk
  *   variant ... k_prev, S0, flags   as falcon_fwd_chunk_ex (flags 0 or
- *             FALCON_SAME_STEP); dk, dv in {16, 32, 64}; dtype bf16 or fp32
+ *             FALCON_SAME_STEP); dk, dv in {16, 32, 64, 128}; dtype bf16 or fp32
  *   window    1, or 2..4 for FALCON_3 / FALCON_3A; a windowed call takes no
  *             start state (S0 must be NULL: its window history is not an input)
  *   dO        [batch, heads, L, dv] float32, gradient of o
@@ -253,8 +257,8 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  *   workspace, workspace_bytes   device scratch of at least
  *             falcon_bwd_workspace_bytes(..., window) bytes, 16-byte aligned
  * Outputs must not overlap each other, the inputs or the workspace.
- * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 4, a
- * windowed start state, or sizes above 64.
+ * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 4 or a
+ * windowed start state.
  */
 unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk, int dv,
                                               int window);

@@ -234,12 +234,22 @@ def _bwd(lib, **over):
 
 
 def test_backward_workspace_size(lib):
-    # per chunk of 16 / window steps and (batch, head): start state, S0 x, Gram (fp32)
-    rec = (32 * 64 + 16 * 32 + 256) * 4
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 1) == 2 * 3 * 7 * rec
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 2) == 2 * 3 * 13 * rec
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 4) == 2 * 3 * 25 * rec
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 3) == 2 * 3 * 20 * rec
+    # per (batch, head), per slice of value rows (all of them up to 64 with dk <= 64,
+    # 16 with dk = 128) and per chunk of floor(16 / window) steps: start state, S0 x,
+    # Gram (fp32); with two or more slices also their partial dq, dk (L x dk each),
+    # dk_prev (dk) and per-token dbeta (L)
+    def size(B, H, L, dk, dv, window):
+        nch = -(-L // (16 // window))
+        rb = min(dv, 64) if dk <= 64 else 16
+        nrg = dv // rb
+        rec = B * H * nrg * nch * (rb * dk + 16 * rb + 256)
+        part = nrg * B * H * (2 * L * dk + dk + L) if nrg > 1 else 0
+        return (rec + part) * 4
+    for w in (1, 2, 3, 4):
+        assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, w) == size(2, 3, 100, 64, 32, w)
+    assert lib.falcon_bwd_workspace_bytes(1, 2, 64, 128, 128, 4) == size(1, 2, 64, 128, 128, 4)
+    assert lib.falcon_bwd_workspace_bytes(1, 1, 64, 16, 16, 1) == size(1, 1, 64, 16, 16, 1)
+    assert lib.falcon_bwd_workspace_bytes(1, 3, 50, 64, 128, 2) == size(1, 3, 50, 64, 128, 2)
     assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 5) == 0
     assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32, 1) == 0
     assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32, 1) == 0
@@ -251,7 +261,7 @@ def test_backward_workspace_size(lib):
     (dict(variant=0, window=2), INVALID),            # window > 1 outside Falcon-3/3A
     (dict(variant=2, window=0), INVALID),
     (dict(variant=2, window=2, k_prev=P[8], S0=P[9]), UNSUPPORTED),   # windowed start state
-    (dict(dk=128), UNSUPPORTED),
+    (dict(dk=256), UNSUPPORTED),
     (dict(flags=2), INVALID),
     (dict(dq=None), INVALID),
     (dict(ws=None), INVALID),

@@ -574,6 +574,39 @@ def test_backward_window(variant, window, dk, dv, carried, same_step, per_token,
     assert max(errs.values()) <= TOL_FP32_MATH, errs
 
 
+@pytest.mark.parametrize("variant,window", [(fw.FALCON_1, 1), (fw.FALCON_2, 1), (fw.FALCON_3, 4),
+                                            (fw.FALCON_3A, 3)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 16), (16, 128)])
+def test_backward_wide(variant, window, dk, dv):
+    """dk or dv = 128: the value rows of a head are split over several workgroups
+    whose partial key and query gradients are summed by a second kernel."""
+    per_ch = variant == fw.FALCON_2
+    L = 29
+    inp = seq_inputs(2, 1, L, dk, dv, seed=840 + variant + dk + dv, dtype="bf16",
+                     beta_per_channel=per_ch, beta_per_token=not per_ch, with_k_prev=True,
+                     with_S0=window == 1, s_std=0.2)
+    rng = np.random.default_rng(841 + variant)
+    dO = rng.standard_normal((2, 1, L, dv)).astype(np.float32)
+    dS_L = rng.standard_normal((2, 1, dv, dk)).astype(np.float32)
+    dk_last = rng.standard_normal((2, 1, dk)).astype(np.float32)
+    dev = lambda n: to_dev(torch, inp[n], torch.bfloat16) if n in inp else None
+    f32 = lambda a: to_dev(torch, a, torch.float32)
+    got = fw.bwd_chunk(dev("q"), dev("k"), dev("v"), f32(dO), variant=variant, beta=None,
+                       lam=0.02, eps=1e-6, window=window, beta_t=dev("beta_t"),
+                       k_prev=dev("k_prev"),
+                       S0=to_dev(torch, inp["S0"], torch.float32) if "S0" in inp else None,
+                       dS_L=f32(dS_L), dk_last=f32(dk_last))
+    torch.cuda.synchronize()
+    ref = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta=None, lam=0.02,
+                             eps=1e-6, window=window, beta_t=inp["beta_t"],
+                             k_prev=inp["k_prev"], S0=inp.get("S0"), dS_L=dS_L, dk_last=dk_last)
+    assert set(got) == set(ref)
+    errs = {n: _grad_err(got[n].cpu().numpy(), ref[n]) for n in ref}
+    print("backward wide v%d w%d dk %d dv %d: %s" % (variant, window, dk, dv,
+                                                    {n: "%.2e" % e for n, e in errs.items()}))
+    assert max(errs.values()) <= TOL_FP32_MATH, errs
+
+
 def test_backward_8x12x2048x64_sampled():
     """Headline workload: all chains on the GPU, two chains recomputed by the oracle."""
     cfg = WORKLOADS["chunk_8x12x2048x64"]

@@ -338,7 +338,6 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
   // which this entry point does not take
   if (!bwd_window(window)) return FALCON_ERR_UNSUPPORTED;
   if (window > 1 && S0) return FALCON_ERR_UNSUPPORTED;
-  if (dk > 64 || dv > 64) return FALCON_ERR_UNSUPPORTED;
   const size_t es = dtype == FALCON_BF16 ? 2 : 4;
   const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
   const size_t need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);

@@ -50,30 +50,30 @@ constexpr int BC = 16;        // chunk length of the backward
 constexpr int BNT = 512;
 constexpr int BNW = BNT / 64;
 
-template <int DK, int DV, int BW>
+template <int DK, int RB, int BW>
 struct BwdLds {
   static constexpr int WR = BW > 1 ? BC : 1;     // rows of the window-only arrays
   static constexpr int WH = BW > 1 ? BW - 1 : 1;
-  static constexpr int KP = DK + 4, VP = DV + 4, BP = BC + 4;   // fp32 row pitches
-  float S[DV][KP];        // chunk-start state
-  float dS[DV][KP];       // gradient of the chunk-end state
+  static constexpr int KP = DK + 4, VP = RB + 4, BP = BC + 4;   // fp32 row pitches
+  float S[RB][KP];        // chunk-start state
+  float dS[RB][KP];       // gradient of the chunk-end state
   float X[BC][KP];        // key tile: samples t0 - (B-1) + k (shifted keys)
   float Q[BC][KP];
   float Y[BC][VP];        // values
   float dO[BC][VP];
-  float bt[BC][DV];           // gain per step and row
+  float bt[BC][RB];           // gain per step and row
   float nrm[BC];              // squared norms of the key tile rows
   float nsum[BC];             // per step: window sums of the squared norms
   float XU[WR][KP];       // window: the key of each unknown (step, slot)
   float DR[WR][VP];       // window: d y per unknown
   float dxh[2][WH][DK];       // window: d x of the samples before the chunk (to the next one)
-  float dyh[2][WH][DV];
+  float dyh[2][WH][RB];
   float G[BC][BP];        // strictly lower
   float P[BC][BP];        // lower incl. diagonal
   float XS[BC][VP];       // s0_i . x_t
   float QS[BC][VP];       // s0_i . q_t
   float XdS[BC][VP];      // ds_i . x_t
-  float sds[DV];              // s0_i . ds_i
+  float sds[RB];              // s0_i . ds_i
   float E[BC][VP];        // residuals
   float dZ[BC][VP];
   float H[BC][VP];        // sum_{s<t} G_ts z_s
@@ -84,7 +84,7 @@ struct BwdLds {
   float DGO[BC][VP];      // do_t (o_t / g_t)
   float ETA[BC][VP];
   float dxp[BC][KP];      // partial dx
-  float gC[DV];
+  float gC[RB];
   float dG[BC][BP];
   float dP[BC][BP];
   float dn[BC];
@@ -200,17 +200,17 @@ __device__ __forceinline__ floatx4 mtile(floatx4 acc, int lane, FA fa, FB fb) {
   return acc;
 }
 
-template <typename T, int DK, int DV, int BW>
+template <typename T, int DK, int RB, int BW>
 __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
-  using SM = BwdLds<DK, DV, BW>;
+  using SM = BwdLds<DK, RB, BW>;
   // unknowns u = BW s + w (step s of the chunk, window slot w) on the 16 lanes of a
   // row; the chunk has NS steps and a key tile of NK rows (the BW-1 samples
   // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w.  With
   // window 3 lane 15 is past the last step: its tile row NK is zero, so it stays 0.
   constexpr int NS = BC / BW, NK = BW - 1 + NS;
   static_assert(BW >= 1 && BW <= 4, "window 1..4");   // window 3: 15 unknowns, lane 15 idle
-  constexpr int GX = BC * DK / 4, GY = BC * DV / 4, GS = DV * DK / 4;
-  constexpr int NIB = DV / 16, NKB = DK / 16;     // row and column tiles
+  constexpr int GX = BC * DK / 4, GY = BC * RB / 4, GS = RB * DK / 4;
+  constexpr int NIB = RB / 16, NKB = DK / 16;     // row and column tiles
   __shared__ __align__(16) SM sm;
   const T* __restrict__ qg = static_cast<const T*>(a.q);
   const T* __restrict__ kg = static_cast<const T*>(a.k);
@@ -221,16 +221,46 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int mn = lane & 15, rq = 4 * (lane >> 4);   // tile column, first tile row of the lane
-  const long chain = blockIdx.x;
+  // workgroup = (chain, slice of RB value rows); the slices of a chain share an XCD
+  const int dvf = a.ndv, nrg = dvf / RB;
+  long chain;
+  int rg;
+  {
+    const int b = blockIdx.x;
+    const int nchain = a.batch * a.heads;
+    if (nchain % 8 == 0) {
+      const int xcd = b & 7, slot = b >> 3;
+      chain = xcd + 8 * (slot / nrg);
+      rg = slot % nrg;
+    } else {
+      chain = b / nrg;
+      rg = b % nrg;
+    }
+  }
+  const int i0 = rg * RB;                          // first value row of the slice
   const long L = a.seqlen;
   const int nch = (int)((L + NS - 1) / NS);
   const int ks = a.key_shift;
   const bool fresh = ks == 1 && kpg == nullptr;
   const long qk_base = chain * L * DK;
-  const long v_base = chain * L * DV;
+  const long v_base = chain * L * dvf;
   // workspace per chunk: start state, S0 x, Gram
-  constexpr int WS_XS = DV * DK, WS_G = WS_XS + BC * DV, WS_CHUNK = WS_G + BC * BC;
-  float* __restrict__ ws = a.workspace + chain * (long)nch * WS_CHUNK;
+  constexpr int WS_XS = RB * DK, WS_G = WS_XS + BC * RB, WS_CHUNK = WS_G + BC * BC;
+  float* __restrict__ ws = a.workspace + (chain * nrg + rg) * (long)nch * WS_CHUNK;
+  // cross-row sums (dq, dk, dk_prev, per-token dbeta): with several slices each
+  // writes its partial sums to the workspace (after the chunk records) and a
+  // second kernel adds them in slice order; with one slice, straight to the outputs
+  const long BH = (long)a.batch * a.heads;
+  float* __restrict__ part = a.workspace + BH * nrg * (long)nch * WS_CHUNK;
+  const bool split = nrg > 1;
+  float* __restrict__ oq = split ? part + rg * (BH * L * DK) : a.dq;
+  float* __restrict__ ok = split ? part + (nrg + rg) * (BH * L * DK) : a.dk;
+  float* __restrict__ okp = split ? (a.dk_prev ? part + 2 * nrg * (BH * L * DK) + rg * (BH * DK) : nullptr) : a.dk_prev;
+  float* __restrict__ odb = split ? ((a.dbeta_t && a.beta_kind == 1)
+                                         ? part + 2 * nrg * (BH * L * DK) + nrg * (BH * DK) + rg * (BH * L)
+                                         : nullptr)
+                                 : a.dbeta_t;
+  const float* __restrict__ dkl = split ? nullptr : a.dk_last;   // with slices, added by the sum kernel
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
   // the keys as the unknowns see them (window 1: the tile itself)
   float (*XU)[SM::KP] = BW == 1 ? sm.X : sm.XU;
@@ -252,9 +282,9 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   };
   const auto rsk = rsrc(kg + qk_base, L * DK * ES);
   const auto rsq = rsrc(qg + qk_base, L * DK * ES);
-  const auto rsv = rsrc(vg + v_base, L * DV * ES);
-  const auto rsdo = rsrc(a.dO + v_base, L * DV * 4);
-  const auto rsb = a.beta_kind == 2 ? rsrc(bg + v_base, L * DV * ES)
+  const auto rsv = rsrc(vg + v_base, L * dvf * ES);
+  const auto rsdo = rsrc(a.dO + v_base, L * dvf * 4);
+  const auto rsb = a.beta_kind == 2 ? rsrc(bg + v_base, L * dvf * ES)
                                     : (a.beta_kind == 1 ? rsrc(bg + chain * L, L * ES) : rsrc(vg, 0));
   const auto rsws = rsrc(ws, (long)nch * WS_CHUNK * 4);
   auto ldr_t = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
@@ -291,13 +321,13 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       } else if (g < 2 * GX + 2 * GY + GY) {
         const int r0 = g - 2 * GX;
         const int which = r0 / GY, r = r0 % GY;
-        const int t = r / (DV / 4), i4 = 4 * (r % (DV / 4));
+        const int t = r / (RB / 4), i4 = 4 * (r % (RB / 4));
         const long st = t0 + t;
         const bool in = t < c;
         const long j = t0 - (BW - 1) + t;     // values: tile row t is sample j
-        if (which == 0) v = ldr_t(rsv, (t < NK && j >= 0 && j < L) ? (uint32_t)((j * DV + i4) * ES) : PARKED);
-        else if (which == 1) v = ldr_f(rsdo, (in && bwd) ? (uint32_t)((st * DV + i4) * 4) : PARKED);
-        else if (a.beta_kind == 2) v = ldr_t(rsb, in ? (uint32_t)((st * DV + i4) * ES) : PARKED);
+        if (which == 0) v = ldr_t(rsv, (t < NK && j >= 0 && j < L) ? (uint32_t)((j * dvf + i0 + i4) * ES) : PARKED);
+        else if (which == 1) v = ldr_f(rsdo, (in && bwd) ? (uint32_t)((st * dvf + i0 + i4) * 4) : PARKED);
+        else if (a.beta_kind == 2) v = ldr_t(rsb, in ? (uint32_t)((st * dvf + i0 + i4) * ES) : PARKED);
         else if (a.beta_kind == 1) {   // per-token gain of step t, for every row
           uint32_t b;
           if constexpr (sizeof(T) == 2) b = __builtin_amdgcn_raw_buffer_load_b16(rsb, in ? (uint32_t)(st * ES) : PARKED, 0, 0);
@@ -324,7 +354,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       } else if (g < 2 * GX + 2 * GY + GY) {
         const int r0 = g - 2 * GX;
         const int which = r0 / GY, r = r0 % GY;
-        const int t = r / (DV / 4), i4 = 4 * (r % (DV / 4));
+        const int t = r / (RB / 4), i4 = 4 * (r % (RB / 4));
         if (which == 0) *reinterpret_cast<float4*>(&sm.Y[t][i4]) = cvt4(val[u], vg);
         else if (which == 1) *reinterpret_cast<float4*>(&sm.dO[t][i4]) = cvt4(val[u], a.dO);
         else {
@@ -347,7 +377,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           const int e = 4 * (g - (NG - WS_CHUNK / 4));
           float* dst;
           if (e < WS_XS) dst = &sm.S[e / DK][e % DK];
-          else if (e < WS_G) dst = &sm.XS[(e - WS_XS) / DV][(e - WS_XS) % DV];
+          else if (e < WS_G) dst = &sm.XS[(e - WS_XS) / RB][(e - WS_XS) % RB];
           else dst = &sm.G[(e - WS_G) / BC][(e - WS_G) % BC];
           *reinterpret_cast<float4*>(dst) = v;
         }
@@ -399,7 +429,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int t = rq + r, i = 16 * ib + mn;
       sm.XS[t][i] = acc[r];
-      wsc[WS_XS + t * DV + i] = acc[r];
+      wsc[WS_XS + t * RB + i] = acc[r];
     }
   };
   // backward sweep: q.x (lower incl. diagonal), S0 q, dS x tiles; s0.ds and the
@@ -423,8 +453,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         }
       }
     }
-    if (tid >= BNT - DV) {
-      const int i = tid - (BNT - DV);
+    if (tid >= BNT - RB) {
+      const int i = tid - (BNT - RB);
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < DK; k += 4) acc = dot4(f4(&sm.S[i][k]), f4(&sm.dS[i][k]), acc);
@@ -483,9 +513,9 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     if (t == 0) sm.gC[i] = gc;
   };
   // ================= forward sweep: chunk-start states =================
-  for (int idx = tid; idx < DV * DK; idx += BNT) {
+  for (int idx = tid; idx < RB * DK; idx += BNT) {
     const int i = idx / DK, kk = idx % DK;
-    sm.S[i][kk] = a.S0 ? a.S0[(chain * DV + i) * DK + kk] : 0.0f;
+    sm.S[i][kk] = a.S0 ? a.S0[(chain * dvf + i0 + i) * DK + kk] : 0.0f;
   }
   uint4 pre[NPER];
   issue_chunk(pre, 0, false);
@@ -520,7 +550,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       xs_tile(wave - 1, wsc);
     }
     lds_barrier();
-    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), false);
+    for (int i = 4 * wave + (lane >> 4); i < RB; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), false);
     lds_barrier();
     // S <- gC (S + Z^T X): tiles (ib, kb)
     for (int tt = wave; tt < NIB * NKB; tt += BNW) {
@@ -542,17 +572,17 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   // the workspace records written above are read back by other threads below
   __syncthreads();
   // ================= backward sweep =================
-  for (int idx = tid; idx < DV * DK; idx += BNT) {
+  for (int idx = tid; idx < RB * DK; idx += BNT) {
     const int i = idx / DK, kk = idx % DK;
-    sm.dS[i][kk] = a.dS_L ? a.dS_L[(chain * DV + i) * DK + kk] : 0.0f;
+    sm.dS[i][kk] = a.dS_L ? a.dS_L[(chain * dvf + i0 + i) * DK + kk] : 0.0f;
   }
-  if (ks == 1) {   // k_{L-1} only leaves the call as k_last
+  if (ks == 1 && !split) {   // k_{L-1} only leaves the call as k_last
     for (int kk = tid; kk < DK; kk += BNT)
       a.dk[qk_base + (L - 1) * DK + kk] = a.dk_last ? a.dk_last[chain * DK + kk] : 0.0f;
   }
   if constexpr (BW > 1) {   // no later chunk: nothing carried into the last one
     for (int idx = tid; idx < 2 * (BW - 1) * DK; idx += BNT) (&sm.dxh[0][0][0])[idx] = 0.0f;
-    for (int idx = tid; idx < 2 * (BW - 1) * DV; idx += BNT) (&sm.dyh[0][0][0])[idx] = 0.0f;
+    for (int idx = tid; idx < 2 * (BW - 1) * RB; idx += BNT) (&sm.dyh[0][0][0])[idx] = 0.0f;
   }
   issue_chunk(pre, nch - 1, true);
   for (int ci = nch - 1; ci >= 0; --ci) {
@@ -570,7 +600,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     bwd_products();
     lds_barrier();
     // ---- per-row sweeps on 16-lane DPP rows, shared products on the matrix cores ----
-    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), true);
+    for (int i = 4 * wave + (lane >> 4); i < RB; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), true);
     lds_barrier();
     // o/g = QS + P Z (kept as do o/g), dZ = P^T GD + gC XdS: tiles (kind, ib)
     for (int tt = wave; tt < 2 * NIB; tt += BNW) {
@@ -594,7 +624,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     }
     lds_barrier();
     // transposed sweep and the scalar chain of each row (lane t of its 16-lane row)
-    for (int i = 4 * wave + (lane >> 4); i < DV; i += 4 * BNW) {
+    for (int i = 4 * wave + (lane >> 4); i < RB; i += 4 * BNW) {
       const int t = lane & 15;
       const RowScal r = row_scal_dpp(i, t0, c);
       const float dz = sm.dZ[t][i], e = sm.E[t][i];
@@ -650,8 +680,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       if (t % BW == 0) sm.DE[s][i] = deta;
       if constexpr (BW == 1) {
         if (t < c) {
-          a.dv[v_base + (t0 + t) * DV + i] = dr;
-          if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (t0 + t) * DV + i] = deta / (a.eps + sm.nrm[t]);
+          a.dv[v_base + (t0 + t) * dvf + i0 + i] = dr;
+          if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (t0 + t) * dvf + i0 + i] = deta / (a.eps + sm.nrm[t]);
         }
       } else {
         sm.DR[t][i] = dr;   // d y of the unknown's sample, summed per sample below
@@ -661,7 +691,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     // ---- sums over value rows: dG, dP (matrix cores), dn ----
     for (int tt = wave; tt < 2; tt += BNW) {
       const bool dg = tt == 0;
-      const floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(dg ? &sm.W[m][k] : &sm.GD[m][k]); },
+      const floatx4 acc = mtile<RB>(zero4, lane, [&](int m, int k) { return f4(dg ? &sm.W[m][k] : &sm.GD[m][k]); },
                                     [&](int k, int n) { return f4(&sm.Z[n][k]); });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -674,81 +704,106 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       const int t = tid - (BNT - BC);
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < DV; k += 4) acc = dot4(f4(&sm.DE[t][k]), f4(&sm.ETA[t][k]), acc);
+      for (int k = 0; k < RB; k += 4) acc = dot4(f4(&sm.DE[t][k]), f4(&sm.ETA[t][k]), acc);
       sm.dn[t] = -acc / (a.eps + nsum[t]);   // per step
-      if (a.dbeta_t && a.beta_kind == 1 && t < c) {   // a per-token gain feeds every row
+      if (odb && a.beta_kind == 1 && t < c) {   // a per-token gain feeds every row
         float sde = 0.0f;
 #pragma unroll
-        for (int k = 0; k < DV; k += 4) {
+        for (int k = 0; k < RB; k += 4) {
           const float4 d4 = f4(&sm.DE[t][k]);
           sde += d4.x + d4.y + d4.z + d4.w;
         }
-        a.dbeta_t[chain * L + t0 + t] = sde / (a.eps + nsum[t]);
+        odb[chain * L + t0 + t] = sde / (a.eps + nsum[t]);
       }
     }
     lds_barrier();
-    // ---- dq and dx, column tiles kb: waves 0..NKB-1 take dq and the gC z ds part
-    // of dx (to LDS); waves NKB..2NKB-1 the rest of dx, completed after the barrier
-    floatx4 dxr = zero4;
-    const bool dxw = wave >= NKB && wave < 2 * NKB;
-    if (wave < NKB) {
-      const int kb = wave;
+    // ---- dq and dx by column tiles kb ----
+    // dx of unknown t, column kk: to the key's gradient (window 1) or to LDS for the
+    // per-sample sums (windows)
+    auto dx_out = [&](int t, int kk, float v) __attribute__((always_inline)) {
+      if constexpr (BW == 1) {
+        const long j = t0 + t - ks;    // x_t = k_j
+        if (t < c) {
+          if (j >= 0) {
+            if (ks == 0 && j == L - 1 && dkl) v += dkl[chain * DK + kk];
+            ok[qk_base + j * DK + kk] = v;
+          } else if (okp) {
+            okp[chain * DK + kk] = v;
+          }
+        }
+      } else {
+        sm.dxp[t][kk] = v;   // d x of the unknown's key, summed per sample below
+      }
+    };
+    auto dq_tile = [&](int kb) __attribute__((always_inline)) {
       // dq_t = sum_i g_t do_t s0_i + sum_s dP_ts x_s
-      floatx4 acc = mtile<DV>(zero4, lane, [&](int m, int k) { return f4(&sm.GD[m][k]); },
+      floatx4 acc = mtile<RB>(zero4, lane, [&](int m, int k) { return f4(&sm.GD[m][k]); },
                               [&](int k, int n) { return col4(sm.S, k, 16 * kb + n); });
       acc = mtile<BC>(acc, lane, [&](int m, int k) { return f4(&sm.dP[m][k]); },
                       [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = rq + r;
-        if (t < c) a.dq[qk_base + (t0 + t) * DK + 16 * kb + mn] = acc[r];
+        if (t < c) oq[qk_base + (t0 + t) * DK + 16 * kb + mn] = acc[r];
       }
-      // sum_i gC_i z_t ds_i
-      acc = mtile<DV>(zero4, lane, [&](int m, int k) {
-                        const float4 z4 = f4(&sm.Z[m][k]);
-                        const float4 g4 = f4(&sm.gC[k]);
-                        return make_float4(g4.x * z4.x, g4.y * z4.y, g4.z * z4.z, g4.w * z4.w);
-                      },
-                      [&](int k, int n) { return col4(sm.dS, k, 16 * kb + n); });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.dxp[rq + r][16 * kb + mn] = acc[r];
-    } else if (dxw) {
-      const int kb = wave - NKB;
-      // -sum_i w_t s0_i + sum_s (dG_ts + dG_st) x_s + sum_t' dP_t't q_t'
-      dxr = mtile<DV>(zero4, lane, [&](int m, int k) {
+    };
+    auto dx_gz = [&](int kb) __attribute__((always_inline)) {   // sum_i gC_i z_t ds_i
+      return mtile<RB>(zero4, lane, [&](int m, int k) {
+                         const float4 z4 = f4(&sm.Z[m][k]);
+                         const float4 g4 = f4(&sm.gC[k]);
+                         return make_float4(g4.x * z4.x, g4.y * z4.y, g4.z * z4.z, g4.w * z4.w);
+                       },
+                       [&](int k, int n) { return col4(sm.dS, k, 16 * kb + n); });
+    };
+    // -sum_i w_t s0_i + sum_s (dG_ts + dG_st) x_s + sum_t' dP_t't q_t'
+    auto dx_rest = [&](int kb, floatx4 acc) __attribute__((always_inline)) {
+      acc = mtile<RB>(acc, lane, [&](int m, int k) {
                         const float4 w4 = f4(&sm.W[m][k]);
                         return make_float4(-w4.x, -w4.y, -w4.z, -w4.w);
                       },
                       [&](int k, int n) { return col4(sm.S, k, 16 * kb + n); });
-      dxr = mtile<BC>(dxr, lane, [&](int m, int k) {
+      acc = mtile<BC>(acc, lane, [&](int m, int k) {
                         return make_float4(sm.dG[m][k] + sm.dG[k][m], sm.dG[m][k + 1] + sm.dG[k + 1][m],
                                            sm.dG[m][k + 2] + sm.dG[k + 2][m], sm.dG[m][k + 3] + sm.dG[k + 3][m]);
                       },
                       [&](int k, int n) { return col4(XU, k, 16 * kb + n); });
-      dxr = mtile<BC>(dxr, lane, [&](int m, int k) { return col4(sm.dP, k, m); },
-                      [&](int k, int n) { return col4(sm.Q, k, 16 * kb + n); });
-    }
-    lds_barrier();
-    if (dxw) {
-      const int kb = wave - NKB;
+      return mtile<BC>(acc, lane, [&](int m, int k) { return col4(sm.dP, k, m); },
+                       [&](int k, int n) { return col4(sm.Q, k, 16 * kb + n); });
+    };
+    if constexpr (2 * NKB <= BNW) {
+      // waves 0..NKB-1: dq and the gC z ds part of dx (to LDS); waves NKB..2NKB-1:
+      // the rest of dx, completed after the barrier
+      floatx4 dxr = zero4;
+      const bool dxw = wave >= NKB && wave < 2 * NKB;
+      if (wave < NKB) {
+        dq_tile(wave);
+        const floatx4 acc = dx_gz(wave);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rq + r, kk = 16 * kb + mn;
-        float v = dxr[r] + sm.dxp[t][kk] + 2.0f * sm.dn[t / BW] * XU[t][kk];
-        if constexpr (BW == 1) {
-          const long j = t0 + t - ks;    // x_t = k_j
-          if (t < c) {
-            if (j >= 0) {
-              if (ks == 0 && j == L - 1 && a.dk_last) v += a.dk_last[chain * DK + kk];
-              a.dk[qk_base + j * DK + kk] = v;
-            } else if (a.dk_prev) {
-              a.dk_prev[chain * DK + kk] = v;
-            }
-          }
-        } else {
-          sm.dxp[t][kk] = v;   // d x of the unknown's key, summed per sample below
+        for (int r = 0; r < 4; ++r) sm.dxp[rq + r][16 * wave + mn] = acc[r];
+      } else if (dxw) {
+        dxr = dx_rest(wave - NKB, zero4);
+      }
+      lds_barrier();
+      if (dxw) {
+        const int kb = wave - NKB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rq + r, kk = 16 * kb + mn;
+          dx_out(t, kk, dxr[r] + sm.dxp[t][kk] + 2.0f * sm.dn[t / BW] * XU[t][kk]);
         }
       }
+    } else {
+      // every wave takes whole column tiles (dk = 128)
+      for (int kb = wave; kb < NKB; kb += BNW) {
+        dq_tile(kb);
+        const floatx4 acc = dx_rest(kb, dx_gz(kb));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rq + r, kk = 16 * kb + mn;
+          dx_out(t, kk, acc[r] + 2.0f * sm.dn[t / BW] * XU[t][kk]);
+        }
+      }
+      lds_barrier();
     }
     // ---- dS <- gC dS + sum_t g_t do_t q_t - sum_t w_t x_t: tiles (ib, kb); every
     // reader of dS finished before the barrier above ----
@@ -793,16 +848,16 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           const long j = t0 - (BW - 1) + k;     // sample; x_j = k_{j - ks}
           if (j < L) {
             if (j - ks >= 0) {
-              if (ks == 0 && j == L - 1 && a.dk_last) v += a.dk_last[chain * DK + kk];
-              a.dk[qk_base + (j - ks) * DK + kk] = v;
-            } else if (a.dk_prev) {
-              a.dk_prev[chain * DK + kk] = v;
+              if (ks == 0 && j == L - 1 && dkl) v += dkl[chain * DK + kk];
+              ok[qk_base + (j - ks) * DK + kk] = v;
+            } else if (okp) {
+              okp[chain * DK + kk] = v;
             }
           }
         }
       }
-      for (int idx = tid; idx < NK * DV; idx += BNT) {
-        const int k = idx / DV, i = idx % DV;
+      for (int idx = tid; idx < NK * RB; idx += BNT) {
+        const int k = idx / RB, i = idx % RB;
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < BW; ++w) {
@@ -814,34 +869,88 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         } else {
           if (k >= NS) v += sm.dyh[nxt][k - NS][i];
           const long j = t0 - (BW - 1) + k;
-          if (j < L) a.dv[v_base + j * DV + i] = v;
+          if (j < L) a.dv[v_base + j * dvf + i0 + i] = v;
         }
       }
     }
   }
   if (a.dS0) {
-    for (int idx = tid; idx < DV * DK; idx += BNT)
-      a.dS0[(chain * DV + idx / DK) * DK + idx % DK] = sm.dS[idx / DK][idx % DK];
+    for (int idx = tid; idx < RB * DK; idx += BNT)
+      a.dS0[(chain * dvf + i0 + idx / DK) * DK + idx % DK] = sm.dS[idx / DK][idx % DK];
   }
 }
 
-template <typename T, int DK, int DV>
-hipError_t launch_bwd3(const BwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((long)a.batch * a.heads));
-  if (a.window == 1) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 1>), grid, dim3(BNT), 0, stream, a);
-  else if (a.window == 2) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 2>), grid, dim3(BNT), 0, stream, a);
-  else if (a.window == 3) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 3>), grid, dim3(BNT), 0, stream, a);
-  else if (a.window == 4) hipLaunchKernelGGL((backward_kernel<T, DK, DV, 4>), grid, dim3(BNT), 0, stream, a);
+// Sum of the slices' partial dq, dk, dk_prev and per-token dbeta, in slice order
+// (deterministic); dk_last enters here: k_{L-1} is k_last itself with the previous
+// pairing, an input key of the last sample with the same-step pairing.
+__global__ __launch_bounds__(256) void backward_sum_kernel(BwdArgs a, int nrg, const float* part) {
+  const long BH = (long)a.batch * a.heads, L = a.seqlen;
+  const int DK = a.ndk;
+  const long nq = BH * L * DK;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nkp = a.dk_prev ? BH * DK : 0;
+  const long nb = (a.dbeta_t && a.beta_kind == 1) ? BH * L : 0;
+  if (e < nq) {
+    float q = 0.0f, k = 0.0f;
+    for (int r = 0; r < nrg; ++r) {
+      q += part[r * nq + e];
+      k += part[(nrg + r) * nq + e];
+    }
+    const long chain = e / (L * DK), t = (e / DK) % L, kk = e % DK;
+    if (t == L - 1) {
+      const float dl = a.dk_last ? a.dk_last[chain * DK + kk] : 0.0f;
+      k = a.key_shift ? dl : k + dl;
+    }
+    a.dq[e] = q;
+    a.dk[e] = k;
+  } else if (e < nq + nkp) {
+    const long f = e - nq;
+    float v = 0.0f;
+    for (int r = 0; r < nrg; ++r) v += part[2 * nrg * nq + r * (BH * DK) + f];
+    a.dk_prev[f] = v;
+  } else if (e < nq + nkp + nb) {
+    const long f = e - nq - nkp;
+    float v = 0.0f;
+    for (int r = 0; r < nrg; ++r) v += part[2 * nrg * nq + nrg * (BH * DK) + r * (BH * L) + f];
+    a.dbeta_t[f] = v;
+  }
+}
+
+// value rows per workgroup (a head's rows are split over dv / RB workgroups): all
+// of them (up to 64) when the state and its gradient fit LDS with dk <= 64 (the
+// per-chunk work is latency-bound, so a narrower slice gains nothing and repeats
+// the dk-wide products); slices of 16 rows for dk = 128
+__host__ __device__ constexpr int bwd_rows(int dk, int dv) { return dk <= 64 ? (dv < 64 ? dv : 64) : 16; }
+
+template <typename T, int DK, int RB>
+hipError_t launch_bwd_rb(const BwdArgs& a, hipStream_t stream) {
+  const int nrg = a.ndv / RB;
+  const dim3 grid((unsigned)((long)a.batch * a.heads * nrg));
+  if (a.window == 1) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 1>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 2) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 2>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 3) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 3>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 4) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 4>), grid, dim3(BNT), 0, stream, a);
   else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nrg == 1) return e;
+  const long BH = (long)a.batch * a.heads;
+  const long ns = BC / a.window, nch = (a.seqlen + ns - 1) / ns;
+  const float* part = a.workspace + BH * nrg * nch * ((long)RB * DK + (long)BC * RB + (long)BC * BC);
+  const long n = BH * a.seqlen * DK + (a.dk_prev ? BH * DK : 0) + ((a.dbeta_t && a.beta_kind == 1) ? BH * a.seqlen : 0);
+  hipLaunchKernelGGL(backward_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, nrg, part);
   return hipGetLastError();
 }
 
 template <typename T, int DK>
-hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t stream) {
-  switch (a.ndv) {
-    case 16: return launch_bwd3<T, DK, 16>(a, stream);
-    case 32: return launch_bwd3<T, DK, 32>(a, stream);
-    case 64: return launch_bwd3<T, DK, 64>(a, stream);
+hipError_t launch_bwd_dk2(const BwdArgs& a, hipStream_t stream) {
+  switch (bwd_rows(DK, a.ndv)) {
+    case 16: return launch_bwd_rb<T, DK, 16>(a, stream);
+    case 32:
+      if constexpr (DK <= 64) return launch_bwd_rb<T, DK, 32>(a, stream);
+      break;
+    case 64:
+      if constexpr (DK <= 64) return launch_bwd_rb<T, DK, 64>(a, stream);
+      break;
   }
   return hipErrorInvalidValue;
 }
@@ -849,9 +958,10 @@ hipError_t launch_bwd_dv(const BwdArgs& a, hipStream_t stream) {
 template <typename T>
 hipError_t launch_bwd_dk(const BwdArgs& a, hipStream_t stream) {
   switch (a.ndk) {
-    case 16: return launch_bwd_dv<T, 16>(a, stream);
-    case 32: return launch_bwd_dv<T, 32>(a, stream);
-    case 64: return launch_bwd_dv<T, 64>(a, stream);
+    case 16: return launch_bwd_dk2<T, 16>(a, stream);
+    case 32: return launch_bwd_dk2<T, 32>(a, stream);
+    case 64: return launch_bwd_dk2<T, 64>(a, stream);
+    case 128: return launch_bwd_dk2<T, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -859,11 +969,15 @@ hipError_t launch_bwd_dk(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv, int window) {
-  // per chunk of 16 / window steps: start state, S0 x, Gram (fp32)
+  // per slice of value rows (bwd_rows) and chunk of floor(16 / window) steps: start state,
+  // S0 x, Gram (fp32); with several slices per chain also their partial dq, dk,
+  // dk_prev and per-token dbeta (the larger of what any call may need)
   const long ns = BC / window;
   const long nch = (seqlen + ns - 1) / ns;
-  const long per_chunk = (long)dv * dk + (long)BC * dv + (long)BC * BC;
-  return (size_t)batch * heads * nch * per_chunk * sizeof(float);
+  const long RB = bwd_rows(dk, dv), nrg = dv / RB, BH = (long)batch * heads;
+  const long records = BH * nrg * nch * (RB * dk + (long)BC * RB + (long)BC * BC);
+  const long partials = nrg > 1 ? nrg * BH * (2 * seqlen * dk + dk + seqlen) : 0;
+  return (size_t)(records + partials) * sizeof(float);
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
