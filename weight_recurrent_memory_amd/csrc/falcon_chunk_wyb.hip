@@ -24,16 +24,16 @@
 //
 // Structure.  One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
 // Iteration c: waves 0, 1 run the state of sub-chunk c (16 rows each, S in
-// registers); waves 2..7 finish sub-chunk c and prepare c+1 in three phases
-// separated by workgroup barriers (regression family):
-//   1  H_y Y, Q_y Y of c | Gram and q.x of the key tile, keys transposed and
-//      per-step scalars of c+1               (state: split S, XS = X S0^T)
-//   2  T_bb by a DPP forward substitution, -M and P' fragments of c+1; commit
-//      the loads of c+2 to LDS and issue those of c+3   (state: Fk, readout)
-//   3  blocked substitution for F_x, F_y and the folds H, Q of c+1, one wave
-//      per SIMD                              (state: carry)
-// The inner-product family needs two phases: scalars, q.x and transposes of
-// c+1 (state: readout, carry), then Fk and Q_y Y of c+1 and the commits.
+// registers); waves 2..7 prepare the sub-chunks after it, three deep, in two
+// phases separated by workgroup barriers (regression family):
+//   A  blocked substitution for F_x, F_y and the folds H, Q of c+1 (waves 2-5,
+//      one per SIMD) | Gram and q.x of the key tile, keys transposed and
+//      per-step scalars of c+2        (state: split S, XS = X S0^T, Fk, readout)
+//   B  T_bb by a DPP forward substitution, -M and P' fragments of c+2 | H_y Y,
+//      Q_y Y of c+1 | commit the loads of c+3 to LDS and issue those of c+4
+//                                     (state: carry)
+// The inner-product family: scalars, q.x and transposes of c+1 (state:
+// readout, carry), then Fk and Q_y Y of c+1 and the commits.
 // Operands are stored in the fragment order of the register operand they meet
 // (within a 32-wide group, slots 8g..8g+3 hold indices 4g..4g+3 and
 // 8g+4..8g+7 hold 16+4g..16+4g+3); non-exact operands are split-bf16 (Henry,
@@ -75,10 +75,10 @@ struct WybLds {
   float beta[4][CS];
   float G[NXT][FP];                      // Gram of the key tile
   float P[CS][FP];                       // q . x over the tile
-  alignas(16) float gam[2][CS];
-  alignas(16) float zeta[2][CS];
-  alignas(16) float omega[2][CS];
-  alignas(16) float zcum[2][CS];         // prefix sums of zeta
+  alignas(16) float gam[4][CS];          // per-step scalars by sub-chunk & 3
+  alignas(16) float zeta[4][CS];
+  alignas(16) float omega[4][CS];
+  alignas(16) float zcum[4][CS];         // prefix sums of zeta
   float TS[4][16][SP];                   // diagonal blocks of T, row-major
   uint16_t Hxhi[2][NXT][HP];             // -H_x rows, keys in fragment order
   uint16_t Hxlo[2][NXT][HP];
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
   };
 
-  // ---------------- phase-1 stages of sub-chunk j ----------------
+  // ---------------- Gram, q.x, transposes, scalars (phase A of j - 2) ----------------
   // Gram tile (mi, mj) of the key tile (blocks j-1, j): stored transposed, G symmetric
   auto gram_tile = [&](int j, int mi, int mj) __attribute__((always_inline)) {
     const int bi = (j - 1 + mi) & 3, bj = (j - 1 + mj) & 3;
@@ -382,13 +382,13 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
   };
   // c_{m,t} = sum of zeta_s over the unknowns (s, w) of key m with s <= t
-  auto ckey = [&](int sb, int m, int t) __attribute__((always_inline)) {
+  auto ckey = [&](int ss, int m, int t) __attribute__((always_inline)) {
     const int lo = m - 16 < 0 ? 0 : m - 16;
     const int hi0 = m - 16 + B - 1;
     const int hi = hi0 < t ? hi0 : t;
     const int hic = hi < 0 ? 0 : hi;
-    const float top = sm.zcum[sb][hic];
-    const float bot = sm.zcum[sb][lo > 0 ? lo - 1 : 0];
+    const float top = sm.zcum[ss][hic];
+    const float bot = sm.zcum[ss][lo > 0 ? lo - 1 : 0];
     const float v = top - (lo > 0 ? bot : 0.0f);
     return hi < lo ? 0.0f : v;
   };
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   // eta = 0, a = 1.  Lanes 0..15 = steps (one DPP row).
   auto scalars = [&](int j) __attribute__((always_inline)) {
     const int t = lr;
-    const int sb = j & 1;
+    const int ss = j & 3;
     float n = 0.0f;
 #pragma unroll
     for (int w = 0; w < B; ++w) {
@@ -423,23 +423,23 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     zc += dpp_shr<4>(zc, 0.0f);
     zc += dpp_shr<8>(zc, 0.0f);
     if (lane < 16) {
-      sm.gam[sb][t] = gsc;
-      sm.zeta[sb][t] = z;
-      sm.omega[sb][t] = z * gprev;
-      sm.zcum[sb][t] = zc;
+      sm.gam[ss][t] = gsc;
+      sm.zeta[ss][t] = z;
+      sm.omega[ss][t] = z * gprev;
+      sm.zcum[ss][t] = zc;
     }
     if constexpr (!REG) {   // c_m: zeta summed over the unknowns of key m (this wave wrote zcum)
-      if (lane < NXT) sm.cm[sb][lane] = ckey(sb, lane, CS - 1);
+      if (lane < NXT) sm.cm[j & 1][lane] = ckey(ss, lane, CS - 1);
     }
   };
 
-  // ---------------- phase 2 (regression): diagonal blocks of T ----------------
+  // ---------------- phase B (regression): diagonal blocks of T ----------------
   // One wave; 16-lane row b = block b (rows beyond B repeat the last block).
   // Lane n solves column n of (I + M_bb).  Row n of the block's coupling,
   // G[m(u_n)][m(u_r)] for the unknowns u_r of other steps, is read around the
   // block's key range; the same-step entries are zero.
   auto diag_blocks = [&](int j) __attribute__((always_inline)) {
-    const int sb = j & 1;
+    const int ss = j & 3;
     const int b = lg < B ? lg : B - 1;
     const int n = lr;
     const int un = 16 * b + n;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     float os[16 / B];
 #pragma unroll
     for (int q = 0; q < 16 / B; q += 4) {
-      const float4 o4 = *reinterpret_cast<const float4*>(&sm.omega[sb][16 * b / B + q]);
+      const float4 o4 = *reinterpret_cast<const float4*>(&sm.omega[ss][16 * b / B + q]);
       os[q] = o4.x; os[q + 1] = o4.y; os[q + 2] = o4.z; os[q + 3] = o4.w;
     }
 #pragma unroll
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
   };
 
-  // ---------------- phase 2 (regression): operand fragments of the blocked solve ----------------
+  // ---------------- phase B (regression): operand fragments of the blocked solve ----------------
   // fragment f = (block b, pair k): -M[u][u'] for u = 16 b + lr and the unknowns
   // u' of blocks 2k (slots 0-3) and 2k+1 (slots 4-7, zero unless 2k+1 < b)
   constexpr int NMF = NB == 4 ? 4 : 1;
@@ -491,9 +491,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     int b, k;
     mf_bk(f, b, k);
     const int b2 = 2 * k + 1 < b ? 2 * k + 1 : -1;
-    const int sb = j & 1;
     const int u = 16 * b + lr;
-    const float nom = -sm.omega[sb][u / B];
+    const float nom = -sm.omega[j & 3][u / B];
     const float* grow = &sm.G[mof(u)][0];
     float v[8];
 #pragma unroll
@@ -516,7 +515,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     store_split4(&sm.Pfhi[k][lr][8 * lg + 4], &sm.Pflo[k][lr][8 * lg + 4], pv + 4);
   };
 
-  // ---------------- phase 3 (regression): blocked substitution and folds ----------------
+  // ---------------- phase A (regression): blocked substitution and folds ----------------
   // One wave per (F_x | F_y) x key-column tile mc.  V[b] (C layout) holds
   // V[16 b + 4 lg + e][16 mc + lr]; Vop[k] the split fragment over blocks 2k, 2k+1.
   // Gath fragments (B operand over the unknowns of blocks 2k, 2k+1; column m = 16 mj + lr)
@@ -538,7 +537,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
   auto combine = [&](int j, bool fx, int mc) __attribute__((always_inline)) {
     const int sb = j & 1;
-    const float* sc = fx ? sm.omega[sb] : sm.zeta[sb];
+    const float* sc = fx ? sm.omega[j & 3] : sm.zeta[j & 3];
     const float z4[4] = {0.f, 0.f, 0.f, 0.f};
     const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
     floatx4 V[NB];
@@ -611,7 +610,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   auto yfrag = [&](int j, int i) __attribute__((always_inline)) {
     return frag_two(&sm.YT[(j - 1) & 3][i][4 * lg], &sm.YT[j & 3][i][4 * lg]);
   };
-  // ---------------- phase 4 (regression): H_y Y and Q_y Y ----------------
+  // ---------------- phase B (regression): H_y Y and Q_y Y ----------------
   auto ufk_tile = [&](int j, int mt, int it) __attribute__((always_inline)) {
     const HL hy = hl_pair(&sm.Hyhi[j & 1][16 * mt + lr][8 * lg], &sm.Hylo[j & 1][16 * mt + lr][8 * lg]);
     const floatx4 acc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, hy, yfrag(j, 16 * it + lr));
@@ -642,17 +641,21 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int m = 4 * lg + (e & 3) + 16 * (e >> 2);
-      pv[e] = sm.P[t][m] * ckey(j & 1, m, t);
+      pv[e] = sm.P[t][m] * ckey(j & 3, m, t);
     }
     const HL qy = hl_vals(pv);
     oy_tile(j, 0, qy);
     oy_tile(j, 1, qy);
   };
 
-  // iterations c = -2 .. nchunks-1: state of sub-chunk c, preparation of c+1,
-  // commit of c+2, loads of c+3.  Regression: four phases per iteration; inner
-  // product: two.
-  const int c_begin = -2;
+  // Regression, iterations c = -3 .. nchunks-1, two phases each:
+  //   A  state of sub-chunk c up to its readout | blocked substitution and folds
+  //      of c+1 | Gram, q.x, scalars and transposed keys of c+2
+  //   B  carry of c, H_y Y and Q_y Y of c+1 | diagonal blocks of T, -M and P'
+  //      fragments of c+2 | commit of c+3, loads of c+4
+  // Inner product, iterations c = -2 .. nchunks-1: state of c, preparation of
+  // c+1, commit of c+2, loads of c+3, also in two phases.
+  const int c_begin = REG ? -3 : -2;
   if (wave < 2) {
     // ---------------- state waves ----------------
     const int rt = wave;
@@ -679,14 +682,14 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) oacc = mma2(oacc, sf[ks], frag_bf16(&sm.Q[c & 3][lr][32 * ks + 8 * lg]));
         if constexpr (REG) oacc = mma3(oacc, xsf, hl_pair(&sm.Qxhi[cb][lr][8 * lg], &sm.Qxlo[cb][lr][8 * lg]));
-        const float gt = sm.gam[cb][lr];
+        const float gt = sm.gam[c & 3][lr];
         if ((long)c * CS + lr < L)
           *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
         orow += CS * dv;
       };
       auto carry = [&]() __attribute__((always_inline)) {     // S <- g_15 (S + Fk^T X)
         const HL fkf = hl_x4(fk[0], fk[1]);
-        const float gC = sm.gam[cb][CS - 1];
+        const float gC = sm.gam[c & 3][CS - 1];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
           const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][16 * kt + lr][4 * lg], &sm.XT[c & 3][16 * kt + lr][4 * lg]);
@@ -705,7 +708,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       };
       __syncthreads();
       if constexpr (REG) {
-        // phase 1: split the state, XS = X S0^T
+        // phase A: split the state, XS = X S0^T, Fk = Ufk - H_x XS, readout
         if (run) {
           resplit();
           floatx4 xs[2];
@@ -717,10 +720,6 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
               xs[mi] = mma2(xs[mi], frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * ks + 8 * lg]), sf[ks]);
           }
           xsf = hl_x4(xs[0], xs[1]);
-        }
-        __syncthreads();
-        // phase 2: Fk = Ufk - H_x XS; readout
-        if (run) {
           load_fk();
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi)
@@ -728,8 +727,9 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
           readout();
         }
         __syncthreads();
-        // phase 3: carry
+        // phase B: carry; one tile of H_y Y of the next sub-chunk
         if (run) carry();
+        if (live_chunk(c + 1)) ufk_tile(c + 1, 0, rt);
       } else {
         if (run) load_fk();
         if (run) {                    // phase 1
@@ -770,45 +770,42 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       const bool pj = live_chunk(j);
       __syncthreads();
       if constexpr (REG) {
-        // phase 1: H_y Y, Q_y Y of sub-chunk c; Gram, q.x, scalars, keys transposed of c+1
-        const bool pc = live_chunk(c);
-        if (wave == 2) {
-          if (pc) ufk_tile(c, 0, 0);
-          if (pj) { gram_tile(j, 0, 0); gram_tile(j, 1, 0); }
-        } else if (wave == 3) {
-          if (pc) ufk_tile(c, 0, 1);
-          if (pj) { gram_tile(j, 0, 1); gram_tile(j, 1, 1); }
-        } else if (wave == 4) {
-          if (pc) ufk_tile(c, 1, 0);
-          if (pj) { qx_tile(j, 0); qx_tile(j, 1); }
-        } else if (wave == 5) {
-          if (pc) ufk_tile(c, 1, 1);
-          if (pj) transpose_keys(j, lane);
+        const int j2 = c + 2;
+        const bool pj2 = live_chunk(j2);
+        // phase A: blocked substitution and folds of c+1 (one wave per SIMD:
+        // waves 2, 3 F_x, waves 4, 5 F_y); Gram, q.x, scalars, transposed keys of c+2
+        if (wave <= 5) {
+          if (pj) combine(j, wave < 4, wave & 1);
         } else if (wave == 6) {
-          if (pc) oy_tile(c, 0, hl_pair(&sm.Qyhi[c & 1][lr][8 * lg], &sm.Qylo[c & 1][lr][8 * lg]));
-          if (pj) scalars(j);
+          if (pj2) { gram_tile(j2, 0, 0); gram_tile(j2, 1, 0); gram_tile(j2, 0, 1); scalars(j2); }
         } else {
-          if (pc) oy_tile(c, 1, hl_pair(&sm.Qyhi[c & 1][lr][8 * lg], &sm.Qylo[c & 1][lr][8 * lg]));
-          if (pj) transpose_keys(j, 64 + lane);
+          if (pj2) {
+            gram_tile(j2, 1, 1);
+            qx_tile(j2, 0);
+            qx_tile(j2, 1);
+            transpose_keys(j2, lane);
+            transpose_keys(j2, 64 + lane);
+          }
         }
         __syncthreads();
-        // phase 2: diagonal blocks of T; -M and P' fragments; commits
-        if (pj) {
-          if (wave == 4) diag_blocks(j);
-          if (wave == 2) { mfrag_store(j, 0); if (NMF > 1) mfrag_store(j, 1); }
-          if (wave == 3 && NMF > 2) { mfrag_store(j, 2); mfrag_store(j, 3); }
+        // phase B: diagonal blocks of T, -M and P' fragments of c+2; H_y Y and
+        // Q_y Y of c+1; commit of c+3, loads of c+4
+        if (pj2) {
+          if (wave == 4) diag_blocks(j2);
+          if (wave == 2) { mfrag_store(j2, 0); if (NMF > 1) mfrag_store(j2, 1); }
+          if (wave == 3 && NMF > 2) { mfrag_store(j2, 2); mfrag_store(j2, 3); }
           if (wave == 5) pfrag_store(0);
           if (wave == 7 && NKU > 1) pfrag_store(NKU - 1);
         }
-        move(c);
-        __syncthreads();
-        // phase 3: blocked substitution and folds (one wave per SIMD)
         if (pj) {
-          if (wave == 2) combine(j, true, 0);
-          if (wave == 3) combine(j, true, 1);
-          if (wave == 4) combine(j, false, 0);
-          if (wave == 5) combine(j, false, 1);
+          if (wave == 5) ufk_tile(j, 1, 0);
+          if (wave == 6) {
+            ufk_tile(j, 1, 1);
+            oy_tile(j, 0, hl_pair(&sm.Qyhi[j & 1][lr][8 * lg], &sm.Qylo[j & 1][lr][8 * lg]));
+          }
+          if (wave == 7) oy_tile(j, 1, hl_pair(&sm.Qyhi[j & 1][lr][8 * lg], &sm.Qylo[j & 1][lr][8 * lg]));
         }
+        move(c + 1);
       } else {
         // phase 1: Gram-free stages of c+1
         if (pj) {
