@@ -232,9 +232,9 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  * recomputed by a forward sweep.
  *
  * falcon_bwd_workspace_bytes - bytes of device workspace falcon_bwd_chunk needs:
- *   per (batch, head), per slice of R value rows (R = min(dv, 64) with dk <= 64,
- *   16 with dk = 128; a head's rows are split over dv / R workgroups) and per
- *   chunk of floor(16 / window) steps, fp32: the chunk-start state (R x dk), S0 x
+ *   per (batch, head), per slice of R = min(dv, 32) value rows (a head's rows are
+ *   split over dv / R workgroups) and per chunk of floor(16 / window) steps,
+ *   fp32: the chunk-start state (R x dk), S0 x
  *   (16 x R) and the unknowns' Gram (16 x 16); with two or more slices also each
  *   slice's partial dq, dk (L x dk each), dk_prev (dk) and per-token dbeta (L),
  *   which a second kernel adds in slice order.  0 for invalid sizes or a window

@@ -234,13 +234,13 @@ def _bwd(lib, **over):
 
 
 def test_backward_workspace_size(lib):
-    # per (batch, head), per slice of value rows (all of them up to 64 with dk <= 64,
-    # 16 with dk = 128) and per chunk of floor(16 / window) steps: start state, S0 x,
-    # Gram (fp32); with two or more slices also their partial dq, dk (L x dk each),
-    # dk_prev (dk) and per-token dbeta (L)
+    # per (batch, head), per slice of min(dv, 32) value rows and per chunk of
+    # floor(16 / window) steps: start state, S0 x, Gram (fp32); with two or more
+    # slices also their partial dq, dk (L x dk each), dk_prev (dk) and per-token
+    # dbeta (L)
     def size(B, H, L, dk, dv, window):
         nch = -(-L // (16 // window))
-        rb = min(dv, 64) if dk <= 64 else 16
+        rb = min(dv, 32)
         nrg = dv // rb
         rec = B * H * nrg * nch * (rb * dk + 16 * rb + 256)
         part = nrg * B * H * (2 * L * dk + dk + L) if nrg > 1 else 0

@@ -916,11 +916,11 @@ __global__ __launch_bounds__(256) void backward_sum_kernel(BwdArgs a, int nrg, c
   }
 }
 
-// value rows per workgroup (a head's rows are split over dv / RB workgroups): all
-// of them (up to 64) when the state and its gradient fit LDS with dk <= 64 (the
-// per-chunk work is latency-bound, so a narrower slice gains nothing and repeats
-// the dk-wide products); slices of 16 rows for dk = 128
-__host__ __device__ constexpr int bwd_rows(int dk, int dv) { return dk <= 64 ? (dv < 64 ? dv : 64) : 16; }
+// value rows per workgroup (a head's rows are split over dv / RB workgroups):
+// 32, so that every per-row sweep is one pass of the 32 sixteen-lane rows of the
+// eight waves (64 rows take two passes of latency-bound DPP chains, 16 leave half
+// the waves idle and double the partial sums); fewer when dv is smaller
+__host__ __device__ constexpr int bwd_rows(int dk, int dv) { return (void)dk, dv < 32 ? dv : 32; }
 
 template <typename T, int DK, int RB>
 hipError_t launch_bwd_rb(const BwdArgs& a, hipStream_t stream) {
@@ -945,12 +945,7 @@ template <typename T, int DK>
 hipError_t launch_bwd_dk2(const BwdArgs& a, hipStream_t stream) {
   switch (bwd_rows(DK, a.ndv)) {
     case 16: return launch_bwd_rb<T, DK, 16>(a, stream);
-    case 32:
-      if constexpr (DK <= 64) return launch_bwd_rb<T, DK, 32>(a, stream);
-      break;
-    case 64:
-      if constexpr (DK <= 64) return launch_bwd_rb<T, DK, 64>(a, stream);
-      break;
+    case 32: return launch_bwd_rb<T, DK, 32>(a, stream);
   }
   return hipErrorInvalidValue;
 }
