@@ -396,17 +396,21 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         *reinterpret_cast<float4*>(&sm.XU[u][k4]) = f4(&sm.X[BW - 1 + s - w][k4]);
       }
     }
-    if (tid < BC) {
+    // key norms; with window 1 on wave BNW - 2, which has no product tile in
+    // either sweep (the windowed gather above needs a barrier first anyway)
+    constexpr int GT0 = BW == 1 ? 64 * (BNW - 2) : 0;
+    if (tid >= GT0 && tid < GT0 + BC) {
+      const int t = tid - GT0;
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < DK; k += 4) acc = dot4(f4(&sm.X[tid][k]), f4(&sm.X[tid][k]), acc);
-      sm.nrm[tid] = acc;
+      for (int k = 0; k < DK; k += 4) acc = dot4(f4(&sm.X[t][k]), f4(&sm.X[t][k]), acc);
+      sm.nrm[t] = acc;
       if constexpr (BW > 1) {
         wave_sync();
         float n = 0.0f;
 #pragma unroll
-        for (int w = 0; w < BW; ++w) n += tid < NS ? sm.nrm[BW - 1 + tid - w] : 0.0f;
-        sm.nsum[tid] = n;
+        for (int w = 0; w < BW; ++w) n += t < NS ? sm.nrm[BW - 1 + t - w] : 0.0f;
+        sm.nsum[t] = n;
       }
     }
   };
@@ -545,10 +549,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           wsc[WS_G + (rq + r) * BC + mn] = 0.0f;
         }
       }
-      if constexpr (BW == 1) gather();
     } else if (wave <= NIB) {
       xs_tile(wave - 1, wsc);
     }
+    if constexpr (BW == 1) gather();
     lds_barrier();
     for (int i = 4 * wave + (lane >> 4); i < RB; i += 4 * BNW) row_forward(i, row_scal_dpp(i, t0, c), false);
     lds_barrier();
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       gather();
       lds_barrier();
     } else {
-      gather();   // wave 0: the key norms
+      gather();   // the key norms
     }
     bwd_products();
     lds_barrier();
@@ -807,7 +811,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     }
     // ---- dS <- gC dS + sum_t g_t do_t q_t - sum_t w_t x_t: tiles (ib, kb); every
     // reader of dS finished before the barrier above ----
-    for (int tt = wave; tt < NIB * NKB; tt += BNW) {
+    constexpr bool SPLITX = 2 * NKB <= BNW;   // waves NKB..2NKB-1 finish dx above
+    const int widx = (SPLITX && wave >= 2 * NKB) ? wave - NKB : wave;
+    const int nwk = SPLITX ? BNW - NKB : BNW;
+    for (int tt = (SPLITX && wave >= NKB && wave < 2 * NKB) ? NIB * NKB : widx; tt < NIB * NKB; tt += nwk) {
       const int ib = tt / NKB, kb = tt % NKB;
       floatx4 acc;
 #pragma unroll
