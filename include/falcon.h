@@ -222,7 +222,7 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
                           void* stream);
 
 /*
- * Backward pass of the chunk form (every variant; windows 1 to 4): gradients
+ * Backward pass of the chunk form (every variant; windows 1 to 8): gradients
  * of  sum_t <dO_t, o_t> + <dS_L, S_L> + <dk_last, k_last>  with respect to q, k,
  * v, the gains, k_prev and S0.  The pages present the chunk-parallel form as
  * the training form (explainer §3; 163.com section 02 (2)) but print no
@@ -238,12 +238,12 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  *   (16 x R) and the unknowns' Gram (16 x 16); with two or more slices also each
  *   slice's partial dq, dk (L x dk each), dk_prev (dk) and per-token dbeta (L),
  *   which a second kernel adds in slice order.  0 for invalid sizes or a window
- *   outside 1..4.
+ *   outside 1..8.
  *
  * falcon_bwd_chunk
  *   variant ... k_prev, S0, flags   as falcon_fwd_chunk_ex (flags 0 or
  *             FALCON_SAME_STEP); dk, dv in {16, 32, 64, 128}; dtype bf16 or fp32
- *   window    1, or 2..4 for FALCON_3 / FALCON_3A; a windowed call takes no
+ *   window    1, or 2..8 for FALCON_3 / FALCON_3A; a windowed call takes no
  *             start state (S0 must be NULL: its window history is not an input)
  *   dO        [batch, heads, L, dv] float32, gradient of o
  *   dS_L      [batch, heads, dv, dk] float32 gradient of the final state, or NULL
@@ -257,7 +257,7 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  *   workspace, workspace_bytes   device scratch of at least
  *             falcon_bwd_workspace_bytes(..., window) bytes, 16-byte aligned
  * Outputs must not overlap each other, the inputs or the workspace.
- * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 4 or a
+ * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 8 or a
  * windowed start state.
  */
 unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk, int dv,

@@ -245,19 +245,19 @@ def test_backward_workspace_size(lib):
         rec = B * H * nrg * nch * (rb * dk + 16 * rb + 256)
         part = nrg * B * H * (2 * L * dk + dk + L) if nrg > 1 else 0
         return (rec + part) * 4
-    for w in (1, 2, 3, 4):
+    for w in range(1, 9):
         assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, w) == size(2, 3, 100, 64, 32, w)
     assert lib.falcon_bwd_workspace_bytes(1, 2, 64, 128, 128, 4) == size(1, 2, 64, 128, 128, 4)
     assert lib.falcon_bwd_workspace_bytes(1, 1, 64, 16, 16, 1) == size(1, 1, 64, 16, 16, 1)
     assert lib.falcon_bwd_workspace_bytes(1, 3, 50, 64, 128, 2) == size(1, 3, 50, 64, 128, 2)
-    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 5) == 0
+    assert lib.falcon_bwd_workspace_bytes(2, 3, 100, 64, 32, 9) == 0
     assert lib.falcon_bwd_workspace_bytes(0, 3, 100, 64, 32, 1) == 0
     assert lib.falcon_bwd_workspace_bytes(1, 1, 16, 48, 32, 1) == 0
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(variant=2, window=5), UNSUPPORTED),        # windows 1..4 only
-    (dict(variant=5, window=8), UNSUPPORTED),
+    (dict(variant=2, window=9), UNSUPPORTED),        # windows 1..8 only
+    (dict(variant=5, window=16), UNSUPPORTED),
     (dict(variant=0, window=2), INVALID),            # window > 1 outside Falcon-3/3A
     (dict(variant=2, window=0), INVALID),
     (dict(variant=2, window=2, k_prev=P[8], S0=P[9]), UNSUPPORTED),   # windowed start state

@@ -539,14 +539,15 @@ def test_backward_small(variant, dk, dv, carried, same_step, dtype):
 
 
 @pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
-@pytest.mark.parametrize("window", [2, 3, 4])
+@pytest.mark.parametrize("window", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (32, 16)])
 @pytest.mark.parametrize("carried,same_step,per_token", [(False, False, False), (True, False, True),
                                                          (False, True, True)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_window(variant, window, dk, dv, carried, same_step, per_token, dtype):
     """Sliding window: the chunk's unknowns are (step, window slot) pairs; several
-    chunks, a ragged tail, halo samples crossing chunk boundaries."""
+    chunks, a ragged tail, halo samples crossing chunk boundaries (from window 5
+    on, more than one boundary; windows 3, 5, 6, 7 leave lanes idle)."""
     L = 37
     inp = seq_inputs(2, 2, L, dk, dv, seed=820 + 5 * variant + window + dk + dv, dtype=dtype,
                      beta_per_token=per_token, with_k_prev=carried and not same_step)
@@ -575,11 +576,12 @@ def test_backward_window(variant, window, dk, dv, carried, same_step, per_token,
 
 
 @pytest.mark.parametrize("variant,window", [(fw.FALCON_1, 1), (fw.FALCON_2, 1), (fw.FALCON_3, 4),
-                                            (fw.FALCON_3A, 3)])
+                                            (fw.FALCON_3A, 3), (fw.FALCON_3, 8), (fw.FALCON_3A, 6)])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 16), (16, 128)])
 def test_backward_wide(variant, window, dk, dv):
     """dk or dv = 128: the value rows of a head are split over several workgroups
-    whose partial key and query gradients are summed by a second kernel."""
+    whose partial key and query gradients are summed by a second kernel; the
+    carried key lands in a tile row that another wave's commit also covers."""
     per_ch = variant == fw.FALCON_2
     L = 29
     inp = seq_inputs(2, 1, L, dk, dv, seed=840 + variant + dk + dv, dtype="bf16",

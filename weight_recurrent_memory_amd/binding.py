@@ -247,7 +247,7 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
 def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
               k_prev=None, S0=None, dS_L=None, dk_last=None, same_step=False, stream=None):
     """Gradients of sum <dO, o> + <dS_L, S_L> + <dk_last, k_last> for the chunk form
-    (window 1 to 4).  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
+    (window 1 to 8).  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
     dk_prev / dS0 when beta_t / k_prev / S0 are given."""
     import torch
     lib = load_library()

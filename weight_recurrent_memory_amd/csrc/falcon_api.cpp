@@ -300,7 +300,7 @@ FALCON_EXPORT int falcon_decode_step_ex(int variant, int window, int flags, floa
                      dk, dv, dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }
 
-bool bwd_window(int window) { return window >= 1 && window <= 4; }
+bool bwd_window(int window) { return window >= 1 && window <= 8; }
 
 FALCON_EXPORT unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk,
                                                             int dv, int window) {
@@ -334,7 +334,7 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
   const void* ptrs[] = {dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
-  // windows 1..4; a windowed start state would need its window history,
+  // windows 1..8; a windowed start state would need its window history,
   // which this entry point does not take
   if (!bwd_window(window)) return FALCON_ERR_UNSUPPORTED;
   if (window > 1 && S0) return FALCON_ERR_UNSUPPORTED;

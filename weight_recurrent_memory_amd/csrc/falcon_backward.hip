@@ -1,5 +1,5 @@
-// falcon_backward.hip - gradients of the window-1 chunk form (Falcon-1/2/1A/2A)
-// on gfx950.
+// falcon_backward.hip - gradients of the chunk form (every variant; window 1, or
+// sliding windows of 2..8 samples for Falcon-3/3A) on gfx950.
 //
 // The pages give no gradients; the chunk form they describe for training
 // (explainer of arXiv 2608.27763, section 核心方法 §3 chunk-parallel; 163.com
@@ -22,8 +22,11 @@
 //             deta = dzeta / g - lambda da;  dbeta = deta / (eps + n);
 //             dn = -sum_i deta eta / (eps + n)
 //
-// One workgroup (8 waves) per (batch*head) chain holds the whole state and its
-// gradient in LDS, so every sum over value rows stays inside the workgroup.  A
+// One workgroup (8 waves) per (batch*head) chain and slice of up to 32 value rows
+// holds that slice of the state and its gradient in LDS; the sums over value rows
+// (dq, dk, a per-token gain's gradient) are partial per slice and a second kernel
+// adds them in slice order.  Windows: the unknowns are (step, window slot) pairs,
+// 16 per chunk of floor(16 / window) steps, with the same per-row sweeps.  A
 // forward sweep over 16-step chunks stores each chunk's starting state in the
 // caller's workspace; the backward sweep walks the chunks in reverse, reloads
 // that state, recomputes the chunk's forward quantities and carries dS.  Per
@@ -205,10 +208,11 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   using SM = BwdLds<DK, RB, BW>;
   // unknowns u = BW s + w (step s of the chunk, window slot w) on the 16 lanes of a
   // row; the chunk has NS steps and a key tile of NK rows (the BW-1 samples
-  // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w.  With
-  // window 3 lane 15 is past the last step: its tile row NK is zero, so it stays 0.
-  constexpr int NS = BC / BW, NK = BW - 1 + NS;
-  static_assert(BW >= 1 && BW <= 4, "window 1..4");   // window 3: 15 unknowns, lane 15 idle
+  // before it, then its own); the key of u is tile row kt(u) = BW-1 + s - w.  When
+  // BW does not divide 16 the lanes past the last step (u >= NU, all in step NS)
+  // are idle: their keys are zero, so every quantity they hold stays 0.
+  constexpr int NS = BC / BW, NK = BW - 1 + NS, NU = BW * NS;
+  static_assert(BW >= 1 && BW <= 8, "window 1..8");
   constexpr int GX = BC * DK / 4, GY = BC * RB / 4, GS = RB * DK / 4;
   constexpr int NIB = RB / 16, NKB = DK / 16;     // row and column tiles
   __shared__ __align__(16) SM sm;
@@ -344,13 +348,18 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     }
   };
   auto commit_chunk = [&](const uint4 (&val)[NPER], int ci, bool bwd) {
+    // the carried key is x_0: tile row BW-1 of chunk 0, and a halo row of the
+    // next chunks while the window still reaches sample 0 (windows above NS + 1);
+    // written by the thread that owns the row's piece
+    const int r0 = (ks == 1 && kpg) ? BW - 1 - ci * NS : -1;
 #pragma unroll
     for (int u = 0; u < NPER; ++u) {
       const int g = tid + u * BNT;
       if (g < 2 * GX) {
         const int r = g < GX ? g : g - GX;
         const int t = r / (DK / 4), k4 = 4 * (r % (DK / 4));
-        *reinterpret_cast<float4*>(g < GX ? &sm.X[t][k4] : &sm.Q[t][k4]) = cvt4(val[u], kg);
+        if (g < GX && t == r0) *reinterpret_cast<float4*>(&sm.X[t][k4]) = ld4(kpg, chain * DK + k4);
+        else *reinterpret_cast<float4*>(g < GX ? &sm.X[t][k4] : &sm.Q[t][k4]) = cvt4(val[u], kg);
       } else if (g < 2 * GX + 2 * GY + GY) {
         const int r0 = g - 2 * GX;
         const int which = r0 / GY, r = r0 % GY;
@@ -383,8 +392,6 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         }
       }
     }
-    if (ci == 0 && ks == 1 && kpg && tid < DK / 4)   // the carried key is x_0
-      *reinterpret_cast<float4*>(&sm.X[BW - 1][4 * tid]) = ld4(kpg, chain * DK + 4 * tid);
   };
   // after a commit: the unknowns' keys (window) and, on wave 0, the tile's
   // squared norms and their window sums per step
@@ -393,7 +400,8 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       for (int idx = tid; idx < BC * DK / 4; idx += BNT) {
         const int u = idx / (DK / 4), k4 = 4 * (idx % (DK / 4));
         const int s = u / BW, w = u % BW;
-        *reinterpret_cast<float4*>(&sm.XU[u][k4]) = f4(&sm.X[BW - 1 + s - w][k4]);
+        *reinterpret_cast<float4*>(&sm.XU[u][k4]) =
+            u < NU ? f4(&sm.X[BW - 1 + s - w][k4]) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     // key norms; with window 1 on wave BNW - 2, which has no product tile in
@@ -645,21 +653,23 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       float dgm = a.regression ? -dr * (sm.H[t][i] + sm.XS[t][i]) : 0.0f;
       const int s = t / BW;
       if constexpr (BW > 1) {   // step sums over the step's window slots (lanes of a group)
-        if constexpr (BW == 3) {   // groups of three lanes: gather from the group
-          const int g0 = (lane & 48) | (s < NS ? s * 3 : 0);
-          dzeta = __shfl(dzeta, g0) + __shfl(dzeta, g0 + 1) + __shfl(dzeta, g0 + 2);
-          dgm = __shfl(dgm, g0) + __shfl(dgm, g0 + 1) + __shfl(dgm, g0 + 2);
-          if (s >= NS) {   // the idle lane
-            dzeta = 0.0f;
-            dgm = 0.0f;
-          }
-        } else {
+        if constexpr (BW == 2 || BW == 4) {
           dzeta += __shfl_xor(dzeta, 1);
           dgm += __shfl_xor(dgm, 1);
           if constexpr (BW == 4) {
             dzeta += __shfl_xor(dzeta, 2);
             dgm += __shfl_xor(dgm, 2);
           }
+        } else {   // gather from the group, in slot order
+          const int g0 = (lane & 48) | (s < NS ? s * BW : 0);
+          float sz = 0.0f, sg = 0.0f;
+#pragma unroll
+          for (int w = 0; w < BW; ++w) {
+            sz += __shfl(dzeta, g0 + w);
+            sg += __shfl(dgm, g0 + w);
+          }
+          dzeta = s < NS ? sz : 0.0f;   // idle lanes
+          dgm = s < NS ? sg : 0.0f;
         }
       }
       // d gC: s0.ds + sum_t z_t (x_t . ds), a row sum
@@ -835,10 +845,11 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     lds_barrier();
     if constexpr (BW > 1) {
       // d x and d y per sample: the sum over the unknowns that hold it (slot w of
-      // step k - (BW-1) + w for tile row k).  The tile's first BW-1 rows are the
-      // previous chunk's last samples: their sums go to that chunk, which adds
-      // them to its rows NS .. NS+BW-2 (double-buffered by chunk parity).  Nothing
-      // here is touched by the next chunk's commit.
+      // step k - (BW-1) + w for tile row k).  The tile's first BW-1 rows are samples
+      // of earlier chunks: their sums go to the previous chunk, which adds them to
+      // its rows NS .. NS+BW-2 (double-buffered by chunk parity); when BW-1 > NS some
+      // of those rows are again before that chunk and travel on.  Nothing here is
+      // touched by the next chunk's commit.
       const int cur = ci & 1, nxt = (ci + 1) & 1;
       for (int idx = tid; idx < NK * DK; idx += BNT) {
         const int k = idx / DK, kk = idx % DK;
@@ -848,10 +859,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           const int st = k - (BW - 1) + w;
           if (st >= 0 && st < NS) v += sm.dxp[BW * st + w][kk];
         }
+        if (k >= NS) v += sm.dxh[nxt][k - NS][kk];   // carried from the chunk after
         if (k < BW - 1) {
-          sm.dxh[cur][k][kk] = v;
+          sm.dxh[cur][k][kk] = v;                    // on to the chunk before
         } else {
-          if (k >= NS) v += sm.dxh[nxt][k - NS][kk];
           const long j = t0 - (BW - 1) + k;     // sample; x_j = k_{j - ks}
           if (j < L) {
             if (j - ks >= 0) {
@@ -871,10 +882,10 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
           const int st = k - (BW - 1) + w;
           if (st >= 0 && st < NS) v += sm.DR[BW * st + w][i];
         }
+        if (k >= NS) v += sm.dyh[nxt][k - NS][i];
         if (k < BW - 1) {
           sm.dyh[cur][k][i] = v;
         } else {
-          if (k >= NS) v += sm.dyh[nxt][k - NS][i];
           const long j = t0 - (BW - 1) + k;
           if (j < L) a.dv[v_base + j * dvf + i0 + i] = v;
         }
@@ -937,6 +948,10 @@ hipError_t launch_bwd_rb(const BwdArgs& a, hipStream_t stream) {
   else if (a.window == 2) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 2>), grid, dim3(BNT), 0, stream, a);
   else if (a.window == 3) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 3>), grid, dim3(BNT), 0, stream, a);
   else if (a.window == 4) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 4>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 5) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 5>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 6) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 6>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 7) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 7>), grid, dim3(BNT), 0, stream, a);
+  else if (a.window == 8) hipLaunchKernelGGL((backward_kernel<T, DK, RB, 8>), grid, dim3(BNT), 0, stream, a);
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nrg == 1) return e;

@@ -54,10 +54,10 @@ struct DecodeArgs {
   int key_shift;     // 1: x = k_prev (then k_prev <- k); 0: x = k, k_prev unused
 };
 
-// Backward of the chunk form, windows 1..4 (falcon_backward.hip).
+// Backward of the chunk form, windows 1..8 (falcon_backward.hip).
 struct BwdArgs {
   int regression;
-  int window;        // 1..4
+  int window;        // 1..8
   int key_shift;
   float beta;
   const void* beta_t;
