@@ -136,19 +136,35 @@ __device__ __forceinline__ float row_shl_fill(float v, float fill) {
 // Forward: e_t = y_t - gm_t (xs_t + acc_t), z_t = zeta_t e_t with acc_t =
 // sum_{s<t} G_ts z_s; every lane forms its candidate z and step M takes lane M's
 // (grow = the lane's Gram row, zero at and above the diagonal).
-template <int M>
+// With a window the lanes are unknowns and the BW unknowns of one step do not
+// couple (their Gram entries are zero), so the pivots of a step share one
+// candidate: a sweep has ceil(16 / BW) dependent stages of BW multiply-adds, in
+// pivot order as before.
+template <int M, int E>   // acc += v(lane m) g[m], m = M .. E-1
+__device__ __forceinline__ void fmacs_up(float& acc, float v, const float (&g)[16]) {
+  acc = fmac_bcast_nop<M>(acc, v, g[M]);
+  if constexpr (M + 1 < E) fmacs_up<M + 1, E>(acc, v, g);
+}
+template <int M, int E>   // the same for m = E-1 down to M
+__device__ __forceinline__ void fmacs_down(float& acc, float v, const float (&g)[16]) {
+  acc = fmac_bcast_nop<E - 1>(acc, v, g[E - 1]);
+  if constexpr (E - 1 > M) fmacs_down<M, E - 1>(acc, v, g);
+}
+template <int BW, int S>
 __device__ __forceinline__ void fsweep(float& acc, const float (&grow)[16], float y, float xs, float gm, float zeta) {
+  constexpr int M = BW * S, E = M + BW < 16 ? M + BW : 16;
   const float zc = zeta * (y - gm * (xs + acc));
-  acc = fmac_bcast_nop<M>(acc, zc, grow[M]);
-  if constexpr (M < 15) fsweep<M + 1>(acc, grow, y, xs, gm, zeta);
+  fmacs_up<M, E>(acc, zc, grow);
+  if constexpr (E < 16) fsweep<BW, S + 1>(acc, grow, y, xs, gm, zeta);
 }
 // Transposed: dr_s = zeta_s (dz_s - acc2_s), w_s = gm_s dr_s with acc2_s =
-// sum_{t>s} G_ts w_t, steps M = 15 .. 0 (gcol = the lane's Gram column)
-template <int M>
+// sum_{t>s} G_ts w_t, pivots 15 .. 0 (gcol = the lane's Gram column)
+template <int BW, int S>
 __device__ __forceinline__ void bsweep(float& acc2, const float (&gcol)[16], float dz, float gm, float zeta) {
+  constexpr int M = BW * S, E = M + BW < 16 ? M + BW : 16;
   const float wc = gm * zeta * (dz - acc2);
-  acc2 = fmac_bcast_nop<M>(acc2, wc, gcol[M]);
-  if constexpr (M > 0) bsweep<M - 1>(acc2, gcol, dz, gm, zeta);
+  fmacs_down<M, E>(acc2, wc, gcol);
+  if constexpr (S > 0) bsweep<BW, S - 1>(acc2, gcol, dz, gm, zeta);
 }
 
 // raw 16-byte register images of four elements (converted only when stored
@@ -509,7 +525,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       float grow[16];
 #pragma unroll
       for (int m = 0; m < 16; ++m) grow[m] = sm.G[t][m];
-      fsweep<0>(acc, grow, y, xs, r.gm, r.zeta);
+      fsweep<BW, 0>(acc, grow, y, xs, r.gm, r.zeta);
     }
     const float e = a.regression ? y - r.gm * (xs + acc) : y;
     sm.Z[t][i] = r.zeta * e;
@@ -645,7 +661,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
         float gcol[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) gcol[m] = sm.G[m][t];
-        bsweep<15>(acc2, gcol, dz, r.gm, r.zeta);
+        bsweep<BW, 15 / BW>(acc2, gcol, dz, r.gm, r.zeta);
       }
       const float dr = r.zeta * (dz - acc2);
       const float w = a.regression ? r.gm * dr : 0.0f;

@@ -111,13 +111,15 @@ __device__ __forceinline__ float fmac_bcast(float acc, float g, float r) {
   return acc;
 }
 // forward substitution of (I + M) x = rhs over a 16-unknown block from pivot
-// P on, M = diag(om) L(g): lane m of each 16-lane row holds row m in g[]
-template <int P>
+// P on, M = diag(om) L(g): lane m of each 16-lane row holds row m in g[].  The B
+// unknowns of a step do not couple (g is zero between them), so a pivot updates
+// only the unknowns of later steps and the pivots of one step are independent.
+template <int B, int P>
 __device__ __forceinline__ void sweep(float (&rhs)[16], float (&acc)[16], const float (&g)[16], const float (&om)[16]) {
   rhs[P] = __builtin_fmaf(-om[P], acc[P], rhs[P]);
 #pragma unroll
-  for (int r = P + 1; r < 16; ++r) acc[r] = fmac_bcast<P>(acc[r], g[r], rhs[P]);
-  if constexpr (P < 15) sweep<P + 1>(rhs, acc, g, om);
+  for (int r = B * (P / B + 1); r < 16; ++r) acc[r] = fmac_bcast<P>(acc[r], g[r], rhs[P]);
+  if constexpr (P < 15) sweep<B, P + 1>(rhs, acc, g, om);
 }
 template <int N>
 __device__ __forceinline__ float dpp_shr(float v, float fill) {
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       acc[m] = 0.0f;
     }
     asm volatile("s_nop 4");
-    sweep<0>(rhs, acc, g, om);
+    sweep<B, 0>(rhs, acc, g, om);
     if (lg < B) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sm.TS[b][r][n] = rhs[r];
