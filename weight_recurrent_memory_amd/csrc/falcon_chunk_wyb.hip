@@ -777,7 +777,13 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         // phase A: blocked substitution and folds of c+1 (one wave per SIMD:
         // waves 2, 3 F_x, waves 4, 5 F_y); Gram, q.x, scalars, transposed keys of c+2
         if (wave <= 5) {
+          // window 4: the substitution (four blocks) is the longest chain of the
+          // phase, so its waves issue first on the SIMDs they share with the state
+          // and Gram waves (measured: 3-5% faster; with window 2 it is not, and
+          // the priority costs time)
+          if constexpr (B == 4) __builtin_amdgcn_s_setprio(2);
           if (pj) combine(j, wave < 4, wave & 1);
+          if constexpr (B == 4) __builtin_amdgcn_s_setprio(0);
         } else if (wave == 6) {
           if (pj2) { gram_tile(j2, 0, 0); gram_tile(j2, 1, 0); gram_tile(j2, 0, 1); scalars(j2); }
         } else {
