@@ -11,12 +11,16 @@ lambda = 0.01, eps = 1e-6.  Inputs are resident in HBM before the timed region;
 launch time is measured with HIP events on the stream the kernel runs on.
 
 Prints one JSON line.  Besides the contract fields it carries
+  timing        mean, median and minimum of the timed calls
   roofline      the chunk kernel against HBM bandwidth (algorithmic bytes)
+  roofline_mfma the sliding-window forward (Falcon-3, 4 x 16 x 8192, d = 128)
+                against the bf16 matrix-core peak, in model flops
   cpu_baseline  the fp64 oracle on the host cores, same workload
   secondary     the other workloads: Falcon-1A, per-channel Falcon-2, windowed
                 Falcon-3/3A at d = 128, the backward of the headline workload,
-                the decode step (state GB/s), a copy kernel for attainable
-                bandwidth, and model-FLOP utilization.
+                the decode step (warm, and cold: the state evicted from every
+                cache before each step), a copy kernel for attainable bandwidth,
+                and model-FLOP utilization.
 """
 from __future__ import annotations
 
@@ -36,6 +40,12 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic.json")
 CHUNK_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
                  for f in ("falcon_chunk_wy.hip", "falcon_mma.h", "falcon_device.h")]
+PROFILE_MFMA = os.path.join(ROOT, "profiles", "window_mfma_counters.json")
+WINDOW_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
+                  for f in ("falcon_chunk_wyb.hip", "falcon_mma.h", "falcon_device.h")]
+HEADLINE_KERNEL = "chunk_wy_kernel<64,true>"
+HEADLINE_KERNEL_CHUNK = 32
+WINDOW_KERNEL = "chunk_wyb_kernel<128,true,4>"
 
 
 def algorithmic_bytes(batch, heads, L, dk, dv, beta_channel=False, elem=2):
@@ -88,6 +98,30 @@ def _traffic():
     return rec.get("bytes_per_launch")
 
 
+def _mfma_counters():
+    """Matrix-core counters of the sliding-window kernel (rocprofv3 --pmc), if they
+    were taken on the current kernel source (else None)."""
+    try:
+        with open(PROFILE_MFMA) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != _source_hash(WINDOW_SOURCES):
+        return None
+    return rec
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,21 +151,45 @@ def main():
     def up(a, dt):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dt)
 
-    def time_calls(fn, steps, warmup):
+    def time_calls(fn, steps, warmup, between=None, stats=None):
+        """Seconds per call over `steps` timed calls (HIP events on the stream the
+        library launches on, torch's current stream).  An event is recorded
+        between consecutive calls, so `stats` (a dict) also receives the median and
+        minimum single-call times.  `between` runs outside the events before each
+        call (the cache-flushing leg); then the per-call times are the only
+        measure and the mean is taken over them."""
         for _ in range(warmup):
+            if between is not None:
+                between()
             fn()
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(steps):
-            fn()
-        e1.record(s)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / steps    # seconds per call
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        if between is None:
+            ev[0].record(s)
+            for i in range(steps):
+                fn()
+                ev[i + 1].record(s)
+            torch.cuda.synchronize()
+            per = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(steps)]
+            mean = ev[0].elapsed_time(ev[steps]) / 1e3 / steps
+        else:
+            ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+            for i in range(steps):
+                between()
+                ev[i].record(s)
+                fn()
+                ev2[i].record(s)
+            torch.cuda.synchronize()
+            per = [ev[i].elapsed_time(ev2[i]) / 1e3 for i in range(steps)]
+            mean = sum(per) / steps
+        if stats is not None:
+            srt = sorted(per)
+            stats.update(median_s=srt[steps // 2] if steps % 2 else 0.5 * (srt[steps // 2 - 1] + srt[steps // 2]),
+                         min_s=srt[0], mean_s=mean, calls=steps)
+        return mean
 
-    def seq_leg(name, variant, steps, warmup, window=1):
+    def seq_leg(name, variant, steps, warmup, window=1, stats=None):
         cfg = WORKLOADS[name]
         B, H, L, dk, dv = cfg["shape"]
         per_ch = bool(cfg.get("beta_per_channel"))
@@ -144,7 +202,7 @@ def main():
         fn = lambda: fw.fwd_chunk(q, k, v, variant=variant, beta=beta, lam=cfg["lam"],
                                   eps=cfg["eps"], chunk=cfg["chunk"], window=window,
                                   beta_t=bt, out=out)
-        sec = time_calls(fn, steps, warmup)
+        sec = time_calls(fn, steps, warmup, stats=stats)
         nbytes = algorithmic_bytes(B, H, L, dk, dv, beta_channel=per_ch)
         return dict(sec=sec, tokens=B * L, head_tokens=B * H * L, bytes=nbytes, d=dk,
                     chunk=cfg["chunk"], inp=inp, cfg=cfg)
@@ -153,11 +211,12 @@ def main():
     # ---------------- headline: Falcon-1 chunk forward, 8 x 12 x 2048 x 64 ----------------
     head_name = "chunk_8x12x2048x64"
     if args.only in (None, "headline"):
-        h = seq_leg(head_name, fw.FALCON_1, args.steps, args.warmup)
+        st = {}
+        h = seq_leg(head_name, fw.FALCON_1, args.steps, args.warmup, stats=st)
         sec = h["sec"]
         value = h["tokens"] / sec
         achieved = h["bytes"] / sec / 1e9
-        mflops = model_flops_per_head_token(True, 64, 32) * h["head_tokens"]
+        mflops = model_flops_per_head_token(True, 64, 64) * h["head_tokens"]
         traffic = _traffic()
         out.update({
             "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -165,17 +224,21 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic",
             "config": {"workload": head_name, "variant": "falcon1", "batch": 8, "heads": 12,
-                       "seq_len": 2048, "dk": 64, "dv": 64, "chunk": 64, "kernel_chunk": 32,
-                       "beta": 0.5,
+                       "seq_len": 2048, "dk": 64, "dv": 64, "chunk": 64,
+                       "kernel_chunk": HEADLINE_KERNEL_CHUNK, "beta": 0.5,
                        "lambda": 0.01, "eps": 1e-6, "parallelism": "single-gpu"},
+            "timing": {"calls": st["calls"], "mean_us": st["mean_s"] * 1e6,
+                       "median_us": st["median_s"] * 1e6, "min_us": st["min_s"] * 1e6},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": traffic,
-                         "kernel": "chunk_wy_kernel<64,true>",
+                         "kernel": HEADLINE_KERNEL,
                          "algorithmic_bytes_per_launch": h["bytes"],
                          "avg_launch_us": sec * 1e6},
-            "mfma_model_util": {"model_tflops": mflops / sec / 1e12,
-                                "frac_of_bf16_peak": mflops / sec / 1e12 / BF16_PEAK_TFLOPS},
+            "mfma_model_util": {"model_gflop_per_call": mflops / 1e9,
+                                "model_tflops": mflops / sec / 1e12,
+                                "frac_of_bf16_peak": mflops / sec / 1e12 / BF16_PEAK_TFLOPS,
+                                "flop_formula": "canonical single-level chunk form, C = 64"},
         })
         head_inp = h["inp"]
     else:
@@ -193,14 +256,32 @@ def main():
         for key, name, variant, win in legs:
             if args.only not in (None, key.split("_")[0]):
                 continue
-            r = seq_leg(name, variant, 20, 3, window=win)
-            fl = model_flops_per_head_token(variant in (fw.FALCON_2, fw.FALCON_3), r["d"], r["chunk"], win) * r["head_tokens"]
+            st = {}
+            r = seq_leg(name, variant, 20, 3, window=win, stats=st)
+            regression = variant in (fw.FALCON_2, fw.FALCON_3)
+            fl = model_flops_per_head_token(regression, r["d"], r["chunk"], win) * r["head_tokens"]
             sec_out[key] = {"workload": name, "variant": names[variant],
                             "tokens_per_s": r["tokens"] / r["sec"], "ms_per_call": r["sec"] * 1e3,
+                            "median_ms": st["median_s"] * 1e3, "min_ms": st["min_s"] * 1e3,
                             "hbm_gbs": r["bytes"] / r["sec"] / 1e9,
                             "hbm_frac": r["bytes"] / r["sec"] / 1e9 / HBM_PEAK_GBS,
+                            "model_gflop_per_call": fl / 1e9,
                             "model_tflops": fl / r["sec"] / 1e12,
                             "mfma_model_frac": fl / r["sec"] / 1e12 / BF16_PEAK_TFLOPS}
+            if key == "window_falcon3":
+                # the matrix-core target of the chunk-parallel forward: Falcon-3 at
+                # L = 8192, d = 128 (model flops of the canonical C = 64 form)
+                achieved_tf = fl / r["sec"] / 1e12
+                counters = _mfma_counters()
+                out["roofline_mfma"] = {
+                    "bound": "mfma", "achieved": achieved_tf, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved_tf / BF16_PEAK_TFLOPS,
+                    "workload": name, "variant": "falcon3", "window": 4,
+                    "model_gflop_per_call": fl / 1e9, "avg_launch_us": r["sec"] * 1e6,
+                    "kernel": WINDOW_KERNEL,
+                    "mfma_busy_frac": counters.get("mfma_busy_frac") if counters else None,
+                    "issued_tflops": counters.get("issued_tflops") if counters else None,
+                    "counters_source": counters.get("source") if counters else None}
             del r
             torch.cuda.empty_cache()
         if args.only in (None, "backward"):
@@ -216,10 +297,12 @@ def main():
                              generator=torch.Generator(device=dev).manual_seed(7))
             fn = lambda: fw.bwd_chunk(q, k, v, dO, variant=fw.FALCON_1, beta=cfg["beta"],
                                       lam=cfg["lam"], eps=cfg["eps"])
-            sec = time_calls(fn, 10, 2)
+            st = {}
+            sec = time_calls(fn, 10, 2, stats=st)
             nbytes = B * H * L * ((2 * dk + dv) * 2 + dv * 4 + (2 * dk + dv) * 4)
             sec_out["backward"] = {"workload": head_name, "variant": "falcon1",
-                                   "ms_per_call": sec * 1e3, "tokens_per_s": B * L / sec,
+                                   "ms_per_call": sec * 1e3, "median_ms": st["median_s"] * 1e3,
+                                   "tokens_per_s": B * L / sec,
                                    "hbm_gbs": nbytes / sec / 1e9,
                                    "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
                                    "algorithmic_bytes": nbytes}
@@ -249,15 +332,32 @@ def main():
                 it[0] += 1
                 fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=fw.FALCON_1, beta=cfg["beta"],
                                lam=cfg["lam"], eps=cfg["eps"], out=o)
-            sec = time_calls(step, args.decode_steps, 20)
             state_bytes = 2 * N * H * dv * dk * 4
             io_bytes = N * H * (3 * dk * 2 + dv * 2 + dv * 4 + dk * 2)  # k_prev r/w, q, k, v, o
+            nb = state_bytes + io_bytes
+            # warm: back-to-back steps, the 100.7 MB state can stay in the 256 MB
+            # Infinity Cache (MALL) between steps
+            st = {}
+            sec = time_calls(step, args.decode_steps, 20, stats=st)
+            # cold: a 1 GiB buffer is written before every timed step (outside its
+            # events), which evicts the state from the MALL and the L2s; the step's
+            # own time is then what a state that lives in HBM costs
+            scratch = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+            stc = {}
+            sec_cold = time_calls(step, 200, 5, between=lambda: scratch.fill_(1.0), stats=stc)
+            del scratch
             sec_out["decode"] = {"workload": "decode_512x12x64", "variant": "falcon1",
-                                 "steps": args.decode_steps, "us_per_step": sec * 1e6,
-                                 "state_gbs": state_bytes / sec / 1e9,
-                                 "total_gbs": (state_bytes + io_bytes) / sec / 1e9,
-                                 "hbm_frac": (state_bytes + io_bytes) / sec / 1e9 / HBM_PEAK_GBS,
-                                 "bytes_per_step": state_bytes + io_bytes}
+                                 "bytes_per_step": nb,
+                                 "warm": {"steps": args.decode_steps, "us_per_step": sec * 1e6,
+                                          "median_us": st["median_s"] * 1e6,
+                                          "state_gbs": state_bytes / sec / 1e9,
+                                          "total_gbs": nb / sec / 1e9,
+                                          "frac_of_peak": nb / sec / 1e9 / HBM_PEAK_GBS},
+                                 "cold": {"steps": 200, "flush_bytes": 1 << 30,
+                                          "us_per_step": sec_cold * 1e6,
+                                          "median_us": stc["median_s"] * 1e6,
+                                          "total_gbs": nb / stc["median_s"] / 1e9,
+                                          "hbm_frac": nb / stc["median_s"] / 1e9 / HBM_PEAK_GBS}}
             del S, qs, ks, vs
             torch.cuda.empty_cache()
         if args.only in (None, "copy"):
@@ -285,6 +385,7 @@ def main():
                                "cores": threads, "kind": "oracle",
                                "sample": "the whole headline batch (8 x 12 x 2048 tokens, "
                                          "Falcon-1, fp64 numpy recurrence), %.1f s" % cpu_sec,
+                               "cpu_model": _cpu_model(),
                                "host_cpus": len(os.sched_getaffinity(0))}
     print(json.dumps(out))
 

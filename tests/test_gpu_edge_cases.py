@@ -1,0 +1,189 @@
+"""GPU parity on the method's own edge cases, for every chunk kernel family and
+for the recurrent and decode kernels (the oracle decides).
+
+* strong decay: lambda * beta in {0.5, 0.9, 0.99}, so the per-step decay
+  a_t = 1 - eta_t lambda falls to about 0.01 and its products over a chunk
+  leave the float32 range (the decayed NLMS write of the 163.com article,
+  section 02 (1));
+* unnormalized keys, norms 0.1 .. 3: the step eta_t = beta / (eps + n_t) varies
+  by a factor of about 900 from token to token;
+* lambda = eps = 0 with a carried key: textbook NLMS (163.com 02 (1));
+* beta = 1, lambda = eps = 0 in fp32: every write interpolates its sample,
+  S_t x_t = y_t (explainer 核心方法 §1: one normalized step on the squared
+  error with unit gain).
+"""
+import numpy as np
+import pytest
+
+from oracle import falcon_oracle as fo
+from weight_recurrent_memory_amd.inputs import decode_inputs, seq_inputs
+from parity_util import TOL_BF16, TOL_FP32_MATH, state_err, to_dev, token_normwise_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import weight_recurrent_memory_amd as fw  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fw.load_library()
+
+
+# (label, variant, dk, dv, window, gains, chunk): one entry per chunk kernel
+# family and shape class the dispatcher distinguishes
+FAMILIES = [
+    ("wy", fw.FALCON_1, 64, 64, 1, "scalar", 64),
+    ("wy_1a", fw.FALCON_1A, 64, 64, 1, "token", 64),
+    ("wy_dk32", fw.FALCON_1, 32, 32, 1, "token", 64),
+    ("w1_percol", fw.FALCON_2, 64, 64, 1, "channel", 64),
+    ("w1_percol_2a", fw.FALCON_2A, 32, 16, 1, "channel", 64),
+    ("w1_percol_c16", fw.FALCON_2, 64, 32, 1, "channel", 16),
+    ("w1_dk128", fw.FALCON_1, 128, 32, 1, "scalar", 64),
+    ("w1_dk16", fw.FALCON_1, 16, 32, 1, "token", 64),
+    ("wyb_w4", fw.FALCON_3, 128, 32, 4, "scalar", 64),
+    ("wyb_w2", fw.FALCON_3, 64, 64, 2, "token", 64),
+    ("ip_w4", fw.FALCON_3A, 128, 64, 4, "scalar", 64),
+    ("ip_1a_dk128", fw.FALCON_1A, 128, 32, 1, "token", 64),
+    ("ip_w8", fw.FALCON_3A, 64, 32, 8, "token", 64),
+    ("generic_w3", fw.FALCON_3, 64, 32, 3, "token", 64),
+    ("generic_w2_dk32", fw.FALCON_3A, 32, 32, 2, "scalar", 32),
+]
+
+
+def _inputs(label, variant, dk, dv, gains, L, seed, **extra):
+    return seq_inputs(2, 2, L, dk, dv, seed=seed, dtype="bf16",
+                      beta_per_channel=gains == "channel", beta_per_token=gains == "token",
+                      **extra)
+
+
+def _chunk_vs_oracle(label, variant, dk, dv, window, gains, chunk, inp, *, beta, lam, eps,
+                     carried=False):
+    dt = torch.bfloat16
+    q, k, v = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
+    bt = to_dev(torch, inp["beta_t"], dt) if "beta_t" in inp else None
+    kp = to_dev(torch, inp["k_prev"], dt) if carried else None
+    S0 = to_dev(torch, inp["S0"], torch.float32) if carried and "S0" in inp else None
+    b = beta if gains == "scalar" else None
+    print("%s: launching" % label, flush=True)
+    o, S = fw.fwd_chunk(q, k, v, variant=variant, beta=b, lam=lam, eps=eps, window=window,
+                        chunk=chunk, beta_t=bt, k_prev=kp, S0=S0, return_state=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], beta=b,
+                                           lam=lam, eps=eps, window=window,
+                                           beta_t=inp.get("beta_t"),
+                                           k_prev=inp["k_prev"] if carried else None,
+                                           S0=inp["S0"] if carried and "S0" in inp else None)
+    o = o.cpu().numpy()
+    S = S.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S)), "non-finite output"
+    err, zok = token_normwise_err(o, o_ref)
+    serr = state_err(S, S_ref)
+    print("%s: o err %.3e S err %.3e" % (label, err, serr))
+    assert zok and err <= TOL_BF16 and serr <= TOL_BF16
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+@pytest.mark.parametrize("lam_beta", [0.5, 0.9, 0.99])
+def test_chunk_strong_decay(fam, lam_beta):
+    """beta = 1 (or per-token / per-channel gains in (0, 1)) and lambda = the
+    target product: with normalized keys eta_t lambda reaches lam_beta."""
+    label, variant, dk, dv, window, gains, chunk = fam
+    L = 3 * 64 + 11
+    inp = _inputs(label, variant, dk, dv, gains, L, seed=900 + int(100 * lam_beta) + dk + window)
+    _chunk_vs_oracle("%s lam*beta %.2f" % (label, lam_beta), variant, dk, dv, window, gains,
+                     chunk, inp, beta=1.0, lam=lam_beta, eps=1e-6)
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_chunk_unnormalized_keys(fam):
+    label, variant, dk, dv, window, gains, chunk = fam
+    L = 2 * 64 + 37
+    inp = _inputs(label, variant, dk, dv, gains, L, seed=950 + dk + window,
+                  key_norms=(0.1, 3.0), with_k_prev=True)
+    _chunk_vs_oracle(label + " key norms 0.1..3", variant, dk, dv, window, gains, chunk, inp,
+                     beta=0.5, lam=0.01, eps=1e-6, carried=True)
+
+
+REGRESSION_FAMILIES = [f for f in FAMILIES if fo.is_regression(f[1])]
+
+
+@pytest.mark.parametrize("fam", REGRESSION_FAMILIES, ids=[f[0] for f in REGRESSION_FAMILIES])
+def test_chunk_exact_nlms_carried_key(fam):
+    """lambda = eps = 0: no decay, eta_t = beta / ||x_t||^2 (textbook NLMS); the
+    carried key makes x_1 non-zero, so no step has a zero normalizer."""
+    label, variant, dk, dv, window, gains, chunk = fam
+    L = 2 * 64 + 9
+    inp = _inputs(label, variant, dk, dv, gains, L, seed=970 + dk + window, with_k_prev=True)
+    _chunk_vs_oracle(label + " NLMS", variant, dk, dv, window, gains, chunk, inp, beta=0.7,
+                     lam=0.0, eps=0.0, carried=True)
+
+
+@pytest.mark.parametrize("variant,window", [(fw.FALCON_1, 1), (fw.FALCON_2, 1), (fw.FALCON_3, 3)])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (16, 32), (128, 16)])
+def test_recurrent_interpolation_fp32(variant, window, dk, dv):
+    """beta = 1, lambda = eps = 0, fp32 inputs: after the call the state maps the
+    last window's newest sample onto its value, and o matches the oracle."""
+    per_ch = variant == fw.FALCON_2
+    L = 40
+    inp = seq_inputs(1, 2, L, dk, dv, seed=990 + variant + dk, dtype="f32", with_k_prev=True,
+                     beta_per_channel=per_ch)
+    if per_ch:
+        inp["beta_t"] = np.ones_like(inp["beta_t"])
+    dt = torch.float32
+    q, k, v, kp = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "k_prev"))
+    bt = to_dev(torch, inp["beta_t"], dt) if per_ch else None
+    o, S = fw.fwd_recurrent(q, k, v, variant=variant, beta=None if per_ch else 1.0, lam=0.0,
+                            eps=0.0, window=window, beta_t=bt, k_prev=kp, return_state=True)
+    torch.cuda.synchronize()
+    S = S.cpu().numpy().astype(np.float64)
+    x_last = inp["k"][:, :, L - 2].astype(np.float64)          # x_L = k_{L-1}
+    y_last = inp["v"][:, :, L - 1].astype(np.float64)
+    Sx = np.einsum("bhik,bhk->bhi", S, x_last)
+    interp = float(np.max(np.abs(Sx - y_last)) / np.max(np.abs(y_last)))
+    o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"],
+                                           beta=None if per_ch else 1.0, lam=0.0, eps=0.0,
+                                           window=window, beta_t=inp.get("beta_t"),
+                                           k_prev=inp["k_prev"])
+    err, zok = token_normwise_err(o.cpu().numpy(), o_ref)
+    print("recurrent interpolation v%d w%d dk %d: |S x - y| %.2e, o err %.2e"
+          % (variant, window, dk, interp, err))
+    if window == 1:
+        assert interp <= TOL_FP32_MATH
+    assert zok and err <= TOL_FP32_MATH and state_err(S, S_ref) <= TOL_FP32_MATH
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_2])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 32)])
+def test_decode_interpolation_fp32(variant, dk, dv):
+    """One decode step with beta = 1, lambda = eps = 0: S_new k_prev = v."""
+    per_ch = variant == fw.FALCON_2
+    inp = decode_inputs(4, 3, dk, dv, seed=995 + variant + dk, steps=3, s_std=0.3, dtype="f32",
+                        beta_per_channel=per_ch)
+    dt = torch.float32
+    S = to_dev(torch, inp["S"], torch.float32)
+    kp = to_dev(torch, inp["k_prev"], dt)
+    S_r, kp_r = inp["S"].astype(np.float64), inp["k_prev"].astype(np.float64)
+    for s in range(3):
+        x = kp.cpu().numpy().astype(np.float64)
+        bt = torch.ones((4, 3, dv), device="cuda", dtype=dt) if per_ch else None
+        o = fw.decode_step(S, kp, to_dev(torch, inp["q"][s], dt), to_dev(torch, inp["k"][s], dt),
+                           to_dev(torch, inp["v"][s], dt), variant=variant,
+                           beta=None if per_ch else 1.0, lam=0.0, eps=0.0, beta_t=bt)
+        o_r, S_r, kp_r = fo.falcon_decode_step(variant, S_r, kp_r, inp["q"][s], inp["k"][s],
+                                               inp["v"][s], beta=None if per_ch else 1.0,
+                                               lam=0.0, eps=0.0,
+                                               beta_t=np.ones((4, 3, dv)) if per_ch else None)
+        torch.cuda.synchronize()
+        Sn = S.cpu().numpy().astype(np.float64)
+        Sx = np.einsum("nhik,nhk->nhi", Sn, x)
+        y = inp["v"][s].astype(np.float64)
+        interp = float(np.max(np.abs(Sx - y)) / np.max(np.abs(y)))
+        err, zok = token_normwise_err(o.cpu().numpy(), o_r)
+        print("decode interpolation v%d dk %d step %d: |S x - y| %.2e, o err %.2e"
+              % (variant, dk, s, interp, err))
+        assert interp <= TOL_FP32_MATH
+        assert zok and err <= TOL_FP32_MATH
+    assert state_err(S.cpu().numpy(), S_r) <= TOL_FP32_MATH

@@ -1,14 +1,15 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
 
 Small cases span several tiles and a ragged tail and are compared element by
-element on every output; the full workloads are compared on sampled
-(batch, head) chains that the oracle recomputes one by one.
+element on every output; the full workloads are compared on every (batch, head)
+chain, the oracle running over groups of chains in worker processes.
 """
 import numpy as np
 import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import WORKLOADS, decode_inputs, seq_inputs
+import oracle_pool
 from parity_util import (TOL_BF16, TOL_F32, TOL_FP32_MATH, state_err, to_dev,
                          token_normwise_err)
 
@@ -223,9 +224,9 @@ def test_chunk_inner_product_windows(dk, dv, window, carried):
 
 
 # ---------------------------------------------------------------------------
-# chunk form at the full workload sizes, sampled chains
+# chunk form at the full workload sizes: every chain against the oracle
 
-def _full_chunk_case(name, variant, chains, window=1):
+def _full_chunk_case(name, variant, window=1):
     cfg = WORKLOADS[name]
     B, H, L, dk, dv = cfg["shape"]
     per_ch = bool(cfg.get("beta_per_channel"))
@@ -234,37 +235,38 @@ def _full_chunk_case(name, variant, chains, window=1):
     print("case %s variant %d: launching" % (name, variant), flush=True)
     o, S = _run_seq("chunk", variant, inp, torch.bfloat16, beta=beta, lam=cfg["lam"],
                     eps=cfg["eps"], window=window, chunk=cfg["chunk"])
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
-    o_ref, S_ref, _ = _oracle(variant, inp, beta=beta, lam=cfg["lam"], eps=cfg["eps"],
-                              window=window, chains=chains)
-    o_s = o.reshape((-1,) + o.shape[2:])[chains]
-    S_s = S.reshape((-1,) + S.shape[2:])[chains]
-    err, zok = token_normwise_err(o_s, o_ref[:, 0])
-    serr = state_err(S_s, S_ref[:, 0])
-    print("%s variant %d: o err %.3e  S err %.3e" % (name, variant, err, serr))
+    print("case %s variant %d: oracle over %d chains (%d workers)"
+          % (name, variant, B * H, oracle_pool.workers()), flush=True)
+    o_ref, S_ref = oracle_pool.recurrence_all_chains(variant, inp, beta=beta, lam=cfg["lam"],
+                                                     eps=cfg["eps"], window=window)
+    err, zok = token_normwise_err(o.reshape(o_ref.shape), o_ref)
+    serr = state_err(S.reshape(S_ref.shape), S_ref)
+    print("%s variant %d, all %d chains: o err %.3e  S err %.3e" % (name, variant, B * H, err, serr))
     assert zok and err <= TOL_BF16
     assert serr <= TOL_BF16
 
 
 @pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_1A])
 def test_chunk_8x12x2048x64(variant):
-    _full_chunk_case("chunk_8x12x2048x64", variant, chains=[0, 41, 95])
+    _full_chunk_case("chunk_8x12x2048x64", variant)
 
 
 def test_chunk_percol_8x12x4096x64():
-    _full_chunk_case("chunk_percol_8x12x4096x64", fw.FALCON_2, chains=[0, 50, 95])
+    _full_chunk_case("chunk_percol_8x12x4096x64", fw.FALCON_2)
 
 
 @pytest.mark.parametrize("variant", [fw.FALCON_3, fw.FALCON_3A])
 def test_chunk_window4_4x16x8192x128(variant):
-    _full_chunk_case("chunk_window4_4x16x8192x128", variant, chains=[0, 63], window=4)
+    _full_chunk_case("chunk_window4_4x16x8192x128", variant, window=4)
 
 
 # ---------------------------------------------------------------------------
 # decode
 
-def _decode_run(variant, nseq, heads, dk, dv, steps, pool, seed, sample, check_steps,
+def _decode_run(variant, nseq, heads, dk, dv, steps, pool, seed, check_steps,
                 beta=0.5, lam=0.01, eps=1e-6, per_ch=False):
+    """Every (sequence, head) pair against the oracle's decode run: o at the
+    steps in check_steps, S and k_prev at the end."""
     inp = decode_inputs(nseq, heads, dk, dv, seed=seed, steps=pool, beta_per_channel=per_ch)
     dt = torch.bfloat16
     S = to_dev(torch, inp["S"], torch.float32)
@@ -273,38 +275,35 @@ def _decode_run(variant, nseq, heads, dk, dv, steps, pool, seed, sample, check_s
     ks = to_dev(torch, inp["k"], dt)
     vs = to_dev(torch, inp["v"], dt)
     bs = to_dev(torch, inp["beta_t"], dt) if per_ch else None
-    flat = lambda a: a.reshape((-1,) + a.shape[2:])
-    S_ref = flat(inp["S"].astype(np.float64))[sample][:, None]
-    kp_ref = flat(inp["k_prev"].astype(np.float64))[sample][:, None]
-    worst = 0.0
+    got = {}
     for s in range(1, steps + 1):
         p = (s - 1) % pool
         o = fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=variant, beta=beta, lam=lam,
                            eps=eps, beta_t=bs[p] if per_ch else None)
-        pick = lambda a: flat(a[p].astype(np.float64))[sample][:, None]
-        o_ref, S_ref, kp_ref = fo.falcon_decode_step(
-            variant, S_ref, kp_ref, pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), beta=beta,
-            lam=lam, eps=eps, beta_t=pick(inp["beta_t"]) if per_ch else None)
         if s in check_steps:
             torch.cuda.synchronize()
-            o_s = flat(o.cpu().numpy())[sample]
-            err, _ = token_normwise_err(o_s, o_ref[:, 0])
-            worst = max(worst, err)
-            print("decode v%d step %d: o err %.3e" % (variant, s, err))
-            assert err <= TOL_BF16
+            got[s] = o.cpu().numpy().reshape(nseq * heads, dv)
     torch.cuda.synchronize()
-    serr = state_err(flat(S.cpu().numpy())[sample], S_ref[:, 0])
+    o_ref, S_ref, kp_ref = oracle_pool.decode_all_pairs(variant, inp, steps, check_steps,
+                                                        beta=beta, lam=lam, eps=eps)
+    worst = 0.0
+    for s in sorted(check_steps):
+        err, zok = token_normwise_err(got[s], o_ref[s])
+        worst = max(worst, err)
+        print("decode v%d step %d, all %d pairs: o err %.3e" % (variant, s, nseq * heads, err))
+        assert zok and err <= TOL_FP32_MATH
+    serr = state_err(S.cpu().numpy().reshape(S_ref.shape), S_ref)
     print("decode v%d after %d steps: S err %.3e" % (variant, steps, serr))
-    assert serr <= TOL_BF16
-    np.testing.assert_array_equal(flat(kp.cpu().float().numpy())[sample], kp_ref[:, 0])
+    assert serr <= TOL_FP32_MATH
+    np.testing.assert_array_equal(kp.cpu().float().numpy().reshape(kp_ref.shape), kp_ref)
     return worst
 
 
 def test_decode_512x12x64_1000_steps():
     cfg = WORKLOADS["decode_512x12x64"]
     N, H, dk, dv = cfg["shape"]
-    sample = np.array([0, 1, 777, 3000, N * H - 1])
-    _decode_run(fw.FALCON_1, N, H, dk, dv, 1000, 8, cfg["seed"], sample, {1, 10, 100, 1000},
+    print("decode 512x12x64: 1000 steps on the GPU, then the oracle over all pairs", flush=True)
+    _decode_run(fw.FALCON_1, N, H, dk, dv, 1000, 8, cfg["seed"], {1, 10, 100, 1000},
                 beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"])
 
 
@@ -312,8 +311,7 @@ def test_decode_512x12x64_1000_steps():
 @pytest.mark.parametrize("dk,dv", [(64, 64), (16, 128), (128, 32)])
 def test_decode_small(variant, dk, dv):
     per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
-    sample = np.arange(6)
-    _decode_run(variant, 3, 2, dk, dv, 20, 4, 500 + variant, sample, {1, 20}, per_ch=per_ch)
+    _decode_run(variant, 3, 2, dk, dv, 20, 4, 500 + variant, {1, 20}, per_ch=per_ch)
 
 
 # ---------------------------------------------------------------------------
@@ -326,8 +324,6 @@ def test_decode_small(variant, dk, dv):
 @pytest.mark.parametrize("same_step", [False, True])
 def test_window_history_resume(form, variant, dk, dv, window, same_step):
     """Resumed call: S0, k_prev and the window history in; o, S and the history out."""
-    if form == "rec" and dk == 128:
-        pytest.skip("covered by the chunk form")
     inp = seq_inputs(2, 2, 77, dk, dv, seed=600 + 7 * variant + 3 * window + dk, dtype="bf16",
                      with_k_prev=True, with_S0=True, beta_per_token=True, s_std=0.2,
                      history=window - 1)
@@ -609,25 +605,25 @@ def test_backward_wide(variant, window, dk, dv):
     assert max(errs.values()) <= TOL_FP32_MATH, errs
 
 
-def test_backward_8x12x2048x64_sampled():
-    """Headline workload: all chains on the GPU, two chains recomputed by the oracle."""
+def test_backward_8x12x2048x64():
+    """Headline workload: every chain's gradients against the oracle's."""
     cfg = WORKLOADS["chunk_8x12x2048x64"]
     B, H, L, dk, dv = cfg["shape"]
     inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16")
     rng = np.random.default_rng(809)
     dO = rng.standard_normal((B, H, L, dv)).astype(np.float32)
     dt = torch.bfloat16
+    print("backward 8x12x2048x64: launching", flush=True)
     got = fw.bwd_chunk(*(to_dev(torch, inp[n], dt) for n in ("q", "k", "v")),
                        to_dev(torch, dO, torch.float32), variant=fw.FALCON_1, beta=cfg["beta"],
                        lam=cfg["lam"], eps=cfg["eps"])
     torch.cuda.synchronize()
-    chains = np.array([5, B * H - 1])
-    sel = lambda a: a.reshape((-1,) + a.shape[2:])[chains][:, None]
-    ref = fo.falcon_backward(fw.FALCON_1, sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(dO),
-                             beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"])
-    errs = {n: _grad_err(sel(got[n].cpu().numpy()), ref[n]) for n in ref}
-    print("backward 8x12x2048x64 chains %s: %s" % (list(chains), {n: "%.2e" % e for n, e in errs.items()}))
-    assert max(errs.values()) <= 1e-3, errs
+    print("backward 8x12x2048x64: oracle over %d chains" % (B * H), flush=True)
+    ref = oracle_pool.backward_all_chains(fw.FALCON_1, inp, dO, beta=cfg["beta"],
+                                          lam=cfg["lam"], eps=cfg["eps"])
+    errs = {n: _grad_err(got[n].cpu().numpy().reshape(ref[n].shape), ref[n]) for n in ref}
+    print("backward 8x12x2048x64, all chains: %s" % {n: "%.2e" % e for n, e in errs.items()})
+    assert max(errs.values()) <= TOL_FP32_MATH, errs
 
 
 # ---------------------------------------------------------------------------

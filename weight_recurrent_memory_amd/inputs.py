@@ -52,7 +52,7 @@ def _l2n(a: np.ndarray) -> np.ndarray:
 
 def seq_inputs(batch, heads, L, dk, dv, *, seed, dtype="bf16", beta_per_token=False,
                beta_per_channel=False, with_k_prev=False, with_S0=False, s_std=0.02,
-               history=0):
+               history=0, key_norms=None):
     """q, k [B,H,L,dk], v [B,H,L,dv] ~ N(0,1) with q, k L2-normalized per token.
 
     Returns a dict of float32 arrays holding exactly the values of the chosen
@@ -61,6 +61,9 @@ def seq_inputs(batch, heads, L, dk, dv, *, seed, dtype="bf16", beta_per_token=Fa
     (one normalized key per (batch, head)), S0 (N(0, s_std^2)) and, with
     history = n > 0, a carried window history x_hist [B,H,n,dk] (normalized
     keys) and y_hist [B,H,n,dv] (N(0,1)), drawn after everything else.
+    key_norms = (lo, hi) rescales every key (and k_prev, x_hist) to a norm drawn
+    log-uniformly from [lo, hi], after all other draws (unnormalized keys: the
+    step size beta / (eps + ||x||^2) then varies from token to token).
     """
     rng = np.random.default_rng(seed)
     q = _l2n(rng.standard_normal((batch, heads, L, dk), dtype=np.float32))
@@ -81,6 +84,12 @@ def seq_inputs(batch, heads, L, dk, dv, *, seed, dtype="bf16", beta_per_token=Fa
     if history > 0:
         out["x_hist"] = _l2n(rng.standard_normal((batch, heads, history, dk), dtype=np.float32))
         out["y_hist"] = rng.standard_normal((batch, heads, history, dv), dtype=np.float32)
+    if key_norms is not None:
+        lo, hi = np.log(key_norms[0]), np.log(key_norms[1])
+        for name in ("k", "k_prev", "x_hist"):
+            if name in out:
+                r = np.exp(rng.uniform(lo, hi, size=out[name].shape[:-1] + (1,)))
+                out[name] = (out[name] * r).astype(np.float32)
     if dtype == "bf16":
         for name in ("q", "k", "v", "beta_t", "k_prev", "x_hist", "y_hist"):
             if name in out:
