@@ -103,7 +103,7 @@ const char* falcon_status_string(int status);
  *   k_prev    key carried from the previous call, or NULL (fresh sequence)
  *   S0        initial state, or NULL (zero).  S0 != NULL requires k_prev.
  *             window > 1 with S0 != NULL is unsupported here (the window
- *             history is carried by falcon_fwd_recurrent_hist).
+ *             history is carried by falcon_fwd_recurrent_ex).
  *   o         output [batch, heads, L, dv] float32 (must not alias inputs)
  *   S_out     final state, or NULL; may equal S0 (in-place carry)
  *   stream    hipStream_t or NULL
@@ -119,15 +119,27 @@ int falcon_fwd_recurrent(int variant, int window, float beta, const void* beta_t
  * falcon_fwd_chunk - the chunk-parallel form (explainer §3 "chunk-parallel";
  * 163.com section 02 (2): parallel inside a chunk, only the fixed-size state
  * crosses chunks).  Same arguments and results as falcon_fwd_recurrent plus
- *   chunk     tokens per chunk, in {16, 32, 64}; any L (a short last chunk is
- *             handled in place)
+ *   chunk     requested tokens per chunk, in {16, 32, 64}; any L (a short last
+ *             chunk is handled in place)
  * Restrictions (FALCON_ERR_UNSUPPORTED): dtype must be FALCON_BF16;
  * window <= 4, except FALCON_3A with gains shared by the value rows (scalar or
  * per-token beta), dk in {64, 128} and dv a multiple of 32: window <= 16.
  * window <= chunk (FALCON_ERR_INVALID_ARG otherwise).
+ *   chunk is a tuning hint: each kernel family runs its own chunk length (32
+ *   steps for window 1 with shared gains and dk 32 or 64; 16-step sub-chunks for
+ *   windows 2..4 of the regression family; 64 for the inner-product family with
+ *   shared gains; the requested length, halved until chunk * window <= 64 and
+ *   at most 32 at dk 128, otherwise); the result does not depend on it beyond
+ *   rounding.
  * The result equals the recurrence up to floating-point rounding (state
  * carried in float32, products on bf16 matrix cores with split-bf16 operands
- * where an operand is not an exact bf16 input).
+ * where an operand is not an exact bf16 input) for every finite input: the
+ * chunk algebra scales a chunk's unknowns by the decay products
+ * g_t = prod (1 - eta_r lambda) over the chunk, and when some |g_t| leaves
+ * [2^-100, 2^100] or some decay |1 - eta_t lambda| is below 2^-24 (strong
+ * forgetting, eta_t lambda near 1 or above 2) the kernel recomputes that
+ * (batch, head) chain exactly by the recurrence, in the same launch (slower:
+ * one token at a time).
  */
 int falcon_fwd_chunk(int variant, int window, float beta, const void* beta_t,
                      int beta_kind, float lambda, float eps, int batch, int heads,
@@ -259,6 +271,12 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  * Outputs must not overlap each other, the inputs or the workspace.
  * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 8 or a
  * windowed start state.
+ * Range: the chunks of floor(16 / window) steps are scaled by their decay
+ * products g_t = prod (1 - eta_r lambda); for a (batch, head) chain in which
+ * some |g_t| leaves [2^-100, 2^100] or some |1 - eta_t lambda| is below 2^-24
+ * (strong forgetting) the gradients are not computed: every output of that
+ * chain is set to NaN (the forward entry points have an exact path for such
+ * chains; the backward has none).
  */
 unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk, int dv,
                                               int window);

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from oracle import falcon_oracle as fo
-from weight_recurrent_memory_amd.inputs import decode_inputs, seq_inputs
+from weight_recurrent_memory_amd.inputs import decode_inputs, seq_inputs, to_bf16_values
 from parity_util import TOL_BF16, TOL_FP32_MATH, state_err, to_dev, token_normwise_err
 
 pytestmark = pytest.mark.gpu
@@ -88,13 +88,18 @@ def _chunk_vs_oracle(label, variant, dk, dv, window, gains, chunk, inp, *, beta,
 @pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
 @pytest.mark.parametrize("lam_beta", [0.5, 0.9, 0.99])
 def test_chunk_strong_decay(fam, lam_beta):
-    """beta = 1 (or per-token / per-channel gains in (0, 1)) and lambda = the
-    target product: with normalized keys eta_t lambda reaches lam_beta."""
+    """eta_t lambda close to lam_beta at every step: gains near 1 (scalar 1, or
+    per-token / per-channel gains in [0.95, 1]) and lambda = lam_beta * window,
+    so with unit keys (n_t = window) the decay a_t = 1 - eta_t lambda sits
+    between 1 - lam_beta and about 1.05 (1 - lam_beta); at 0.99 the product of
+    the decays over 32 steps is far below the float32 range."""
     label, variant, dk, dv, window, gains, chunk = fam
     L = 3 * 64 + 11
     inp = _inputs(label, variant, dk, dv, gains, L, seed=900 + int(100 * lam_beta) + dk + window)
+    if "beta_t" in inp:
+        inp["beta_t"] = to_bf16_values(0.95 + 0.05 * inp["beta_t"])
     _chunk_vs_oracle("%s lam*beta %.2f" % (label, lam_beta), variant, dk, dv, window, gains,
-                     chunk, inp, beta=1.0, lam=lam_beta, eps=1e-6)
+                     chunk, inp, beta=1.0, lam=lam_beta * window, eps=1e-6)
 
 
 @pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
@@ -187,3 +192,86 @@ def test_decode_interpolation_fp32(variant, dk, dv):
         assert interp <= TOL_FP32_MATH
         assert zok and err <= TOL_FP32_MATH
     assert state_err(S.cpu().numpy(), S_r) <= TOL_FP32_MATH
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=[f[0] for f in FAMILIES])
+def test_chunk_zero_decay(fam):
+    """a_t = 0 exactly: one-hot keys (unit norm in bfloat16), eps = 0, gains 1 and
+    lambda = window, so eta_t lambda = 1 at every step whose window is full; the
+    state forgets everything but the current write (inner-product family) or
+    its projection (regression family)."""
+    label, variant, dk, dv, window, gains, chunk = fam
+    L = 2 * 64 + 21
+    inp = _inputs(label, variant, dk, dv, gains, L, seed=980 + dk + window, with_k_prev=True)
+    rng = np.random.default_rng(981 + dk + window)
+    onehot = lambda shape: np.eye(dk, dtype=np.float32)[rng.integers(0, dk, size=shape)]
+    inp["k"] = onehot(inp["k"].shape[:-1])
+    inp["k_prev"] = onehot(inp["k_prev"].shape[:-1])
+    if "beta_t" in inp:
+        inp["beta_t"] = np.ones_like(inp["beta_t"])
+    _chunk_vs_oracle(label + " zero decay", variant, dk, dv, window, gains, chunk, inp,
+                     beta=1.0, lam=float(window), eps=0.0, carried=True)
+
+
+@pytest.mark.parametrize("variant,window", [(fw.FALCON_1, 1), (fw.FALCON_2, 1), (fw.FALCON_3, 4),
+                                            (fw.FALCON_1A, 1), (fw.FALCON_3A, 3)])
+@pytest.mark.parametrize("lam_beta", [0.5, 0.9])
+def test_backward_strong_decay(variant, window, lam_beta):
+    """The backward's 16-step chunks keep their decay products in range up to
+    eta_t lambda of about 0.95: gradients match the oracle's at 0.5 and 0.9."""
+    per_ch = variant == fw.FALCON_2
+    L, dk, dv = 53, 32, 16
+    inp = seq_inputs(2, 2, L, dk, dv, seed=1300 + variant + window + int(10 * lam_beta),
+                     dtype="bf16", beta_per_channel=per_ch, beta_per_token=not per_ch,
+                     with_k_prev=True)
+    inp["beta_t"] = to_bf16_values(0.95 + 0.05 * inp["beta_t"])
+    rng = np.random.default_rng(1301 + variant)
+    dO = rng.standard_normal((2, 2, L, dv)).astype(np.float32)
+    dev = lambda n: to_dev(torch, inp[n], torch.bfloat16)
+    got = fw.bwd_chunk(dev("q"), dev("k"), dev("v"), to_dev(torch, dO, torch.float32),
+                       variant=variant, beta=None, lam=lam_beta * window, eps=1e-6,
+                       window=window, beta_t=dev("beta_t"), k_prev=dev("k_prev"))
+    torch.cuda.synchronize()
+    ref = fo.falcon_backward(variant, inp["q"], inp["k"], inp["v"], dO, beta=None,
+                             lam=lam_beta * window, eps=1e-6, window=window,
+                             beta_t=inp["beta_t"], k_prev=inp["k_prev"])
+    errs = {}
+    for n in ref:
+        g = got[n].cpu().numpy().astype(np.float64)
+        errs[n] = float(np.max(np.abs(g - ref[n])) / max(np.max(np.abs(ref[n])), 1e-30))
+    print("backward strong decay v%d w%d lam*beta %.1f: %s"
+          % (variant, window, lam_beta, {n: "%.2e" % e for n, e in errs.items()}))
+    assert max(errs.values()) <= TOL_FP32_MATH, errs
+
+
+@pytest.mark.parametrize("variant,window", [(fw.FALCON_1, 1), (fw.FALCON_3, 4), (fw.FALCON_1A, 1)])
+@pytest.mark.parametrize("dv", [16, 64])
+def test_backward_out_of_range_is_nan(variant, window, dv):
+    """a_t = 0 exactly (one-hot keys, eps = 0, lambda = window): the backward has
+    no exact path for such chains and marks every gradient of the chain NaN;
+    a chain whose decays stay in range (keys of norm 2: eta_t lambda near 1/4)
+    keeps finite, oracle-exact gradients."""
+    L, dk = 41, 32
+    inp = seq_inputs(1, 2, L, dk, dv, seed=1310 + variant + window + dv, dtype="bf16",
+                     with_k_prev=True)
+    rng = np.random.default_rng(1311 + dv)
+    onehot = lambda shape: np.eye(dk, dtype=np.float32)[rng.integers(0, dk, size=shape)]
+    inp["k"][:, 0] = onehot((1, L))             # head 0: zero decay
+    inp["k_prev"][:, 0] = onehot((1,))
+    inp["k"][:, 1] *= 2.0                       # head 1: keys of norm 2, a_t near 3/4
+    inp["k_prev"][:, 1] *= 2.0
+    dO = rng.standard_normal((1, 2, L, dv)).astype(np.float32)
+    dev = lambda n: to_dev(torch, inp[n], torch.bfloat16)
+    got = fw.bwd_chunk(dev("q"), dev("k"), dev("v"), to_dev(torch, dO, torch.float32),
+                       variant=variant, beta=1.0, lam=float(window), eps=0.0, window=window,
+                       k_prev=dev("k_prev"))
+    torch.cuda.synchronize()
+    ref = fo.falcon_backward(variant, inp["q"][:, 1:], inp["k"][:, 1:], inp["v"][:, 1:],
+                             dO[:, 1:], beta=1.0, lam=float(window), eps=0.0, window=window,
+                             k_prev=inp["k_prev"][:, 1:])
+    for n, g in got.items():
+        g = g.cpu().numpy()
+        assert np.all(np.isnan(g[:, 0])), n
+        assert np.all(np.isfinite(g[:, 1])), n
+        err = float(np.max(np.abs(g[:, 1:] - ref[n])) / max(np.max(np.abs(ref[n])), 1e-30))
+        assert err <= TOL_FP32_MATH, (n, err)

@@ -41,8 +41,18 @@ def flags():
             "-I" + INCLUDE, "-I" + CSRC, "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")] \
+        + [os.path.join(INCLUDE, h) for h in os.listdir(INCLUDE)]
+    return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     cmd = [hipcc()] + flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,10 +61,11 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (only the stale ones with incremental=True) and link."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, incremental), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,5 +78,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

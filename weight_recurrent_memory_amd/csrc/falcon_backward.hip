@@ -43,6 +43,7 @@
 // written by the forward sweep come back through the workspace.  Arithmetic is
 // fp32 throughout.
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -91,6 +92,7 @@ struct BwdLds {
   float dG[BC][BP];
   float dP[BC][BP];
   float dn[BC];
+  int bad;                // some chunk's decay products left the range
 };
 
 // workgroup barrier that orders LDS only: global stores issued before it may
@@ -512,6 +514,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
       r.gm = s == 0 ? 1.0f : gp;
     }
     r.zeta = r.eta / g;
+    if (gauge_out_of_range(g, r.av)) sm.bad = 1;
     return r;
   };
   // forward sweep of value row i (lane t): z (and for the backward e, h, eta,
@@ -541,6 +544,7 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     if (t == 0) sm.gC[i] = gc;
   };
   // ================= forward sweep: chunk-start states =================
+  if (tid == 0) sm.bad = 0;
   for (int idx = tid; idx < RB * DK; idx += BNT) {
     const int i = idx / DK, kk = idx % DK;
     sm.S[i][kk] = a.S0 ? a.S0[(chain * dvf + i0 + i) * DK + kk] : 0.0f;
@@ -911,6 +915,29 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
   if (a.dS0) {
     for (int idx = tid; idx < RB * DK; idx += BNT)
       a.dS0[(chain * dvf + i0 + idx / DK) * DK + idx % DK] = sm.dS[idx / DK][idx % DK];
+  }
+  // A chunk whose decay products left the range of the chunk algebra: the
+  // chain's gradients are not computed; every output this workgroup writes for
+  // the chain (its value rows, and the chain's dq, dk, dk_prev and per-token
+  // dbeta, or its slice's partial sums of them, which the sum kernel adds) is
+  // set to NaN instead.
+  __syncthreads();
+  if (sm.bad) {
+    const float nan = __builtin_nanf("");
+    for (long e = tid; e < L * RB; e += BNT) {
+      a.dv[v_base + (e / RB) * dvf + i0 + e % RB] = nan;
+      if (a.dbeta_t && a.beta_kind == 2) a.dbeta_t[v_base + (e / RB) * dvf + i0 + e % RB] = nan;
+    }
+    for (long e = tid; e < L * DK; e += BNT) {
+      oq[qk_base + e] = nan;
+      ok[qk_base + e] = nan;
+    }
+    if (okp)
+      for (int e = tid; e < DK; e += BNT) okp[chain * DK + e] = nan;
+    if (odb && a.beta_kind == 1)
+      for (long e = tid; e < L; e += BNT) odb[chain * L + e] = nan;
+    if (a.dS0)
+      for (int idx = tid; idx < RB * DK; idx += BNT) a.dS0[(chain * dvf + i0 + idx / DK) * DK + idx % DK] = nan;
   }
 }
 

@@ -47,6 +47,7 @@
 // (at most 64 unknowns per triangular system) and to at most 32 for dk = 128
 // (LDS budget); the result does not depend on it beyond rounding.
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -111,6 +112,7 @@ struct Lds {
   float gam[SR][CS];
   float gm1[SR][CS];
   float zeta[SR][CS];
+  int bad;                           // some sub-chunk's decay products left the range
 };
 
 struct Geom {
@@ -225,6 +227,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
   };
 
   // ---------------- state ----------------
+  if (tid == 0) sm.bad = 0;
   for (int idx = tid; idx < RW * DK; idx += NT) {
     const int i = idx / DK, kk = idx % DK;
     float s = 0.0f;
@@ -314,6 +317,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
         }
         float gprev = __shfl_up(gsc, 1, 64);
         if (lane == 0) gprev = 1.0f;
+        if (__builtin_amdgcn_ballot_w64(t < CS && gauge_out_of_range(gsc, dec)) != 0 && lane == 0) sm.bad = 1;
         if (t < CS) {
           sm.gam[i][t] = gsc;
           sm.gm1[i][t] = gprev;
@@ -650,12 +654,16 @@ __global__ __launch_bounds__(NT) void chunk_kernel(SeqArgs a, Geom geo) {
     }
   }
   __syncthreads();
-  if (a.S_out) {
+  if (a.S_out && !sm.bad) {
     for (int idx = tid; idx < RW * DK; idx += NT) {
       const int i = idx / DK, kk = idx % DK;
       if (i0 + i < dv) a.S_out[((long)chain * dv + i0 + i) * DK + kk] = sm.S[i][kk];
     }
   }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (S_out was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, NT, B>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
 }
 
 template <int DK, int CS, int B, bool REG, bool PERROW>

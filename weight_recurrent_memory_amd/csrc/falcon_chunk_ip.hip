@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -71,6 +72,7 @@ struct IpLds {
   float zq[2][IK + 4];                 // [16 + j] = Z_{min(j+B-1, C-1)}
   float c63[2][IK];                    // c_{m, C-1}, by chunk parity
   float opart[4][IC][OPP];             // S0 q partial sums of the state waves, [t][row]
+  int bad;                             // some chunk's decay products left the range
 };
 
 struct IpGeom {
@@ -362,6 +364,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     g *= lg >= 1 ? p0 : 1.0f;
     g *= lg >= 2 ? p1 : 1.0f;
     g *= lg >= 3 ? p2 : 1.0f;
+    if (__builtin_amdgcn_ballot_w64(gauge_out_of_range(g, av)) != 0 && lane == 0) sm.bad = 1;
     float z = eta * __builtin_amdgcn_rcpf(g);
     z += ip_shr<1>(z, 0.0f);
     z += ip_shr<2>(z, 0.0f);
@@ -390,6 +393,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     if (lane < 16) sm.c63[pb][IC + lane] = cweight(sm.zs[pb], IC + lane, IC - 1);
   };
 
+  if (threadIdx.x == 0) sm.bad = 0;
   Set s0, s1;
   issue(s0, 0);
   issue(s1, 1);
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
       body(c, s1, s0);
       body(c + 1, s0, s1);
     }
-    if (a.S_out) {
+    if (a.S_out && !sm.bad) {
 #pragma unroll
       for (int kt = 0; kt < HKT; ++kt)
         *reinterpret_cast<float4*>(a.S_out + ((long)chain * dv + row) * DK + 16 * (hh * HKT + kt) + 4 * lg) =
@@ -623,8 +627,13 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
       // issues first on the SIMD it shares (measured: about 2%)
       __builtin_amdgcn_s_setprio(1);
       readout(std::integral_constant<int, 3>{});
+      __builtin_amdgcn_s_setprio(0);
     }
   }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (S_out was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, INT, 16>(chain, i0, IRB);
 }
 
 template <int DK>

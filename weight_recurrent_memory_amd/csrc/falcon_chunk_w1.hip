@@ -30,6 +30,7 @@
 //            of chunk c+1 (shared eta) or its Gram and q.x (per-channel eta)
 // One workgroup = 8 wave64 = one (batch*head) chain x 32 value rows.
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -114,6 +115,7 @@ struct W1Lds {
   alignas(16) float gam[SCB][SR][CS];
   alignas(16) float gm1[SCB][SR][CS];
   alignas(16) float zeta[SCB][SR][CS];
+  int bad;                           // some chunk's decay products left the range
 };
 
 struct W1Geom {
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     }
     float gprev = __shfl_up(gsc, 1, 64);
     if (lane == 0) gprev = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(t < CS && gauge_out_of_range(gsc, dec)) != 0 && lane == 0) sm.bad = 1;
     if (t < CS) {
       sm.gam[dst][row][t] = gsc;
       sm.gm1[dst][row][t] = gprev;
@@ -306,12 +309,13 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     const int t = lane % CS, rl = lane / CS;
     const bool live = t < c && !(t0 + t == 0 && kpg == nullptr && a.key_shift);
     const float rn = __builtin_amdgcn_rcpf(a.eps + sm.nrm[s][t]);
-    float eta[NC], g[NC];
+    float eta[NC], g[NC], dec[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
       const float bv = bf16_to_f32(sm.BT[s][r0 + k * rstep + rl][t]);
       eta[k] = live ? bv * rn : 0.0f;
       g[k] = __builtin_fmaf(-eta[k], a.lambda, 1.0f);
+      dec[k] = g[k];
     }
 #pragma unroll
     for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<1>(g[k]);
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         fill = (lane & 31) == 16 ? tot : 1.0f;
       }
       const float gprev = row_shr<1>(g[k], fill);
+      if (__builtin_amdgcn_ballot_w64(gauge_out_of_range(g[k], dec[k])) != 0 && lane == 0) sm.bad = 1;
       const int row = r0 + k * rstep + rl;
       sm.gam[dst][row][t] = g[k];
       sm.gm1[dst][row][t] = gprev;
@@ -438,6 +443,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
   };
 
   // ---------------- prologue: state, chunk 0 ----------------
+  if (tid == 0) sm.bad = 0;
   for (int idx = tid; idx < RW * DK; idx += NT) {
     const int i = idx / DK, kk = idx % DK;
     float sv = 0.0f;
@@ -668,12 +674,16 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     __syncthreads();
   }
   if (optr) *reinterpret_cast<float4*>(optr) = opend;
-  if (a.S_out) {
+  if (a.S_out && !sm.bad) {
     for (int idx = tid; idx < RW * DK; idx += NT) {
       const int i = idx / DK, kk = idx % DK;
       if (i0 + i < dv) a.S_out[((long)chain * dv + i0 + i) * DK + kk] = sm.S[i][kk];
     }
   }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (S_out was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, NT, 1>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
 }
 
 template <int DK, int CS, bool REG, bool PERROW>

@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -78,6 +79,7 @@ struct WyLds {
   alignas(16) float gm1[8][CS];
   alignas(16) float zeta[8][CS];
   alignas(16) float omega[8][CS];
+  int bad;                               // some chunk's decay products left the range
 };
 
 struct WyGeom {
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
   };
 
   // ---------------- zero the fragment slots no stage writes ----------------
+  if (tid == 0) sm.bad = 0;
   for (int idx = tid; idx < 2 * 2 * 16 * (CS + 4); idx += NT) (&sm.SA[0][0][0][0])[idx] = 0.0f;
   for (int idx = tid; idx < 2 * CS * SM::TR; idx += NT) {
     (&sm.Phi[0][0][0])[idx] = 0;
@@ -326,6 +329,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     const float row0 = lane_value(gsc, 15);
     if (lane >= 16) gsc *= row0;
     const float gprev = dpp_shr<1>(gsc, lane == 16 ? row0 : 1.0f);
+    if (__builtin_amdgcn_ballot_w64(gauge_out_of_range(gsc, dec)) != 0 && lane == 0) sm.bad = 1;
     if (lane < CS) {
       const float z = eta * __builtin_amdgcn_rcpf(gsc);
       sm.gam[sb][t] = gsc;
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
       if (state_wave && c + 1 >= 0 && c + 1 < nchunks) ops = load_ops(c + 1);
       __syncthreads();
     }
-    if (state_wave && a.S_out) {
+    if (state_wave && a.S_out && !sm.bad) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
         *reinterpret_cast<float4*>(a.S_out + ((long)chain * dv + i0 + 16 * rt + lr) * DK + 16 * kt + 4 * lg) =
@@ -737,6 +741,10 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
       }
     }
   }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (the state was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, NT, 1>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
 }
 
 template <int DK, bool REG>

@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "falcon_device.h"
+#include "falcon_exact.h"
 #include "falcon_launch.h"
 #include "falcon_mma.h"
 
@@ -95,6 +96,7 @@ struct WybLds {
   uint16_t Pfhi[2][CS][HP];              // P' fragments over the unknowns, by pair of blocks
   uint16_t Pflo[2][CS][HP];
   alignas(16) float cm[2][NXT];          // inner-product family: sum of zeta per key
+  int bad;                               // some sub-chunk's decay products left the range
 };
 
 struct WybGeom {
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   auto mof = [](int u) __attribute__((always_inline)) { return 16 + u / B - u % B; };
 
   // ---------------- block -1 (before the sequence) is zero ----------------
+  if (tid == 0) sm.bad = 0;
   for (int idx = tid; idx < CS * SM::XR; idx += NT) (&sm.X[3][0][0])[idx] = 0;
   for (int idx = tid; idx < DK * SM::TP; idx += NT) (&sm.XT[3][0][0])[idx] = 0;
   for (int idx = tid; idx < RW * SM::TP; idx += NT) (&sm.YT[3][0][0])[idx] = 0;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     gsc *= dpp_shr<4>(gsc, 1.0f);
     gsc *= dpp_shr<8>(gsc, 1.0f);
     const float gprev = dpp_shr<1>(gsc, 1.0f);
+    if (__builtin_amdgcn_ballot_w64(lane < 16 && gauge_out_of_range(gsc, dec)) != 0 && lane == 0) sm.bad = 1;
     const float z = eta * __builtin_amdgcn_rcpf(gsc);
     float zc = z;
     zc += dpp_shr<1>(zc, 0.0f);
@@ -743,7 +747,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       }
     }
     __syncthreads();
-    if (rows_in && a.S_out && i0 + 16 * rt + lr < dv) {
+    if (rows_in && a.S_out && !sm.bad && i0 + 16 * rt + lr < dv) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
         *reinterpret_cast<float4*>(a.S_out + ((long)chain * dv + i0 + 16 * rt + lr) * DK + 16 * kt + 4 * lg) =
@@ -832,6 +836,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     }
     __syncthreads();
   }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (S_out was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, NT, B>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
 }
 
 template <int DK, bool REG, int B>
