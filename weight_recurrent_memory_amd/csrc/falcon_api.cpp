@@ -310,14 +310,16 @@ FALCON_EXPORT unsigned long long falcon_bwd_workspace_bytes(int batch, int heads
   return (unsigned long long)falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);
 }
 
-FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float beta, const void* beta_t,
-                                   int beta_kind, float lambda, float eps, int batch, int heads,
-                                   int seqlen, int dk, int dv, int dtype, const void* q,
-                                   const void* k, const void* v, const void* k_prev,
-                                   const float* S0, const float* dO, const float* dS_L,
-                                   const float* dk_last, float* dq, float* dk_out, float* dv_out,
-                                   float* dbeta_t, float* dk_prev, float* dS0, void* workspace,
-                                   unsigned long long workspace_bytes, void* stream) {
+namespace {
+
+// Validation of a backward call, everything but the workspace.  On success
+// fills *b (workspace left null) and *need (workspace bytes).
+int check_bwd(int variant, int window, int flags, float beta, const void* beta_t, int beta_kind,
+              float lambda, float eps, int batch, int heads, int seqlen, int dk, int dv, int dtype,
+              const void* q, const void* k, const void* v, const void* k_prev, const float* S0,
+              const float* dO, const float* dS_L, const float* dk_last, float* dq, float* dk_out,
+              float* dv_out, float* dbeta_t, float* dk_prev, float* dS0, falcon::BwdArgs* b,
+              size_t* need) {
   if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
   const int key_shift = (flags & FALCON_SAME_STEP) ? 0 : 1;
   // the forward arguments are checked as the forward checks them (dO takes the
@@ -327,11 +329,11 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
                     const_cast<float*>(dO), nullptr, 0, nullptr, nullptr, key_shift};
   int st = check_seq(a, true);
   if (st != FALCON_OK) return st;
-  if (!dq || !dk_out || !dv_out || !workspace) return FALCON_ERR_INVALID_ARG;
+  if (!dq || !dk_out || !dv_out) return FALCON_ERR_INVALID_ARG;
   if (dbeta_t && beta_kind == FALCON_BETA_SCALAR) return FALCON_ERR_INVALID_ARG;
   if (dk_prev && (!k_prev || !key_shift)) return FALCON_ERR_INVALID_ARG;
   if (dS0 && !S0) return FALCON_ERR_INVALID_ARG;
-  const void* ptrs[] = {dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0, workspace};
+  const void* ptrs[] = {dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FALCON_ERR_INVALID_ARG;
   // windows 1..8; a windowed start state would need its window history,
@@ -340,15 +342,12 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
   if (window > 1 && S0) return FALCON_ERR_UNSUPPORTED;
   const size_t es = dtype == FALCON_BF16 ? 2 : 4;
   const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
-  const size_t need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);
-  if (workspace_bytes < need) return FALCON_ERR_INVALID_ARG;
   Range outs[] = {{dq, BH * L * dk * 4},
                   {dk_out, BH * L * dk * 4},
                   {dv_out, BH * L * dv * 4},
                   {dbeta_t, BH * L * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * 4},
                   {dk_prev, BH * dk * 4},
-                  {dS0, BH * dv * dk * 4},
-                  {workspace, need}};
+                  {dS0, BH * dv * dk * 4}};
   Range ins[] = {{q, BH * L * dk * es},
                  {k, BH * L * dk * es},
                  {v, BH * L * dv * es},
@@ -358,15 +357,56 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
                  {dO, BH * L * dv * 4},
                  {dS_L, BH * dv * dk * 4},
                  {dk_last, BH * dk * 4}};
-  for (int i = 0; i < 7; ++i) {
-    for (int j = i + 1; j < 7; ++j)
+  for (int i = 0; i < 6; ++i) {
+    for (int j = i + 1; j < 6; ++j)
       if (overlap(outs[i], outs[j])) return FALCON_ERR_INVALID_ARG;
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return FALCON_ERR_INVALID_ARG;
   }
-  falcon::BwdArgs b{is_regression(variant), window, key_shift, beta, beta_t, beta_kind, lambda, eps,
-                    batch, heads, (long)seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO, dS_L,
-                    dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0,
-                    static_cast<float*>(workspace)};
+  *need = falcon::backward_workspace_bytes(batch, heads, seqlen, dk, dv, window);
+  *b = falcon::BwdArgs{is_regression(variant), window, key_shift, beta, beta_t, beta_kind, lambda,
+                       eps, batch, heads, (long)seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO,
+                       dS_L, dk_last, dq, dk_out, dv_out, dbeta_t, dk_prev, dS0, nullptr};
+  return FALCON_OK;
+}
+
+}  // namespace
+
+FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float beta, const void* beta_t,
+                                   int beta_kind, float lambda, float eps, int batch, int heads,
+                                   int seqlen, int dk, int dv, int dtype, const void* q,
+                                   const void* k, const void* v, const void* k_prev,
+                                   const float* S0, const float* dO, const float* dS_L,
+                                   const float* dk_last, float* dq, float* dk_out, float* dv_out,
+                                   float* dbeta_t, float* dk_prev, float* dS0, void* workspace,
+                                   unsigned long long workspace_bytes, void* stream) {
+  falcon::BwdArgs b;
+  size_t need = 0;
+  int st = check_bwd(variant, window, flags, beta, beta_t, beta_kind, lambda, eps, batch, heads,
+                     seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO, dS_L, dk_last, dq, dk_out,
+                     dv_out, dbeta_t, dk_prev, dS0, &b, &need);
+  if (st != FALCON_OK) return st;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FALCON_ERR_INVALID_ARG;
+  const size_t es = dtype == FALCON_BF16 ? 2 : 4;
+  const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
+  const Range ws{workspace, need};
+  const Range others[] = {{dq, BH * L * dk * 4},
+                          {dk_out, BH * L * dk * 4},
+                          {dv_out, BH * L * dv * 4},
+                          {dbeta_t, BH * L * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * 4},
+                          {dk_prev, BH * dk * 4},
+                          {dS0, BH * dv * dk * 4},
+                          {q, BH * L * dk * es},
+                          {k, BH * L * dk * es},
+                          {v, BH * L * dv * es},
+                          {k_prev, BH * dk * es},
+                          {S0, BH * dv * dk * 4},
+                          {beta_t, BH * L * (beta_kind == FALCON_BETA_CHANNEL ? dv : 1) * es},
+                          {dO, BH * L * dv * 4},
+                          {dS_L, BH * dv * dk * 4},
+                          {dk_last, BH * dk * 4}};
+  for (const Range& r : others)
+    if (overlap(ws, r)) return FALCON_ERR_INVALID_ARG;
+  b.workspace = static_cast<float*>(workspace);
   return finish_launch(falcon::launch_backward(b, (hipStream_t)stream));
 }
