@@ -544,7 +544,11 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     if (t == 0) sm.gC[i] = gc;
   };
   // ================= forward sweep: chunk-start states =================
-  if (tid == 0) sm.bad = 0;
+  // LDS starts as zeros: rows of the last, partial chunk that the sweeps read
+  // without writing (padded steps, idle window lanes) then hold zeros, not
+  // whatever an earlier workgroup left there
+  for (int idx = tid; idx < (int)(sizeof(SM) / sizeof(float)); idx += BNT) reinterpret_cast<float*>(&sm)[idx] = 0.0f;
+  __syncthreads();
   for (int idx = tid; idx < RB * DK; idx += BNT) {
     const int i = idx / DK, kk = idx % DK;
     sm.S[i][kk] = a.S0 ? a.S0[(chain * dvf + i0 + i) * DK + kk] : 0.0f;
@@ -930,7 +934,9 @@ __global__ __launch_bounds__(BNT) void backward_kernel(BwdArgs a) {
     }
     for (long e = tid; e < L * DK; e += BNT) {
       oq[qk_base + e] = nan;
-      ok[qk_base + e] = nan;
+      // k_{L-1} only leaves the call as k_last (previous-key pairing): its
+      // gradient is dk_last, written above, whatever the chain
+      if (!(ks == 1 && e / DK == L - 1)) ok[qk_base + e] = nan;
     }
     if (okp)
       for (int e = tid; e < DK; e += BNT) okp[chain * DK + e] = nan;
