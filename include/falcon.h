@@ -31,7 +31,8 @@
  *            [batch, heads, L, dv] (FALCON_BETA_CHANNEL, Falcon-2/2A only)
  *
  * Ownership: every pointer is device memory owned by the caller.  The library
- * allocates nothing, keeps no mutable global state and is reentrant.  Work is
+ * allocates nothing, keeps no mutable global state and is reentrant (except
+ * falcon_bwd_chunk_noalloc, which uses a device array of its own).  Work is
  * enqueued on `stream` (a hipStream_t passed as void*, NULL = the default
  * stream) and is asynchronous; buffers must stay alive until it completes.
  *
@@ -287,6 +288,29 @@ int falcon_bwd_chunk(int variant, int window, int flags, float beta, const void*
                      const float* dk_last, float* dq, float* dk_out, float* dv_out,
                      float* dbeta_t, float* dk_prev, float* dS0, void* workspace,
                      unsigned long long workspace_bytes, void* stream);
+
+/*
+ * falcon_bwd_chunk_noalloc - falcon_bwd_chunk without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * device array of FALCON_BWD_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends; the call allocates nothing.  Arguments,
+ * results and errors as falcon_bwd_chunk; in addition
+ *   FALCON_ERR_UNSUPPORTED  falcon_bwd_workspace_bytes(...) of the call exceeds
+ *                           FALCON_BWD_SCRATCH_BYTES (use falcon_bwd_chunk)
+ *   FALCON_ERR_HIP          the array's device address could not be obtained
+ * Every call on one GPU uses that GPU's array: calls that overlap in time on
+ * one GPU (different streams or host threads) race and give wrong gradients;
+ * calls in order on one stream are safe.
+ */
+#define FALCON_BWD_SCRATCH_BYTES (64ull << 20)
+int falcon_bwd_chunk_noalloc(int variant, int window, int flags, float beta, const void* beta_t,
+                             int beta_kind, float lambda, float eps, int batch, int heads,
+                             int seqlen, int dk, int dv, int dtype, const void* q, const void* k,
+                             const void* v, const void* k_prev, const float* S0, const float* dO,
+                             const float* dS_L, const float* dk_last, float* dq, float* dk_out,
+                             float* dv_out, float* dbeta_t, float* dk_prev, float* dS0,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -276,3 +276,39 @@ def test_backward_workspace_size(lib):
 ])
 def test_backward_validation(lib, over, status):
     assert _bwd(lib, **over) == status
+
+
+def _bwd_noalloc(lib, **over):
+    a = dict(variant=0, window=1, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, batch=1,
+             heads=2, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2], k_prev=None,
+             S0=None, dO=P[3], dS_L=None, dk_last=None, dq=P[4], dk_=P[5], dv_=P[6],
+             dbeta_t=None, dk_prev=None, dS0=None)
+    a.update(over)
+    return lib.falcon_bwd_chunk_noalloc(a["variant"], a["window"], a["flags"], a["beta"], a["beta_t"],
+                                        a["beta_kind"], a["lam"], a["eps"], a["batch"], a["heads"],
+                                        a["seqlen"], a["dk"], a["dv"], a["dtype"], a["q"], a["k"],
+                                        a["v"], a["k_prev"], a["S0"], a["dO"], a["dS_L"], a["dk_last"],
+                                        a["dq"], a["dk_"], a["dv_"], a["dbeta_t"], a["dk_prev"],
+                                        a["dS0"], None)
+
+
+def test_backward_noalloc_scratch_limit():
+    text = open(HEADER).read()
+    m = re.search(r"#define FALCON_BWD_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 64 << 20
+
+
+@pytest.mark.parametrize("over,status", [
+    # the headline backward needs about 276 MB of workspace: beyond the library's array
+    (dict(batch=8, heads=12, seqlen=2048), UNSUPPORTED),
+    (dict(variant=2, window=9), UNSUPPORTED),
+    (dict(variant=0, window=2), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(dq=P[0]), INVALID),                        # output aliases q
+    (dict(dS0=P[8]), INVALID),                       # no S0
+    (dict(flags=2), INVALID),
+])
+def test_backward_noalloc_validation(lib, over, status):
+    """The allocation-free backward checks every argument, and its workspace need
+    against the array it uses, before any HIP call."""
+    assert _bwd_noalloc(lib, **over) == status

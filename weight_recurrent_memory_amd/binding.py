@@ -68,6 +68,9 @@ def load_library():
     lib.falcon_bwd_chunk.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_ulonglong,
                                      vp]
+    lib.falcon_bwd_chunk_noalloc.restype = i
+    lib.falcon_bwd_chunk_noalloc.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, i, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     _LIB = lib
     return lib
 
@@ -245,7 +248,8 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
 
 
 def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
-              k_prev=None, S0=None, dS_L=None, dk_last=None, same_step=False, stream=None):
+              k_prev=None, S0=None, dS_L=None, dk_last=None, same_step=False, stream=None,
+              _noalloc=False):
     """Gradients of sum <dO, o> + <dS_L, S_L> + <dk_last, k_last> for the chunk form
     (window 1 to 8).  Returns a dict of float32 tensors: dq, dk, dv, and dbeta_t /
     dk_prev / dS0 when beta_t / k_prev / S0 are given."""
@@ -278,6 +282,16 @@ def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, be
         out["dk_prev"] = torch.empty((B, H, dk), device=dev, dtype=f32)
     if S0 is not None:
         out["dS0"] = torch.empty((B, H, dv, dk), device=dev, dtype=f32)
+    if _noalloc:
+        status = lib.falcon_bwd_chunk_noalloc(
+            variant, int(window), SAME_STEP if same_step else 0,
+            float(beta if beta is not None else 0.0), _ptr(beta_t), kind, float(lam), float(eps),
+            B, H, L, dk, dv, dcode, _ptr(q), _ptr(k), _ptr(v), _ptr(k_prev), _ptr(S0), _ptr(dO),
+            _ptr(dS_L), _ptr(dk_last), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+            _ptr(out.get("dbeta_t")), _ptr(out.get("dk_prev")), _ptr(out.get("dS0")),
+            _stream(torch, dev, stream))
+        _raise(lib, "falcon_bwd_chunk_noalloc", status)
+        return out
     wsb = int(lib.falcon_bwd_workspace_bytes(B, H, L, dk, dv, int(window)))
     ws = torch.empty((max(wsb, 16) // 4 + 4,), device=dev, dtype=f32)
     status = lib.falcon_bwd_chunk(
@@ -288,3 +302,11 @@ def bwd_chunk(q, k, v, dO, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, be
         _ptr(out.get("dS0")), _ptr(ws), wsb, _stream(torch, dev, stream))
     _raise(lib, "falcon_bwd_chunk", status)
     return out
+
+
+def bwd_chunk_noalloc(q, k, v, dO, **kw):
+    """bwd_chunk through falcon_bwd_chunk_noalloc: the library's per-GPU workspace
+    array instead of one allocated per call (the outputs are still allocated here;
+    a caller that cannot allocate calls the C entry point with its own buffers).
+    Calls that overlap in time on one GPU race."""
+    return bwd_chunk(q, k, v, dO, _noalloc=True, **kw)

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "falcon.h"
 #include "falcon_launch.h"
 
@@ -408,5 +410,58 @@ FALCON_EXPORT int falcon_bwd_chunk(int variant, int window, int flags, float bet
   for (const Range& r : others)
     if (overlap(ws, r)) return FALCON_ERR_INVALID_ARG;
   b.workspace = static_cast<float*>(workspace);
+  return finish_launch(falcon::launch_backward(b, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Backward without a caller workspace: the workspace is a file-scope device
+// array of FALCON_BWD_SCRATCH_BYTES.  In host code `scratch` names a host-side
+// stand-in, not device memory; its device address is looked up once per device
+// (with that device current) and only that address is passed to kernels.
+
+namespace {
+
+__device__ __align__(256) float scratch[FALCON_BWD_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once known
+
+// Device address of this device's `scratch`, or nullptr if it cannot be found.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+FALCON_EXPORT int falcon_bwd_chunk_noalloc(int variant, int window, int flags, float beta,
+                                           const void* beta_t, int beta_kind, float lambda,
+                                           float eps, int batch, int heads, int seqlen, int dk,
+                                           int dv, int dtype, const void* q, const void* k,
+                                           const void* v, const void* k_prev, const float* S0,
+                                           const float* dO, const float* dS_L,
+                                           const float* dk_last, float* dq, float* dk_out,
+                                           float* dv_out, float* dbeta_t, float* dk_prev,
+                                           float* dS0, void* stream) {
+  falcon::BwdArgs b;
+  size_t need = 0;
+  int st = check_bwd(variant, window, flags, beta, beta_t, beta_kind, lambda, eps, batch, heads,
+                     seqlen, dk, dv, dtype, q, k, v, k_prev, S0, dO, dS_L, dk_last, dq, dk_out,
+                     dv_out, dbeta_t, dk_prev, dS0, &b, &need);
+  if (st != FALCON_OK) return st;
+  if (need > FALCON_BWD_SCRATCH_BYTES) return FALCON_ERR_UNSUPPORTED;
+  void* ws = scratch_on_current_device();
+  if (!ws) return FALCON_ERR_HIP;
+  // every workspace element the kernels read is written earlier in the same
+  // call, so nothing is cleared
+  b.workspace = static_cast<float*>(ws);
   return finish_launch(falcon::launch_backward(b, (hipStream_t)stream));
 }
