@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "chunk_traffic.json")
 CHUNK_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
-                 for f in ("falcon_chunk_wy.hip", "falcon_mma.h", "falcon_device.h")]
+                 for f in ("falcon_chunk_wy.hip", "falcon_exact.h", "falcon_mma.h", "falcon_device.h")]
 PROFILE_MFMA = os.path.join(ROOT, "profiles", "window_mfma_counters.json")
 WINDOW_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
-                  for f in ("falcon_chunk_wyb.hip", "falcon_mma.h", "falcon_device.h")]
+                  for f in ("falcon_chunk_wyb.hip", "falcon_exact.h", "falcon_mma.h", "falcon_device.h")]
 HEADLINE_KERNEL = "chunk_wy_kernel<64,true>"
 HEADLINE_KERNEL_CHUNK = 32
 WINDOW_KERNEL = "chunk_wyb_kernel<128,true,4>"
