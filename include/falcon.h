@@ -270,8 +270,12 @@ int falcon_decode_step_ex(int variant, int window, int flags, float beta, const 
  *   workspace, workspace_bytes   device scratch of at least
  *             falcon_bwd_workspace_bytes(..., window) bytes, 16-byte aligned
  * Outputs must not overlap each other, the inputs or the workspace.
- * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 8 or a
- * windowed start state.
+ * Errors as elsewhere; FALCON_ERR_UNSUPPORTED for a window above 8, a
+ * windowed start state, or a chain whose inputs or workspace records reach
+ * 1 GiB: the kernel addresses a chain's buffers with 32-bit offsets.  The
+ * records dominate: 4 * (R * dk + 16 * R + 256) bytes per chunk of
+ * floor(16 / window) steps, so the limit is about 880 K steps at
+ * dk = dv = 128, window 1, and about 110 K steps at window 8.
  * Range: the chunks of floor(16 / window) steps are scaled by their decay
  * products g_t = prod (1 - eta_r lambda); for a (batch, head) chain in which
  * some |g_t| leaves [2^-100, 2^100] or some |1 - eta_t lambda| is below 2^-24

@@ -278,6 +278,26 @@ def test_backward_validation(lib, over, status):
     assert _bwd(lib, **over) == status
 
 
+# fake device addresses 4 GiB apart, for calls whose buffers are larger than P's spacing
+BIG = [0x1000000000 + 0x100000000 * i for i in range(12)]
+
+
+@pytest.mark.parametrize("seqlen,window,variant,status", [
+    # dk = dv = 128: a chain's chunk records take 4 (32 * 128 + 16 * 32 + 256) bytes per
+    # chunk of floor(16 / window) steps; at 1 GiB and above the call is refused
+    (900_000, 1, 0, UNSUPPORTED),
+    (860_000, 1, 0, INVALID),          # below the limit: fails later, on the small workspace
+    (111_000, 8, 2, UNSUPPORTED),
+    (109_000, 8, 2, INVALID),
+])
+def test_backward_chain_limit(lib, seqlen, window, variant, status):
+    """The backward kernel addresses a chain's inputs and records with 32-bit
+    offsets; a chain that needs 1 GiB or more of them is refused up front."""
+    assert _bwd(lib, batch=1, heads=1, seqlen=seqlen, dk=128, dv=128, window=window,
+                variant=variant, q=BIG[0], k=BIG[1], v=BIG[2], dO=BIG[3], dq=BIG[4],
+                dk_=BIG[5], dv_=BIG[6], ws=BIG[7], wsb=1 << 26) == status
+
+
 def _bwd_noalloc(lib, **over):
     a = dict(variant=0, window=1, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6, batch=1,
              heads=2, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2], k_prev=None,

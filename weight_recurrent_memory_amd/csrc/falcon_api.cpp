@@ -342,6 +342,9 @@ int check_bwd(int variant, int window, int flags, float beta, const void* beta_t
   // which this entry point does not take
   if (!bwd_window(window)) return FALCON_ERR_UNSUPPORTED;
   if (window > 1 && S0) return FALCON_ERR_UNSUPPORTED;
+  // a chain's inputs and workspace record are addressed with 32-bit offsets
+  if (falcon::backward_chain_bytes(seqlen, dk, dv, window, dtype) >= (1ull << 30))
+    return FALCON_ERR_UNSUPPORTED;
   const size_t es = dtype == FALCON_BF16 ? 2 : 4;
   const size_t BH = (size_t)batch * heads, L = (size_t)seqlen;
   Range outs[] = {{dq, BH * L * dk * 4},

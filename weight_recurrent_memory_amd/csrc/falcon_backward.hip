@@ -1046,6 +1046,17 @@ size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int d
   return (size_t)(records + partials) * sizeof(float);
 }
 
+size_t backward_chain_bytes(long seqlen, int dk, int dv, int window, int dtype) {
+  // the kernel reads a chain's q, k, v, gains, dO and workspace record through
+  // 32-bit buffer ranges; the largest of them
+  const long es = dtype == 0 ? 2 : 4;
+  const long ns = BC / window, nch = (seqlen + ns - 1) / ns, RB = bwd_rows(dk, dv);
+  long m = seqlen * dk * es;
+  m = m > seqlen * dv * 4 ? m : seqlen * dv * 4;
+  const long rec = nch * (RB * dk + (long)BC * RB + (long)BC * BC) * 4;
+  return (size_t)(m > rec ? m : rec);
+}
+
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   if (a.dtype == 0) return launch_bwd_dk<uint16_t>(a, stream);

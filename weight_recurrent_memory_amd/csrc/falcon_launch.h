@@ -84,6 +84,9 @@ struct BwdArgs {
   float* workspace;      // backward_workspace_bytes(...)
 };
 size_t backward_workspace_bytes(int batch, int heads, long seqlen, int dk, int dv, int window);
+// Largest per-chain buffer range the backward kernel addresses (bytes); the
+// kernel needs it below 2^30.
+size_t backward_chain_bytes(long seqlen, int dk, int dv, int window, int dtype);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
