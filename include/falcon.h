@@ -215,6 +215,29 @@ int falcon_fwd_chunk_ex(int variant, int window, int flags, float beta, const vo
                         void* x_hist_out, void* y_hist_out, int chunk, void* stream);
 
 /*
+ * falcon_fwd_masked - the masked-parallel form (explainer of arXiv 2608.27763,
+ * section 核心方法 §3: the recurrence unrolled under a causal mask into one
+ * parallel system, the form for short sequences): the whole call is one masked
+ * system.  The samples' Gram matrix X X^T and the key-query products X Q^T are
+ * formed for the whole sequence at once; the causally masked, decay-weighted
+ * unit-lower-triangular system over every (step, window sample) unknown is then
+ * solved by forward substitution in those coordinates, so no dk-sized state is
+ * carried from step to step and no decay product is divided by (any decay,
+ * however strong, is exact).
+ * Arguments, results and errors as falcon_fwd_recurrent_ex (every variant,
+ * window 1..8, bf16 or fp32 inputs, carried key, state and window history,
+ * FALCON_SAME_STEP); in addition FALCON_ERR_UNSUPPORTED for
+ * seqlen > FALCON_MASKED_MAX_LEN.
+ */
+#define FALCON_MASKED_MAX_LEN 64
+int falcon_fwd_masked(int variant, int window, int flags, float beta, const void* beta_t,
+                      int beta_kind, float lambda, float eps, int batch, int heads, int seqlen,
+                      int dk, int dv, int dtype, const void* q, const void* k, const void* v,
+                      const void* k_prev, const float* S0, const void* x_hist,
+                      const void* y_hist, float* o, float* S_out, void* x_hist_out,
+                      void* y_hist_out, void* stream);
+
+/*
  * falcon_decode_step_ex - falcon_decode_step for every variant, with the
  * window history of Falcon-3/3A and the pairing flag:
  *   window    B in 1..8; > 1 only for FALCON_3 / FALCON_3A

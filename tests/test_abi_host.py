@@ -125,6 +125,44 @@ def test_chunk_only_validation(lib, over, status):
     assert _seq(lib, "falcon_fwd_chunk", **over) == status
 
 
+def _masked(lib, **over):
+    a = dict(variant=0, window=1, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6,
+             batch=1, heads=1, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2],
+             k_prev=None, S0=None, x_hist=None, y_hist=None, o=P[3], S_out=None, xo=None, yo=None)
+    a.update(over)
+    return lib.falcon_fwd_masked(a["variant"], a["window"], a["flags"], a["beta"], a["beta_t"],
+                                 a["beta_kind"], a["lam"], a["eps"], a["batch"], a["heads"],
+                                 a["seqlen"], a["dk"], a["dv"], a["dtype"], a["q"], a["k"], a["v"],
+                                 a["k_prev"], a["S0"], a["x_hist"], a["y_hist"], a["o"],
+                                 a["S_out"], a["xo"], a["yo"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(seqlen=65), UNSUPPORTED),                  # one masked system covers at most 64 steps
+    (dict(seqlen=4096), UNSUPPORTED),
+    (dict(variant=2, window=9), UNSUPPORTED),
+    (dict(variant=0, window=2), INVALID),
+    (dict(flags=2), INVALID),
+    (dict(flags=1, k_prev=P[7]), INVALID),           # same-step pairing takes no carried key
+    (dict(S0=P[6]), INVALID),                        # state without the carried key
+    (dict(variant=2, window=3, x_hist=P[8]), INVALID),   # one history pointer without the other
+    (dict(variant=2, window=3, k_prev=P[7], S0=P[6]), INVALID),  # windowed state, no history
+    (dict(dk=48), UNSUPPORTED),
+    (dict(o=P[0]), INVALID),
+    (dict(seqlen=0), INVALID),
+])
+def test_masked_validation(lib, over, status):
+    """The masked-parallel entry point validates like the recurrent one and refuses
+    sequences longer than one masked system, before any HIP call."""
+    assert _masked(lib, **over) == status
+
+
+def test_masked_max_len():
+    text = open(HEADER).read()
+    m = re.search(r"#define FALCON_MASKED_MAX_LEN (\d+)", text)
+    assert m and int(m.group(1)) == 64
+
+
 def test_recurrent_window_limit(lib):
     assert _seq(lib, "falcon_fwd_recurrent", variant=2, window=9) == UNSUPPORTED
 

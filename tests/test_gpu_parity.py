@@ -627,15 +627,14 @@ def test_backward_8x12x2048x64():
 
 
 # ---------------------------------------------------------------------------
-# short sequences against the masked-parallel evaluation (explainer §3)
+# short sequences: chunk form against the masked-parallel evaluation (explainer §3)
 
 @pytest.mark.parametrize("variant", ALL)
 @pytest.mark.parametrize("same_step", [False, True])
-def test_short_sequence_matches_masked_parallel(variant, same_step):
-    """For L <= 64 the chunk form is the masked-parallel system itself (causally
-    masked Gram and q.x over the whole sequence, one triangular solve); checked
-    against the oracle's transition-product expansion, which never forms a
-    residual."""
+def test_short_sequence_chunk_matches_masked_parallel(variant, same_step):
+    """The chunk form on a short sequence against the oracle's masked-parallel
+    evaluation (transition products, no residuals).  The masked-parallel form's
+    own kernel (falcon_fwd_masked) has its tests in test_gpu_masked.py."""
     per_ch = variant in (fw.FALCON_2, fw.FALCON_2A)
     win = _win(variant, 2)
     L, dk, dv = 24, 16, 16

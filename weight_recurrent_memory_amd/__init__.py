@@ -7,5 +7,5 @@ load the library; the first call does, and fails loudly if it is missing.
 from .binding import (  # noqa: F401
     FALCON_1, FALCON_2, FALCON_3, FALCON_1A, FALCON_2A, FALCON_3A,
     VARIANT_NAMES, FalconError, bwd_chunk, bwd_chunk_noalloc, decode_step, fwd_chunk,
-    fwd_recurrent, library_path, load_library,
+    fwd_masked, fwd_recurrent, library_path, load_library,
 )

@@ -59,6 +59,8 @@ def load_library():
     lib.falcon_fwd_recurrent_ex.argtypes = ex_args + [vp]
     lib.falcon_fwd_chunk_ex.restype = i
     lib.falcon_fwd_chunk_ex.argtypes = ex_args + [i, vp]
+    lib.falcon_fwd_masked.restype = i
+    lib.falcon_fwd_masked.argtypes = ex_args + [vp]
     lib.falcon_decode_step_ex.restype = i
     lib.falcon_decode_step_ex.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp]
@@ -149,7 +151,8 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
     if S_out is None and return_state:
         S_out = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
     _check(torch, "S_out", S_out, (B, H, dv, dk), torch.float32, dev)
-    ext = (x_hist is not None or y_hist is not None or return_history
+    masked = fn_name == "falcon_fwd_masked"     # one signature, the _ex form
+    ext = (masked or x_hist is not None or y_hist is not None or return_history
            or x_hist_out is not None or y_hist_out is not None or same_step)
     nh = int(window) - 1
     _check(torch, "x_hist", x_hist, (B, H, nh, dk), dt, dev)
@@ -165,7 +168,8 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
             float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k), _ptr(v),
             _ptr(k_prev), _ptr(S0)]
     if ext:
-        fn_name += "_ex"
+        if not masked:
+            fn_name += "_ex"
         args = [variant, int(window), SAME_STEP if same_step else 0] + args
         args += [_ptr(x_hist), _ptr(y_hist), _ptr(out), _ptr(S_out), _ptr(x_hist_out),
                  _ptr(y_hist_out)]
@@ -202,6 +206,17 @@ def fwd_chunk(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, chunk=64, window
     """Chunk-parallel form; results, history and pairing arguments as fwd_recurrent."""
     return _seq_call("falcon_fwd_chunk", q, k, v, variant, beta, lam, eps, window, beta_t,
                      k_prev, S0, out, S_out, return_state, chunk, stream, x_hist, y_hist,
+                     return_history, x_hist_out, y_hist_out, same_step)
+
+
+def fwd_masked(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,
+               k_prev=None, S0=None, out=None, S_out=None, return_state=False, stream=None,
+               x_hist=None, y_hist=None, return_history=False, x_hist_out=None,
+               y_hist_out=None, same_step=False):
+    """Masked-parallel form, the whole call one masked system (L <= 64); results,
+    history and pairing arguments as fwd_recurrent."""
+    return _seq_call("falcon_fwd_masked", q, k, v, variant, beta, lam, eps, window, beta_t,
+                     k_prev, S0, out, S_out, return_state, None, stream, x_hist, y_hist,
                      return_history, x_hist_out, y_hist_out, same_step)
 
 

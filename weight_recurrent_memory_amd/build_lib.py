@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["falcon_api.cpp", "falcon_recurrent.hip", "falcon_decode.hip", "falcon_chunk.hip",
            "falcon_chunk_w1.hip", "falcon_chunk_wy.hip", "falcon_chunk_wyb.hip",
-           "falcon_chunk_ip.hip", "falcon_backward.hip"]
+           "falcon_chunk_ip.hip", "falcon_backward.hip", "falcon_masked.hip"]
 ARCH = os.environ.get("FALCON_OFFLOAD_ARCH", "gfx950")
 
 

@@ -165,6 +165,16 @@ int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipSt
   return launch_with_history(true, a, xo, yo, stream);
 }
 
+int fwd_masked(const falcon::SeqArgs& a, void* xo, void* yo, hipStream_t stream) {
+  int st = check_seq(a, true);
+  if (st == FALCON_OK) st = check_history(a, xo, yo);
+  if (st != FALCON_OK) return st;
+  if (a.seqlen > falcon::kMaskedMaxLen || a.window > 8) return FALCON_ERR_UNSUPPORTED;
+  hipError_t e = falcon::launch_masked(a, stream);
+  if (e == hipSuccess && xo) e = falcon::launch_history_out(a, xo, yo, stream);
+  return finish_launch(e);
+}
+
 }  // namespace
 
 FALCON_EXPORT int falcon_abi_version(void) { return FALCON_ABI_VERSION; }
@@ -231,6 +241,20 @@ FALCON_EXPORT int falcon_fwd_chunk_ex(int variant, int window, int flags, float 
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
                     chunk, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
   return fwd_chunk(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
+}
+
+FALCON_EXPORT int falcon_fwd_masked(int variant, int window, int flags, float beta,
+                                    const void* beta_t, int beta_kind, float lambda, float eps,
+                                    int batch, int heads, int seqlen, int dk, int dv, int dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const void* k_prev, const float* S0, const void* x_hist,
+                                    const void* y_hist, float* o, float* S_out, void* x_hist_out,
+                                    void* y_hist_out, void* stream) {
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
+  falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
+                    eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
+                    0, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
+  return fwd_masked(a, x_hist_out, y_hist_out, (hipStream_t)stream);
 }
 
 namespace {

@@ -90,6 +90,10 @@ size_t backward_chain_bytes(long seqlen, int dk, int dv, int window, int dtype);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
+// masked-parallel form, the whole call one masked system (falcon_masked.hip):
+// seqlen 1..kMaskedMaxLen, window 1..8
+constexpr int kMaskedMaxLen = 64;
+hipError_t launch_masked(const SeqArgs& a, hipStream_t stream);
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
 // window-1 chunk form, per-channel gains (falcon_chunk_w1.hip); cs = sub-chunk length
 hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs);
