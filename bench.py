@@ -131,7 +131,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None, help="profiling aid: run only this leg "
-                    "(headline|falcon1a|percol|window|backward|decode|copy)")
+                    "(headline|falcon1a|percol|window|masked|backward|decode|copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Falcon state update has no cross-GPU "
@@ -283,6 +283,28 @@ def main():
                     "issued_tflops": counters.get("issued_tflops") if counters else None,
                     "counters_source": counters.get("source") if counters else None}
             del r
+            torch.cuda.empty_cache()
+        if args.only in (None, "masked"):
+            # short sequences: the masked-parallel form (one masked system per call of
+            # 64 steps) and the chunk form on the same inputs
+            cfg = WORKLOADS["masked_256x12x64x64"]
+            B, H, L, dk, dv = cfg["shape"]
+            inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16")
+            q, k, v = (up(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+            o = torch.empty((B, H, L, dv), device=dev, dtype=torch.float32)
+            kw = dict(variant=fw.FALCON_1, beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"], out=o)
+            st, stc = {}, {}
+            sec = time_calls(lambda: fw.fwd_masked(q, k, v, **kw), 20, 3, stats=st)
+            sec_c = time_calls(lambda: fw.fwd_chunk(q, k, v, chunk=64, **kw), 20, 3, stats=stc)
+            nbytes = algorithmic_bytes(B, H, L, dk, dv)
+            sec_out["masked"] = {"workload": "masked_256x12x64x64", "variant": "falcon1",
+                                 "kernel": "masked_kernel<64,1,true>",
+                                 "ms_per_call": sec * 1e3, "median_ms": st["median_s"] * 1e3,
+                                 "tokens_per_s": B * L / sec,
+                                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                                 "chunk_form_ms_per_call": sec_c * 1e3,
+                                 "chunk_form_median_ms": stc["median_s"] * 1e3}
+            del q, k, v, o
             torch.cuda.empty_cache()
         if args.only in (None, "backward"):
             # gradients of the headline workload: q, k, v bf16 and dO fp32 read, dq, dk,

@@ -25,6 +25,8 @@ WORKLOADS = {
     "chunk_window4_4x16x8192x128": dict(kind="seq", shape=(4, 16, 8192, 128, 128),
                                         dtype="bf16", seed=1004, beta=0.5, lam=0.01,
                                         eps=1e-6, chunk=64, window=4),
+    "masked_256x12x64x64": dict(kind="seq", shape=(256, 12, 64, 64, 64), dtype="bf16",
+                                seed=1006, beta=0.5, lam=0.01, eps=1e-6, chunk=64),
     "decode_512x12x64": dict(kind="decode", shape=(512, 12, 64, 64), dtype="bf16",
                              seed=1005, beta=0.5, lam=0.01, eps=1e-6, s_std=0.02),
 }
