@@ -326,7 +326,9 @@ FALCON_EXPORT int falcon_decode_step_ex(int variant, int window, int flags, floa
                      dk, dv, dtype, S, k_prev, x_hist, y_hist, q, k, v, o, true, stream);
 }
 
+namespace {
 bool bwd_window(int window) { return window >= 1 && window <= 8; }
+}  // namespace
 
 FALCON_EXPORT unsigned long long falcon_bwd_workspace_bytes(int batch, int heads, int seqlen, int dk,
                                                             int dv, int window) {
