@@ -45,7 +45,7 @@ WINDOW_SOURCES = [os.path.join(ROOT, "weight_recurrent_memory_amd", "csrc", f)
                   for f in ("falcon_chunk_wyb.hip", "falcon_exact.h", "falcon_mma.h", "falcon_device.h")]
 HEADLINE_KERNEL = "chunk_wy_kernel<64,true>"
 HEADLINE_KERNEL_CHUNK = 32
-WINDOW_KERNEL = "chunk_wyb_kernel<128,true,4>"
+WINDOW_KERNEL = "chunk_wyb_kernel<128,true,4,true> + wyb_state_kernel<128,4>"
 
 
 def algorithmic_bytes(batch, heads, L, dk, dv, beta_channel=False, elem=2):

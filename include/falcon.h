@@ -215,6 +215,34 @@ int falcon_fwd_chunk_ex(int variant, int window, int flags, float beta, const vo
                         void* x_hist_out, void* y_hist_out, int chunk, void* stream);
 
 /*
+ * falcon_fwd_workspace_bytes - bytes of device workspace with which
+ * falcon_fwd_chunk_ws runs the two-kernel form of the call; 0 where that form
+ * does not apply (it applies to the regression family with a window of 2 or 4,
+ * gains shared by the value rows, dk in {64, 128}, bf16 inputs).  Per
+ * (batch, head) and 16-step sub-chunk one record of 12416 bytes: the
+ * sub-chunk's folds of the chunk equations (the state-independent part of
+ * every step), its decay products and a range flag.
+ *
+ * falcon_fwd_chunk_ws - falcon_fwd_chunk_ex with a caller workspace (device
+ * memory, 16-byte aligned, overlapping no other argument; NULL: none).  With
+ * workspace_bytes >= falcon_fwd_workspace_bytes(...) a first kernel prepares
+ * every sub-chunk of every chain in parallel into the workspace and a second
+ * runs only the sequential state part; otherwise the call runs exactly as
+ * falcon_fwd_chunk_ex.  Results as falcon_fwd_chunk_ex (rounding aside);
+ * errors as falcon_fwd_chunk_ex, and FALCON_ERR_INVALID_ARG for a misaligned
+ * or overlapping workspace.
+ */
+unsigned long long falcon_fwd_workspace_bytes(int variant, int window, int beta_kind, int batch,
+                                              int heads, int seqlen, int dk, int dv, int dtype);
+int falcon_fwd_chunk_ws(int variant, int window, int flags, float beta, const void* beta_t,
+                        int beta_kind, float lambda, float eps, int batch, int heads, int seqlen,
+                        int dk, int dv, int dtype, const void* q, const void* k, const void* v,
+                        const void* k_prev, const float* S0, const void* x_hist,
+                        const void* y_hist, float* o, float* S_out, void* x_hist_out,
+                        void* y_hist_out, void* workspace, unsigned long long workspace_bytes,
+                        int chunk, void* stream);
+
+/*
  * falcon_fwd_masked - the masked-parallel form (explainer of arXiv 2608.27763,
  * section 核心方法 §3: the recurrence unrolled under a causal mask into one
  * parallel system, the form for short sequences): the whole call is one masked

@@ -163,6 +163,51 @@ def test_masked_max_len():
     assert m and int(m.group(1)) == 64
 
 
+def test_fwd_workspace_bytes(lib):
+    # one 12416-byte record per (batch, head) and 16-step sub-chunk, for the
+    # regression family with a window of 2 or 4, shared gains, dk 64 / 128, bf16
+    def rec(B, H, L):
+        return B * H * ((L + 15) // 16) * 12416
+    assert lib.falcon_fwd_workspace_bytes(2, 4, 0, 4, 16, 8192, 128, 128, 0) == rec(4, 16, 8192)
+    assert lib.falcon_fwd_workspace_bytes(2, 2, 1, 1, 3, 77, 64, 32, 0) == rec(1, 3, 77)
+    assert lib.falcon_fwd_workspace_bytes(5, 4, 0, 4, 16, 8192, 128, 128, 0) == 0   # Falcon-3A
+    assert lib.falcon_fwd_workspace_bytes(0, 1, 0, 8, 12, 2048, 64, 64, 0) == 0     # window 1
+    assert lib.falcon_fwd_workspace_bytes(2, 3, 0, 1, 1, 64, 64, 64, 0) == 0        # window 3
+    assert lib.falcon_fwd_workspace_bytes(2, 4, 0, 1, 1, 64, 32, 64, 0) == 0        # dk 32
+    assert lib.falcon_fwd_workspace_bytes(2, 4, 0, 1, 1, 64, 64, 64, 1) == 0        # fp32 inputs
+    assert lib.falcon_fwd_workspace_bytes(0, 4, 0, 1, 1, 64, 64, 64, 0) == 0        # window on Falcon-1
+    assert lib.falcon_fwd_workspace_bytes(2, 4, 0, 0, 1, 64, 64, 64, 0) == 0
+
+
+def _ws(lib, **over):
+    a = dict(variant=2, window=4, flags=0, beta=0.5, beta_t=None, beta_kind=0, lam=0.01, eps=1e-6,
+             batch=1, heads=1, seqlen=64, dk=64, dv=64, dtype=0, q=P[0], k=P[1], v=P[2],
+             k_prev=None, S0=None, x_hist=None, y_hist=None, o=P[3], S_out=None, xo=None,
+             yo=None, ws=P[8], wsb=1 << 20, chunk=64)
+    a.update(over)
+    return lib.falcon_fwd_chunk_ws(a["variant"], a["window"], a["flags"], a["beta"], a["beta_t"],
+                                   a["beta_kind"], a["lam"], a["eps"], a["batch"], a["heads"],
+                                   a["seqlen"], a["dk"], a["dv"], a["dtype"], a["q"], a["k"],
+                                   a["v"], a["k_prev"], a["S0"], a["x_hist"], a["y_hist"], a["o"],
+                                   a["S_out"], a["xo"], a["yo"], a["ws"], a["wsb"], a["chunk"],
+                                   None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ws=P[8] + 8), INVALID),                    # misaligned workspace
+    (dict(ws=P[0]), INVALID),                        # workspace overlaps q
+    (dict(ws=P[3] + 4096), INVALID),                 # workspace inside o
+    (dict(flags=2), INVALID),
+    (dict(chunk=48), UNSUPPORTED),
+    (dict(variant=0), INVALID),                      # window 4 on Falcon-1
+    (dict(q=None), INVALID),
+])
+def test_fwd_chunk_ws_validation(lib, over, status):
+    """falcon_fwd_chunk_ws validates like falcon_fwd_chunk_ex, and its workspace's
+    alignment and overlap, before any HIP call."""
+    assert _ws(lib, **over) == status
+
+
 def test_recurrent_window_limit(lib):
     assert _seq(lib, "falcon_fwd_recurrent", variant=2, window=9) == UNSUPPORTED
 

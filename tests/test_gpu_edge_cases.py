@@ -43,8 +43,10 @@ FAMILIES = [
     ("w1_percol_c16", fw.FALCON_2, 64, 32, 1, "channel", 16),
     ("w1_dk128", fw.FALCON_1, 128, 32, 1, "scalar", 64),
     ("w1_dk16", fw.FALCON_1, 16, 32, 1, "token", 64),
-    ("wyb_w4", fw.FALCON_3, 128, 32, 4, "scalar", 64),
+    ("wyb_w4", fw.FALCON_3, 128, 32, 4, "scalar", 64),        # two kernels (pre-pass + state)
     ("wyb_w2", fw.FALCON_3, 64, 64, 2, "token", 64),
+    ("wyb_w4_fused", fw.FALCON_3, 128, 32, 4, "token", 64),   # one kernel (no workspace)
+    ("wyb_w2_fused", fw.FALCON_3, 64, 64, 2, "scalar", 64),
     ("ip_w4", fw.FALCON_3A, 128, 64, 4, "scalar", 64),
     ("ip_1a_dk128", fw.FALCON_1A, 128, 32, 1, "token", 64),
     ("ip_w8", fw.FALCON_3A, 64, 32, 8, "token", 64),
@@ -68,8 +70,9 @@ def _chunk_vs_oracle(label, variant, dk, dv, window, gains, chunk, inp, *, beta,
     S0 = to_dev(torch, inp["S0"], torch.float32) if carried and "S0" in inp else None
     b = beta if gains == "scalar" else None
     print("%s: launching" % label, flush=True)
+    ws = None if label.endswith("_fused") else "auto"
     o, S = fw.fwd_chunk(q, k, v, variant=variant, beta=b, lam=lam, eps=eps, window=window,
-                        chunk=chunk, beta_t=bt, k_prev=kp, S0=S0, return_state=True)
+                        chunk=chunk, beta_t=bt, k_prev=kp, S0=S0, return_state=True, workspace=ws)
     torch.cuda.synchronize()
     o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], beta=b,
                                            lam=lam, eps=eps, window=window,

@@ -61,6 +61,10 @@ def load_library():
     lib.falcon_fwd_chunk_ex.argtypes = ex_args + [i, vp]
     lib.falcon_fwd_masked.restype = i
     lib.falcon_fwd_masked.argtypes = ex_args + [vp]
+    lib.falcon_fwd_workspace_bytes.restype = ctypes.c_ulonglong
+    lib.falcon_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.falcon_fwd_chunk_ws.restype = i
+    lib.falcon_fwd_chunk_ws.argtypes = ex_args + [vp, ctypes.c_ulonglong, i, vp]
     lib.falcon_decode_step_ex.restype = i
     lib.falcon_decode_step_ex.argtypes = [i, i, i, f, vp, i, f, f, i, i, i, i, i, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp]
@@ -81,6 +85,13 @@ def _variant(v):
     if isinstance(v, str):
         return VARIANT_NAMES[v.lower().replace("-", "")]
     return int(v)
+
+
+def kind_of(beta_t):
+    """Gain kind of a beta_t argument: scalar, per token ([B,H,L]) or per channel."""
+    if beta_t is None:
+        return _BETA_SCALAR
+    return _BETA_TOKEN if beta_t.dim() == 3 else _BETA_CHANNEL
 
 
 def _ptr(t):
@@ -121,7 +132,8 @@ def _raise(lib, fn, status):
 
 def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev, S0,
               out, S_out, return_state, chunk, stream, x_hist=None, y_hist=None,
-              return_history=False, x_hist_out=None, y_hist_out=None, same_step=False):
+              return_history=False, x_hist_out=None, y_hist_out=None, same_step=False,
+              workspace=None):
     import torch
     lib = load_library()
     variant = _variant(variant)
@@ -152,7 +164,21 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
         S_out = torch.empty((B, H, dv, dk), device=dev, dtype=torch.float32)
     _check(torch, "S_out", S_out, (B, H, dv, dk), torch.float32, dev)
     masked = fn_name == "falcon_fwd_masked"     # one signature, the _ex form
-    ext = (masked or x_hist is not None or y_hist is not None or return_history
+    ws_ptr, ws_bytes = None, 0
+    if fn_name == "falcon_fwd_chunk" and workspace is not None:
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace: None, 'auto' or a device tensor")
+            need = lib.falcon_fwd_workspace_bytes(variant, int(window), kind_of(beta_t), B, H, L,
+                                                  dk, dv, dcode)
+            workspace = (torch.empty(int(need), device=dev, dtype=torch.uint8) if need > 0
+                         else None)
+        if workspace is not None:
+            if workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    ws = ws_ptr is not None
+    ext = (masked or ws or x_hist is not None or y_hist is not None or return_history
            or x_hist_out is not None or y_hist_out is not None or same_step)
     nh = int(window) - 1
     _check(torch, "x_hist", x_hist, (B, H, nh, dk), dt, dev)
@@ -168,13 +194,17 @@ def _seq_call(fn_name, q, k, v, variant, beta, lam, eps, window, beta_t, k_prev,
             float(lam), float(eps), B, H, L, dk, dv, dcode, _ptr(q), _ptr(k), _ptr(v),
             _ptr(k_prev), _ptr(S0)]
     if ext:
-        if not masked:
+        if ws:
+            fn_name += "_ws"
+        elif not masked:
             fn_name += "_ex"
         args = [variant, int(window), SAME_STEP if same_step else 0] + args
         args += [_ptr(x_hist), _ptr(y_hist), _ptr(out), _ptr(S_out), _ptr(x_hist_out),
                  _ptr(y_hist_out)]
     else:
         args = [variant, int(window)] + args + [_ptr(out), _ptr(S_out)]
+    if ws:
+        args += [ws_ptr, ws_bytes]
     if fn_name.startswith("falcon_fwd_chunk"):
         args.append(int(chunk))
     args.append(_stream(torch, dev, stream))
@@ -202,11 +232,14 @@ def fwd_recurrent(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, be
 def fwd_chunk(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, chunk=64, window=1,
               beta_t=None, k_prev=None, S0=None, out=None, S_out=None, return_state=False,
               stream=None, x_hist=None, y_hist=None, return_history=False, x_hist_out=None,
-              y_hist_out=None, same_step=False):
-    """Chunk-parallel form; results, history and pairing arguments as fwd_recurrent."""
+              y_hist_out=None, same_step=False, workspace="auto"):
+    """Chunk-parallel form; results, history and pairing arguments as fwd_recurrent.
+    workspace: "auto" (default) allocates the device workspace of the two-kernel
+    form where the library has one for the call (falcon_fwd_workspace_bytes > 0),
+    a uint8 device tensor supplies it, None runs the single-kernel form."""
     return _seq_call("falcon_fwd_chunk", q, k, v, variant, beta, lam, eps, window, beta_t,
                      k_prev, S0, out, S_out, return_state, chunk, stream, x_hist, y_hist,
-                     return_history, x_hist_out, y_hist_out, same_step)
+                     return_history, x_hist_out, y_hist_out, same_step, workspace)
 
 
 def fwd_masked(q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, window=1, beta_t=None,

@@ -138,8 +138,8 @@ int finish_launch(hipError_t e) { return e == hipSuccess ? FALCON_OK : FALCON_ER
 
 // The history outputs are written after the main kernel, on the same stream.
 int launch_with_history(bool chunk_form, const falcon::SeqArgs& a, void* xo, void* yo,
-                        hipStream_t stream) {
-  hipError_t e = chunk_form ? falcon::launch_chunk(a, stream) : falcon::launch_recurrent(a, stream);
+                        hipStream_t stream, void* ws = nullptr, size_t ws_bytes = 0) {
+  hipError_t e = chunk_form ? falcon::launch_chunk(a, stream, ws, ws_bytes) : falcon::launch_recurrent(a, stream);
   if (e == hipSuccess && xo) e = falcon::launch_history_out(a, xo, yo, stream);
   return finish_launch(e);
 }
@@ -152,7 +152,31 @@ int fwd_recurrent(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, h
   return launch_with_history(false, a, xo, yo, stream);
 }
 
-int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipStream_t stream) {
+// The workspace of falcon_fwd_chunk_ws may overlap no other argument.
+bool ws_overlaps(const falcon::SeqArgs& a, const void* xo, const void* yo, const void* ws,
+                 size_t ws_bytes) {
+  const size_t es = a.dtype == FALCON_BF16 ? 2 : 4;
+  const size_t BH = (size_t)a.batch * a.heads, L = (size_t)a.seqlen, NH = (size_t)a.window - 1;
+  const Range w{ws, ws_bytes};
+  const Range others[] = {{a.q, BH * L * a.dk * es},
+                          {a.k, BH * L * a.dk * es},
+                          {a.v, BH * L * a.dv * es},
+                          {a.k_prev, BH * a.dk * es},
+                          {a.S0, BH * a.dv * a.dk * 4},
+                          {a.o, BH * L * a.dv * 4},
+                          {a.S_out, BH * a.dv * a.dk * 4},
+                          {a.beta_t, BH * L * (a.beta_kind == FALCON_BETA_CHANNEL ? a.dv : 1) * es},
+                          {a.x_hist, BH * NH * a.dk * es},
+                          {a.y_hist, BH * NH * a.dv * es},
+                          {xo, BH * NH * a.dk * es},
+                          {yo, BH * NH * a.dv * es}};
+  for (const Range& r : others)
+    if (overlap(w, r)) return true;
+  return false;
+}
+
+int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipStream_t stream,
+              void* ws = nullptr, size_t ws_bytes = 0) {
   int st = check_seq(a, hist_api);
   if (st == FALCON_OK && hist_api) st = check_history(a, xo, yo);
   if (st != FALCON_OK) return st;
@@ -162,7 +186,11 @@ int fwd_chunk(const falcon::SeqArgs& a, bool hist_api, void* xo, void* yo, hipSt
   if (a.dtype != FALCON_BF16) return FALCON_ERR_UNSUPPORTED;
   // wider windows: the inner-product kernel takes any window up to 16
   if (a.window > 4 && !falcon::chunk_ip_supported(a)) return FALCON_ERR_UNSUPPORTED;
-  return launch_with_history(true, a, xo, yo, stream);
+  if (ws != nullptr) {
+    if (!aligned16(ws)) return FALCON_ERR_INVALID_ARG;
+    if (ws_overlaps(a, xo, yo, ws, ws_bytes)) return FALCON_ERR_INVALID_ARG;
+  }
+  return launch_with_history(true, a, xo, yo, stream, ws, ws_bytes);
 }
 
 int fwd_masked(const falcon::SeqArgs& a, void* xo, void* yo, hipStream_t stream) {
@@ -241,6 +269,37 @@ FALCON_EXPORT int falcon_fwd_chunk_ex(int variant, int window, int flags, float 
                     eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
                     chunk, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
   return fwd_chunk(a, true, x_hist_out, y_hist_out, (hipStream_t)stream);
+}
+
+FALCON_EXPORT unsigned long long falcon_fwd_workspace_bytes(int variant, int window, int beta_kind,
+                                                            int batch, int heads, int seqlen,
+                                                            int dk, int dv, int dtype) {
+  if (variant < FALCON_1 || variant > FALCON_3A || window < 1 || batch < 1 || heads < 1 ||
+      seqlen < 1 || dk < 1 || dv < 1 || dtype != FALCON_BF16)
+    return 0;
+  if (beta_kind < FALCON_BETA_SCALAR || beta_kind > FALCON_BETA_CHANNEL) return 0;
+  if (window != 1 && !window_variant(variant)) return 0;
+  falcon::SeqArgs a{variant, window, is_regression(variant), 0.0f, nullptr, beta_kind, 0.0f, 0.0f,
+                    batch, heads, seqlen, dk, dv, dtype, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, nullptr, nullptr, 64};
+  return (unsigned long long)falcon::chunk_wyb2_workspace_bytes(a);
+}
+
+FALCON_EXPORT int falcon_fwd_chunk_ws(int variant, int window, int flags, float beta,
+                                      const void* beta_t, int beta_kind, float lambda, float eps,
+                                      int batch, int heads, int seqlen, int dk, int dv, int dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const void* k_prev, const float* S0, const void* x_hist,
+                                      const void* y_hist, float* o, float* S_out,
+                                      void* x_hist_out, void* y_hist_out, void* workspace,
+                                      unsigned long long workspace_bytes, int chunk,
+                                      void* stream) {
+  if (flags & ~FALCON_SAME_STEP) return FALCON_ERR_INVALID_ARG;
+  falcon::SeqArgs a{variant, window, is_regression(variant), beta, beta_t, beta_kind, lambda,
+                    eps, batch, heads, seqlen, dk, dv, dtype, q, k, v, k_prev, S0, o, S_out,
+                    chunk, x_hist, y_hist, (flags & FALCON_SAME_STEP) ? 0 : 1};
+  return fwd_chunk(a, true, x_hist_out, y_hist_out, (hipStream_t)stream, workspace,
+                   (size_t)workspace_bytes);
 }
 
 FALCON_EXPORT int falcon_fwd_masked(int variant, int window, int flags, float beta,

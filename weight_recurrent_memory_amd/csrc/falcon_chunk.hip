@@ -708,11 +708,15 @@ int chunk_sub_length(int chunk, int window, int dk) {
   return c;
 }
 
-hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream) {
+hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
   (void)hipGetLastError();
   const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
   if (chunk_wy_supported(a)) return launch_chunk_wy(a, stream);
   if (chunk_ip_supported(a)) return launch_chunk_ip(a, stream);
+  if (ws != nullptr) {
+    const size_t need = chunk_wyb2_workspace_bytes(a);
+    if (need > 0 && ws_bytes >= need) return launch_chunk_wyb2(a, ws, stream);
+  }
   if (chunk_wyb_supported(a)) return launch_chunk_wyb(a, stream);
   if (a.window == 1) return launch_chunk_w1(a, stream, cs);
   switch (a.dk) {

@@ -97,13 +97,26 @@ struct WybLds {
   uint16_t Pflo[2][CS][HP];
   alignas(16) float cm[2][NXT];          // inner-product family: sum of zeta per key
   int bad;                               // some sub-chunk's decay products left the range
+  int badj[4];                           // the same per sub-chunk (& 3), pre-pass form
 };
 
 struct WybGeom {
   int nrbg;
   int remap;
   int nchunks;
+  int seg_len;          // pre-pass: sub-chunks per workgroup
+  int nseg;             // pre-pass: workgroups per chain
+  unsigned char* rec;   // pre-pass records, [chain][sub-chunk][kWybRecBytes]
 };
+
+// One pre-pass record per (chain, sub-chunk): the folds of the sub-chunk as
+// split-bf16 rows in fragment order (-H_x, H_y: 32 x 32; -Q_x, Q_y: 16 x 32;
+// hi then lo), the decay products g_t (16 fp32) and a flag set when they leave
+// the range of the chunk algebra.
+constexpr int kWybRecFrag = 12288;      // bytes of bf16 fragments
+constexpr int kWybRecGam = 12288;       // offset of g_t
+constexpr int kWybRecBad = 12352;       // offset of the flag
+constexpr int kWybRecBytes = 12416;
 
 // acc + g(lane N of this 16-lane row) * r as one DPP multiply-add (g is only
 // loaded from LDS, never written by the vector ALU, so no wait states apply)
@@ -157,7 +170,10 @@ __device__ __forceinline__ bf16x8 frag_two(const uint16_t* a, const uint16_t* b)
   return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
 }
 
-template <int DK, bool REG, int B>
+// PREP: the pre-pass form.  A workgroup prepares sub-chunks [s0, s1) of one
+// chain (no state, no outputs) and writes one record per sub-chunk; waves 0 and
+// 1, the state waves of the fused form, store the records.
+template <int DK, bool REG, int B, bool PREP>
 __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   using SM = WybLds<DK>;
   constexpr int NKT = DK / 16, NKS = DK / 32, VPR = DK / 8;
@@ -172,8 +188,16 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
   const uint16_t* __restrict__ bg = static_cast<const uint16_t*>(a.beta_t);
 
-  int chain, rbg;
-  {
+  int chain, rbg, s0, s1;
+  if constexpr (PREP) {
+    const int b = blockIdx.x;
+    chain = b / geo.nseg;
+    rbg = 0;
+    s0 = (b % geo.nseg) * geo.seg_len;
+    s1 = s0 + geo.seg_len < geo.nchunks ? s0 + geo.seg_len : geo.nchunks;
+  } else {
+    s0 = 0;
+    s1 = geo.nchunks;
     const int b = blockIdx.x;
     if (geo.remap) {   // the row groups of one chain share an XCD (and its L2)
       const int xcd = b & 7, slot = b >> 3;
@@ -195,7 +219,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   const long qk_base = (long)chain * L * DK;
   const long v_base = (long)chain * L * dv;
   const int nchunks = geo.nchunks;
-  auto live_chunk = [&](int j) __attribute__((always_inline)) { return j >= 0 && j < nchunks; };
+  auto live_chunk = [&](int j) __attribute__((always_inline)) { return j >= s0 && j < s1; };
   auto steps = [&](int j) __attribute__((always_inline)) {
     const long t0 = (long)j * CS;
     return (int)((L - t0) < CS ? (L - t0) : CS);
@@ -205,6 +229,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 
   // ---------------- block -1 (before the sequence) is zero ----------------
   if (tid == 0) sm.bad = 0;
+  if (PREP && s0 > 0) {
+    // a later segment: block s0 - 1 of the sequence, whose keys the first
+    // sub-chunk's tile and windows reach, is loaded here (below)
+  } else {
   for (int idx = tid; idx < CS * SM::XR; idx += NT) (&sm.X[3][0][0])[idx] = 0;
   for (int idx = tid; idx < DK * SM::TP; idx += NT) (&sm.XT[3][0][0])[idx] = 0;
   for (int idx = tid; idx < RW * SM::TP; idx += NT) (&sm.YT[3][0][0])[idx] = 0;
@@ -234,6 +262,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       }
       sm.knorm[3][CS - NH + tid] = n;
     }
+  }
   }
 
   // ---------------- global loads (buffer resources, range checked) ----------------
@@ -332,6 +361,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       put8(&sm.Q[jb][p / VPR][0], (p % VPR) * 8, s.p[u]);
     }
     if (lane < 32) {
+      if constexpr (PREP) return;   // the pre-pass does not use the values
       const uint32_t w[8] = {s.v.x, s.v.y, s.v.z, s.v.w, s.v2.x, s.v2.y, s.v2.z, s.v2.w};
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -421,7 +451,12 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     gsc *= dpp_shr<4>(gsc, 1.0f);
     gsc *= dpp_shr<8>(gsc, 1.0f);
     const float gprev = dpp_shr<1>(gsc, 1.0f);
-    if (__builtin_amdgcn_ballot_w64(lane < 16 && gauge_out_of_range(gsc, dec)) != 0 && lane == 0) sm.bad = 1;
+    const bool out_of_range = __builtin_amdgcn_ballot_w64(lane < 16 && gauge_out_of_range(gsc, dec)) != 0;
+    if constexpr (PREP) {
+      if (lane == 0) sm.badj[ss] = out_of_range ? 1 : 0;
+    } else {
+      if (out_of_range && lane == 0) sm.bad = 1;
+    }
     const float z = eta * __builtin_amdgcn_rcpf(gsc);
     float zc = z;
     zc += dpp_shr<1>(zc, 0.0f);
@@ -661,7 +696,38 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
   //      fragments of c+2 | commit of c+3, loads of c+4
   // Inner product, iterations c = -2 .. nchunks-1: state of c, preparation of
   // c+1, commit of c+2, loads of c+3, also in two phases.
-  const int c_begin = REG ? -3 : -2;
+  const int c_begin = REG ? s0 - 3 : -2;
+  if (PREP && wave < 2) {
+    // ---------------- pre-pass: record stores ----------------
+    // iteration c prepares sub-chunk c + 1 in phase A (its folds) and stores its
+    // record in phase B; g_t and the range flag were formed two iterations before
+    for (int c = c_begin; c < s1 - 1; ++c) {
+      __syncthreads();
+      __syncthreads();
+      const int j = c + 1;
+      if (!live_chunk(j)) continue;
+      unsigned char* rp = geo.rec + ((long)chain * nchunks + j) * kWybRecBytes;
+      const int sb = j & 1;
+      for (int pc = tid; pc < kWybRecFrag / 16; pc += 128) {
+        const uint16_t* src;
+        if (pc < 512) {
+          const int ar = pc >> 7, r = (pc & 127) >> 2, g = pc & 3;
+          const uint16_t* base = ar == 0 ? &sm.Hxhi[sb][0][0] : ar == 1 ? &sm.Hxlo[sb][0][0]
+                               : ar == 2 ? &sm.Hyhi[sb][0][0] : &sm.Hylo[sb][0][0];
+          src = base + r * SM::HP + 8 * g;
+        } else {
+          const int q = pc - 512, ar = q >> 6, r = (q & 63) >> 2, g = q & 3;
+          const uint16_t* base = ar == 0 ? &sm.Qxhi[sb][0][0] : ar == 1 ? &sm.Qxlo[sb][0][0]
+                               : ar == 2 ? &sm.Qyhi[sb][0][0] : &sm.Qylo[sb][0][0];
+          src = base + r * SM::HP + 8 * g;
+        }
+        *reinterpret_cast<uint4*>(rp + 16 * pc) = *reinterpret_cast<const uint4*>(src);
+      }
+      if (tid < CS) reinterpret_cast<float*>(rp + kWybRecGam)[tid] = sm.gam[j & 3][tid];
+      if (tid == CS) *reinterpret_cast<int*>(rp + kWybRecBad) = sm.badj[j & 3];
+    }
+    return;
+  }
   if (wave < 2) {
     // ---------------- state waves ----------------
     const int rt = wave;
@@ -757,8 +823,12 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
     // ---------------- preparation waves ----------------
     KSet ks0;
     QSet qs0;
-    if (wave == 6) prefetch_k(ks0, 0);
-    if (wave == 7) prefetch_q(qs0, 0);
+    if (PREP && s0 > 0 && wave == 6) {   // block s0 - 1 of a later segment
+      prefetch_k(ks0, s0 - 1);
+      commit_k(ks0, s0 - 1);
+    }
+    if (wave == 6) prefetch_k(ks0, s0);
+    if (wave == 7) prefetch_q(qs0, s0);
     // commit of sub-chunk c+2 (its ring slot is free during the whole iteration)
     // and the loads of c+3
     auto move = [&](int c) __attribute__((always_inline)) {
@@ -771,7 +841,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         prefetch_q(qs0, c + 3);
       }
     };
-    for (int c = c_begin; c < nchunks; ++c) {
+    const int c_end = PREP ? s1 - 1 : nchunks;
+    for (int c = c_begin; c < c_end; ++c) {
       const int j = c + 1;
       const bool pj = live_chunk(j);
       __syncthreads();
@@ -795,8 +866,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
             gram_tile(j2, 1, 1);
             qx_tile(j2, 0);
             qx_tile(j2, 1);
-            transpose_keys(j2, lane);
-            transpose_keys(j2, 64 + lane);
+            if constexpr (!PREP) {     // the pre-pass has no carry to feed
+              transpose_keys(j2, lane);
+              transpose_keys(j2, 64 + lane);
+            }
           }
         }
         __syncthreads();
@@ -809,7 +882,7 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
           if (wave == 5) pfrag_store(0);
           if (wave == 7 && NKU > 1) pfrag_store(NKU - 1);
         }
-        if (pj) {
+        if (pj && !PREP) {
           if (wave == 5) ufk_tile(j, 1, 0);
           if (wave == 6) {
             ufk_tile(j, 1, 1);
@@ -834,12 +907,420 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
         move(c);
       }
     }
+    if constexpr (PREP) return;     // as many barriers as the record-store waves
     __syncthreads();
   }
   // a chain whose decay products left the range of the chunk algebra: its rows
   // again, exactly, by the recurrence (S_out was left untouched above)
   __syncthreads();
   if (sm.bad) recurrence_rows<DK, NT, B>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
+}
+
+// ---------------------------------------------------------------------------
+// State kernel of the two-kernel form: the sequential part only.  The pre-pass
+// has written every sub-chunk's folds (-H_x, H_y, -Q_x, Q_y, split-bf16 rows in
+// fragment order), its decay products and its range flag; per sub-chunk c this
+// kernel forms XS = X S0^T, Fk = H_y Y - H_x XS, o_t = g_t (S0 q_t + (Q_y Y)_t -
+// (Q_x XS)_t) and S_c = g_15 (S0 + Fk^T X) (the same equations as above).
+// One workgroup = 8 wave64 = one chain x 32 value rows.  Waves 0-3 hold the
+// state: wave w owns the 16-row tile w & 1 and the column half w >> 1 of S in
+// registers (one wave per SIMD); XS and S0 q, sums over all columns, are formed
+// as two column-half partials and added in LDS (one barrier per sub-chunk).
+// Waves 4-7 move the data, each one part of every sub-chunk: its global reads
+// four sub-chunks ahead, its commit to LDS two sub-chunks ahead (keys in
+// fragment order and transposed, queries, values transposed, the -H_x and -Q_x
+// fragments and g_t for the state waves), and H_y Y and Q_y Y one ahead.
+constexpr int ST_NW = 8;
+constexpr int ST_NT = 64 * ST_NW;
+
+template <int DK>
+struct WybStLds {
+  static constexpr int XR = DK + 16;
+  static constexpr int TP = CS + 12;
+  static constexpr int FP = NXT + 4;
+  static constexpr int OP = RW + 4;
+  static constexpr int FR = NXT + 8;     // bf16 row of a fold fragment array
+  uint16_t X[4][CS][XR];                 // key blocks by sub-chunk & 3 (fragment order)
+  uint16_t Q[4][CS][XR];                 // query blocks
+  uint16_t XT[4][DK][TP];                // key blocks transposed
+  uint16_t YT[4][RW][TP];                // value blocks transposed
+  uint16_t Hx[4][2][NXT][FR];            // -H_x rows, hi / lo
+  uint16_t Qx[4][2][CS][FR];             // -Q_x rows, hi / lo
+  float gam[4][CS];                      // g_t
+  float Ufk[4][RW][FP];                  // (H_y Y)[m][i] stored [i][m]
+  float Oy[4][CS][OP];                   // (Q_y Y)[t][i]
+  floatx4 PX[2][2][2][2][64];            // XS partials [c & 1][row tile][column half][key tile][lane]
+  floatx4 PO[2][2][2][64];               // S0 q partials [c & 1][row tile][column half][lane]
+  int bad;
+};
+
+template <int DK, int B>
+__global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo) {
+  using SM = WybStLds<DK>;
+  constexpr int NKT = DK / 16, NKS = DK / 32, VPR = DK / 8;
+  constexpr int NKH = NKT / 2, NKSH = NKS / 2;     // 16-column tiles and 32-column steps per half
+  static_assert(B == 2 || B == 4, "window 2 or 4");
+  static_assert(DK == 64 || DK == 128, "dk in {64, 128}");
+  __shared__ __align__(16) SM sm;
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ kpg = static_cast<const uint16_t*>(a.k_prev);
+  int chain, rbg;
+  {
+    const int b = blockIdx.x;
+    if (geo.remap) {   // the row groups of one chain share an XCD (and its L2)
+      const int xcd = b & 7, slot = b >> 3;
+      chain = xcd + 8 * (slot / geo.nrbg);
+      rbg = slot % geo.nrbg;
+    } else {
+      chain = b / geo.nrbg;
+      rbg = b % geo.nrbg;
+    }
+  }
+  const int dv = a.dv;
+  const int i0 = rbg * RW;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const long L = a.seqlen;
+  const long qk_base = (long)chain * L * DK;
+  const long v_base = (long)chain * L * dv;
+  const int nchunks = geo.nchunks;
+
+  // ---------------- block -1: zero, or the carried window samples ----------------
+  if (tid == 0) sm.bad = 0;
+  for (int idx = tid; idx < CS * SM::XR; idx += ST_NT) (&sm.X[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < DK * SM::TP; idx += ST_NT) (&sm.XT[3][0][0])[idx] = 0;
+  for (int idx = tid; idx < RW * SM::TP; idx += ST_NT) (&sm.YT[3][0][0])[idx] = 0;
+  if (a.x_hist) {
+    const uint16_t* __restrict__ xhg = static_cast<const uint16_t*>(a.x_hist);
+    const uint16_t* __restrict__ yhg = static_cast<const uint16_t*>(a.y_hist);
+    constexpr int NH = B - 1;
+    __syncthreads();
+    for (int idx = tid; idx < NH * DK; idx += ST_NT) {
+      const int h = idx / DK, kk = idx % DK, t = CS - NH + h;
+      const uint16_t xv = xhg[((long)chain * NH + h) * DK + kk];
+      sm.X[3][t][fpos(kk)] = xv;
+      sm.XT[3][kk][t] = xv;
+    }
+    for (int idx = tid; idx < NH * RW; idx += ST_NT) {
+      const int h = idx / RW, i = idx % RW, t = CS - NH + h;
+      sm.YT[3][i][t] = (i0 + i < dv) ? yhg[((long)chain * NH + h) * dv + i0 + i] : (uint16_t)0;
+    }
+  }
+
+  if (wave < 4) {
+    // ---------------- state waves ----------------
+    const int rt = wave & 1, ch = wave >> 1;
+    float sv[NKH][4];                          // S[16 rt + lr][16 (NKH ch + kt) + 4 lg + e]
+#pragma unroll
+    for (int kt = 0; kt < NKH; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 16 * rt + lr, kk = 16 * (NKH * ch + kt) + 4 * lg + e;
+        sv[kt][e] = (a.S0 && i < dv) ? a.S0[((long)chain * dv + i) * DK + kk] : 0.0f;
+      }
+    HL sf[NKSH];
+    auto resplit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < NKSH; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
+    };
+    resplit();
+    float* orow = a.o + v_base + (long)lr * dv + i0 + 16 * rt + 4 * lg;
+    const bool rows_in = i0 + 16 * rt < dv;
+    for (int c = -2; c < nchunks; ++c) {
+      const bool run = c >= 0 && rows_in;
+      const int cb = c & 1, cs = c & 3;
+      // phase 1: this column half's partials of XS = X S0^T and of S0 q
+      if (run) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          floatx4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKSH; ++ks)
+            xs = mma2(xs, frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * (NKSH * ch + ks) + 8 * lg]), sf[ks]);
+          sm.PX[cb][rt][ch][mi][lane] = xs;
+        }
+        floatx4 oq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKSH; ++ks)
+          oq = mma2(oq, sf[ks], frag_bf16(&sm.Q[cs][lr][32 * (NKSH * ch + ks) + 8 * lg]));
+        sm.PO[cb][rt][ch][lane] = oq;
+      }
+      __syncthreads();
+      if (!run) continue;
+      // phase 2: XS, Fk = Ufk - H_x XS, the readout (column half 0), the carry
+      floatx4 xs[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const floatx4 p0 = sm.PX[cb][rt][0][mi][lane], p1 = sm.PX[cb][rt][1][mi][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[mi][e] = p0[e] + p1[e];
+      }
+      const HL xsf = hl_x4(xs[0], xs[1]);
+      floatx4 fk[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cs][16 * rt + lr][16 * mi + 4 * lg]));
+        fk[mi] = mma3(fk[mi], hl_pair(&sm.Hx[cs][0][16 * mi + lr][8 * lg], &sm.Hx[cs][1][16 * mi + lr][8 * lg]), xsf);
+      }
+      if (ch == 0) {
+        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cs][lr][16 * rt + 4 * lg]));
+        const floatx4 p0 = sm.PO[cb][rt][0][lane], p1 = sm.PO[cb][rt][1][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[e] += p0[e] + p1[e];
+        oacc = mma3(oacc, xsf, hl_pair(&sm.Qx[cs][0][lr][8 * lg], &sm.Qx[cs][1][lr][8 * lg]));
+        const float gt = sm.gam[cs][lr];
+        if ((long)c * CS + lr < L)
+          *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
+        orow += CS * dv;
+      }
+      const float gC = sm.gam[cs][CS - 1];
+      const HL fkf = hl_x4(fk[0], fk[1]);
+#pragma unroll
+      for (int kt = 0; kt < NKH; ++kt) {
+        const int col = 16 * (NKH * ch + kt) + lr;
+        const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][col][4 * lg], &sm.XT[cs][col][4 * lg]);
+        const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xt, fkf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
+      }
+      resplit();
+    }
+    __syncthreads();
+    if (rows_in && a.S_out && !sm.bad && i0 + 16 * rt + lr < dv) {
+#pragma unroll
+      for (int kt = 0; kt < NKH; ++kt)
+        *reinterpret_cast<float4*>(a.S_out + ((long)chain * dv + i0 + 16 * rt + lr) * DK + 16 * (NKH * ch + kt) + 4 * lg) =
+            make_float4(sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]);
+    }
+  } else {
+    // ---------------- data-movement waves ----------------
+    // Iteration c commits sub-chunk c + 2 and issues the reads of c + 6 (four
+    // sub-chunks ahead, into a ring of four register sets indexed by c & 3):
+    // wave 4 the keys (fragment order and transposed), wave 5 the queries and
+    // values, wave 6 the -H_x / -Q_x fragments, g_t and the range flag; wave 7
+    // forms H_y Y and Q_y Y of c + 1 from its own ring of H_y / Q_y fragments.
+    const int role = wave - 4;
+    constexpr int KP = CS * VPR / 64;          // 16-byte pieces per lane of a key or query block
+    constexpr uint32_t KQ_CHUNK = CS * DK * 2;
+    constexpr int BUF_WORD3 = 0x00020000;
+    constexpr uint32_t PARKED = 0xC0000000u;
+    auto rsrc = [](const void* base, long bytes) __attribute__((always_inline)) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, BUF_WORD3);
+    };
+    auto ld128 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+      return make_uint4(v[0], v[1], v[2], v[3]);
+    };
+    const auto rk = rsrc(kg + qk_base, L * DK * 2);
+    const auto rq = rsrc(qg + qk_base, L * DK * 2);
+    const auto rv = rsrc(vg + v_base, L * dv * 2);
+    const auto rrec = rsrc(geo.rec + (long)chain * nchunks * kWybRecBytes, (long)nchunks * kWybRecBytes);
+    auto koff = [&](int u) __attribute__((always_inline)) {
+      const int p = lane + 64 * u;
+      return (uint32_t)(((p / VPR - a.key_shift) * DK + (p % VPR) * 8) * 2);
+    };
+    auto qoff = [&](int u) __attribute__((always_inline)) {
+      const int p = lane + 64 * u;
+      return (uint32_t)(((p / VPR) * DK + (p % VPR) * 8) * 2);
+    };
+    // record j: array ar (0 -H_x hi, 1 lo, 2 H_y hi, 3 lo; 4 -Q_x hi, 5 lo, 6 Q_y hi,
+    // 7 lo), row r, this lane's 8 columns
+    auto rec_frag = [&](int j, int ar, int r) __attribute__((always_inline)) {
+      const uint32_t base = ar < 4 ? 2048u * ar : 8192u + 1024u * (ar - 4);
+      return ld128(rrec, (uint32_t)j * kWybRecBytes + base + (uint32_t)((r * 4 + lg) * 16));
+    };
+    const int vb_t4 = 4 * ((lane & 31) >> 3), vb_i4 = 4 * (lane & 7);
+    const uint32_t voff = (lane < 32 && i0 + vb_i4 < dv) ? (uint32_t)((vb_t4 * dv + i0 + vb_i4) * 2) : PARKED;
+    const uint32_t V_CHUNK = (uint32_t)(CS * dv * 2);
+    uint4 kprev[KP];
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      kprev[u] = make_uint4(0u, 0u, 0u, 0u);
+      const int p = lane + 64 * u;
+      if (role == 0 && kpg != nullptr && p / VPR == 0)
+        kprev[u] = *reinterpret_cast<const uint4*>(kpg + (long)chain * DK + (p % VPR) * 8);
+    }
+    auto put8 = [&](uint16_t* row, int k0, uint4 val) __attribute__((always_inline)) {
+      *reinterpret_cast<uint2*>(row + fpos(k0)) = make_uint2(val.x, val.y);
+      *reinterpret_cast<uint2*>(row + fpos(k0 + 4)) = make_uint2(val.z, val.w);
+    };
+    auto hl_u = [](uint4 h, uint4 l) __attribute__((always_inline)) {
+      HL f;
+      f.hi = __builtin_bit_cast(bf16x8, h);
+      f.lo = __builtin_bit_cast(bf16x8, l);
+      return f;
+    };
+    auto mover = [&](auto rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(rc)::value;
+      // one register set per ring slot, read by role: w[0..KP) key pieces (role 0);
+      // query pieces and values in w[4], w[5] (role 1); -H_x or H_y [2 tile + hi/lo]
+      // in w[0..3] and -Q_x or Q_y [hi/lo] in w[4], w[5] (roles 2, 3); g_t of this
+      // lane's step and the range flag (role 2)
+      static_assert(KP <= 4, "key pieces fit the set");
+      struct Set {
+        uint4 w[6];
+        float g;
+        uint32_t flag;
+      };
+      Set ring0, ring1, ring2, ring3;             // the ring, one variable per slot
+      auto slot = [&](auto ic) -> Set& {
+        constexpr int i = decltype(ic)::value & 3;
+        if constexpr (i == 0) return ring0;
+        else if constexpr (i == 1) return ring1;
+        else if constexpr (i == 2) return ring2;
+        else return ring3;
+      };
+      auto load = [&](Set& st, int j) __attribute__((always_inline)) {
+        if constexpr (R == 0) {
+  #pragma unroll
+          for (int u = 0; u < KP; ++u) st.w[u] = ld128(rk, koff(u) + (uint32_t)j * KQ_CHUNK);
+        } else if constexpr (R == 1) {
+  #pragma unroll
+          for (int u = 0; u < KP; ++u) st.w[u] = ld128(rq, qoff(u) + (uint32_t)j * KQ_CHUNK);
+          uint32_t w[8];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto val = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + (uint32_t)j * V_CHUNK + (uint32_t)(e * dv * 2)), 0, 0);
+            w[2 * e] = val[0];
+            w[2 * e + 1] = val[1];
+          }
+          st.w[4] = make_uint4(w[0], w[1], w[2], w[3]);
+          st.w[5] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+          constexpr int a0 = R == 2 ? 0 : 2;     // -H_x or H_y
+  #pragma unroll
+          for (int m = 0; m < 2; ++m)
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) st.w[2 * m + h] = rec_frag(j, a0 + h, 16 * m + lr);
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) st.w[4 + h] = rec_frag(j, 4 + a0 + h, lr);
+          if constexpr (R == 2) {
+            st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                       rrec, (int)((uint32_t)j * kWybRecBytes + kWybRecGam + 4u * lr), 0, 0));
+            st.flag = __builtin_amdgcn_raw_buffer_load_b32(rrec, (int)((uint32_t)j * kWybRecBytes + kWybRecBad), 0, 0);
+          }
+        }
+      };
+      auto commit = [&](const Set& st, int j) __attribute__((always_inline)) {
+        const int jb = j & 3;
+        if constexpr (R == 0) {
+  #pragma unroll
+          for (int u = 0; u < KP; ++u) {
+            const int p = lane + 64 * u;
+            const int t = p / VPR, kv = p % VPR;
+            put8(&sm.X[jb][t][0], kv * 8, (j == 0 && t == 0 && a.key_shift) ? kprev[u] : st.w[u]);
+          }
+          // keys transposed: XT[k][t] from X[t][k]; item idx moves a 4 (t) x 4 (k) block
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int idx = lane + 64 * h;
+            if (idx < (CS / 4) * (DK / 4)) {
+              const int t4 = 4 * (idx % (CS / 4)), k4 = 4 * (idx / (CS / 4));
+              const int pk4 = fpos(k4);
+              uint32_t w[8];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint2 r = *reinterpret_cast<const uint2*>(&sm.X[jb][t4 + e][pk4]);
+                w[2 * e] = r.x;
+                w[2 * e + 1] = r.y;
+              }
+  #pragma unroll
+              for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t sel = (kk & 1) ? 0x07060302u : 0x05040100u;
+                const int hh = kk >> 1;
+                *reinterpret_cast<uint2*>(&sm.XT[jb][k4 + kk][t4]) =
+                    make_uint2(__builtin_amdgcn_perm(w[2 + hh], w[hh], sel), __builtin_amdgcn_perm(w[6 + hh], w[4 + hh], sel));
+              }
+            }
+          }
+        } else if constexpr (R == 1) {
+  #pragma unroll
+          for (int u = 0; u < KP; ++u) {
+            const int p = lane + 64 * u;
+            put8(&sm.Q[jb][p / VPR][0], (p % VPR) * 8, st.w[u]);
+          }
+          if (lane < 32) {
+            const uint32_t w[8] = {st.w[4].x, st.w[4].y, st.w[4].z, st.w[4].w, st.w[5].x, st.w[5].y, st.w[5].z, st.w[5].w};
+  #pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const uint32_t sel = (ii & 1) ? 0x07060302u : 0x05040100u;
+              const int h = ii >> 1;
+              *reinterpret_cast<uint2*>(&sm.YT[jb][vb_i4 + ii][vb_t4]) =
+                  make_uint2(__builtin_amdgcn_perm(w[2 + h], w[h], sel), __builtin_amdgcn_perm(w[6 + h], w[4 + h], sel));
+            }
+          }
+        } else if constexpr (R == 2) {
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {
+  #pragma unroll
+            for (int m = 0; m < 2; ++m) *reinterpret_cast<uint4*>(&sm.Hx[jb][h][16 * m + lr][8 * lg]) = st.w[2 * m + h];
+            *reinterpret_cast<uint4*>(&sm.Qx[jb][h][lr][8 * lg]) = st.w[4 + h];
+          }
+          if (lg == 0) sm.gam[jb][lr] = st.g;
+          if (lane == 0 && st.flag != 0) sm.bad = 1;
+        }
+      };
+      // role 3: H_y Y and Q_y Y of sub-chunk j (values of blocks j - 1 and j)
+      auto fold_y = [&](const Set& st, int j) __attribute__((always_inline)) {
+        const int jb = j & 3;
+        const HL hy0 = hl_u(st.w[0], st.w[1]), hy1 = hl_u(st.w[2], st.w[3]);
+        const HL qy = hl_u(st.w[4], st.w[5]);
+  #pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const bf16x8 yf = frag_two(&sm.YT[(j - 1) & 3][16 * it + lr][4 * lg], &sm.YT[jb][16 * it + lr][4 * lg]);
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const floatx4 acc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, mt == 0 ? hy0 : hy1, yf);
+            *reinterpret_cast<float4*>(&sm.Ufk[jb][16 * it + lr][16 * mt + 4 * lg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          }
+          const floatx4 oacc = mma2(floatx4{0.f, 0.f, 0.f, 0.f}, yf, qy);
+          *reinterpret_cast<float4*>(&sm.Oy[jb][lr][16 * it + 4 * lg]) = make_float4(oacc[0], oacc[1], oacc[2], oacc[3]);
+        }
+      };
+      // the first reads: sub-chunks 0..3 (role 3: 0..2, its iteration -2 reads 3)
+      load(ring0, 0);
+      load(ring1, 1);
+      load(ring2, 2);
+      if constexpr (R != 3) load(ring3, 3);
+      // iteration c = c4 + U; c4 + 2 is a multiple of 4, so the ring slots are constants
+      auto iteration = [&](auto uc, int c4) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value;
+        const int c = c4 + U;
+        if (c >= nchunks) return;
+        __syncthreads();
+        if constexpr (R == 3) {
+          Set& st = slot(std::integral_constant<int, U + 3>{});
+          if (c + 1 >= 0 && c + 1 < nchunks) fold_y(st, c + 1);
+          load(st, c + 5);
+        } else {
+          Set& st = slot(std::integral_constant<int, U>{});
+          if (c + 2 < nchunks) commit(st, c + 2);
+          load(st, c + 6);
+        }
+      };
+      for (int c4 = -2; c4 < nchunks; c4 += 4) {
+        iteration(std::integral_constant<int, 0>{}, c4);
+        iteration(std::integral_constant<int, 1>{}, c4);
+        iteration(std::integral_constant<int, 2>{}, c4);
+        iteration(std::integral_constant<int, 3>{}, c4);
+      }
+    };
+    if (role == 0) mover(std::integral_constant<int, 0>{});
+    else if (role == 1) mover(std::integral_constant<int, 1>{});
+    else if (role == 2) mover(std::integral_constant<int, 2>{});
+    else mover(std::integral_constant<int, 3>{});
+    __syncthreads();
+  }
+  // a chain whose decay products left the range of the chunk algebra: its rows
+  // again, exactly, by the recurrence (S_out was left untouched above)
+  __syncthreads();
+  if (sm.bad) recurrence_rows<DK, ST_NT, B>(chain, i0, dv - i0 < RW ? dv - i0 : RW);
 }
 
 template <int DK, bool REG, int B>
@@ -851,7 +1332,10 @@ hipError_t launch_wyb(const SeqArgs& a, hipStream_t stream) {
   geo.remap = (nchain % 8 == 0) ? 1 : 0;
   geo.nchunks = (int)((a.seqlen + CS - 1) / CS);
   const unsigned nblocks = (unsigned)(nchain * geo.nrbg);
-  hipLaunchKernelGGL((chunk_wyb_kernel<DK, REG, B>), dim3(nblocks), dim3(NT), 0, stream, a, geo);
+  geo.seg_len = 0;
+  geo.nseg = 0;
+  geo.rec = nullptr;
+  hipLaunchKernelGGL((chunk_wyb_kernel<DK, REG, B, false>), dim3(nblocks), dim3(NT), 0, stream, a, geo);
   return hipGetLastError();
 }
 
@@ -861,7 +1345,46 @@ hipError_t launch_wyb_dk(const SeqArgs& a, hipStream_t stream) {
   return a.regression ? launch_wyb<DK, true, 4>(a, stream) : launch_wyb<DK, false, 4>(a, stream);
 }
 
+template <int DK, int B>
+hipError_t launch_wyb2(const SeqArgs& a, void* ws, hipStream_t stream) {
+  static_assert(sizeof(WybStLds<DK>) <= 160 * 1024, "LDS budget");
+  WybGeom geo;
+  const int nchain = a.batch * a.heads;
+  geo.nrbg = (a.dv + RW - 1) / RW;
+  geo.remap = (nchain % 8 == 0) ? 1 : 0;
+  geo.nchunks = (int)((a.seqlen + CS - 1) / CS);
+  geo.rec = static_cast<unsigned char*>(ws);
+  // pre-pass: each workgroup prepares a run of sub-chunks of one chain (about one
+  // workgroup per compute unit; every run restarts the preparation pipeline)
+  const long total = (long)nchain * geo.nchunks;
+  int seg = (int)((total + 255) / 256);
+  if (seg < 16) seg = 16;
+  if (seg > geo.nchunks) seg = geo.nchunks;
+  geo.seg_len = seg;
+  geo.nseg = (geo.nchunks + seg - 1) / seg;
+  hipLaunchKernelGGL((chunk_wyb_kernel<DK, true, B, true>), dim3((unsigned)(nchain * geo.nseg)), dim3(NT), 0,
+                     stream, a, geo);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((wyb_state_kernel<DK, B>), dim3((unsigned)(nchain * geo.nrbg)), dim3(ST_NT), 0, stream, a,
+                     geo);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t chunk_wyb2_workspace_bytes(const SeqArgs& a) {
+  if (!a.regression || !chunk_wyb_supported(a)) return 0;
+  const long nchunks = ((long)a.seqlen + CS - 1) / CS;
+  if (nchunks * kWybRecBytes >= (1L << 30)) return 0;   // per-chain buffer range
+  return (size_t)a.batch * a.heads * nchunks * kWybRecBytes;
+}
+
+hipError_t launch_chunk_wyb2(const SeqArgs& a, void* workspace, hipStream_t stream) {
+  if (a.dk == 64) return a.window == 2 ? launch_wyb2<64, 2>(a, workspace, stream) : launch_wyb2<64, 4>(a, workspace, stream);
+  if (a.dk == 128) return a.window == 2 ? launch_wyb2<128, 2>(a, workspace, stream) : launch_wyb2<128, 4>(a, workspace, stream);
+  return hipErrorInvalidValue;
+}
 
 bool chunk_wyb_supported(const SeqArgs& a) {
   const long bytes = (long)a.seqlen * (a.dk > a.dv ? a.dk : a.dv) * 2;

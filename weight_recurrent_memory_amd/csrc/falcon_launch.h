@@ -94,7 +94,9 @@ hipError_t launch_recurrent(const SeqArgs& a, hipStream_t stream);
 // seqlen 1..kMaskedMaxLen, window 1..8
 constexpr int kMaskedMaxLen = 64;
 hipError_t launch_masked(const SeqArgs& a, hipStream_t stream);
-hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream);
+// workspace (optional): the two-kernel sliding-window form runs where it applies and
+// ws_bytes >= chunk_wyb2_workspace_bytes(a)
+hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream, void* ws = nullptr, size_t ws_bytes = 0);
 // window-1 chunk form, per-channel gains (falcon_chunk_w1.hip); cs = sub-chunk length
 hipError_t launch_chunk_w1(const SeqArgs& a, hipStream_t stream, int cs);
 // window-1 chunk form, gains shared by the value rows, dk in {32, 64}
@@ -105,6 +107,11 @@ hipError_t launch_chunk_wy(const SeqArgs& a, hipStream_t stream);
 // {64, 128} (falcon_chunk_wyb.hip); 16-step sub-chunks whatever the requested chunk
 bool chunk_wyb_supported(const SeqArgs& a);
 hipError_t launch_chunk_wyb(const SeqArgs& a, hipStream_t stream);
+// the same in two kernels (regression family): a pre-pass writes every
+// sub-chunk's folds to a workspace, a state kernel runs the sequential part;
+// the workspace bytes it needs (0 where it does not apply) and its launch
+size_t chunk_wyb2_workspace_bytes(const SeqArgs& a);
+hipError_t launch_chunk_wyb2(const SeqArgs& a, void* workspace, hipStream_t stream);
 // inner-product family, any window up to 16, gains shared by the value rows, dk in
 // {64, 128}, dv a multiple of 32 (falcon_chunk_ip.hip); 64-step chunks
 bool chunk_ip_supported(const SeqArgs& a);
