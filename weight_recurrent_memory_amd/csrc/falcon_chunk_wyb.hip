@@ -929,7 +929,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 // Waves 4-7 move the data, each one part of every sub-chunk: its global reads
 // four sub-chunks ahead, its commit to LDS two sub-chunks ahead (keys in
 // fragment order and transposed, queries, values transposed, the -H_x and -Q_x
-// fragments and g_t for the state waves), and H_y Y and Q_y Y one ahead.
+// fragments and g_t), and H_y Y and Q_y Y one ahead; waves 5 and 6 also form
+// the outputs of the current sub-chunk from the state waves' partials.
 constexpr int ST_NW = 8;
 constexpr int ST_NT = 64 * ST_NW;
 
@@ -1030,7 +1031,6 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
       for (int ks = 0; ks < NKSH; ++ks) sf[ks] = hl_two(sv[2 * ks], sv[2 * ks + 1]);
     };
     resplit();
-    float* orow = a.o + v_base + (long)lr * dv + i0 + 16 * rt + 4 * lg;
     const bool rows_in = i0 + 16 * rt < dv;
     for (int c = -2; c < nchunks; ++c) {
       const bool run = c >= 0 && rows_in;
@@ -1053,7 +1053,7 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
       }
       __syncthreads();
       if (!run) continue;
-      // phase 2: XS, Fk = Ufk - H_x XS, the readout (column half 0), the carry
+      // phase 2: XS, Fk = Ufk - H_x XS, the carry (the readout is on waves 5, 6)
       floatx4 xs[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
@@ -1067,17 +1067,6 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
       for (int mi = 0; mi < 2; ++mi) {
         fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cs][16 * rt + lr][16 * mi + 4 * lg]));
         fk[mi] = mma3(fk[mi], hl_pair(&sm.Hx[cs][0][16 * mi + lr][8 * lg], &sm.Hx[cs][1][16 * mi + lr][8 * lg]), xsf);
-      }
-      if (ch == 0) {
-        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cs][lr][16 * rt + 4 * lg]));
-        const floatx4 p0 = sm.PO[cb][rt][0][lane], p1 = sm.PO[cb][rt][1][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[e] += p0[e] + p1[e];
-        oacc = mma3(oacc, xsf, hl_pair(&sm.Qx[cs][0][lr][8 * lg], &sm.Qx[cs][1][lr][8 * lg]));
-        const float gt = sm.gam[cs][lr];
-        if ((long)c * CS + lr < L)
-          *reinterpret_cast<float4*>(orow) = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
-        orow += CS * dv;
       }
       const float gC = sm.gam[cs][CS - 1];
       const HL fkf = hl_x4(fk[0], fk[1]);
@@ -1283,6 +1272,30 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
           *reinterpret_cast<float4*>(&sm.Oy[jb][lr][16 * it + 4 * lg]) = make_float4(oacc[0], oacc[1], oacc[2], oacc[3]);
         }
       };
+      // roles 1 and 2: the readout of sub-chunk c for row tile R - 1, from the
+      // state waves' partials: o_t = g_t (S_c q_t + (Q_y Y)_t - (Q_x XS_c)_t)
+      auto readout = [&](int c) __attribute__((always_inline)) {
+        constexpr int rt = R - 1;
+        if (i0 + 16 * rt >= dv) return;
+        const int cb = c & 1, cs = c & 3;
+        floatx4 xs[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const floatx4 p0 = sm.PX[cb][rt][0][mi][lane], p1 = sm.PX[cb][rt][1][mi][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[mi][e] = p0[e] + p1[e];
+        }
+        const HL xsf = hl_x4(xs[0], xs[1]);
+        floatx4 oacc = f4x(*reinterpret_cast<const float4*>(&sm.Oy[cs][lr][16 * rt + 4 * lg]));
+        const floatx4 p0 = sm.PO[cb][rt][0][lane], p1 = sm.PO[cb][rt][1][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[e] += p0[e] + p1[e];
+        oacc = mma3(oacc, xsf, hl_pair(&sm.Qx[cs][0][lr][8 * lg], &sm.Qx[cs][1][lr][8 * lg]));
+        const float gt = sm.gam[cs][lr];
+        if ((long)c * CS + lr < L)
+          *reinterpret_cast<float4*>(a.o + v_base + ((long)c * CS + lr) * dv + i0 + 16 * rt + 4 * lg) =
+              make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
+      };
       // the first reads: sub-chunks 0..3 (role 3: 0..2, its iteration -2 reads 3)
       load(ring0, 0);
       load(ring1, 1);
@@ -1301,6 +1314,9 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         } else {
           Set& st = slot(std::integral_constant<int, U>{});
           if (c + 2 < nchunks) commit(st, c + 2);
+          if constexpr (R == 1 || R == 2) {
+            if (c >= 0) readout(c);
+          }
           load(st, c + 6);
         }
       };
