@@ -325,6 +325,7 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
     for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<4>(g[k]);
 #pragma unroll
     for (int k = 0; k < NC; ++k) g[k] = row_shr_mul<8>(g[k]);
+    bool out_of_range = false;
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
       float fill = 1.0f;
@@ -336,12 +337,13 @@ __global__ __launch_bounds__(NT) void chunk_w1_kernel(SeqArgs a, W1Geom geo) {
         fill = (lane & 31) == 16 ? tot : 1.0f;
       }
       const float gprev = row_shr<1>(g[k], fill);
-      if (__builtin_amdgcn_ballot_w64(gauge_out_of_range(g[k], dec[k])) != 0 && lane == 0) sm.bad = 1;
+      out_of_range |= gauge_out_of_range(g[k], dec[k]);
       const int row = r0 + k * rstep + rl;
       sm.gam[dst][row][t] = g[k];
       sm.gm1[dst][row][t] = gprev;
       sm.zeta[dst][row][t] = eta[k] * __builtin_amdgcn_rcpf(g[k]);
     }
+    if (__builtin_amdgcn_ballot_w64(out_of_range) != 0 && lane == 0) sm.bad = 1;
   };
 
   // Per-channel residual solve of the chunk in slot s: value row 4 wave + lg on
