@@ -930,7 +930,11 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 // four sub-chunks ahead, its commit to LDS two sub-chunks ahead (keys in
 // fragment order and transposed, queries, values transposed, the -H_x and -Q_x
 // fragments and g_t), and H_y Y and Q_y Y one ahead; waves 5 and 6 also form
-// the outputs of the current sub-chunk from the state waves' partials.
+// the outputs of the current sub-chunk from the state waves' partials, into
+// LDS; state waves 0 and 1 store them to global memory two sub-chunks later, so
+// the movers issue global loads only (with loads and stores pending on one wave
+// the vector-memory counter no longer counts in order, and the compiler's wait
+// before a commit then covers every read the wave has in flight).
 constexpr int ST_NW = 8;
 constexpr int ST_NT = 64 * ST_NW;
 
@@ -952,6 +956,7 @@ struct WybStLds {
   float Oy[4][CS][OP];                   // (Q_y Y)[t][i]
   floatx4 PX[2][2][2][2][64];            // XS partials [c & 1][row tile][column half][key tile][lane]
   floatx4 PO[2][2][2][64];               // S0 q partials [c & 1][row tile][column half][lane]
+  float4 OT[2][2][64];                   // outputs o_t [c & 1][row tile][lane]
   int bad;
 };
 
@@ -1032,55 +1037,91 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
     };
     resplit();
     const bool rows_in = i0 + 16 * rt < dv;
+    // Every operand but the partials and H_y Y was committed to LDS at least one
+    // barrier before its use, so its read is issued early, off the chain: the
+    // keys and queries of sub-chunk c + 1 right after barrier c, the -H_x rows,
+    // transposed keys and g_t of sub-chunk c at the start of phase 1 of c.
+    // outputs of sub-chunk c (in LDS from waves 5, 6) to global memory: the
+    // waves of column half 0, one row tile each
+    auto store_o = [&](int c) __attribute__((always_inline)) {
+      if (ch == 0 && (long)c * CS + lr < L)
+        *reinterpret_cast<float4*>(a.o + v_base + ((long)c * CS + lr) * dv + i0 + 16 * rt + 4 * lg) =
+            sm.OT[c & 1][rt][lane];
+    };
+    bf16x8 xf[2][NKSH], qf[NKSH];
+    auto load_p1 = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < NKSH; ++ks) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) xf[mi][ks] = frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * (NKSH * ch + ks) + 8 * lg]);
+        qf[ks] = frag_bf16(&sm.Q[c & 3][lr][32 * (NKSH * ch + ks) + 8 * lg]);
+      }
+    };
     for (int c = -2; c < nchunks; ++c) {
       const bool run = c >= 0 && rows_in;
       const int cb = c & 1, cs = c & 3;
+      HL hxf[2];
+      bf16x8 xtf[NKH];
+      float gC = 0.0f;
       // phase 1: this column half's partials of XS = X S0^T and of S0 q
       if (run) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          hxf[mi] = hl_pair(&sm.Hx[cs][0][16 * mi + lr][8 * lg], &sm.Hx[cs][1][16 * mi + lr][8 * lg]);
+#pragma unroll
+        for (int kt = 0; kt < NKH; ++kt) {
+          const int col = 16 * (NKH * ch + kt) + lr;
+          xtf[kt] = frag_two(&sm.XT[(c - 1) & 3][col][4 * lg], &sm.XT[cs][col][4 * lg]);
+        }
+        gC = sm.gam[cs][CS - 1];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
           floatx4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < NKSH; ++ks)
-            xs = mma2(xs, frag_bf16(&sm.X[(c - 1 + mi) & 3][lr][32 * (NKSH * ch + ks) + 8 * lg]), sf[ks]);
+          for (int ks = 0; ks < NKSH; ++ks) xs = mma2(xs, xf[mi][ks], sf[ks]);
           sm.PX[cb][rt][ch][mi][lane] = xs;
         }
         floatx4 oq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKSH; ++ks)
-          oq = mma2(oq, sf[ks], frag_bf16(&sm.Q[cs][lr][32 * (NKSH * ch + ks) + 8 * lg]));
+        for (int ks = 0; ks < NKSH; ++ks) oq = mma2(oq, sf[ks], qf[ks]);
         sm.PO[cb][rt][ch][lane] = oq;
+        if (c >= 2) store_o(c - 2);
       }
       __syncthreads();
-      if (!run) continue;
+      if (!run) {
+        if (c == -1 && rows_in && nchunks > 0) load_p1(0);
+        continue;
+      }
       // phase 2: XS, Fk = Ufk - H_x XS, the carry (the readout is on waves 5, 6)
-      floatx4 xs[2];
+      floatx4 xs[2], fk[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
         const floatx4 p0 = sm.PX[cb][rt][0][mi][lane], p1 = sm.PX[cb][rt][1][mi][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) xs[mi][e] = p0[e] + p1[e];
-      }
-      const HL xsf = hl_x4(xs[0], xs[1]);
-      floatx4 fk[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
         fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cs][16 * rt + lr][16 * mi + 4 * lg]));
-        fk[mi] = mma3(fk[mi], hl_pair(&sm.Hx[cs][0][16 * mi + lr][8 * lg], &sm.Hx[cs][1][16 * mi + lr][8 * lg]), xsf);
       }
-      const float gC = sm.gam[cs][CS - 1];
+      if (c + 1 < nchunks) load_p1(c + 1);
+      const HL xsf = hl_x4(xs[0], xs[1]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) fk[mi] = mma3(fk[mi], hxf[mi], xsf);
       const HL fkf = hl_x4(fk[0], fk[1]);
 #pragma unroll
       for (int kt = 0; kt < NKH; ++kt) {
-        const int col = 16 * (NKH * ch + kt) + lr;
-        const bf16x8 xt = frag_two(&sm.XT[(c - 1) & 3][col][4 * lg], &sm.XT[cs][col][4 * lg]);
-        const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xt, fkf);
+        const floatx4 cacc = mma2(floatx4{sv[kt][0], sv[kt][1], sv[kt][2], sv[kt][3]}, xtf[kt], fkf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
       }
       resplit();
     }
     __syncthreads();
+    if (rows_in && !sm.bad) {
+      if (nchunks >= 2) store_o(nchunks - 2);
+      if (nchunks >= 1) store_o(nchunks - 1);
+    }
+    // the exact pass below rewrites this chain's outputs: the stores issued in
+    // the loop complete first
+    if (sm.bad) __threadfence();
     if (rows_in && a.S_out && !sm.bad && i0 + 16 * rt + lr < dv) {
 #pragma unroll
       for (int kt = 0; kt < NKH; ++kt)
@@ -1292,9 +1333,7 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         for (int e = 0; e < 4; ++e) oacc[e] += p0[e] + p1[e];
         oacc = mma3(oacc, xsf, hl_pair(&sm.Qx[cs][0][lr][8 * lg], &sm.Qx[cs][1][lr][8 * lg]));
         const float gt = sm.gam[cs][lr];
-        if ((long)c * CS + lr < L)
-          *reinterpret_cast<float4*>(a.o + v_base + ((long)c * CS + lr) * dv + i0 + 16 * rt + 4 * lg) =
-              make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
+        sm.OT[cb][rt][lane] = make_float4(gt * oacc[0], gt * oacc[1], gt * oacc[2], gt * oacc[3]);
       };
       // the first reads: sub-chunks 0..3 (role 3: 0..2, its iteration -2 reads 3)
       load(ring0, 0);
@@ -1314,10 +1353,10 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         } else {
           Set& st = slot(std::integral_constant<int, U>{});
           if (c + 2 < nchunks) commit(st, c + 2);
+          load(st, c + 6);      // the reads go out as soon as their slot is free, before the readout
           if constexpr (R == 1 || R == 2) {
             if (c >= 0) readout(c);
           }
-          load(st, c + 6);
         }
       };
       for (int c4 = -2; c4 < nchunks; c4 += 4) {
