@@ -128,3 +128,20 @@ def test_two_kernel_explicit_workspace_and_reuse():
     o2, _ = _call(inp, 4, workspace=short, beta=0.5, lam=0.01, eps=1e-6, carried=False)
     o3, _ = _call(inp, 4, workspace=None, beta=0.5, lam=0.01, eps=1e-6, carried=False)
     np.testing.assert_array_equal(o2, o3)
+
+
+@pytest.mark.parametrize("window", [2, 4])
+@pytest.mark.parametrize("L", [1, 7, 16, 17, 33, 48])
+@pytest.mark.parametrize("carried", [False, True])
+def test_two_kernel_short_sequences(window, L, carried):
+    """One to three sub-chunks: the outputs of the last two sub-chunks are
+    stored after the state loop, earlier ones inside it."""
+    inp = seq_inputs(2, 2, L, 64, 64, seed=1380 + 3 * window + L + carried, dtype="bf16",
+                     beta_per_token=True, with_k_prev=carried, with_S0=carried, s_std=0.2,
+                     history=window - 1 if carried else 0)
+    o, S = _call(inp, window, workspace="auto", beta=None, lam=0.02, eps=1e-6, carried=carried)
+    o_ref, S_ref = _ref(inp, window, beta=None, lam=0.02, eps=1e-6, carried=carried)
+    err, zok = token_normwise_err(o, o_ref)
+    serr = state_err(S, S_ref)
+    print("window %d L %d carried %d: o err %.3e S err %.3e" % (window, L, carried, err, serr))
+    assert zok and err <= TOL_BF16 and serr <= TOL_BF16
