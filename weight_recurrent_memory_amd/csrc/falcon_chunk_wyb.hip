@@ -708,12 +708,20 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
       if (!live_chunk(j)) continue;
       unsigned char* rp = geo.rec + ((long)chain * nchunks + j) * kWybRecBytes;
       const int sb = j & 1;
-      for (int pc = tid; pc < kWybRecFrag / 16; pc += 128) {
+      // piece pc = tid + 128 i (16 bytes): i < 4 the 32-row arrays -H_x hi, lo,
+      // H_y hi, lo; i = 4, 5 the 16-row arrays -Q_x hi, lo, Q_y hi, lo (two per
+      // i).  All six reads are issued before the stores, so the copy waits for
+      // one LDS round trip instead of six.
+      static_assert(kWybRecFrag == 16 * 128 * 6, "six 16-byte pieces per record thread");
+      uint4 piece[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int pc = tid + 128 * i;
         const uint16_t* src;
-        if (pc < 512) {
-          const int ar = pc >> 7, r = (pc & 127) >> 2, g = pc & 3;
-          const uint16_t* base = ar == 0 ? &sm.Hxhi[sb][0][0] : ar == 1 ? &sm.Hxlo[sb][0][0]
-                               : ar == 2 ? &sm.Hyhi[sb][0][0] : &sm.Hylo[sb][0][0];
+        if (i < 4) {
+          const int r = (pc & 127) >> 2, g = pc & 3;
+          const uint16_t* base = i == 0 ? &sm.Hxhi[sb][0][0] : i == 1 ? &sm.Hxlo[sb][0][0]
+                               : i == 2 ? &sm.Hyhi[sb][0][0] : &sm.Hylo[sb][0][0];
           src = base + r * SM::HP + 8 * g;
         } else {
           const int q = pc - 512, ar = q >> 6, r = (q & 63) >> 2, g = q & 3;
@@ -721,8 +729,10 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
                                : ar == 2 ? &sm.Qyhi[sb][0][0] : &sm.Qylo[sb][0][0];
           src = base + r * SM::HP + 8 * g;
         }
-        *reinterpret_cast<uint4*>(rp + 16 * pc) = *reinterpret_cast<const uint4*>(src);
+        piece[i] = *reinterpret_cast<const uint4*>(src);
       }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) *reinterpret_cast<uint4*>(rp + 16 * (tid + 128 * i)) = piece[i];
       if (tid < CS) reinterpret_cast<float*>(rp + kWybRecGam)[tid] = sm.gam[j & 3][tid];
       if (tid == CS) *reinterpret_cast<int*>(rp + kWybRecBad) = sm.badj[j & 3];
     }
