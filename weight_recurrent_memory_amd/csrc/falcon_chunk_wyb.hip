@@ -1047,10 +1047,6 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
     };
     resplit();
     const bool rows_in = i0 + 16 * rt < dv;
-    // Every operand but the partials and H_y Y was committed to LDS at least one
-    // barrier before its use, so its read is issued early, off the chain: the
-    // keys and queries of sub-chunk c + 1 right after barrier c, the -H_x rows,
-    // transposed keys and g_t of sub-chunk c at the start of phase 1 of c.
     // outputs of sub-chunk c (in LDS from waves 5, 6) to global memory: the
     // waves of column half 0, one row tile each
     auto store_o = [&](int c) __attribute__((always_inline)) {
@@ -1058,6 +1054,10 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         *reinterpret_cast<float4*>(a.o + v_base + ((long)c * CS + lr) * dv + i0 + 16 * rt + 4 * lg) =
             sm.OT[c & 1][rt][lane];
     };
+    // Every operand but the partials and H_y Y was committed to LDS at least one
+    // barrier before its use, so its read is issued off the chain: after barrier
+    // c, the keys and queries of sub-chunk c + 1 and, once the carry of c has
+    // used those of c, its -H_x rows, transposed keys and g_t.
     bf16x8 xf[2][NKSH], qf[NKSH];
     auto load_p1 = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -1067,34 +1067,43 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         qf[ks] = frag_bf16(&sm.Q[c & 3][lr][32 * (NKSH * ch + ks) + 8 * lg]);
       }
     };
+    HL hxf[2];
+    bf16x8 xtf[NKH];
+    float gC = 0.0f;
+    auto load_p2 = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        hxf[mi] = hl_pair(&sm.Hx[c & 3][0][16 * mi + lr][8 * lg], &sm.Hx[c & 3][1][16 * mi + lr][8 * lg]);
+#pragma unroll
+      for (int kt = 0; kt < NKH; ++kt) {
+        const int col = 16 * (NKH * ch + kt) + lr;
+        xtf[kt] = frag_two(&sm.XT[(c - 1) & 3][col][4 * lg], &sm.XT[c & 3][col][4 * lg]);
+      }
+      gC = sm.gam[c & 3][CS - 1];
+    };
+    // this column half's partials of XS = X S_c^T and of S_c q for sub-chunk c,
+    // from the state of its start
+    auto products = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        floatx4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKSH; ++ks) xs = mma2(xs, xf[mi][ks], sf[ks]);
+        sm.PX[c & 1][rt][ch][mi][lane] = xs;
+      }
+      floatx4 oq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKSH; ++ks) oq = mma2(oq, sf[ks], qf[ks]);
+      sm.PO[c & 1][rt][ch][lane] = oq;
+    };
     for (int c = -2; c < nchunks; ++c) {
       const bool run = c >= 0 && rows_in;
       const int cb = c & 1, cs = c & 3;
-      HL hxf[2];
-      bf16x8 xtf[NKH];
-      float gC = 0.0f;
-      // phase 1: this column half's partials of XS = X S0^T and of S0 q
       if (run) {
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          hxf[mi] = hl_pair(&sm.Hx[cs][0][16 * mi + lr][8 * lg], &sm.Hx[cs][1][16 * mi + lr][8 * lg]);
-#pragma unroll
-        for (int kt = 0; kt < NKH; ++kt) {
-          const int col = 16 * (NKH * ch + kt) + lr;
-          xtf[kt] = frag_two(&sm.XT[(c - 1) & 3][col][4 * lg], &sm.XT[cs][col][4 * lg]);
+        if (c == 0) {
+          load_p2(0);
+          products(0);
         }
-        gC = sm.gam[cs][CS - 1];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          floatx4 xs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKSH; ++ks) xs = mma2(xs, xf[mi][ks], sf[ks]);
-          sm.PX[cb][rt][ch][mi][lane] = xs;
-        }
-        floatx4 oq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKSH; ++ks) oq = mma2(oq, sf[ks], qf[ks]);
-        sm.PO[cb][rt][ch][lane] = oq;
         if (c >= 2) store_o(c - 2);
       }
       __syncthreads();
@@ -1102,7 +1111,9 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         if (c == -1 && rows_in && nchunks > 0) load_p1(0);
         continue;
       }
-      // phase 2: XS, Fk = Ufk - H_x XS, the carry (the readout is on waves 5, 6)
+      // XS, Fk = Ufk - H_x XS, the carry (the readout is on waves 5, 6), then
+      // the products of sub-chunk c + 1 in the same block as the carry (after
+      // the last sub-chunk they fill a partial buffer that nothing reads)
       floatx4 xs[2], fk[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
@@ -1111,7 +1122,7 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         for (int e = 0; e < 4; ++e) xs[mi][e] = p0[e] + p1[e];
         fk[mi] = f4x(*reinterpret_cast<const float4*>(&sm.Ufk[cs][16 * rt + lr][16 * mi + 4 * lg]));
       }
-      if (c + 1 < nchunks) load_p1(c + 1);
+      load_p1(c + 1);
       const HL xsf = hl_x4(xs[0], xs[1]);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) fk[mi] = mma3(fk[mi], hxf[mi], xsf);
@@ -1123,6 +1134,8 @@ __global__ __launch_bounds__(ST_NT) void wyb_state_kernel(SeqArgs a, WybGeom geo
         for (int e = 0; e < 4; ++e) sv[kt][e] = gC * cacc[e];
       }
       resplit();
+      load_p2(c + 1);
+      products(c + 1);
     }
     __syncthreads();
     if (rows_in && !sm.bad) {
