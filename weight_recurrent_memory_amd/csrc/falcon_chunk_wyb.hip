@@ -941,10 +941,8 @@ __global__ __launch_bounds__(NT) void chunk_wyb_kernel(SeqArgs a, WybGeom geo) {
 // fragment order and transposed, queries, values transposed, the -H_x and -Q_x
 // fragments and g_t), and H_y Y and Q_y Y one ahead; waves 5 and 6 also form
 // the outputs of the current sub-chunk from the state waves' partials, into
-// LDS; state waves 0 and 1 store them to global memory two sub-chunks later, so
-// the movers issue global loads only (with loads and stores pending on one wave
-// the vector-memory counter no longer counts in order, and the compiler's wait
-// before a commit then covers every read the wave has in flight).
+// LDS; state waves 0 and 1 store them to global memory two sub-chunks later
+// (the data-movement waves then issue global loads only; measured no slower).
 constexpr int ST_NW = 8;
 constexpr int ST_NT = 64 * ST_NW;
 
