@@ -316,23 +316,16 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     }
   };
 
-  // c_{m,t} for key row m (sample m - 16 of the chunk) from the prefix sums z;
-  // branch-free (both reads always issued, clamped)
-  auto cweight = [&](const float* z, int m, int t) __attribute__((always_inline)) {
-    const int j = m - 16;
-    const int lo = j > 0 ? j : 0;
-    const int hj = j + B - 1;
-    const int hi = hj < t ? hj : t;
-    const float zh = z[hi > 0 ? hi : 0];
-    const float zl = z[lo > 0 ? lo - 1 : 0];
-    const float v = zh - (lo > 0 ? zl : 0.0f);
-    return hi >= lo ? v : 0.0f;
-  };
   // one wave, after the barrier that made chunk c's partial norms and gains
   // visible (lane t = step t): squared norms (the halo rows keep the previous
   // chunk's last 16), eta, a = 1 - eta lambda, g = prefix product of a,
   // zeta = eta / g and its prefix sum, c_{., C-1}.  Padded steps and the
-  // fresh-sequence first step take eta = 0, a = 1.
+  // fresh-sequence first step take eta = 0, a = 1.  The shifted copies of the
+  // prefix sums and the weights are formed from the register z by lane reads
+  // (ds_bpermute, independent of each other), not stored and read back.
+  auto lane_read = [](float v, int src) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+  };
   auto scalars = [&](int c) __attribute__((always_inline)) {
     const int t = lane;
     const int pb = c & 1;
@@ -378,19 +371,35 @@ __global__ __launch_bounds__(INT) void chunk_ip_kernel(SeqArgs a, IpGeom geo) {
     z += lg >= 3 ? s2 : 0.0f;
     sm.gs[pb][t] = g;
     sm.zs[pb][t] = z;
-    wave_sync();
-    // shifted copies for the readout's 4-key reads
-    sm.zp[pb][16 + t] = t > 0 ? sm.zs[pb][t > 0 ? t - 1 : 0] : 0.0f;
-    {
-      const int j = t - 16 + B - 1;   // keys -16..47 on lanes 0..63
-      sm.zq[pb][t] = sm.zs[pb][j < 0 ? 0 : (j > IC - 1 ? IC - 1 : j)];
-      if (lane < 16) {
-        const int j2 = 48 + lane + B - 1;   // keys 48..63
-        sm.zq[pb][64 + lane] = sm.zs[pb][j2 > IC - 1 ? IC - 1 : j2];
-      }
-    }
-    sm.c63[pb][lane] = cweight(sm.zs[pb], lane, IC - 1);
-    if (lane < 16) sm.c63[pb][IC + lane] = cweight(sm.zs[pb], IC + lane, IC - 1);
+    // shifted copies for the readout's 4-key reads, and c_{m, C-1} for key rows
+    // m = lane and m = 64 + lane: c_{m, C-1} = Z_{min(m-16+B-1, C-1)} - Z_{m-17},
+    // zero where that window of steps is empty
+    const int j = t - 16 + B - 1;                 // keys -16..47 on lanes 0..63
+    const int j2 = 48 + lane + B - 1;             // keys 48..63 on lanes 0..15
+    auto cw_lanes = [&](int m, int& hi_l, int& lo_l, bool& use_lo, bool& ok) __attribute__((always_inline)) {
+      const int jm = m - 16;
+      const int lo = jm > 0 ? jm : 0;
+      const int hj = jm + B - 1;
+      const int hi = hj < IC - 1 ? hj : IC - 1;
+      hi_l = hi > 0 ? hi : 0;
+      lo_l = lo > 0 ? lo - 1 : 0;
+      use_lo = lo > 0;
+      ok = hi >= lo;
+    };
+    int h1, l1, h2, l2;
+    bool u1, o1, u2, o2;
+    cw_lanes(lane, h1, l1, u1, o1);
+    cw_lanes(IC + lane, h2, l2, u2, o2);
+    const float zm1 = lane_read(z, t > 0 ? t - 1 : 0);
+    const float zq1 = lane_read(z, j < 0 ? 0 : (j > IC - 1 ? IC - 1 : j));
+    const float zq2 = lane_read(z, j2 > IC - 1 ? IC - 1 : j2);
+    const float zh1 = lane_read(z, h1), zl1 = lane_read(z, l1);
+    const float zh2 = lane_read(z, h2), zl2 = lane_read(z, l2);
+    sm.zp[pb][16 + t] = t > 0 ? zm1 : 0.0f;
+    sm.zq[pb][t] = zq1;
+    if (lane < 16) sm.zq[pb][64 + lane] = zq2;
+    sm.c63[pb][lane] = o1 ? zh1 - (u1 ? zl1 : 0.0f) : 0.0f;
+    if (lane < 16) sm.c63[pb][IC + lane] = o2 ? zh2 - (u2 ? zl2 : 0.0f) : 0.0f;
   };
 
   if (threadIdx.x == 0) sm.bad = 0;
