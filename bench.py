@@ -298,7 +298,7 @@ def main():
             sec_c = time_calls(lambda: fw.fwd_chunk(q, k, v, chunk=64, **kw), 20, 3, stats=stc)
             nbytes = algorithmic_bytes(B, H, L, dk, dv)
             sec_out["masked"] = {"workload": "masked_256x12x64x64", "variant": "falcon1",
-                                 "kernel": "masked_kernel<64,1,true>",
+                                 "kernel": "masked_wy_kernel<64,true,false,false>",
                                  "ms_per_call": sec * 1e3, "median_ms": st["median_s"] * 1e3,
                                  "tokens_per_s": B * L / sec,
                                  "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,

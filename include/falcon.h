@@ -249,9 +249,12 @@ int falcon_fwd_chunk_ws(int variant, int window, int flags, float beta, const vo
  * system.  The samples' Gram matrix X X^T and the key-query products X Q^T are
  * formed for the whole sequence at once; the causally masked, decay-weighted
  * unit-lower-triangular system over every (step, window sample) unknown is then
- * solved by forward substitution in those coordinates, so no dk-sized state is
- * carried from step to step and no decay product is divided by (any decay,
- * however strong, is exact).
+ * solved without carrying a dk-sized state from step to step, and no decay
+ * product is divided by (any decay, however strong, is exact).  With window 1
+ * and gains shared by the value rows (scalar or per-token beta) the system is
+ * the same for every value row and is solved once, in 16-step blocks on the
+ * matrix cores; per-channel gains and windows 2..8 solve it per value row by
+ * forward substitution.
  * Arguments, results and errors as falcon_fwd_recurrent_ex (every variant,
  * window 1..8, bf16 or fp32 inputs, carried key, state and window history,
  * FALCON_SAME_STEP); in addition FALCON_ERR_UNSUPPORTED for

@@ -449,3 +449,113 @@ def chunk_backward(regression, q, k, v, dO, *, beta, lam, eps, chunk, beta_t=Non
     if S0 is not None:
         out["dS0"] = dS
     return out
+
+
+def masked_blocked(regression, q, k, v, *, beta, lam, eps, beta_t=None, k_prev=None, S0=None,
+                   same_step=False, rnd=None):
+    """The masked-parallel form for one short call (L <= 64, window 1, gains shared
+    by the value rows) in the blocked shape the matrix-core masked kernel uses.
+
+    Steps t = 0..63 (padded steps: zero sample, eta = 0, a = 1), blocks of 16.
+    With D[t][s] = prod_{s<r<=t} a_r and d_t = D[t][-1]:
+      A[t][s] = eta_s D[t-1][s] (x_t . x_s)   (s < t; regression family)
+      (I + A) E = Y - diag(d_{t-1}) X S0^T     (E = Y for the inner-product family)
+      W[t][s] = eta_s D[t][s] (q_t . x_s)      (s <= t)
+      O = diag(d_t) Q S0^T + W E
+      S_L = d_63 S0 + E^T diag(eta_s D[63][s]) X
+    Every decay factor is a product of a's (no division): inside a block a running
+    product; across blocks  D[t-1][s] = suf_s * mid(k, b) * pin_t  with suf_s the
+    product over the rest of s's block, mid the products of the whole blocks in
+    between and pin_t the product over t's block before t (inclusive of t for W).
+    The solve is blocked: T_bb = (I + A_bb)^-1, E_b = T_bb (R_b - sum_{k<b} A_bk E_k).
+    ``rnd``: optional rounding applied to every product operand (precision study).
+    """
+    L, dk = q.shape
+    dv = v.shape[1]
+    N, NB = 64, 4
+    f = (lambda a: a) if rnd is None else rnd
+    X = np.zeros((N, dk))
+    Q = np.zeros((N, dk))
+    Y = np.zeros((N, dv))
+    s = 0 if same_step else 1
+    for t in range(L):
+        g = t - s
+        if g >= 0:
+            X[t] = k[g]
+        elif k_prev is not None:
+            X[t] = k_prev
+        Q[t] = q[t]
+        Y[t] = v[t]
+    fresh = (not same_step) and k_prev is None
+    n = np.sum(X * X, axis=1)
+    bt = np.full(N, beta if beta is not None else 0.0)
+    if beta_t is not None:
+        bt[:L] = beta_t
+    live = np.arange(N) < L
+    eta = np.zeros(N)
+    eta[live] = bt[live] / (eps + n[live])
+    if fresh:
+        eta[0] = 0.0
+    a = 1.0 - eta * lam
+    a[np.arange(N) >= L] = 1.0
+    if fresh:
+        a[0] = 1.0
+    G = f(X) @ f(X).T
+    P = f(Q) @ f(X).T
+    blk = np.arange(N) // 16
+    # in-block products: pin_x[t] = prod_{16 b(t) <= r < t} a_r, pin_i[t] includes a_t,
+    # suf[s] = prod_{s < r < 16 (b(s) + 1)} a_r, bp[b] = product of block b
+    pin_x = np.ones(N)
+    pin_i = np.ones(N)
+    suf = np.ones(N)
+    bp = np.ones(NB)
+    for b in range(NB):
+        run = 1.0
+        for t in range(16 * b, 16 * b + 16):
+            pin_x[t] = run
+            run *= a[t]
+            pin_i[t] = run
+        bp[b] = run
+        run = 1.0
+        for t in range(16 * b + 15, 16 * b - 1, -1):
+            suf[t] = run
+            run *= a[t]
+
+    def mid(kb, b):                 # product of the whole blocks strictly between
+        return np.prod(bp[kb + 1:b]) if b > kb + 1 else 1.0
+
+    def dec(t, s_, incl):           # D[t][s] (incl) or D[t-1][s]
+        if blk[t] == blk[s_]:
+            r = 1.0
+            for q_ in range(s_ + 1, t + (1 if incl else 0)):
+                r *= a[q_]
+            return r
+        return suf[s_] * mid(blk[s_], blk[t]) * (pin_i[t] if incl else pin_x[t])
+
+    A = np.zeros((N, N))
+    W = np.zeros((N, N))
+    for t in range(N):
+        for s_ in range(t + 1):
+            if s_ < t:
+                A[t, s_] = eta[s_] * dec(t, s_, False) * G[t, s_]
+            W[t, s_] = eta[s_] * dec(t, s_, True) * P[t, s_]
+    dprev = np.array([np.prod(bp[:blk[t]]) * pin_x[t] for t in range(N)])
+    dincl = np.array([np.prod(bp[:blk[t]]) * pin_i[t] for t in range(N)])
+    S0m = np.zeros((dv, dk)) if S0 is None else S0.astype(np.float64)
+    R = Y - (dprev[:, None] * (f(X) @ f(S0m).T) if regression else 0.0)
+    if regression:
+        E = np.zeros((N, dv))
+        for b in range(NB):
+            sl = slice(16 * b, 16 * b + 16)
+            Tbb = np.linalg.inv(np.eye(16) + A[sl, sl])
+            acc = R[sl].copy()
+            for kb in range(b):
+                sk = slice(16 * kb, 16 * kb + 16)
+                acc -= f(A[sl, sk]) @ f(E[sk])
+            E[sl] = f(Tbb) @ f(acc)
+    else:
+        E = Y
+    O = dincl[:, None] * (f(Q) @ f(S0m).T) + f(W) @ f(E)
+    c = eta * suf * np.array([np.prod(bp[blk[s_] + 1:]) for s_ in range(N)])
+    S_L = np.prod(bp) * S0m + (f(E * c[:, None])).T @ f(X)
+    return O[:L], S_L

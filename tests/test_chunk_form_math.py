@@ -8,7 +8,8 @@ import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import seq_inputs
-from chunk_form_model import chunk_backward, chunk_forward, chunk_forward_folded, chunk_forward_wy
+from chunk_form_model import (chunk_backward, chunk_forward, chunk_forward_folded, chunk_forward_wy,
+                              masked_blocked)
 
 pytestmark = pytest.mark.cpu
 
@@ -101,3 +102,35 @@ def test_chunk_backward_equals_oracle_backward(variant, chunk, carried, same_ste
     for name in ref:
         np.testing.assert_allclose(got[name], ref[name][0, 0], rtol=1e-8, atol=1e-9,
                                    err_msg=name)
+
+
+@pytest.mark.parametrize("variant", [fo.FALCON_1, fo.FALCON_1A])
+@pytest.mark.parametrize("L", [1, 16, 37, 64])
+@pytest.mark.parametrize("case", ["plain", "carried", "same_step", "nlms", "strong", "negative"])
+def test_masked_blocked_form_equals_recurrence(variant, L, case):
+    """The blocked masked system of the matrix-core masked kernel (window 1, shared
+    gains): decay factors as products only, 16-step blocks, T_bb = (I + A_bb)^-1 and
+    the block forward substitution; fresh and carried calls, both pairings, exact
+    NLMS (lambda = eps = 0, beta = 1), forgetting far past the chunk algebra's range
+    and decays below zero."""
+    carried = case in ("carried", "nlms", "strong", "negative")
+    same_step = case == "same_step"
+    beta, lam, eps = {"nlms": (1.0, 0.0, 0.0), "strong": (0.99, 1.0, 1e-6),
+                      "negative": (0.5, 3.0, 1e-6)}.get(case, (None, 0.02, 1e-6))
+    inp = seq_inputs(1, 1, L, 8, 5, seed=1200 + 7 * variant + L, dtype="bf16",
+                     beta_per_token=beta is None, with_k_prev=carried and not same_step,
+                     with_S0=carried, s_std=0.3)
+    bt = inp["beta_t"] if beta is None else None
+    kw = dict(beta=beta, lam=lam, eps=eps, window=1, beta_t=bt,
+              k_prev=inp.get("k_prev") if carried else None,
+              S0=inp.get("S0") if carried else None, same_step=same_step)
+    o_ref, S_ref, _ = fo.falcon_recurrence(variant, inp["q"], inp["k"], inp["v"], **kw)
+    o, S = masked_blocked(fo.is_regression(variant), inp["q"][0, 0], inp["k"][0, 0],
+                          inp["v"][0, 0], beta=beta, lam=lam, eps=eps,
+                          beta_t=None if bt is None else bt[0, 0],
+                          k_prev=inp["k_prev"][0, 0] if carried else None,
+                          S0=inp["S0"][0, 0] if carried else None, same_step=same_step)
+    scale_o = max(np.max(np.abs(o_ref)), 1e-300)
+    scale_s = max(np.max(np.abs(S_ref)), 1e-300)
+    np.testing.assert_allclose(o / scale_o, o_ref[0, 0] / scale_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S / scale_s, S_ref[0, 0] / scale_s, rtol=0, atol=1e-12)

@@ -34,6 +34,7 @@
 
 #include "falcon_device.h"
 #include "falcon_launch.h"
+#include "falcon_mma.h"
 
 namespace falcon {
 namespace {
@@ -366,6 +367,659 @@ __global__ __launch_bounds__(1024) void masked_kernel(SeqArgs a, int rb) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Window 1 with gains shared by the value rows (Falcon-1/1A, and Falcon-2/2A,
+// Falcon-3/3A called with window 1 and a scalar or per-token beta): every value
+// row sees the same masked system, so it is solved once for all of them on the
+// matrix cores.  Steps t = 0..63 (steps past L: zero sample, eta = 0, a = 1),
+// D[t][s] = prod_{s<r<=t} a_r, d_t = prod_{r<=t} a_r (d_{-1} = 1):
+//   A[t][s] = eta_s D[t-1][s] (x_t . x_s)   (s < t)
+//   (I + A) E = Y - diag(d_{t-1}) X S0^T     (regression; E = Y for the
+//                                             inner-product family)
+//   W[t][s] = eta_s D[t][s] (q_t . x_s)      (s <= t)
+//   O = diag(d_t) Q S0^T + W E
+//   S_L = d_63 S0 + E^T diag(eta_s D[63][s]) X
+// (the same unrolling of the recurrence as above, written as matrices).  Every
+// decay factor is a product of decays, never a quotient: inside a 16-step block
+// D comes from a running product; across blocks it factors as
+// D[t-1][s] = suf_s mid(k, b) pin_t, with suf_s the product over the rest of
+// s's block k, mid the products of the whole blocks strictly between k and b,
+// and pin_t the product over t's block b before t (up to t itself for W), so
+// strong forgetting stays exact here too.  The solve is blocked:
+// T_bb = (I + A_bb)^-1 by a DPP forward substitution, then
+// E_b = T_bb (R_b - sum_{k<b} A_bk E_k) on the matrix cores, split-bf16
+// (Henry, Tang & Heinecke, ARITH 2019) for every operand that is not an exact
+// bf16 input.
+//
+// Work decomposition: one workgroup (4 waves, about 37 KB of LDS at dk = 64, so
+// four workgroups share a compute unit) per (chain, block of <= 64 value rows);
+// phases separated by barriers: (0) every global read issued at once
+// (samples, queries and squared norms to LDS; the lane's values and start-state
+// row to registers), (1) per-step scalars and block products | the Gram and
+// key-query tiles, kept in registers in the layout of the operand fragments
+// they become | X S0^T and Q S0^T, (2) the diagonal blocks of T | the -A and W
+// fragments, (3) each wave solves and reads out its 16 value rows, then forms
+// its rows of the final state.
+constexpr int kWyThreads = 256;
+
+template <int DK, bool F32IN>
+struct MaskedWyLds {
+  // bf16 inputs: samples and queries as bf16 (exact; product depth padded to the
+  // MFMA K of 32); fp32 inputs: as fp32, for exact products on the fp32 matrix cores
+  using XE = std::conditional_t<F32IN, float, uint16_t>;
+  static constexpr int KP = F32IN ? DK : (DK < 32 ? 32 : DK);
+  static constexpr int XR = F32IN ? DK + 4 : KP + 8;   // row over the features
+  static constexpr int FR = 32;                         // bf16 row of an operand fragment
+  XE X[64][XR];                     // samples, K-contiguous
+  union {
+    XE Q[64][XR];                   // queries (until phase 1 ends)
+    struct {
+      uint16_t Ah[4][16][FR], Al[4][16][FR];   // -A fragments by (block, pair of blocks)
+      uint16_t Wh[6][16][FR], Wl[6][16][FR];   // W fragments
+    } f;
+  };
+  union {
+    float Gd[4][16][20];            // diagonal 16 x 16 tiles of X X^T, [b][t][s]
+    float Acol[4][16][20];          // columns of the diagonal blocks of A, [b][s][t]
+    float TS[4][16][20];            // diagonal blocks of (I + A)^-1, [b][r][n]
+  };
+  float nrm[64], bet[64];
+  alignas(16) float eta[64];
+  alignas(16) float dec[64];
+  alignas(16) float pinx[64];       // product over the block before t
+  alignas(16) float pini[64];       // the same up to t
+  alignas(16) float suf[64];        // product over the block after t
+  float bpre[5], bsuf[4], mid[4][4];
+};
+
+template <int N>
+__device__ __forceinline__ float wy_shr(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             0x110 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float wy_shl(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
+                                                             0x100 + N, 0xF, 0xF, false));
+}
+// acc + g(lane N of this 16-lane row) * r (g is loaded from LDS, never written
+// by the vector ALU, so the DPP read needs no wait states)
+template <int N>
+__device__ __forceinline__ float wy_fmac_bcast(float acc, float g, float r) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(g), "v"(r), "i"(N));
+  return acc;
+}
+// column n (this lane) of (I + A_bb)^-1: x_p = [p == n] - sum_{q<p} A[p][q] x_q,
+// with A[.][q] held by lane q of the 16-lane row in g[]
+template <int P>
+__device__ __forceinline__ void wy_sweep(float (&x)[16], float (&acc)[16], const float (&g)[16]) {
+  x[P] -= acc[P];
+#pragma unroll
+  for (int r = P + 1; r < 16; ++r) acc[r] = wy_fmac_bcast<P>(acc[r], g[r], x[P]);
+  if constexpr (P < 15) wy_sweep<P + 1>(x, acc, g);
+}
+__device__ __forceinline__ floatx4 wy_mma3(floatx4 acc, const HL& a, const HL& b) {
+  acc = mfma16(a.hi, b.lo, acc);
+  acc = mfma16(a.lo, b.hi, acc);
+  return mfma16(a.hi, b.hi, acc);
+}
+__device__ __forceinline__ floatx4 wy_mma2(floatx4 acc, const bf16x8& a, const HL& b) {
+  acc = mfma16(a, b.hi, acc);
+  return mfma16(a, b.lo, acc);
+}
+// 4 values in slots 0-3 and 4 in slots 4-7 as one split fragment
+__device__ __forceinline__ HL wy_hl(const float* a, const float* b) {
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return hl_vals(v);
+}
+// 8 consecutive input elements as fp32 (16-byte aligned for bf16, 32 for fp32)
+template <bool F32IN>
+__device__ __forceinline__ void wy_load8(const void* p, long i, float (&v)[8]) {
+  if constexpr (F32IN) {
+    const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 y = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+}
+// 8 exact bf16 values to an LDS row
+__device__ __forceinline__ void wy_put8(uint16_t* row, const float (&v)[8]) {
+  uint32_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+  *reinterpret_cast<uint4*>(row) = make_uint4(h[0], h[1], h[2], h[3]);
+}
+// 8 fp32 values as three bf16 fragments whose sum is the value to 2^-24
+// (an exact bf16 operand times the three pieces: an fp32-exact product)
+struct Split3 {
+  bf16x8 p[3];
+};
+__device__ __forceinline__ Split3 wy_split3(const float (&v)[8]) {
+  uint32_t w[3][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float r0 = v[2 * e], r1 = v[2 * e + 1];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const uint32_t h = pack_bf16x2(r0, r1);
+      w[k][e] = h;
+      r0 -= __uint_as_float(h << 16);
+      r1 -= __uint_as_float(h & 0xffff0000u);
+    }
+  }
+  Split3 s;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) s.p[k] = __builtin_bit_cast(bf16x8, make_uint4(w[k][0], w[k][1], w[k][2], w[k][3]));
+  return s;
+}
+
+// HS0: the call carries a start state (its terms cost registers, so a fresh
+// call, which has none, runs at a higher occupancy)
+template <int DK, bool RG, bool F32IN, bool HS0>
+__global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqArgs a, int rb) {
+  using SM = MaskedWyLds<DK, F32IN>;
+  constexpr int KP = SM::KP, NKS = KP / 32, NCT = DK / 16, C8 = DK / 8;
+  constexpr int IT = (64 * C8 + kWyThreads - 1) / kWyThreads;   // 8-element pieces per thread
+  __shared__ __align__(16) SM sm;
+  const int L = a.seqlen;                    // 1..64
+  const int dv = a.dv;
+  const int chain = blockIdx.x;
+  const int row0 = blockIdx.y * rb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int ks = a.key_shift;
+  const bool fresh = ks == 1 && a.k_prev == nullptr;
+  constexpr bool has_s0 = HS0;
+  const long qk_base = (long)chain * L * DK;
+  const long v_base = (long)chain * L * dv;
+  const bool solver = wave < rb / 16;        // wave w owns value rows 16 w .. 16 w + 15
+  const int col = row0 + 16 * wave + lr;     // the lane's value row (solver waves)
+
+  // ---- phase 0: every global read is issued before any is used: the lane's
+  // values (rows 16 b + 4 lg + e) and start-state row go to registers; samples
+  // (x_t = k_{t-ks}, x_0 = k_prev or 0 under the prefix pairing) and queries to
+  // LDS, with the samples' squared norms
+  float yv[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * b + 4 * lg + e;
+      yv[b][e] = (solver && t < L) ? ld_elem(a.v, v_base + (long)t * dv + col, !F32IN) : 0.0f;
+    }
+  float xv[IT][8], qv[IT][8];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + kWyThreads * it;
+    const int t = idx / C8, c0 = 8 * (idx % C8);
+    const int g = t - ks;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[it][e] = qv[it][e] = 0.0f;
+    if (idx < 64 * C8 && t < L) {
+      if (g >= 0) wy_load8<F32IN>(a.k, qk_base + (long)g * DK + c0, xv[it]);
+      else if (a.k_prev) wy_load8<F32IN>(a.k_prev, (long)chain * DK + c0, xv[it]);
+      wy_load8<F32IN>(a.q, qk_base + (long)t * DK + c0, qv[it]);
+    }
+  }
+  // start-state row of the lane (fp32 inputs: 4 features per 16-wide K block;
+  // bf16 inputs: 8 per 32-wide K step, in three bf16 pieces)
+  float4 s0v[F32IN ? DK / 16 : 1];
+  float s08[F32IN ? 1 : NKS][8];
+  if constexpr (F32IN) {
+#pragma unroll
+    for (int kq = 0; kq < DK / 16; ++kq)
+      s0v[kq] = (solver && has_s0) ? *reinterpret_cast<const float4*>(a.S0 + ((long)chain * dv + col) * DK + 16 * kq + 4 * lg)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s08[kk][e] = 0.0f;
+      if (solver && has_s0 && 32 * kk + 8 * lg < DK) {
+        const float* sr = a.S0 + ((long)chain * dv + col) * DK + 32 * kk + 8 * lg;
+        const float4 u = *reinterpret_cast<const float4*>(sr);
+        const float4 w = *reinterpret_cast<const float4*>(sr + 4);
+        s08[kk][0] = u.x; s08[kk][1] = u.y; s08[kk][2] = u.z; s08[kk][3] = u.w;
+        s08[kk][4] = w.x; s08[kk][5] = w.y; s08[kk][6] = w.z; s08[kk][7] = w.w;
+      }
+    }
+  }
+  if (tid < 64) sm.bet[tid] = (a.beta_kind == 1 && tid < L) ? ld_elem(a.beta_t, (long)chain * L + tid, !F32IN) : a.beta;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = tid + kWyThreads * it;
+    if (idx < 64 * C8) {
+      const int t = idx / C8, c0 = 8 * (idx % C8);
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          *reinterpret_cast<float4*>(&sm.X[t][c0 + 4 * h]) =
+              make_float4(xv[it][4 * h], xv[it][4 * h + 1], xv[it][4 * h + 2], xv[it][4 * h + 3]);
+          *reinterpret_cast<float4*>(&sm.Q[t][c0 + 4 * h]) =
+              make_float4(qv[it][4 * h], qv[it][4 * h + 1], qv[it][4 * h + 2], qv[it][4 * h + 3]);
+        }
+      } else {
+        wy_put8(&sm.X[t][c0], xv[it]);
+        wy_put8(&sm.Q[t][c0], qv[it]);
+      }
+      float n = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) n = __builtin_fmaf(xv[it][e], xv[it][e], n);
+      n = group_sum<C8>(n);
+      if (idx % C8 == 0) sm.nrm[t] = n;
+    }
+  }
+  if constexpr (DK < KP) {                   // zero the padding of the product depth (bf16)
+    for (int t = tid; t < 64; t += kWyThreads)
+      for (int c = DK; c < KP; c += 8) {
+        *reinterpret_cast<uint4*>(&sm.X[t][c]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sm.Q[t][c]) = make_uint4(0u, 0u, 0u, 0u);
+      }
+  }
+  __syncthreads();
+
+  // ---- phase 1: every dot product, exact up to fp32 accumulation (these are
+  // the sums that may cancel).  Wave 0: per-step scalars (lane = step) and the
+  // diagonal Gram tiles; waves 1-3: the Gram and key-query tiles of their
+  // operand fragments, kept in registers (tile (kb, b) in the layout of the
+  // matrix-core result holds on lane (lg, lr) the values of steps 16 kb + 4 lg + e
+  // for row 16 b + lr: the lane's own fragment slots); solver waves: X S0^T and
+  // Q S0^T of their value rows
+  // tile product: rows 16 kb + 4 lg + e of X against rows 16 b + lr of X (or Q)
+  auto tile = [&](int kb, int b, bool withq) __attribute__((always_inline)) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const auto* ar = &sm.X[16 * kb + lr][0];
+    const auto* br = withq ? &sm.Q[16 * b + lr][0] : &sm.X[16 * b + lr][0];
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int kq = 0; kq < DK; kq += 16)
+        acc = mfma_f32x4(*reinterpret_cast<const float4*>(ar + kq + 4 * lg),
+                         *reinterpret_cast<const float4*>(br + kq + 4 * lg), acc);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) acc = mfma16(frag_bf16(ar + 32 * kk + 8 * lg), frag_bf16(br + 32 * kk + 8 * lg), acc);
+    }
+    return acc;
+  };
+  // fragment jobs: wave 1 the -A fragments (b, p) = (1,0) (2,0) (3,0) (3,1);
+  // wave 2 the W fragments (0,0) (1,0) (2,0), wave 3 (2,1) (3,0) (3,1)
+  floatx4 tl[3][2];
+#pragma unroll
+  for (int fi = 0; fi < 3; ++fi)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tl[fi][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto frag_bp = [&](int w, int fi, int& f, int& b, int& p) __attribute__((always_inline)) {
+    if (w == 1) {
+      f = fi;
+      b = f == 0 ? 1 : f == 1 ? 2 : 3;
+      p = f == 3 ? 1 : 0;
+    } else {
+      f = 3 * (w - 2) + fi;
+      b = f == 0 ? 0 : f == 1 ? 1 : f <= 3 ? 2 : 3;
+      p = (f == 3 || f == 5) ? 1 : 0;
+    }
+  };
+  if (wave == 0) {
+    const int t = lane;
+    float eta = 0.0f, dec = 1.0f;
+    if (t < L && !(t == 0 && fresh)) {
+      eta = sm.bet[t] / (a.eps + sm.nrm[t]);
+      dec = 1.0f - eta * a.lambda;
+    }
+    float pi = dec;                          // inclusive products within the 16-step block
+    pi *= wy_shr<1>(pi, 1.0f);
+    pi *= wy_shr<2>(pi, 1.0f);
+    pi *= wy_shr<4>(pi, 1.0f);
+    pi *= wy_shr<8>(pi, 1.0f);
+    float su = dec;                          // inclusive products to the end of the block
+    su *= wy_shl<1>(su, 1.0f);
+    su *= wy_shl<2>(su, 1.0f);
+    su *= wy_shl<4>(su, 1.0f);
+    su *= wy_shl<8>(su, 1.0f);
+    sm.eta[t] = eta;
+    sm.dec[t] = dec;
+    sm.pinx[t] = wy_shr<1>(pi, 1.0f);
+    sm.pini[t] = pi;
+    sm.suf[t] = wy_shl<1>(su, 1.0f);
+    float bp[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bp[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pi), 16 * b + 15));
+    if (lane == 0) {
+      sm.bpre[0] = 1.0f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sm.bpre[b + 1] = sm.bpre[b] * bp[b];
+      float s = 1.0f;
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        sm.bsuf[b] = s;
+        s *= bp[b];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float m = 1.0f;
+#pragma unroll
+        for (int b = k + 1; b < 4; ++b) {
+          sm.mid[k][b] = m;
+          m *= bp[b];
+        }
+      }
+    }
+    if constexpr (RG) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const floatx4 g4 = tile(b, b, false);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Gd[b][4 * lg + e][lr] = g4[e];
+      }
+    }
+  } else if (RG || wave >= 2) {
+#pragma unroll
+    for (int fi = 0; fi < 3; ++fi) {
+      int f, b, p;
+      frag_bp(wave, fi, f, b, p);
+      if (wave == 1 && fi == 2) {            // wave 1 holds four fragments: (3,0) and (3,1)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tl[2][h] = tile(h, 3, false);
+        break;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * p + h;
+        if (wave == 1 ? kb < b : kb <= b) tl[fi][h] = tile(kb, b, wave != 1);
+      }
+    }
+  }
+  floatx4 tl3 = {0.f, 0.f, 0.f, 0.f};        // wave 1: G tile (2, 3) of fragment (3,1)
+  if (RG && wave == 1) tl3 = tile(2, 3, false);
+  floatx4 xs0[4], qs0[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    xs0[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    qs0[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (solver && has_s0) {
+    if constexpr (F32IN) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int kq = 0; kq < DK / 16; ++kq) {
+          const int c = 16 * kq + 4 * lg;
+          if constexpr (RG) xs0[b] = mfma_f32x4(*reinterpret_cast<const float4*>(&sm.X[16 * b + lr][c]), s0v[kq], xs0[b]);
+          qs0[b] = mfma_f32x4(*reinterpret_cast<const float4*>(&sm.Q[16 * b + lr][c]), s0v[kq], qs0[b]);
+        }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk) {
+        const Split3 s3 = wy_split3(s08[kk]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = 32 * kk + 8 * lg;
+          const bf16x8 xf = frag_bf16(&sm.X[16 * b + lr][c]);
+          const bf16x8 qf = frag_bf16(&sm.Q[16 * b + lr][c]);
+#pragma unroll
+          for (int k = 2; k >= 0; --k) {     // smallest piece first
+            if constexpr (RG) xs0[b] = mfma16(xf, s3.p[k], xs0[b]);
+            qs0[b] = mfma16(qf, s3.p[k], qs0[b]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: diagonal blocks of T (wave 0: 16-lane row b = block b, lane n
+  // = column n); the -A and W operand fragments (waves 1-3) from the tiles in
+  // registers.  Fragment (b, pair p): row t = 16 b + lr, slots 0-3 the steps
+  // 32 p + 4 lg + 0..3, slots 4-7 the steps 32 p + 16 + 4 lg + 0..3 (zero where
+  // the block is not coupled)
+  if (wave == 0) {
+    if constexpr (RG) {
+      const int b = lg, n = lr, s = 16 * b + n;
+      const float es = sm.eta[s];
+      float gv[16], dq[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.Gd[b][n][4 * q4]);   // G[s][16 b + r] (G symmetric)
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dec[16 * b + 4 * q4]);
+        gv[4 * q4] = g4.x; gv[4 * q4 + 1] = g4.y; gv[4 * q4 + 2] = g4.z; gv[4 * q4 + 3] = g4.w;
+        dq[4 * q4] = d4.x; dq[4 * q4 + 1] = d4.y; dq[4 * q4 + 2] = d4.z; dq[4 * q4 + 3] = d4.w;
+      }
+      float colv[16], run = 1.0f;            // A[16 b + r][s] = eta_s D[16 b + r - 1][s]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        colv[r] = 0.0f;
+        if (r > n) {
+          colv[r] = es * run * gv[r];
+          run *= dq[r];
+        }
+      }
+      wave_sync();                           // every lane has read Gd before Acol overwrites it
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(&sm.Acol[b][n][4 * q4]) =
+            make_float4(colv[4 * q4], colv[4 * q4 + 1], colv[4 * q4 + 2], colv[4 * q4 + 3]);
+      wave_sync();
+      float g[16], x[16], acc[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.Acol[b][n][4 * q4]);
+        g[4 * q4] = g4.x; g[4 * q4 + 1] = g4.y; g[4 * q4 + 2] = g4.z; g[4 * q4 + 3] = g4.w;
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        x[m] = m == n ? 1.0f : 0.0f;
+        acc[m] = 0.0f;
+      }
+      wave_sync();                           // every lane has read Acol before TS overwrites it
+      wy_sweep<0>(x, acc, g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.TS[b][r][n] = x[r];
+    }
+  } else if (RG || wave >= 2) {
+    const int nf = wave == 1 ? 4 : 3;
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi) {
+      if (fi >= nf) break;
+      int f, b, p;
+      frag_bp(wave, fi, f, b, p);
+      const int t = 16 * b + lr;
+      float v[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * p + h;
+        const floatx4 tv = fi == 3 ? (h == 0 ? tl3 : floatx4{0.f, 0.f, 0.f, 0.f})
+                                   : (fi == 2 && wave == 1 ? (h == 0 ? tl[2][0] : tl[2][1]) : tl[fi][h]);
+        if (wave == 1) {                     // -A[t][s] = -eta_s D[t-1][s] G[t][s], blocks kb < b
+          if (kb < b) {
+            const float sc = -sm.pinx[t] * sm.mid[kb][b];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int s = 16 * kb + 4 * lg + e;
+              v[4 * h + e] = sc * sm.eta[s] * sm.suf[s] * tv[e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * h + e] = 0.0f;
+          }
+        } else {                             // W[t][s] = eta_s D[t][s] P[t][s], s <= t
+          if (kb < b) {
+            const float sc = sm.pini[t] * sm.mid[kb][b];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int s = 16 * kb + 4 * lg + e;
+              v[4 * h + e] = sc * sm.eta[s] * sm.suf[s] * tv[e];
+            }
+          } else if (kb == b) {
+            // D[t][s] = prod_{s<q<=t} a_q for the four steps s = 16 b + 4 lg + e <= t
+            float dq[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const float4 d4 = *reinterpret_cast<const float4*>(&sm.dec[16 * b + 4 * q4]);
+              dq[4 * q4] = d4.x; dq[4 * q4 + 1] = d4.y; dq[4 * q4 + 2] = d4.z; dq[4 * q4 + 3] = d4.w;
+            }
+            float dd = 1.0f;                 // D[t][16 b + 4 lg + 3]
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+              if (q > 4 * lg + 3 && q <= lr) dd *= dq[q];
+            // D[t][s] = D[t][s+1] a_{s+1} while s + 1 <= t; D[t][t] = 1
+            float dcur[4];
+            dcur[3] = dd;
+#pragma unroll
+            for (int e = 2; e >= 0; --e) dcur[e] = 4 * lg + e + 1 <= lr ? dcur[e + 1] * dq[4 * lg + e + 1] : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int sl = 4 * lg + e;
+              v[4 * h + e] = sl <= lr ? sm.eta[16 * b + sl] * dcur[e] * tv[e] : 0.0f;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * h + e] = 0.0f;
+          }
+        }
+      }
+      uint16_t* fh = wave == 1 ? &sm.f.Ah[f][lr][8 * lg] : &sm.f.Wh[f][lr][8 * lg];
+      uint16_t* fl = wave == 1 ? &sm.f.Al[f][lr][8 * lg] : &sm.f.Wl[f][lr][8 * lg];
+      store_split4(fh, fl, v);
+      store_split4(fh + 4, fl + 4, v + 4);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: solve, readout and final state of the wave's 16 value rows
+  if (!solver) return;
+  const floatx4 zacc = {0.f, 0.f, 0.f, 0.f};
+  const float z4[4] = {0.f, 0.f, 0.f, 0.f};
+  floatx4 E[4];
+  HL Eop[2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    floatx4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * b + 4 * lg + e;
+      acc[e] = yv[b][e];
+      if (RG && has_s0) acc[e] = __builtin_fmaf(-sm.bpre[b] * sm.pinx[t], xs0[b][e], acc[e]);
+    }
+    if constexpr (RG) {
+#pragma unroll
+      for (int p = 0; 2 * p < b; ++p) {
+        const int f = b == 1 ? 0 : b == 2 ? 1 : (p == 0 ? 2 : 3);
+        acc = wy_mma3(acc, hl_pair(&sm.f.Ah[f][lr][8 * lg], &sm.f.Al[f][lr][8 * lg]), Eop[p]);
+      }
+      const float4 t4 = *reinterpret_cast<const float4*>(&sm.TS[b][lr][4 * lg]);
+      const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+      const float av[4] = {acc[0], acc[1], acc[2], acc[3]};
+      E[b] = wy_mma3(zacc, wy_hl(tv, z4), wy_hl(av, z4));
+    } else {
+      E[b] = acc;
+    }
+    if (b & 1) {
+      const float lo4[4] = {E[b - 1][0], E[b - 1][1], E[b - 1][2], E[b - 1][3]};
+      const float hi4[4] = {E[b][0], E[b][1], E[b][2], E[b][3]};
+      Eop[b >> 1] = wy_hl(lo4, hi4);
+    } else {
+      const float lo4[4] = {E[b][0], E[b][1], E[b][2], E[b][3]};
+      Eop[b >> 1] = wy_hl(lo4, z4);
+    }
+  }
+  // o_t = d_t (Q S0^T)_t + (W E)_t
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    floatx4 o = zacc;
+    if (has_s0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = sm.bpre[b] * sm.pini[16 * b + 4 * lg + e] * qs0[b][e];
+    }
+#pragma unroll
+    for (int p = 0; 2 * p <= b; ++p) {
+      const int f = b == 0 ? 0 : b == 1 ? 1 : b == 2 ? 2 + p : 4 + p;
+      o = wy_mma3(o, hl_pair(&sm.f.Wh[f][lr][8 * lg], &sm.f.Wl[f][lr][8 * lg]), Eop[p]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * b + 4 * lg + e;
+      if (t < L) a.o[v_base + (long)t * dv + col] = o[e];
+    }
+  }
+  if (a.S_out == nullptr) return;
+  // S_L^T tile (16 features x 16 value rows) = d_63 S0^T + X^T diag(c) E,
+  // c_s = eta_s D[63][s] = eta_s suf_s (products of the later blocks); the
+  // operand X^T is read column-wise from the row-major samples
+  HL ec[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = 2 * p + h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * b + 4 * lg + e;
+        v[4 * h + e] = E[b][e] * (sm.eta[s] * sm.suf[s] * sm.bsuf[b]);
+      }
+    }
+    ec[p] = hl_vals(v);
+  }
+  const float dL = sm.bpre[4];
+  float* srow = a.S_out + ((long)chain * dv + col) * DK;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    floatx4 acc = zacc;
+    if (has_s0) {
+      const float4 s4 = *reinterpret_cast<const float4*>(a.S0 + ((long)chain * dv + col) * DK + 16 * ct + 4 * lg);
+      acc = floatx4{dL * s4.x, dL * s4.y, dL * s4.z, dL * s4.w};
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = 16 * ct + lr;
+      if constexpr (F32IN) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = sm.X[32 * p + 16 * (j >> 2) + 4 * lg + (j & 3)][c];
+        acc = wy_mma3(acc, hl_vals(v), ec[p]);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s0 = 32 * p + 16 * (j >> 1) + 4 * lg + 2 * (j & 1);
+          w[j] = (uint32_t)sm.X[s0][c] | ((uint32_t)sm.X[s0 + 1][c] << 16);
+        }
+        acc = wy_mma2(acc, __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3])), ec[p]);
+      }
+    }
+    *reinterpret_cast<float4*>(srow + 16 * ct + 4 * lg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
+template <int DK, bool F32IN, bool HS0>
+hipError_t launch_wy_s0(const SeqArgs& a, hipStream_t stream) {
+  const int rb = a.dv < kMaskedMaxRows ? a.dv : kMaskedMaxRows;
+  const dim3 grid((unsigned)(a.batch * a.heads), (unsigned)(a.dv / rb));
+  if (a.regression)
+    hipLaunchKernelGGL((masked_wy_kernel<DK, true, F32IN, HS0>), grid, dim3(kWyThreads), 0, stream, a, rb);
+  else
+    hipLaunchKernelGGL((masked_wy_kernel<DK, false, F32IN, HS0>), grid, dim3(kWyThreads), 0, stream, a, rb);
+  return hipGetLastError();
+}
+
+template <int DK, bool F32IN>
+hipError_t launch_wy_dt(const SeqArgs& a, hipStream_t stream) {
+  return a.S0 ? launch_wy_s0<DK, F32IN, true>(a, stream) : launch_wy_s0<DK, F32IN, false>(a, stream);
+}
+
+template <int DK>
+hipError_t launch_wy(const SeqArgs& a, hipStream_t stream) {
+  return a.dtype == 0 ? launch_wy_dt<DK, false>(a, stream) : launch_wy_dt<DK, true>(a, stream);
+}
+
 template <int DKM, int BW>
 hipError_t launch_bw(const SeqArgs& a, hipStream_t stream) {
   const int rb = a.dv < kMaskedMaxRows ? a.dv : kMaskedMaxRows;
@@ -397,6 +1051,15 @@ hipError_t launch_dkm(const SeqArgs& a, hipStream_t stream) {
 hipError_t launch_masked(const SeqArgs& a, hipStream_t stream) {
   (void)hipGetLastError();
   if (a.seqlen < 1 || a.seqlen > kMaskedMaxL || a.window < 1 || a.window > 8) return hipErrorInvalidValue;
+  if (a.window == 1 && a.beta_kind != 2) {   // one system shared by every value row
+    switch (a.dk) {
+      case 16: return launch_wy<16>(a, stream);
+      case 32: return launch_wy<32>(a, stream);
+      case 64: return launch_wy<64>(a, stream);
+      case 128: return launch_wy<128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.dk <= 64) return launch_dkm<64>(a, stream);
   return launch_dkm<128>(a, stream);
 }
