@@ -393,13 +393,13 @@ __global__ __launch_bounds__(1024) void masked_kernel(SeqArgs a, int rb) {
 //
 // Work decomposition: one workgroup (4 waves, about 37 KB of LDS at dk = 64, so
 // four workgroups share a compute unit) per (chain, block of <= 64 value rows);
-// phases separated by barriers: (0) every global read issued at once
-// (samples, queries and squared norms to LDS; the lane's values and start-state
-// row to registers), (1) per-step scalars and block products | the Gram and
-// key-query tiles, kept in registers in the layout of the operand fragments
-// they become | X S0^T and Q S0^T, (2) the diagonal blocks of T | the -A and W
-// fragments, (3) each wave solves and reads out its 16 value rows, then forms
-// its rows of the final state.
+// phases separated by barriers: (0) every global read issued at once, as
+// 16-byte loads (samples, queries, values and squared norms to LDS; the
+// start-state row to registers), (1) per-step scalars and block products |
+// the Gram and key-query tiles, kept in registers in the layout of the operand
+// fragments they become | X S0^T and Q S0^T, (2) the diagonal blocks of T |
+// the -A and W fragments, (3) each wave solves and reads out its 16 value rows,
+// then forms its rows of the final state.
 constexpr int kWyThreads = 256;
 
 template <int DK, bool F32IN>
@@ -411,8 +411,13 @@ struct MaskedWyLds {
   static constexpr int XR = F32IN ? DK + 4 : KP + 8;   // row over the features
   static constexpr int FR = 32;                         // bf16 row of an operand fragment
   XE X[64][XR];                     // samples, K-contiguous
+  static constexpr int YR = F32IN ? 64 + 4 : 64 + 8;   // row over the value columns
   union {
-    XE Q[64][XR];                   // queries (until phase 1 ends)
+    struct {
+      XE Q[64][XR];                 // queries (until phase 1 ends)
+      XE Y[64][YR];                 // values of the workgroup's rows (read to registers
+                                    // at the start of phase 1)
+    } qy;
     struct {
       uint16_t Ah[4][16][FR], Al[4][16][FR];   // -A fragments by (block, pair of blocks)
       uint16_t Wh[6][16][FR], Wl[6][16][FR];   // W fragments
@@ -543,18 +548,21 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
   const bool solver = wave < rb / 16;        // wave w owns value rows 16 w .. 16 w + 15
   const int col = row0 + 16 * wave + lr;     // the lane's value row (solver waves)
 
-  // ---- phase 0: every global read is issued before any is used: the lane's
-  // values (rows 16 b + 4 lg + e) and start-state row go to registers; samples
-  // (x_t = k_{t-ks}, x_0 = k_prev or 0 under the prefix pairing) and queries to
-  // LDS, with the samples' squared norms
-  float yv[4][4];
+  // ---- phase 0: every global read is issued before any is used, as 16-byte
+  // loads: values, samples (x_t = k_{t-ks}, x_0 = k_prev or 0 under the prefix
+  // pairing) and queries go to LDS, with the samples' squared norms; the
+  // start-state row to registers
+  constexpr int IV = (64 * 8 + kWyThreads - 1) / kWyThreads;   // 8-value pieces per thread
+  const int npr = rb / 8;                    // pieces per row of values
+  float yl[IV][8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int it = 0; it < IV; ++it) {
+    const int idx = tid + kWyThreads * it;
+    const int t = idx / npr, c0 = 8 * (idx % npr);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * b + 4 * lg + e;
-      yv[b][e] = (solver && t < L) ? ld_elem(a.v, v_base + (long)t * dv + col, !F32IN) : 0.0f;
-    }
+    for (int e = 0; e < 8; ++e) yl[it][e] = 0.0f;
+    if (idx < 64 * npr && t < L) wy_load8<F32IN>(a.v, v_base + (long)t * dv + row0 + c0, yl[it]);
+  }
   float xv[IT][8], qv[IT][8];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -603,12 +611,12 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
         for (int h = 0; h < 2; ++h) {
           *reinterpret_cast<float4*>(&sm.X[t][c0 + 4 * h]) =
               make_float4(xv[it][4 * h], xv[it][4 * h + 1], xv[it][4 * h + 2], xv[it][4 * h + 3]);
-          *reinterpret_cast<float4*>(&sm.Q[t][c0 + 4 * h]) =
+          *reinterpret_cast<float4*>(&sm.qy.Q[t][c0 + 4 * h]) =
               make_float4(qv[it][4 * h], qv[it][4 * h + 1], qv[it][4 * h + 2], qv[it][4 * h + 3]);
         }
       } else {
         wy_put8(&sm.X[t][c0], xv[it]);
-        wy_put8(&sm.Q[t][c0], qv[it]);
+        wy_put8(&sm.qy.Q[t][c0], qv[it]);
       }
       float n = 0.0f;
 #pragma unroll
@@ -617,11 +625,26 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
       if (idx % C8 == 0) sm.nrm[t] = n;
     }
   }
+#pragma unroll
+  for (int it = 0; it < IV; ++it) {
+    const int idx = tid + kWyThreads * it;
+    if (idx < 64 * npr) {
+      const int t = idx / npr, c0 = 8 * (idx % npr);
+      if constexpr (F32IN) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<float4*>(&sm.qy.Y[t][c0 + 4 * h]) =
+              make_float4(yl[it][4 * h], yl[it][4 * h + 1], yl[it][4 * h + 2], yl[it][4 * h + 3]);
+      } else {
+        wy_put8(&sm.qy.Y[t][c0], yl[it]);
+      }
+    }
+  }
   if constexpr (DK < KP) {                   // zero the padding of the product depth (bf16)
     for (int t = tid; t < 64; t += kWyThreads)
       for (int c = DK; c < KP; c += 8) {
         *reinterpret_cast<uint4*>(&sm.X[t][c]) = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&sm.Q[t][c]) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&sm.qy.Q[t][c]) = make_uint4(0u, 0u, 0u, 0u);
       }
   }
   __syncthreads();
@@ -633,11 +656,22 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
   // matrix-core result holds on lane (lg, lr) the values of steps 16 kb + 4 lg + e
   // for row 16 b + lr: the lane's own fragment slots); solver waves: X S0^T and
   // Q S0^T of their value rows
+  float yv[4][4];                            // the lane's values, rows 16 b + 4 lg + e
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      yv[b][e] = 0.0f;
+      if (solver) {
+        if constexpr (F32IN) yv[b][e] = sm.qy.Y[16 * b + 4 * lg + e][16 * wave + lr];
+        else yv[b][e] = bf16_to_f32(sm.qy.Y[16 * b + 4 * lg + e][16 * wave + lr]);
+      }
+    }
   // tile product: rows 16 kb + 4 lg + e of X against rows 16 b + lr of X (or Q)
   auto tile = [&](int kb, int b, bool withq) __attribute__((always_inline)) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     const auto* ar = &sm.X[16 * kb + lr][0];
-    const auto* br = withq ? &sm.Q[16 * b + lr][0] : &sm.X[16 * b + lr][0];
+    const auto* br = withq ? &sm.qy.Q[16 * b + lr][0] : &sm.X[16 * b + lr][0];
     if constexpr (F32IN) {
 #pragma unroll
       for (int kq = 0; kq < DK; kq += 16)
@@ -753,7 +787,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
         for (int kq = 0; kq < DK / 16; ++kq) {
           const int c = 16 * kq + 4 * lg;
           if constexpr (RG) xs0[b] = mfma_f32x4(*reinterpret_cast<const float4*>(&sm.X[16 * b + lr][c]), s0v[kq], xs0[b]);
-          qs0[b] = mfma_f32x4(*reinterpret_cast<const float4*>(&sm.Q[16 * b + lr][c]), s0v[kq], qs0[b]);
+          qs0[b] = mfma_f32x4(*reinterpret_cast<const float4*>(&sm.qy.Q[16 * b + lr][c]), s0v[kq], qs0[b]);
         }
     } else {
 #pragma unroll
@@ -763,7 +797,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
         for (int b = 0; b < 4; ++b) {
           const int c = 32 * kk + 8 * lg;
           const bf16x8 xf = frag_bf16(&sm.X[16 * b + lr][c]);
-          const bf16x8 qf = frag_bf16(&sm.Q[16 * b + lr][c]);
+          const bf16x8 qf = frag_bf16(&sm.qy.Q[16 * b + lr][c]);
 #pragma unroll
           for (int k = 2; k >= 0; --k) {     // smallest piece first
             if constexpr (RG) xs0[b] = mfma16(xf, s3.p[k], xs0[b]);
