@@ -222,3 +222,33 @@ def test_masked_deterministic():
     b = _run(inp, fw.FALCON_3, "bf16", window=4, beta=None, lam=0.01, eps=1e-6, history=True)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_1A, fw.FALCON_3, fw.FALCON_3A])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(16, 32), (64, 64), (128, 128)])
+@pytest.mark.parametrize("L,same_step", [(23, False), (64, False), (64, True)])
+def test_masked_shared_gains_start_state(variant, dtype, dk, dv, L, same_step):
+    """Window 1 with gains shared by the value rows (the one-system matrix-core
+    path) and a live start state: both input types (fp32 inputs take their dot
+    products on the fp32 matrix cores), per-token gains, wide heads split over
+    two row blocks, both pairings, and the windowed variants called with window 1."""
+    inp = seq_inputs(2, 2, L, dk, dv, seed=1300 + 7 * variant + dk + L + same_step,
+                     dtype=dtype, with_k_prev=not same_step, with_S0=True, s_std=0.3,
+                     beta_per_token=True)
+    o, S = _run(inp, variant, dtype, window=1, beta=None, lam=0.02, eps=1e-6,
+                same_step=same_step)
+    o_ref, S_ref = _ref(inp, variant, window=1, beta=None, lam=0.02, eps=1e-6,
+                        same_step=same_step)
+    _check(o, S, o_ref, S_ref, label="v%d %s dk %d dv %d L %d same %d" % (
+        variant, dtype, dk, dv, L, same_step))
+
+
+def test_masked_shared_gains_deterministic():
+    """The one-system path twice on the same inputs: bit-identical outputs."""
+    inp = seq_inputs(4, 3, 64, 64, 128, seed=1400, dtype="bf16", with_k_prev=True,
+                     with_S0=True, beta_per_token=True)
+    a = _run(inp, fw.FALCON_1, "bf16", window=1, beta=None, lam=0.01, eps=1e-6)
+    b = _run(inp, fw.FALCON_1, "bf16", window=1, beta=None, lam=0.01, eps=1e-6)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
