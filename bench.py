@@ -367,7 +367,46 @@ def main():
             scratch = torch.empty(1 << 28, device=dev, dtype=torch.float32)
             stc = {}
             sec_cold = time_calls(step, 200, 5, between=lambda: scratch.fill_(1.0), stats=stc)
-            del scratch
+            # graph: a serving loop's form, `pool` steps captured once in a HIP graph
+            # and replayed, so the host launch path leaves the step.  Warm: steps
+            # back to back.  Cold: a graph with the 1 GiB fill before every step and
+            # a graph of the fills alone; the per-step difference is the step with
+            # its state evicted (the fill and the step run one after the other on
+            # one stream).
+            outs = torch.empty((pool, N, H, dv), device=dev, dtype=torch.float32)
+
+            def capture(with_step, with_fill):
+                g = torch.cuda.CUDAGraph()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    for p in range(pool):
+                        if with_fill:
+                            scratch.fill_(1.0)
+                        if with_step:
+                            fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=fw.FALCON_1,
+                                           beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"],
+                                           out=outs[p])
+                return g
+
+            def replay_time(g, reps):
+                for _ in range(2):
+                    g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / 1e3 / (reps * pool)
+
+            reps = max(1, args.decode_steps // pool)
+            g_warm = capture(True, False)
+            sec_gw = replay_time(g_warm, reps)
+            g_cold, g_fill = capture(True, True), capture(False, True)
+            creps = max(1, 200 // pool)
+            sec_gc = replay_time(g_cold, creps) - replay_time(g_fill, creps)
+            del g_warm, g_cold, g_fill, scratch, outs
             sec_out["decode"] = {"workload": "decode_512x12x64", "variant": "falcon1",
                                  "bytes_per_step": nb,
                                  "warm": {"steps": args.decode_steps, "us_per_step": sec * 1e6,
@@ -379,7 +418,13 @@ def main():
                                           "us_per_step": sec_cold * 1e6,
                                           "median_us": stc["median_s"] * 1e6,
                                           "total_gbs": nb / stc["median_s"] / 1e9,
-                                          "hbm_frac": nb / stc["median_s"] / 1e9 / HBM_PEAK_GBS}}
+                                          "hbm_frac": nb / stc["median_s"] / 1e9 / HBM_PEAK_GBS},
+                                 "graph": {"steps_per_graph": pool,
+                                           "warm_us_per_step": sec_gw * 1e6,
+                                           "warm_total_gbs": nb / sec_gw / 1e9,
+                                           "cold_us_per_step": sec_gc * 1e6,
+                                           "cold_total_gbs": nb / sec_gc / 1e9,
+                                           "cold_hbm_frac": nb / sec_gc / 1e9 / HBM_PEAK_GBS}}
             del S, qs, ks, vs
             torch.cuda.empty_cache()
         if args.only in (None, "copy"):

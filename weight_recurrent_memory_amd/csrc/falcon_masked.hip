@@ -755,15 +755,12 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
       }
     }
   } else if (RG || wave >= 2) {
+    // the -A fragments couple earlier blocks only (kb < b), the W fragments
+    // include the diagonal block (kb <= b)
 #pragma unroll
     for (int fi = 0; fi < 3; ++fi) {
       int f, b, p;
       frag_bp(wave, fi, f, b, p);
-      if (wave == 1 && fi == 2) {            // wave 1 holds four fragments: (3,0) and (3,1)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) tl[2][h] = tile(h, 3, false);
-        break;
-      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kb = 2 * p + h;
@@ -771,7 +768,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
       }
     }
   }
-  floatx4 tl3 = {0.f, 0.f, 0.f, 0.f};        // wave 1: G tile (2, 3) of fragment (3,1)
+  floatx4 tl3 = {0.f, 0.f, 0.f, 0.f};        // wave 1's fourth fragment (3,1): G tile (2, 3)
   if (RG && wave == 1) tl3 = tile(2, 3, false);
   floatx4 xs0[4], qs0[4];
 #pragma unroll
@@ -869,8 +866,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kb = 2 * p + h;
-        const floatx4 tv = fi == 3 ? (h == 0 ? tl3 : floatx4{0.f, 0.f, 0.f, 0.f})
-                                   : (fi == 2 && wave == 1 ? (h == 0 ? tl[2][0] : tl[2][1]) : tl[fi][h]);
+        const floatx4 tv = fi == 3 ? (h == 0 ? tl3 : floatx4{0.f, 0.f, 0.f, 0.f}) : tl[fi][h];
         if (wave == 1) {                     // -A[t][s] = -eta_s D[t-1][s] G[t][s], blocks kb < b
           if (kb < b) {
             const float sc = -sm.pinx[t] * sm.mid[kb][b];
