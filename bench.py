@@ -286,24 +286,21 @@ def main():
             torch.cuda.empty_cache()
         if args.only in (None, "masked"):
             # short sequences: the masked-parallel form (one masked system per call of
-            # 64 steps) and the chunk form on the same inputs
+            # 64 steps; falcon_fwd_chunk routes such calls to the same kernel)
             cfg = WORKLOADS["masked_256x12x64x64"]
             B, H, L, dk, dv = cfg["shape"]
             inp = seq_inputs(B, H, L, dk, dv, seed=cfg["seed"], dtype="bf16")
             q, k, v = (up(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
             o = torch.empty((B, H, L, dv), device=dev, dtype=torch.float32)
             kw = dict(variant=fw.FALCON_1, beta=cfg["beta"], lam=cfg["lam"], eps=cfg["eps"], out=o)
-            st, stc = {}, {}
+            st = {}
             sec = time_calls(lambda: fw.fwd_masked(q, k, v, **kw), 20, 3, stats=st)
-            sec_c = time_calls(lambda: fw.fwd_chunk(q, k, v, chunk=64, **kw), 20, 3, stats=stc)
             nbytes = algorithmic_bytes(B, H, L, dk, dv)
             sec_out["masked"] = {"workload": "masked_256x12x64x64", "variant": "falcon1",
                                  "kernel": "masked_wy_kernel<64,true,false,false>",
                                  "ms_per_call": sec * 1e3, "median_ms": st["median_s"] * 1e3,
                                  "tokens_per_s": B * L / sec,
-                                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
-                                 "chunk_form_ms_per_call": sec_c * 1e3,
-                                 "chunk_form_median_ms": stc["median_s"] * 1e3}
+                                 "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS}
             del q, k, v, o
             torch.cuda.empty_cache()
         if args.only in (None, "backward"):

@@ -131,7 +131,9 @@ int falcon_fwd_recurrent(int variant, int window, float beta, const void* beta_t
  *   windows 2..4 of the regression family; 64 for the inner-product family with
  *   shared gains; the requested length, halved until chunk * window <= 64 and
  *   at most 32 at dk 128, otherwise); the result does not depend on it beyond
- *   rounding.
+ *   rounding.  A call of at most FALCON_MASKED_MAX_LEN (64) steps with window 1
+ *   and gains shared by the value rows is one chunk; it runs the kernel of
+ *   falcon_fwd_masked (the whole call as one masked system, exact for any decay).
  * The result equals the recurrence up to floating-point rounding (state
  * carried in float32, products on bf16 matrix cores with split-bf16 operands
  * where an operand is not an exact bf16 input) for every finite input: the

@@ -711,6 +711,11 @@ int chunk_sub_length(int chunk, int window, int dk) {
 hipError_t launch_chunk(const SeqArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
   (void)hipGetLastError();
   const int cs = chunk_sub_length(a.chunk, a.window, a.dk);
+  // a call of at most 64 steps (window 1, gains shared by the value rows) is a
+  // single chunk: the masked-parallel kernel solves that system once for every
+  // value row, exactly (no decay product is divided by) and faster than the
+  // 32-step kernel's pipeline, which needs several chunks to fill
+  if (a.window == 1 && a.beta_kind != 2 && a.seqlen <= kMaskedMaxLen) return launch_masked(a, stream);
   if (chunk_wy_supported(a)) return launch_chunk_wy(a, stream);
   if (chunk_ip_supported(a)) return launch_chunk_ip(a, stream);
   if (ws != nullptr) {
