@@ -387,9 +387,12 @@ __global__ __launch_bounds__(1024) void masked_kernel(SeqArgs a, int rb) {
 // and pin_t the product over t's block b before t (up to t itself for W), so
 // strong forgetting stays exact here too.  The solve is blocked:
 // T_bb = (I + A_bb)^-1 by a DPP forward substitution, then
-// E_b = T_bb (R_b - sum_{k<b} A_bk E_k) on the matrix cores, split-bf16
-// (Henry, Tang & Heinecke, ARITH 2019) for every operand that is not an exact
-// bf16 input.
+// E_b = T_bb (R_b - sum_{k<b} A_bk E_k) on the matrix cores.  Precision: the
+// entry-wise factors (A, W, T, E) are split-bf16 (Henry, Tang & Heinecke, ARITH
+// 2019: hi + lo, three products); every dot product that may cancel (x . x,
+// q . x, X S0^T, Q S0^T) is exact up to fp32 accumulation: bf16 inputs on the
+// bf16 matrix cores, the fp32 start state in three bf16 pieces (2^-24), fp32
+// inputs on the fp32 matrix cores.
 //
 // Work decomposition: one workgroup (4 waves, about 37 KB of LDS at dk = 64, so
 // four workgroups share a compute unit) per (chain, block of <= 64 value rows);
