@@ -11,7 +11,7 @@ import pytest
 
 from oracle import falcon_oracle as fo
 from weight_recurrent_memory_amd.inputs import seq_inputs
-from parity_util import TOL_FP32_MATH, state_err, to_dev, token_normwise_err
+from parity_util import TOL_BF16, TOL_FP32_MATH, state_err, to_dev, token_normwise_err
 
 pytestmark = pytest.mark.gpu
 
@@ -252,3 +252,36 @@ def test_masked_shared_gains_deterministic():
     b = _run(inp, fw.FALCON_1, "bf16", window=1, beta=None, lam=0.01, eps=1e-6)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("variant", [fw.FALCON_1, fw.FALCON_1A])
+@pytest.mark.parametrize("L,carried", [(1, False), (33, True), (64, False), (64, True)])
+def test_chunk_call_of_one_chunk_runs_the_masked_kernel(variant, L, carried):
+    """falcon_fwd_chunk with at most 64 steps, window 1 and shared gains is one chunk:
+    it runs the masked form's one-system kernel, so both entry points return the
+    same bits; a 65-step call still takes the chunk kernel and meets the bf16 gate."""
+    inp = seq_inputs(3, 2, L, 64, 64, seed=1500 + 3 * variant + L, dtype="bf16",
+                     with_k_prev=carried, with_S0=carried, s_std=0.2, beta_per_token=True)
+    dt = torch.bfloat16
+    q, k, v, bt = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "beta_t"))
+    kp = to_dev(torch, inp["k_prev"], dt) if carried else None
+    S0 = to_dev(torch, inp["S0"], torch.float32) if carried else None
+    kw = dict(variant=variant, beta=None, lam=0.01, eps=1e-6, beta_t=bt, k_prev=kp, S0=S0,
+              return_state=True)
+    o_c, S_c = fw.fwd_chunk(q, k, v, chunk=64, **kw)
+    o_m, S_m = fw.fwd_masked(q, k, v, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_m) and torch.equal(S_c, S_m)
+
+
+def test_chunk_call_past_one_chunk():
+    inp = seq_inputs(3, 2, 65, 64, 64, seed=1520, dtype="bf16", with_k_prev=True,
+                     with_S0=True, s_std=0.2)
+    dt = torch.bfloat16
+    q, k, v, kp = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v", "k_prev"))
+    S0 = to_dev(torch, inp["S0"], torch.float32)
+    o, S = fw.fwd_chunk(q, k, v, variant=fw.FALCON_1, beta=0.5, lam=0.01, eps=1e-6, chunk=64,
+                        k_prev=kp, S0=S0, return_state=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _ref(inp, fw.FALCON_1, window=1, beta=0.5, lam=0.01, eps=1e-6)
+    _check(o.cpu().numpy(), S.cpu().numpy(), o_ref, S_ref, tol=TOL_BF16, label="L 65 chunk")
