@@ -435,7 +435,7 @@ def main():
             del a, b
     if sec_out:
         out["secondary"] = sec_out
-    # the attainable bandwidth of this machine (the same run's 1 GiB copy) beside the
+    # the attainable bandwidth of this GPU (the same run's 1 GiB copy) beside the
     # data-sheet peak: each HBM-bound figure as a fraction of both
     copy_gbs = sec_out.get("copy_1GiB", {}).get("gbs")
     if copy_gbs:
