@@ -277,7 +277,10 @@ def decode_step(S, k_prev, q, k, v, *, variant, beta=0.5, lam=0.0, eps=1e-6, bet
     if out is None:
         out = torch.empty((N, H, dv), device=dev, dtype=torch.float32)
     _check(torch, "out", out, (N, H, dv), torch.float32, dev)
-    if window > 1 or x_hist is not None or y_hist is not None or same_step:
+    # Falcon-3/3A (any window), a history or the same-step pairing: the extended
+    # entry point; the plain one takes the un-windowed variants only
+    if (window > 1 or x_hist is not None or y_hist is not None or same_step
+            or variant in (FALCON_3, FALCON_3A)):
         _check(torch, "x_hist", x_hist, (N, H, int(window) - 1, dk), dt, dev)
         _check(torch, "y_hist", y_hist, (N, H, int(window) - 1, dv), dt, dev)
         status = lib.falcon_decode_step_ex(
