@@ -493,6 +493,38 @@ def test_decode_same_step(variant):
     assert state_err(S.cpu().numpy(), S_r) <= TOL_FP32_MATH
 
 
+@pytest.mark.parametrize("variant,base", [(fw.FALCON_3, fw.FALCON_1), (fw.FALCON_3A, fw.FALCON_1A)])
+@pytest.mark.parametrize("same_step", [False, True])
+def test_decode_windowed_variant_at_window_1(variant, base, same_step):
+    """A window of one sample: the windowed variant's decode step is its un-windowed
+    base (same bits), and meets the oracle's windowed decode; the binding takes the
+    extended entry point for it (the plain one refuses the windowed variants)."""
+    inp = decode_inputs(3, 2, 64, 32, seed=730 + variant, steps=4, s_std=0.2)
+    dt = torch.bfloat16
+    qs, ks, vs = (to_dev(torch, inp[n], dt) for n in ("q", "k", "v"))
+    runs = {}
+    for var in (variant, base):
+        S = to_dev(torch, inp["S"], torch.float32)
+        kp = None if same_step else to_dev(torch, inp["k_prev"], dt)
+        os_ = [fw.decode_step(S, kp, qs[p], ks[p], vs[p], variant=var, beta=0.6, lam=0.02,
+                              eps=1e-6, same_step=same_step).cpu().numpy() for p in range(4)]
+        torch.cuda.synchronize()
+        runs[var] = (os_, S.cpu().numpy(), None if kp is None else kp.float().cpu().numpy())
+    for a, b in zip(runs[variant][0], runs[base][0]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(runs[variant][1], runs[base][1])
+    S_r, kp_r = inp["S"].astype(np.float64), inp["k_prev"].astype(np.float64)
+    for p in range(4):
+        o_r, S_r, kp_r, _, _ = fo.falcon_decode_step_window(
+            variant, 1, S_r, kp_r, None, None, inp["q"][p], inp["k"][p], inp["v"][p], beta=0.6,
+            lam=0.02, eps=1e-6, same_step=same_step)
+        err, zok = token_normwise_err(runs[variant][0][p], o_r)
+        assert zok and err <= TOL_FP32_MATH, (p, err)
+    assert state_err(runs[variant][1], S_r) <= TOL_FP32_MATH
+    if not same_step:
+        np.testing.assert_array_equal(runs[variant][2], kp_r)
+
+
 # ---------------------------------------------------------------------------
 # backward of the window-1 chunk form
 
