@@ -440,6 +440,12 @@ struct MaskedWyLds {
   float bpre[5], bsuf[4], mid[4][4];
 };
 
+// Position of the 16-byte group lg (0..3) of fragment row lr in a 64-byte row of
+// Ah/Al/Wh/Wl: the group index is XORed with bits 2-3 of the row, so the 16 rows
+// that a quarter-wave reads or writes at one group fall on 16 different 4-bank
+// slots instead of four rows per slot.
+__device__ __forceinline__ int wy_frag_col(int lr, int lg) { return 8 * (lg ^ ((lr >> 2) & 3)); }
+
 template <int N>
 __device__ __forceinline__ float wy_shr(float v, float fill) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, v),
@@ -918,10 +924,12 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
           }
         }
       }
-      uint16_t* fh = wave == 1 ? &sm.f.Ah[f][lr][8 * lg] : &sm.f.Wh[f][lr][8 * lg];
-      uint16_t* fl = wave == 1 ? &sm.f.Al[f][lr][8 * lg] : &sm.f.Wl[f][lr][8 * lg];
-      store_split4(fh, fl, v);
-      store_split4(fh + 4, fl + 4, v + 4);
+      const int fc = wy_frag_col(lr, lg);
+      uint16_t* fh = wave == 1 ? &sm.f.Ah[f][lr][fc] : &sm.f.Wh[f][lr][fc];
+      uint16_t* fl = wave == 1 ? &sm.f.Al[f][lr][fc] : &sm.f.Wl[f][lr][fc];
+      const HL hv = hl_vals(v);             // one 16-byte store per piece
+      *reinterpret_cast<bf16x8*>(fh) = hv.hi;
+      *reinterpret_cast<bf16x8*>(fl) = hv.lo;
     }
   }
   __syncthreads();
@@ -945,7 +953,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
 #pragma unroll
       for (int p = 0; 2 * p < b; ++p) {
         const int f = b == 1 ? 0 : b == 2 ? 1 : (p == 0 ? 2 : 3);
-        acc = wy_mma3(acc, hl_pair(&sm.f.Ah[f][lr][8 * lg], &sm.f.Al[f][lr][8 * lg]), Eop[p]);
+        acc = wy_mma3(acc, hl_pair(&sm.f.Ah[f][lr][wy_frag_col(lr, lg)], &sm.f.Al[f][lr][wy_frag_col(lr, lg)]), Eop[p]);
       }
       const float4 t4 = *reinterpret_cast<const float4*>(&sm.TS[b][lr][4 * lg]);
       const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
@@ -974,7 +982,7 @@ __global__ __launch_bounds__(kWyThreads, HS0 ? 2 : 4) void masked_wy_kernel(SeqA
 #pragma unroll
     for (int p = 0; 2 * p <= b; ++p) {
       const int f = b == 0 ? 0 : b == 1 ? 1 : b == 2 ? 2 + p : 4 + p;
-      o = wy_mma3(o, hl_pair(&sm.f.Wh[f][lr][8 * lg], &sm.f.Wl[f][lr][8 * lg]), Eop[p]);
+      o = wy_mma3(o, hl_pair(&sm.f.Wh[f][lr][wy_frag_col(lr, lg)], &sm.f.Wl[f][lr][wy_frag_col(lr, lg)]), Eop[p]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
