@@ -652,11 +652,13 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
     }
   } else {
     // ---------------- preparation waves ----------------
-    // iteration c:  wave 2  Gram of c+4, q.x of c+2, keys of c+3 transposed
+    // iteration c:  wave 2  Gram of c+4, q.x of c+2 (inner-product family:
+    //                       q.x of c+2, keys of c+3 transposed)
     //               wave 3  Wt tiles 0, 1 of c+2    wave 6  Wt tiles 2, 3 of c+2
     //               wave 7  Ut tiles of c+2
     //               waves 2, 3, 6, 7  commit keys of c+5, queries of c+3
-    //               wave 4  scalars of c+4, commit gains of c+5 and values of c+3
+    //               wave 4  scalars of c+4, keys of c+3 transposed (regression
+    //                       family), commit gains of c+5 and values of c+3
     //               wave 5  factors of c+3 (inner-product family: part of z of c+2)
     // A wave reads its LDS operands first, then commits, then computes (the LDS
     // round trip overlaps the commit).  Global loads are issued two iterations
@@ -689,9 +691,11 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
         move();
         if (REG && live_chunk(c + 4)) gram_store(c + 4, xg);
         if (live_chunk(c + 2)) qx_store(c + 2, xq, qq);
-        if (live_chunk(c + 3)) {
-          transpose_keys(c + 3, lane);
-          transpose_keys(c + 3, 64 + lane);
+        if constexpr (!REG) {
+          if (live_chunk(c + 3)) {
+            transpose_keys(c + 3, lane);
+            transpose_keys(c + 3, 64 + lane);
+          }
         }
       });
     } else if (wave != 4 && wave != 5) {
@@ -722,6 +726,16 @@ __global__ __launch_bounds__(NT) void chunk_wy_kernel(SeqArgs a, WyGeom geo) {
         commit_vb(cur, c + 5, c + 3);
         prefetch_vb(cur, c + 7, c + 5);
         if (c + 4 >= 0 && c + 4 < nchunks) scalars(c + 4);
+        // regression family: the key transposes leave wave 2 (Gram and q.x, on
+        // the SIMD of a solve-tile wave) for this light wave (measured 0.5-2% on
+        // 8x12x2048x64); in the inner-product family wave 2 has no Gram and this
+        // wave's SIMD carries the critical state wave, so they stay on wave 2
+        if constexpr (REG) {
+          if (live_chunk(c + 3)) {
+            transpose_keys(c + 3, lane);
+            transpose_keys(c + 3, 64 + lane);
+          }
+        }
       };
       for (int c = -5; c < cend; c += 2) {
         iteration(c, ps0);
